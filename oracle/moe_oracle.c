@@ -1,0 +1,314 @@
+/* CPU ORACLE for one GLM-5.2-style (glm_moe_dsa) MoE layer forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the plain, slow, fp64 definition of what
+ * the layer computes.  Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg may load it; the GPU library never does, and the two share
+ * no code (this file has its own types, decoders and loops).
+ *
+ * Sources (web pages; cited by title and section):
+ *  [PORT]   "GLM-5.2 on a 32 GB Mac - native MLX port of the Colibri hierarchy"
+ *           (mlx-bun design doc): section "N1. GLM-5.2 graph" (sigmoid scores plus
+ *           correction bias select, un-biased weights execute, true top-8, optional
+ *           normalisation and routed scale, shared expert in parallel);
+ *           "G2 implementation status" (lower expert ID wins exact ties; unbiased
+ *           sigmoid for execution; routed scaling; unweighted shared expert; Q4
+ *           nibbles are offset-binary, i.e. value = nibble - 8, MLX bias = -8*scale;
+ *           dequantise then f32 multiply-accumulate).
+ *  [README] colibri README, "What's implemented" (DeepSeek-V3-style sigmoid
+ *           router, noaux_tc, routed_scaling_factor, shared expert).
+ *  [MODELS] "Model support" doc, section 4.3 UniversalMoE (top-k, norm_topk_probs,
+ *           sigmoid scoring, routing scale, shared expert, grouped routing in the
+ *           deepseek_v3 style) and section 6.4 GLM-5.2.
+ *
+ * Readings where the pages are silent (all of them listed in the design notes):
+ *  R1 groups are n_group contiguous blocks of E/n_group experts; a group's score
+ *     is the sum of its two largest selection keys; the topk_group best groups
+ *     are kept (ties: lower group index) and experts outside them are excluded.
+ *  R2 ranking compares fp32-rounded keys key_e = fp32(sigmoid(l_e) + bias_e) with
+ *     the sigmoid and the sum in fp64; a group score is fp32(k1 + k2); exact ties
+ *     go to the lower expert (group) index.  idx is emitted in rank order.
+ *  R3 w_j = s_j / sum_m s_m * rsf when norm_topk_prob, else s_j * rsf; no epsilon.
+ *  R4 SwiGLU expert: h = silu(Wg x) * (Wu x), y_e = Wd h, silu(z) = z/(1+e^-z);
+ *     no biases, no clamp.  Shared expert has weight 1, added after the routed sum.
+ *  R5 int4 scales are fp16, one per 32 consecutive elements along the contraction.
+ *
+ * Parity pins: tests/test_oracle_pins.py (brute force, closed forms, invariants).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- decoders */
+
+/* IEEE 754 binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+double oracle_f16_to_f64(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int ex = (h >> 10) & 0x1F;
+  int frac = h & 0x3FF;
+  double v;
+  if (ex == 0) {
+    v = ldexp((double)frac, -24); /* subnormal: frac * 2^-14 * 2^-10 */
+  } else if (ex == 31) {
+    v = frac ? NAN : INFINITY;
+  } else {
+    v = ldexp(1024.0 + (double)frac, ex - 25); /* (1 + frac/1024) * 2^(ex-15) */
+  }
+  return sign ? -v : v;
+}
+
+/* bfloat16 is the upper half of an fp32 word. */
+double oracle_bf16_to_f64(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* int4 element c of a row of offset-binary nibbles: value = nibble - 8
+ * (element 2j in the low nibble of byte j, 2j+1 in the high nibble). */
+static int q_of(const uint8_t *row, int c) {
+  uint8_t b = row[c >> 1];
+  int u = (c & 1) ? (b >> 4) : (b & 0x0F);
+  return u - 8;
+}
+
+/* Dequantised weight matrix [R, K]: W[r,c] = q[r,c] * s[r, c/gsz]  (exact in fp64). */
+void oracle_dequant(int R, int K, int gsz, const uint8_t *q, const uint16_t *s, double *out) {
+  for (int r = 0; r < R; ++r)
+    for (int c = 0; c < K; ++c)
+      out[(size_t)r * K + c] =
+          (double)q_of(q + (size_t)r * (K / 2), c) * oracle_f16_to_f64(s[(size_t)r * (K / gsz) + c / gsz]);
+}
+
+/* ------------------------------------------------------------------ router */
+
+/* distance-from-midpoint test: is fp64 v within 2^-40 |v| of a point where
+ * rounding to fp32 changes direction? */
+static int near_f32_midpoint(double v) {
+  float f = (float)v;
+  if ((double)f == v || !isfinite(v)) return 0;
+  float g = nextafterf(f, v > (double)f ? INFINITY : -INFINITY);
+  double mid = 0.5 * ((double)f + (double)g);
+  return fabs(v - mid) <= ldexp(fabs(v), -40);
+}
+
+static double ulp32(float f) {
+  float g = nextafterf(fabsf(f), INFINITY);
+  return (double)g - (double)fabsf(f);
+}
+
+/* Decision diagnostics per token. */
+typedef struct {
+  double expert_margin; /* key(k-th pick) - best excluded candidate key, fp32 values */
+  double group_margin;  /* score(Gk-th group) - best dropped group score */
+  int32_t flags;        /* bit0: a fp32 rounding near a midpoint could change a decision */
+  int32_t n_candidates; /* experts in the kept groups */
+} oracle_diag;
+
+/* One token's selection from its logits l[E] (fp64).
+ * Steps follow [PORT] N1 / G2 status and [MODELS] 4.3 with readings R1-R3. */
+int oracle_select(int E, int G, int Gk, int k, double rsf, int norm, const double *logits,
+                  const float *bias, int32_t *idx, double *w, double *s_out, oracle_diag *diag) {
+  if (E <= 0 || G <= 0 || E % G || Gk < 1 || Gk > G || k < 1 || k > Gk * (E / G)) return -1;
+  const int per = E / G;
+  double *s = malloc(sizeof(double) * E);
+  double *key64 = malloc(sizeof(double) * E);
+  float *key = malloc(sizeof(float) * E);
+  float *gscore = malloc(sizeof(float) * G);
+  double *gscore64 = malloc(sizeof(double) * G);
+  char *gkeep = calloc(G, 1), *taken = calloc(E, 1), *cand = calloc(E, 1);
+  int flags = 0;
+
+  /* sigmoid scores (unbiased) and biased selection keys */
+  for (int e = 0; e < E; ++e) {
+    s[e] = 1.0 / (1.0 + exp(-logits[e]));
+    key64[e] = s[e] + (double)bias[e];
+    key[e] = (float)key64[e];
+    if (s_out) s_out[e] = s[e];
+  }
+  /* group score = sum of the two largest keys in the group */
+  for (int j = 0; j < G; ++j) {
+    int b1 = -1, b2 = -1;
+    for (int e = j * per; e < (j + 1) * per; ++e) {
+      if (b1 < 0 || key[e] > key[b1]) { b2 = b1; b1 = e; }
+      else if (b2 < 0 || key[e] > key[b2]) { b2 = e; }
+    }
+    double sum = (double)key[b1] + (b2 >= 0 ? (double)key[b2] : 0.0);
+    gscore64[j] = sum;
+    gscore[j] = (float)sum;
+  }
+  /* keep the topk_group best groups (ties: lower group index) */
+  float last_kept = 0.0f;
+  for (int it = 0; it < Gk; ++it) {
+    int best = -1;
+    for (int j = 0; j < G; ++j)
+      if (!gkeep[j] && (best < 0 || gscore[j] > gscore[best])) best = j;
+    gkeep[best] = 1;
+    last_kept = gscore[best];
+  }
+  double gmargin = INFINITY;
+  for (int j = 0; j < G; ++j)
+    if (!gkeep[j]) {
+      double m = (double)last_kept - (double)gscore[j];
+      if (m < gmargin) gmargin = m;
+      if (m <= 2.0 * ulp32(last_kept)) {
+        /* a near-tied group decision: sensitive if any score or key feeding it sits near a midpoint */
+        for (int jj = 0; jj < G; ++jj)
+          if ((gkeep[jj] && gscore[jj] == last_kept) || jj == j) {
+            if (near_f32_midpoint(gscore64[jj])) flags |= 1;
+            for (int e = jj * per; e < (jj + 1) * per; ++e)
+              if (near_f32_midpoint(key64[e])) flags |= 1;
+          }
+      }
+    }
+  int ncand = 0;
+  for (int e = 0; e < E; ++e)
+    if (gkeep[e / per]) { cand[e] = 1; ++ncand; }
+  /* top-k over the kept experts (ties: lower expert index), emitted in rank order */
+  for (int it = 0; it < k; ++it) {
+    int best = -1;
+    for (int e = 0; e < E; ++e)
+      if (cand[e] && !taken[e] && (best < 0 || key[e] > key[best])) best = e;
+    taken[best] = 1;
+    idx[it] = best;
+  }
+  /* sensitivity of the expert decisions: adjacent ranks and the cut-off */
+  double emargin = INFINITY;
+  for (int e = 0; e < E; ++e)
+    if (cand[e] && !taken[e]) {
+      double m = (double)key[idx[k - 1]] - (double)key[e];
+      if (m < emargin) emargin = m;
+    }
+  for (int it = 0; it < k; ++it) {
+    float a = key[idx[it]];
+    for (int e = 0; e < E; ++e) {
+      if (!cand[e] || e == idx[it]) continue;
+      int later = !taken[e];
+      for (int jt = it + 1; jt < k; ++jt) later |= (idx[jt] == e);
+      if (!later) continue;
+      if ((double)a - (double)key[e] <= ulp32(a) &&
+          (near_f32_midpoint(key64[idx[it]]) || near_f32_midpoint(key64[e])))
+        flags |= 1;
+    }
+  }
+  /* weights from the unbiased sigmoid, renormalised and scaled */
+  double denom = 0.0;
+  for (int it = 0; it < k; ++it) denom += s[idx[it]];
+  for (int it = 0; it < k; ++it) w[it] = norm ? s[idx[it]] / denom * rsf : s[idx[it]] * rsf;
+
+  if (diag) {
+    diag->expert_margin = emargin;
+    diag->group_margin = gmargin;
+    diag->flags = flags;
+    diag->n_candidates = ncand;
+  }
+  free(s); free(key64); free(key); free(gscore); free(gscore64);
+  free(gkeep); free(taken); free(cand);
+  return 0;
+}
+
+/* logit l[t,e] = sum_h x[t,h] W[e,h], fp64, h ascending. x is fp32, or bf16 bits. */
+static double x_at(const void *x, int x_is_bf16, size_t i) {
+  return x_is_bf16 ? oracle_bf16_to_f64(((const uint16_t *)x)[i]) : (double)((const float *)x)[i];
+}
+
+int oracle_route(int S, int H, int E, int G, int Gk, int k, double rsf, int norm, int x_is_bf16,
+                 const void *x, const float *W, const float *bias, int32_t *idx, double *w,
+                 double *logits_out, oracle_diag *diag) {
+  if (S < 0 || H <= 0) return -1;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int t = 0; t < S; ++t) {
+    double *l = malloc(sizeof(double) * E);
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int h = 0; h < H; ++h) acc += x_at(x, x_is_bf16, (size_t)t * H + h) * (double)W[(size_t)e * H + h];
+      l[e] = acc;
+      if (logits_out) logits_out[(size_t)t * E + e] = acc;
+    }
+    if (oracle_select(E, G, Gk, k, rsf, norm, l, bias, idx + (size_t)t * k, w + (size_t)t * k, NULL,
+                      diag ? diag + t : NULL))
+      bad = 1;
+    free(l);
+  }
+  return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------ expert FFN */
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* y[H] = Wd (silu(Wg x) * (Wu x)) for one token, fp64.  Matrices in the
+ * interchange layout: gate/up [I, H], down [H, I], nibbles + fp16 group scales.
+ * h_out (optional) receives the [I] hidden activation. */
+void oracle_expert_ffn(int H, int I, int gsz, const uint8_t *qg, const uint16_t *sg, const uint8_t *qu,
+                       const uint16_t *su, const uint8_t *qd, const uint16_t *sd, const double *x, double *y,
+                       double *h_out) {
+  double *h = malloc(sizeof(double) * I);
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < I; ++r) {
+    const uint8_t *rg = qg + (size_t)r * (H / 2), *ru = qu + (size_t)r * (H / 2);
+    double g = 0.0, u = 0.0;
+    for (int c = 0; c < H; ++c) {
+      double wg = (double)q_of(rg, c) * oracle_f16_to_f64(sg[(size_t)r * (H / gsz) + c / gsz]);
+      double wu = (double)q_of(ru, c) * oracle_f16_to_f64(su[(size_t)r * (H / gsz) + c / gsz]);
+      g += wg * x[c];
+      u += wu * x[c];
+    }
+    h[r] = silu(g) * u;
+  }
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < H; ++r) {
+    const uint8_t *rd = qd + (size_t)r * (I / 2);
+    double acc = 0.0;
+    for (int c = 0; c < I; ++c)
+      acc += (double)q_of(rd, c) * oracle_f16_to_f64(sd[(size_t)r * (I / gsz) + c / gsz]) * h[c];
+    y[r] = acc;
+  }
+  if (h_out) memcpy(h_out, h, sizeof(double) * I);
+  free(h);
+}
+
+/* The layer for S tokens given routing (idx, w):
+ *   y[t] = sum_j w[t,j] * FFN_{idx[t,j]}(x_t)  (rank order)  +  FFN_shared(x_t).
+ * Expert e's six parts are qg[e], sg[e], ... (pointer arrays of length E+1; entry E
+ * is the shared expert, NULL when the layer has none).  Only experts that the
+ * routing names need non-NULL pointers. */
+int oracle_moe_ffn(int S, int H, int E, int k, int I, int Is, int gsz, int x_is_bf16, const void *x,
+                   const int32_t *idx, const double *w, const uint8_t *const *qg, const uint16_t *const *sg,
+                   const uint8_t *const *qu, const uint16_t *const *su, const uint8_t *const *qd,
+                   const uint16_t *const *sd, double *y) {
+  double *xt = malloc(sizeof(double) * H), *ye = malloc(sizeof(double) * H), *acc = malloc(sizeof(double) * H);
+  int rc = 0;
+  for (int t = 0; t < S && !rc; ++t) {
+    for (int c = 0; c < H; ++c) xt[c] = x_at(x, x_is_bf16, (size_t)t * H + c);
+    for (int c = 0; c < H; ++c) acc[c] = 0.0;
+    for (int j = 0; j < k; ++j) {
+      int e = idx[(size_t)t * k + j];
+      if (e < 0 || e >= E || !qg[e] || !sg[e] || !qu[e] || !su[e] || !qd[e] || !sd[e]) { rc = -1; break; }
+      oracle_expert_ffn(H, I, gsz, qg[e], sg[e], qu[e], su[e], qd[e], sd[e], xt, ye, NULL);
+      for (int c = 0; c < H; ++c) acc[c] += w[(size_t)t * k + j] * ye[c];
+    }
+    if (rc) break;
+    if (Is > 0) {
+      if (!qg[E]) { rc = -1; break; }
+      oracle_expert_ffn(H, Is, gsz, qg[E], sg[E], qu[E], su[E], qd[E], sd[E], xt, ye, NULL);
+      for (int c = 0; c < H; ++c) acc[c] += ye[c];
+    }
+    for (int c = 0; c < H; ++c) y[(size_t)t * H + c] = acc[c];
+  }
+  free(xt); free(ye); free(acc);
+  return rc;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,17 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; runs the HIP library")
+    config.addinivalue_line("markers", "slow: long CPU-side oracle runs")
+
+
+def pytest_report_header(config):
+    return ["int4 routed-expert MoE layer: oracle pins (CPU) and HIP parity (gpu)"]

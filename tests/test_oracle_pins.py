@@ -1,0 +1,342 @@
+"""Pins of the fp64 CPU oracle against things other than itself.
+
+* router selection: brute force over every group subset and every expert subset
+  (exact rational sums) on tiny seeded inputs, including constructed exact ties;
+* special cases that reduce to a library routine (one group: a stable argsort;
+  zero bias: top-k of the logits);
+* closed-form weights (tests/golden/router_hand_example.json) and the invariant
+  sum(w) = routed_scaling_factor;
+* fp16 / bf16 decoders against numpy over every bit pattern; dequantisation
+  against the closed form q * s computed with numpy;
+* the expert FFN and the routed + shared composition against numpy float64
+  matmuls on independently dequantised matrices; zero input gives exactly zero;
+  a single routed expert gets weight rsf exactly.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from gen import inputs as gen
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def cfg_of(E, G, Gk, k, rsf=2.5, norm=1, H=8, I=32):
+    return gen.LayerConfig(hidden=H, n_experts=E, n_group=G, topk_group=Gk, top_k=k, moe_inter=I,
+                           shared_inter=I, routed_scaling_factor=rsf, norm_topk_prob=norm)
+
+
+# ------------------------------------------------------------------ decoders
+
+def test_f16_decoder_all_bit_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    mine = np.array([O.f16_to_f64(int(b)) for b in bits])
+    both_nan = np.isnan(ref) & np.isnan(mine)
+    assert np.all((ref == mine) | both_nan)
+    assert np.array_equal(np.signbit(ref[~both_nan]), np.signbit(mine[~both_nan]))
+
+
+def test_bf16_decoder_all_bit_patterns():
+    bits = np.arange(65536, dtype=np.uint32)
+    ref = (bits << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    mine = np.array([O.bf16_to_f64(int(b)) for b in bits])
+    both_nan = np.isnan(ref) & np.isnan(mine)
+    assert np.all((ref == mine) | both_nan)
+
+
+def numpy_dequant(q, s, gsz=32):
+    """Independent closed form: offset-binary nibbles (low nibble = even element) times fp16 scales."""
+    lo = (q & 0x0F).astype(np.int64) - 8
+    hi = (q >> 4).astype(np.int64) - 8
+    vals = np.empty((q.shape[0], q.shape[1] * 2), np.float64)
+    vals[:, 0::2] = lo
+    vals[:, 1::2] = hi
+    sc = np.repeat(s.view(np.float16).astype(np.float64), gsz, axis=1)
+    return vals * sc
+
+
+def test_dequant_closed_form():
+    rng = np.random.default_rng(5)
+    q = rng.integers(0, 256, (7, 48), dtype=np.uint8)
+    s = gen.encode_f16(np.abs(rng.normal(0, 0.02, (7, 3))))
+    s[0, 0] = 0x0001  # smallest subnormal
+    s[1, 1] = 0x7BFF  # largest normal
+    got = O.dequant(q, s)
+    assert np.array_equal(got, numpy_dequant(q, s))
+    # q * s is exact in fp32 as well (4-bit integer times 11-bit significand)
+    assert np.array_equal(got.astype(np.float32).astype(np.float64), got)
+
+
+def test_nibble_order_and_offset_binary():
+    # byte 0x8F: low nibble 15 -> +7 at element 0, high nibble 8 -> 0 at element 1
+    q = np.array([[0x8F, 0x07]], np.uint8)
+    s = gen.encode_f16(np.ones((1, 1)))
+    q32 = np.zeros((1, 16), np.uint8)
+    q32[0, :2] = q[0]
+    got = O.dequant(q32, s)[0, :4]
+    assert list(got) == [7.0, 0.0, -1.0, -8.0]
+
+
+# ------------------------------------------------------------- router: brute force
+
+def brute_force_select(E, G, Gk, k, s, bias, rsf=2.5, norm=1):
+    """Every subset, exact rational sums: the kept groups are the Gk-subset of
+    maximal total score (ties: lexicographically smallest), the experts the
+    k-subset of maximal total key among the kept ones (ties likewise); rank by
+    key desc then index asc."""
+    per = E // G
+    key = [np.float32(np.float64(s[e]) + np.float64(bias[e])) for e in range(E)]
+    kf = [Fraction(float(v)) for v in key]
+    gscore = []
+    for j in range(G):
+        mem = list(range(j * per, (j + 1) * per))
+        if per == 1:
+            best = kf[mem[0]]
+        else:
+            best = max(kf[a] + kf[b] for a, b in itertools.combinations(mem, 2))
+        gscore.append(Fraction(float(np.float32(float(best)))))
+    best_groups, best_val = None, None
+    for sub in itertools.combinations(range(G), Gk):  # lexicographic order
+        v = sum(gscore[j] for j in sub)
+        if best_val is None or v > best_val:
+            best_groups, best_val = sub, v
+    cand = [e for e in range(E) if e // per in best_groups]
+    best_set, best_val = None, None
+    for sub in itertools.combinations(cand, k):
+        v = sum(kf[e] for e in sub)
+        if best_val is None or v > best_val:
+            best_set, best_val = sub, v
+    order = sorted(best_set, key=lambda e: (-kf[e], e))
+    ssum = sum(s[e] for e in order)
+    w = [s[e] / ssum * rsf if norm else s[e] * rsf for e in order]
+    return order, w
+
+
+SHAPES = [(16, 4, 2, 2), (16, 4, 2, 3), (16, 4, 4, 5), (32, 8, 3, 4), (12, 3, 1, 2), (8, 8, 3, 2), (6, 2, 2, 6)]
+
+
+@pytest.mark.parametrize("E,G,Gk,k", SHAPES)
+def test_router_selection_brute_force_random(E, G, Gk, k):
+    rng = np.random.default_rng(1000 + E * 7 + G * 3 + k)
+    cfg = cfg_of(E, G, Gk, k)
+    n_subsets = math.comb(Gk * (E // G), k)
+    n = 1500 if n_subsets < 1000 else 120
+    for _ in range(n):
+        logits = rng.normal(0, 1, E)
+        bias = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+        idx, w, s, dg = O.select(cfg, logits, bias)
+        ref_idx, ref_w = brute_force_select(E, G, Gk, k, s, bias)
+        assert list(idx) == ref_idx
+        np.testing.assert_allclose(w, ref_w, rtol=1e-15)
+
+
+@pytest.mark.parametrize("E,G,Gk,k", SHAPES)
+def test_router_selection_brute_force_ties(E, G, Gk, k):
+    """Exact key ties: zero logits (s = 1/2) and biases drawn from a small set."""
+    rng = np.random.default_rng(77 + E + k)
+    cfg = cfg_of(E, G, Gk, k)
+    n_trials = 400 if math.comb(Gk * (E // G), k) < 1000 else 60
+    for trial in range(n_trials):
+        choices = np.float32([0.0, 0.125, 0.25, -0.125]) if trial % 2 else np.float32([0.0, 0.25])
+        bias = rng.choice(choices, E).astype(np.float32)
+        logits = np.zeros(E) if trial % 3 else rng.choice([0.0, 1.0], E)
+        idx, w, s, dg = O.select(cfg, logits, bias)
+        ref_idx, ref_w = brute_force_select(E, G, Gk, k, s, bias)
+        assert list(idx) == ref_idx
+        np.testing.assert_allclose(w, ref_w, rtol=1e-15)
+
+
+def test_single_group_is_stable_argsort():
+    rng = np.random.default_rng(3)
+    E, k = 24, 5
+    cfg = cfg_of(E, 1, 1, k)
+    for trial in range(500):
+        logits = rng.normal(0, 1, E) if trial % 2 else np.zeros(E)
+        bias = rng.choice(np.float32([0, 0.25, 0.5]), E).astype(np.float32)
+        idx, w, s, _ = O.select(cfg, logits, bias)
+        key = (s + bias.astype(np.float64)).astype(np.float32)
+        assert list(idx) == list(np.argsort(-key, kind="stable")[:k])
+
+
+def test_zero_bias_is_topk_of_logits():
+    rng = np.random.default_rng(4)
+    E, k = 64, 8
+    cfg = cfg_of(E, 1, 1, k)
+    for _ in range(200):
+        logits = rng.normal(0, 3, E)
+        idx, _, _, _ = O.select(cfg, logits, np.zeros(E, np.float32))
+        assert set(idx) == set(np.argsort(-logits)[:k])
+
+
+def test_hand_examples_golden():
+    d = json.load(open(os.path.join(GOLDEN, "router_hand_example.json")))
+    vals = {"ln3": math.log(3), "-ln3": -math.log(3), "0": 0.0, "ln4": math.log(4)}
+    cfg = cfg_of(4, 1, 1, 2)
+    for case in d["cases"]:
+        logits = np.array([vals[v] for v in case["logits"]])
+        idx, w, s, _ = O.select(cfg, logits, np.array(case["bias"], np.float32))
+        assert list(idx) == case["idx"], case["note"]
+        want = [a / b for a, b in case["w_fraction"]]
+        np.testing.assert_allclose(w, want, rtol=1e-15)
+
+
+def test_weights_sum_to_rsf_and_no_norm():
+    rng = np.random.default_rng(6)
+    cfg = cfg_of(256, 8, 4, 8)
+    cfg_nonorm = cfg_of(256, 8, 4, 8, norm=0)
+    for _ in range(200):
+        logits = rng.normal(0, 1, 256)
+        bias = rng.uniform(-0.1, 0.1, 256).astype(np.float32)
+        idx, w, s, _ = O.select(cfg, logits, bias)
+        assert abs(w.sum() - 2.5) <= 4e-15
+        assert len(set(idx)) == 8
+        idx2, w2, _, _ = O.select(cfg_nonorm, logits, bias)
+        assert list(idx2) == list(idx)
+        np.testing.assert_allclose(w2, 2.5 / (1 + np.exp(-logits[idx])), rtol=1e-15)
+
+
+def test_group_limit_excludes_strong_expert_outside_kept_groups():
+    # expert 0 has the single best key but its group's second key is poor;
+    # groups 1 and 2 have two strong experts each and win the group stage.
+    E, G, Gk, k = 12, 3, 2, 2
+    bias = np.zeros(E, np.float32)
+    bias[0] = 0.5
+    bias[[4, 5, 8, 9]] = 0.3
+    idx, _, _, _ = O.select(cfg_of(E, G, Gk, k), np.zeros(E), bias)
+    assert 0 not in idx and list(idx) == [4, 5]
+
+
+def test_rejects_bad_config():
+    with pytest.raises(ValueError):
+        O.select(cfg_of(16, 5, 2, 2), np.zeros(16), np.zeros(16, np.float32))
+    with pytest.raises(ValueError):
+        O.select(cfg_of(16, 4, 1, 5), np.zeros(16), np.zeros(16, np.float32))
+
+
+# --------------------------------------------------------------- router logits
+
+def test_route_logits_match_numpy_fp64():
+    w = gen.WORKLOADS["tiny"].with_(tokens=9)
+    x = gen.tokens(w)
+    W = gen.router_weights(w)
+    b = gen.router_bias(w)
+    idx, wt, logits, flags, _ = O.route(w.cfg, x, W, b)
+    ref = x.astype(np.float64) @ W.astype(np.float64).T
+    np.testing.assert_allclose(logits, ref, rtol=0, atol=1e-13)
+    for t in range(9):
+        i2, w2, _, _ = O.select(w.cfg, logits[t], b)
+        assert list(i2) == list(idx[t])
+    assert not flags.any()
+
+
+def test_route_bf16_input_decoding():
+    w = gen.WORKLOADS["tiny"].with_(tokens=3, x_dtype="bf16")
+    xb = gen.tokens(w)
+    xf = (xb.astype(np.uint32) << 16).view(np.float32)
+    W = gen.router_weights(w)
+    b = gen.router_bias(w)
+    i1, w1, l1, _, _ = O.route(w.cfg, xb, W, b, x_is_bf16=True)
+    i2, w2, l2, _, _ = O.route(w.cfg, np.ascontiguousarray(xf), W, b)
+    assert np.array_equal(i1, i2) and np.array_equal(l1, l2)
+
+
+def test_zero_input_router():
+    w = gen.WORKLOADS["tiny"].with_(tokens=2)
+    c = w.cfg
+    x = np.zeros((2, c.hidden), np.float32)
+    b = gen.router_bias(w)
+    idx, wt, _, _, _ = O.route(c, x, gen.router_weights(w), b)
+    assert np.all(wt == c.routed_scaling_factor / c.top_k)  # 1.25, exactly representable
+    ref_idx, _ = brute_force_select(c.n_experts, c.n_group, c.topk_group, c.top_k, np.full(c.n_experts, 0.5), b)
+    assert list(idx[0]) == ref_idx and list(idx[1]) == ref_idx
+
+
+# ------------------------------------------------------------------- expert FFN
+
+def numpy_expert(ex, x):
+    Wg = numpy_dequant(ex.qg, ex.sg)
+    Wu = numpy_dequant(ex.qu, ex.su)
+    Wd = numpy_dequant(ex.qd, ex.sd)
+    g = Wg @ x
+    u = Wu @ x
+    h = g / (1.0 + np.exp(-g)) * u
+    return Wd @ h, h
+
+
+def test_expert_ffn_matches_numpy():
+    w = gen.WORKLOADS["tiny"]
+    c = w.cfg
+    ex = gen.expert_weights(w, 0, 3)
+    x = gen.tokens(w)[0].astype(np.float64)
+    y, h = O.expert_ffn(ex, x, c.hidden, return_h=True)
+    ry, rh = numpy_expert(ex, x)
+    np.testing.assert_allclose(h, rh, rtol=1e-12, atol=1e-14 * np.abs(rh).max())
+    np.testing.assert_allclose(y, ry, rtol=1e-12, atol=1e-13 * np.abs(ry).max())
+    assert np.abs(ry).max() > 0.1
+
+
+def test_layer_composition_matches_numpy():
+    w = gen.WORKLOADS["tiny"].with_(tokens=5)
+    c = w.cfg
+    x = gen.tokens(w)
+    idx, wt, _, _, _ = O.route(c, x, gen.router_weights(w), gen.router_bias(w))
+    experts = {e: gen.expert_weights(w, 0, e) for e in set(idx.ravel().tolist()) | {c.n_experts}}
+    y = O.moe_ffn(c, x, idx, wt, experts)
+    for t in range(5):
+        xt = x[t].astype(np.float64)
+        ref = sum(wt[t, j] * numpy_expert(experts[idx[t, j]], xt)[0] for j in range(c.top_k))
+        ref = ref + numpy_expert(experts[c.n_experts], xt)[0]
+        np.testing.assert_allclose(y[t], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_zero_input_gives_zero_output():
+    w = gen.WORKLOADS["tiny"].with_(tokens=2)
+    c = w.cfg
+    x = np.zeros((2, c.hidden), np.float32)
+    idx, wt, _, _, _ = O.route(c, x, gen.router_weights(w), gen.router_bias(w))
+    experts = {e: gen.expert_weights(w, 0, e) for e in set(idx.ravel().tolist()) | {c.n_experts}}
+    y = O.moe_ffn(c, x, idx, wt, experts)
+    assert np.all(y == 0.0)
+
+
+def test_single_expert_weight_is_rsf():
+    base = gen.WORKLOADS["tiny"]
+    c = gen.LayerConfig(**{**base.cfg.__dict__, "top_k": 1})
+    w = base.with_(cfg=c, tokens=3)
+    x = gen.tokens(w)
+    idx, wt, _, _, _ = O.route(c, x, gen.router_weights(w), gen.router_bias(w))
+    assert np.all(wt == 2.5)
+    experts = {e: gen.expert_weights(w, 0, e) for e in set(idx.ravel().tolist()) | {c.n_experts}}
+    y = O.moe_ffn(c, x, idx, wt, experts)
+    for t in range(3):
+        xt = x[t].astype(np.float64)
+        ref = 2.5 * numpy_expert(experts[idx[t, 0]], xt)[0] + numpy_expert(experts[c.n_experts], xt)[0]
+        np.testing.assert_allclose(y[t], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_no_shared_expert():
+    base = gen.WORKLOADS["tiny"]
+    c = gen.LayerConfig(**{**base.cfg.__dict__, "shared_inter": 0})
+    w = base.with_(cfg=c, tokens=2)
+    x = gen.tokens(w)
+    idx, wt, _, _, _ = O.route(c, x, gen.router_weights(w), gen.router_bias(w))
+    experts = {e: gen.expert_weights(w, 0, e) for e in set(idx.ravel().tolist())}
+    y = O.moe_ffn(c, x, idx, wt, experts)
+    ref = sum(wt[0, j] * numpy_expert(experts[idx[0, j]], x[0].astype(np.float64))[0] for j in range(c.top_k))
+    np.testing.assert_allclose(y[0], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_missing_expert_is_an_error():
+    w = gen.WORKLOADS["tiny"]
+    c = w.cfg
+    x = gen.tokens(w)
+    idx = np.array([[0, 1]], np.int32)
+    with pytest.raises(ValueError):
+        O.moe_ffn(c, x, idx, np.ones((1, 2)), {0: gen.expert_weights(w, 0, 0)})
