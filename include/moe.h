@@ -1,0 +1,158 @@
+/* int4 routed-expert MoE layer for AMD Instinct MI355X (gfx950): C ABI.
+ *
+ * One GLM-5.2-style (glm_moe_dsa) MoE layer forward, split in two calls:
+ *   moe_route : router logits, sigmoid scores, group-limited top-k selection and
+ *               renormalised weights  ->  idx[S,k], w[S,k]
+ *   moe_ffn   : the selected experts' int4 SwiGLU FFN, the weighted sum of their
+ *               outputs and the always-on shared expert  ->  y[S,H]
+ * plus host helpers (configuration checks, buffer sizes, the packer that turns
+ * interchange-format weights into the library's slot layout) and an HBM expert
+ * slot pool whose misses are filled from pinned host memory on a side stream.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [PORT]   "GLM-5.2 on a 32 GB Mac - native MLX port of the Colibri hierarchy":
+ *           N1 "GLM-5.2 graph" (router and shared expert), "G2 implementation
+ *           status" (offset-binary Q4, lower expert ID wins exact ties, un-biased
+ *           sigmoid weights, routed scale, unweighted shared expert, dequantise
+ *           then f32 multiply-accumulate), "G3 implementation status" (slot
+ *           catalog, per-layer LRU slots, batch union, resident work first).
+ *  [README] colibri README, "What's implemented" (DeepSeek-V3-style sigmoid
+ *           router, noaux_tc, routed_scaling_factor, batch-union MoE).
+ *  [MODELS] "Model support" doc, 4.3 UniversalMoE (grouped routing) and 6.4.
+ *
+ * Conventions for every call below:
+ *  - Tensor pointers are DEVICE pointers owned by the caller unless stated.
+ *    Nothing here allocates device memory except moe_pool_create.
+ *  - `stream` is a hipStream_t (NULL: the default stream).  GPU work is enqueued
+ *    on it and the call returns without synchronising.
+ *  - Return value: MOE_OK (0) or a negative moe_status.  Arguments are checked
+ *    before anything is enqueued; a failed call enqueues nothing and leaves the
+ *    outputs untouched.  MOE_EHIP reports a failed launch or copy; the HIP error
+ *    string is kept for moe_last_hip_error().
+ *  - Values that only the GPU sees (an idx entry outside [0, E), a slot-table
+ *    entry outside [0, n_slots)) cannot be checked on the host without a
+ *    synchronisation; the kernels never read out of bounds for them and write
+ *    NaN into the affected output rows instead.
+ */
+#ifndef INT4_ROUTED_EXPERT_MOE_H
+#define INT4_ROUTED_EXPERT_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,     /* configuration or shape not supported */
+  MOE_ENULL = -2,      /* a required pointer is NULL */
+  MOE_EDTYPE = -3,     /* unknown activation dtype */
+  MOE_EWORKSPACE = -4, /* workspace smaller than moe_workspace_bytes() */
+  MOE_ENOSLOT = -5,    /* slot pool: the union of experts exceeds the layer's slots */
+  MOE_ESTALE = -6,     /* slot pool: generation mismatch or bad lease state */
+  MOE_EHIP = -7,       /* a HIP call failed */
+};
+
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+
+/* Layer constants.  Limits checked by moe_validate_cfg:
+ *  hidden H, moe_inter I, shared_inter Is: multiples of 32, H and I in [32, 8192],
+ *  Is = 0 (no shared expert) or in [32, 8192]; group_size = 32;
+ *  1 <= n_experts E <= 1024, n_group G divides E, 1 <= topk_group Gk <= G <= 64,
+ *  1 <= top_k k <= min(16, Gk * E / G); norm_topk_prob 0 or 1;
+ *  routed_scaling_factor finite. */
+typedef struct moe_cfg {
+  int32_t hidden;
+  int32_t n_experts;
+  int32_t n_group;
+  int32_t topk_group;
+  int32_t top_k;
+  int32_t moe_inter;
+  int32_t shared_inter;
+  int32_t group_size;
+  float routed_scaling_factor;
+  int32_t norm_topk_prob;
+} moe_cfg;
+
+/* Where the routed experts live.  Expert e's packed weights start at
+ * base + table[e] * slot_bytes.  `table` is a DEVICE array of E int32 slot
+ * numbers (entries outside [0, n_slots) poison the rows that use them).
+ * With every expert resident in one array, table[e] = e. */
+typedef struct moe_slot_view {
+  const void *base;
+  int64_t slot_bytes; /* >= moe_expert_bytes(cfg, moe_inter), multiple of 256 */
+  const int32_t *table;
+  int32_t n_slots;
+} moe_slot_view;
+
+int moe_validate_cfg(const moe_cfg *cfg);
+const char *moe_status_string(int status);
+const char *moe_last_hip_error(void);
+
+/* Bytes of one packed expert with intermediate size `inter` in the slot layout
+ * (gate/up row tiles, then down row tiles; see the packer), rounded up to 4096.
+ * Returns a negative moe_status on a bad configuration. */
+int64_t moe_expert_bytes(const moe_cfg *cfg, int32_t inter);
+
+/* Device workspace needed by moe_route and moe_ffn for up to max_S tokens.
+ * 0 on a bad configuration. */
+size_t moe_workspace_bytes(const moe_cfg *cfg, int32_t max_S);
+
+/* Pack one expert from the interchange format into the slot layout.
+ * Interchange format of an R x K matrix (K = contraction, groups of 32 along K):
+ *   q: uint8 [R, K/2], element (r, 2j) in the low nibble of byte (r, j), (r, 2j+1)
+ *      in the high nibble; offset binary, value = nibble - 8 ([PORT] G2 status);
+ *   s: uint16 [R, K/32] fp16 bits, scale of elements (r, 32g .. 32g+31).
+ * Gate and up are [inter, H], down is [H, inter].  dst receives
+ * moe_expert_bytes(cfg, inter) bytes.  where = 0: all pointers are host memory and
+ * the packing runs on the CPU (stream ignored); where = 1: all pointers are device
+ * memory and a kernel packs on `stream`. */
+int moe_pack_expert(const moe_cfg *cfg, int32_t inter, const uint8_t *q_gate, const uint16_t *s_gate,
+                    const uint8_t *q_up, const uint16_t *s_up, const uint8_t *q_down, const uint16_t *s_down,
+                    void *dst, int32_t where, void *stream);
+
+/* Inverse of moe_pack_expert for host memory (round-trip checks). */
+int moe_unpack_expert(const moe_cfg *cfg, int32_t inter, const void *src, uint8_t *q_gate, uint16_t *s_gate,
+                      uint8_t *q_up, uint16_t *s_up, uint8_t *q_down, uint16_t *s_down);
+
+/* Router ([PORT] N1 and G2 status; [README] "What's implemented"; [MODELS] 4.3):
+ *   l[t,e] = sum_h x[t,h] W_gate[e,h]         (fp64 accumulation)
+ *   s = sigmoid(l) (fp64); key = fp32(s + bias)
+ *   group score = fp32(sum of the group's two largest keys), groups are G
+ *   contiguous blocks of E/G experts; keep the Gk best groups (ties: lower group);
+ *   top-k keys over the kept experts (ties: lower expert ID), rank order;
+ *   w = s[idx] / sum(s[idx]) * rsf (or s[idx] * rsf without renormalisation).
+ * x: [S, H] fp32 or bf16 (x_dtype); W_gate: [E, H] fp32 row-major; bias: [E] fp32.
+ * Out: idx [S, k] int32, w [S, k] fp32, both rank-ordered.  S = 0 is a no-op.
+ * ws: device workspace of at least moe_workspace_bytes(cfg, S) bytes. */
+int moe_route(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, const float *W_gate,
+              const float *bias, int32_t *idx, float *w, void *ws, size_t ws_bytes, void *stream);
+
+/* Expert FFN ([PORT] N1 and G2 status; [README] batch-union MoE):
+ *   y[t] = sum_j w[t,j] * FFN_{idx[t,j]}(x_t) + FFN_shared(x_t),
+ *   FFN(x) = Wd (silu(Wg x) * (Wu x)),  W = dequant(q, s) = (nibble - 8) * scale.
+ * Every expert named by idx is streamed once per call and applied to all the
+ * tokens that chose it.  x: [S, H] fp32 or bf16; idx/w: [S, k] as from moe_route;
+ * experts: routed slots (host struct holding device pointers); shared: the packed
+ * shared expert (moe_expert_bytes(cfg, shared_inter) bytes), ignored when
+ * shared_inter = 0.  Out: y [S, H] fp32.  Arithmetic: S <= 4 uses fp32
+ * dequantise-and-multiply-accumulate throughout; larger batches use the same for
+ * experts with few tokens and bf16 MFMA (fp32 accumulation) for the others. */
+int moe_ffn(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, const int32_t *idx, const float *w,
+            const moe_slot_view *experts, const void *shared, float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* Timing instrumentation (not part of the layer's computation).  While enabled,
+ * the library brackets each kernel it launches with two hipEvents recorded on the
+ * launch stream.  moe_profile_report waits for the recorded events, writes
+ * {"kernel": [total_ms, launches], ...} as a NUL-terminated JSON string into out
+ * (cap bytes; MOE_EINVAL if too small) and forgets the records.  Host state is
+ * process-wide and not thread-safe. */
+int moe_profile_enable(int on);
+int moe_profile_report(char *out, size_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

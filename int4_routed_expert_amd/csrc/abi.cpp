@@ -1,0 +1,288 @@
+// C ABI of the MoE-layer library: argument checks, workspace layout, host-side
+// packing and kernel dispatch.  Declarations and contracts: include/moe.h.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace moe {
+
+static thread_local std::string g_last_hip_error = "no error";
+
+static int hip_fail(hipError_t e) {
+  g_last_hip_error = hipGetErrorString(e);
+  return MOE_EHIP;
+}
+
+// ---- timing instrumentation ---------------------------------------------------
+struct ProfRec {
+  const char *name;
+  hipEvent_t a, b;
+};
+static bool g_prof = false;
+static std::vector<ProfRec> g_recs;
+static std::vector<hipEvent_t> g_pool;
+
+static hipEvent_t pool_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  (void)hipEventCreate(&e);
+  return e;
+}
+
+bool prof_on() { return g_prof; }
+
+void prof_begin(const char *name, hipStream_t st) {
+  ProfRec r{name, pool_event(), nullptr};
+  (void)hipEventRecord(r.a, st);
+  g_recs.push_back(r);
+}
+
+void prof_end(hipStream_t st) {
+  for (auto it = g_recs.rbegin(); it != g_recs.rend(); ++it)
+    if (!it->b) {
+      it->b = pool_event();
+      (void)hipEventRecord(it->b, st);
+      return;
+    }
+}
+
+static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+WsLayout ws_layout(const moe_cfg &c, int32_t S) {
+  WsLayout L{};
+  const size_t k1 = (size_t)c.top_k + 1;
+  const size_t imax = (size_t)std::max(c.moe_inter, c.shared_inter);
+  size_t off = 0;
+  L.logits = off; off += align256((size_t)S * c.n_experts * sizeof(double));
+  L.h = off; off += align256((size_t)S * k1 * imax * sizeof(float));
+  L.max_items = 0;
+  if (S > kSmallS) {
+    L.part = off; off += align256((size_t)S * k1 * c.hidden * sizeof(float));
+    L.lists = off; off += align256((size_t)c.n_experts * S * sizeof(int32_t));
+    L.counts = off; off += align256((size_t)(c.n_experts + 1) * sizeof(int32_t));
+    L.max_items = (int32_t)(((size_t)S * c.top_k + 3) / 4 + c.n_experts + (S + 3) / 4);
+    L.items = off; off += align256((size_t)L.max_items * 3 * sizeof(int32_t));
+    L.n_items = off; off += align256(2 * sizeof(int32_t));
+  }
+  L.total = std::max<size_t>(off, 256);
+  return L;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_validate_cfg(const moe_cfg *c) {
+  if (!c) return MOE_ENULL;
+  const bool ok = c->group_size == kGroup && c->hidden >= 32 && c->hidden <= 8192 && c->hidden % 32 == 0 &&
+                  c->moe_inter >= 32 && c->moe_inter <= 8192 && c->moe_inter % 32 == 0 &&
+                  (c->shared_inter == 0 || (c->shared_inter >= 32 && c->shared_inter <= 8192 && c->shared_inter % 32 == 0)) &&
+                  c->n_experts >= 1 && c->n_experts <= kMaxE && c->n_group >= 1 && c->n_group <= kMaxG &&
+                  c->n_experts % c->n_group == 0 && c->topk_group >= 1 && c->topk_group <= c->n_group &&
+                  c->top_k >= 1 && c->top_k <= kMaxK && c->top_k <= c->topk_group * (c->n_experts / c->n_group) &&
+                  (c->norm_topk_prob == 0 || c->norm_topk_prob == 1) && std::isfinite(c->routed_scaling_factor);
+  return ok ? MOE_OK : MOE_EINVAL;
+}
+
+const char *moe_status_string(int s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid configuration or shape";
+    case MOE_ENULL: return "required pointer is NULL";
+    case MOE_EDTYPE: return "unknown activation dtype";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_ENOSLOT: return "slot pool: expert union exceeds the layer's slots";
+    case MOE_ESTALE: return "slot pool: stale generation or bad lease state";
+    case MOE_EHIP: return "HIP call failed";
+    default: return "unknown status";
+  }
+}
+
+const char *moe_last_hip_error(void) { return g_last_hip_error.c_str(); }
+
+int moe_profile_enable(int on) {
+  g_prof = on != 0;
+  return MOE_OK;
+}
+
+int moe_profile_report(char *out, size_t cap) {
+  if (!out || cap == 0) return MOE_ENULL;
+  std::map<std::string, std::pair<double, long>> agg;
+  for (auto &r : g_recs) {
+    if (r.b) {
+      hipError_t e = hipEventSynchronize(r.b);
+      if (e != hipSuccess) return hip_fail(e);
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, r.a, r.b);
+      if (e != hipSuccess) return hip_fail(e);
+      auto &v = agg[r.name];
+      v.first += ms;
+      v.second += 1;
+      g_pool.push_back(r.b);
+    }
+    g_pool.push_back(r.a);
+  }
+  g_recs.clear();
+  std::string js = "{";
+  bool first = true;
+  for (auto &kv : agg) {
+    char buf[256];
+    std::snprintf(buf, sizeof buf, "%s\"%s\": [%.6f, %ld]", first ? "" : ", ", kv.first.c_str(), kv.second.first,
+                  kv.second.second);
+    js += buf;
+    first = false;
+  }
+  js += "}";
+  if (js.size() + 1 > cap) return MOE_EINVAL;
+  std::memcpy(out, js.c_str(), js.size() + 1);
+  return MOE_OK;
+}
+
+int64_t moe_expert_bytes(const moe_cfg *c, int32_t inter) {
+  const int v = moe_validate_cfg(c);
+  if (v) return v;
+  if (inter < 32 || inter > 8192 || inter % 32) return MOE_EINVAL;
+  return slot_stride(c->hidden, inter);
+}
+
+size_t moe_workspace_bytes(const moe_cfg *c, int32_t max_S) {
+  if (moe_validate_cfg(c) || max_S < 0) return 0;
+  return ws_layout(*c, max_S).total;
+}
+
+int moe_pack_expert(const moe_cfg *c, int32_t inter, const uint8_t *qg, const uint16_t *sg, const uint8_t *qu,
+                    const uint16_t *su, const uint8_t *qd, const uint16_t *sd, void *dst, int32_t where, void *stream) {
+  const int64_t nb = moe_expert_bytes(c, inter);
+  if (nb < 0) return (int)nb;
+  if (!qg || !sg || !qu || !su || !qd || !sd || !dst) return MOE_ENULL;
+  if (where != 0 && where != 1) return MOE_EINVAL;
+  const int H = c->hidden, I = inter;
+  if (where == 1) {
+    hipError_t e = launch_pack(H, I, qg, sg, qu, su, qd, sd, (uint8_t *)dst, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+  }
+  uint8_t *d = (uint8_t *)dst;
+  const int ngh = H / kGroup, ngi = I / kGroup;
+  for (int t = 0; t < I / kGuPairs; ++t) {
+    uint8_t *tile = d + (size_t)t * gu_tile_bytes(H);
+    uint16_t *scl = (uint16_t *)(tile + (size_t)kGuRows * (H / 2));
+    for (int i = 0; i < kGuRows; ++i) {
+      const int r = kGuPairs * t + i / 2;
+      const uint8_t *q = (i & 1) ? qu : qg;
+      const uint16_t *s = (i & 1) ? su : sg;
+      std::memcpy(tile + (size_t)i * (H / 2), q + (size_t)r * (H / 2), H / 2);
+      for (int g = 0; g < ngh; ++g) scl[g * kGuRows + i] = s[(size_t)r * ngh + g];
+    }
+  }
+  for (int t = 0; t < H / kDnRows; ++t) {
+    uint8_t *tile = d + down_offset(H, I) + (size_t)t * dn_tile_bytes(I);
+    uint16_t *scl = (uint16_t *)(tile + (size_t)kDnRows * (I / 2));
+    for (int i = 0; i < kDnRows; ++i) {
+      const int r = kDnRows * t + i;
+      std::memcpy(tile + (size_t)i * (I / 2), qd + (size_t)r * (I / 2), I / 2);
+      for (int g = 0; g < ngi; ++g) scl[g * kDnRows + i] = sd[(size_t)r * ngi + g];
+    }
+  }
+  const size_t used = (size_t)packed_bytes(H, I);
+  std::memset(d + used, 0, (size_t)nb - used);
+  return MOE_OK;
+}
+
+int moe_unpack_expert(const moe_cfg *c, int32_t inter, const void *src, uint8_t *qg, uint16_t *sg, uint8_t *qu,
+                      uint16_t *su, uint8_t *qd, uint16_t *sd) {
+  const int64_t nb = moe_expert_bytes(c, inter);
+  if (nb < 0) return (int)nb;
+  if (!src || !qg || !sg || !qu || !su || !qd || !sd) return MOE_ENULL;
+  const int H = c->hidden, I = inter;
+  const uint8_t *d = (const uint8_t *)src;
+  const int ngh = H / kGroup, ngi = I / kGroup;
+  for (int t = 0; t < I / kGuPairs; ++t) {
+    const uint8_t *tile = d + (size_t)t * gu_tile_bytes(H);
+    const uint16_t *scl = (const uint16_t *)(tile + (size_t)kGuRows * (H / 2));
+    for (int i = 0; i < kGuRows; ++i) {
+      const int r = kGuPairs * t + i / 2;
+      uint8_t *q = (i & 1) ? qu : qg;
+      uint16_t *s = (i & 1) ? su : sg;
+      std::memcpy(q + (size_t)r * (H / 2), tile + (size_t)i * (H / 2), H / 2);
+      for (int g = 0; g < ngh; ++g) s[(size_t)r * ngh + g] = scl[g * kGuRows + i];
+    }
+  }
+  for (int t = 0; t < H / kDnRows; ++t) {
+    const uint8_t *tile = d + down_offset(H, I) + (size_t)t * dn_tile_bytes(I);
+    const uint16_t *scl = (const uint16_t *)(tile + (size_t)kDnRows * (I / 2));
+    for (int i = 0; i < kDnRows; ++i) {
+      const int r = kDnRows * t + i;
+      std::memcpy(qd + (size_t)r * (I / 2), tile + (size_t)i * (I / 2), I / 2);
+      for (int g = 0; g < ngi; ++g) sd[(size_t)r * ngi + g] = scl[g * kDnRows + i];
+    }
+  }
+  return MOE_OK;
+}
+
+int moe_route(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const float *W, const float *bias,
+              int32_t *idx, float *w, void *ws, size_t ws_bytes, void *stream) {
+  int v = moe_validate_cfg(c);
+  if (v) return v;
+  if (S < 0) return MOE_EINVAL;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EDTYPE;
+  if (S == 0) return MOE_OK;
+  if (!x || !W || !bias || !idx || !w || !ws) return MOE_ENULL;
+  const WsLayout L = ws_layout(*c, S);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  RouteArgs a{};
+  a.H = c->hidden; a.E = c->n_experts; a.G = c->n_group; a.Gk = c->topk_group; a.k = c->top_k; a.S = S;
+  a.x_bf16 = x_dtype == MOE_BF16; a.norm = c->norm_topk_prob; a.rsf = c->routed_scaling_factor;
+  a.x = x; a.W = W; a.bias = bias; a.idx = idx; a.w = w;
+  a.logits = (double *)((char *)ws + L.logits);
+  hipError_t e = launch_route(a, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int moe_ffn(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const int32_t *idx, const float *w,
+            const moe_slot_view *ex, const void *shared, float *y, void *ws, size_t ws_bytes, void *stream) {
+  int v = moe_validate_cfg(c);
+  if (v) return v;
+  if (S < 0) return MOE_EINVAL;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EDTYPE;
+  if (S == 0) return MOE_OK;
+  if (!x || !idx || !w || !ex || !y || !ws || !ex->base || !ex->table) return MOE_ENULL;
+  if (c->shared_inter > 0 && !shared) return MOE_ENULL;
+  if (ex->n_slots < 1 || ex->slot_bytes < slot_stride(c->hidden, c->moe_inter) || ex->slot_bytes % 256) return MOE_EINVAL;
+  const WsLayout L = ws_layout(*c, S);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  FfnArgs a{};
+  a.H = c->hidden; a.E = c->n_experts; a.k = c->top_k; a.I = c->moe_inter; a.Is = c->shared_inter; a.S = S;
+  a.x_bf16 = x_dtype == MOE_BF16;
+  a.x = x; a.idx = idx; a.w = w;
+  a.base = (const uint8_t *)ex->base; a.slot_bytes = ex->slot_bytes; a.table = ex->table; a.n_slots = ex->n_slots;
+  a.shared = (const uint8_t *)shared;
+  a.y = y;
+  char *b = (char *)ws;
+  a.h = (float *)(b + L.h);
+  hipError_t e;
+  if (S <= kSmallS) {
+    e = launch_ffn_small(a, (hipStream_t)stream);
+  } else {
+    a.part = (float *)(b + L.part);
+    a.lists = (int32_t *)(b + L.lists);
+    a.counts = (int32_t *)(b + L.counts);
+    a.items = (int32_t *)(b + L.items);
+    a.n_items = (int32_t *)(b + L.n_items);
+    a.max_items = L.max_items;
+    e = launch_ffn_large(a, (hipStream_t)stream);
+  }
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Internal definitions shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kGroup = 32;       // int4 elements per fp16 scale (along the contraction)
+constexpr int kGuRows = 8;       // rows per gate/up tile: gate r, up r for 4 consecutive r
+constexpr int kGuPairs = 4;      // feature rows per gate/up tile
+constexpr int kDnRows = 8;       // rows per down tile
+constexpr int kSmallS = 4;       // batches up to this size take the decode path
+constexpr int kMaxK = 16;        // top_k limit
+constexpr int kMaxE = 1024;      // n_experts limit
+constexpr int kMaxG = 64;        // n_group limit
+
+// ---- slot layout of one packed expert (inter = I, hidden = H) -------------
+// gate/up: I/4 tiles.  Tile t holds 8 rows, in order (g 4t, u 4t, g 4t+1, u 4t+1,
+// ..., g 4t+3, u 4t+3), each row H/2 bytes of nibbles in interchange order, then
+// the tile's scales as [H/32 groups][8 rows] fp16.
+// down: H/8 tiles.  Tile t holds rows 8t..8t+7 (I/2 bytes each), then scales
+// [I/32 groups][8 rows] fp16.
+__host__ __device__ inline int64_t gu_tile_bytes(int H) { return (int64_t)kGuRows * (H / 2) + (int64_t)(H / kGroup) * kGuRows * 2; }
+__host__ __device__ inline int64_t dn_tile_bytes(int I) { return (int64_t)kDnRows * (I / 2) + (int64_t)(I / kGroup) * kDnRows * 2; }
+__host__ __device__ inline int64_t down_offset(int H, int I) { return (int64_t)(I / kGuPairs) * gu_tile_bytes(H); }
+__host__ __device__ inline int64_t packed_bytes(int H, int I) { return down_offset(H, I) + (int64_t)(H / kDnRows) * dn_tile_bytes(I); }
+inline int64_t slot_stride(int H, int I) { return (packed_bytes(H, I) + 4095) / 4096 * 4096; }
+
+// ---- kernel arguments -------------------------------------------------------
+struct RouteArgs {
+  int H, E, G, Gk, k, S, x_bf16, norm;
+  float rsf;
+  const void *x;
+  const float *W;
+  const float *bias;
+  double *logits;  // [S, E]
+  int32_t *idx;
+  float *w;
+};
+
+struct FfnArgs {
+  int H, E, k, I, Is, S, x_bf16;
+  const void *x;
+  const int32_t *idx;
+  const float *w;
+  const uint8_t *base;
+  int64_t slot_bytes;
+  const int32_t *table;
+  int32_t n_slots;
+  const uint8_t *shared;
+  float *y;
+  // workspace views
+  float *h;        // [S * (k+1), max(I, Is)] fp32 hidden activations
+  float *part;     // [S, k+1, H] fp32 per-(token, rank) expert outputs (large-batch path)
+  int32_t *lists;  // [E+1, S] token lists per expert (large-batch path), entry = token*(k+1)+rank
+  int32_t *counts; // [E+1]
+  int32_t *items;  // work items (large-batch path)
+  int32_t *n_items;
+  int32_t max_items;
+};
+
+// ---- timing instrumentation (host) --------------------------------------------
+// When enabled (moe_profile_enable), launchers bracket each kernel with a pair of
+// hipEvents on its stream; moe_profile_report sums the elapsed times per kernel.
+bool prof_on();
+void prof_begin(const char *name, hipStream_t st);
+void prof_end(hipStream_t st);
+struct ProfScope {
+  hipStream_t st;
+  ProfScope(const char *name, hipStream_t s) : st(s) { if (prof_on()) prof_begin(name, st); }
+  ~ProfScope() { if (prof_on()) prof_end(st); }
+};
+
+// ---- launchers (host) --------------------------------------------------------
+hipError_t launch_route(const RouteArgs &a, hipStream_t st);
+hipError_t launch_ffn_small(const FfnArgs &a, hipStream_t st);
+hipError_t launch_ffn_large(const FfnArgs &a, hipStream_t st);
+hipError_t launch_pack(int H, int I, const uint8_t *qg, const uint16_t *sg, const uint8_t *qu, const uint16_t *su,
+                       const uint8_t *qd, const uint16_t *sd, uint8_t *dst, hipStream_t st);
+
+// workspace layout (bytes, each region 256-aligned)
+struct WsLayout {
+  size_t logits, h, part, lists, counts, items, n_items, total;
+  int32_t max_items;
+};
+WsLayout ws_layout(const moe_cfg &c, int32_t S);
+
+}  // namespace moe

@@ -1,0 +1,48 @@
+// Device-side packer: interchange format -> slot layout (see common.h).
+// One thread per (tile, 32-element group): 8 rows x 16 bytes of nibbles and the
+// 8 fp16 scales of that group.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void k_pack(int H, int I, const uint8_t *qg, const uint16_t *sg, const uint8_t *qu,
+                                              const uint16_t *su, const uint8_t *qd, const uint16_t *sd, uint8_t *dst) {
+  const long id = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long ngh = H / kGroup, ngi = I / kGroup;
+  const long n_gu = (long)(I / kGuPairs) * ngh;
+  const long n_dn = (long)(H / kDnRows) * ngi;
+  if (id < n_gu) {
+    const int t = (int)(id / ngh), g = (int)(id - (long)t * ngh);
+    uint8_t *tile = dst + (size_t)t * gu_tile_bytes(H);
+    uint16_t *scl = (uint16_t *)(tile + (size_t)kGuRows * (H / 2));
+    for (int i = 0; i < kGuRows; ++i) {
+      const int r = kGuPairs * t + i / 2;
+      const uint8_t *q = (i & 1) ? qu : qg;
+      const uint16_t *s = (i & 1) ? su : sg;
+      *(uint4 *)(tile + (size_t)i * (H / 2) + g * 16) = *(const uint4 *)(q + (size_t)r * (H / 2) + g * 16);
+      scl[g * kGuRows + i] = s[(size_t)r * ngh + g];
+    }
+  } else if (id < n_gu + n_dn) {
+    const long j = id - n_gu;
+    const int t = (int)(j / ngi), g = (int)(j - (long)t * ngi);
+    uint8_t *tile = dst + down_offset(H, I) + (size_t)t * dn_tile_bytes(I);
+    uint16_t *scl = (uint16_t *)(tile + (size_t)kDnRows * (I / 2));
+    for (int i = 0; i < kDnRows; ++i) {
+      const int r = kDnRows * t + i;
+      *(uint4 *)(tile + (size_t)i * (I / 2) + g * 16) = *(const uint4 *)(qd + (size_t)r * (I / 2) + g * 16);
+      scl[g * kDnRows + i] = sd[(size_t)r * ngi + g];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack(int H, int I, const uint8_t *qg, const uint16_t *sg, const uint8_t *qu, const uint16_t *su,
+                       const uint8_t *qd, const uint16_t *sd, uint8_t *dst, hipStream_t st) {
+  const long n = (long)(I / kGuPairs) * (H / kGroup) + (long)(H / kDnRows) * (I / kGroup);
+  hipLaunchKernelGGL(k_pack, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, H, I, qg, sg, qu, su, qd, sd, dst);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,157 @@
+"""Python binding of ``libmoe.so`` (include/moe.h): argument marshalling only.
+
+Every function with a ``moe_`` name calls the C entry point of the same name.
+Tensors are passed as raw pointers (``torch.Tensor.data_ptr()`` for device
+memory, numpy arrays for host memory); streams as ``torch.cuda.Stream`` handles.
+The library does all the work; if it is missing this module raises on import.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
+
+MOE_OK, MOE_EINVAL, MOE_ENULL, MOE_EDTYPE, MOE_EWORKSPACE, MOE_ENOSLOT, MOE_ESTALE, MOE_EHIP = 0, -1, -2, -3, -4, -5, -6, -7
+MOE_F32, MOE_BF16 = 0, 1
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.moe_status_string(status).decode()
+        if status == MOE_EHIP:
+            msg += ": " + _lib.moe_last_hip_error().decode()
+        super().__init__(f"{where}: {msg} ({status})")
+
+
+class moe_cfg(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("n_group", ctypes.c_int32),
+                ("topk_group", ctypes.c_int32), ("top_k", ctypes.c_int32), ("moe_inter", ctypes.c_int32),
+                ("shared_inter", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("routed_scaling_factor", ctypes.c_float), ("norm_topk_prob", ctypes.c_int32)]
+
+
+class moe_slot_view(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("slot_bytes", ctypes.c_int64), ("table", ctypes.c_void_p),
+                ("n_slots", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() (hipcc for gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    cp = ctypes.POINTER(moe_cfg)
+    sigs = {
+        "moe_validate_cfg": (ctypes.c_int, [cp]),
+        "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "moe_last_hip_error": (ctypes.c_char_p, []),
+        "moe_expert_bytes": (i64, [cp, i32]),
+        "moe_workspace_bytes": (sz, [cp, i32]),
+        "moe_pack_expert": (ctypes.c_int, [cp, i32, p, p, p, p, p, p, p, i32, p]),
+        "moe_unpack_expert": (ctypes.c_int, [cp, i32, p, p, p, p, p, p, p]),
+        "moe_route": (ctypes.c_int, [cp, p, i32, i32, p, p, p, p, p, sz, p]),
+        "moe_ffn": (ctypes.c_int, [cp, p, i32, i32, p, p, ctypes.POINTER(moe_slot_view), p, p, p, sz, p]),
+        "moe_profile_enable": (ctypes.c_int, [ctypes.c_int]),
+        "moe_profile_report": (ctypes.c_int, [ctypes.c_char_p, sz]),
+    }
+    for name, (res, args) in sigs.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+_lib = _load()
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/moe.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def make_cfg(c) -> moe_cfg:
+    """moe_cfg from any object with the LayerConfig field names."""
+    return moe_cfg(c.hidden, c.n_experts, c.n_group, c.topk_group, c.top_k, c.moe_inter, c.shared_inter,
+                   c.group_size, c.routed_scaling_factor, c.norm_topk_prob)
+
+
+def ptr(t) -> int | None:
+    """Raw address of a torch tensor or numpy array (None passes NULL)."""
+    if t is None:
+        return None
+    if hasattr(t, "data_ptr"):
+        return t.data_ptr()
+    return t.ctypes.data
+
+
+def stream_handle(stream=None) -> int | None:
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != MOE_OK:
+        raise MoeError(rc, where)
+
+
+def moe_validate_cfg(cfg: moe_cfg) -> int:
+    return _lib.moe_validate_cfg(ctypes.byref(cfg))
+
+
+def moe_expert_bytes(cfg: moe_cfg, inter: int) -> int:
+    return _lib.moe_expert_bytes(ctypes.byref(cfg), inter)
+
+
+def moe_workspace_bytes(cfg: moe_cfg, max_S: int) -> int:
+    return _lib.moe_workspace_bytes(ctypes.byref(cfg), max_S)
+
+
+def moe_pack_expert(cfg: moe_cfg, inter: int, qg, sg, qu, su, qd, sd, dst, where: int, stream=None) -> None:
+    st = stream_handle(stream) if where == 1 else None
+    _check(_lib.moe_pack_expert(ctypes.byref(cfg), inter, ptr(qg), ptr(sg), ptr(qu), ptr(su), ptr(qd), ptr(sd),
+                                ptr(dst), where, st), "moe_pack_expert")
+
+
+def moe_unpack_expert(cfg: moe_cfg, inter: int, src, qg, sg, qu, su, qd, sd) -> None:
+    _check(_lib.moe_unpack_expert(ctypes.byref(cfg), inter, ptr(src), ptr(qg), ptr(sg), ptr(qu), ptr(su), ptr(qd),
+                                  ptr(sd)), "moe_unpack_expert")
+
+
+def moe_route(cfg: moe_cfg, x, x_dtype: int, S: int, W, bias, idx, w, ws, ws_bytes: int, stream=None) -> None:
+    _check(_lib.moe_route(ctypes.byref(cfg), ptr(x), x_dtype, S, ptr(W), ptr(bias), ptr(idx), ptr(w), ptr(ws),
+                          ws_bytes, stream_handle(stream)), "moe_route")
+
+
+def moe_ffn(cfg: moe_cfg, x, x_dtype: int, S: int, idx, w, view: moe_slot_view, shared, y, ws, ws_bytes: int,
+            stream=None) -> None:
+    _check(_lib.moe_ffn(ctypes.byref(cfg), ptr(x), x_dtype, S, ptr(idx), ptr(w), ctypes.byref(view), ptr(shared),
+                        ptr(y), ptr(ws), ws_bytes, stream_handle(stream)), "moe_ffn")
+
+
+def moe_profile_enable(on: bool) -> None:
+    _check(_lib.moe_profile_enable(int(on)), "moe_profile_enable")
+
+
+def moe_profile_report() -> dict:
+    """{kernel: (total_ms, launches)} since the last report."""
+    import json
+    buf = ctypes.create_string_buffer(1 << 16)
+    _check(_lib.moe_profile_report(buf, len(buf)), "moe_profile_report")
+    return {k: (v[0], v[1]) for k, v in json.loads(buf.value.decode()).items()}
+
+
+def slot_view(base, slot_bytes: int, table, n_slots: int) -> moe_slot_view:
+    return moe_slot_view(ptr(base), slot_bytes, ptr(table), n_slots)

@@ -1,0 +1,160 @@
+"""C ABI checks that need no GPU: the library loads and exports every declared
+symbol, configurations are validated, sizes are as documented, the host packer
+round-trips and lays bytes out as documented, and argument errors return the
+documented codes before anything is enqueued."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from gen import inputs as gen
+from int4_routed_expert_amd import moe as M
+
+
+def test_exports_every_declared_symbol():
+    names = M.header_functions()
+    assert {"moe_route", "moe_ffn", "moe_pack_expert", "moe_workspace_bytes", "moe_expert_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(M.lib(), n), n
+        assert callable(getattr(M, n, None) or getattr(M.lib(), n))
+
+
+def test_validate_cfg():
+    assert M.moe_validate_cfg(M.make_cfg(gen.GLM52)) == M.MOE_OK
+    assert M.moe_validate_cfg(M.make_cfg(gen.TINY)) == M.MOE_OK
+    bad = [
+        dict(hidden=100), dict(hidden=0), dict(hidden=8224), dict(moe_inter=48), dict(shared_inter=16),
+        dict(n_group=3), dict(topk_group=9), dict(topk_group=0), dict(top_k=0), dict(top_k=17),
+        dict(n_experts=2048, n_group=8), dict(group_size=64), dict(norm_topk_prob=2),
+        dict(n_experts=16, n_group=4, topk_group=1, top_k=5),
+    ]
+    for b in bad:
+        c = gen.LayerConfig(**{**gen.GLM52.__dict__, **b})
+        assert M.moe_validate_cfg(M.make_cfg(c)) == M.MOE_EINVAL, b
+    c = M.make_cfg(gen.GLM52)
+    c.routed_scaling_factor = float("nan")
+    assert M.moe_validate_cfg(c) == M.MOE_EINVAL
+    assert M.lib().moe_validate_cfg(None) == M.MOE_ENULL
+    ok_no_shared = gen.LayerConfig(**{**gen.GLM52.__dict__, "shared_inter": 0})
+    assert M.moe_validate_cfg(M.make_cfg(ok_no_shared)) == M.MOE_OK
+
+
+def test_expert_bytes_glm_shape():
+    # 3 * 6144 * 2048 nibbles (18,874,368 B) + fp16 scale per 32 (2,359,296 B)
+    c = M.make_cfg(gen.GLM52)
+    assert M.moe_expert_bytes(c, 2048) == 21_233_664
+    assert M.moe_expert_bytes(c, 48) == M.MOE_EINVAL
+    t = M.make_cfg(gen.TINY)
+    payload = 3 * 256 * 128 // 2 + 3 * 256 * 128 // 32 * 2
+    assert M.moe_expert_bytes(t, 128) == (payload + 4095) // 4096 * 4096
+
+
+def test_workspace_sizes():
+    c = M.make_cfg(gen.GLM52)
+    sizes = [M.moe_workspace_bytes(c, s) for s in (0, 1, 4, 5, 64, 2048)]
+    assert all(s >= 256 and s % 256 == 0 for s in sizes)
+    assert sizes == sorted(sizes)
+    bad = M.make_cfg(gen.GLM52)
+    bad.hidden = 100
+    assert M.moe_workspace_bytes(bad, 4) == 0
+
+
+def _expert_host(shape_cfg, inter, seed=0):
+    w = gen.Workload("t", shape_cfg, tokens=1, seed=seed)
+    e = shape_cfg.n_experts if inter == shape_cfg.shared_inter and inter != shape_cfg.moe_inter else 1
+    return gen.expert_weights(w, 0, e)
+
+
+@pytest.mark.parametrize("shape", [gen.TINY, gen.LayerConfig(hidden=96, n_experts=4, n_group=2, topk_group=1,
+                                                                 top_k=2, moe_inter=64, shared_inter=32)])
+def test_host_pack_round_trip_and_layout(shape):
+    c = M.make_cfg(shape)
+    ex = _expert_host(shape, shape.moe_inter)
+    nb = M.moe_expert_bytes(c, shape.moe_inter)
+    dst = np.full(nb, 0xAB, np.uint8)
+    M.moe_pack_expert(c, shape.moe_inter, *ex.parts(), dst, 0)
+    out = gen.empty_expert(shape, shape.moe_inter)
+    M.moe_unpack_expert(c, shape.moe_inter, dst, *out.parts())
+    for a, b in zip(ex.parts(), out.parts()):
+        assert np.array_equal(a, b)
+    # documented layout, re-derived: gate/up tiles of 8 rows (g r, u r for 4 r), then scales [group][8]
+    H, I = shape.hidden, shape.moe_inter
+    tile = 8 * (H // 2) + (H // 32) * 8 * 2
+    for t in range(I // 4):
+        base = t * tile
+        for i in range(8):
+            src = ex.qu if i % 2 else ex.qg
+            r = 4 * t + i // 2
+            assert np.array_equal(dst[base + i * (H // 2): base + (i + 1) * (H // 2)], src[r])
+        scl = dst[base + 8 * (H // 2): base + tile].view(np.uint16).reshape(H // 32, 8)
+        for i in range(8):
+            s = ex.su if i % 2 else ex.sg
+            assert np.array_equal(scl[:, i], s[4 * t + i // 2])
+    dtile = 8 * (I // 2) + (I // 32) * 8 * 2
+    d0 = (I // 4) * tile
+    for t in range(H // 8):
+        base = d0 + t * dtile
+        for i in range(8):
+            assert np.array_equal(dst[base + i * (I // 2): base + (i + 1) * (I // 2)], ex.qd[8 * t + i])
+        scl = dst[base + 8 * (I // 2): base + dtile].view(np.uint16).reshape(I // 32, 8)
+        assert np.array_equal(scl.T, ex.sd[8 * t: 8 * t + 8])
+    assert np.all(dst[d0 + (H // 8) * dtile:] == 0)
+
+
+def test_pack_argument_errors():
+    c = M.make_cfg(gen.TINY)
+    ex = _expert_host(gen.TINY, 128)
+    dst = np.zeros(M.moe_expert_bytes(c, 128), np.uint8)
+    L = M.lib()
+    p = [M.ptr(a) for a in ex.parts()]
+    assert L.moe_pack_expert(ctypes.byref(c), 128, *p, None, 0, None) == M.MOE_ENULL
+    assert L.moe_pack_expert(ctypes.byref(c), 128, None, *p[1:], M.ptr(dst), 0, None) == M.MOE_ENULL
+    assert L.moe_pack_expert(ctypes.byref(c), 100, *p, M.ptr(dst), 0, None) == M.MOE_EINVAL
+    assert L.moe_pack_expert(ctypes.byref(c), 128, *p, M.ptr(dst), 2, None) == M.MOE_EINVAL
+
+
+def test_route_and_ffn_argument_errors_before_any_launch():
+    """These return before touching the GPU, so they run without one."""
+    c = M.make_cfg(gen.TINY)
+    L = M.lib()
+    fake = ctypes.c_void_p(4096)  # never dereferenced: every call below fails validation first
+    ws_need = M.moe_workspace_bytes(c, 4)
+    R = lambda **kw: L.moe_route(ctypes.byref(kw.get("cfg", c)), kw.get("x", fake), kw.get("dt", M.MOE_F32),
+                                 kw.get("S", 4), kw.get("W", fake), kw.get("b", fake), kw.get("idx", fake),
+                                 kw.get("w", fake), kw.get("ws", fake), kw.get("wsb", ws_need), None)
+    assert R(x=None) == M.MOE_ENULL
+    assert R(W=None) == M.MOE_ENULL
+    assert R(dt=7) == M.MOE_EDTYPE
+    assert R(wsb=ws_need - 1) == M.MOE_EWORKSPACE
+    assert R(S=-1) == M.MOE_EINVAL
+    assert R(S=0, x=None) == M.MOE_OK  # empty batch: a no-op
+    bad = M.make_cfg(gen.TINY)
+    bad.n_group = 3
+    assert R(cfg=bad) == M.MOE_EINVAL
+
+    sb = M.moe_expert_bytes(c, 128)
+    view = M.moe_slot_view(4096, sb, 4096, 16)
+    F = lambda **kw: L.moe_ffn(ctypes.byref(kw.get("cfg", c)), kw.get("x", fake), kw.get("dt", M.MOE_F32),
+                               kw.get("S", 4), kw.get("idx", fake), kw.get("w", fake),
+                               ctypes.byref(kw.get("view", view)), kw.get("shared", fake), kw.get("y", fake),
+                               kw.get("ws", fake), kw.get("wsb", ws_need), None)
+    assert F(shared=None) == M.MOE_ENULL
+    assert F(y=None) == M.MOE_ENULL
+    assert F(dt=-1) == M.MOE_EDTYPE
+    assert F(wsb=10) == M.MOE_EWORKSPACE
+    assert F(view=M.moe_slot_view(4096, sb - 256, 4096, 16)) == M.MOE_EINVAL
+    assert F(view=M.moe_slot_view(4096, sb + 1, 4096, 16)) == M.MOE_EINVAL
+    assert F(view=M.moe_slot_view(4096, sb, 4096, 0)) == M.MOE_EINVAL
+    assert F(view=M.moe_slot_view(None, sb, 4096, 16)) == M.MOE_ENULL
+    assert F(S=0, x=None) == M.MOE_OK
+    noshared = M.make_cfg(gen.TINY)
+    noshared.shared_inter = 0
+    # without a shared expert a NULL shared pointer is fine; validation then passes and the call
+    # would launch, so only check that the NULL-shared rule is not applied (use a bad workspace)
+    assert F(cfg=noshared, shared=None, wsb=10) == M.MOE_EWORKSPACE
+
+
+def test_status_strings():
+    for s in range(0, -8, -1):
+        assert M.lib().moe_status_string(s)
+    assert M.lib().moe_status_string(-99) == b"unknown status"

@@ -1,0 +1,244 @@
+"""HIP path vs the fp64 CPU oracle, through the C ABI, on seeded synthetic inputs.
+
+Bars (from the layer's contract): router indices identical (rank order), weights
+within 1e-6 * rsf, outputs within max relative error 2e-3 where every expert is
+contracted in fp32 (decode batches and the large-batch fp32 path) and 1e-2 where
+bf16 MFMA is used (prefill).  Per token: max_i |y - y_ref| / max_i |y_ref|.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gen import inputs as gen
+from int4_routed_expert_amd import moe as M
+from oracle import oracle as O
+from tests.devlayer import DeviceLayer, dev, max_rel_err, x_device
+
+pytestmark = pytest.mark.gpu
+
+TOL_FP32 = 2e-3
+TOL_BF16 = 1e-2
+
+MID = gen.LayerConfig(hidden=512, n_experts=32, n_group=4, topk_group=2, top_k=4, moe_inter=256, shared_inter=192)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_gpu(dl: DeviceLayer, x_host: np.ndarray, table=None):
+    x, dt = x_device(dl.w, x_host)
+    idx, wt = dl.route(x, dt)
+    y = dl.ffn(x, dt, idx, wt, table=table)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), wt.cpu().numpy(), y.cpu().numpy()
+
+
+def check_route(dl: DeviceLayer, x_host, idx, wt):
+    c = dl.c
+    ridx, rw, _, flags, margins = O.route(c, x_host, dl.W_host, dl.bias_host, x_is_bf16=dl.w.x_dtype == "bf16")
+    ok = flags == 0
+    assert ok.sum() == len(ok), f"{(~ok).sum()} tokens sit on an fp32 rounding boundary"
+    mism = np.where((idx != ridx).any(axis=1))[0]
+    assert len(mism) == 0, f"idx mismatch on tokens {mism[:10]}: gpu {idx[mism[:3]]} oracle {ridx[mism[:3]]}"
+    assert np.abs(wt - rw).max() <= 1e-6 * c.routed_scaling_factor
+    return ridx, rw
+
+
+def check_ffn(dl: DeviceLayer, x_host, ridx, rw, y, tokens, tol):
+    c = dl.c
+    xs = x_host[tokens]
+    need = set(ridx[tokens].ravel().tolist())
+    experts = {e: dl.host_expert(e) for e in need}
+    if c.shared_inter > 0:
+        experts[c.n_experts] = dl.host[c.n_experts]
+    ref = O.moe_ffn(c, np.ascontiguousarray(xs), ridx[tokens], rw[tokens], experts, x_is_bf16=dl.w.x_dtype == "bf16")
+    err = max_rel_err(y[tokens], ref)
+    say(f"  max rel err over {len(tokens)} tokens: {err:.3e}")
+    assert err <= tol
+    return err
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return DeviceLayer(gen.WORKLOADS["tiny"], host_experts=True)
+
+
+@pytest.fixture(scope="module")
+def mid():
+    return DeviceLayer(gen.Workload("mid", MID, tokens=67, seed=11), host_experts=True)
+
+
+@pytest.fixture(scope="module")
+def glm():
+    say("packing 256 + 1 GLM-5.2-shaped experts into HBM")
+    return DeviceLayer(gen.WORKLOADS["decode"])
+
+
+def test_device_pack_equals_host_pack(tiny):
+    c = tiny.cfg
+    for e in (0, 5, 15):
+        ex = tiny.host_expert(e)
+        host = np.zeros(tiny.slot_bytes, np.uint8)
+        M.moe_pack_expert(c, 128, *ex.parts(), host, 0)
+        devb = tiny.slab[e * tiny.slot_bytes:(e + 1) * tiny.slot_bytes].cpu().numpy()
+        assert np.array_equal(host, devb)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 5, 9, 37])
+def test_tiny_layer(tiny, S):
+    w = tiny.w.with_(tokens=S)
+    x = gen.tokens(w, step=S)
+    idx, wt, y = run_gpu(tiny, x)
+    ridx, rw = check_route(tiny, x, idx, wt)
+    check_ffn(tiny, x, ridx, rw, y, np.arange(S), TOL_FP32)
+
+
+@pytest.mark.parametrize("S", [1, 4, 67])
+def test_mid_layer(mid, S):
+    x = gen.tokens(mid.w.with_(tokens=S), step=100 + S)
+    idx, wt, y = run_gpu(mid, x)
+    ridx, rw = check_route(mid, x, idx, wt)
+    check_ffn(mid, x, ridx, rw, y, np.arange(S), TOL_FP32)
+
+
+def test_decode_full_size(glm):
+    """GLM-5.2 shape, one token per call (the decode launch configuration)."""
+    w = glm.w
+    errs = []
+    for step in range(6):
+        x = gen.tokens(w, step=step)
+        idx, wt, y = run_gpu(glm, x)
+        ridx, rw = check_route(glm, x, idx, wt)
+        say(f"step {step}: experts {ridx[0].tolist()}")
+        errs.append(check_ffn(glm, x, ridx, rw, y, np.arange(1), TOL_FP32))
+    say("decode worst", max(errs))
+
+
+def test_decode_bf16_input(glm):
+    w = glm.w.with_(x_dtype="bf16")
+    x = gen.tokens(w, step=3)
+    xt = dev(x.view(np.int16)).view(torch.bfloat16)
+    idx, wt = glm.route(xt, M.MOE_BF16)
+    y = glm.ffn(xt, M.MOE_BF16, idx, wt)
+    torch.cuda.synchronize()
+    dl = glm
+    ridx, rw, _, flags, _ = O.route(dl.c, x, dl.W_host, dl.bias_host, x_is_bf16=True)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    experts = {e: dl.host_expert(e) for e in ridx.ravel().tolist()}
+    experts[dl.c.n_experts] = dl.host[dl.c.n_experts]
+    ref = O.moe_ffn(dl.c, x, ridx, rw, experts, x_is_bf16=True)
+    assert max_rel_err(y.cpu().numpy(), ref) <= TOL_FP32
+
+
+def test_verify_batch_full_size():
+    """S = 4 verify batch with the skewed bias: the union is streamed once."""
+    w = gen.WORKLOADS["verify"]
+    dl = DeviceLayer(w)
+    for step in range(2):
+        x = gen.tokens(w, step=step)
+        idx, wt, y = run_gpu(dl, x)
+        ridx, rw = check_route(dl, x, idx, wt)
+        U = len(set(ridx.ravel().tolist()))
+        say(f"verify step {step}: union {U}")
+        check_ffn(dl, x, ridx, rw, y, np.arange(4), TOL_FP32)
+
+
+def test_row_stability_decode_family(tiny, glm):
+    """A token's output in a 4-token batch is bitwise equal to its 1-token result."""
+    for dl in (tiny, glm):
+        x4 = gen.tokens(dl.w.with_(tokens=4), step=77)
+        _, _, y4 = run_gpu(dl, x4)
+        for t in range(4):
+            _, _, y1 = run_gpu(dl, x4[t:t + 1])
+            assert np.array_equal(y1[0], y4[t])
+
+
+def test_zero_input(tiny, glm):
+    for dl in (tiny, glm):
+        c = dl.c
+        for S in (1, 6):
+            x = np.zeros((S, c.hidden), np.float32)
+            idx, wt, y = run_gpu(dl, x)
+            assert np.all(wt == np.float32(c.routed_scaling_factor / c.top_k))
+            ridx, _ = check_route(dl, x, idx, wt)
+            assert np.all(y == 0.0)
+
+
+def test_empty_batch(tiny):
+    x = torch.zeros((0, tiny.c.hidden), device="cuda")
+    idx = torch.full((1, 2), 7, dtype=torch.int32, device="cuda")
+    wt = torch.zeros((1, 2), device="cuda")
+    ws = tiny.workspace(1)
+    M.moe_route(tiny.cfg, x, M.MOE_F32, 0, tiny.W, tiny.bias, idx, wt, ws, ws.numel())
+    y = torch.full((1, tiny.c.hidden), 3.0, device="cuda")
+    M.moe_ffn(tiny.cfg, x, M.MOE_F32, 0, idx, wt, tiny.view(), tiny.shared, y, ws, ws.numel())
+    torch.cuda.synchronize()
+    assert torch.all(idx == 7) and torch.all(y == 3.0)
+
+
+@pytest.mark.parametrize("S", [1, 3, 8])
+def test_unresident_slot_poisons_only_its_tokens(tiny, S):
+    x = gen.tokens(tiny.w.with_(tokens=S), step=500 + S)
+    idx, wt, y_ok = run_gpu(tiny, x)
+    victim = int(idx[0, 0])
+    table = tiny.table.clone()
+    table[victim] = -1
+    xt = dev(x)
+    y = tiny.ffn(xt, M.MOE_F32, dev(idx), dev(wt), table=table).cpu().numpy()
+    uses = (idx == victim).any(axis=1)
+    assert np.all(np.isnan(y[uses]).all(axis=1))
+    assert np.array_equal(y[~uses], y_ok[~uses])
+    table[victim] = 10 ** 6
+    y = tiny.ffn(xt, M.MOE_F32, dev(idx), dev(wt), table=table).cpu().numpy()
+    assert np.all(np.isnan(y[uses]).all(axis=1))
+
+
+@pytest.mark.parametrize("S", [2, 6])
+@pytest.mark.parametrize("mode", ["out_of_range", "negative", "repeated"])
+def test_invalid_idx_poisons_only_its_token(tiny, S, mode):
+    x = gen.tokens(tiny.w.with_(tokens=S), step=900 + S)
+    idx, wt, y_ok = run_gpu(tiny, x)
+    bad = idx.copy()
+    bad[1, 1] = {"out_of_range": 12345, "negative": -3, "repeated": bad[1, 0]}[mode]
+    y = tiny.ffn(dev(x), M.MOE_F32, dev(bad), dev(wt)).cpu().numpy()
+    assert np.all(np.isnan(y[1]))
+    keep = np.ones(S, bool)
+    keep[1] = False
+    # each token's arithmetic does not depend on the others: the rest is bitwise unchanged
+    assert np.array_equal(y[keep], y_ok[keep])
+
+
+def test_largest_shapes():
+    """H = I = Is = 8192 (the largest supported), small and large-batch paths."""
+    cfg = gen.LayerConfig(hidden=8192, n_experts=8, n_group=2, topk_group=1, top_k=2, moe_inter=8192,
+                          shared_inter=8192)
+    w = gen.Workload("max", cfg, tokens=5, seed=21)
+    dl = DeviceLayer(w)
+    for S in (1, 5):
+        x = gen.tokens(w.with_(tokens=S), step=S)
+        idx, wt, y = run_gpu(dl, x)
+        ridx, rw = check_route(dl, x, idx, wt)
+        check_ffn(dl, x, ridx, rw, y, np.arange(min(S, 2)), TOL_FP32)
+
+
+def test_prefill_full_size():
+    """2048 tokens, bf16 activations, Zipf-skewed routing: every token's indices
+    and weights are checked, outputs on a sample of tokens (the oracle runs one
+    token at a time)."""
+    w = gen.WORKLOADS["prefill"]
+    dl = DeviceLayer(w)
+    x = gen.tokens(w)
+    say("prefill: running GPU path")
+    idx, wt, y = run_gpu(dl, x)
+    ridx, rw = check_route(dl, x, idx, wt)
+    counts = np.bincount(ridx.ravel(), minlength=w.cfg.n_experts)
+    say(f"prefill: max tokens per expert {counts.max()}, experts with >= 16 tokens {(counts >= 16).sum()}")
+    rng = np.random.default_rng(0)
+    hot = int(np.argmax(counts))
+    tokens = sorted(set(rng.choice(2048, 6, replace=False).tolist())
+                    | {int(np.where((ridx == hot).any(axis=1))[0][0]), 2047})
+    check_ffn(dl, x, ridx, rw, y, np.array(tokens), TOL_BF16)
+    assert np.isfinite(y).all()
