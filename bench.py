@@ -150,7 +150,7 @@ def main() -> int:
     kernels = {name: {"avg_us": ms * 1e3 / n, "launches": n} for name, (ms, n) in prof.items()}
     log("per-kernel (hipEvent) averages:", json.dumps(kernels))
     gu_bytes = 9 * 2 * (I * H // 2 + I * (H // 32) * 2)  # gate+up payload and scales of 9 experts
-    gu_us = kernels["gateup_small"]["avg_us"]
+    gu_us = kernels["gateup_s1"]["avg_us"]
     achieved = gu_bytes / (gu_us * 1e-6) / 1e9
 
     traffic = None
@@ -209,7 +209,7 @@ def main() -> int:
         "router_bytes_per_token": router_bytes,
         "eager_us_per_step": eager_us,
         "kernels_us": {n: round(v["avg_us"], 3) for n, v in kernels.items()},
-        "roofline": {"kernel": "gateup_small", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+        "roofline": {"kernel": "gateup_s1", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": gu_bytes},
         "cpu_baseline": cpu,

@@ -55,15 +55,38 @@ void prof_end(hipStream_t st) {
     }
 }
 
+// Compute units of the current device (cached per device id).
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+// offset-binary nibbles (interchange) <-> two's complement nibbles (slot layout)
+static void copy_flip(uint8_t *dst, const uint8_t *src, size_t n) {
+  for (size_t i = 0; i < n; ++i) dst[i] = src[i] ^ 0x88u;
+}
 
 WsLayout ws_layout(const moe_cfg &c, int32_t S) {
   WsLayout L{};
   const size_t k1 = (size_t)c.top_k + 1;
   const size_t imax = (size_t)std::max(c.moe_inter, c.shared_inter);
+  const size_t gh = (size_t)c.hidden / kGroup, gi = imax / kGroup;
   size_t off = 0;
   L.logits = off; off += align256((size_t)S * c.n_experts * sizeof(double));
   L.h = off; off += align256((size_t)S * k1 * imax * sizeof(float));
+  L.xl = off; off += align256((size_t)S * gh * 24 * sizeof(uint32_t));
+  L.xf = off; off += align256((size_t)S * gh * sizeof(float));
+  L.hl = off; off += align256((size_t)S * k1 * gi * 24 * sizeof(uint32_t));
+  L.hf = off; off += align256((size_t)S * k1 * gi * sizeof(float));
   L.max_items = 0;
   if (S > kSmallS) {
     L.part = off; off += align256((size_t)S * k1 * c.hidden * sizeof(float));
@@ -181,7 +204,7 @@ int moe_pack_expert(const moe_cfg *c, int32_t inter, const uint8_t *qg, const ui
       const int r = kGuPairs * t + i / 2;
       const uint8_t *q = (i & 1) ? qu : qg;
       const uint16_t *s = (i & 1) ? su : sg;
-      std::memcpy(tile + (size_t)i * (H / 2), q + (size_t)r * (H / 2), H / 2);
+      copy_flip(tile + (size_t)i * (H / 2), q + (size_t)r * (H / 2), H / 2);
       for (int g = 0; g < ngh; ++g) scl[g * kGuRows + i] = s[(size_t)r * ngh + g];
     }
   }
@@ -190,7 +213,7 @@ int moe_pack_expert(const moe_cfg *c, int32_t inter, const uint8_t *qg, const ui
     uint16_t *scl = (uint16_t *)(tile + (size_t)kDnRows * (I / 2));
     for (int i = 0; i < kDnRows; ++i) {
       const int r = kDnRows * t + i;
-      std::memcpy(tile + (size_t)i * (I / 2), qd + (size_t)r * (I / 2), I / 2);
+      copy_flip(tile + (size_t)i * (I / 2), qd + (size_t)r * (I / 2), I / 2);
       for (int g = 0; g < ngi; ++g) scl[g * kDnRows + i] = sd[(size_t)r * ngi + g];
     }
   }
@@ -214,7 +237,7 @@ int moe_unpack_expert(const moe_cfg *c, int32_t inter, const void *src, uint8_t 
       const int r = kGuPairs * t + i / 2;
       uint8_t *q = (i & 1) ? qu : qg;
       uint16_t *s = (i & 1) ? su : sg;
-      std::memcpy(q + (size_t)r * (H / 2), tile + (size_t)i * (H / 2), H / 2);
+      copy_flip(q + (size_t)r * (H / 2), tile + (size_t)i * (H / 2), H / 2);
       for (int g = 0; g < ngh; ++g) s[(size_t)r * ngh + g] = scl[g * kGuRows + i];
     }
   }
@@ -223,7 +246,7 @@ int moe_unpack_expert(const moe_cfg *c, int32_t inter, const void *src, uint8_t 
     const uint16_t *scl = (const uint16_t *)(tile + (size_t)kDnRows * (I / 2));
     for (int i = 0; i < kDnRows; ++i) {
       const int r = kDnRows * t + i;
-      std::memcpy(qd + (size_t)r * (I / 2), tile + (size_t)i * (I / 2), I / 2);
+      copy_flip(qd + (size_t)r * (I / 2), tile + (size_t)i * (I / 2), I / 2);
       for (int g = 0; g < ngi; ++g) sd[(size_t)r * ngi + g] = scl[g * kDnRows + i];
     }
   }
@@ -270,9 +293,18 @@ int moe_ffn(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const i
   a.y = y;
   char *b = (char *)ws;
   a.h = (float *)(b + L.h);
+  a.xl = (uint32_t *)(b + L.xl);
+  a.xf = (float *)(b + L.xf);
+  a.hl = (uint32_t *)(b + L.hl);
+  a.hf = (float *)(b + L.hf);
+  a.n_cu = device_cus();
   hipError_t e;
   if (S <= kSmallS) {
-    e = launch_ffn_small(a, (hipStream_t)stream);
+    // one-token down kernel: about one row block per compute unit, at most 8 tiles each
+    const int nt = c->hidden / kDnRows;
+    a.tb = std::min(8, std::max(1, (nt + a.n_cu - 1) / a.n_cu));
+    a.n_blk = (nt + a.tb - 1) / a.tb;
+    e = launch_ffn_decode(a, (hipStream_t)stream);
   } else {
     a.part = (float *)(b + L.part);
     a.lists = (int32_t *)(b + L.lists);
@@ -280,7 +312,7 @@ int moe_ffn(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const i
     a.items = (int32_t *)(b + L.items);
     a.n_items = (int32_t *)(b + L.n_items);
     a.max_items = L.max_items;
-    e = launch_ffn_large(a, (hipStream_t)stream);
+    e = launch_ffn_batch(a, (hipStream_t)stream);
   }
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }

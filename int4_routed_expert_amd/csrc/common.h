@@ -20,10 +20,13 @@ constexpr int kMaxG = 64;        // n_group limit
 
 // ---- slot layout of one packed expert (inter = I, hidden = H) -------------
 // gate/up: I/4 tiles.  Tile t holds 8 rows, in order (g 4t, u 4t, g 4t+1, u 4t+1,
-// ..., g 4t+3, u 4t+3), each row H/2 bytes of nibbles in interchange order, then
-// the tile's scales as [H/32 groups][8 rows] fp16.
+// ..., g 4t+3, u 4t+3), each row H/2 bytes, then the tile's scales as
+// [H/32 groups][8 rows] fp16.
 // down: H/8 tiles.  Tile t holds rows 8t..8t+7 (I/2 bytes each), then scales
 // [I/32 groups][8 rows] fp16.
+// Element order within a row is the interchange order (element 2j in the low
+// nibble of byte j), but each nibble holds the int4 value in two's complement
+// (interchange nibble XOR 8), the operand format of v_dot8_i32_i4.
 __host__ __device__ inline int64_t gu_tile_bytes(int H) { return (int64_t)kGuRows * (H / 2) + (int64_t)(H / kGroup) * kGuRows * 2; }
 __host__ __device__ inline int64_t dn_tile_bytes(int I) { return (int64_t)kDnRows * (I / 2) + (int64_t)(I / kGroup) * kDnRows * 2; }
 __host__ __device__ inline int64_t down_offset(int H, int I) { return (int64_t)(I / kGuPairs) * gu_tile_bytes(H); }
@@ -61,6 +64,15 @@ struct FfnArgs {
   int32_t *items;  // work items (large-batch path)
   int32_t *n_items;
   int32_t max_items;
+  // activations in limb form (see dot.h): [rows][groups][24] words and [rows][groups] factors
+  uint32_t *xl;    // x: S rows of H/32 groups
+  float *xf;
+  uint32_t *hl;    // h: S*(k+1) rows of Imax/32 groups
+  float *hf;
+  // one-token decode path
+  int32_t n_blk;   // row blocks of the down kernel
+  int32_t tb;      // down tiles (8 rows) per row block
+  int32_t n_cu;    // compute units of the device
 };
 
 // ---- timing instrumentation (host) --------------------------------------------
@@ -77,14 +89,16 @@ struct ProfScope {
 
 // ---- launchers (host) --------------------------------------------------------
 hipError_t launch_route(const RouteArgs &a, hipStream_t st);
-hipError_t launch_ffn_small(const FfnArgs &a, hipStream_t st);
-hipError_t launch_ffn_large(const FfnArgs &a, hipStream_t st);
+hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st);  // S <= kSmallS
+hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st);   // S > kSmallS
+hipError_t launch_to_limbs(const void *src, int src_bf16, int rows, int K, int src_stride, uint32_t *limbs,
+                           float *factors, hipStream_t st);
 hipError_t launch_pack(int H, int I, const uint8_t *qg, const uint16_t *sg, const uint8_t *qu, const uint16_t *su,
                        const uint8_t *qd, const uint16_t *sd, uint8_t *dst, hipStream_t st);
 
 // workspace layout (bytes, each region 256-aligned)
 struct WsLayout {
-  size_t logits, h, part, lists, counts, items, n_items, total;
+  size_t logits, h, xl, xf, hl, hf, part, lists, counts, items, n_items, total;
   int32_t max_items;
 };
 WsLayout ws_layout(const moe_cfg &c, int32_t S);

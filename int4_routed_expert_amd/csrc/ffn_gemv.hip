@@ -1,104 +1,402 @@
-// Expert FFN on the fp32 dequantise-and-multiply-accumulate path.
+// Expert FFN for decode batches (S <= 4 tokens): gate/up projection, SwiGLU,
+// down projection and the route-order combine with the shared expert.
 //
 // Method: "GLM-5.2 on a 32 GB Mac - native MLX port of the Colibri hierarchy",
-// N1 and "G2 implementation status": routed experts are SwiGLU FFNs over Q4
-// weights whose nibbles are offset-binary (value = nibble - 8) with a scale per
-// group; numerics are dequantise then f32 multiply-accumulate; the weighted
-// expert outputs are composed in route order and the shared expert is added
-// unweighted.  colibri README "What's implemented" (batch-union MoE): every
-// unique expert of the batch is read once and applied to all tokens that chose it.
+// N1 and "G2 implementation status": routed experts are SwiGLU FFNs over int4
+// weights with a scale per group; the weighted expert outputs are composed in
+// route order and the shared expert is added unweighted.  colibri README
+// "What's implemented" (batch-union MoE): every unique expert of the batch is
+// read once and applied to all tokens that chose it.
 //
-// Per 32-element group g of a weight row, with nibbles u and scale s:
-//   sum_c (u_c - 8) s x_c = s * (sum_c u_c x_c - 8 * sum_c x_c)
-// so the inner loop is one byte-to-float conversion and one FMA per weight, and
-// the group sum of x is shared by the 8 rows of a tile.
+// Every weight group is contracted with the exact integer dot product of dot.h.
+// All paths use the same per-token arithmetic in the same order (lane groups in
+// order, then one fixed wave reduction, then the route-order combine), so a
+// token's output does not depend on which other tokens share its batch.
 //
-// Decode path (S <= 4): two kernels.  Each workgroup derives the batch union
-// from idx itself (at most 64 entries), so no planning launch is needed.
-//  * k_gateup_small: one wave per gate/up tile (4 features: gate and up rows),
-//    lanes own 32-element groups of K = H; h = silu(g) * u -> workspace.
-//  * k_down_small: one workgroup per 8-row tile of y; its waves take the union's
-//    experts, write per-(token, rank) dot products to LDS, and the workgroup
-//    sums them in route order plus the shared expert: deterministic, no atomics,
-//    and each token's result does not depend on the other tokens of the batch.
-// Large-batch path: per-expert token lists (k_bucket), work items of up to 4
-// tokens (k_schedule), the same tile math over items, and a combine kernel.
+// One token (the decode step): two streaming kernels.
+//  * k_gateup_s1: the work is the list of features (gate row r and up row r of
+//    one expert).  Each wave takes an equal share of the shared expert's
+//    features first (their weights do not depend on the routing, so they stream
+//    while the wave resolves idx -> slot), then an equal share of the routed
+//    experts' features, with two features in flight while one is computed.
+//    x is converted to limbs once per workgroup in LDS and kept in registers.
+//  * k_down_s1: one workgroup per block of output rows; its waves take the
+//    experts (routed in rank order, then shared), stream that expert's down tiles
+//    for the block and leave the dot products in LDS; the workgroup then adds them
+//    in route order into y: deterministic, no atomics, no cross-workgroup sync.
+// Two to four tokens: the batch union is derived in every workgroup from idx (at
+// most 64 entries), activations are converted to limbs by a small pass, and the
+// same tile math runs over (unique expert, tile) pairs.
 #include <algorithm>
 
-#include "common.h"
+#include "dot.h"
 
 namespace moe {
 namespace {
 
-constexpr int kTB = 4;  // tokens per work item
+__device__ inline float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
-__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
-__device__ inline float wave_sum(float v) {
+// 32 activations (fp32, or bf16 bits) starting at element `off`.
+__device__ inline void load32(const void *x, int bf16, size_t off, float *v) {
+  if (bf16) {
+    const uint16_t *p = (const uint16_t *)x + off;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-// sum_c u_c x_c over one group: q holds 32 nibbles (element 2j low, 2j+1 high).
-__device__ inline float dot_group(const uint4 q, const float *x) {
-  const uint32_t d[4] = {q.x, q.y, q.z, q.w};
-  float acc = 0.f;
+    for (int m = 0; m < 4; ++m) {
+      const uint4 r = ldg<uint4>(p + 8 * m);
+      const uint32_t d[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = d[i] & 0x0F0F0F0Fu;
-    const uint32_t hi = (d[i] >> 4) & 0x0F0F0F0Fu;
+      for (int j = 0; j < 4; ++j) {
+        v[8 * m + 2 * j] = __uint_as_float(d[j] << 16);
+        v[8 * m + 2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const float *p = (const float *)x + off;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      acc = fmaf((float)((lo >> (8 * b)) & 0xFFu), x[8 * i + 2 * b], acc);
-      acc = fmaf((float)((hi >> (8 * b)) & 0xFFu), x[8 * i + 2 * b + 1], acc);
+    for (int m = 0; m < 8; ++m) {
+      const float4 r = ldg<float4>(p + 4 * m);
+      v[4 * m] = r.x; v[4 * m + 1] = r.y; v[4 * m + 2] = r.z; v[4 * m + 3] = r.w;
     }
   }
-  return acc;
+}
+
+__device__ inline void store_limbs(uint32_t *dst, float *fdst, const Limbs &L) {
+  uint4 *d = (uint4 *)dst;
+#pragma unroll
+  for (int l = 0; l < 6; ++l) d[l] = make_uint4(L.L[l][0], L.L[l][1], L.L[l][2], L.L[l][3]);
+  *fdst = L.f;
+}
+__device__ inline void load_limbs_lds(const uint32_t *src, const float *fsrc, Limbs &L) {
+  const uint4 *s = (const uint4 *)src;
+#pragma unroll
+  for (int l = 0; l < 6; ++l) {
+    const uint4 r = s[l];
+    L.L[l][0] = r.x; L.L[l][1] = r.y; L.L[l][2] = r.z; L.L[l][3] = r.w;
+  }
+  L.f = *fsrc;
+}
+__device__ inline void load_limbs_global(const uint32_t *src, const float *fsrc, Limbs &L) {
+#pragma unroll
+  for (int l = 0; l < 6; ++l) {
+    const uint4 r = ldg<uint4>(src + 4 * l);
+    L.L[l][0] = r.x; L.L[l][1] = r.y; L.L[l][2] = r.z; L.L[l][3] = r.w;
+  }
+  L.f = ldg<float>(fsrc);
+}
+
+// ---- activations -> limbs (global), one thread per (row, group) ---------------
+__global__ __launch_bounds__(256) void k_to_limbs(const void *src, int bf16, int rows, int K, int stride,
+                                                  uint32_t *limbs, float *factors) {
+  const int ng = K / kGroup;
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long)rows * ng) return;
+  const int r = (int)(i / ng), g = (int)(i - (long)r * ng);
+  float v[32];
+  load32(src, bf16, (size_t)r * stride + (size_t)g * kGroup, v);
+  Limbs L;
+  to_limbs(v, L);
+  uint4 *d = (uint4 *)(limbs + (size_t)i * 24);
+#pragma unroll
+  for (int l = 0; l < 6; ++l) stg<uint4>(d + l, make_uint4(L.L[l][0], L.L[l][1], L.L[l][2], L.L[l][3]));
+  stg<float>(factors + i, L.f);
+}
+
+// ---- one token: gate/up ---------------------------------------------------------
+template <int NG>
+struct GuFeat {
+  uint4 g[NG], u[NG];
+  uint32_t s[NG];  // fp16 scales of (gate r, up r) for the lane's groups
+  int valid;
+};
+
+// Slot of routed expert `lane` (< k): idx entry in [0, E) and table entry in
+// [0, n_slots), else 0 (the expert's outputs become NaN).
+__device__ inline uint64_t routed_ptr_lane(const FfnArgs &a, int lane) {
+  uint64_t p = 0;
+  if (lane < a.k) {
+    const int e = ldg<int>(a.idx + lane);
+    if (e >= 0 && e < a.E) {
+      const int s = ldg<int>(a.table + e);
+      if (s >= 0 && s < a.n_slots) p = (uint64_t)(uintptr_t)(a.base + (size_t)s * (size_t)a.slot_bytes);
+    }
+  }
+  return p;
+}
+
+// Loads of feature i of this wave's list (clamped into range so that loads are
+// unconditional; lanes past the last group read the last group and contribute
+// zero because their activation limbs are zero).
+template <int NG>
+__device__ inline void gu_feat_load(GuFeat<NG> &b, const FfnArgs &a, int i, int n, int ns, int s0, int r0,
+                                    uint64_t my_ptr, int lane) {
+  const int H = a.H, ng = H / kGroup;
+  i = min(i, n - 1);
+  int r;
+  const uint8_t *ex;
+  if (i < ns) {
+    r = s0 + i;
+    ex = a.shared;
+  } else {
+    const int f = r0 + i - ns, j = f / a.I;
+    r = f - j * a.I;
+    ex = lane_ptr(my_ptr, j);
+  }
+  b.valid = ex != nullptr;
+  if (!ex) ex = a.base;  // readable stand-in; the result is replaced by NaN
+  const int pos = r & 3;
+  const uint8_t *tile = ex + (size_t)(r >> 2) * gu_tile_bytes(H);
+  const uint8_t *rg = tile + (size_t)(2 * pos) * (H / 2);
+  const uint8_t *sc = tile + (size_t)kGuRows * (H / 2) + 4 * pos;
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const int g = min(lane + 64 * j, ng - 1);
+    b.g[j] = ldg<uint4>(rg + g * 16);
+    b.u[j] = ldg<uint4>(rg + H / 2 + g * 16);
+    b.s[j] = ldg<uint32_t>(sc + g * 16);
+  }
+}
+
+// h of one feature: the sums land in lane 63; the value is parked in lane
+// `slot` of hout so that the loop issues no stores (stores would perturb the
+// in-order load counter the prefetch ring relies on).
+template <int NG>
+__device__ inline float gu_feat_compute(const GuFeat<NG> &b, const Limbs (&xv)[NG], int slot, float hout) {
+  float g = 0.f, u = 0.f;
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    g = fmaf(group_dot(b.g[j], xv[j]), half_bits_to_float(b.s[j]) * xv[j].f, g);
+    u = fmaf(group_dot(b.u[j], xv[j]), half_bits_to_float(b.s[j] >> 16) * xv[j].f, u);
+  }
+  g = wave_sum_to63(g);
+  u = wave_sum_to63(u);
+  const float hv = b.valid ? silu_mul(g, u) : __builtin_nanf("");
+  const float h63 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hv), 63));
+  return (int)(threadIdx.x & 63) == slot ? h63 : hout;
+}
+
+constexpr int kGuMaxPerWave = 64;  // features per wave (one parked h per lane)
+
+template <int NG>
+__global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
+  extern __shared__ uint32_t lds[];  // x limbs [H/32][24], then factors [H/32]
+  const int lane = threadIdx.x & 63;
+  const int W = gridDim.x * 4, wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int ng = a.H / kGroup, Imax = max(a.I, a.Is);
+  const long Is = a.Is, Fr = (long)a.k * a.I;
+  const int s0 = (int)(wid * Is / W), s1 = (int)((wid + 1) * Is / W);
+  const int r0 = (int)(wid * Fr / W), r1 = (int)((wid + 1) * Fr / W);
+  const int ns = s1 - s0, n = ns + (r1 - r0);
+  const uint64_t my_ptr = routed_ptr_lane(a, lane);
+  // three-slot ring, two features in flight while one is computed; the first
+  // two (shared-expert features when the wave has any) are issued before the
+  // activations are staged.  Loads are unconditional (indices clamped; repeats
+  // at the tail hit in cache) so the load counter order is fixed.
+  GuFeat<NG> b0, b1, b2;
+  if (n > 0) {
+    gu_feat_load(b0, a, 0, n, ns, s0, r0, my_ptr, lane);
+    gu_feat_load(b1, a, 1, n, ns, s0, r0, my_ptr, lane);
+  }
+  float *lf = (float *)(lds + (size_t)ng * 24);
+  for (int g = threadIdx.x; g < ng; g += blockDim.x) {
+    float v[32];
+    load32(a.x, a.x_bf16, (size_t)g * kGroup, v);
+    Limbs L;
+    to_limbs(v, L);
+    store_limbs(lds + (size_t)g * 24, lf + g, L);
+  }
+  __syncthreads();
+  if (n <= 0) return;
+  Limbs xv[NG];
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const int g = lane + 64 * j;
+    if (g < ng) {
+      load_limbs_lds(lds + (size_t)g * 24, lf + g, xv[j]);
+    } else {
+#pragma unroll
+      for (int l = 0; l < 6; ++l)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) xv[j].L[l][m] = 0u;
+      xv[j].f = 0.f;
+    }
+  }
+  float hout = 0.f;
+  for (int i = 0; i < n; i += 3) {
+    gu_feat_load(b2, a, i + 2, n, ns, s0, r0, my_ptr, lane);
+    hout = gu_feat_compute(b0, xv, i, hout);
+    gu_feat_load(b0, a, i + 3, n, ns, s0, r0, my_ptr, lane);
+    if (i + 1 < n) hout = gu_feat_compute(b1, xv, i + 1, hout);
+    gu_feat_load(b1, a, i + 4, n, ns, s0, r0, my_ptr, lane);
+    if (i + 2 < n) hout = gu_feat_compute(b2, xv, i + 2, hout);
+  }
+  if (lane < n) {
+    int hrow;
+    if (lane < ns) {
+      hrow = a.k * Imax + s0 + lane;
+    } else {
+      const int f = r0 + lane - ns, j = f / a.I;
+      hrow = j * Imax + (f - j * a.I);
+    }
+    stg<float>(a.h + hrow, hout);
+  }
+}
+
+// ---- one token: down + route-order combine -----------------------------------------
+template <int NGD>
+struct DnTile {
+  uint4 q[kDnRows][NGD], sc[NGD];
+};
+
+// Tile t (clamped to the block's last tile: loads stay unconditional).
+template <int NGD>
+__device__ inline void dn_tile_load(DnTile<NGD> &b, const uint8_t *dn, int inter, int t, int t1, int lane) {
+  const int ng = inter / kGroup;
+  const uint8_t *tile = dn + (size_t)min(t, t1 - 1) * dn_tile_bytes(inter);
+#pragma unroll
+  for (int j = 0; j < NGD; ++j) {
+    const int g = min(lane + 64 * j, ng - 1);
+#pragma unroll
+    for (int i = 0; i < kDnRows; ++i) b.q[i][j] = ldg<uint4>(tile + (size_t)i * (inter / 2) + g * 16);
+    b.sc[j] = ldg<uint4>(tile + (size_t)kDnRows * (inter / 2) + g * 16);
+  }
 }
 
 __device__ inline float scale_of(const uint4 sc, int i) {
   const uint32_t d[4] = {sc.x, sc.y, sc.z, sc.w};
-  const uint16_t bits = (uint16_t)(d[i >> 1] >> (16 * (i & 1)));
-  return __half2float(__ushort_as_half(bits));
+  return half_bits_to_float(d[i >> 1] >> (16 * (i & 1)));
 }
 
-// Load a 32-element activation group (fp32 or bf16) and its sum.
-__device__ inline float load_group(const void *x, int bf16, size_t off, float *xv) {
-  if (bf16) {
-    const uint4 *p = (const uint4 *)((const uint16_t *)x + off);
+// 8 row dots of one tile against one activation set; lane 63 holds the sums.
+template <int NGD>
+__device__ inline void dn_tile_dots(const DnTile<NGD> &b, const Limbs (&hv)[NGD], float (&acc)[kDnRows]) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const uint4 r = p[v];
-      const uint32_t d[4] = {r.x, r.y, r.z, r.w};
+  for (int i = 0; i < kDnRows; ++i) acc[i] = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        xv[8 * v + 2 * j] = __uint_as_float(d[j] << 16);
-        xv[8 * v + 2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
+  for (int j = 0; j < NGD; ++j)
+#pragma unroll
+    for (int i = 0; i < kDnRows; ++i) acc[i] = fmaf(group_dot(b.q[i][j], hv[j]), scale_of(b.sc[j], i) * hv[j].f, acc[i]);
+#pragma unroll
+  for (int i = 0; i < kDnRows; ++i) acc[i] = wave_sum_to63(acc[i]);
+}
+
+constexpr int kDnMaxTb = 8;    // down tiles per row block, at most
+constexpr int kDnS1Waves = 9;  // waves per one-token down workgroup
+
+// HLDS: h of every expert is converted to limbs into LDS by the workgroup;
+// otherwise the limbs come from global memory (converted by k_to_limbs).
+template <int NGD, bool HLDS>
+__global__ __launch_bounds__(kDnS1Waves * 64) void k_down_s1(FfnArgs a) {
+  __shared__ float part[kMaxK + 1][kDnRows * kDnMaxTb];
+  __shared__ int s_idx[kMaxK];
+  __shared__ float s_w[kMaxK];
+  extern __shared__ uint32_t hlds[];  // HLDS: [NE][Imax/32][24] limbs, then [NE][Imax/32] factors
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int NE = a.k + (a.Is > 0 ? 1 : 0);
+  const int Imax = max(a.I, a.Is), ngm = Imax / kGroup, nt = a.H / kDnRows;
+  const int t0 = blockIdx.x * a.tb, t1 = min(nt, t0 + a.tb);
+  if ((int)threadIdx.x < a.k) {  // for the combine; read once, up front
+    s_idx[threadIdx.x] = ldg<int>(a.idx + threadIdx.x);
+    s_w[threadIdx.x] = ldg<float>(a.w + threadIdx.x);
+  }
+  // this wave's first expert: issue its first two tiles before staging h
+  int j = wave;
+  const uint8_t *dn = a.base;
+  int inter = a.I;
+  bool valid = false;
+  DnTile<NGD> q0, q1;
+  auto resolve = [&](int jj) {
+    const bool sh = jj == a.k;
+    inter = sh ? a.Is : a.I;
+    const uint8_t *ex = nullptr;
+    if (sh) {
+      ex = a.shared;
+    } else {
+      const int e = ldg<int>(a.idx + jj);
+      if (e >= 0 && e < a.E) {
+        const int s = ldg<int>(a.table + e);
+        if (s >= 0 && s < a.n_slots) ex = a.base + (size_t)s * (size_t)a.slot_bytes;
       }
     }
-  } else {
-    const float4 *p = (const float4 *)((const float *)x + off);
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const float4 r = p[v];
-      xv[4 * v] = r.x; xv[4 * v + 1] = r.y; xv[4 * v + 2] = r.z; xv[4 * v + 3] = r.w;
+    valid = ex != nullptr;
+    if (!valid) inter = a.I;
+    dn = uniform_ptr((valid ? ex : a.base) + down_offset(a.H, inter));
+  };
+  if (j < NE) {
+    resolve(j);
+    dn_tile_load(q0, dn, inter, t0, t1, lane);
+    dn_tile_load(q1, dn, inter, t0 + 1, t1, lane);
+  }
+  float *hf_lds = (float *)(hlds + (size_t)NE * ngm * 24);
+  if (HLDS) {
+    for (int i = threadIdx.x; i < NE * ngm; i += blockDim.x) {
+      const int e2 = i / ngm, g = i - e2 * ngm;
+      const int ie = e2 == a.k ? a.Is : a.I;
+      if (g * kGroup < ie) {
+        float v[32];
+        load32(a.h, 0, (size_t)e2 * Imax + (size_t)g * kGroup, v);
+        Limbs L;
+        to_limbs(v, L);
+        store_limbs(hlds + (size_t)i * 24, hf_lds + i, L);
+      }
     }
   }
-  float s = 0.f;
+  __syncthreads();
+  for (; j < NE; j += nw) {
+    if (j != wave) {
+      resolve(j);
+      dn_tile_load(q0, dn, inter, t0, t1, lane);
+      dn_tile_load(q1, dn, inter, t0 + 1, t1, lane);
+    }
+    const int ng = inter / kGroup;
+    Limbs hv[NGD];
 #pragma unroll
-  for (int c = 0; c < 32; ++c) s += xv[c];
-  return s;
+    for (int g2 = 0; g2 < NGD; ++g2) {
+      const int g = min(lane + 64 * g2, ng - 1);
+      if (HLDS) load_limbs_lds(hlds + ((size_t)j * ngm + g) * 24, hf_lds + (size_t)j * ngm + g, hv[g2]);
+      else load_limbs_global(a.hl + ((size_t)j * ngm + g) * 24, a.hf + (size_t)j * ngm + g, hv[g2]);
+      if (lane + 64 * g2 >= ng) hv[g2].f = 0.f;  // clamped duplicate group contributes zero
+    }
+    float *dst = &part[j][0];
+    for (int t = t0; t < t1; t += 2) {
+      float acc[kDnRows];
+      dn_tile_dots(q0, hv, acc);
+      if (lane == 63) {
+        const int o = (t - t0) * kDnRows;
+#pragma unroll
+        for (int i = 0; i < kDnRows; ++i) dst[o + i] = valid ? acc[i] : __builtin_nanf("");
+      }
+      dn_tile_load(q0, dn, inter, t + 2, t1, lane);
+      if (t + 1 < t1) {
+        dn_tile_dots(q1, hv, acc);
+        if (lane == 63) {
+          const int o = (t + 1 - t0) * kDnRows;
+#pragma unroll
+          for (int i = 0; i < kDnRows; ++i) dst[o + i] = valid ? acc[i] : __builtin_nanf("");
+        }
+      }
+      dn_tile_load(q1, dn, inter, t + 3, t1, lane);
+    }
+  }
+  __syncthreads();
+  const int rows = (t1 - t0) * kDnRows;
+  if ((int)threadIdx.x < rows) {
+    bool bad = false;
+    for (int jj = 0; jj < a.k; ++jj) {
+      const int e = s_idx[jj];
+      bad |= e < 0 || e >= a.E;
+      for (int ii = 0; ii < jj; ++ii) bad |= s_idx[ii] == e;
+    }
+    const int i = threadIdx.x;
+    float acc = 0.f;
+    for (int jj = 0; jj < a.k; ++jj) acc = fmaf(s_w[jj], part[jj][i], acc);
+    if (a.Is > 0) acc += part[a.k][i];
+    stg<float>(a.y + t0 * kDnRows + i, bad ? __builtin_nanf("") : acc);
+  }
 }
 
-// Keeps the compiler from hoisting the nibble unpacking of a whole tile out of
-// the per-token loop (that would need 8 * 32 * NG registers per lane).
-__device__ inline void opaque(uint4 &v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
-
-__device__ inline float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
-
-// Batch union for S <= 4, in LDS.  uniq[0..U) ascending expert ids; for unique
-// slot u: ntok[u] tokens tok[u][a] (ascending) with pair index pair[u][a] =
+// ---- two to four tokens ---------------------------------------------------------
+// Batch union in LDS.  uniq[0..U) ascending expert ids; for unique slot u:
+// ntok[u] tokens tok[u][a] (ascending) with pair index pair[u][a] =
 // token * (k+1) + rank.  Slot U is the shared expert with every token.
 struct SmallPlan {
   int U;
@@ -118,10 +416,10 @@ __device__ void build_small_plan(const FfnArgs &a, SmallPlan &p) {
   if (tid < a.S) p.tokbad[tid] = 0;
   __syncthreads();
   if (tid < n) {
-    const int e = a.idx[tid];
+    const int e = ldg<int>(a.idx + tid);
     const int t = tid / a.k;
     bool ok = e >= 0 && e < a.E;
-    for (int j = t * a.k; j < tid && ok; ++j) ok = a.idx[j] != e;
+    for (int j = t * a.k; j < tid && ok; ++j) ok = ldg<int>(a.idx + j) != e;
     p.sidx[tid] = ok ? e : -1;
     if (!ok) atomicOr(&p.tokbad[t], 1);
   }
@@ -158,69 +456,45 @@ __device__ void build_small_plan(const FfnArgs &a, SmallPlan &p) {
 }
 
 __device__ inline const uint8_t *expert_ptr(const FfnArgs &a, int e) {
-  const int s = a.table[e];
+  const int s = ldg<int>(a.table + e);
   if (s < 0 || s >= a.n_slots) return nullptr;
   return a.base + (size_t)s * (size_t)a.slot_bytes;
 }
 
-// ---- one gate/up tile for a set of tokens -----------------------------------
-// Lane owns groups lane + 64 j (j < NG) of K = H.  Activations come from LDS
-// (xl: fp32 [S, H] and group sums xsum [S, H/32], staged by the workgroup) when
-// XLDS is set, else from global memory (fp32 or bf16).
-template <int NG, bool XLDS>
+// One gate/up tile (4 features) for a set of tokens; x limbs from global.
+template <int NG>
 __device__ inline void gateup_tile(const FfnArgs &a, const uint8_t *tile, int ntok, const int *toks, const int *pairs,
-                                   int feat0, int inter_stride, const float *xl, const float *xsum) {
+                                   int feat0, int inter_stride) {
   const int lane = threadIdx.x & 63, H = a.H, ng = H / kGroup;
   uint4 q[kGuRows][NG], sc[NG];
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
-    const int g = lane + 64 * j;
-    if (g < ng) {
+    const int g = min(lane + 64 * j, ng - 1);
 #pragma unroll
-      for (int i = 0; i < kGuRows; ++i) q[i][j] = *(const uint4 *)(tile + (size_t)i * (H / 2) + g * 16);
-      sc[j] = *(const uint4 *)(tile + (size_t)kGuRows * (H / 2) + g * 16);
-    }
+    for (int i = 0; i < kGuRows; ++i) q[i][j] = ldg<uint4>(tile + (size_t)i * (H / 2) + g * 16);
+    sc[j] = ldg<uint4>(tile + (size_t)kGuRows * (H / 2) + g * 16);
   }
   for (int tt = 0; tt < ntok; ++tt) {
+    Limbs xv[NG];
 #pragma unroll
-    for (int j = 0; j < NG; ++j)
-#pragma unroll
-      for (int i = 0; i < kGuRows; ++i) opaque(q[i][j]);
+    for (int j = 0; j < NG; ++j) {
+      const int g = min(lane + 64 * j, ng - 1);
+      load_limbs_global(a.xl + ((size_t)toks[tt] * ng + g) * 24, a.xf + (size_t)toks[tt] * ng + g, xv[j]);
+      if (lane + 64 * j >= ng) xv[j].f = 0.f;
+    }
     float acc[kGuRows];
 #pragma unroll
     for (int i = 0; i < kGuRows; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int j = 0; j < NG; ++j) {
-      const int g = lane + 64 * j;
-      if (g < ng) {
-        float xv[32], xs;
-        if (XLDS) {
-          const float4 *p = (const float4 *)(xl + (size_t)toks[tt] * H + g * kGroup);
+    for (int j = 0; j < NG; ++j)
 #pragma unroll
-          for (int v = 0; v < 8; ++v) {
-            const float4 r = p[v];
-            xv[4 * v] = r.x; xv[4 * v + 1] = r.y; xv[4 * v + 2] = r.z; xv[4 * v + 3] = r.w;
-          }
-          xs = xsum[toks[tt] * ng + g];
-        } else {
-          xs = load_group(a.x, a.x_bf16, (size_t)toks[tt] * H + g * kGroup, xv);
-        }
+      for (int i = 0; i < kGuRows; ++i) acc[i] = fmaf(group_dot(q[i][j], xv[j]), scale_of(sc[j], i) * xv[j].f, acc[i]);
 #pragma unroll
-        for (int i = 0; i < kGuRows; ++i) {
-          const float d = dot_group(q[i][j], xv);
-          acc[i] = fmaf(scale_of(sc[j], i), fmaf(-8.f, xs, d), acc[i]);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kGuRows; ++i) acc[i] = wave_sum(acc[i]);
-    if (lane < kGuPairs) {
-      float gv = acc[0], uv = acc[1];
-#pragma unroll
-      for (int r = 1; r < kGuPairs; ++r)
-        if (lane == r) { gv = acc[2 * r]; uv = acc[2 * r + 1]; }
-      a.h[(size_t)pairs[tt] * inter_stride + feat0 + lane] = silu_mul(gv, uv);
-    }
+    for (int i = 0; i < kGuRows; ++i) acc[i] = wave_sum_to63(acc[i]);
+    if (lane == 63)
+      stg<float4>(a.h + (size_t)pairs[tt] * inter_stride + feat0,
+                  make_float4(silu_mul(acc[0], acc[1]), silu_mul(acc[2], acc[3]), silu_mul(acc[4], acc[5]),
+                              silu_mul(acc[6], acc[7])));
   }
 }
 
@@ -230,29 +504,13 @@ __device__ inline void poison_h(const FfnArgs &a, int ntok, const int *pairs, in
     for (int tt = 0; tt < ntok; ++tt) a.h[(size_t)pairs[tt] * inter_stride + feat0 + lane] = __builtin_nanf("");
 }
 
-constexpr int kGuWaves = 8;  // waves per gate/up workgroup, one tile each
+constexpr int kGuWaves = 8;  // waves per small-batch gate/up workgroup, one tile each
 
-// ---- decode path: gate/up ------------------------------------------------------
-template <int NG, bool XLDS>
+template <int NG>
 __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_small(FfnArgs a) {
-  extern __shared__ float xl[];  // XLDS: [S, H] fp32 then [S, H/32] group sums
   __shared__ SmallPlan plan;
   build_small_plan(a, plan);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int ng = a.H / kGroup;
-  float *xsum = xl + (size_t)a.S * a.H;
-  if (XLDS) {
-    const int n = a.S * ng;  // one thread per (token, group): copy 32 values and sum them in order
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      float xv[32];
-      const float s = load_group(a.x, a.x_bf16, (size_t)i * kGroup, xv);
-      float4 *d = (float4 *)(xl + (size_t)i * kGroup);
-#pragma unroll
-      for (int v = 0; v < 8; ++v) d[v] = make_float4(xv[4 * v], xv[4 * v + 1], xv[4 * v + 2], xv[4 * v + 3]);
-      xsum[i] = s;
-    }
-    __syncthreads();
-  }
+  const int wave = threadIdx.x >> 6;
   const int Imax = max(a.I, a.Is);
   const int tr = a.I / kGuPairs, ts = a.Is / kGuPairs;
   const int total = plan.U * tr + ts;
@@ -267,70 +525,21 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_small(FfnArgs a) {
     u = plan.U; t = tile - plan.U * tr;
     ex = a.shared;
   }
-  (void)lane;
   if (!ex) { poison_h(a, plan.ntok[u], plan.pair[u], t * kGuPairs, Imax); return; }
-  gateup_tile<NG, XLDS>(a, ex + (size_t)t * gu_tile_bytes(a.H), plan.ntok[u], plan.tok[u], plan.pair[u],
-                        t * kGuPairs, Imax, xl, xsum);
+  gateup_tile<NG>(a, uniform_ptr(ex + (size_t)t * gu_tile_bytes(a.H)), plan.ntok[u], plan.tok[u], plan.pair[u],
+                  t * kGuPairs, Imax);
 }
 
-// ---- one down tile: dots of 8 rows with h of each token ------------------------
-// Lane i < 8 stores row i of token tt's dot at dst[pairs[tt] * dst_stride + i].
+// One workgroup per 8-row tile of y; its waves take the union's experts and leave
+// per-(token, rank) dot products in LDS; the workgroup sums them in route order.
 template <int NGD>
-__device__ inline void down_tile(const FfnArgs &a, const uint8_t *tile, int inter, int ntok, const int *pairs,
-                                 int inter_stride, float *dst, int dst_stride) {
-  const int lane = threadIdx.x & 63, ng = inter / kGroup;
-  uint4 q[kDnRows][NGD], sc[NGD];
-#pragma unroll
-  for (int j = 0; j < NGD; ++j) {
-    const int g = lane + 64 * j;
-    if (g < ng) {
-#pragma unroll
-      for (int i = 0; i < kDnRows; ++i) q[i][j] = *(const uint4 *)(tile + (size_t)i * (inter / 2) + g * 16);
-      sc[j] = *(const uint4 *)(tile + (size_t)kDnRows * (inter / 2) + g * 16);
-    }
-  }
-  for (int tt = 0; tt < ntok; ++tt) {
-#pragma unroll
-    for (int j = 0; j < NGD; ++j)
-#pragma unroll
-      for (int i = 0; i < kDnRows; ++i) opaque(q[i][j]);
-    float acc[kDnRows];
-#pragma unroll
-    for (int i = 0; i < kDnRows; ++i) acc[i] = 0.f;
-#pragma unroll
-    for (int j = 0; j < NGD; ++j) {
-      const int g = lane + 64 * j;
-      if (g < ng) {
-        float hv[32];
-        const float hs = load_group(a.h, 0, (size_t)pairs[tt] * inter_stride + g * kGroup, hv);
-#pragma unroll
-        for (int i = 0; i < kDnRows; ++i) {
-          const float d = dot_group(q[i][j], hv);
-          acc[i] = fmaf(scale_of(sc[j], i), fmaf(-8.f, hs, d), acc[i]);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kDnRows; ++i) acc[i] = wave_sum(acc[i]);
-    if (lane < kDnRows) {
-      float v = acc[0];
-#pragma unroll
-      for (int i = 1; i < kDnRows; ++i)
-        if (lane == i) v = acc[i];
-      dst[(size_t)pairs[tt] * dst_stride + lane] = v;
-    }
-  }
-}
-
-// ---- decode path: down + route-order combine ------------------------------------
-template <int NGD>
-__global__ __launch_bounds__(1024) void k_down_small(FfnArgs a) {
+__global__ __launch_bounds__(1024, 1) void k_down_small(FfnArgs a) {
   __shared__ SmallPlan plan;
   __shared__ float part[kSmallS * (kMaxK + 1)][kDnRows];
   build_small_plan(a, plan);
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6, lane = threadIdx.x & 63;
-  const int Imax = max(a.I, a.Is);
-  const int rt = blockIdx.x;  // row tile of y
+  const int Imax = max(a.I, a.Is), ngm = Imax / kGroup;
+  const int rt = blockIdx.x;
   const int nu = plan.U + (a.Is > 0 ? 1 : 0);
   for (int u = wave; u < nu; u += nw) {
     const bool sh = u == plan.U;
@@ -341,8 +550,24 @@ __global__ __launch_bounds__(1024) void k_down_small(FfnArgs a) {
         for (int tt = 0; tt < plan.ntok[u]; ++tt) part[plan.pair[u][tt]][lane] = __builtin_nanf("");
       continue;
     }
-    down_tile<NGD>(a, ex + down_offset(a.H, inter) + (size_t)rt * dn_tile_bytes(inter), inter, plan.ntok[u],
-                   plan.pair[u], Imax, &part[0][0], kDnRows);
+    DnTile<NGD> q;
+    dn_tile_load(q, uniform_ptr(ex + down_offset(a.H, inter)), inter, rt, rt + 1, lane);
+    const int ng = inter / kGroup;
+    for (int tt = 0; tt < plan.ntok[u]; ++tt) {
+      const int pr = plan.pair[u][tt];
+      Limbs hv[NGD];
+#pragma unroll
+      for (int g2 = 0; g2 < NGD; ++g2) {
+        const int g = min(lane + 64 * g2, ng - 1);
+        load_limbs_global(a.hl + ((size_t)pr * ngm + g) * 24, a.hf + (size_t)pr * ngm + g, hv[g2]);
+        if (lane + 64 * g2 >= ng) hv[g2].f = 0.f;
+      }
+      float acc[kDnRows];
+      dn_tile_dots(q, hv, acc);
+      if (lane == 63)
+#pragma unroll
+        for (int i = 0; i < kDnRows; ++i) part[pr][i] = acc[i];
+    }
   }
   __syncthreads();
   const int tid = threadIdx.x;
@@ -351,13 +576,19 @@ __global__ __launch_bounds__(1024) void k_down_small(FfnArgs a) {
     float acc = 0.f;
     const bool bad = plan.tokbad[t] != 0;
     if (!bad)
-      for (int j = 0; j < a.k; ++j) acc = fmaf(a.w[t * a.k + j], part[t * (a.k + 1) + j][i], acc);
+      for (int j = 0; j < a.k; ++j) acc = fmaf(ldg<float>(a.w + t * a.k + j), part[t * (a.k + 1) + j][i], acc);
     if (a.Is > 0) acc += part[t * (a.k + 1) + a.k][i];
-    a.y[(size_t)t * a.H + rt * kDnRows + i] = bad ? __builtin_nanf("") : acc;
+    stg<float>(a.y + (size_t)t * a.H + rt * kDnRows + i, bad ? __builtin_nanf("") : acc);
   }
 }
 
-// ---- large-batch path ----------------------------------------------------------
+
+// ---- large batches (S > 4) -------------------------------------------------------
+// Per-expert token lists (k_bucket), work items of up to 4 tokens (k_schedule),
+// the same tile math over (item, tile) pairs writing per-(token, rank) expert
+// outputs, and a combine in route order.
+constexpr int kTB = 4;  // tokens per work item
+
 // Per-expert token list in token order: block e scans idx in order and compacts
 // the entries equal to e (each token names an expert at most once).
 __global__ __launch_bounds__(256) void k_bucket(FfnArgs a) {
@@ -369,10 +600,10 @@ __global__ __launch_bounds__(256) void k_bucket(FfnArgs a) {
   __syncthreads();
   for (int c0 = 0; c0 < n; c0 += 256) {
     const int i = c0 + tid;
-    bool m = i < n && a.idx[i] == e;
+    bool m = i < n && ldg<int>(a.idx + i) == e;
     if (m) {  // a token that names e twice contributes once; the combine poisons it
       const int t0 = i / a.k * a.k;
-      for (int j = t0; j < i; ++j) m = m && a.idx[j] != e;
+      for (int j = t0; j < i; ++j) m = m && ldg<int>(a.idx + j) != e;
     }
     const unsigned long long bal = __ballot(m);
     const int pre = __popcll(bal & ((1ull << lane) - 1ull));
@@ -445,7 +676,7 @@ __global__ __launch_bounds__(256) void k_gateup_items(FfnArgs a) {
     const int n = item_tokens(a, it, toks, pairs);
     const uint8_t *ex = it[0] == a.E ? a.shared : expert_ptr(a, it[0]);
     if (!ex) { poison_h(a, n, pairs, t * kGuPairs, Imax); continue; }
-    gateup_tile<NG, false>(a, ex + (size_t)t * gu_tile_bytes(a.H), n, toks, pairs, t * kGuPairs, Imax, nullptr, nullptr);
+    gateup_tile<NG>(a, uniform_ptr(ex + (size_t)t * gu_tile_bytes(a.H)), n, toks, pairs, t * kGuPairs, Imax);
   }
 }
 
@@ -453,7 +684,7 @@ template <int NGD>
 __global__ __launch_bounds__(256) void k_down_items(FfnArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nr = a.n_items[0], nsh = a.n_items[1];
-  const int Imax = max(a.I, a.Is);
+  const int Imax = max(a.I, a.Is), ngm = Imax / kGroup;
   const int nt = a.H / kDnRows;
   const long total = (long)(nr + nsh) * nt;
   for (long w = (long)blockIdx.x * 4 + wave; w < total; w += (long)gridDim.x * 4) {
@@ -469,8 +700,26 @@ __global__ __launch_bounds__(256) void k_down_items(FfnArgs a) {
         for (int tt = 0; tt < n; ++tt) a.part[(size_t)pairs[tt] * a.H + rt * kDnRows + lane] = __builtin_nanf("");
       continue;
     }
-    down_tile<NGD>(a, ex + down_offset(a.H, inter) + (size_t)rt * dn_tile_bytes(inter), inter, n, pairs, Imax,
-                   a.part + (size_t)rt * kDnRows, a.H);
+    DnTile<NGD> q;
+    dn_tile_load(q, uniform_ptr(ex + down_offset(a.H, inter)), inter, rt, rt + 1, lane);
+    const int ng = inter / kGroup;
+    for (int tt = 0; tt < n; ++tt) {
+      const int pr = pairs[tt];
+      Limbs hv[NGD];
+#pragma unroll
+      for (int g2 = 0; g2 < NGD; ++g2) {
+        const int g = min(lane + 64 * g2, ng - 1);
+        load_limbs_global(a.hl + ((size_t)pr * ngm + g) * 24, a.hf + (size_t)pr * ngm + g, hv[g2]);
+        if (lane + 64 * g2 >= ng) hv[g2].f = 0.f;
+      }
+      float acc[kDnRows];
+      dn_tile_dots(q, hv, acc);
+      if (lane == 63) {
+        float4 *d = (float4 *)(a.part + (size_t)pr * a.H + rt * kDnRows);
+        stg<float4>(d, make_float4(acc[0], acc[1], acc[2], acc[3]));
+        stg<float4>(d + 1, make_float4(acc[4], acc[5], acc[6], acc[7]));
+      }
+    }
   }
 }
 
@@ -482,9 +731,9 @@ __global__ __launch_bounds__(256) void k_combine(FfnArgs a) {
   if (threadIdx.x == 0) {
     int b = 0;
     for (int j = 0; j < a.k; ++j) {
-      const int e = a.idx[t * a.k + j];
+      const int e = ldg<int>(a.idx + t * a.k + j);
       b |= (e < 0 || e >= a.E);
-      for (int i = 0; i < j; ++i) b |= a.idx[t * a.k + i] == e;
+      for (int i = 0; i < j; ++i) b |= ldg<int>(a.idx + t * a.k + i) == e;
     }
     bad = b;
   }
@@ -492,51 +741,98 @@ __global__ __launch_bounds__(256) void k_combine(FfnArgs a) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= a.H) return;
   float acc = 0.f;
-  for (int j = 0; j < a.k; ++j) acc = fmaf(a.w[t * a.k + j], a.part[((size_t)t * (a.k + 1) + j) * a.H + c], acc);
-  if (a.Is > 0) acc += a.part[((size_t)t * (a.k + 1) + a.k) * a.H + c];
-  a.y[(size_t)t * a.H + c] = bad ? __builtin_nanf("") : acc;
-}
-
-template <int NG>
-hipError_t gateup_small_ng(const FfnArgs &a, hipStream_t st, int grid) {
-  const size_t lds = (size_t)a.S * a.H * sizeof(float) + (size_t)a.S * (a.H / kGroup) * sizeof(float);
-  ProfScope ps("gateup_small", st);
-  if (lds <= 48 * 1024)
-    hipLaunchKernelGGL((k_gateup_small<NG, true>), dim3(grid), dim3(kGuWaves * 64), lds, st, a);
-  else
-    hipLaunchKernelGGL((k_gateup_small<NG, false>), dim3(grid), dim3(kGuWaves * 64), 0, st, a);
-  return hipGetLastError();
+  for (int j = 0; j < a.k; ++j)
+    acc = fmaf(ldg<float>(a.w + t * a.k + j), ldg<float>(a.part + ((size_t)t * (a.k + 1) + j) * a.H + c), acc);
+  if (a.Is > 0) acc += ldg<float>(a.part + ((size_t)t * (a.k + 1) + a.k) * a.H + c);
+  stg<float>(a.y + (size_t)t * a.H + c, bad ? __builtin_nanf("") : acc);
 }
 
 int ceil_groups(int K) { return (K / kGroup + 63) / 64; }
 
 }  // namespace
 
-hipError_t launch_ffn_small(const FfnArgs &a, hipStream_t st) {
-  const int Umax = std::min(a.S * a.k, a.E);
-  const long tiles = (long)Umax * (a.I / kGuPairs) + a.Is / kGuPairs;
-  const int grid = (int)((tiles + kGuWaves - 1) / kGuWaves);
-  hipError_t e;
-  switch (ceil_groups(a.H)) {
-    case 1: e = gateup_small_ng<1>(a, st, grid); break;
-    case 2: e = gateup_small_ng<2>(a, st, grid); break;
-    case 3: e = gateup_small_ng<3>(a, st, grid); break;
-    default: e = gateup_small_ng<4>(a, st, grid); break;
-  }
-  if (e != hipSuccess) return e;
-  const int nw = std::min(Umax + 1, 16);
-  dim3 g2(a.H / kDnRows), b2(64 * nw);
-  ProfScope ps("down_small", st);
-  switch (ceil_groups(std::max(a.I, a.Is))) {
-    case 1: hipLaunchKernelGGL(k_down_small<1>, g2, b2, 0, st, a); break;
-    case 2: hipLaunchKernelGGL(k_down_small<2>, g2, b2, 0, st, a); break;
-    case 3: hipLaunchKernelGGL(k_down_small<3>, g2, b2, 0, st, a); break;
-    default: hipLaunchKernelGGL(k_down_small<4>, g2, b2, 0, st, a); break;
-  }
+hipError_t launch_to_limbs(const void *src, int src_bf16, int rows, int K, int src_stride, uint32_t *limbs,
+                           float *factors, hipStream_t st) {
+  const long n = (long)rows * (K / kGroup);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_to_limbs, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, src_bf16, rows, K,
+                     src_stride, limbs, factors);
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_large(const FfnArgs &a, hipStream_t st) {
+#define MOE_DISPATCH_NG(ng, KERNEL, GRID, BLOCK, LDS, ST, ...)                                          \
+  switch (ng) {                                                                                         \
+    case 1: hipLaunchKernelGGL((KERNEL<1 __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;   \
+    case 2: hipLaunchKernelGGL((KERNEL<2 __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;   \
+    case 3: hipLaunchKernelGGL((KERNEL<3 __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;   \
+    default: hipLaunchKernelGGL((KERNEL<4 __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;  \
+  }
+
+hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st) {
+  const int Imax = std::max(a.I, a.Is);
+  hipError_t e;
+  if (a.S == 1) {
+    {
+      ProfScope ps("gateup_s1", st);
+      const long feats = (long)a.k * a.I + a.Is;
+      const long waves = std::max<long>((long)a.n_cu * 8, (feats + kGuMaxPerWave - 1) / kGuMaxPerWave);
+      const dim3 g((unsigned)((waves + 3) / 4)), blk(256);
+      const size_t lds = (size_t)(a.H / kGroup) * 25 * sizeof(uint32_t);
+      MOE_DISPATCH_NG(ceil_groups(a.H), k_gateup_s1, g, blk, lds, st);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    const int NE = a.k + (a.Is > 0 ? 1 : 0);
+    const size_t hlds = (size_t)NE * (Imax / kGroup) * 25 * sizeof(uint32_t);
+    const bool in_lds = hlds <= 64 * 1024;
+    if (!in_lds) {
+      ProfScope ps("h_limbs", st);
+      e = launch_to_limbs(a.h, 0, NE, Imax, Imax, a.hl, a.hf, st);
+      if (e != hipSuccess) return e;
+    }
+    ProfScope ps("down_s1", st);
+    const dim3 g((unsigned)a.n_blk), blk(64 * std::min(NE, kDnS1Waves));
+    if (in_lds) {
+      MOE_DISPATCH_NG(ceil_groups(Imax), k_down_s1, g, blk, hlds, st, true);
+    } else {
+      MOE_DISPATCH_NG(ceil_groups(Imax), k_down_s1, g, blk, 0, st, false);
+    }
+    return hipGetLastError();
+  }
+  {
+    ProfScope ps("x_limbs", st);
+    e = launch_to_limbs(a.x, a.x_bf16, a.S, a.H, a.H, a.xl, a.xf, st);
+    if (e != hipSuccess) return e;
+  }
+  const int Umax = std::min(a.S * a.k, a.E);
+  {
+    ProfScope ps("gateup_small", st);
+    const long tiles = (long)Umax * (a.I / kGuPairs) + a.Is / kGuPairs;
+    const dim3 g((unsigned)((tiles + kGuWaves - 1) / kGuWaves)), blk(kGuWaves * 64);
+    MOE_DISPATCH_NG(ceil_groups(a.H), k_gateup_small, g, blk, 0, st);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    ProfScope ps("h_limbs", st);
+    e = launch_to_limbs(a.h, 0, a.S * (a.k + 1), Imax, Imax, a.hl, a.hf, st);
+    if (e != hipSuccess) return e;
+  }
+  ProfScope ps("down_small", st);
+  const int nw = std::min(Umax + 1, 16);
+  const dim3 g2(a.H / kDnRows), b2(64 * nw);
+  MOE_DISPATCH_NG(ceil_groups(Imax), k_down_small, g2, b2, 0, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st) {
+  const int Imax = std::max(a.I, a.Is);
+  hipError_t e;
+  {
+    ProfScope ps("x_limbs", st);
+    e = launch_to_limbs(a.x, a.x_bf16, a.S, a.H, a.H, a.xl, a.xf, st);
+    if (e != hipSuccess) return e;
+  }
   {
     ProfScope ps("bucket", st);
     hipLaunchKernelGGL(k_bucket, dim3(a.E), dim3(256), 0, st, a);
@@ -545,28 +841,27 @@ hipError_t launch_ffn_large(const FfnArgs &a, hipStream_t st) {
     ProfScope ps("schedule", st);
     hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), 0, st, a);
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long tiles_max = (long)a.max_items * (std::max(a.I, a.Is) / kGuPairs);
-  const int grid = (int)std::min<long>((tiles_max + 3) / 4, 8192);
-  ProfScope ps1("gateup_items", st);
-  switch (ceil_groups(a.H)) {
-    case 1: hipLaunchKernelGGL(k_gateup_items<1>, dim3(grid), dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(k_gateup_items<2>, dim3(grid), dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL(k_gateup_items<3>, dim3(grid), dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL(k_gateup_items<4>, dim3(grid), dim3(256), 0, st, a); break;
-  }
-  const long dtiles = (long)a.max_items * (a.H / kDnRows);
-  const int g2 = (int)std::min<long>((dtiles + 3) / 4, 8192);
-  ProfScope ps2("down_items", st);
-  switch (ceil_groups(std::max(a.I, a.Is))) {
-    case 1: hipLaunchKernelGGL(k_down_items<1>, dim3(g2), dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(k_down_items<2>, dim3(g2), dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL(k_down_items<3>, dim3(g2), dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL(k_down_items<4>, dim3(g2), dim3(256), 0, st, a); break;
+  {
+    ProfScope ps("gateup_items", st);
+    const long tiles_max = (long)a.max_items * (Imax / kGuPairs);
+    const dim3 g((unsigned)std::min<long>((tiles_max + 3) / 4, 8192)), blk(256);
+    MOE_DISPATCH_NG(ceil_groups(a.H), k_gateup_items, g, blk, 0, st);
   }
   {
-    ProfScope ps3("combine", st);
+    ProfScope ps("h_limbs", st);
+    e = launch_to_limbs(a.h, 0, a.S * (a.k + 1), Imax, Imax, a.hl, a.hf, st);
+    if (e != hipSuccess) return e;
+  }
+  {
+    ProfScope ps("down_items", st);
+    const long dtiles = (long)a.max_items * (a.H / kDnRows);
+    const dim3 g((unsigned)std::min<long>((dtiles + 3) / 4, 8192)), blk(256);
+    MOE_DISPATCH_NG(ceil_groups(Imax), k_down_items, g, blk, 0, st);
+  }
+  {
+    ProfScope ps("combine", st);
     hipLaunchKernelGGL(k_combine, dim3((a.H + 255) / 256, a.S), dim3(256), 0, st, a);
   }
   return hipGetLastError();

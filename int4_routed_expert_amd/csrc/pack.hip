@@ -1,10 +1,15 @@
 // Device-side packer: interchange format -> slot layout (see common.h).
-// One thread per (tile, 32-element group): 8 rows x 16 bytes of nibbles and the
-// 8 fp16 scales of that group.
+// One thread per (tile, 32-element group): 8 rows x 16 bytes of nibbles (turned
+// from offset binary into two's complement by flipping each nibble's top bit)
+// and the 8 fp16 scales of that group.
 #include "common.h"
 
 namespace moe {
 namespace {
+
+__device__ inline uint4 to_twos(uint4 v) {
+  return make_uint4(v.x ^ 0x88888888u, v.y ^ 0x88888888u, v.z ^ 0x88888888u, v.w ^ 0x88888888u);
+}
 
 __global__ __launch_bounds__(256) void k_pack(int H, int I, const uint8_t *qg, const uint16_t *sg, const uint8_t *qu,
                                               const uint16_t *su, const uint8_t *qd, const uint16_t *sd, uint8_t *dst) {
@@ -20,7 +25,7 @@ __global__ __launch_bounds__(256) void k_pack(int H, int I, const uint8_t *qg, c
       const int r = kGuPairs * t + i / 2;
       const uint8_t *q = (i & 1) ? qu : qg;
       const uint16_t *s = (i & 1) ? su : sg;
-      *(uint4 *)(tile + (size_t)i * (H / 2) + g * 16) = *(const uint4 *)(q + (size_t)r * (H / 2) + g * 16);
+      *(uint4 *)(tile + (size_t)i * (H / 2) + g * 16) = to_twos(*(const uint4 *)(q + (size_t)r * (H / 2) + g * 16));
       scl[g * kGuRows + i] = s[(size_t)r * ngh + g];
     }
   } else if (id < n_gu + n_dn) {
@@ -30,7 +35,7 @@ __global__ __launch_bounds__(256) void k_pack(int H, int I, const uint8_t *qg, c
     uint16_t *scl = (uint16_t *)(tile + (size_t)kDnRows * (I / 2));
     for (int i = 0; i < kDnRows; ++i) {
       const int r = kDnRows * t + i;
-      *(uint4 *)(tile + (size_t)i * (I / 2) + g * 16) = *(const uint4 *)(qd + (size_t)r * (I / 2) + g * 16);
+      *(uint4 *)(tile + (size_t)i * (I / 2) + g * 16) = to_twos(*(const uint4 *)(qd + (size_t)r * (I / 2) + g * 16));
       scl[g * kDnRows + i] = sd[(size_t)r * ngi + g];
     }
   }

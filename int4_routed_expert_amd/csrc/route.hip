@@ -33,24 +33,6 @@ __device__ inline double wave_sum_f64(double v) {
   return v;
 }
 
-__device__ inline unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    unsigned long long u = __shfl_xor(v, o);
-    v = u > v ? u : v;
-  }
-  return v;
-}
-
-// Order-preserving map of a finite float onto uint32, combined with an index so
-// that the larger key wins and, among equal keys, the lower index wins.
-__device__ inline unsigned long long rank_key(float f, int index) {
-  uint32_t b = __float_as_uint(f);
-  uint32_t s = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((unsigned long long)s << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)index);
-}
-__device__ inline int rank_index(unsigned long long r) { return (int)(0xFFFFFFFFu - (uint32_t)(r & 0xFFFFFFFFu)); }
-
 constexpr int kLogitTokens = 4;  // tokens per block in the logits kernel
 
 // One wave per expert row, kLogitTokens tokens per block: lanes stride over H in
@@ -85,68 +67,168 @@ __global__ __launch_bounds__(256) void k_route_logits(RouteArgs a) {
   }
 }
 
-// One wave per token.
-__global__ __launch_bounds__(64) void k_route_select(RouteArgs a) {
-  __shared__ float key[kMaxE];
+// Few tokens: one workgroup per expert, its 4 waves split H; all loads of a
+// lane are issued before the FMAs; partial sums meet in LDS in a fixed order.
+constexpr int kFewTokens = 8;
+__global__ __launch_bounds__(256) void k_route_logits_few(RouteArgs a) {
+  __shared__ double part[4][kFewTokens];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = blockIdx.x;
+  const int q = a.H / 4;  // each wave's share of H (H is a multiple of 32)
+  const float *wr = a.W + (size_t)e * a.H + (size_t)wave * q;
+  constexpr int kMaxChunks = 8;  // q / 256 <= 8 for H <= 8192
+  const int nch = q / 256;
+  float4 wv[kMaxChunks];
+#pragma unroll
+  for (int m = 0; m < kMaxChunks; ++m)
+    if (m < nch) wv[m] = *(const float4 *)(wr + m * 256 + lane * 4);
+  double acc[kFewTokens];
+#pragma unroll
+  for (int s = 0; s < kFewTokens; ++s) {
+    acc[s] = 0.0;
+    if (s < a.S) {
+      float4 xv[kMaxChunks];
+#pragma unroll
+      for (int m = 0; m < kMaxChunks; ++m) {
+        if (m < nch) {
+          const size_t base = (size_t)s * a.H + (size_t)wave * q + m * 256 + lane * 4;
+          if (a.x_bf16) {
+            const uint2 r = *(const uint2 *)((const uint16_t *)a.x + base);
+            xv[m] = make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u),
+                                __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xFFFF0000u));
+          } else {
+            xv[m] = *(const float4 *)((const float *)a.x + base);
+          }
+        }
+      }
+      double t = 0.0;
+#pragma unroll
+      for (int m = 0; m < kMaxChunks; ++m) {
+        if (m < nch) {
+          t = fma((double)wv[m].x, (double)xv[m].x, t);
+          t = fma((double)wv[m].y, (double)xv[m].y, t);
+          t = fma((double)wv[m].z, (double)xv[m].z, t);
+          t = fma((double)wv[m].w, (double)xv[m].w, t);
+        }
+      }
+      acc[s] = t;
+    }
+  }
+  for (int s = 0; s < a.S; ++s) {
+    const double v = wave_sum_f64(acc[s]);
+    if (lane == 0) part[wave][s] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < a.S) {
+    const int s = threadIdx.x;
+    a.logits[(size_t)s * a.E + e] = ((part[0][s] + part[1][s]) + part[2][s]) + part[3][s];
+  }
+}
+
+// One workgroup per token.  Selection by ranks instead of repeated arg-max:
+// an item's rank is the number of items that beat it (larger key, or equal key
+// and lower index), which is exactly its position in the tie-broken order.  The
+// kept groups' experts are first compacted (in expert order) so every rank is a
+// short unrolled scan of LDS.
+__global__ __launch_bounds__(256) void k_route_select(RouteArgs a) {
+  __shared__ __align__(16) float key[kMaxE];
+  __shared__ __align__(16) float ckey[kMaxE];
   __shared__ double sg[kMaxE];
-  __shared__ int keep[kMaxG];
-  const int t = blockIdx.x, lane = threadIdx.x;
+  __shared__ float gsc[kMaxG];
+  __shared__ int keep[kMaxG], before[kMaxG];
+  __shared__ int sel[kMaxK];
+  __shared__ double ssel[kMaxK];
+  const int t = blockIdx.x, tid = threadIdx.x;
   const int E = a.E, G = a.G, per = a.E / a.G;
   const double *l = a.logits + (size_t)t * E;
-  for (int e = lane; e < E; e += 64) {
+  for (int e = tid; e < E; e += blockDim.x) {
     const double s = 1.0 / (1.0 + exp(-l[e]));
     sg[e] = s;
     key[e] = __double2float_rn(s + (double)a.bias[e]);
   }
   __syncthreads();
-  // group scores: lane j scores group j
-  unsigned long long gk = 0;
-  if (lane < G) {
+  // group score: sum of the group's two largest keys
+  for (int j = tid; j < G; j += blockDim.x) {
     float k1 = -INFINITY, k2 = -INFINITY;
-    for (int e = lane * per; e < (lane + 1) * per; ++e) {
-      const float v = key[e];
-      if (v > k1) { k2 = k1; k1 = v; }
-      else if (v > k2) { k2 = v; }
+    if ((per & 3) == 0) {
+      const float4 *p = (const float4 *)(key + j * per);
+#pragma unroll 4
+      for (int m = 0; m < per / 4; ++m) {
+        const float4 v4 = p[m];
+        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float v = vv[c];
+          if (v > k1) { k2 = k1; k1 = v; }
+          else if (v > k2) { k2 = v; }
+        }
+      }
+    } else {
+      for (int e = j * per; e < (j + 1) * per; ++e) {
+        const float v = key[e];
+        if (v > k1) { k2 = k1; k1 = v; }
+        else if (v > k2) { k2 = v; }
+      }
     }
-    const float score = per == 1 ? k1 : __double2float_rn((double)k1 + (double)k2);
-    gk = rank_key(score, lane);
+    gsc[j] = per == 1 ? k1 : __double2float_rn((double)k1 + (double)k2);
   }
-  bool kept = false;
-  for (int it = 0; it < a.Gk; ++it) {
-    const unsigned long long m = wave_max_u64(kept ? 0ull : gk);
-    if (lane < G && gk == m) kept = true;
-  }
-  if (lane < G) keep[lane] = kept ? 1 : 0;
   __syncthreads();
-  // candidate keys, up to kMaxE / 64 per lane
-  constexpr int kPer = kMaxE / 64;
-  unsigned long long ck[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int e = lane + 64 * j;
-    ck[j] = (e < E && keep[e / per]) ? rank_key(key[e], e) : 0ull;
+  // keep the topk_group best groups (ties: lower group index)
+  for (int j = tid; j < G; j += blockDim.x) {
+    const float v = gsc[j];
+    int r = 0;
+    for (int i = 0; i < G; ++i) r += (gsc[i] > v || (gsc[i] == v && i < j)) ? 1 : 0;
+    keep[j] = r < a.Gk;
   }
-  int my_idx[kMaxK];
-  for (int it = 0; it < a.k; ++it) {
-    unsigned long long loc = 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) loc = ck[j] > loc ? ck[j] : loc;
-    const unsigned long long m = wave_max_u64(loc);
-    const int e = rank_index(m);
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (ck[j] == m) ck[j] = 0ull;
-    my_idx[it] = e;
+  __syncthreads();
+  for (int j = tid; j < G; j += blockDim.x) {
+    int b = 0;
+    for (int i = 0; i < j; ++i) b += keep[i];
+    before[j] = b;
   }
-  if (lane == 0) {
-    double denom = 0.0;
-    for (int it = 0; it < a.k; ++it) denom += sg[my_idx[it]];
-    for (int it = 0; it < a.k; ++it) {
-      const double s = sg[my_idx[it]];
-      const double wv = a.norm ? s / denom * (double)a.rsf : s * (double)a.rsf;
-      a.idx[(size_t)t * a.k + it] = my_idx[it];
-      a.w[(size_t)t * a.k + it] = (float)wv;
+  __syncthreads();
+  // candidates in expert order
+  for (int e = tid; e < E; e += blockDim.x) {
+    const int j = e / per;
+    if (keep[j]) ckey[before[j] * per + (e - j * per)] = key[e];
+  }
+  const int nc = a.Gk * per;
+  for (int p = nc + tid; p < ((nc + 3) & ~3); p += blockDim.x) ckey[p] = -INFINITY;
+  __syncthreads();
+  // rank of each candidate (ties: lower position = lower expert index)
+  for (int p = tid; p < nc; p += blockDim.x) {
+    const float v = ckey[p];
+    int r = 0;
+    const float4 *c4 = (const float4 *)ckey;
+#pragma unroll 8
+    for (int m = 0; m < (nc + 3) / 4; ++m) {
+      const float4 w4 = c4[m];
+      const int q = 4 * m;
+      r += (w4.x > v || (w4.x == v && q < p)) ? 1 : 0;
+      r += (w4.y > v || (w4.y == v && q + 1 < p)) ? 1 : 0;
+      r += (w4.z > v || (w4.z == v && q + 2 < p)) ? 1 : 0;
+      r += (w4.w > v || (w4.w == v && q + 3 < p)) ? 1 : 0;
     }
+    if (r < a.k) {
+      // position p -> expert index: p-th candidate in the kept groups, in order
+      const int kg = p / per;  // kg-th kept group
+      int j = 0;
+      for (int c = 0; j < G; ++j)
+        if (keep[j] && c++ == kg) break;
+      const int e = j * per + (p - kg * per);
+      sel[r] = e;
+      ssel[r] = sg[e];
+    }
+  }
+  __syncthreads();
+  // weights: un-biased sigmoid, renormalised over the selection (summed in rank order), scaled
+  if (tid < a.k) {
+    double denom = 0.0;
+    for (int it = 0; it < a.k; ++it) denom += ssel[it];
+    const double s = ssel[tid];
+    const double wv = a.norm ? s / denom * (double)a.rsf : s * (double)a.rsf;
+    a.idx[(size_t)t * a.k + tid] = sel[tid];
+    a.w[(size_t)t * a.k + tid] = (float)wv;
   }
 }
 
@@ -154,16 +236,20 @@ __global__ __launch_bounds__(64) void k_route_select(RouteArgs a) {
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
   if (a.S == 0) return hipSuccess;
-  dim3 grid((a.E + 3) / 4, (a.S + kLogitTokens - 1) / kLogitTokens);
   {
     ProfScope ps("route_logits", st);
-    hipLaunchKernelGGL(k_route_logits, grid, dim3(256), 0, st, a);
+    if (a.S <= kFewTokens && a.H % 1024 == 0) {
+      hipLaunchKernelGGL(k_route_logits_few, dim3(a.E), dim3(256), 0, st, a);
+    } else {
+      dim3 grid((a.E + 3) / 4, (a.S + kLogitTokens - 1) / kLogitTokens);
+      hipLaunchKernelGGL(k_route_logits, grid, dim3(256), 0, st, a);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     ProfScope ps("route_select", st);
-    hipLaunchKernelGGL(k_route_select, dim3(a.S), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(k_route_select, dim3(a.S), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }

@@ -77,15 +77,17 @@ def test_host_pack_round_trip_and_layout(shape):
     M.moe_unpack_expert(c, shape.moe_inter, dst, *out.parts())
     for a, b in zip(ex.parts(), out.parts()):
         assert np.array_equal(a, b)
-    # documented layout, re-derived: gate/up tiles of 8 rows (g r, u r for 4 r), then scales [group][8]
+    # documented layout, re-derived: gate/up tiles of 8 rows (g r, u r for 4 r), then scales [group][8];
+    # nibbles hold the int4 value in two's complement (interchange nibble with its top bit flipped)
     H, I = shape.hidden, shape.moe_inter
+    tw = lambda q: q ^ np.uint8(0x88)
     tile = 8 * (H // 2) + (H // 32) * 8 * 2
     for t in range(I // 4):
         base = t * tile
         for i in range(8):
             src = ex.qu if i % 2 else ex.qg
             r = 4 * t + i // 2
-            assert np.array_equal(dst[base + i * (H // 2): base + (i + 1) * (H // 2)], src[r])
+            assert np.array_equal(dst[base + i * (H // 2): base + (i + 1) * (H // 2)], tw(src[r]))
         scl = dst[base + 8 * (H // 2): base + tile].view(np.uint16).reshape(H // 32, 8)
         for i in range(8):
             s = ex.su if i % 2 else ex.sg
@@ -95,7 +97,7 @@ def test_host_pack_round_trip_and_layout(shape):
     for t in range(H // 8):
         base = d0 + t * dtile
         for i in range(8):
-            assert np.array_equal(dst[base + i * (I // 2): base + (i + 1) * (I // 2)], ex.qd[8 * t + i])
+            assert np.array_equal(dst[base + i * (I // 2): base + (i + 1) * (I // 2)], tw(ex.qd[8 * t + i]))
         scl = dst[base + 8 * (I // 2): base + dtile].view(np.uint16).reshape(I // 32, 8)
         assert np.array_equal(scl.T, ex.sd[8 * t: 8 * t + 8])
     assert np.all(dst[d0 + (H // 8) * dtile:] == 0)
