@@ -143,6 +143,41 @@ int moe_route(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, con
 int moe_ffn(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, const int32_t *idx, const float *w,
             const moe_slot_view *experts, const void *shared, float *y, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- HBM expert-slot pool ([PORT] N3 and G3 status; [README] per-layer LRU) ----
+ * One device slab of n_layers * slots_per_layer slots of moe_expert_bytes(cfg,
+ * moe_inter) bytes, a device table per layer (table[e] = slot, or -1), and a
+ * host-side LRU per layer.  The packed experts live in caller-owned host memory
+ * (pinned: hipHostMalloc) registered with moe_pool_register_host.
+ *
+ * moe_pool_acquire(layer, idx[n]) takes the union of the experts named by idx
+ * (host memory, n entries, e.g. S*k routing results copied back), leases the
+ * resident ones, and for each miss takes a free slot or evicts the least recently
+ * used unleased slot of the layer (ties: lowest slot).  Miss copies are enqueued
+ * on `side` after the victim slot's previous consumer has finished; the layer's
+ * table is updated on `compute` after the copies completed, so a kernel on
+ * `compute` never sees a partially filled slot.  view_out then addresses the
+ * layer (pass it to moe_ffn on `compute`).  Each acquire must be followed by
+ * moe_pool_release(layer, compute) after the consuming work is enqueued; it
+ * records the consumer-done event of every leased slot.
+ * Errors: MOE_ENOSLOT (union larger than slots_per_layer), MOE_ESTALE (acquire
+ * of a layer with an unreleased lease, or release without acquire), MOE_ENULL
+ * (a missing expert has no registered host source), MOE_EINVAL (bad layer or
+ * expert id).  All calls on one pool must come from one host thread. */
+typedef struct moe_pool moe_pool;
+enum { MOE_POOL_NO_DEVICE = 1, /* policy only: no device memory, no copies (host tests) */
+       MOE_POOL_POISON = 2 /* overwrite a slot with 0xFF bytes before refilling it (ordering tests) */ };
+int moe_pool_create(const moe_cfg *cfg, int32_t n_layers, int32_t slots_per_layer, int32_t flags, moe_pool **out);
+void moe_pool_destroy(moe_pool *pool);
+int moe_pool_register_host(moe_pool *pool, int32_t layer, int32_t expert, const void *packed_host_src);
+int moe_pool_acquire(moe_pool *pool, int32_t layer, const int32_t *idx_host, int32_t n, moe_slot_view *view_out,
+                     int32_t *n_miss_out, void *compute_stream, void *side_stream);
+int moe_pool_release(moe_pool *pool, int32_t layer, void *compute_stream);
+/* The last acquire's decisions as (expert, slot, hit) triples in out[3 * i ..];
+ * returns the number of triples, or a negative status (cap too small). */
+int moe_pool_trace(const moe_pool *pool, int32_t *out, int32_t cap);
+/* {"acquires", "hits", "misses", "evictions", "fill_bytes", ...} as JSON. */
+int moe_pool_stats(const moe_pool *pool, char *out_json, size_t cap);
+
 /* Timing instrumentation (not part of the layer's computation).  While enabled,
  * the library brackets each kernel it launches with two hipEvents recorded on the
  * launch stream.  moe_profile_report waits for the recorded events, writes

@@ -13,8 +13,10 @@ namespace moe {
 
 static thread_local std::string g_last_hip_error = "no error";
 
+void set_hip_error(hipError_t e) { g_last_hip_error = hipGetErrorString(e); }
+
 static int hip_fail(hipError_t e) {
-  g_last_hip_error = hipGetErrorString(e);
+  set_hip_error(e);
   return MOE_EHIP;
 }
 

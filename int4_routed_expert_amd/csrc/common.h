@@ -87,6 +87,9 @@ struct ProfScope {
   ~ProfScope() { if (prof_on()) prof_end(st); }
 };
 
+// Keeps a failed HIP call's message for moe_last_hip_error().
+void set_hip_error(hipError_t e);
+
 // ---- launchers (host) --------------------------------------------------------
 hipError_t launch_route(const RouteArgs &a, hipStream_t st);
 hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st);  // S <= kSmallS

@@ -1,0 +1,278 @@
+// HBM expert-slot pool: a per-layer LRU cache of packed experts in one device
+// slab, filled from pinned host memory on a side stream.
+//
+// Source: "GLM-5.2 on a 32 GB Mac - native MLX port of the Colibri hierarchy",
+// N3 (explicit residency manager: resident / loading / in-use states, no reuse
+// of a slot before its consumer completes, never publish a partially filled
+// slot), "G3 implementation status" (fixed per-layer LRU slots, deterministic
+// LRU ties, batch union, resident work submitted before miss reads); the
+// colibri README "What's implemented" (per-layer LRU of streamed experts); the
+// strata audit's slot map (residency changes by writing one table entry).
+//
+// Per layer the pool owns `slots_per_layer` slots and a device table
+// table[e] = slot or -1.  acquire() resolves the union of the experts named by a
+// routing: hits are leased, misses take a free slot or evict the least recently
+// used unleased slot (ties: the lowest slot), are copied from the registered host
+// source on the side stream after the victim's last consumer has finished, and
+// are published in the device table on the compute stream only after their copy
+// completed (the compute stream waits on the copy's event).  release() records
+// the consumer-done event of every leased slot.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+using namespace moe;
+
+struct moe_pool {
+  moe_cfg cfg;
+  int n_layers = 0, spl = 0;  // slots per layer
+  int E = 0;
+  int64_t slot_bytes = 0;
+  bool device = true;
+  bool poison = false;
+  uint8_t *slab = nullptr;        // device: n_layers * spl slots
+  int32_t *d_tables = nullptr;    // device: [n_layers][E]
+  int32_t *h_stage = nullptr;     // pinned: [n_layers][E] staging for table uploads
+  std::vector<hipEvent_t> table_ev;  // per layer: staging buffer's last upload
+  std::vector<int32_t> table;     // host mirror [n_layers][E]
+  std::vector<const void *> src;  // [n_layers][E] pinned host sources
+  struct Slot {
+    int expert = -1;
+    uint64_t last_use = 0;  // LRU clock of the last acquire
+    uint64_t gen = 0;       // fills of this slot so far
+    bool leased = false;
+    hipEvent_t done = nullptr;  // consumer-done event (valid when used)
+    bool has_done = false;
+  };
+  std::vector<Slot> slots;  // [n_layers][spl]
+  std::vector<int> leased_layer;  // per layer: number of slots leased by the open acquire, -1 none
+  std::vector<std::vector<int>> lease_list;
+  std::vector<hipEvent_t> ev_pool;
+  uint64_t clock = 0;
+  // statistics
+  uint64_t hits = 0, misses = 0, evictions = 0, fill_bytes = 0, acquires = 0;
+  std::vector<int32_t> trace;  // last acquire: (expert, slot, hit) triples
+};
+
+static hipEvent_t get_event(moe_pool *p) {
+  if (!p->ev_pool.empty()) {
+    hipEvent_t e = p->ev_pool.back();
+    p->ev_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
+  return e;
+}
+
+extern "C" {
+
+int moe_pool_create(const moe_cfg *cfg, int32_t n_layers, int32_t slots_per_layer, int32_t flags, moe_pool **out) {
+  if (!out) return MOE_ENULL;
+  *out = nullptr;
+  int v = moe_validate_cfg(cfg);
+  if (v) return v;
+  if (n_layers < 1 || slots_per_layer < 1 || (flags & ~3)) return MOE_EINVAL;
+  moe_pool *p = new moe_pool();
+  p->cfg = *cfg;
+  p->n_layers = n_layers;
+  p->spl = slots_per_layer;
+  p->E = cfg->n_experts;
+  p->slot_bytes = moe_expert_bytes(cfg, cfg->moe_inter);
+  p->device = !(flags & MOE_POOL_NO_DEVICE);
+  p->poison = (flags & MOE_POOL_POISON) != 0;
+  p->table.assign((size_t)n_layers * p->E, -1);
+  p->src.assign((size_t)n_layers * p->E, nullptr);
+  p->slots.resize((size_t)n_layers * slots_per_layer);
+  p->leased_layer.assign(n_layers, -1);
+  p->lease_list.resize(n_layers);
+  if (p->device) {
+    const size_t slab = (size_t)n_layers * slots_per_layer * (size_t)p->slot_bytes;
+    hipError_t e = hipMalloc(&p->slab, slab);
+    if (e == hipSuccess) e = hipMalloc(&p->d_tables, (size_t)n_layers * p->E * sizeof(int32_t));
+    if (e == hipSuccess) e = hipHostMalloc(&p->h_stage, (size_t)n_layers * p->E * sizeof(int32_t), hipHostMallocDefault);
+    if (e == hipSuccess) e = hipMemset(p->d_tables, 0xFF, (size_t)n_layers * p->E * sizeof(int32_t));  // all -1
+    if (e == hipSuccess) {
+      p->table_ev.assign(n_layers, nullptr);
+      for (int l = 0; l < n_layers && e == hipSuccess; ++l) e = hipEventCreateWithFlags(&p->table_ev[l], hipEventDisableTiming);
+    }
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      moe_pool_destroy(p);
+      return MOE_EHIP;
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+void moe_pool_destroy(moe_pool *p) {
+  if (!p) return;
+  if (p->device) (void)hipDeviceSynchronize();
+  for (auto &s : p->slots)
+    if (s.done) (void)hipEventDestroy(s.done);
+  for (auto e : p->ev_pool) (void)hipEventDestroy(e);
+  for (auto e : p->table_ev)
+    if (e) (void)hipEventDestroy(e);
+  if (p->slab) (void)hipFree(p->slab);
+  if (p->d_tables) (void)hipFree(p->d_tables);
+  if (p->h_stage) (void)hipHostFree(p->h_stage);
+  delete p;
+}
+
+int moe_pool_register_host(moe_pool *p, int32_t layer, int32_t expert, const void *src) {
+  if (!p || !src) return MOE_ENULL;
+  if (layer < 0 || layer >= p->n_layers || expert < 0 || expert >= p->E) return MOE_EINVAL;
+  p->src[(size_t)layer * p->E + expert] = src;
+  return MOE_OK;
+}
+
+int moe_pool_acquire(moe_pool *p, int32_t layer, const int32_t *idx, int32_t n, moe_slot_view *view,
+                     int32_t *n_miss, void *compute, void *side) {
+  if (!p || !view || (n > 0 && !idx)) return MOE_ENULL;
+  if (layer < 0 || layer >= p->n_layers || n < 0) return MOE_EINVAL;
+  if (p->leased_layer[layer] >= 0) return MOE_ESTALE;  // previous lease of this layer not released
+  // union of the named experts, in first-appearance order
+  std::vector<int> uniq;
+  for (int i = 0; i < n; ++i) {
+    const int e = idx[i];
+    if (e < 0 || e >= p->E) return MOE_EINVAL;
+    if (std::find(uniq.begin(), uniq.end(), e) == uniq.end()) uniq.push_back(e);
+  }
+  if ((int)uniq.size() > p->spl) return MOE_ENOSLOT;
+  for (int e : uniq)
+    if (p->table[(size_t)layer * p->E + e] < 0 && !p->src[(size_t)layer * p->E + e]) return MOE_ENULL;
+  moe_pool::Slot *base = &p->slots[(size_t)layer * p->spl];
+  int32_t *tab = &p->table[(size_t)layer * p->E];
+  ++p->acquires;
+  const uint64_t now = ++p->clock;
+  p->trace.clear();
+  std::vector<int> leased;
+  // hits first: lease them so that misses cannot evict them
+  for (int e : uniq) {
+    const int s = tab[e];
+    if (s >= 0) {
+      base[s].leased = true;
+      base[s].last_use = now;
+      leased.push_back(s);
+      ++p->hits;
+      p->trace.insert(p->trace.end(), {e, s, 1});
+    }
+  }
+  std::vector<std::pair<int, int>> fills;  // (expert, slot)
+  for (int e : uniq) {
+    if (tab[e] >= 0) continue;
+    int victim = -1;
+    for (int s = 0; s < p->spl; ++s)  // free slot first (lowest), else least recently used unleased (ties: lowest)
+      if (base[s].expert < 0 && !base[s].leased) { victim = s; break; }
+    if (victim < 0)
+      for (int s = 0; s < p->spl; ++s)
+        if (!base[s].leased && (victim < 0 || base[s].last_use < base[victim].last_use)) victim = s;
+    if (victim < 0) return MOE_ENOSLOT;  // cannot happen: uniq <= spl
+    if (base[victim].expert >= 0) {
+      tab[base[victim].expert] = -1;
+      ++p->evictions;
+    }
+    base[victim].expert = e;
+    base[victim].leased = true;
+    base[victim].last_use = now;
+    base[victim].gen += 1;
+    tab[e] = victim;
+    leased.push_back(victim);
+    fills.emplace_back(e, victim);
+    ++p->misses;
+    p->trace.insert(p->trace.end(), {e, victim, 0});
+  }
+  p->leased_layer[layer] = (int)leased.size();
+  p->lease_list[layer] = leased;
+  if (n_miss) *n_miss = (int32_t)fills.size();
+  view->base = p->slab + (size_t)layer * p->spl * (size_t)p->slot_bytes;
+  view->slot_bytes = p->slot_bytes;
+  view->table = p->d_tables ? p->d_tables + (size_t)layer * p->E : nullptr;
+  view->n_slots = p->spl;
+  if (!p->device) return MOE_OK;
+  hipStream_t cs = (hipStream_t)compute, ss = (hipStream_t)side;
+  hipError_t err = hipSuccess;
+  for (auto &f : fills) {
+    moe_pool::Slot &sl = base[f.second];
+    uint8_t *dst = p->slab + ((size_t)layer * p->spl + f.second) * (size_t)p->slot_bytes;
+    if (sl.has_done) err = hipStreamWaitEvent(ss, sl.done, 0);  // previous consumer of the victim is done
+    if (err == hipSuccess && p->poison) err = hipMemsetAsync(dst, 0xFF, (size_t)p->slot_bytes, ss);
+    if (err == hipSuccess)
+      err = hipMemcpyAsync(dst, p->src[(size_t)layer * p->E + f.first], (size_t)p->slot_bytes, hipMemcpyHostToDevice, ss);
+    p->fill_bytes += (uint64_t)p->slot_bytes;
+    if (err != hipSuccess) break;
+  }
+  if (err == hipSuccess && !fills.empty()) {
+    hipEvent_t filled = get_event(p);
+    if (!filled) err = hipErrorOutOfMemory;
+    if (err == hipSuccess) err = hipEventRecord(filled, ss);
+    if (err == hipSuccess) err = hipStreamWaitEvent(cs, filled, 0);  // publish only complete slots
+    if (filled) p->ev_pool.push_back(filled);  // reusable: the wait has captured its state
+  }
+  if (err == hipSuccess && !fills.empty()) {  // the table changed: upload it on the compute stream
+    int32_t *stage = p->h_stage + (size_t)layer * p->E;
+    err = hipEventSynchronize(p->table_ev[layer]);  // the staging buffer's previous upload is complete
+    if (err == hipSuccess) {
+      std::memcpy(stage, tab, sizeof(int32_t) * p->E);
+      err = hipMemcpyAsync(p->d_tables + (size_t)layer * p->E, stage, sizeof(int32_t) * p->E, hipMemcpyHostToDevice, cs);
+    }
+    if (err == hipSuccess) err = hipEventRecord(p->table_ev[layer], cs);
+  }
+  if (err != hipSuccess) {
+    set_hip_error(err);
+    return MOE_EHIP;
+  }
+  return MOE_OK;
+}
+
+int moe_pool_release(moe_pool *p, int32_t layer, void *compute) {
+  if (!p) return MOE_ENULL;
+  if (layer < 0 || layer >= p->n_layers) return MOE_EINVAL;
+  if (p->leased_layer[layer] < 0) return MOE_ESTALE;
+  moe_pool::Slot *base = &p->slots[(size_t)layer * p->spl];
+  hipError_t err = hipSuccess;
+  for (int s : p->lease_list[layer]) {
+    base[s].leased = false;
+    if (p->device && err == hipSuccess) {
+      if (!base[s].done) err = hipEventCreateWithFlags(&base[s].done, hipEventDisableTiming);
+      if (err == hipSuccess) err = hipEventRecord(base[s].done, (hipStream_t)compute);
+      base[s].has_done = err == hipSuccess;
+    }
+  }
+  p->leased_layer[layer] = -1;
+  p->lease_list[layer].clear();
+  if (err != hipSuccess) {
+    set_hip_error(err);
+    return MOE_EHIP;
+  }
+  return MOE_OK;
+}
+
+int moe_pool_trace(const moe_pool *p, int32_t *out, int32_t cap) {
+  if (!p || !out) return MOE_ENULL;
+  const int n = (int)p->trace.size() / 3;
+  if (cap < n * 3) return MOE_EINVAL;
+  std::memcpy(out, p->trace.data(), sizeof(int32_t) * p->trace.size());
+  return n;
+}
+
+int moe_pool_stats(const moe_pool *p, char *out, size_t cap) {
+  if (!p || !out) return MOE_ENULL;
+  char buf[512];
+  const int len = std::snprintf(buf, sizeof buf,
+                                "{\"acquires\": %llu, \"hits\": %llu, \"misses\": %llu, \"evictions\": %llu, "
+                                "\"fill_bytes\": %llu, \"slots_per_layer\": %d, \"layers\": %d, \"slot_bytes\": %lld}",
+                                (unsigned long long)p->acquires, (unsigned long long)p->hits,
+                                (unsigned long long)p->misses, (unsigned long long)p->evictions,
+                                (unsigned long long)p->fill_bytes, p->spl, p->n_layers, (long long)p->slot_bytes);
+  if (len < 0 || (size_t)len + 1 > cap) return MOE_EINVAL;
+  std::memcpy(out, buf, (size_t)len + 1);
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -56,6 +56,13 @@ def _load():
         "moe_unpack_expert": (ctypes.c_int, [cp, i32, p, p, p, p, p, p, p]),
         "moe_route": (ctypes.c_int, [cp, p, i32, i32, p, p, p, p, p, sz, p]),
         "moe_ffn": (ctypes.c_int, [cp, p, i32, i32, p, p, ctypes.POINTER(moe_slot_view), p, p, p, sz, p]),
+        "moe_pool_create": (ctypes.c_int, [cp, i32, i32, i32, ctypes.POINTER(p)]),
+        "moe_pool_destroy": (None, [p]),
+        "moe_pool_register_host": (ctypes.c_int, [p, i32, i32, p]),
+        "moe_pool_acquire": (ctypes.c_int, [p, i32, p, i32, ctypes.POINTER(moe_slot_view), ctypes.POINTER(i32), p, p]),
+        "moe_pool_release": (ctypes.c_int, [p, i32, p]),
+        "moe_pool_trace": (ctypes.c_int, [p, p, i32]),
+        "moe_pool_stats": (ctypes.c_int, [p, ctypes.c_char_p, sz]),
         "moe_profile_enable": (ctypes.c_int, [ctypes.c_int]),
         "moe_profile_report": (ctypes.c_int, [ctypes.c_char_p, sz]),
     }
@@ -151,6 +158,62 @@ def moe_profile_report() -> dict:
     buf = ctypes.create_string_buffer(1 << 16)
     _check(_lib.moe_profile_report(buf, len(buf)), "moe_profile_report")
     return {k: (v[0], v[1]) for k, v in json.loads(buf.value.decode()).items()}
+
+
+MOE_POOL_NO_DEVICE, MOE_POOL_POISON = 1, 2
+
+
+class Pool:
+    """Owner of a moe_pool handle (the C calls, with errors raised as MoeError)."""
+
+    def __init__(self, cfg: moe_cfg, n_layers: int, slots_per_layer: int, flags: int = 0):
+        self.h = ctypes.c_void_p()
+        _check(_lib.moe_pool_create(ctypes.byref(cfg), n_layers, slots_per_layer, flags, ctypes.byref(self.h)),
+               "moe_pool_create")
+
+    def register_host(self, layer: int, expert: int, src) -> None:
+        _check(_lib.moe_pool_register_host(self.h, layer, expert, ptr(src)), "moe_pool_register_host")
+
+    def acquire(self, layer: int, idx_host, compute=None, side=None):
+        """-> (moe_slot_view, n_miss); idx_host: int32 numpy array."""
+        import numpy as np
+        idx = np.ascontiguousarray(idx_host, np.int32).ravel()
+        view = moe_slot_view()
+        n_miss = ctypes.c_int32(0)
+        c = stream_handle(compute) if compute is not None or side is not None else None
+        s_ = stream_handle(side) if side is not None else c
+        _check(_lib.moe_pool_acquire(self.h, layer, idx.ctypes.data, idx.size, ctypes.byref(view), ctypes.byref(n_miss),
+                                     c, s_), "moe_pool_acquire")
+        return view, n_miss.value
+
+    def release(self, layer: int, compute=None) -> None:
+        c = stream_handle(compute) if compute is not None else None
+        _check(_lib.moe_pool_release(self.h, layer, c), "moe_pool_release")
+
+    def trace(self):
+        import numpy as np
+        out = np.zeros(3 * 4096, np.int32)
+        n = _lib.moe_pool_trace(self.h, out.ctypes.data, out.size)
+        if n < 0:
+            raise MoeError(n, "moe_pool_trace")
+        return [tuple(out[3 * i:3 * i + 3]) for i in range(n)]
+
+    def stats(self) -> dict:
+        import json
+        buf = ctypes.create_string_buffer(1024)
+        _check(_lib.moe_pool_stats(self.h, buf, len(buf)), "moe_pool_stats")
+        return json.loads(buf.value.decode())
+
+    def close(self) -> None:
+        if self.h:
+            _lib.moe_pool_destroy(self.h)
+            self.h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def slot_view(base, slot_bytes: int, table, n_slots: int) -> moe_slot_view:

@@ -1,0 +1,90 @@
+"""Slot pool on the GPU: a stack of layers decoded token by token with experts
+streamed from pinned host memory into a small per-layer LRU of HBM slots.  Every
+(step, layer) is checked against the fp64 oracle (indices exact, outputs within
+2e-3); with poisoning on, every refilled slot is first overwritten with 0xFF
+bytes on the side stream, so any read of a slot outside its published lifetime
+would corrupt an output."""
+import numpy as np
+import pytest
+import torch
+
+from gen import inputs as gen
+from int4_routed_expert_amd import moe as M
+from oracle import oracle as O
+from tests.devlayer import dev, max_rel_err
+
+pytestmark = pytest.mark.gpu
+
+MID = gen.LayerConfig(hidden=512, n_experts=32, n_group=4, topk_group=2, top_k=4, moe_inter=256, shared_inter=192)
+
+
+def run_stack(w: gen.Workload, n_layers: int, steps: int, spl: int, flags: int, check_ffn_every: int = 1):
+    c = w.cfg
+    cfg = M.make_cfg(c)
+    E, I = c.n_experts, c.moe_inter
+    sb = M.moe_expert_bytes(cfg, I)
+    host = torch.empty((n_layers * E, sb), dtype=torch.uint8, pin_memory=True)
+    hostw = {}
+    for l in range(n_layers):
+        for e in range(E):
+            ex = gen.expert_weights(w, l, e)
+            hostw[(l, e)] = ex
+            M.moe_pack_expert(cfg, I, *ex.parts(), host[l * E + e].numpy(), 0)
+    pool = M.Pool(cfg, n_layers, spl, flags)
+    for l in range(n_layers):
+        for e in range(E):
+            pool.register_host(l, e, host[l * E + e])
+    layers = []
+    for l in range(n_layers):
+        sh = gen.expert_weights(w, l, E)
+        shared = torch.zeros(M.moe_expert_bytes(cfg, c.shared_inter), dtype=torch.uint8, device="cuda")
+        M.moe_pack_expert(cfg, c.shared_inter, *[dev(a) for a in sh.parts()], shared, 1)
+        layers.append(dict(W=gen.router_weights(w, l), b=gen.router_bias(w, l), shared=shared, shared_h=sh))
+    torch.cuda.synchronize()
+    compute = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    ws = torch.empty(M.moe_workspace_bytes(cfg, 1), dtype=torch.uint8, device="cuda")
+    worst, n_checked = 0.0, 0
+    for step in range(steps):
+        for l in range(n_layers):
+            L = layers[l]
+            xh = gen.tokens(w, layer=l, step=step)
+            x = dev(xh)
+            idx = torch.empty((1, c.top_k), dtype=torch.int32, device="cuda")
+            wt = torch.empty((1, c.top_k), dtype=torch.float32, device="cuda")
+            M.moe_route(cfg, x, M.MOE_F32, 1, dev(L["W"]), dev(L["b"]), idx, wt, ws, ws.numel())
+            idx_h = idx.cpu().numpy()  # the host decides residency: one sync per layer
+            view, n_miss = pool.acquire(l, idx_h, compute, side)
+            y = torch.full((1, c.hidden), float("nan"), device="cuda")
+            M.moe_ffn(cfg, x, M.MOE_F32, 1, idx, wt, view, L["shared"], y, ws, ws.numel())
+            pool.release(l, compute)
+            ridx, rw, _, flags_, _ = O.route(c, xh, L["W"], L["b"])
+            assert not flags_.any()
+            assert np.array_equal(idx_h, ridx), (step, l)
+            if (step * n_layers + l) % check_ffn_every == 0:
+                experts = {e: hostw[(l, e)] for e in ridx.ravel().tolist()}
+                experts[E] = L["shared_h"]
+                ref = O.moe_ffn(c, xh, ridx, rw, experts)
+                err = max_rel_err(y.cpu().numpy(), ref)
+                worst = max(worst, err)
+                n_checked += 1
+                assert err <= 2e-3, (step, l, err)
+    torch.cuda.synchronize()
+    st = pool.stats()
+    pool.close()
+    return st, worst, n_checked
+
+
+@pytest.mark.parametrize("flags", [0, M.MOE_POOL_POISON])
+def test_pool_stack_mid_shape_heavy_churn(flags):
+    w = gen.Workload("stack-mid", MID, tokens=1, bias_recipe="hotset", layers=6, steps=8, seed=41)
+    st, worst, n = run_stack(w, n_layers=6, steps=8, spl=5, flags=flags)
+    print("pool stats", st, "worst", worst, "checked", n, flush=True)
+    assert st["misses"] > 6 * 4 and st["evictions"] > 0 and st["hits"] > 0
+
+
+def test_pool_stack_glm_shape():
+    w = gen.WORKLOADS["stack"]
+    st, worst, n = run_stack(w, n_layers=2, steps=3, spl=12, flags=M.MOE_POOL_POISON, check_ffn_every=2)
+    print("pool stats", st, "worst", worst, "checked", n, flush=True)
+    assert st["evictions"] >= 0 and st["misses"] >= 16
