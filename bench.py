@@ -31,7 +31,86 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_source_hash() -> str:
+    """sha256 over the sources of the decode kernels (counter readings go stale when they change)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("ffn_gemv.hip", "dot.h", "common.h"):
+        with open(os.path.join(ROOT, "int4_routed_expert_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when
+    the summary is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        t = json.load(open(path))
+    except ValueError:
+        return None
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def _pmc_means(path: str, counter: str) -> dict:
+    """Mean reading (KiB) per dispatch of `counter`, by kernel name, from a rocprofv3 --pmc CSV."""
+    import csv
+    acc: dict = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            v = acc.setdefault(r["Kernel_Name"], [0.0, 0])
+            v[0] += float(r["Counter_Value"])
+            v[1] += 1
+    return {k: v[0] / v[1] for k, v in acc.items()}
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str, copy_mib: int,
+                  kernels: list) -> None:
+    """Writes profiles/traffic_<kernel>.json: HBM bytes per launch from FETCH_SIZE and WRITE_SIZE,
+    each scaled by what the same counter reads for a copy kernel that moves copy_mib MiB each way."""
+    def one(path, counter, name_part):
+        means = _pmc_means(path, counter)
+        hit = [v for k, v in means.items() if name_part in k]
+        if len(hit) != 1:
+            raise SystemExit(f"{path}: expected one kernel matching {name_part!r}, found {len(hit)}")
+        return hit[0]
+    true_kib = copy_mib * 1024.0
+    f_scale = true_kib / one(copy_fetch_csv, "FETCH_SIZE", "k_copy")
+    w_scale = true_kib / one(copy_write_csv, "WRITE_SIZE", "k_copy")
+    for short in kernels:
+        fetch = one(fetch_csv, "FETCH_SIZE", f"k_{short}<")
+        write = one(write_csv, "WRITE_SIZE", f"k_{short}<")
+        out = {"kernel": short, "source_sha256": kernel_source_hash(),
+               "fetch_kib_per_dispatch_raw": fetch, "write_kib_per_dispatch_raw": write,
+               "fetch_scale": f_scale, "write_scale": w_scale,
+               "bytes_per_launch": (fetch * f_scale + write * w_scale) * 1024.0,
+               "calibration": f"copy kernel moving {copy_mib} MiB read + {copy_mib} MiB write"}
+        path = os.path.join(ROOT, "profiles", f"traffic_{short}.json")
+        with open(path, "w") as fh:
+            json.dump(out, fh, indent=1)
+            fh.write("\n")
+        log(f"{path}: {out['bytes_per_launch'] / 1e6:.2f} MB per launch")
+
+
 def main() -> int:
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
+        ap = argparse.ArgumentParser(prog="bench.py --summarize-pmc")
+        ap.add_argument("--summarize-pmc", action="store_true")
+        ap.add_argument("--fetch", required=True)
+        ap.add_argument("--write", required=True)
+        ap.add_argument("--copy-fetch", required=True)
+        ap.add_argument("--copy-write", required=True)
+        ap.add_argument("--copy-mib", type=int, default=1024)
+        ap.add_argument("--kernels", default="gateup_s1,down_s1")
+        a = ap.parse_args()
+        summarize_pmc(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib, a.kernels.split(","))
+        return 0
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=4096)
@@ -153,13 +232,7 @@ def main() -> int:
     gu_us = kernels["gateup_s1"]["avg_us"]
     achieved = gu_bytes / (gu_us * 1e-6) / 1e9
 
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", "traffic_gateup_decode.json")
-    if os.path.exists(tfile):
-        try:
-            traffic = json.load(open(tfile)).get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = measured_traffic("gateup_s1")
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample ------------------------
     cpu = None

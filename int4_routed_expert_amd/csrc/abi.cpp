@@ -24,6 +24,7 @@ static int hip_fail(hipError_t e) {
 struct ProfRec {
   const char *name;
   hipEvent_t a, b;
+  bool launched;
 };
 static bool g_prof = false;
 static std::vector<ProfRec> g_recs;
@@ -42,19 +43,21 @@ static hipEvent_t pool_event() {
 
 bool prof_on() { return g_prof; }
 
-void prof_begin(const char *name, hipStream_t st) {
-  ProfRec r{name, pool_event(), nullptr};
-  (void)hipEventRecord(r.a, st);
-  g_recs.push_back(r);
+static thread_local long t_armed = -1;  // record awaiting its kernel
+
+void prof_arm(const char *name) {
+  g_recs.push_back(ProfRec{name, pool_event(), pool_event(), false});
+  t_armed = (long)g_recs.size() - 1;
 }
 
-void prof_end(hipStream_t st) {
-  for (auto it = g_recs.rbegin(); it != g_recs.rend(); ++it)
-    if (!it->b) {
-      it->b = pool_event();
-      (void)hipEventRecord(it->b, st);
-      return;
-    }
+bool prof_take(hipEvent_t *start, hipEvent_t *stop) {
+  if (t_armed < 0 || t_armed >= (long)g_recs.size()) return false;
+  ProfRec &r = g_recs[(size_t)t_armed];
+  t_armed = -1;
+  r.launched = true;
+  *start = r.a;
+  *stop = r.b;
+  return true;
 }
 
 // Compute units of the current device (cached per device id).
@@ -145,7 +148,7 @@ int moe_profile_report(char *out, size_t cap) {
   if (!out || cap == 0) return MOE_ENULL;
   std::map<std::string, std::pair<double, long>> agg;
   for (auto &r : g_recs) {
-    if (r.b) {
+    if (r.launched) {
       hipError_t e = hipEventSynchronize(r.b);
       if (e != hipSuccess) return hip_fail(e);
       float ms = 0.f;
@@ -154,10 +157,11 @@ int moe_profile_report(char *out, size_t cap) {
       auto &v = agg[r.name];
       v.first += ms;
       v.second += 1;
-      g_pool.push_back(r.b);
     }
     g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
   }
+  t_armed = -1;
   g_recs.clear();
   std::string js = "{";
   bool first = true;

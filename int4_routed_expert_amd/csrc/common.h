@@ -2,8 +2,11 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
+
+#include <tuple>
 
 #include "../../include/moe.h"
 
@@ -76,16 +79,34 @@ struct FfnArgs {
 };
 
 // ---- timing instrumentation (host) --------------------------------------------
-// When enabled (moe_profile_enable), launchers bracket each kernel with a pair of
-// hipEvents on its stream; moe_profile_report sums the elapsed times per kernel.
+// When enabled (moe_profile_enable), a launcher names the kernel it is about to
+// launch (ProfScope); the next launch_kernel() on this thread then goes through
+// hipExtLaunchKernel with a start and a stop event that the command processor
+// stamps at the kernel's own begin and end, so the per-kernel averages that
+// moe_profile_report sums cover the same span as a kernel trace.
 bool prof_on();
-void prof_begin(const char *name, hipStream_t st);
-void prof_end(hipStream_t st);
+void prof_arm(const char *name);
+bool prof_take(hipEvent_t *start, hipEvent_t *stop);
 struct ProfScope {
-  hipStream_t st;
-  ProfScope(const char *name, hipStream_t s) : st(s) { if (prof_on()) prof_begin(name, st); }
-  ~ProfScope() { if (prof_on()) prof_end(st); }
+  ProfScope(const char *name, hipStream_t) { if (prof_on()) prof_arm(name); }
 };
+
+// Every kernel of the library is launched here (kernel parameters by value).
+template <typename... P, typename... A>
+inline void launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t st, A... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<P...> vals{static_cast<P>(args)...};
+  void *argv[sizeof...(P) > 0 ? sizeof...(P) : 1];
+  std::apply([&](auto &...v) {
+    int i = 0;
+    ((argv[i++] = (void *)&v), ...);
+  }, vals);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (prof_take(&e0, &e1))
+    (void)hipExtLaunchKernel((const void *)kernel, grid, block, argv, lds, st, e0, e1, 0);
+  else
+    (void)hipLaunchKernel((const void *)kernel, grid, block, argv, lds, st);
+}
 
 // Keeps a failed HIP call's message for moe_last_hip_error().
 void set_hip_error(hipError_t e);
