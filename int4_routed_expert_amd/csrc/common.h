@@ -6,8 +6,6 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 
-#include <tuple>
-
 #include "../../include/moe.h"
 
 namespace moe {
@@ -80,7 +78,7 @@ struct FfnArgs {
 
 // ---- timing instrumentation (host) --------------------------------------------
 // When enabled (moe_profile_enable), a launcher names the kernel it is about to
-// launch (ProfScope); the next launch_kernel() on this thread then goes through
+// launch (ProfScope); the next MOE_LAUNCH on this thread then goes through
 // hipExtLaunchKernel with a start and a stop event that the command processor
 // stamps at the kernel's own begin and end, so the per-kernel averages that
 // moe_profile_report sums cover the same span as a kernel trace.
@@ -91,22 +89,17 @@ struct ProfScope {
   ProfScope(const char *name, hipStream_t) { if (prof_on()) prof_arm(name); }
 };
 
-// Every kernel of the library is launched here (kernel parameters by value).
-template <typename... P, typename... A>
-inline void launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t st, A... args) {
-  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
-  std::tuple<P...> vals{static_cast<P>(args)...};
-  void *argv[sizeof...(P) > 0 ? sizeof...(P) : 1];
-  std::apply([&](auto &...v) {
-    int i = 0;
-    ((argv[i++] = (void *)&v), ...);
-  }, vals);
-  hipEvent_t e0 = nullptr, e1 = nullptr;
-  if (prof_take(&e0, &e1))
-    (void)hipExtLaunchKernel((const void *)kernel, grid, block, argv, lds, st, e0, e1, 0);
-  else
-    (void)hipLaunchKernel((const void *)kernel, grid, block, argv, lds, st);
-}
+// Every kernel of the library is launched through this macro: a plain launch, or,
+// when a ProfScope has armed a record, one stamped with kernel start/stop events.
+#define MOE_LAUNCH(KERNEL, GRID, BLOCK, LDS, ST, ...)                                        \
+  do {                                                                                      \
+    hipEvent_t moe_e0_ = nullptr, moe_e1_ = nullptr;                                        \
+    if (::moe::prof_take(&moe_e0_, &moe_e1_))                                               \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, (uint32_t)(LDS), ST, moe_e0_, moe_e1_, 0,  \
+                            __VA_ARGS__);                                                   \
+    else                                                                                    \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, ST, __VA_ARGS__);                        \
+  } while (0)
 
 // Keeps a failed HIP call's message for moe_last_hip_error().
 void set_hip_error(hipError_t e);

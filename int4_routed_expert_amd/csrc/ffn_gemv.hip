@@ -755,17 +755,17 @@ hipError_t launch_to_limbs(const void *src, int src_bf16, int rows, int K, int s
                            float *factors, hipStream_t st) {
   const long n = (long)rows * (K / kGroup);
   if (n == 0) return hipSuccess;
-  launch_kernel(k_to_limbs, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, src_bf16, rows, K,
+  MOE_LAUNCH(k_to_limbs, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, src_bf16, rows, K,
                      src_stride, limbs, factors);
   return hipGetLastError();
 }
 
 #define MOE_DISPATCH_NG(ng, KERNEL, GRID, BLOCK, LDS, ST, ...)                                          \
   switch (ng) {                                                                                         \
-    case 1: launch_kernel((KERNEL<1 __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;   \
-    case 2: launch_kernel((KERNEL<2 __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;   \
-    case 3: launch_kernel((KERNEL<3 __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;   \
-    default: launch_kernel((KERNEL<4 __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;  \
+    case 1: MOE_LAUNCH((KERNEL<1 __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;   \
+    case 2: MOE_LAUNCH((KERNEL<2 __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;   \
+    case 3: MOE_LAUNCH((KERNEL<3 __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;   \
+    default: MOE_LAUNCH((KERNEL<4 __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;  \
   }
 
 hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st) {
@@ -835,11 +835,11 @@ hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st) {
   }
   {
     ProfScope ps("bucket", st);
-    launch_kernel(k_bucket, dim3(a.E), dim3(256), 0, st, a);
+    MOE_LAUNCH(k_bucket, dim3(a.E), dim3(256), 0, st, a);
   }
   {
     ProfScope ps("schedule", st);
-    launch_kernel(k_schedule, dim3(1), dim3(1024), 0, st, a);
+    MOE_LAUNCH(k_schedule, dim3(1), dim3(1024), 0, st, a);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -862,7 +862,7 @@ hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st) {
   }
   {
     ProfScope ps("combine", st);
-    launch_kernel(k_combine, dim3((a.H + 255) / 256, a.S), dim3(256), 0, st, a);
+    MOE_LAUNCH(k_combine, dim3((a.H + 255) / 256, a.S), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }

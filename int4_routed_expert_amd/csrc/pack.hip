@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void k_pack(int H, int I, const uint8_t *qg, c
 hipError_t launch_pack(int H, int I, const uint8_t *qg, const uint16_t *sg, const uint8_t *qu, const uint16_t *su,
                        const uint8_t *qd, const uint16_t *sd, uint8_t *dst, hipStream_t st) {
   const long n = (long)(I / kGuPairs) * (H / kGroup) + (long)(H / kDnRows) * (I / kGroup);
-  launch_kernel(k_pack, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, H, I, qg, sg, qu, su, qd, sd, dst);
+  MOE_LAUNCH(k_pack, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, H, I, qg, sg, qu, su, qd, sd, dst);
   return hipGetLastError();
 }
 

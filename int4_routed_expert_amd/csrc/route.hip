@@ -239,17 +239,17 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
   {
     ProfScope ps("route_logits", st);
     if (a.S <= kFewTokens && a.H % 1024 == 0) {
-      launch_kernel(k_route_logits_few, dim3(a.E), dim3(256), 0, st, a);
+      MOE_LAUNCH(k_route_logits_few, dim3(a.E), dim3(256), 0, st, a);
     } else {
       dim3 grid((a.E + 3) / 4, (a.S + kLogitTokens - 1) / kLogitTokens);
-      launch_kernel(k_route_logits, grid, dim3(256), 0, st, a);
+      MOE_LAUNCH(k_route_logits, grid, dim3(256), 0, st, a);
     }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     ProfScope ps("route_select", st);
-    launch_kernel(k_route_select, dim3(a.S), dim3(256), 0, st, a);
+    MOE_LAUNCH(k_route_select, dim3(a.S), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }

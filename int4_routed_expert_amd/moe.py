@@ -43,6 +43,11 @@ class moe_slot_view(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() (hipcc for gfx950)")
+    # torch ships its own HIP runtime and loads it by path.  Loaded first, the
+    # library would resolve libamdhip64.so.7 through its run path to a second
+    # runtime in the same process, which sees no device and knows none of
+    # torch's streams; with torch loaded first, the soname binds to torch's copy.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     cp = ctypes.POINTER(moe_cfg)

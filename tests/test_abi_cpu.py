@@ -3,12 +3,15 @@ symbol, configurations are validated, sizes are as documented, the host packer
 round-trips and lays bytes out as documented, and argument errors return the
 documented codes before anything is enqueued."""
 import ctypes
+import os
 
 import numpy as np
 import pytest
 
 from gen import inputs as gen
 from int4_routed_expert_amd import moe as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def test_exports_every_declared_symbol():
@@ -160,3 +163,20 @@ def test_status_strings():
     for s in range(0, -8, -1):
         assert M.lib().moe_status_string(s)
     assert M.lib().moe_status_string(-99) == b"unknown status"
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Importing the binding first must still leave one HIP runtime in the process
+    (the library binds to the copy torch loads; a second copy sees no device)."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from int4_routed_expert_amd import moe\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read().split('\\n')\n"
+            "print(sorted({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n") % ROOT
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    import ast
+    libs = ast.literal_eval(out.stdout.strip().splitlines()[-1])
+    assert len(libs) == 1, libs
