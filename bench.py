@@ -160,7 +160,7 @@ def main() -> int:
             bias=torch.from_numpy(gen.router_bias(w, l)).to(dev)))
         log(f"layer {l}: {E}+1 experts packed into HBM ({(E * sb + ssb) / 1e9:.2f} GB), {time.time() - t0:.1f}s")
     xs = torch.from_numpy(np.concatenate([gen.tokens(w, layer=0, step=s) for s in range(args.tokens)])).to(dev)
-    ws = torch.empty(M.moe_workspace_bytes(cfg, 1), dtype=torch.uint8, device=dev)
+    ws = M.workspace(cfg, 1, device=dev)
     n_out = CHUNK * ((args.tokens + CHUNK - 1) // CHUNK)
     idx = torch.empty((n_out, k), dtype=torch.int32, device=dev)
     wt = torch.empty((n_out, k), dtype=torch.float32, device=dev)

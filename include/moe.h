@@ -100,6 +100,18 @@ int64_t moe_expert_bytes(const moe_cfg *cfg, int32_t inter);
  * 0 on a bad configuration. */
 size_t moe_workspace_bytes(const moe_cfg *cfg, int32_t max_S);
 
+/* Initialise a workspace once, before its first use by moe_route or moe_ffn:
+ * writes the 256-byte header at its start (two magic words and completion
+ * counters) with a small kernel on `stream` (no memset node, so it may be
+ * captured in a graph).  Every call leaves the counters back at zero, so the
+ * header stays valid across calls and graph replays; re-initialise only when no
+ * call using the workspace is in flight.  A workspace is used by one call at a
+ * time (calls that share one must be stream-ordered).  moe_route with S <= 8
+ * checks the magic words and, on a workspace that was not initialised, writes
+ * idx = -1 and w = NaN for every token (moe_ffn then yields NaN rows).
+ * ws_bytes must be at least 256.  Errors: MOE_ENULL, MOE_EWORKSPACE, MOE_EHIP. */
+int moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
 /* Pack one expert from the interchange format into the slot layout.
  * Interchange format of an R x K matrix (K = contraction, groups of 32 along K):
  *   q: uint8 [R, K/2], element (r, 2j) in the low nibble of byte (r, j), (r, 2j+1)
@@ -126,7 +138,10 @@ int moe_unpack_expert(const moe_cfg *cfg, int32_t inter, const void *src, uint8_
  *   w = s[idx] / sum(s[idx]) * rsf (or s[idx] * rsf without renormalisation).
  * x: [S, H] fp32 or bf16 (x_dtype); W_gate: [E, H] fp32 row-major; bias: [E] fp32.
  * Out: idx [S, k] int32, w [S, k] fp32, both rank-ordered.  S = 0 is a no-op.
- * ws: device workspace of at least moe_workspace_bytes(cfg, S) bytes. */
+ * ws: device workspace of at least moe_workspace_bytes(cfg, S) bytes, initialised
+ * by moe_workspace_init.  S <= 8 runs as one kernel: each expert's workgroup
+ * computes its logits and the last one to finish (device-scope counter in the
+ * workspace header) selects for all tokens. */
 int moe_route(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, const float *W_gate,
               const float *bias, int32_t *idx, float *w, void *ws, size_t ws_bytes, void *stream);
 

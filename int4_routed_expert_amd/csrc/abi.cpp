@@ -86,6 +86,7 @@ WsLayout ws_layout(const moe_cfg &c, int32_t S) {
   const size_t imax = (size_t)std::max(c.moe_inter, c.shared_inter);
   const size_t gh = (size_t)c.hidden / kGroup, gi = imax / kGroup;
   size_t off = 0;
+  L.sync = off; off += kWsSyncBytes;
   L.logits = off; off += align256((size_t)S * c.n_experts * sizeof(double));
   L.h = off; off += align256((size_t)S * k1 * imax * sizeof(float));
   L.xl = off; off += align256((size_t)S * gh * 24 * sizeof(uint32_t));
@@ -190,6 +191,13 @@ size_t moe_workspace_bytes(const moe_cfg *c, int32_t max_S) {
   return ws_layout(*c, max_S).total;
 }
 
+int moe_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+  if (!ws) return MOE_ENULL;
+  if (ws_bytes < (size_t)kWsSyncBytes) return MOE_EWORKSPACE;
+  hipError_t e = launch_ws_init((uint32_t *)ws, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
 int moe_pack_expert(const moe_cfg *c, int32_t inter, const uint8_t *qg, const uint16_t *sg, const uint8_t *qu,
                     const uint16_t *su, const uint8_t *qd, const uint16_t *sd, void *dst, int32_t where, void *stream) {
   const int64_t nb = moe_expert_bytes(c, inter);
@@ -274,6 +282,7 @@ int moe_route(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const
   a.x_bf16 = x_dtype == MOE_BF16; a.norm = c->norm_topk_prob; a.rsf = c->routed_scaling_factor;
   a.x = x; a.W = W; a.bias = bias; a.idx = idx; a.w = w;
   a.logits = (double *)((char *)ws + L.logits);
+  a.sync = (uint32_t *)((char *)ws + L.sync);
   hipError_t e = launch_route(a, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }

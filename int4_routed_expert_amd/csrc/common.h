@@ -19,6 +19,12 @@ constexpr int kMaxK = 16;        // top_k limit
 constexpr int kMaxE = 1024;      // n_experts limit
 constexpr int kMaxG = 64;        // n_group limit
 
+// Workspace header (first kWsSyncBytes bytes): two magic words written by
+// moe_workspace_init, then completion counters that every call leaves at zero.
+constexpr int kWsSyncBytes = 256;
+constexpr uint32_t kWsMagic0 = 0x6D6F6534u, kWsMagic1 = 0x77733031u;
+constexpr int kSyncRouteCtr = 2;  // word index: expert workgroups done (fused router)
+
 // ---- slot layout of one packed expert (inter = I, hidden = H) -------------
 // gate/up: I/4 tiles.  Tile t holds 8 rows, in order (g 4t, u 4t, g 4t+1, u 4t+1,
 // ..., g 4t+3, u 4t+3), each row H/2 bytes, then the tile's scales as
@@ -44,6 +50,7 @@ struct RouteArgs {
   double *logits;  // [S, E]
   int32_t *idx;
   float *w;
+  uint32_t *sync;  // workspace header
 };
 
 struct FfnArgs {
@@ -106,6 +113,7 @@ void set_hip_error(hipError_t e);
 
 // ---- launchers (host) --------------------------------------------------------
 hipError_t launch_route(const RouteArgs &a, hipStream_t st);
+hipError_t launch_ws_init(uint32_t *sync, hipStream_t st);
 hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st);  // S <= kSmallS
 hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st);   // S > kSmallS
 hipError_t launch_to_limbs(const void *src, int src_bf16, int rows, int K, int src_stride, uint32_t *limbs,
@@ -115,7 +123,7 @@ hipError_t launch_pack(int H, int I, const uint8_t *qg, const uint16_t *sg, cons
 
 // workspace layout (bytes, each region 256-aligned)
 struct WsLayout {
-  size_t logits, h, xl, xf, hl, hf, part, lists, counts, items, n_items, total;
+  size_t sync, logits, h, xl, xf, hl, hf, part, lists, counts, items, n_items, total;
   int32_t max_items;
 };
 WsLayout ws_layout(const moe_cfg &c, int32_t S);

@@ -57,6 +57,7 @@ def _load():
         "moe_last_hip_error": (ctypes.c_char_p, []),
         "moe_expert_bytes": (i64, [cp, i32]),
         "moe_workspace_bytes": (sz, [cp, i32]),
+        "moe_workspace_init": (ctypes.c_int, [p, sz, p]),
         "moe_pack_expert": (ctypes.c_int, [cp, i32, p, p, p, p, p, p, p, i32, p]),
         "moe_unpack_expert": (ctypes.c_int, [cp, i32, p, p, p, p, p, p, p]),
         "moe_route": (ctypes.c_int, [cp, p, i32, i32, p, p, p, p, p, sz, p]),
@@ -129,6 +130,20 @@ def moe_expert_bytes(cfg: moe_cfg, inter: int) -> int:
 
 def moe_workspace_bytes(cfg: moe_cfg, max_S: int) -> int:
     return _lib.moe_workspace_bytes(ctypes.byref(cfg), max_S)
+
+
+def moe_workspace_init(ws, ws_bytes: int | None = None, stream=None) -> None:
+    """Write the workspace header (magic words, zeroed counters) on `stream`."""
+    n = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(_lib.moe_workspace_init(ptr(ws), n, stream_handle(stream)), "moe_workspace_init")
+
+
+def workspace(cfg: moe_cfg, max_S: int, device="cuda", stream=None):
+    """A device workspace for up to max_S tokens, initialised (torch uint8 tensor)."""
+    import torch
+    ws = torch.empty(moe_workspace_bytes(cfg, max_S), dtype=torch.uint8, device=device)
+    moe_workspace_init(ws, stream=stream)
+    return ws
 
 
 def moe_pack_expert(cfg: moe_cfg, inter: int, qg, sg, qu, su, qd, sd, dst, where: int, stream=None) -> None:

@@ -62,8 +62,7 @@ class DeviceLayer:
         return M.slot_view(self.slab, self.slot_bytes, t, self.c.n_experts)
 
     def workspace(self, S: int) -> torch.Tensor:
-        n = M.moe_workspace_bytes(self.cfg, S)
-        return torch.empty(n, dtype=torch.uint8, device="cuda")
+        return M.workspace(self.cfg, S)
 
     def route(self, x: torch.Tensor, x_dtype: int, ws: torch.Tensor | None = None):
         S = x.shape[0]

@@ -117,6 +117,54 @@ def test_decode_full_size(glm):
     say("decode worst", max(errs))
 
 
+@pytest.mark.parametrize("layer", ["tiny", "mid", "glm"])
+def test_router_reused_workspace_all_sizes(tiny, mid, glm, layer):
+    """One workspace for a run of calls with S = 1..8 (single fused launch whose
+    last workgroup selects) and S = 9, 13 (logits + per-token select kernels),
+    fp32 and bf16 inputs: indices exact and weights within 1e-6 * rsf on every
+    call, so the completion counter is back at zero after each call."""
+    dl = {"tiny": tiny, "mid": mid, "glm": glm}[layer]
+    ws = dl.workspace(16)
+    sizes = [1, 2, 3, 4, 5, 6, 7, 8, 9, 1, 8, 13, 1]
+    for n, S in enumerate(sizes):
+        for bf16 in (False, True):
+            w = dl.w.with_(tokens=S, x_dtype="bf16" if bf16 else "f32")
+            x = gen.tokens(w, step=500 + n)
+            xt, dt = x_device(w, x)
+            idx = torch.empty((S, dl.c.top_k), dtype=torch.int32, device="cuda")
+            wt = torch.empty((S, dl.c.top_k), dtype=torch.float32, device="cuda")
+            M.moe_route(dl.cfg, xt, dt, S, dl.W, dl.bias, idx, wt, ws, ws.numel())
+            torch.cuda.synchronize()
+            ridx, rw, _, flags, _ = O.route(dl.c, x, dl.W_host, dl.bias_host, x_is_bf16=bf16)
+            assert not flags.any()
+            assert np.array_equal(idx.cpu().numpy(), ridx), (layer, S, bf16)
+            assert np.abs(wt.cpu().numpy() - rw).max() <= 1e-6 * dl.c.routed_scaling_factor
+
+
+@pytest.mark.parametrize("S", [1, 5, 8])
+def test_router_uninitialised_workspace_is_poisoned(tiny, S):
+    """A workspace whose header was never written gives idx -1 and w NaN for
+    every token (and then NaN rows from moe_ffn), not a silent selection;
+    after moe_workspace_init the same buffer routes correctly."""
+    c = tiny.c
+    ws = torch.full((M.moe_workspace_bytes(tiny.cfg, S),), 0xAB, dtype=torch.uint8, device="cuda")
+    x = gen.tokens(tiny.w.with_(tokens=S), step=77)
+    xt = dev(x)
+    idx = torch.zeros((S, c.top_k), dtype=torch.int32, device="cuda")
+    wt = torch.zeros((S, c.top_k), dtype=torch.float32, device="cuda")
+    M.moe_route(tiny.cfg, xt, M.MOE_F32, S, tiny.W, tiny.bias, idx, wt, ws, ws.numel())
+    y = tiny.ffn(xt, M.MOE_F32, idx, wt)
+    torch.cuda.synchronize()
+    assert (idx.cpu().numpy() == -1).all()
+    assert np.isnan(wt.cpu().numpy()).all()
+    assert np.isnan(y.cpu().numpy()).all()
+    M.moe_workspace_init(ws)
+    M.moe_route(tiny.cfg, xt, M.MOE_F32, S, tiny.W, tiny.bias, idx, wt, ws, ws.numel())
+    torch.cuda.synchronize()
+    ridx, rw, _, _, _ = O.route(c, x, tiny.W_host, tiny.bias_host)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+
+
 def test_decode_bf16_input(glm):
     w = glm.w.with_(x_dtype="bf16")
     x = gen.tokens(w, step=3)

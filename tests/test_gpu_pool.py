@@ -43,7 +43,7 @@ def run_stack(w: gen.Workload, n_layers: int, steps: int, spl: int, flags: int, 
     torch.cuda.synchronize()
     compute = torch.cuda.current_stream()
     side = torch.cuda.Stream()
-    ws = torch.empty(M.moe_workspace_bytes(cfg, 1), dtype=torch.uint8, device="cuda")
+    ws = M.workspace(cfg, 1)
     worst, n_checked = 0.0, 0
     for step in range(steps):
         for l in range(n_layers):
