@@ -98,6 +98,294 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_writ
         log(f"{path}: {out['bytes_per_launch'] / 1e6:.2f} MB per launch")
 
 
+def pack_layer(w, l, dev, cfg):
+    """Routed experts of layer l packed into one HBM slab (table[e] = e), the shared
+    expert in its own buffer, router weights and bias on the device."""
+    import torch
+    from gen import inputs as gen
+    from int4_routed_expert_amd import moe as M
+    c = w.cfg
+    E, I = c.n_experts, c.moe_inter
+    sb, ssb = M.moe_expert_bytes(cfg, I), M.moe_expert_bytes(cfg, c.shared_inter)
+    slab = torch.empty(E * sb, dtype=torch.uint8, device=dev)
+    stage = gen.empty_expert(c, I)
+    shared = torch.empty(ssb, dtype=torch.uint8, device=dev)
+    for e in range(E + 1):
+        ex = gen.expert_weights(w, l, e, out=stage if e < E else None)
+        parts = [torch.from_numpy(a).to(dev) for a in ex.parts()]
+        if e < E:
+            M.moe_pack_expert(cfg, I, *parts, slab[e * sb:(e + 1) * sb], 1)
+        else:
+            M.moe_pack_expert(cfg, c.shared_inter, *parts, shared, 1)
+        torch.cuda.current_stream().synchronize()
+    return dict(slab=slab, shared=shared, table=torch.arange(E, dtype=torch.int32, device=dev),
+                W=torch.from_numpy(gen.router_weights(w, l)).to(dev),
+                bias=torch.from_numpy(gen.router_bias(w, l)).to(dev), sb=sb)
+
+
+def x_tensor(w, batch_list, dev):
+    """Token batches as one device tensor and its dtype code."""
+    import torch
+    from int4_routed_expert_amd import moe as M
+    xs = np.concatenate(batch_list)
+    if w.x_dtype == "bf16":
+        return torch.from_numpy(xs.view(np.int16)).to(dev).view(torch.bfloat16), M.MOE_BF16
+    return torch.from_numpy(xs).to(dev), M.MOE_F32
+
+
+def emit(out):
+    print(json.dumps(out), flush=True)
+
+
+def bench_verify(args) -> int:
+    """Speculative-verify batches: 4 tokens per call (GLM-5.2 shape), 1024 distinct
+    batches rotated over 4 resident layers, HIP graphs of 16 calls."""
+    import torch
+    from gen import inputs as gen
+    from int4_routed_expert_amd import moe as M
+    w = gen.WORKLOADS["verify"]
+    c, S = w.cfg, w.tokens
+    cfg = M.make_cfg(c)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers = [pack_layer(w, l, dev, cfg) for l in range(args.layers)]
+    nb = args.tokens
+    x, dt = x_tensor(w, [gen.tokens(w, layer=0, step=j) for j in range(nb)], dev)
+    ws = M.workspace(cfg, S, device=dev)
+    n_out = CHUNK * ((nb + CHUNK - 1) // CHUNK)
+    idx = torch.empty((n_out, S, c.top_k), dtype=torch.int32, device=dev)
+    wt = torch.empty((n_out, S, c.top_k), dtype=torch.float32, device=dev)
+    y = torch.empty((n_out, S, c.hidden), dtype=torch.float32, device=dev)
+    views = [M.slot_view(L["slab"], L["sb"], L["table"], c.n_experts) for L in layers]
+
+    def step(j):
+        L, b, o = layers[j % len(layers)], j % nb, j % n_out
+        xb = x[b * S:(b + 1) * S]
+        M.moe_route(cfg, xb, dt, S, L["W"], L["bias"], idx[o], wt[o], ws, ws.numel())
+        M.moe_ffn(cfg, xb, dt, S, idx[o], wt[o], views[j % len(layers)], L["shared"], y[o], ws, ws.numel())
+
+    tok_s, ms_per_step, steps, warm = run_graphs(step, args, nb)
+    # experts streamed per call: the batch union plus the shared expert
+    idx_h = idx.cpu().numpy()
+    U = np.array([len(set(idx_h[o].ravel().tolist())) for o in range(min(nb, n_out))])
+    per_call = (U.mean() + 1) * layers[0]["sb"]
+    gbps = per_call / (ms_per_step * 1e-3) / 1e9
+    emit({"metric": "MoE-layer tokens/s and effective int4 weight GB/s (% of HBM peak), GLM-5.2",
+          "value": tok_s * S, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+          "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+          "dtype": "f32", "data": "synthetic",
+          "config": {"workload": "glm52_moe_layer_verify_S4", "tokens_per_call": S, "bias": w.bias_recipe,
+                     "layers_rotated": args.layers, "batches_rotated": nb, "launch": "hip graphs of 16 calls"},
+          "union_mean": float(U.mean()), "union_min": int(U.min()), "union_max": int(U.max()),
+          "shared_fraction": float(1.0 - U.mean() / (S * c.top_k)),
+          "effective_gbps": gbps, "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS})
+    return 0
+
+
+def run_graphs(step, args, period_tokens):
+    """Captures HIP graphs of CHUNK steps over the rotation and times their replay."""
+    import torch
+    period = int(np.lcm(period_tokens, args.layers))
+    n_graphs = min((period + CHUNK - 1) // CHUNK, 64)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for j in range(CHUNK):
+            step(j)
+    torch.cuda.synchronize()
+    graphs = []
+    for gi in range(n_graphs):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for j in range(CHUNK):
+                step(gi * CHUNK + j)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    steps = CHUNK * ((args.steps + CHUNK - 1) // CHUNK)
+    warm = CHUNK * ((args.warmup + CHUNK - 1) // CHUNK)
+    for i in range(warm // CHUNK):
+        graphs[i % n_graphs].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps // CHUNK):
+        graphs[i % n_graphs].replay()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    log(f"graph replay: {el * 1e6 / steps:.2f} us/call over {steps} calls")
+    return steps / el, el * 1e3 / steps, steps, warm
+
+
+def bench_prefill(args) -> int:
+    """Prefill: 2048 bf16 tokens per call (Zipf-skewed router bias), GLM-5.2 shape;
+    4 distinct batches rotated; every call routes and runs the whole layer."""
+    import torch
+    from gen import inputs as gen
+    from int4_routed_expert_amd import moe as M
+    w = gen.WORKLOADS["prefill"]
+    c, S = w.cfg, w.tokens
+    cfg = M.make_cfg(c)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = pack_layer(w, 0, dev, cfg)
+    nb = 4
+    xs = [x_tensor(w, [gen.tokens(w, layer=0, step=j)], dev) for j in range(nb)]
+    ws = M.workspace(cfg, S, device=dev)
+    idx = torch.empty((S, c.top_k), dtype=torch.int32, device=dev)
+    wt = torch.empty((S, c.top_k), dtype=torch.float32, device=dev)
+    y = torch.empty((S, c.hidden), dtype=torch.float32, device=dev)
+    view = M.slot_view(L["slab"], L["sb"], L["table"], c.n_experts)
+
+    def call(j):
+        x, dt = xs[j % nb]
+        M.moe_route(cfg, x, dt, S, L["W"], L["bias"], idx, wt, ws, ws.numel())
+        M.moe_ffn(cfg, x, dt, S, idx, wt, view, L["shared"], y, ws, ws.numel())
+
+    n_warm, n_iter = max(2, min(args.warmup, 8)), max(4, min(args.steps, 40))
+    for j in range(n_warm):
+        call(j)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(n_iter):
+        call(j)
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / n_iter
+    M.moe_profile_enable(True)
+    M.moe_profile_report()
+    for j in range(4):
+        call(j)
+    torch.cuda.synchronize()
+    prof = M.moe_profile_report()
+    M.moe_profile_enable(False)
+    kernels = {n: round(ms * 1e3 / k, 2) for n, (ms, k) in prof.items()}
+    used = len(set(idx.cpu().numpy().ravel().tolist()))
+    bytes_call = (used + 1) * L["sb"]
+    flop = 2 * 3 * c.hidden * c.moe_inter * (S * c.top_k) + 2 * 3 * c.hidden * c.shared_inter * S
+    log(f"prefill: {el * 1e3:.3f} ms per call, {used} experts used, kernels (us) {kernels}")
+    emit({"metric": "MoE-layer tokens/s and effective int4 weight GB/s (% of HBM peak), GLM-5.2",
+          "value": S / el, "unit": "tokens/s", "n_gpus": 1, "steps": n_iter, "warmup": n_warm,
+          "ms_per_step": el * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+          "dtype": "f32", "data": "synthetic",
+          "config": {"workload": "glm52_moe_layer_prefill_S2048", "tokens_per_call": S, "x": "bf16",
+                     "bias": w.bias_recipe, "batches_rotated": nb},
+          "experts_used": used, "effective_gbps": bytes_call / el / 1e9,
+          "pct_hbm_peak": 100.0 * bytes_call / el / 1e9 / HBM_PEAK_GBPS,
+          "tflops": flop / el / 1e12, "kernels_us": kernels})
+    return 0
+
+
+def bench_stack(args) -> int:
+    """75-layer MoE stack decode from a cold HBM slot pool: routed experts live in
+    pinned host memory (logical experts aliased onto --blobs distinct blobs),
+    100 slots per layer in HBM (159 GB), misses filled on a side stream; one
+    token per step through all 75 layers, 64 steps.  Per (step, layer): route,
+    copy idx to the host, acquire (LRU + fills), ffn, release."""
+    import torch
+    from gen import inputs as gen
+    from int4_routed_expert_amd import moe as M
+    w = gen.WORKLOADS["stack"]
+    if args.blobs:
+        w = w.with_(n_blobs=args.blobs)
+    c = w.cfg
+    cfg = M.make_cfg(c)
+    E, I, NL, steps = c.n_experts, c.moe_inter, w.layers, args.stack_steps or w.steps
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sb = M.moe_expert_bytes(cfg, I)
+    t0 = time.time()
+    host = torch.empty((w.n_blobs, sb), dtype=torch.uint8, pin_memory=True)
+    stage_d = torch.empty(sb, dtype=torch.uint8, device=dev)
+    stage = gen.empty_expert(c, I)
+    blob_ids = {}
+    for l in range(NL):
+        for e in range(E):
+            b = gen.blob_of(w, l, e)[1]
+            if b not in blob_ids:
+                ex = gen.expert_weights(w, l, e, out=stage)
+                parts = [torch.from_numpy(a).to(dev) for a in ex.parts()]
+                M.moe_pack_expert(cfg, I, *parts, stage_d, 1)
+                host[b].copy_(stage_d)
+                blob_ids[b] = True
+    torch.cuda.synchronize()
+    log(f"{len(blob_ids)} blobs packed into pinned host memory ({host.numel() / 1e9:.1f} GB), {time.time() - t0:.1f}s")
+    spl = args.slots_per_layer
+    pool = M.Pool(cfg, NL, spl, 0)
+    for l in range(NL):
+        for e in range(E):
+            pool.register_host(l, e, host[gen.blob_of(w, l, e)[1]])
+    layers = []
+    for l in range(NL):
+        sh = gen.expert_weights(w, l, E)
+        shared = torch.empty(M.moe_expert_bytes(cfg, c.shared_inter), dtype=torch.uint8, device=dev)
+        M.moe_pack_expert(cfg, c.shared_inter, *[torch.from_numpy(a).to(dev) for a in sh.parts()], shared, 1)
+        layers.append(dict(W=torch.from_numpy(gen.router_weights(w, l)).to(dev),
+                           bias=torch.from_numpy(gen.router_bias(w, l)).to(dev), shared=shared))
+    xs = [torch.from_numpy(np.concatenate([gen.tokens(w, layer=l, step=s) for s in range(steps)])).to(dev)
+          for l in range(NL)]
+    torch.cuda.synchronize()
+    log(f"pool of {NL} x {spl} slots ({NL * spl * sb / 1e9:.0f} GB HBM), inputs ready, {time.time() - t0:.1f}s")
+    # pinned host -> HBM copy ceiling for one expert-sized transfer
+    side = torch.cuda.Stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(side):
+        stage_d.copy_(host[0], non_blocking=True)
+        e0.record(side)
+        for r in range(16):
+            stage_d.copy_(host[r % w.n_blobs], non_blocking=True)
+        e1.record(side)
+    side.synchronize()
+    h2d_gbps = 16 * sb / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    compute = torch.cuda.current_stream()
+    ws = M.workspace(cfg, 1, device=dev)
+    idx = torch.empty((1, c.top_k), dtype=torch.int32, device=dev)
+    idx_h = torch.empty((1, c.top_k), dtype=torch.int32, pin_memory=True)
+    wt = torch.empty((1, c.top_k), dtype=torch.float32, device=dev)
+    y = torch.empty((1, c.hidden), dtype=torch.float32, device=dev)
+    misses = np.zeros((steps, NL), np.int64)
+    kernel_bytes = 0
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for st in range(steps):
+        for l in range(NL):
+            L = layers[l]
+            x = xs[l][st:st + 1]
+            M.moe_route(cfg, x, M.MOE_F32, 1, L["W"], L["bias"], idx, wt, ws, ws.numel())
+            idx_h.copy_(idx, non_blocking=True)
+            compute.synchronize()  # the host decides residency
+            view, n_miss = pool.acquire(l, idx_h.numpy(), compute, side)
+            M.moe_ffn(cfg, x, M.MOE_F32, 1, idx, wt, view, L["shared"], y, ws, ws.numel())
+            pool.release(l, compute)
+            misses[st, l] = n_miss
+            kernel_bytes += (len(set(idx_h.numpy().ravel().tolist())) + 1) * sb
+        if st == 0:
+            torch.cuda.synchronize()
+            t_step0 = time.perf_counter() - t_start
+            log(f"step 0 (cold pool): {t_step0 * 1e3:.1f} ms, {misses[0].sum()} misses")
+        elif st % 8 == 0:
+            log(f"step {st}: {time.perf_counter() - t_start:.2f} s, {misses[st].sum()} misses this step")
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t_start
+    stt = pool.stats()
+    pool.close()
+    sel = NL * c.top_k
+    hit0 = 1.0 - misses[0].sum() / sel
+    hit_rest = 1.0 - misses[1:].sum() / (sel * max(1, steps - 1))
+    warm_el = el - t_step0
+    log(f"stack: {el:.3f} s for {steps} steps x {NL} layers; hit rate step0 {hit0:.3f}, steps 1+ {hit_rest:.3f}; "
+        f"fills {stt['fill_bytes'] / 1e9:.1f} GB; H2D ceiling {h2d_gbps:.1f} GB/s")
+    emit({"metric": "MoE-layer tokens/s and effective int4 weight GB/s (% of HBM peak), GLM-5.2",
+          "value": steps / el, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": 0,
+          "ms_per_step": el * 1e3 / steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+          "dtype": "f32", "data": "synthetic",
+          "config": {"workload": "glm52_moe_stack_75_layers_decode", "layers": NL, "steps": steps,
+                     "slots_per_layer": spl, "pool_gb": NL * spl * sb / 1e9, "distinct_blobs": w.n_blobs,
+                     "bias": w.bias_recipe, "launch": "eager; host sync per layer for residency"},
+          "tokens_per_s_warm": (steps - 1) / warm_el if steps > 1 else None,
+          "hit_rate_step0": hit0, "hit_rate_steps_1_plus": hit_rest, "misses": int(misses.sum()),
+          "fill_bytes": int(stt["fill_bytes"]), "fill_gbps_wall": stt["fill_bytes"] / el / 1e9,
+          "h2d_ceiling_gbps": h2d_gbps, "kernel_bytes": kernel_bytes,
+          "kernel_bytes_gbps_wall": kernel_bytes / el / 1e9})
+    return 0
+
+
 def main() -> int:
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
         ap = argparse.ArgumentParser(prog="bench.py --summarize-pmc")
@@ -112,6 +400,8 @@ def main() -> int:
         summarize_pmc(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib, a.kernels.split(","))
         return 0
     ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", default="decode", choices=["decode", "verify", "prefill", "stack"],
+                    help="decode (default, the headline line); verify, prefill and stack are separate lines")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=4096)
     ap.add_argument("--warmup", type=int, default=512)
@@ -120,11 +410,21 @@ def main() -> int:
     ap.add_argument("--profile-steps", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--blobs", type=int, default=0, help="stack: distinct pinned weight blobs (0: 1024)")
+    ap.add_argument("--slots-per-layer", type=int, default=100, help="stack: HBM slots per layer")
+    ap.add_argument("--stack-steps", type=int, default=0, help="stack: decode steps (0: 64)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this MoE-layer path runs on one GPU only; --gpus must be 1", file=sys.stderr)
         return 2
+
+    if args.workload == "verify":
+        return bench_verify(args)
+    if args.workload == "prefill":
+        return bench_prefill(args)
+    if args.workload == "stack":
+        return bench_stack(args)
 
     import torch
     from gen import inputs as gen
