@@ -74,6 +74,11 @@ typedef struct moe_cfg {
   int32_t group_size;
   float routed_scaling_factor;
   int32_t norm_topk_prob;
+  /* Batches of more than 4 tokens: an expert (routed or shared) that receives at
+   * least this many tokens is contracted on the matrix cores in bf16 (x and h
+   * rounded to bf16, weights dequantised to bf16, fp32 accumulation); the others
+   * keep the exact fp32 path.  0 disables the matrix-core path.  >= 0. */
+  int32_t mfma_min_tokens;
 } moe_cfg;
 
 /* Where the routed experts live.  Expert e's packed weights start at

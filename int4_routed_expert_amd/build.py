@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmoe.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["abi.cpp", "pool.cpp", "route.hip", "ffn_gemv.hip", "pack.hip"]
+SOURCES = ["abi.cpp", "pool.cpp", "route.hip", "ffn_gemv.hip", "ffn_mfma.hip", "pack.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 VALU instructions stay disabled for every device compile.

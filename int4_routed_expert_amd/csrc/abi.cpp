@@ -94,13 +94,19 @@ WsLayout ws_layout(const moe_cfg &c, int32_t S) {
   L.hl = off; off += align256((size_t)S * k1 * gi * 24 * sizeof(uint32_t));
   L.hf = off; off += align256((size_t)S * k1 * gi * sizeof(float));
   L.max_items = 0;
+  L.max_mtiles = 0;
   if (S > kSmallS) {
     L.part = off; off += align256((size_t)S * k1 * c.hidden * sizeof(float));
     L.lists = off; off += align256((size_t)c.n_experts * S * sizeof(int32_t));
     L.counts = off; off += align256((size_t)(c.n_experts + 1) * sizeof(int32_t));
     L.max_items = (int32_t)(((size_t)S * c.top_k + 3) / 4 + c.n_experts + (S + 3) / 4);
     L.items = off; off += align256((size_t)L.max_items * 3 * sizeof(int32_t));
-    L.n_items = off; off += align256(2 * sizeof(int32_t));
+    L.n_items = off; off += align256(4 * sizeof(int32_t));
+    // a tile per kMfmaTileTokens rows of each expert's list: at most one partial tile per expert
+    const size_t pairs = (size_t)S * c.top_k;
+    L.max_mtiles = (int32_t)((pairs + kMfmaTileTokens - 1) / kMfmaTileTokens + std::min<size_t>(c.n_experts, pairs) +
+                             (S + kMfmaTileTokens - 1) / kMfmaTileTokens);
+    L.mtiles = off; off += align256((size_t)L.max_mtiles * 3 * sizeof(int32_t));
   }
   L.total = std::max<size_t>(off, 256);
   return L;
@@ -120,7 +126,8 @@ int moe_validate_cfg(const moe_cfg *c) {
                   c->n_experts >= 1 && c->n_experts <= kMaxE && c->n_group >= 1 && c->n_group <= kMaxG &&
                   c->n_experts % c->n_group == 0 && c->topk_group >= 1 && c->topk_group <= c->n_group &&
                   c->top_k >= 1 && c->top_k <= kMaxK && c->top_k <= c->topk_group * (c->n_experts / c->n_group) &&
-                  (c->norm_topk_prob == 0 || c->norm_topk_prob == 1) && std::isfinite(c->routed_scaling_factor);
+                  (c->norm_topk_prob == 0 || c->norm_topk_prob == 1) && std::isfinite(c->routed_scaling_factor) &&
+                  c->mfma_min_tokens >= 0;
   return ok ? MOE_OK : MOE_EINVAL;
 }
 
@@ -327,6 +334,9 @@ int moe_ffn(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const i
     a.items = (int32_t *)(b + L.items);
     a.n_items = (int32_t *)(b + L.n_items);
     a.max_items = L.max_items;
+    a.mtiles = (int32_t *)(b + L.mtiles);
+    a.max_mtiles = L.max_mtiles;
+    a.mfma_thr = c->mfma_min_tokens;
     e = launch_ffn_batch(a, (hipStream_t)stream);
   }
   return e == hipSuccess ? MOE_OK : hip_fail(e);

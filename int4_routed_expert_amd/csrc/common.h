@@ -15,6 +15,7 @@ constexpr int kGuRows = 8;       // rows per gate/up tile: gate r, up r for 4 co
 constexpr int kGuPairs = 4;      // feature rows per gate/up tile
 constexpr int kDnRows = 8;       // rows per down tile
 constexpr int kSmallS = 4;       // batches up to this size take the decode path
+constexpr int kMfmaTileTokens = 128;  // token rows per matrix-core tile (many-token experts)
 constexpr int kMaxK = 16;        // top_k limit
 constexpr int kMaxE = 1024;      // n_experts limit
 constexpr int kMaxG = 64;        // n_group limit
@@ -69,9 +70,12 @@ struct FfnArgs {
   float *part;     // [S, k+1, H] fp32 per-(token, rank) expert outputs (large-batch path)
   int32_t *lists;  // [E+1, S] token lists per expert (large-batch path), entry = token*(k+1)+rank
   int32_t *counts; // [E+1]
-  int32_t *items;  // work items (large-batch path)
-  int32_t *n_items;
+  int32_t *items;  // GEMV work items {expert, list position, tokens} (large-batch path)
+  int32_t *n_items;  // [0] routed items, [1] shared items, [2] routed MFMA tiles, [3] shared MFMA tiles
   int32_t max_items;
+  int32_t *mtiles;   // MFMA tiles {expert, list position, rows <= kMfmaTileTokens}
+  int32_t max_mtiles;
+  int32_t mfma_thr;  // experts with at least this many tokens use the matrix cores (0: never)
   // activations in limb form (see dot.h): [rows][groups][24] words and [rows][groups] factors
   uint32_t *xl;    // x: S rows of H/32 groups
   float *xf;
@@ -116,6 +120,8 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t st);
 hipError_t launch_ws_init(uint32_t *sync, hipStream_t st);
 hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st);  // S <= kSmallS
 hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st);   // S > kSmallS
+hipError_t launch_gu_mfma(const FfnArgs &a, hipStream_t st);
+hipError_t launch_dn_mfma(const FfnArgs &a, hipStream_t st);
 hipError_t launch_to_limbs(const void *src, int src_bf16, int rows, int K, int src_stride, uint32_t *limbs,
                            float *factors, hipStream_t st);
 hipError_t launch_pack(int H, int I, const uint8_t *qg, const uint16_t *sg, const uint8_t *qu, const uint16_t *su,
@@ -123,8 +129,8 @@ hipError_t launch_pack(int H, int I, const uint8_t *qg, const uint16_t *sg, cons
 
 // workspace layout (bytes, each region 256-aligned)
 struct WsLayout {
-  size_t sync, logits, h, xl, xf, hl, hf, part, lists, counts, items, n_items, total;
-  int32_t max_items;
+  size_t sync, logits, h, xl, xf, hl, hf, part, lists, counts, items, n_items, mtiles, total;
+  int32_t max_items, max_mtiles;
 };
 WsLayout ws_layout(const moe_cfg &c, int32_t S);
 

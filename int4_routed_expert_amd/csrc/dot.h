@@ -154,6 +154,14 @@ __device__ inline float group_dot(const uint4 q, const Limbs &x) {
   return (float)T;
 }
 
+// Packed weights of routed expert e through the slot table, or null when its
+// slot number is outside [0, n_slots).
+__device__ inline const uint8_t *expert_ptr(const FfnArgs &a, int e) {
+  const int s = ldg<int>(a.table + e);
+  if (s < 0 || s >= a.n_slots) return nullptr;
+  return a.base + (size_t)s * (size_t)a.slot_bytes;
+}
+
 __device__ inline float half_bits_to_float(uint32_t bits16) {
   return __half2float(__ushort_as_half((uint16_t)(bits16 & 0xFFFFu)));
 }

@@ -455,11 +455,6 @@ __device__ void build_small_plan(const FfnArgs &a, SmallPlan &p) {
   __syncthreads();
 }
 
-__device__ inline const uint8_t *expert_ptr(const FfnArgs &a, int e) {
-  const int s = ldg<int>(a.table + e);
-  if (s < 0 || s >= a.n_slots) return nullptr;
-  return a.base + (size_t)s * (size_t)a.slot_bytes;
-}
 
 // One gate/up tile (4 features) for a set of tokens; x limbs from global.
 template <int NG>
@@ -623,32 +618,65 @@ __global__ __launch_bounds__(256) void k_bucket(FfnArgs a) {
 }
 
 // Work items {expert, first list position, n tokens}: routed experts in id order,
-// then the shared expert (id E) over all tokens.
+// then the shared expert (id E) over all tokens.  An expert with at least
+// mfma_thr tokens (mfma_thr > 0) gets matrix-core tiles of up to
+// kMfmaTileTokens rows instead, in the same order.
 __global__ __launch_bounds__(1024) void k_schedule(FfnArgs a) {
-  __shared__ int pre[kMaxE + 1];
+  __shared__ int pre[kMaxE + 1], pmt[kMaxE + 1];
   const int tid = threadIdx.x, E = a.E;
-  for (int e = tid; e < E; e += blockDim.x) pre[e] = (a.counts[e] + kTB - 1) / kTB;
+  const int thr = a.mfma_thr;
+  auto is_mfma = [&](int c) { return thr > 0 && c >= thr; };
+  for (int e = tid; e < E; e += blockDim.x) {
+    const int c = a.counts[e];
+    pre[e] = is_mfma(c) ? 0 : (c + kTB - 1) / kTB;
+    pmt[e] = is_mfma(c) ? (c + kMfmaTileTokens - 1) / kMfmaTileTokens : 0;
+  }
   __syncthreads();
   if (tid == 0) {
-    int s = 0;
-    for (int e = 0; e < E; ++e) { const int c = pre[e]; pre[e] = s; s += c; }
+    int s = 0, m = 0;
+    for (int e = 0; e < E; ++e) {
+      const int c = pre[e], d = pmt[e];
+      pre[e] = s;
+      pmt[e] = m;
+      s += c;
+      m += d;
+    }
     pre[E] = s;
+    pmt[E] = m;
   }
   __syncthreads();
   for (int e = tid; e < E; e += blockDim.x) {
     const int c = a.counts[e];
-    for (int s = 0; s * kTB < c; ++s) {
-      int *it = a.items + 3 * (size_t)(pre[e] + s);
-      it[0] = e; it[1] = s * kTB; it[2] = min(kTB, c - s * kTB);
+    if (is_mfma(c)) {
+      for (int s = 0; s * kMfmaTileTokens < c; ++s) {
+        int *mt = a.mtiles + 3 * (size_t)(pmt[e] + s);
+        mt[0] = e; mt[1] = s * kMfmaTileTokens; mt[2] = min(kMfmaTileTokens, c - s * kMfmaTileTokens);
+      }
+    } else {
+      for (int s = 0; s * kTB < c; ++s) {
+        int *it = a.items + 3 * (size_t)(pre[e] + s);
+        it[0] = e; it[1] = s * kTB; it[2] = min(kTB, c - s * kTB);
+      }
     }
   }
-  const int nr = pre[E];
-  const int nsh = a.Is > 0 ? (a.S + kTB - 1) / kTB : 0;
+  const int nr = pre[E], mr = pmt[E];
+  const bool sh_mfma = a.Is > 0 && is_mfma(a.S);
+  const int nsh = a.Is > 0 && !sh_mfma ? (a.S + kTB - 1) / kTB : 0;
+  const int msh = sh_mfma ? (a.S + kMfmaTileTokens - 1) / kMfmaTileTokens : 0;
   for (int s = tid; s < nsh; s += blockDim.x) {
     int *it = a.items + 3 * (size_t)(nr + s);
     it[0] = E; it[1] = s * kTB; it[2] = min(kTB, a.S - s * kTB);
   }
-  if (tid == 0) { a.n_items[0] = nr; a.n_items[1] = nsh; }
+  for (int s = tid; s < msh; s += blockDim.x) {
+    int *mt = a.mtiles + 3 * (size_t)(mr + s);
+    mt[0] = E; mt[1] = s * kMfmaTileTokens; mt[2] = min(kMfmaTileTokens, a.S - s * kMfmaTileTokens);
+  }
+  if (tid == 0) {
+    a.n_items[0] = nr;
+    a.n_items[1] = nsh;
+    a.n_items[2] = mr;
+    a.n_items[3] = msh;
+  }
 }
 
 __device__ inline int item_tokens(const FfnArgs &a, const int *it, int *toks, int *pairs) {
@@ -849,6 +877,8 @@ hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st) {
     const dim3 g((unsigned)std::min<long>((tiles_max + 3) / 4, 8192)), blk(256);
     MOE_DISPATCH_NG(ceil_groups(a.H), k_gateup_items, g, blk, 0, st);
   }
+  e = launch_gu_mfma(a, st);
+  if (e != hipSuccess) return e;
   {
     ProfScope ps("h_limbs", st);
     e = launch_to_limbs(a.h, 0, a.S * (a.k + 1), Imax, Imax, a.hl, a.hf, st);
@@ -860,6 +890,8 @@ hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st) {
     const dim3 g((unsigned)std::min<long>((dtiles + 3) / 4, 8192)), blk(256);
     MOE_DISPATCH_NG(ceil_groups(Imax), k_down_items, g, blk, 0, st);
   }
+  e = launch_dn_mfma(a, st);
+  if (e != hipSuccess) return e;
   {
     ProfScope ps("combine", st);
     MOE_LAUNCH(k_combine, dim3((a.H + 255) / 256, a.S), dim3(256), 0, st, a);

@@ -17,11 +17,12 @@ class DeviceLayer:
     """Routed experts of one layer packed into one slab (table[e] = e), the shared
     expert in its own buffer, router weights on the device."""
 
-    def __init__(self, w: gen.Workload, layer: int = 0, experts=None, host_experts: bool = False):
+    def __init__(self, w: gen.Workload, layer: int = 0, experts=None, host_experts: bool = False,
+                 mfma_min_tokens: int = M.MFMA_MIN_TOKENS):
         self.w = w
         c = w.cfg
         self.c = c
-        self.cfg = M.make_cfg(c)
+        self.cfg = M.make_cfg(c, mfma_min_tokens)
         E = c.n_experts
         self.slot_bytes = M.moe_expert_bytes(self.cfg, c.moe_inter)
         self.experts = list(range(E)) if experts is None else sorted(set(experts))
@@ -72,11 +73,14 @@ class DeviceLayer:
         M.moe_route(self.cfg, x, x_dtype, S, self.W, self.bias, idx, wt, ws, ws.numel())
         return idx, wt
 
-    def ffn(self, x: torch.Tensor, x_dtype: int, idx: torch.Tensor, wt: torch.Tensor, table=None, ws=None):
+    def ffn(self, x: torch.Tensor, x_dtype: int, idx: torch.Tensor, wt: torch.Tensor, table=None, ws=None,
+            mfma_min_tokens: int | None = None):
+        """moe_ffn; mfma_min_tokens overrides the layer's threshold of the matrix-core path."""
         S = x.shape[0]
         ws = self.workspace(S) if ws is None else ws
+        cfg = self.cfg if mfma_min_tokens is None else M.make_cfg(self.c, mfma_min_tokens)
         y = torch.full((S, self.c.hidden), float("nan"), dtype=torch.float32, device="cuda")
-        M.moe_ffn(self.cfg, x, x_dtype, S, idx, wt, self.view(table), self.shared, y, ws, ws.numel())
+        M.moe_ffn(cfg, x, x_dtype, S, idx, wt, self.view(table), self.shared, y, ws, ws.numel())
         return y
 
 

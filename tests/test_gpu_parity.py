@@ -63,12 +63,13 @@ def check_ffn(dl: DeviceLayer, x_host, ridx, rw, y, tokens, tol):
 
 @pytest.fixture(scope="module")
 def tiny():
-    return DeviceLayer(gen.WORKLOADS["tiny"], host_experts=True)
+    # exact fp32 path at every batch size; the matrix-core path is tested with explicit thresholds
+    return DeviceLayer(gen.WORKLOADS["tiny"], host_experts=True, mfma_min_tokens=0)
 
 
 @pytest.fixture(scope="module")
 def mid():
-    return DeviceLayer(gen.Workload("mid", MID, tokens=67, seed=11), host_experts=True)
+    return DeviceLayer(gen.Workload("mid", MID, tokens=67, seed=11), host_experts=True, mfma_min_tokens=0)
 
 
 @pytest.fixture(scope="module")
@@ -264,12 +265,67 @@ def test_largest_shapes():
     cfg = gen.LayerConfig(hidden=8192, n_experts=8, n_group=2, topk_group=1, top_k=2, moe_inter=8192,
                           shared_inter=8192)
     w = gen.Workload("max", cfg, tokens=5, seed=21)
-    dl = DeviceLayer(w)
+    dl = DeviceLayer(w, mfma_min_tokens=0)
     for S in (1, 5):
         x = gen.tokens(w.with_(tokens=S), step=S)
         idx, wt, y = run_gpu(dl, x)
         ridx, rw = check_route(dl, x, idx, wt)
         check_ffn(dl, x, ridx, rw, y, np.arange(min(S, 2)), TOL_FP32)
+
+
+RAGGED = gen.LayerConfig(hidden=544, n_experts=8, n_group=2, topk_group=1, top_k=2, moe_inter=96, shared_inter=64)
+
+
+@pytest.mark.parametrize("case", ["tiny_S37_t4", "mid_S67_t4", "mid_S300_t16", "ragged_S40_t4", "ragged_bf16_S40_t2"])
+def test_matrix_core_path(tiny, mid, case):
+    """Experts with at least the threshold's tokens run the bf16 grouped GEMM
+    (several and ragged 128-row tiles, 64-column tiles that overhang H = 544,
+    shared expert included): every token within the bf16 bar of the oracle;
+    the same call with the threshold at 0 (exact path) stays within the fp32
+    bar and differs from the matrix-core result, so the tiles really ran."""
+    name, S, thr = case.rsplit("_", 2)[0], int(case.rsplit("_", 2)[1][1:]), int(case.rsplit("_", 1)[1][1:])
+    if name == "tiny":
+        dl = tiny
+    elif name == "mid":
+        dl = mid
+    else:
+        wl = gen.Workload("ragged", RAGGED, tokens=S, seed=31, x_dtype="bf16" if "bf16" in name else "f32")
+        dl = DeviceLayer(wl, host_experts=True)
+    w = dl.w.with_(tokens=S)
+    x = gen.tokens(w, step=900 + S)
+    xt, dt = x_device(w, x)
+    idx, wt = dl.route(xt, dt)
+    y_mfma = dl.ffn(xt, dt, idx, wt, mfma_min_tokens=thr)
+    y_exact = dl.ffn(xt, dt, idx, wt, mfma_min_tokens=0)
+    torch.cuda.synchronize()
+    ridx, rw = check_route(dl, x, idx.cpu().numpy(), wt.cpu().numpy())
+    counts = np.bincount(ridx.ravel(), minlength=dl.c.n_experts)
+    say(f"{case}: tokens per expert max {counts.max()}, experts at or over {thr}: {(counts >= thr).sum()}")
+    assert (counts >= thr).any() or S >= thr
+    ym, ye = y_mfma.cpu().numpy(), y_exact.cpu().numpy()
+    check_ffn(dl, x, ridx, rw, ym, np.arange(S), TOL_BF16)
+    check_ffn(dl, x, ridx, rw, ye, np.arange(S), TOL_FP32)
+    assert not np.array_equal(ym, ye)
+
+
+def test_matrix_core_unresident_slot_poisons_only_its_tokens(mid):
+    S, thr = 67, 4
+    w = mid.w.with_(tokens=S)
+    x = gen.tokens(w, step=4242)
+    xt, dt = x_device(w, x)
+    idx, wt = mid.route(xt, dt)
+    ih = idx.cpu().numpy()
+    counts = np.bincount(ih.ravel(), minlength=mid.c.n_experts)
+    victim = int(np.argmax(counts))  # a matrix-core expert
+    assert counts[victim] >= thr
+    table = mid.table.clone()
+    table[victim] = 1 << 20  # outside [0, n_slots)
+    y = mid.ffn(xt, dt, idx, wt, table=table, mfma_min_tokens=thr).cpu().numpy()
+    hit = (ih == victim).any(axis=1)
+    assert np.isnan(y[hit]).all(axis=1).all()
+    assert np.isfinite(y[~hit]).all()
+    ridx, rw = check_route(mid, x, ih, wt.cpu().numpy())
+    check_ffn(mid, x, ridx, rw, y, np.where(~hit)[0], TOL_BF16)
 
 
 def test_prefill_full_size():
