@@ -107,6 +107,7 @@ WsLayout ws_layout(const moe_cfg &c, int32_t S) {
     L.max_mtiles = (int32_t)((pairs + kMfmaTileTokens - 1) / kMfmaTileTokens + std::min<size_t>(c.n_experts, pairs) +
                              (S + kMfmaTileTokens - 1) / kMfmaTileTokens);
     L.mtiles = off; off += align256((size_t)L.max_mtiles * 3 * sizeof(int32_t));
+    L.xb = off; off += align256((size_t)S * c.hidden * sizeof(uint16_t));
   }
   L.total = std::max<size_t>(off, 256);
   return L;
@@ -335,6 +336,7 @@ int moe_ffn(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const i
     a.n_items = (int32_t *)(b + L.n_items);
     a.max_items = L.max_items;
     a.mtiles = (int32_t *)(b + L.mtiles);
+    a.xb = (uint16_t *)(b + L.xb);
     a.max_mtiles = L.max_mtiles;
     a.mfma_thr = c->mfma_min_tokens;
     e = launch_ffn_batch(a, (hipStream_t)stream);

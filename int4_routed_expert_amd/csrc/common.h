@@ -15,7 +15,7 @@ constexpr int kGuRows = 8;       // rows per gate/up tile: gate r, up r for 4 co
 constexpr int kGuPairs = 4;      // feature rows per gate/up tile
 constexpr int kDnRows = 8;       // rows per down tile
 constexpr int kSmallS = 4;       // batches up to this size take the decode path
-constexpr int kMfmaTileTokens = 128;  // token rows per matrix-core tile (many-token experts)
+constexpr int kMfmaTileTokens = 256;  // token rows per matrix-core tile (many-token experts)
 constexpr int kMaxK = 16;        // top_k limit
 constexpr int kMaxE = 1024;      // n_experts limit
 constexpr int kMaxG = 64;        // n_group limit
@@ -74,6 +74,7 @@ struct FfnArgs {
   int32_t *n_items;  // [0] routed items, [1] shared items, [2] routed MFMA tiles, [3] shared MFMA tiles
   int32_t max_items;
   int32_t *mtiles;   // MFMA tiles {expert, list position, rows <= kMfmaTileTokens}
+  uint16_t *xb;      // [S, H] bf16 copy of fp32 x (matrix-core path)
   int32_t max_mtiles;
   int32_t mfma_thr;  // experts with at least this many tokens use the matrix cores (0: never)
   // activations in limb form (see dot.h): [rows][groups][24] words and [rows][groups] factors
@@ -129,7 +130,7 @@ hipError_t launch_pack(int H, int I, const uint8_t *qg, const uint16_t *sg, cons
 
 // workspace layout (bytes, each region 256-aligned)
 struct WsLayout {
-  size_t sync, logits, h, xl, xf, hl, hf, part, lists, counts, items, n_items, mtiles, total;
+  size_t sync, logits, h, xl, xf, hl, hf, part, lists, counts, items, n_items, mtiles, xb, total;
   int32_t max_items, max_mtiles;
 };
 WsLayout ws_layout(const moe_cfg &c, int32_t S);

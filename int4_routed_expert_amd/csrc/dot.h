@@ -37,6 +37,12 @@ __device__ inline uint4 ldg<uint4>(const void *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 template <>
+__device__ inline uint2 ldg<uint2>(const void *p) {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t v = *(const __attribute__((address_space(1))) u32x2_t *)p;
+  return make_uint2(v.x, v.y);
+}
+template <>
 __device__ inline float4 ldg<float4>(const void *p) {
   const f32x4_t v = *(const __attribute__((address_space(1))) f32x4_t *)p;
   return make_float4(v.x, v.y, v.z, v.w);

@@ -10,20 +10,24 @@
 // packer: gate/up row tiles (rows g0 u0 g1 u1 ... of four features, fp16
 // scale per row and group of 32) and down row tiles of eight output rows.
 //
-// Tiles: a workgroup (4 waves) owns up to 128 token rows of one expert's list
-// (kMT; wave w takes rows 32w .. 32w+31) and 64 output columns (kNT).  One
+// Tiles: a workgroup (8 waves) owns up to 256 token rows of one expert's list
+// (kMT) and 256 output columns (kNT); each wave computes 32 rows x 256
+// columns of it, so an
+// activation row is read once per 256 columns and a dequantised weight feeds
+// 256 rows.  One
 // MFMA contracts exactly one quantisation group (K = 32), so each lane's B
-// fragment carries a single scale.  Per group the 64 x 32 B tile is
-// dequantised once by the whole workgroup (8 values per thread: exact n*s - 8s
-// in fp32, then round-to-nearest-even to bf16) into LDS and read by all four
-// waves; A fragments (token rows, 8 consecutive K per lane) come straight from
-// global memory.  The next group's weights and activations are loaded while
-// the current group's MFMAs run; one barrier per group (double-buffered B).
+// fragment carries a single scale.  Per group the 256 x 32 B tile is
+// dequantised once by the whole workgroup (32 values per thread: exact
+// n*s - 8s in fp32, then round-to-nearest-even to bf16) into LDS and read by
+// all eight waves; A fragments (token rows, 8 consecutive K per lane) come
+// straight from global memory.  Two groups form a pipeline stage (64 MFMAs
+// per wave); weights are loaded two stages ahead and activations one stage
+// ahead; one barrier per stage (double-buffered B, 80 KB of LDS).
 //
 // Gate/up: column c of an N tile is tile row c % 8 of gate/up tile c / 8, so
 // gate and up of a feature sit in adjacent lanes of the accumulator layout;
-// the epilogue forms h = silu(g) * u there and stores it (fp32) for the down
-// GEMM, which rounds it to bf16 as its A operand.  Down: columns are output
+// the epilogue forms h = silu(g) * u there and stores it rounded to bf16 (in
+// the first half of the row's fp32 storage) as the down GEMM's A operand.  Down: columns are output
 // rows of Wd; results go to the per-(token, rank) partials that the combine
 // sums in route order.
 #include "dot.h"
@@ -34,10 +38,18 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+constexpr int kWaves = 8;             // waves per workgroup; wave w owns token rows 32w .. 32w+31
+constexpr int kThreads = 64 * kWaves;
 constexpr int kMT = kMfmaTileTokens;  // token rows per workgroup tile
-constexpr int kNT = 64;               // output columns per workgroup tile
-constexpr int kBStride = 80;          // bytes per column of an LDS B stage (64 + 16 padding: no bank conflicts)
-constexpr int kBStage = kNT * kBStride;
+constexpr int kNT = 256;              // output columns per workgroup tile
+constexpr int kMB = 2;                // MFMA row blocks (16 rows) per wave: 32 rows
+constexpr int kNB = 16;               // MFMA column blocks (16 columns) per wave: all 256 columns
+constexpr int kKG = 1;                // quantisation groups (K = 32 each) per pipeline stage
+constexpr int kBStride = 80;          // bytes per column of an LDS B group (64 + 16 padding: no bank conflicts)
+constexpr int kBGroup = kNT * kBStride;
+constexpr int kBStage = kKG * kBGroup;
+constexpr int kBParts = kThreads / kNT;  // threads that dequantise one column of a group (8 bytes each)
+static_assert(kMT == kWaves * 16 * kMB && kNT == 16 * kNB && kKG == 1 && kBParts == 2, "tile shape");
 
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
@@ -111,63 +123,106 @@ __device__ inline void tile_rows(const FfnArgs &a, const MTile &mt, int *s_tok, 
 }
 
 // The grouped GEMM main loop shared by gate/up and down.  For group g the B
-// column c (0..63) reads 32 nibbles at colp[c] + 16 g and its scale at
+// column c (0..kNT-1) reads 32 nibbles at colp[c] + 16 g and its scale at
 // sclp[c] + 16 g (pointers precomputed per column in LDS); A row r of this
 // wave's M block mb is arow(mb) + 32 g + octet*8 elements.
 struct GemmAcc {
-  f32x4 acc[2][4];  // [M block of 16 rows][N block of 16 columns]
+  f32x4 acc[kMB][kNB];  // [M block of 16 rows][N block of 16 columns] of this wave
 };
+
+// Stage s is group s.  Thread i dequantises half of column i % kNT (8 bytes of
+// nibbles and the scale, loaded two stages ahead) into the LDS stage; each
+// wave then runs 2 x kNB MFMAs from it with its activations (loaded one stage
+// ahead).  One barrier per stage.
+// One stage's MFMAs for the first MBV row blocks of this wave.
+// B fragments are read from LDS four at a time (a compiler fence between the
+// chunks keeps the reads from all being hoisted, which would exhaust registers).
+template <int MBV>
+__device__ inline void stage_mfma(GemmAcc &C, const bf16x8 (&A)[kMB][kKG], const uint8_t *sb, int lane, int oct) {
+#pragma unroll
+  for (int gi = 0; gi < kKG; ++gi)
+#pragma unroll
+    for (int n4 = 0; n4 < kNB; n4 += 4) {
+      bf16x8 B[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        B[q] = __builtin_bit_cast(
+            bf16x8, *(const uint4 *)(sb + gi * kBGroup + ((n4 + q) * 16 + (lane & 15)) * kBStride + oct * 16));
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int mb = 0; mb < MBV; ++mb)
+          C.acc[mb][n4 + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][gi], B[q], C.acc[mb][n4 + q], 0, 0, 0);
+      asm volatile("" ::: "memory");
+    }
+}
 
 template <bool ABF>
 __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_colp, const uint8_t *const *s_sclp,
-                                 uint8_t *s_b, const void *abase, const size_t *arow, int lane) {
+                                 uint8_t *s_b, const void *abase, const size_t *arow, int wn, int lane) {
   const int tid = threadIdx.x;
-  const int bc = tid >> 2, bo = tid & 3;  // this thread's B column and K octet for dequantisation
+  const int bc = tid % kNT, bp = tid / kNT;  // this thread's B column and half of the group's 16 nibble bytes
   const uint8_t *colp = s_colp[bc];
   const uint8_t *sclp = s_sclp[bc];
   const int oct = lane >> 4;  // this lane's K octet in A and B fragments
+  const int ns = (ng + kKG - 1) / kKG;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) C.acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // prologue: group 0
-  {
-    const uint32_t w = ldg<uint32_t>(colp + bo * 4);
-    const float s = half_bits_to_float(ldg<uint16_t>(sclp));
-    *(uint4 *)(s_b + bc * kBStride + bo * 16) = dequant8(w, s);
-  }
-  ARaw<ABF> A[2];
+    for (int nb = 0; nb < kNB; ++nb) C.acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  struct BRaw {
+    uint2 w;
+    uint16_t sc;
+  };
+  auto load_b = [&](int st) {
+    const int g = min(st, ng - 1);
+    return BRaw{ldg<uint2>(colp + (size_t)g * 16 + bp * 8), ldg<uint16_t>(sclp + (size_t)g * 16)};
+  };
+  auto store_b = [&](int buf, const BRaw &r) {
+    const float s = half_bits_to_float(r.sc);
+    uint8_t *d = s_b + buf * kBStage + bc * kBStride + bp * 32;
+    *(uint4 *)(d) = dequant8(r.w.x, s);
+    *(uint4 *)(d + 16) = dequant8(r.w.y, s);
+  };
+  auto load_a = [&](int st, ARaw<ABF> (&r)[kMB][kKG]) {
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) A[mb].load(abase, arow[mb] + oct * 8);
-  __syncthreads();
-  for (int g = 0; g < ng; ++g) {
-    const int gn = min(g + 1, ng - 1);  // unconditional prefetch (the last one repeats)
-    const uint32_t wn = ldg<uint32_t>(colp + (size_t)gn * 16 + bo * 4);
-    const uint16_t sn = ldg<uint16_t>(sclp + (size_t)gn * 16);
-    ARaw<ABF> An[2];
+    for (int gi = 0; gi < kKG; ++gi) {
+      const int g = min(st * kKG + gi, ng - 1);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) An[mb].load(abase, arow[mb] + (size_t)gn * 32 + oct * 8);
-    const uint8_t *sb = s_b + (g & 1) * kBStage;
-    bf16x8 B[4];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      B[nb] = __builtin_bit_cast(bf16x8, *(const uint4 *)(sb + (nb * 16 + (lane & 15)) * kBStride + oct * 16));
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const bf16x8 a8 = A[mb].get();
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        C.acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, B[nb], C.acc[mb][nb], 0, 0, 0);
+      for (int mb = 0; mb < kMB; ++mb) r[mb][gi].load(abase, arow[mb] + (size_t)g * 32 + oct * 8);
     }
-    *(uint4 *)(s_b + ((g + 1) & 1) * kBStage + bc * kBStride + bo * 16) = dequant8(wn, half_bits_to_float(sn));
+  };
+  bf16x8 A[kMB][kKG];
+  BRaw b1 = load_b(min(1, ns - 1));  // stage 1's weights; stage 0's are stored below
+  {
+    const BRaw b0 = load_b(0);
+    ARaw<ABF> r[kMB][kKG];
+    load_a(0, r);
+    store_b(0, b0);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) A[mb] = An[mb];
+    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+      for (int gi = 0; gi < kKG; ++gi) A[mb][gi] = r[mb][gi].get();
+  }
+  __syncthreads();
+  for (int st = 0; st < ns; ++st) {
+    const BRaw b2 = load_b(min(st + 2, ns - 1));  // unconditional prefetch (the last ones repeat)
+    ARaw<ABF> An[kMB][kKG];
+    load_a(min(st + 1, ns - 1), An);
+    const uint8_t *sb = s_b + (st & 1) * kBStage + (wn * 16 * kNB) * kBStride;
+    stage_mfma<kMB>(C, A, sb, lane, oct);  // rows past the tile's end repeat its last row; not stored
+    store_b((st + 1) & 1, b1);
+    b1 = b2;
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+      for (int gi = 0; gi < kKG; ++gi) A[mb][gi] = An[mb][gi].get();
     __syncthreads();
   }
 }
 
-// Gate/up for one (M tile, N tile of 32 features): h[pair][feature] = silu(g) * u.
-__global__ __launch_bounds__(256) void k_gu_mfma(FfnArgs a) {
+// Gate/up for one (M tile, N tile of kNT/2 features): h[pair][feature] = silu(g) * u.
+__global__ __launch_bounds__(kThreads) void k_gu_mfma(FfnArgs a) {
   __shared__ __align__(16) uint8_t s_b[2 * kBStage];
   __shared__ const uint8_t *s_colp[kNT];
   __shared__ const uint8_t *s_sclp[kNT];
@@ -178,7 +233,7 @@ __global__ __launch_bounds__(256) void k_gu_mfma(FfnArgs a) {
   const MTile mt = mtile_of(a, m);
   const bool sh = mt.e == a.E;
   const int inter = sh ? a.Is : a.I;
-  const int nt = blockIdx.y;
+  const int nt = blockIdx.y;  // features nt*kNT/2 ..
   if (nt * (kNT / 2) >= inter) return;
   const uint8_t *ex = sh ? a.shared : expert_ptr(a, mt.e);
   if (!ex) return;  // the down GEMM poisons this tile's rows
@@ -186,41 +241,43 @@ __global__ __launch_bounds__(256) void k_gu_mfma(FfnArgs a) {
   const size_t gtb = gu_tile_bytes(a.H);
   if (threadIdx.x < kNT) {
     const int c = threadIdx.x;
-    const uint8_t *tile = ex + (size_t)(nt * 8 + c / 8) * gtb;
+    // columns past 2 * inter (a partial last tile) read the last gate/up tile and are not stored
+    const int tt = min(nt * (kNT / 8) + c / 8, inter / kGuPairs - 1);
+    const uint8_t *tile = ex + (size_t)tt * gtb;
     s_colp[c] = tile + (size_t)(c % 8) * (a.H / 2);
     s_sclp[c] = tile + (size_t)kGuRows * (a.H / 2) + 2 * (c % 8);
   }
   tile_rows(a, mt, s_tok, s_pair);
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  size_t arow[2];
+  const int wm = wave, wn = 0;  // rows 32 wm .. 32 wm + 31, all columns
+  size_t arow[kMB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) arow[mb] = (size_t)s_tok[wave * 32 + mb * 16 + (lane & 15)] * a.H;
+  for (int mb = 0; mb < kMB; ++mb) arow[mb] = (size_t)s_tok[wm * 32 + mb * 16 + (lane & 15)] * a.H;
   GemmAcc C;
-  if (a.x_bf16)
-    gemm_loop<true>(C, a.H / kGroup, s_colp, s_sclp, s_b, a.x, arow, lane);
-  else
-    gemm_loop<false>(C, a.H / kGroup, s_colp, s_sclp, s_b, a.x, arow, lane);
+  gemm_loop<true>(C, a.H / kGroup, s_colp, s_sclp, s_b, a.x_bf16 ? a.x : (const void *)a.xb, arow, wn, lane);
   // epilogue: even columns are gate, the next lane holds the matching up
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float gv = C.acc[mb][nb][i];
         const float uv = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(gv), 0xB1, 0xF, 0xF, false));
-        const int j = wave * 32 + mb * 16 + (lane >> 4) * 4 + i;
-        const int c = nb * 16 + (lane & 15);
-        if ((c & 1) == 0 && j < mt.n) {
-          const int f = nt * (kNT / 2) + (c / 8) * kGuPairs + (c % 8) / 2;
-          a.h[(size_t)s_pair[j] * Imax + f] = gv / (1.0f + expf(-gv)) * uv;
+        const int j = wm * 32 + mb * 16 + (lane >> 4) * 4 + i;
+        const int c = wn * 16 * kNB + nb * 16 + (lane & 15);
+        const int f = nt * (kNT / 2) + (c / 8) * kGuPairs + (c % 8) / 2;
+        if ((c & 1) == 0 && j < mt.n && f < inter) {
+          const float hv = gv / (1.0f + expf(-gv)) * uv;
+          // bf16 in the first half of the row's fp32 storage: the down GEMM's A operand
+          ((__bf16 *)a.h)[(size_t)s_pair[j] * 2 * Imax + f] = (__bf16)hv;
         }
       }
 }
 
-// Down for one (M tile, N tile of 64 output rows): part[pair][row] = Wd h.
-__global__ __launch_bounds__(256) void k_dn_mfma(FfnArgs a) {
+// Down for one (M tile, N tile of kNT output rows): part[pair][row] = Wd h.
+__global__ __launch_bounds__(kThreads) void k_dn_mfma(FfnArgs a) {
   __shared__ __align__(16) uint8_t s_b[2 * kBStage];
   __shared__ const uint8_t *s_colp[kNT];
   __shared__ const uint8_t *s_sclp[kNT];
@@ -251,37 +308,54 @@ __global__ __launch_bounds__(256) void k_dn_mfma(FfnArgs a) {
   }
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  size_t arow[2];
+  const int wm = wave, wn = 0;
+  size_t arow[kMB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) arow[mb] = (size_t)s_pair[wave * 32 + mb * 16 + (lane & 15)] * Imax;
+  for (int mb = 0; mb < kMB; ++mb) arow[mb] = (size_t)s_pair[wm * 32 + mb * 16 + (lane & 15)] * 2 * Imax;
   GemmAcc C;
-  gemm_loop<false>(C, inter / kGroup, s_colp, s_sclp, s_b, a.h, arow, lane);
+  gemm_loop<true>(C, inter / kGroup, s_colp, s_sclp, s_b, a.h, arow, wn, lane);
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = wave * 32 + mb * 16 + (lane >> 4) * 4 + i;
-        const int n = n0 + nb * 16 + (lane & 15);
+        const int j = wm * 32 + mb * 16 + (lane >> 4) * 4 + i;
+        const int n = n0 + wn * 16 * kNB + nb * 16 + (lane & 15);
         if (j < mt.n && n < a.H) a.part[(size_t)s_pair[j] * a.H + n] = C.acc[mb][nb][i];
       }
+}
+
+// fp32 activations -> bf16 (RNE), eight per thread.
+__global__ __launch_bounds__(256) void k_x_to_bf16(const float *x, uint16_t *xb, long n8) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const float4 p = ldg<float4>(x + 8 * i), q = ldg<float4>(x + 8 * i + 4);
+  stg<uint4>(xb + 8 * i, make_uint4(pack_bf16(p.x, p.y), pack_bf16(p.z, p.w), pack_bf16(q.x, q.y), pack_bf16(q.z, q.w)));
 }
 
 }  // namespace
 
 hipError_t launch_gu_mfma(const FfnArgs &a, hipStream_t st) {
   if (a.mfma_thr <= 0 || a.max_mtiles <= 0) return hipSuccess;
+  if (!a.x_bf16) {
+    ProfScope ps("x_bf16", st);
+    const long n8 = (long)a.S * a.H / 8;
+    MOE_LAUNCH(k_x_to_bf16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, (const float *)a.x, a.xb, n8);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   ProfScope ps("gateup_mfma", st);
   const int Imax = std::max(a.I, a.Is);
-  MOE_LAUNCH(k_gu_mfma, dim3((unsigned)a.max_mtiles, (unsigned)(Imax / (kNT / 2))), dim3(256), 0, st, a);
+  MOE_LAUNCH(k_gu_mfma, dim3((unsigned)a.max_mtiles, (unsigned)((2 * Imax + kNT - 1) / kNT)), dim3(kThreads), 0, st,
+             a);
   return hipGetLastError();
 }
 
 hipError_t launch_dn_mfma(const FfnArgs &a, hipStream_t st) {
   if (a.mfma_thr <= 0 || a.max_mtiles <= 0) return hipSuccess;
   ProfScope ps("down_mfma", st);
-  MOE_LAUNCH(k_dn_mfma, dim3((unsigned)a.max_mtiles, (unsigned)((a.H + kNT - 1) / kNT)), dim3(256), 0, st, a);
+  MOE_LAUNCH(k_dn_mfma, dim3((unsigned)a.max_mtiles, (unsigned)((a.H + kNT - 1) / kNT)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -19,54 +19,6 @@
 namespace moe {
 namespace {
 
-__device__ inline float load_x(const void *x, int bf16, size_t i) {
-  if (bf16) {
-    uint32_t b = (uint32_t)((const uint16_t *)x)[i] << 16;
-    return __uint_as_float(b);
-  }
-  return ((const float *)x)[i];
-}
-
-__device__ inline double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-constexpr int kLogitTokens = 4;  // tokens per block in the logits kernel
-
-// One wave per expert row, kLogitTokens tokens per block: lanes stride over H in
-// float4 chunks, fp64 FMA, then a wave reduction.
-__global__ __launch_bounds__(256) void k_route_logits(RouteArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + wave;
-  const int t0 = blockIdx.y * kLogitTokens;
-  if (e >= a.E) return;
-  const int nt = min(kLogitTokens, a.S - t0);
-  double acc[kLogitTokens];
-#pragma unroll
-  for (int s = 0; s < kLogitTokens; ++s) acc[s] = 0.0;
-  const float *wr = a.W + (size_t)e * a.H;
-  for (int c = lane * 4; c < a.H; c += 256) {
-    const float4 wv = *(const float4 *)(wr + c);
-#pragma unroll
-    for (int s = 0; s < kLogitTokens; ++s) {
-      if (s < nt) {
-        const size_t base = (size_t)(t0 + s) * a.H + c;
-        acc[s] = fma((double)wv.x, (double)load_x(a.x, a.x_bf16, base + 0), acc[s]);
-        acc[s] = fma((double)wv.y, (double)load_x(a.x, a.x_bf16, base + 1), acc[s]);
-        acc[s] = fma((double)wv.z, (double)load_x(a.x, a.x_bf16, base + 2), acc[s]);
-        acc[s] = fma((double)wv.w, (double)load_x(a.x, a.x_bf16, base + 3), acc[s]);
-      }
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < kLogitTokens; ++s) {
-    double v = wave_sum_f64(acc[s]);
-    if (lane == 0 && s < nt) a.logits[(size_t)(t0 + s) * a.E + e] = v;
-  }
-}
-
 // Raw buffer resource over `bytes` bytes at p: loads at byte offsets past the
 // end return zeros (range-checked in hardware; 0x00020000 is the gfx9-family
 // data-format word that raw dword loads need).
@@ -243,6 +195,83 @@ __device__ inline double wave_sum_f64_to63(double v) {
   return v;
 }
 
+// Many tokens: the logits GEMM in fp64, one workgroup per 64 tokens x 32
+// experts.  K advances in chunks of 32 staged in LDS (double-buffered, as fp32:
+// bf16 and fp32 inputs both widen to fp32 exactly); each
+// thread accumulates 4 tokens (strided by 16, so that its LDS reads are free of
+// bank conflicts) x 2 experts with fp64 FMA in h order.
+constexpr int kLT = 64, kLE = 32, kLK = 32, kLPad = 36;  // row stride 144 B
+__global__ __launch_bounds__(256) void k_route_logits_tiled(RouteArgs a) {
+  __shared__ __align__(16) float xs[2][kLT][kLPad];
+  __shared__ __align__(16) float wsm[2][kLE][kLPad];
+  const int t0 = blockIdx.x * kLT, e0 = blockIdx.y * kLE;
+  const int tid = threadIdx.x;
+  const int xr = tid >> 2, xc = (tid & 3) * 8;  // loader: x row, 8 columns
+  const int wr = tid >> 3, wc = (tid & 7) * 4;  // loader: W row, 4 columns
+  const size_t xrow = (size_t)min(t0 + xr, a.S - 1) * a.H;  // rows past S / E are clamped, not stored
+  const float *wrow = a.W + (size_t)min(e0 + wr, a.E - 1) * a.H;
+  const int ct = tid & 15, ce = (tid >> 4) * 2;
+  auto load_x = [&](int k0, float4 &p, float4 &q) {
+    if (a.x_bf16) {
+      const uint4 r = *(const uint4 *)((const uint16_t *)a.x + xrow + k0 + xc);
+      p = make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u), __uint_as_float(r.y << 16),
+                      __uint_as_float(r.y & 0xFFFF0000u));
+      q = make_float4(__uint_as_float(r.z << 16), __uint_as_float(r.z & 0xFFFF0000u), __uint_as_float(r.w << 16),
+                      __uint_as_float(r.w & 0xFFFF0000u));
+    } else {
+      p = *(const float4 *)((const float *)a.x + xrow + k0 + xc);
+      q = *(const float4 *)((const float *)a.x + xrow + k0 + xc + 4);
+    }
+  };
+  float4 px, qx, pw;
+  load_x(0, px, qx);
+  pw = *(const float4 *)(wrow + wc);
+  *(float4 *)&xs[0][xr][xc] = px;
+  *(float4 *)&xs[0][xr][xc + 4] = qx;
+  *(float4 *)&wsm[0][wr][wc] = pw;
+  __syncthreads();
+  double acc[4][2];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r][0] = acc[r][1] = 0.0;
+  const int nk = a.H / kLK;
+  for (int kc = 0; kc < nk; ++kc) {
+    const int kn = min(kc + 1, nk - 1) * kLK;  // unconditional prefetch (the last one repeats)
+    load_x(kn, px, qx);
+    pw = *(const float4 *)(wrow + kn + wc);
+    const int b = kc & 1;
+#pragma unroll
+    for (int kk = 0; kk < kLK; kk += 4) {
+      float4 xv[4], wv[2];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) xv[r] = *(const float4 *)&xs[b][ct + 16 * r][kk];
+      wv[0] = *(const float4 *)&wsm[b][ce][kk];
+      wv[1] = *(const float4 *)&wsm[b][ce + 1][kk];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          double t = acc[r][c];
+          t = fma((double)xv[r].x, (double)wv[c].x, t);
+          t = fma((double)xv[r].y, (double)wv[c].y, t);
+          t = fma((double)xv[r].z, (double)wv[c].z, t);
+          t = fma((double)xv[r].w, (double)wv[c].w, t);
+          acc[r][c] = t;
+        }
+    }
+    *(float4 *)&xs[b ^ 1][xr][xc] = px;
+    *(float4 *)&xs[b ^ 1][xr][xc + 4] = qx;
+    *(float4 *)&wsm[b ^ 1][wr][wc] = pw;
+    __syncthreads();
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int t = t0 + ct + 16 * r, e = e0 + ce + c;
+      if (t < a.S && e < a.E) a.logits[(size_t)t * a.E + e] = acc[r][c];
+    }
+}
+
 // Few tokens (S <= kFewTokens), one launch for the whole router: one workgroup
 // per expert computes that expert's logits (its 4 waves split H; every load of
 // a lane is issued before the FMAs; partial sums meet in LDS in a fixed order),
@@ -377,8 +406,8 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
   }
   {
     ProfScope ps("route_logits", st);
-    dim3 grid((a.E + 3) / 4, (a.S + kLogitTokens - 1) / kLogitTokens);
-    MOE_LAUNCH(k_route_logits, grid, dim3(256), 0, st, a);
+    MOE_LAUNCH(k_route_logits_tiled, dim3((unsigned)((a.S + kLT - 1) / kLT), (unsigned)((a.E + kLE - 1) / kLE)),
+               dim3(256), 0, st, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
