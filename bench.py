@@ -32,12 +32,14 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the sources of the decode kernels (counter readings go stale when they change)."""
+    """sha256 over the library's kernel sources (counter readings go stale when they change)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("ffn_gemv.hip", "dot.h", "common.h"):
-        with open(os.path.join(ROOT, "int4_routed_expert_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "int4_routed_expert_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")) and f != "hbm_probe.hip":
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
 
 
@@ -528,11 +530,11 @@ def main() -> int:
     M.moe_profile_enable(False)
     kernels = {name: {"avg_us": ms * 1e3 / n, "launches": n} for name, (ms, n) in prof.items()}
     log("per-kernel (hipEvent) averages:", json.dumps(kernels))
-    gu_bytes = 9 * 2 * (I * H // 2 + I * (H // 32) * 2)  # gate+up payload and scales of 9 experts
-    gu_us = kernels["gateup_s1"]["avg_us"]
-    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
-
-    traffic = measured_traffic("gateup_s1")
+    rk = "gateup_s1"  # dominant kernel: gate/up of the 9 experts (payload and scales)
+    alg_bytes = 9 * 2 * (I * H // 2 + I * (H // 32) * 2)
+    k_us = kernels[rk]["avg_us"]
+    achieved = alg_bytes / (k_us * 1e-6) / 1e9
+    traffic = measured_traffic(rk)
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample ------------------------
     cpu = None
@@ -582,9 +584,9 @@ def main() -> int:
         "router_bytes_per_token": router_bytes,
         "eager_us_per_step": eager_us,
         "kernels_us": {n: round(v["avg_us"], 3) for n, v in kernels.items()},
-        "roofline": {"kernel": "gateup_s1", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+        "roofline": {"kernel": rk, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": gu_bytes},
+                     "algorithmic_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -275,8 +275,13 @@ int moe_unpack_expert(const moe_cfg *c, int32_t inter, const void *src, uint8_t 
   return MOE_OK;
 }
 
-int moe_route(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const float *W, const float *bias,
-              int32_t *idx, float *w, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace moe {
+
+// Argument checks and kernel arguments of moe_route and moe_ffn.
+static int route_args(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const float *W, const float *bias,
+                      int32_t *idx, float *w, void *ws, size_t ws_bytes, RouteArgs &a) {
   int v = moe_validate_cfg(c);
   if (v) return v;
   if (S < 0) return MOE_EINVAL;
@@ -285,18 +290,17 @@ int moe_route(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const
   if (!x || !W || !bias || !idx || !w || !ws) return MOE_ENULL;
   const WsLayout L = ws_layout(*c, S);
   if (ws_bytes < L.total) return MOE_EWORKSPACE;
-  RouteArgs a{};
+  a = RouteArgs{};
   a.H = c->hidden; a.E = c->n_experts; a.G = c->n_group; a.Gk = c->topk_group; a.k = c->top_k; a.S = S;
   a.x_bf16 = x_dtype == MOE_BF16; a.norm = c->norm_topk_prob; a.rsf = c->routed_scaling_factor;
   a.x = x; a.W = W; a.bias = bias; a.idx = idx; a.w = w;
   a.logits = (double *)((char *)ws + L.logits);
   a.sync = (uint32_t *)((char *)ws + L.sync);
-  hipError_t e = launch_route(a, (hipStream_t)stream);
-  return e == hipSuccess ? MOE_OK : hip_fail(e);
+  return MOE_OK;
 }
 
-int moe_ffn(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const int32_t *idx, const float *w,
-            const moe_slot_view *ex, const void *shared, float *y, void *ws, size_t ws_bytes, void *stream) {
+static int ffn_args(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const int32_t *idx, const float *w,
+                    const moe_slot_view *ex, const void *shared, float *y, void *ws, size_t ws_bytes, FfnArgs &a) {
   int v = moe_validate_cfg(c);
   if (v) return v;
   if (S < 0) return MOE_EINVAL;
@@ -307,7 +311,7 @@ int moe_ffn(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const i
   if (ex->n_slots < 1 || ex->slot_bytes < slot_stride(c->hidden, c->moe_inter) || ex->slot_bytes % 256) return MOE_EINVAL;
   const WsLayout L = ws_layout(*c, S);
   if (ws_bytes < L.total) return MOE_EWORKSPACE;
-  FfnArgs a{};
+  a = FfnArgs{};
   a.H = c->hidden; a.E = c->n_experts; a.k = c->top_k; a.I = c->moe_inter; a.Is = c->shared_inter; a.S = S;
   a.x_bf16 = x_dtype == MOE_BF16;
   a.x = x; a.idx = idx; a.w = w;
@@ -321,13 +325,11 @@ int moe_ffn(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const i
   a.hl = (uint32_t *)(b + L.hl);
   a.hf = (float *)(b + L.hf);
   a.n_cu = device_cus();
-  hipError_t e;
   if (S <= kSmallS) {
     // one-token down kernel: about one row block per compute unit, at most 8 tiles each
     const int nt = c->hidden / kDnRows;
     a.tb = std::min(8, std::max(1, (nt + a.n_cu - 1) / a.n_cu));
     a.n_blk = (nt + a.tb - 1) / a.tb;
-    e = launch_ffn_decode(a, (hipStream_t)stream);
   } else {
     a.part = (float *)(b + L.part);
     a.lists = (int32_t *)(b + L.lists);
@@ -339,8 +341,33 @@ int moe_ffn(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const i
     a.xb = (uint16_t *)(b + L.xb);
     a.max_mtiles = L.max_mtiles;
     a.mfma_thr = c->mfma_min_tokens;
-    e = launch_ffn_batch(a, (hipStream_t)stream);
   }
+  return MOE_OK;
+}
+
+static hipError_t run_ffn(const FfnArgs &a, hipStream_t st) {
+  return a.S <= kSmallS ? launch_ffn_decode(a, st) : launch_ffn_batch(a, st);
+}
+
+}  // namespace moe
+
+extern "C" {
+
+int moe_route(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const float *W, const float *bias,
+              int32_t *idx, float *w, void *ws, size_t ws_bytes, void *stream) {
+  RouteArgs a;
+  const int v = route_args(c, x, x_dtype, S, W, bias, idx, w, ws, ws_bytes, a);
+  if (v || S == 0) return v;
+  hipError_t e = launch_route(a, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int moe_ffn(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const int32_t *idx, const float *w,
+            const moe_slot_view *ex, const void *shared, float *y, void *ws, size_t ws_bytes, void *stream) {
+  FfnArgs a;
+  const int v = ffn_args(c, x, x_dtype, S, idx, w, ex, shared, y, ws, ws_bytes, a);
+  if (v || S == 0) return v;
+  hipError_t e = run_ffn(a, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 

@@ -29,60 +29,10 @@
 // same tile math runs over (unique expert, tile) pairs.
 #include <algorithm>
 
-#include "dot.h"
+#include "gemv_dev.h"
 
 namespace moe {
 namespace {
-
-__device__ inline float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
-
-// 32 activations (fp32, or bf16 bits) starting at element `off`.
-__device__ inline void load32(const void *x, int bf16, size_t off, float *v) {
-  if (bf16) {
-    const uint16_t *p = (const uint16_t *)x + off;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint4 r = ldg<uint4>(p + 8 * m);
-      const uint32_t d[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * m + 2 * j] = __uint_as_float(d[j] << 16);
-        v[8 * m + 2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
-      }
-    }
-  } else {
-    const float *p = (const float *)x + off;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const float4 r = ldg<float4>(p + 4 * m);
-      v[4 * m] = r.x; v[4 * m + 1] = r.y; v[4 * m + 2] = r.z; v[4 * m + 3] = r.w;
-    }
-  }
-}
-
-__device__ inline void store_limbs(uint32_t *dst, float *fdst, const Limbs &L) {
-  uint4 *d = (uint4 *)dst;
-#pragma unroll
-  for (int l = 0; l < 6; ++l) d[l] = make_uint4(L.L[l][0], L.L[l][1], L.L[l][2], L.L[l][3]);
-  *fdst = L.f;
-}
-__device__ inline void load_limbs_lds(const uint32_t *src, const float *fsrc, Limbs &L) {
-  const uint4 *s = (const uint4 *)src;
-#pragma unroll
-  for (int l = 0; l < 6; ++l) {
-    const uint4 r = s[l];
-    L.L[l][0] = r.x; L.L[l][1] = r.y; L.L[l][2] = r.z; L.L[l][3] = r.w;
-  }
-  L.f = *fsrc;
-}
-__device__ inline void load_limbs_global(const uint32_t *src, const float *fsrc, Limbs &L) {
-#pragma unroll
-  for (int l = 0; l < 6; ++l) {
-    const uint4 r = ldg<uint4>(src + 4 * l);
-    L.L[l][0] = r.x; L.L[l][1] = r.y; L.L[l][2] = r.z; L.L[l][3] = r.w;
-  }
-  L.f = ldg<float>(fsrc);
-}
 
 // ---- activations -> limbs (global), one thread per (row, group) ---------------
 __global__ __launch_bounds__(256) void k_to_limbs(const void *src, int bf16, int rows, int K, int stride,
@@ -100,81 +50,6 @@ __global__ __launch_bounds__(256) void k_to_limbs(const void *src, int bf16, int
   for (int l = 0; l < 6; ++l) stg<uint4>(d + l, make_uint4(L.L[l][0], L.L[l][1], L.L[l][2], L.L[l][3]));
   stg<float>(factors + i, L.f);
 }
-
-// ---- one token: gate/up ---------------------------------------------------------
-template <int NG>
-struct GuFeat {
-  uint4 g[NG], u[NG];
-  uint32_t s[NG];  // fp16 scales of (gate r, up r) for the lane's groups
-  int valid;
-};
-
-// Slot of routed expert `lane` (< k): idx entry in [0, E) and table entry in
-// [0, n_slots), else 0 (the expert's outputs become NaN).
-__device__ inline uint64_t routed_ptr_lane(const FfnArgs &a, int lane) {
-  uint64_t p = 0;
-  if (lane < a.k) {
-    const int e = ldg<int>(a.idx + lane);
-    if (e >= 0 && e < a.E) {
-      const int s = ldg<int>(a.table + e);
-      if (s >= 0 && s < a.n_slots) p = (uint64_t)(uintptr_t)(a.base + (size_t)s * (size_t)a.slot_bytes);
-    }
-  }
-  return p;
-}
-
-// Loads of feature i of this wave's list (clamped into range so that loads are
-// unconditional; lanes past the last group read the last group and contribute
-// zero because their activation limbs are zero).
-template <int NG>
-__device__ inline void gu_feat_load(GuFeat<NG> &b, const FfnArgs &a, int i, int n, int ns, int s0, int r0,
-                                    uint64_t my_ptr, int lane) {
-  const int H = a.H, ng = H / kGroup;
-  i = min(i, n - 1);
-  int r;
-  const uint8_t *ex;
-  if (i < ns) {
-    r = s0 + i;
-    ex = a.shared;
-  } else {
-    const int f = r0 + i - ns, j = f / a.I;
-    r = f - j * a.I;
-    ex = lane_ptr(my_ptr, j);
-  }
-  b.valid = ex != nullptr;
-  if (!ex) ex = a.base;  // readable stand-in; the result is replaced by NaN
-  const int pos = r & 3;
-  const uint8_t *tile = ex + (size_t)(r >> 2) * gu_tile_bytes(H);
-  const uint8_t *rg = tile + (size_t)(2 * pos) * (H / 2);
-  const uint8_t *sc = tile + (size_t)kGuRows * (H / 2) + 4 * pos;
-#pragma unroll
-  for (int j = 0; j < NG; ++j) {
-    const int g = min(lane + 64 * j, ng - 1);
-    b.g[j] = ldg<uint4>(rg + g * 16);
-    b.u[j] = ldg<uint4>(rg + H / 2 + g * 16);
-    b.s[j] = ldg<uint32_t>(sc + g * 16);
-  }
-}
-
-// h of one feature: the sums land in lane 63; the value is parked in lane
-// `slot` of hout so that the loop issues no stores (stores would perturb the
-// in-order load counter the prefetch ring relies on).
-template <int NG>
-__device__ inline float gu_feat_compute(const GuFeat<NG> &b, const Limbs (&xv)[NG], int slot, float hout) {
-  float g = 0.f, u = 0.f;
-#pragma unroll
-  for (int j = 0; j < NG; ++j) {
-    g = fmaf(group_dot(b.g[j], xv[j]), half_bits_to_float(b.s[j]) * xv[j].f, g);
-    u = fmaf(group_dot(b.u[j], xv[j]), half_bits_to_float(b.s[j] >> 16) * xv[j].f, u);
-  }
-  g = wave_sum_to63(g);
-  u = wave_sum_to63(u);
-  const float hv = b.valid ? silu_mul(g, u) : __builtin_nanf("");
-  const float h63 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hv), 63));
-  return (int)(threadIdx.x & 63) == slot ? h63 : hout;
-}
-
-constexpr int kGuMaxPerWave = 64;  // features per wave (one parked h per lane)
 
 template <int NG>
 __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
@@ -240,47 +115,6 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
     stg<float>(a.h + hrow, hout);
   }
 }
-
-// ---- one token: down + route-order combine -----------------------------------------
-template <int NGD>
-struct DnTile {
-  uint4 q[kDnRows][NGD], sc[NGD];
-};
-
-// Tile t (clamped to the block's last tile: loads stay unconditional).
-template <int NGD>
-__device__ inline void dn_tile_load(DnTile<NGD> &b, const uint8_t *dn, int inter, int t, int t1, int lane) {
-  const int ng = inter / kGroup;
-  const uint8_t *tile = dn + (size_t)min(t, t1 - 1) * dn_tile_bytes(inter);
-#pragma unroll
-  for (int j = 0; j < NGD; ++j) {
-    const int g = min(lane + 64 * j, ng - 1);
-#pragma unroll
-    for (int i = 0; i < kDnRows; ++i) b.q[i][j] = ldg<uint4>(tile + (size_t)i * (inter / 2) + g * 16);
-    b.sc[j] = ldg<uint4>(tile + (size_t)kDnRows * (inter / 2) + g * 16);
-  }
-}
-
-__device__ inline float scale_of(const uint4 sc, int i) {
-  const uint32_t d[4] = {sc.x, sc.y, sc.z, sc.w};
-  return half_bits_to_float(d[i >> 1] >> (16 * (i & 1)));
-}
-
-// 8 row dots of one tile against one activation set; lane 63 holds the sums.
-template <int NGD>
-__device__ inline void dn_tile_dots(const DnTile<NGD> &b, const Limbs (&hv)[NGD], float (&acc)[kDnRows]) {
-#pragma unroll
-  for (int i = 0; i < kDnRows; ++i) acc[i] = 0.f;
-#pragma unroll
-  for (int j = 0; j < NGD; ++j)
-#pragma unroll
-    for (int i = 0; i < kDnRows; ++i) acc[i] = fmaf(group_dot(b.q[i][j], hv[j]), scale_of(b.sc[j], i) * hv[j].f, acc[i]);
-#pragma unroll
-  for (int i = 0; i < kDnRows; ++i) acc[i] = wave_sum_to63(acc[i]);
-}
-
-constexpr int kDnMaxTb = 8;    // down tiles per row block, at most
-constexpr int kDnS1Waves = 9;  // waves per one-token down workgroup
 
 // HLDS: h of every expert is converted to limbs into LDS by the workgroup;
 // otherwise the limbs come from global memory (converted by k_to_limbs).

@@ -1,0 +1,278 @@
+// Device helpers of the router, shared by the router kernels and the one-token
+// layer kernel: bounded buffer loads, the per-token selection (one wave per
+// token), and the few-token logits (one workgroup per expert) with its
+// completion hand-off.  See route.hip for the method and its citations.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// Raw buffer resource over `bytes` bytes at p: loads at byte offsets past the
+// end return zeros (range-checked in hardware; 0x00020000 is the gfx9-family
+// data-format word that raw dword loads need).
+__device__ inline __amdgpu_buffer_rsrc_t share_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
+}
+__device__ inline float4 buf_f4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+__device__ inline uint2 buf_u2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  return make_uint2(v.x, v.y);
+}
+
+// ---- selection ------------------------------------------------------------------
+// Monotone map of fp32 keys to uint32 (0 is below every key), so that the
+// wave-wide arg-max is an integer max; ties are then broken towards the lower
+// expert index.
+__device__ inline uint32_t ordered_key(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ inline uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Maximum over the wave, returned to every lane.
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<0xB1>(v));        // quad_perm [1,0,3,2]
+  v = max(v, dpp_u<0x4E>(v));        // quad_perm [2,3,0,1]
+  v = max(v, dpp_u<0x141>(v));       // row_half_mirror
+  v = max(v, dpp_u<0x140>(v));       // row_mirror
+  v = max(v, dpp_u<0x142, 0xA>(v));  // row_bcast:15
+  v = max(v, dpp_u<0x143, 0xC>(v));  // row_bcast:31: lane 63 holds the maximum
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// s = sigmoid(l) and key = fp32(s + bias) of one (token, expert), fp64.
+__device__ inline void score(double l, float bias, double &s, float &key) {
+  s = 1.0 / (1.0 + exp(-l));
+  key = __double2float_rn(s + (double)bias);
+}
+
+// One wave selects for token t from its keys and scores already in LDS (skey,
+// ssg: E entries each): group scores, the Gk kept groups, then k rounds of
+// wave arg-max over the kept experts' keys.  Lane l holds experts l, l+64, ...
+// (NPL experts per lane, E <= 64*NPL).
+template <int NPL>
+__device__ void select_wave(const RouteArgs &a, int t, const float *skey, const double *ssg, int lane) {
+  const int E = a.E, G = a.G, per = a.E / a.G;
+  // group score: fp32 sum of the group's two largest keys (one lane per group)
+  float gs = -INFINITY;
+  if (lane < G) {
+    // top two with multiplicity, branch-free: k1 >= k2 always
+    float k1 = -INFINITY, k2 = -INFINITY;
+    const float *p = skey + lane * per;
+    if ((per & 3) == 0) {
+      const float4 *p4 = (const float4 *)p;
+#pragma unroll 8
+      for (int i = 0; i < per / 4; ++i) {
+        const float4 v = p4[i];
+        k2 = fmaxf(k2, fminf(k1, v.x)); k1 = fmaxf(k1, v.x);
+        k2 = fmaxf(k2, fminf(k1, v.y)); k1 = fmaxf(k1, v.y);
+        k2 = fmaxf(k2, fminf(k1, v.z)); k1 = fmaxf(k1, v.z);
+        k2 = fmaxf(k2, fminf(k1, v.w)); k1 = fmaxf(k1, v.w);
+      }
+    } else {
+      for (int i = 0; i < per; ++i) {
+        const float v = p[i];
+        k2 = fmaxf(k2, fminf(k1, v));
+        k1 = fmaxf(k1, v);
+      }
+    }
+    gs = per == 1 ? k1 : __double2float_rn((double)k1 + (double)k2);
+  }
+  // keep the Gk best groups (ties: lower group index)
+  int rk = 0;
+  for (int i = 0; i < G; ++i) {
+    const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gs), i));
+    rk += (v > gs || (v == gs && i < lane)) ? 1 : 0;
+  }
+  const uint64_t kept = __ballot(lane < G && rk < a.Gk);
+  uint32_t cand[NPL];
+#pragma unroll
+  for (int m = 0; m < NPL; ++m) {
+    const int e = lane + 64 * m;
+    cand[m] = (e < E && ((kept >> (e / per)) & 1)) ? ordered_key(skey[e]) : 0u;
+  }
+  int my_idx = -1;  // lane r < k: expert of rank r
+  for (int r = 0; r < a.k; ++r) {
+    uint32_t loc = 0;
+#pragma unroll
+    for (int m = 0; m < NPL; ++m) loc = max(loc, cand[m]);
+    const uint32_t K = wave_max_u32(loc);
+    if (K == 0u) break;  // no candidate left (cannot happen for a valid cfg)
+    int lowest = 0x7fffffff;  // this lane's lowest expert holding K
+#pragma unroll
+    for (int m = NPL - 1; m >= 0; --m)
+      if (cand[m] == K) lowest = lane + 64 * m;
+    uint64_t holders = __ballot(lowest != 0x7fffffff);
+    int e = __builtin_amdgcn_readlane(lowest, (int)__builtin_ctzll(holders));
+    holders &= holders - 1;
+    while (holders) {  // more than one lane only on exactly equal keys
+      e = min(e, __builtin_amdgcn_readlane(lowest, (int)__builtin_ctzll(holders)));
+      holders &= holders - 1;
+    }
+#pragma unroll
+    for (int m = 0; m < NPL; ++m)
+      if (lane + 64 * m == e) cand[m] = 0u;
+    if (lane == r) my_idx = e;
+  }
+  const double my_s = my_idx >= 0 ? ssg[my_idx] : 0.0;
+  double denom = 0.0;  // scores summed in rank order
+  for (int r = 0; r < a.k; ++r) {
+    const int lo = __builtin_amdgcn_readlane((int)__double2loint(my_s), r);
+    const int hi = __builtin_amdgcn_readlane((int)__double2hiint(my_s), r);
+    denom += __hiloint2double(hi, lo);
+  }
+  if (lane < a.k) {
+    const double wv = a.norm ? my_s / denom * (double)a.rsf : my_s * (double)a.rsf;
+    a.idx[(size_t)t * a.k + lane] = my_idx;
+    a.w[(size_t)t * a.k + lane] = my_idx >= 0 ? (float)wv : __builtin_nanf("");
+  }
+}
+
+__device__ void select_wave_dispatch(const RouteArgs &a, int t, const float *skey, const double *ssg, int lane) {
+  const int npl = (a.E + 63) / 64;
+  if (npl <= 1) select_wave<1>(a, t, skey, ssg, lane);
+  else if (npl <= 2) select_wave<2>(a, t, skey, ssg, lane);
+  else if (npl <= 4) select_wave<4>(a, t, skey, ssg, lane);
+  else if (npl <= 8) select_wave<8>(a, t, skey, ssg, lane);
+  else select_wave<16>(a, t, skey, ssg, lane);
+}
+
+// fp64 sum over the wave into lane 63 (DPP on the two halves; fixed order).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ inline double dpp_d(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROW_MASK, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROW_MASK, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+__device__ inline double wave_sum_f64_to63(double v) {
+  v += dpp_d<0xB1>(v);
+  v += dpp_d<0x4E>(v);
+  v += dpp_d<0x141>(v);
+  v += dpp_d<0x140>(v);
+  v += dpp_d<0x142, 0xA>(v);
+  v += dpp_d<0x143, 0xC>(v);
+  return v;
+}
+
+constexpr int kFewTokens = 8;  // the one-launch router handles up to this many tokens
+
+// Few-token logits of expert e, part 1: waves 0..3 issue the loads of their
+// quarter of W's row (bounded buffer loads: lanes past the share read zeros,
+// so every load is unconditional and all are in flight together).
+constexpr int kFewChunks = 8;  // ceil((H/4) / 256) <= 8 for H <= 8192
+__device__ inline void few_logits_load(const RouteArgs &a, int e, int wave, int lane, float4 (&wv)[kFewChunks]) {
+  const int q = a.H / 4;  // each wave's share of H (a multiple of 8)
+  const __amdgpu_buffer_rsrc_t rw = share_rsrc(a.W + (size_t)e * a.H + (size_t)(wave & 3) * q, (uint32_t)q * 4u);
+#pragma unroll
+  for (int m = 0; m < kFewChunks; ++m) wv[m] = buf_f4(rw, (uint32_t)(m * 256 + lane * 4) * 4u);
+}
+
+// Part 2: waves 0..3 form the fp64 dots with the tokens' activations (same
+// bounded loads), reduce each to lane 63, and the four shares are added in a
+// fixed order by thread s < S, which stores logit (s, e).  Every thread of the
+// workgroup must call it (one barrier); waves past the fourth only wait.
+__device__ inline void few_logits_finish(const RouteArgs &a, int e, int wave, int lane, const float4 (&wv)[kFewChunks],
+                                         double (*part)[kFewTokens]) {
+  const int q = a.H / 4;
+  const size_t seg = (size_t)wave * q;
+  if (wave < 4) {
+    double acc[kFewTokens];
+#pragma unroll
+    for (int s = 0; s < kFewTokens; ++s) {
+      acc[s] = 0.0;
+      if (s < a.S) {
+        float4 xv[kFewChunks];
+        if (a.x_bf16) {
+          const __amdgpu_buffer_rsrc_t rx =
+              share_rsrc((const uint16_t *)a.x + (size_t)s * a.H + seg, (uint32_t)q * 2u);
+          uint2 raw[kFewChunks];
+#pragma unroll
+          for (int m = 0; m < kFewChunks; ++m) raw[m] = buf_u2(rx, (uint32_t)(m * 256 + lane * 4) * 2u);
+#pragma unroll
+          for (int m = 0; m < kFewChunks; ++m)
+            xv[m] = make_float4(__uint_as_float(raw[m].x << 16), __uint_as_float(raw[m].x & 0xFFFF0000u),
+                                __uint_as_float(raw[m].y << 16), __uint_as_float(raw[m].y & 0xFFFF0000u));
+        } else {
+          const __amdgpu_buffer_rsrc_t rx =
+              share_rsrc((const float *)a.x + (size_t)s * a.H + seg, (uint32_t)q * 4u);
+#pragma unroll
+          for (int m = 0; m < kFewChunks; ++m) xv[m] = buf_f4(rx, (uint32_t)(m * 256 + lane * 4) * 4u);
+        }
+        double t = 0.0;
+#pragma unroll
+        for (int m = 0; m < kFewChunks; ++m) {
+          t = fma((double)wv[m].x, (double)xv[m].x, t);
+          t = fma((double)wv[m].y, (double)xv[m].y, t);
+          t = fma((double)wv[m].z, (double)xv[m].z, t);
+          t = fma((double)wv[m].w, (double)xv[m].w, t);
+        }
+        acc[s] = t;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kFewTokens; ++s)
+      if (s < a.S) {
+        const double v = wave_sum_f64_to63(acc[s]);
+        if (lane == 63) part[wave][s] = v;
+      }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < a.S) {
+    const int s = threadIdx.x;
+    a.logits[(size_t)s * a.E + e] = ((part[0][s] + part[1][s]) + part[2][s]) + part[3][s];
+  }
+}
+
+// Publishes this workgroup's logits (written by wave 0) and reports whether it
+// completed the count of `total` expert workgroups.  All threads call it.
+__device__ inline bool few_logits_publish(const RouteArgs &a, uint32_t total, int *s_flag) {
+  if (threadIdx.x == 0) {
+    const uint32_t old =
+        __hip_atomic_fetch_add(a.sync + kSyncRouteCtr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = old == total - 1;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// Selection for all S <= kFewTokens tokens by the workgroup that completed the
+// count: tokens in rounds of four; all threads score the round's (token,
+// expert) pairs into per-wave LDS (sel_lds: 4*E doubles then 4*E floats; sbias:
+// the E biases, staged earlier), then wave w < 4 selects for token r + w.
+__device__ inline void few_select(const RouteArgs &a, double *sel_lds, const float *sbias) {
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float *skeys = (float *)(sel_lds + (size_t)4 * a.E);
+  for (int r = 0; r < a.S; r += 4) {
+    const int nt = min(4, a.S - r);
+    for (int ee = threadIdx.x; ee < a.E; ee += blockDim.x)
+      for (int w2 = 0; w2 < nt; ++w2) {
+        double sv;
+        float kv;
+        score(a.logits[(size_t)(r + w2) * a.E + ee], sbias[ee], sv, kv);
+        sel_lds[(size_t)w2 * a.E + ee] = sv;
+        skeys[(size_t)w2 * a.E + ee] = kv;
+      }
+    __syncthreads();
+    if (wave < nt) select_wave_dispatch(a, r + wave, skeys + (size_t)wave * a.E, sel_lds + (size_t)wave * a.E, lane);
+    __syncthreads();
+  }
+}
+
+}  // namespace moe
