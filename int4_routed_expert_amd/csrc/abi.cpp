@@ -93,6 +93,7 @@ WsLayout ws_layout(const moe_cfg &c, int32_t S) {
   L.xf = off; off += align256((size_t)S * gh * sizeof(float));
   L.hl = off; off += align256((size_t)S * k1 * gi * 24 * sizeof(uint32_t));
   L.hf = off; off += align256((size_t)S * k1 * gi * sizeof(float));
+  L.eptr = off; off += align256((size_t)kMaxK * sizeof(uint64_t));
   L.max_items = 0;
   L.max_mtiles = 0;
   if (S > kSmallS) {
@@ -324,6 +325,7 @@ static int ffn_args(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S,
   a.xf = (float *)(b + L.xf);
   a.hl = (uint32_t *)(b + L.hl);
   a.hf = (float *)(b + L.hf);
+  a.eptr = (uint64_t *)(b + L.eptr);
   a.n_cu = device_cus();
   if (S <= kSmallS) {
     // one-token down kernel: about one row block per compute unit, at most 8 tiles each

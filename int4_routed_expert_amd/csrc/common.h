@@ -83,6 +83,7 @@ struct FfnArgs {
   uint32_t *hl;    // h: S*(k+1) rows of Imax/32 groups
   float *hf;
   // one-token decode path
+  uint64_t *eptr;  // [k] routed experts' packed weights (0: not resident), resolved by the gate/up kernel
   int32_t n_blk;   // row blocks of the down kernel
   int32_t tb;      // down tiles (8 rows) per row block
   int32_t n_cu;    // compute units of the device
@@ -130,7 +131,7 @@ hipError_t launch_pack(int H, int I, const uint8_t *qg, const uint16_t *sg, cons
 
 // workspace layout (bytes, each region 256-aligned)
 struct WsLayout {
-  size_t sync, logits, h, xl, xf, hl, hf, part, lists, counts, items, n_items, mtiles, xb, total;
+  size_t sync, logits, h, xl, xf, hl, hf, eptr, part, lists, counts, items, n_items, mtiles, xb, total;
   int32_t max_items, max_mtiles;
 };
 WsLayout ws_layout(const moe_cfg &c, int32_t S);

@@ -61,7 +61,21 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
   const int s0 = (int)(wid * Is / W), s1 = (int)((wid + 1) * Is / W);
   const int r0 = (int)(wid * Fr / W), r1 = (int)((wid + 1) * Fr / W);
   const int ns = s1 - s0, n = ns + (r1 - r0);
-  const uint64_t my_ptr = routed_ptr_lane(a, lane);
+  // The activations are loaded first (group threadIdx.x; H <= 8192 so one
+  // group per thread): loads return in order, so loads issued after the
+  // weight prefetch below would wait for the prefetched weights.
+  // Order (loads return in order): lane j's expert id, the activations, then
+  // the expert's slot; all unconditional (clamped) so the waits are exact.
+  const bool has_x = (int)threadIdx.x < ng;
+  const int e_raw = ldg<int>(a.idx + min(lane, a.k - 1));
+  float v[32];
+  load32(a.x, a.x_bf16, (size_t)min((int)threadIdx.x, ng - 1) * kGroup, v);
+  const bool e_ok = lane < a.k && e_raw >= 0 && e_raw < a.E;
+  const int slot = ldg<int>(a.table + (e_ok ? e_raw : 0));
+  const uint64_t my_ptr = e_ok && slot >= 0 && slot < a.n_slots
+                              ? (uint64_t)(uintptr_t)(a.base + (size_t)slot * (size_t)a.slot_bytes)
+                              : 0;
+  if (blockIdx.x == 0 && threadIdx.x < 64 && lane < a.k) a.eptr[lane] = my_ptr;  // for the down kernel
   // three-slot ring, two features in flight while one is computed; the first
   // two (shared-expert features when the wave has any) are issued before the
   // activations are staged.  Loads are unconditional (indices clamped; repeats
@@ -72,12 +86,10 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
     gu_feat_load(b1, a, 1, n, ns, s0, r0, my_ptr, lane);
   }
   float *lf = (float *)(lds + (size_t)ng * 24);
-  for (int g = threadIdx.x; g < ng; g += blockDim.x) {
-    float v[32];
-    load32(a.x, a.x_bf16, (size_t)g * kGroup, v);
+  if (has_x) {
     Limbs L;
     to_limbs(v, L);
-    store_limbs(lds + (size_t)g * 24, lf + g, L);
+    store_limbs(lds + (size_t)threadIdx.x * 24, lf + threadIdx.x, L);
   }
   __syncthreads();
   if (n <= 0) return;
@@ -121,63 +133,73 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
 template <int NGD, bool HLDS>
 __global__ __launch_bounds__(kDnS1Waves * 64) void k_down_s1(FfnArgs a) {
   __shared__ float part[kMaxK + 1][kDnRows * kDnMaxTb];
-  __shared__ int s_idx[kMaxK];
+  __shared__ int s_idx[kMaxK];  // [0]: the token's idx row is invalid (combine poisons y)
   __shared__ float s_w[kMaxK];
   extern __shared__ uint32_t hlds[];  // HLDS: [NE][Imax/32][24] limbs, then [NE][Imax/32] factors
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int NE = a.k + (a.Is > 0 ? 1 : 0);
   const int Imax = max(a.I, a.Is), ngm = Imax / kGroup, nt = a.H / kDnRows;
   const int t0 = blockIdx.x * a.tb, t1 = min(nt, t0 + a.tb);
-  if ((int)threadIdx.x < a.k) {  // for the combine; read once, up front
-    s_idx[threadIdx.x] = ldg<int>(a.idx + threadIdx.x);
-    s_w[threadIdx.x] = ldg<float>(a.w + threadIdx.x);
-  }
-  // this wave's first expert: issue its first two tiles before staging h
+  // Order of the first loads (they return in order, so a value that is waited
+  // for waits for everything issued before it): the wave's resolved expert
+  // pointer (written by the gate/up kernel: one load instead of idx then
+  // table), this thread's first group of h (staging), the wave's first two
+  // tiles; idx and w for the combine last.
+  float *hf_lds = (float *)(hlds + (size_t)NE * ngm * 24);
+  auto h_group = [&](int i, bool &use, float (&v)[32]) {
+    const int e2 = i / ngm, g = i - e2 * ngm;
+    use = HLDS && i < NE * ngm && g * kGroup < (e2 == a.k ? a.Is : a.I);
+    // unconditional (a group that is not used reads group 0 and is dropped), so
+    // that the wait for the expert pointer loaded before it can be exact
+    load32(a.h, 0, use ? (size_t)e2 * Imax + (size_t)g * kGroup : 0, v);
+  };
   int j = wave;
   const uint8_t *dn = a.base;
   int inter = a.I;
   bool valid = false;
   DnTile<NGD> q0, q1;
-  auto resolve = [&](int jj) {
-    const bool sh = jj == a.k;
-    inter = sh ? a.Is : a.I;
-    const uint8_t *ex = nullptr;
-    if (sh) {
-      ex = a.shared;
-    } else {
-      const int e = ldg<int>(a.idx + jj);
-      if (e >= 0 && e < a.E) {
-        const int s = ldg<int>(a.table + e);
-        if (s >= 0 && s < a.n_slots) ex = a.base + (size_t)s * (size_t)a.slot_bytes;
-      }
-    }
+  auto ex_of = [&](int jj) -> const uint8_t * {
+    return jj == a.k ? a.shared : (const uint8_t *)(uintptr_t)ldg<uint64_t>(a.eptr + min(jj, a.k - 1));
+  };
+  auto resolve = [&](int jj, const uint8_t *ex) {
+    inter = jj == a.k ? a.Is : a.I;
     valid = ex != nullptr;
     if (!valid) inter = a.I;
     dn = uniform_ptr((valid ? ex : a.base) + down_offset(a.H, inter));
   };
+  const uint8_t *ex0 = ex_of(j);
+  bool use_h;
+  float hv0[32];
+  h_group(threadIdx.x, use_h, hv0);
   if (j < NE) {
-    resolve(j);
+    resolve(j, ex0);
     dn_tile_load(q0, dn, inter, t0, t1, lane);
     dn_tile_load(q1, dn, inter, t0 + 1, t1, lane);
   }
-  float *hf_lds = (float *)(hlds + (size_t)NE * ngm * 24);
-  if (HLDS) {
-    for (int i = threadIdx.x; i < NE * ngm; i += blockDim.x) {
-      const int e2 = i / ngm, g = i - e2 * ngm;
-      const int ie = e2 == a.k ? a.Is : a.I;
-      if (g * kGroup < ie) {
-        float v[32];
-        load32(a.h, 0, (size_t)e2 * Imax + (size_t)g * kGroup, v);
-        Limbs L;
-        to_limbs(v, L);
-        store_limbs(hlds + (size_t)i * 24, hf_lds + i, L);
-      }
+  int my_idx = 0;
+  float my_w = 0.f;
+  if ((int)threadIdx.x < a.k) {  // for the combine (stored to LDS after the tiles)
+    my_idx = ldg<int>(a.idx + threadIdx.x);
+    my_w = ldg<float>(a.w + threadIdx.x);
+  }
+  if (use_h) {
+    Limbs L;
+    to_limbs(hv0, L);
+    store_limbs(hlds + (size_t)threadIdx.x * 24, hf_lds + threadIdx.x, L);
+  }
+  for (int i = threadIdx.x + blockDim.x; HLDS && i < NE * ngm; i += blockDim.x) {
+    float v[32];
+    h_group(i, use_h, v);
+    if (use_h) {
+      Limbs L;
+      to_limbs(v, L);
+      store_limbs(hlds + (size_t)i * 24, hf_lds + i, L);
     }
   }
   __syncthreads();
   for (; j < NE; j += nw) {
     if (j != wave) {
-      resolve(j);
+      resolve(j, ex_of(j));
       dn_tile_load(q0, dn, inter, t0, t1, lane);
       dn_tile_load(q1, dn, inter, t0 + 1, t1, lane);
     }
@@ -211,15 +233,22 @@ __global__ __launch_bounds__(kDnS1Waves * 64) void k_down_s1(FfnArgs a) {
       dn_tile_load(q1, dn, inter, t + 3, t1, lane);
     }
   }
+  if ((int)threadIdx.x < a.k) {
+    s_w[threadIdx.x] = my_w;
+  }
+  if (wave == 0) {  // the token's idx row: every entry in [0, E) and no entry twice (lane j < k holds entry j)
+    bool bad_j = lane < a.k && (my_idx < 0 || my_idx >= a.E);
+    for (int ii = 0; ii < a.k; ++ii) {
+      const int e = __builtin_amdgcn_readlane(my_idx, ii);
+      bad_j |= ii < lane && lane < a.k && e == my_idx;
+    }
+    const bool bad = __ballot(bad_j) != 0;
+    if (lane == 0) s_idx[0] = bad;
+  }
   __syncthreads();
   const int rows = (t1 - t0) * kDnRows;
   if ((int)threadIdx.x < rows) {
-    bool bad = false;
-    for (int jj = 0; jj < a.k; ++jj) {
-      const int e = s_idx[jj];
-      bad |= e < 0 || e >= a.E;
-      for (int ii = 0; ii < jj; ++ii) bad |= s_idx[ii] == e;
-    }
+    const bool bad = s_idx[0] != 0;
     const int i = threadIdx.x;
     float acc = 0.f;
     for (int jj = 0; jj < a.k; ++jj) acc = fmaf(s_w[jj], part[jj][i], acc);

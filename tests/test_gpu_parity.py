@@ -245,17 +245,18 @@ def test_unresident_slot_poisons_only_its_tokens(tiny, S):
     assert np.all(np.isnan(y[uses]).all(axis=1))
 
 
-@pytest.mark.parametrize("S", [2, 6])
+@pytest.mark.parametrize("S", [1, 2, 6])
 @pytest.mark.parametrize("mode", ["out_of_range", "negative", "repeated"])
 def test_invalid_idx_poisons_only_its_token(tiny, S, mode):
     x = gen.tokens(tiny.w.with_(tokens=S), step=900 + S)
     idx, wt, y_ok = run_gpu(tiny, x)
     bad = idx.copy()
-    bad[1, 1] = {"out_of_range": 12345, "negative": -3, "repeated": bad[1, 0]}[mode]
+    t = min(1, S - 1)  # the poisoned token
+    bad[t, 1] = {"out_of_range": 12345, "negative": -3, "repeated": bad[t, 0]}[mode]
     y = tiny.ffn(dev(x), M.MOE_F32, dev(bad), dev(wt)).cpu().numpy()
-    assert np.all(np.isnan(y[1]))
+    assert np.all(np.isnan(y[t]))
     keep = np.ones(S, bool)
-    keep[1] = False
+    keep[t] = False
     # each token's arithmetic does not depend on the others: the rest is bitwise unchanged
     assert np.array_equal(y[keep], y_ok[keep])
 
