@@ -167,6 +167,15 @@ def bench_verify(args) -> int:
         M.moe_ffn(cfg, xb, dt, S, idx[o], wt[o], views[j % len(layers)], L["shared"], y[o], ws, ws.numel())
 
     tok_s, ms_per_step, steps, warm = run_graphs(step, args, nb)
+    M.moe_profile_enable(True)
+    M.moe_profile_report()
+    for j in range(64):
+        step(j)
+    torch.cuda.synchronize()
+    prof = M.moe_profile_report()
+    M.moe_profile_enable(False)
+    kernels = {n: round(ms * 1e3 / k, 2) for n, (ms, k) in prof.items()}
+    log(f"verify: kernel-stamped averages (us, per call): {kernels}")
     # experts streamed per call: the batch union plus the shared expert
     idx_h = idx.cpu().numpy()
     U = np.array([len(set(idx_h[o].ravel().tolist())) for o in range(min(nb, n_out))])
@@ -180,7 +189,7 @@ def bench_verify(args) -> int:
                      "layers_rotated": args.layers, "batches_rotated": nb, "launch": "hip graphs of 16 calls"},
           "union_mean": float(U.mean()), "union_min": int(U.min()), "union_max": int(U.max()),
           "shared_fraction": float(1.0 - U.mean() / (S * c.top_k)),
-          "effective_gbps": gbps, "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS})
+          "effective_gbps": gbps, "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS, "kernels_us": kernels})
     return 0
 
 
