@@ -1,7 +1,7 @@
 """MoE-layer benchmark: GLM-5.2-shaped decode, one token per step, one MI355X.
 
-A step is one pass of the whole layer (moe_route then moe_ffn through the C ABI)
-for one token.  Inputs are resident in HBM before timing starts: L layer
+A step is one pass of the whole layer for one token through the C ABI: one
+moe_layer call (default), or moe_route then moe_ffn (--call split).  Inputs are resident in HBM before timing starts: L layer
 instances (256 routed + 1 shared int4 experts each, 5.46 GB per layer) and a
 pool of 1024 distinct seeded tokens; consecutive steps rotate over layers and
 tokens so that no expert set is served from the 256 MB Infinity Cache.  The
@@ -419,6 +419,8 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=4, help="resident layer instances rotated per step")
     ap.add_argument("--tokens", type=int, default=1024, help="distinct tokens rotated per step")
     ap.add_argument("--profile-steps", type=int, default=512)
+    ap.add_argument("--call", default="layer", choices=["layer", "split"],
+                    help="decode: one moe_layer call per step, or moe_route then moe_ffn")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--blobs", type=int, default=0, help="stack: distinct pinned weight blobs (0: 1024)")
@@ -482,6 +484,10 @@ def main() -> int:
         L = layers[j % len(layers)]
         t = j % args.tokens
         o = j % n_out
+        if args.call == "layer":
+            M.moe_layer(cfg, xs[t:t + 1], M.MOE_F32, 1, L["W"], L["bias"], idx[o:o + 1], wt[o:o + 1],
+                        views[j % len(layers)], L["shared"], y[o:o + 1], ws, ws.numel())
+            return
         M.moe_route(cfg, xs[t:t + 1], M.MOE_F32, 1, L["W"], L["bias"], idx[o:o + 1], wt[o:o + 1], ws, ws.numel())
         M.moe_ffn(cfg, xs[t:t + 1], M.MOE_F32, 1, idx[o:o + 1], wt[o:o + 1], views[j % len(layers)], L["shared"],
                   y[o:o + 1], ws, ws.numel())
@@ -586,7 +592,8 @@ def main() -> int:
         "config": {"workload": "glm52_moe_layer_decode_S1", "hidden": H, "n_experts": E, "n_group": c.n_group,
                    "topk_group": c.topk_group, "top_k": k, "moe_inter": I, "shared_inter": c.shared_inter,
                    "quant": "int4 g32 fp16 scales", "layers_rotated": args.layers, "tokens_rotated": args.tokens,
-                   "launch": "hip graphs of 16 steps"},
+                   "launch": "hip graphs of 16 steps",
+                   "call": "moe_layer" if args.call == "layer" else "moe_route + moe_ffn"},
         "effective_gbps": gbps,
         "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
         "expert_bytes_per_token": layer_bytes,

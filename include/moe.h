@@ -163,6 +163,19 @@ int moe_route(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, con
 int moe_ffn(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, const int32_t *idx, const float *w,
             const moe_slot_view *experts, const void *shared, float *y, void *ws, size_t ws_bytes, void *stream);
 
+/* One MoE layer forward: moe_route followed by moe_ffn on the same stream, with
+ * the same arguments and bit-identical results (idx, w and y); [PORT] N1 (the
+ * layer is the router, then the routed experts, then their route-order
+ * combine with the shared expert).  For S = 1 it runs as three kernels instead
+ * of four: the router kernel only stores each expert's score and key (no
+ * completion count, no use of the workspace header), and the gate/up kernel
+ * selects the experts itself in every workgroup from those values (workgroup
+ * 0 also writes idx and w), so the selection costs no grid-wide hand-off.
+ * Other S: moe_route then moe_ffn.  Errors: those of moe_route and moe_ffn. */
+int moe_layer(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, const float *W_gate, const float *bias,
+              int32_t *idx, float *w, const moe_slot_view *experts, const void *shared, float *y, void *ws,
+              size_t ws_bytes, void *stream);
+
 /* ---- HBM expert-slot pool ([PORT] N3 and G3 status; [README] per-layer LRU) ----
  * One device slab of n_layers * slots_per_layer slots of moe_expert_bytes(cfg,
  * moe_inter) bytes, a device table per layer (table[e] = slot, or -1), and a

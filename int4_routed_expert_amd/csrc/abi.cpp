@@ -88,6 +88,8 @@ WsLayout ws_layout(const moe_cfg &c, int32_t S) {
   size_t off = 0;
   L.sync = off; off += kWsSyncBytes;
   L.logits = off; off += align256((size_t)S * c.n_experts * sizeof(double));
+  L.scores = off; off += align256((size_t)S * c.n_experts * sizeof(double));
+  L.keys = off; off += align256((size_t)S * c.n_experts * sizeof(float));
   L.h = off; off += align256((size_t)S * k1 * imax * sizeof(float));
   L.xl = off; off += align256((size_t)S * gh * 24 * sizeof(uint32_t));
   L.xf = off; off += align256((size_t)S * gh * sizeof(float));
@@ -296,6 +298,8 @@ static int route_args(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t 
   a.x_bf16 = x_dtype == MOE_BF16; a.norm = c->norm_topk_prob; a.rsf = c->routed_scaling_factor;
   a.x = x; a.W = W; a.bias = bias; a.idx = idx; a.w = w;
   a.logits = (double *)((char *)ws + L.logits);
+  a.scores = (double *)((char *)ws + L.scores);
+  a.keys = (float *)((char *)ws + L.keys);
   a.sync = (uint32_t *)((char *)ws + L.sync);
   return MOE_OK;
 }
@@ -370,6 +374,33 @@ int moe_ffn(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const i
   const int v = ffn_args(c, x, x_dtype, S, idx, w, ex, shared, y, ws, ws_bytes, a);
   if (v || S == 0) return v;
   hipError_t e = run_ffn(a, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int moe_layer(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const float *W, const float *bias,
+              int32_t *idx, float *w, const moe_slot_view *ex, const void *shared, float *y, void *ws, size_t ws_bytes,
+              void *stream) {
+  RouteArgs r;
+  int v = route_args(c, x, x_dtype, S, W, bias, idx, w, ws, ws_bytes, r);
+  if (v || S == 0) return v;
+  FfnArgs f;
+  v = ffn_args(c, x, x_dtype, S, idx, w, ex, shared, y, ws, ws_bytes, f);
+  if (v) return v;
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (S == 1) {
+    e = launch_route_scores(r, st);
+    if (e == hipSuccess) {
+      f.sel = 1;
+      f.G = r.G; f.Gk = r.Gk; f.norm = r.norm; f.rsf = r.rsf;
+      f.keys = r.keys; f.scores = r.scores;
+      f.idx_out = idx; f.w_out = w;
+      e = launch_ffn_decode(f, st);
+    }
+  } else {
+    e = launch_route(r, st);
+    if (e == hipSuccess) e = run_ffn(f, st);
+  }
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 

@@ -48,7 +48,9 @@ struct RouteArgs {
   const void *x;
   const float *W;
   const float *bias;
-  double *logits;  // [S, E]
+  double *logits;  // [S, E] (many tokens)
+  double *scores;  // [S, E] sigmoid of the logit (few tokens)
+  float *keys;     // [S, E] fp32 selection key, sigmoid + bias (few tokens)
   int32_t *idx;
   float *w;
   uint32_t *sync;  // workspace header
@@ -87,6 +89,15 @@ struct FfnArgs {
   int32_t n_blk;   // row blocks of the down kernel
   int32_t tb;      // down tiles (8 rows) per row block
   int32_t n_cu;    // compute units of the device
+  // one-token layer: the gate/up kernel selects the experts itself from the
+  // router's scores and keys (then idx and w above are written, not read)
+  int32_t sel;
+  int32_t G, Gk, norm;
+  float rsf;
+  const float *keys;     // [E] selection keys of the token
+  const double *scores;  // [E] unbiased sigmoid scores
+  int32_t *idx_out;
+  float *w_out;
 };
 
 // ---- timing instrumentation (host) --------------------------------------------
@@ -120,6 +131,7 @@ void set_hip_error(hipError_t e);
 // ---- launchers (host) --------------------------------------------------------
 hipError_t launch_route(const RouteArgs &a, hipStream_t st);
 hipError_t launch_ws_init(uint32_t *sync, hipStream_t st);
+hipError_t launch_route_scores(const RouteArgs &a, hipStream_t st);  // S <= 8: scores and keys only
 hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st);  // S <= kSmallS
 hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st);   // S > kSmallS
 hipError_t launch_gu_mfma(const FfnArgs &a, hipStream_t st);
@@ -131,7 +143,7 @@ hipError_t launch_pack(int H, int I, const uint8_t *qg, const uint16_t *sg, cons
 
 // workspace layout (bytes, each region 256-aligned)
 struct WsLayout {
-  size_t sync, logits, h, xl, xf, hl, hf, eptr, part, lists, counts, items, n_items, mtiles, xb, total;
+  size_t sync, logits, scores, keys, h, xl, xf, hl, hf, eptr, part, lists, counts, items, n_items, mtiles, xb, total;
   int32_t max_items, max_mtiles;
 };
 WsLayout ws_layout(const moe_cfg &c, int32_t S);

@@ -30,6 +30,7 @@
 #include <algorithm>
 
 #include "gemv_dev.h"
+#include "route_dev.h"
 
 namespace moe {
 namespace {
@@ -51,7 +52,11 @@ __global__ __launch_bounds__(256) void k_to_limbs(const void *src, int bf16, int
   stg<float>(factors + i, L.f);
 }
 
-template <int NG>
+// EPT > 0 (the one-token layer call): the workgroup first selects the token's
+// experts from the router's scores and keys (EPT experts per thread); the
+// loads of the selection inputs go first, then the activations and the first
+// two shared-expert features, so that the selection overlaps them.
+template <int NG, int EPT>
 __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
   extern __shared__ uint32_t lds[];  // x limbs [H/32][24], then factors [H/32]
   const int lane = threadIdx.x & 63;
@@ -61,29 +66,49 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
   const int s0 = (int)(wid * Is / W), s1 = (int)((wid + 1) * Is / W);
   const int r0 = (int)(wid * Fr / W), r1 = (int)((wid + 1) * Fr / W);
   const int ns = s1 - s0, n = ns + (r1 - r0);
-  // The activations are loaded first (group threadIdx.x; H <= 8192 so one
-  // group per thread): loads return in order, so loads issued after the
-  // weight prefetch below would wait for the prefetched weights.
-  // Order (loads return in order): lane j's expert id, the activations, then
-  // the expert's slot; all unconditional (clamped) so the waits are exact.
   const bool has_x = (int)threadIdx.x < ng;
-  const int e_raw = ldg<int>(a.idx + min(lane, a.k - 1));
-  float v[32];
-  load32(a.x, a.x_bf16, (size_t)min((int)threadIdx.x, ng - 1) * kGroup, v);
-  const bool e_ok = lane < a.k && e_raw >= 0 && e_raw < a.E;
-  const int slot = ldg<int>(a.table + (e_ok ? e_raw : 0));
-  const uint64_t my_ptr = e_ok && slot >= 0 && slot < a.n_slots
-                              ? (uint64_t)(uintptr_t)(a.base + (size_t)slot * (size_t)a.slot_bytes)
-                              : 0;
-  if (blockIdx.x == 0 && threadIdx.x < 64 && lane < a.k) a.eptr[lane] = my_ptr;  // for the down kernel
-  // three-slot ring, two features in flight while one is computed; the first
-  // two (shared-expert features when the wave has any) are issued before the
-  // activations are staged.  Loads are unconditional (indices clamped; repeats
-  // at the tail hit in cache) so the load counter order is fixed.
   GuFeat<NG> b0, b1, b2;
-  if (n > 0) {
-    gu_feat_load(b0, a, 0, n, ns, s0, r0, my_ptr, lane);
-    gu_feat_load(b1, a, 1, n, ns, s0, r0, my_ptr, lane);
+  uint64_t my_ptr = 0;
+  float v[32];
+  if constexpr (EPT > 0) {
+    __shared__ SelLds sel;
+    const SelCfg c{a.E, a.G, a.Gk, a.k, a.norm, a.rsf};
+    SelIn<EPT> in;
+    sel_load<EPT, true>(c, a.keys, a.scores, a.table, in);
+    load32(a.x, a.x_bf16, (size_t)min((int)threadIdx.x, ng - 1) * kGroup, v);
+    const bool early = n > 0 && ns >= 2;  // both first features are shared: they need no selection
+    if (early) {
+      gu_feat_load(b0, a, 0, n, ns, s0, r0, 0, lane);
+      gu_feat_load(b1, a, 1, n, ns, s0, r0, 0, lane);
+    }
+    select_block<EPT, true>(c, 0, in, sel, blockIdx.x == 0 ? a.idx_out : nullptr, a.w_out);
+    if (lane < a.k) {
+      const int slot = sel.out_slot[lane];
+      if (slot >= 0 && slot < a.n_slots) my_ptr = (uint64_t)(uintptr_t)(a.base + (size_t)slot * (size_t)a.slot_bytes);
+    }
+    if (blockIdx.x == 0 && threadIdx.x < 64 && lane < a.k) a.eptr[lane] = my_ptr;  // for the down kernel
+    if (n > 0 && !early) {
+      gu_feat_load(b0, a, 0, n, ns, s0, r0, my_ptr, lane);
+      gu_feat_load(b1, a, 1, n, ns, s0, r0, my_ptr, lane);
+    }
+  } else {
+    // Order (loads return in order): lane j's expert id, the activations, then
+    // the expert's slot; all unconditional (clamped) so the waits are exact.
+    const int e_raw = ldg<int>(a.idx + min(lane, a.k - 1));
+    load32(a.x, a.x_bf16, (size_t)min((int)threadIdx.x, ng - 1) * kGroup, v);
+    const bool e_ok = lane < a.k && e_raw >= 0 && e_raw < a.E;
+    const int slot = ldg<int>(a.table + (e_ok ? e_raw : 0));
+    my_ptr = e_ok && slot >= 0 && slot < a.n_slots ? (uint64_t)(uintptr_t)(a.base + (size_t)slot * (size_t)a.slot_bytes)
+                                                    : 0;
+    if (blockIdx.x == 0 && threadIdx.x < 64 && lane < a.k) a.eptr[lane] = my_ptr;  // for the down kernel
+    // three-slot ring, two features in flight while one is computed; the first
+    // two (shared-expert features when the wave has any) are issued before the
+    // activations are staged.  Loads are unconditional (indices clamped; repeats
+    // at the tail hit in cache) so the load counter order is fixed.
+    if (n > 0) {
+      gu_feat_load(b0, a, 0, n, ns, s0, r0, my_ptr, lane);
+      gu_feat_load(b1, a, 1, n, ns, s0, r0, my_ptr, lane);
+    }
   }
   float *lf = (float *)(lds + (size_t)ng * 24);
   if (has_x) {
@@ -669,7 +694,13 @@ hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st) {
       const long waves = std::max<long>((long)a.n_cu * 8, (feats + kGuMaxPerWave - 1) / kGuMaxPerWave);
       const dim3 g((unsigned)((waves + 3) / 4)), blk(256);
       const size_t lds = (size_t)(a.H / kGroup) * 25 * sizeof(uint32_t);
-      MOE_DISPATCH_NG(ceil_groups(a.H), k_gateup_s1, g, blk, lds, st);
+      if (!a.sel) {
+        MOE_DISPATCH_NG(ceil_groups(a.H), k_gateup_s1, g, blk, lds, st, 0);
+      } else if (a.E <= 256) {
+        MOE_DISPATCH_NG(ceil_groups(a.H), k_gateup_s1, g, blk, lds, st, 1);
+      } else {
+        MOE_DISPATCH_NG(ceil_groups(a.H), k_gateup_s1, g, blk, lds, st, 4);
+      }
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

@@ -112,14 +112,14 @@ __global__ __launch_bounds__(256) void k_route_logits_tiled(RouteArgs a) {
 
 // Few tokens (S <= kFewTokens), one launch for the whole router: one workgroup
 // per expert computes that expert's logits (its 4 waves split H; every load of
-// a lane is issued before the FMAs; partial sums meet in LDS in a fixed order),
-// publishes them and counts itself done on a device-scope counter in the
-// workspace header; the workgroup that completes the count selects for all
-// tokens (scores by all its threads, then one wave per token) and puts the
+// a lane is issued before the FMAs; partial sums meet in LDS in a fixed order)
+// and their scores and keys, publishes them and counts itself done on a
+// device-scope counter in the workspace header; the workgroup that completes
+// the count selects for all tokens (whole workgroup per token) and puts the
 // counter back to zero.  A workspace without the header's magic words gets
 // idx = -1 and w = NaN.
 __global__ __launch_bounds__(256) void k_route_fused(RouteArgs a) {
-  extern __shared__ double sel_lds[];  // 4*E doubles, 4*E floats, then E floats of bias
+  __shared__ SelLds sel;
   __shared__ double part[4][kFewTokens];
   __shared__ int s_last;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -135,13 +135,22 @@ __global__ __launch_bounds__(256) void k_route_fused(RouteArgs a) {
       }
     return;
   }
-  // biases for the selection, staged while the logits complete
-  float *sbias = (float *)(sel_lds + (size_t)4 * a.E) + (size_t)4 * a.E;
-  for (int i = threadIdx.x; i < a.E; i += blockDim.x) sbias[i] = a.bias[i];
   few_logits_finish(a, e, wave, lane, wv, part);
   if (!few_logits_publish(a, (uint32_t)a.E, &s_last)) return;
-  few_select(a, sel_lds, sbias);
+  few_select(a, sel);
   if (threadIdx.x == 0) __hip_atomic_store(a.sync + kSyncRouteCtr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Few tokens, logits and selection inputs only (the selection runs in the
+// consumer's first kernel): one workgroup per expert stores the tokens' scores
+// and keys.  No completion count, so no workspace header is involved.
+__global__ __launch_bounds__(256) void k_route_scores(RouteArgs a) {
+  __shared__ double part[4][kFewTokens];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = blockIdx.x;
+  float4 wv[kFewChunks];
+  few_logits_load(a, e, wave, lane, wv);
+  few_logits_finish(a, e, wave, lane, wv, part);
 }
 
 __global__ void k_ws_init(uint32_t *sync) {
@@ -156,7 +165,7 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
   const size_t sel_lds = (size_t)4 * a.E * (sizeof(double) + sizeof(float)) + (size_t)a.E * sizeof(float);
   if (a.S <= kFewTokens) {
     ProfScope ps("route_fused", st);
-    MOE_LAUNCH(k_route_fused, dim3(a.E), dim3(256), sel_lds, st, a);
+    MOE_LAUNCH(k_route_fused, dim3(a.E), dim3(256), 0, st, a);
     return hipGetLastError();
   }
   {
@@ -170,6 +179,14 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
     ProfScope ps("route_select", st);
     MOE_LAUNCH(k_route_select, dim3((a.S + 3) / 4), dim3(256), sel_lds, st, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_route_scores(const RouteArgs &a, hipStream_t st) {
+  if (a.S == 0) return hipSuccess;
+  if (a.S > kFewTokens) return hipErrorInvalidValue;
+  ProfScope ps("route_scores", st);
+  MOE_LAUNCH(k_route_scores, dim3(a.E), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

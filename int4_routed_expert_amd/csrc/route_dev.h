@@ -4,7 +4,7 @@
 // completion hand-off.  See route.hip for the method and its citations.
 #pragma once
 
-#include "common.h"
+#include "dot.h"
 
 namespace moe {
 
@@ -185,8 +185,9 @@ __device__ inline void few_logits_load(const RouteArgs &a, int e, int wave, int 
 
 // Part 2: waves 0..3 form the fp64 dots with the tokens' activations (same
 // bounded loads), reduce each to lane 63, and the four shares are added in a
-// fixed order by thread s < S, which stores logit (s, e).  Every thread of the
-// workgroup must call it (one barrier); waves past the fourth only wait.
+// fixed order by thread s < S, which scores logit (s, e) and stores the score
+// and the selection key.  Every thread of the workgroup must call it (one
+// barrier); waves past the fourth only wait.
 __device__ inline void few_logits_finish(const RouteArgs &a, int e, int wave, int lane, const float4 (&wv)[kFewChunks],
                                          double (*part)[kFewTokens]) {
   const int q = a.H / 4;
@@ -232,10 +233,15 @@ __device__ inline void few_logits_finish(const RouteArgs &a, int e, int wave, in
         if (lane == 63) part[wave][s] = v;
       }
   }
+  const float b = a.bias[e];
   __syncthreads();
   if ((int)threadIdx.x < a.S) {
     const int s = threadIdx.x;
-    a.logits[(size_t)s * a.E + e] = ((part[0][s] + part[1][s]) + part[2][s]) + part[3][s];
+    double sv;
+    float kv;
+    score(((part[0][s] + part[1][s]) + part[2][s]) + part[3][s], b, sv, kv);
+    a.scores[(size_t)s * a.E + e] = sv;
+    a.keys[(size_t)s * a.E + e] = kv;
   }
 }
 
@@ -251,28 +257,205 @@ __device__ inline bool few_logits_publish(const RouteArgs &a, uint32_t total, in
   return *s_flag != 0;
 }
 
+// ---- selection of one token by a whole workgroup ---------------------------------
+// Each expert's key becomes a unique 64-bit value (ordered key above, inverted
+// index below), so "larger value" is exactly "higher key, lower index on ties".
+// Then, with one expert per thread (or a few):
+//   1. rank of the expert within its group (compares with the group's values);
+//      the group's best min(k, per) values and its two best keys go to LDS;
+//   2. every wave: group score = fp32 sum of the two best keys, the Gk best
+//      groups kept (ties: lower group index);
+//   3. an expert of a kept group with in-group rank r < min(k, per) has global
+//      rank r + (number of better values among the other kept groups' best
+//      lists); ranks below k name the selection;
+//   4. lanes r < k of wave 0: weight of rank r from the unbiased scores summed in
+//      rank order.
+// The result is the sequential definition's (k rounds of arg-max over the kept
+// experts) because the packed values are distinct and totally ordered.
+__device__ inline uint64_t packed_rank_value(float key, int e) {
+  return ((uint64_t)ordered_key(key) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+struct SelCfg {
+  int E, G, Gk, k, norm;
+  float rsf;
+};
+
+struct SelLds {
+  alignas(16) uint64_t v[kMaxE];            // packed values of the token's experts
+  alignas(16) uint64_t top[kMaxG * kMaxK];  // [group][rank < kMaxK] best values (0 past min(k, per))
+  float gtop[kMaxG][2];           // two best keys of each group
+  int out_e[kMaxK];               // selected expert of each rank
+  int out_slot[kMaxK];            // and its slot-table entry (when loaded)
+  double out_s[kMaxK];            // and its unbiased score
+};
+
+// One token's inputs, experts threadIdx.x + j * blockDim.x (clamped).
+template <int EPT>
+struct SelIn {
+  float key[EPT];
+  double s[EPT];
+  int slot[EPT];
+};
+
+// Loads of the token's keys and scores (and slot-table entries when SLOT).
+template <int EPT, bool SLOT>
+__device__ inline void sel_load(const SelCfg &c, const float *keys, const double *scores, const int32_t *table,
+                                SelIn<EPT> &in) {
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = min((int)threadIdx.x + j * (int)blockDim.x, c.E - 1);
+    in.key[j] = ldg<float>(keys + e);
+    in.s[j] = ldg<double>(scores + e);
+    in.slot[j] = SLOT ? ldg<int>(table + e) : 0;
+  }
+}
+
+// Every thread of the workgroup calls it (three barriers).  Leaves the ranks'
+// experts, scores and slots in L.out_* (readable by every thread on return);
+// lanes r < k of wave 0 store idx/w row t when idx_out is not null.
+template <int EPT, bool SLOT>
+__device__ void select_block(const SelCfg &c, int t, const SelIn<EPT> &in, SelLds &L, int32_t *idx_out,
+                             float *w_out) {
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63;
+  const int E = c.E, G = c.G, per = E / G, k = c.k, kk = min(k, per);
+  uint64_t v[EPT];
+  int rin[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid + j * nt;
+    v[j] = packed_rank_value(in.key[j], e);
+    if (e < E) L.v[e] = v[j];
+  }
+  for (int i = tid; i < G * kMaxK; i += nt)
+    if ((i & (kMaxK - 1)) >= kk) L.top[i] = 0ull;  // below every packed value
+  __syncthreads();
+  // 1. rank within the group
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid + j * nt;
+    rin[j] = per;
+    if (e < E) {
+      const int g = e / per;
+      const uint64_t *gv = L.v + (size_t)g * per;
+      int r = 0;
+      if ((per & 7) == 0) {
+        for (int cc = 0; cc < per; cc += 8) {
+          ulonglong2 p[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) p[q] = *(const ulonglong2 *)(gv + cc + 2 * q);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) r += (p[q].x > v[j] ? 1 : 0) + (p[q].y > v[j] ? 1 : 0);
+        }
+      } else {
+        for (int cc = 0; cc < per; ++cc) r += (gv[cc] > v[j]) ? 1 : 0;
+      }
+      rin[j] = r;
+      if (r < kk) L.top[(size_t)g * kMaxK + r] = v[j];
+      if (r < 2) L.gtop[g][r] = in.key[j];
+    }
+  }
+  __syncthreads();
+  // 2. kept groups (G <= 64, so lane g of every wave holds group g)
+  float gsc = -INFINITY;
+  if (lane < G) gsc = per == 1 ? L.gtop[lane][0] : __double2float_rn((double)L.gtop[lane][0] + (double)L.gtop[lane][1]);
+  int grk = 0;
+  for (int i = 0; i < G; ++i) {
+    const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gsc), i));
+    grk += (o > gsc || (o == gsc && i < lane)) ? 1 : 0;
+  }
+  const uint64_t kept = __ballot(lane < G && grk < c.Gk);
+  // 3. global rank of the kept groups' leading experts
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid + j * nt;
+    if (e < E && rin[j] < kk) {
+      const int g = e / per;
+      if ((kept >> g) & 1) {
+        int r = rin[j];
+        for (uint64_t m = kept & ~(1ull << g); m; m &= m - 1) {
+          const ulonglong2 *tv = (const ulonglong2 *)(L.top + (size_t)__builtin_ctzll(m) * kMaxK);
+          ulonglong2 p[kMaxK / 2];
+#pragma unroll
+          for (int q = 0; q < kMaxK / 2; ++q) p[q] = tv[q];
+#pragma unroll
+          for (int q = 0; q < kMaxK / 2; ++q) r += (p[q].x > v[j] ? 1 : 0) + (p[q].y > v[j] ? 1 : 0);
+        }
+        if (r < k) {
+          L.out_e[r] = e;
+          L.out_s[r] = in.s[j];
+          L.out_slot[r] = in.slot[j];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // 4. weights (wave 0)
+  if (idx_out && tid < 64) {
+    const int my_e = lane < k ? L.out_e[lane] : -1;
+    const double my_s = lane < k ? L.out_s[lane] : 0.0;
+    double denom = 0.0;
+    for (int r = 0; r < k; ++r) {
+      const int lo = __builtin_amdgcn_readlane((int)__double2loint(my_s), r);
+      const int hi = __builtin_amdgcn_readlane((int)__double2hiint(my_s), r);
+      denom += __hiloint2double(hi, lo);
+    }
+    if (lane < k) {
+      const double wv = c.norm ? my_s / denom * (double)c.rsf : my_s * (double)c.rsf;
+      idx_out[(size_t)t * k + lane] = my_e;
+      w_out[(size_t)t * k + lane] = (float)wv;
+    }
+  }
+}
+
+__device__ inline SelCfg sel_cfg(const RouteArgs &a) { return SelCfg{a.E, a.G, a.Gk, a.k, a.norm, a.rsf}; }
+
 // Selection for all S <= kFewTokens tokens by the workgroup that completed the
-// count: tokens in rounds of four; all threads score the round's (token,
-// expert) pairs into per-wave LDS (sel_lds: 4*E doubles then 4*E floats; sbias:
-// the E biases, staged earlier), then wave w < 4 selects for token r + w.
-__device__ inline void few_select(const RouteArgs &a, double *sel_lds, const float *sbias) {
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+// count, one token after another (the next token's inputs are loaded while the
+// current one is selected), from the scores and keys the expert workgroups
+// published.
+template <int EPT>
+__device__ inline void few_select_t(const RouteArgs &a, SelLds &L) {
+  const SelCfg c = sel_cfg(a);
+  SelIn<EPT> cur, nxt;
+  sel_load<EPT, false>(c, a.keys, a.scores, nullptr, cur);
+  for (int t = 0; t < a.S; ++t) {
+    const int tn = min(t + 1, a.S - 1);
+    sel_load<EPT, false>(c, a.keys + (size_t)tn * a.E, a.scores + (size_t)tn * a.E, nullptr, nxt);
+    select_block<EPT, false>(c, t, cur, L, a.idx, a.w);
+    cur = nxt;
+  }
+}
+
+// Two or more tokens with E <= 256: tokens in rounds of four, wave w selects
+// token r + w with the one-wave selection (keys and scores staged in LDS, in
+// the space of the block selection's arrays).
+__device__ inline void few_select_waves(const RouteArgs &a, SelLds &L) {
+  static_assert(sizeof(L.v) >= 4 * 256 * sizeof(double) && sizeof(L.top) >= 4 * 256 * sizeof(float), "LDS reuse");
+  double *ssg = (double *)L.v;
+  float *skey = (float *)L.top;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float *skeys = (float *)(sel_lds + (size_t)4 * a.E);
   for (int r = 0; r < a.S; r += 4) {
     const int nt = min(4, a.S - r);
-    for (int ee = threadIdx.x; ee < a.E; ee += blockDim.x)
-      for (int w2 = 0; w2 < nt; ++w2) {
-        double sv;
-        float kv;
-        score(a.logits[(size_t)(r + w2) * a.E + ee], sbias[ee], sv, kv);
-        sel_lds[(size_t)w2 * a.E + ee] = sv;
-        skeys[(size_t)w2 * a.E + ee] = kv;
-      }
+    for (int i = threadIdx.x; i < nt * a.E; i += blockDim.x) {
+      ssg[i] = ldg<double>(a.scores + (size_t)r * a.E + i);
+      skey[i] = ldg<float>(a.keys + (size_t)r * a.E + i);
+    }
     __syncthreads();
-    if (wave < nt) select_wave_dispatch(a, r + wave, skeys + (size_t)wave * a.E, sel_lds + (size_t)wave * a.E, lane);
+    if (wave < nt) select_wave_dispatch(a, r + wave, skey + (size_t)wave * a.E, ssg + (size_t)wave * a.E, lane);
     __syncthreads();
   }
+}
+
+__device__ inline void few_select(const RouteArgs &a, SelLds &L) {
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (a.S >= 2 && a.E <= 256 && blockDim.x == 256) {
+    few_select_waves(a, L);
+    return;
+  }
+  const int ept = (a.E + (int)blockDim.x - 1) / (int)blockDim.x;
+  if (ept <= 1) few_select_t<1>(a, L);
+  else few_select_t<4>(a, L);
 }
 
 }  // namespace moe

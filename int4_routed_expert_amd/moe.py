@@ -63,6 +63,7 @@ def _load():
         "moe_unpack_expert": (ctypes.c_int, [cp, i32, p, p, p, p, p, p, p]),
         "moe_route": (ctypes.c_int, [cp, p, i32, i32, p, p, p, p, p, sz, p]),
         "moe_ffn": (ctypes.c_int, [cp, p, i32, i32, p, p, ctypes.POINTER(moe_slot_view), p, p, p, sz, p]),
+        "moe_layer": (ctypes.c_int, [cp, p, i32, i32, p, p, p, p, ctypes.POINTER(moe_slot_view), p, p, p, sz, p]),
         "moe_pool_create": (ctypes.c_int, [cp, i32, i32, i32, ctypes.POINTER(p)]),
         "moe_pool_destroy": (None, [p]),
         "moe_pool_register_host": (ctypes.c_int, [p, i32, i32, p]),
@@ -170,6 +171,13 @@ def moe_ffn(cfg: moe_cfg, x, x_dtype: int, S: int, idx, w, view: moe_slot_view, 
             stream=None) -> None:
     _check(_lib.moe_ffn(ctypes.byref(cfg), ptr(x), x_dtype, S, ptr(idx), ptr(w), ctypes.byref(view), ptr(shared),
                         ptr(y), ptr(ws), ws_bytes, stream_handle(stream)), "moe_ffn")
+
+
+def moe_layer(cfg: moe_cfg, x, x_dtype: int, S: int, W, bias, idx, w, view: moe_slot_view, shared, y, ws,
+              ws_bytes: int, stream=None) -> None:
+    _check(_lib.moe_layer(ctypes.byref(cfg), ptr(x), x_dtype, S, ptr(W), ptr(bias), ptr(idx), ptr(w),
+                          ctypes.byref(view), ptr(shared), ptr(y), ptr(ws), ws_bytes, stream_handle(stream)),
+           "moe_layer")
 
 
 def moe_profile_enable(on: bool) -> None:

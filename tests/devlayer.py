@@ -84,6 +84,18 @@ class DeviceLayer:
         return y
 
 
+    def layer(self, x: torch.Tensor, x_dtype: int, table=None, ws=None):
+        """moe_layer: (idx, w, y)."""
+        S = x.shape[0]
+        ws = self.workspace(S) if ws is None else ws
+        idx = torch.full((S, self.c.top_k), -7, dtype=torch.int32, device="cuda")
+        wt = torch.full((S, self.c.top_k), float("nan"), dtype=torch.float32, device="cuda")
+        y = torch.full((S, self.c.hidden), float("nan"), dtype=torch.float32, device="cuda")
+        M.moe_layer(self.cfg, x, x_dtype, S, self.W, self.bias, idx, wt, self.view(table), self.shared, y, ws,
+                    ws.numel())
+        return idx, wt, y
+
+
 def x_device(w: gen.Workload, x_host: np.ndarray):
     """(tensor, dtype code) for generator activations (fp32, or bf16 bits)."""
     if w.x_dtype == "bf16":

@@ -142,6 +142,119 @@ def test_router_reused_workspace_all_sizes(tiny, mid, glm, layer):
             assert np.abs(wt.cpu().numpy() - rw).max() <= 1e-6 * dl.c.routed_scaling_factor
 
 
+def tied_router(c, W, bias, variant):
+    """Router weights with exact ties: 'all' gives every expert the same row and
+    bias (every key and every group score tied); 'groups' copies group 1 into the
+    last group (whole-group score tie) with groups boosted so that exactly one of
+    the two fits in the kept set, and copies an expert inside group 0 (key tie
+    inside a group)."""
+    W = W.copy()
+    b = bias.copy()
+    E, G = c.n_experts, c.n_group
+    per = E // G
+    if variant == "all":
+        W[:] = W[0]
+        b[:] = b[0]
+        return W, b
+    boost = np.zeros(G, np.float32)
+    boost[: c.topk_group - 1] = 1.0  # these groups are kept outright
+    boost[1] = 0.5                   # group 1 and its copy contest the last kept slot
+    boost[G - 1] = 0.5
+    for g in range(G):
+        b[g * per:(g + 1) * per] += boost[g]
+    W[(G - 1) * per:] = W[per:2 * per]
+    b[(G - 1) * per:] = b[per:2 * per]
+    if per >= 2:
+        W[1] = W[0]
+        b[1] = b[0]
+    return W, b
+
+
+@pytest.mark.parametrize("variant", ["all", "groups"])
+@pytest.mark.parametrize("layer", ["tiny", "glm"])
+def test_router_exact_ties(tiny, glm, layer, variant):
+    """Exactly equal keys and group scores: the lower expert index (group index)
+    wins, on the one-launch router (S <= 8) and the many-token kernels."""
+    dl = {"tiny": tiny, "glm": glm}[layer]
+    c = dl.c
+    Wt, bt = tied_router(c, dl.W_host, dl.bias_host, variant)
+    Wd, bd = dev(Wt), dev(bt)
+    ws = dl.workspace(13)
+    for S in (1, 3, 8, 13):
+        x = gen.tokens(dl.w.with_(tokens=S), step=900 + S)
+        xt, dt = x_device(dl.w, x)
+        idx = torch.empty((S, c.top_k), dtype=torch.int32, device="cuda")
+        wt = torch.empty((S, c.top_k), dtype=torch.float32, device="cuda")
+        M.moe_route(dl.cfg, xt, dt, S, Wd, bd, idx, wt, ws, ws.numel())
+        torch.cuda.synchronize()
+        # (the oracle's near-midpoint flag is not asserted here: an exactly tied pair of
+        # group scores is the fp32 rounding of an exact fp64 sum of two fp32 keys, the
+        # same on both sides even when that sum sits on a midpoint)
+        ridx, rw, _, _, _ = O.route(c, x, Wt, bt, x_is_bf16=dl.w.x_dtype == "bf16")
+        if variant == "all":
+            assert (ridx == np.arange(c.top_k)).all()  # lowest indices of the lowest kept groups
+        assert np.array_equal(idx.cpu().numpy(), ridx), (layer, variant, S)
+        assert np.abs(wt.cpu().numpy() - rw).max() <= 1e-6 * c.routed_scaling_factor
+
+
+@pytest.mark.parametrize("layer", ["tiny", "mid", "glm"])
+def test_layer_call_matches_route_then_ffn(tiny, mid, glm, layer):
+    """moe_layer (for one token: scores-only router kernel, selection inside the
+    gate/up kernel) gives idx, w and y bit-identical to moe_route then moe_ffn,
+    over a run of calls on one workspace (fp32 and bf16 inputs, S = 1 and the
+    S > 1 fallback), and matches the oracle."""
+    dl = {"tiny": tiny, "mid": mid, "glm": glm}[layer]
+    c = dl.c
+    ws = dl.workspace(5)
+    for n, S in enumerate([1, 1, 3, 1, 5, 1]):
+        for bf16 in (False, True):
+            w = dl.w.with_(tokens=S, x_dtype="bf16" if bf16 else "f32")
+            x = gen.tokens(w, step=700 + 10 * n)
+            xt, dt = x_device(w, x)
+            idx_l, wt_l, y_l = dl.layer(xt, dt, ws=ws)
+            idx_r, wt_r = dl.route(xt, dt, ws=ws)
+            y_r = dl.ffn(xt, dt, idx_r, wt_r, ws=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(idx_l.cpu().numpy(), idx_r.cpu().numpy()), (layer, S, bf16)
+            assert np.array_equal(wt_l.cpu().numpy(), wt_r.cpu().numpy()), (layer, S, bf16)
+            assert np.array_equal(y_l.cpu().numpy(), y_r.cpu().numpy()), (layer, S, bf16)
+            if n < 2:
+                ridx, rw, _, flags, _ = O.route(c, x, dl.W_host, dl.bias_host, x_is_bf16=bf16)
+                assert not flags.any()
+                assert np.array_equal(idx_l.cpu().numpy(), ridx)
+                assert np.abs(wt_l.cpu().numpy() - rw).max() <= 1e-6 * c.routed_scaling_factor
+                xs = np.ascontiguousarray(x)
+                experts = {e: dl.host_expert(e) for e in set(ridx.ravel().tolist())}
+                experts[c.n_experts] = dl.host[c.n_experts]
+                ref = O.moe_ffn(c, xs, ridx, rw, experts, x_is_bf16=bf16)
+                assert max_rel_err(y_l.cpu().numpy(), ref) <= TOL_FP32
+
+
+def test_layer_call_unresident_and_tied(tiny):
+    """moe_layer for one token with an unresident selected expert (its row is
+    NaN, as from moe_ffn) and with exactly tied router rows (lowest indices)."""
+    c = tiny.c
+    x = gen.tokens(tiny.w.with_(tokens=1), step=31)
+    xt, dt = x_device(tiny.w, x)
+    idx_r, _ = tiny.route(xt, dt)
+    table = tiny.table.clone()
+    table[int(idx_r[0, 1])] = -1
+    idx_l, wt_l, y_l = tiny.layer(xt, dt, table=table)
+    torch.cuda.synchronize()
+    assert np.isnan(y_l.cpu().numpy()).all()
+    assert np.array_equal(idx_l.cpu().numpy(), idx_r.cpu().numpy())
+    Wt, bt = tied_router(c, tiny.W_host, tiny.bias_host, "all")
+    W0, b0 = tiny.W, tiny.bias
+    try:
+        tiny.W, tiny.bias = dev(Wt), dev(bt)
+        idx_l, wt_l, y_l = tiny.layer(xt, dt)
+        torch.cuda.synchronize()
+    finally:
+        tiny.W, tiny.bias = W0, b0
+    assert (idx_l.cpu().numpy() == np.arange(c.top_k)).all()
+    assert np.allclose(wt_l.cpu().numpy(), c.routed_scaling_factor / c.top_k, rtol=1e-6)
+
+
 @pytest.mark.parametrize("S", [1, 5, 8])
 def test_router_uninitialised_workspace_is_poisoned(tiny, S):
     """A workspace whose header was never written gives idx -1 and w NaN for
