@@ -70,27 +70,34 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
   GuFeat<NG> b0, b1, b2;
   uint64_t my_ptr = 0;
   float v[32];
+  float *lf = (float *)(lds + (size_t)ng * 24);
+  // x becomes limbs right after its loads and one feature's request: behind
+  // the full ring's requests (a long queue while every wave streams) the
+  // staging, and the barrier after it, would start late.
+  auto stage_x = [&]() {
+    if (has_x) {
+      Limbs L;
+      to_limbs(v, L);
+      store_limbs(lds + (size_t)threadIdx.x * 24, lf + threadIdx.x, L);
+    }
+  };
   if constexpr (EPT > 0) {
     __shared__ SelLds sel;
     const SelCfg c{a.E, a.G, a.Gk, a.k, a.norm, a.rsf};
     SelIn<EPT> in;
     sel_load<EPT, true>(c, a.keys, a.scores, a.table, in);
     load32(a.x, a.x_bf16, (size_t)min((int)threadIdx.x, ng - 1) * kGroup, v);
-    const bool early = n > 0 && ns >= 2;  // both first features are shared: they need no selection
-    if (early) {
-      gu_feat_load(b0, a, 0, n, ns, s0, r0, 0, lane);
-      gu_feat_load(b1, a, 1, n, ns, s0, r0, 0, lane);
-    }
+    const bool early = n > 0 && ns >= 1;  // a first feature of the shared expert needs no selection
+    if (early) gu_feat_load(b0, a, 0, n, ns, s0, r0, 0, lane);
+    stage_x();
     select_block<EPT, true>(c, 0, in, sel, blockIdx.x == 0 ? a.idx_out : nullptr, a.w_out);
     if (lane < a.k) {
       const int slot = sel.out_slot[lane];
       if (slot >= 0 && slot < a.n_slots) my_ptr = (uint64_t)(uintptr_t)(a.base + (size_t)slot * (size_t)a.slot_bytes);
     }
     if (blockIdx.x == 0 && threadIdx.x < 64 && lane < a.k) a.eptr[lane] = my_ptr;  // for the down kernel
-    if (n > 0 && !early) {
-      gu_feat_load(b0, a, 0, n, ns, s0, r0, my_ptr, lane);
-      gu_feat_load(b1, a, 1, n, ns, s0, r0, my_ptr, lane);
-    }
+    if (n > 0 && !early) gu_feat_load(b0, a, 0, n, ns, s0, r0, my_ptr, lane);
+    if (n > 0) gu_feat_load(b1, a, 1, n, ns, s0, r0, my_ptr, lane);
   } else {
     // Order (loads return in order): lane j's expert id, the activations, then
     // the expert's slot; all unconditional (clamped) so the waits are exact.
@@ -101,20 +108,12 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
     my_ptr = e_ok && slot >= 0 && slot < a.n_slots ? (uint64_t)(uintptr_t)(a.base + (size_t)slot * (size_t)a.slot_bytes)
                                                     : 0;
     if (blockIdx.x == 0 && threadIdx.x < 64 && lane < a.k) a.eptr[lane] = my_ptr;  // for the down kernel
-    // three-slot ring, two features in flight while one is computed; the first
-    // two (shared-expert features when the wave has any) are issued before the
-    // activations are staged.  Loads are unconditional (indices clamped; repeats
-    // at the tail hit in cache) so the load counter order is fixed.
-    if (n > 0) {
-      gu_feat_load(b0, a, 0, n, ns, s0, r0, my_ptr, lane);
-      gu_feat_load(b1, a, 1, n, ns, s0, r0, my_ptr, lane);
-    }
-  }
-  float *lf = (float *)(lds + (size_t)ng * 24);
-  if (has_x) {
-    Limbs L;
-    to_limbs(v, L);
-    store_limbs(lds + (size_t)threadIdx.x * 24, lf + threadIdx.x, L);
+    // three-slot ring, two features in flight while one is computed.  Loads are
+    // unconditional (indices clamped; repeats at the tail hit in cache) so the
+    // load counter order is fixed.
+    if (n > 0) gu_feat_load(b0, a, 0, n, ns, s0, r0, my_ptr, lane);
+    stage_x();
+    if (n > 0) gu_feat_load(b1, a, 1, n, ns, s0, r0, my_ptr, lane);
   }
   __syncthreads();
   if (n <= 0) return;
@@ -155,8 +154,16 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
 
 // HLDS: h of every expert is converted to limbs into LDS by the workgroup;
 // otherwise the limbs come from global memory (converted by k_to_limbs).
+//
+// Work of a workgroup: the (expert, tile) units of its row block, unit u =
+// expert u / nb, tile t0 + u % nb (nb tiles in the block); wave w takes units
+// w, w + nw, ... .  Each wave requests its first tile, then converts its share
+// of h (staging that waits behind a long queue of weight requests would hold
+// the whole workgroup at the barrier), and after the barrier requests unit
+// m + 1 before it computes unit m.
 template <int NGD, bool HLDS>
 __global__ __launch_bounds__(kDnS1Waves * 64) void k_down_s1(FfnArgs a) {
+  constexpr int MU = 3;  // units per wave per round
   __shared__ float part[kMaxK + 1][kDnRows * kDnMaxTb];
   __shared__ int s_idx[kMaxK];  // [0]: the token's idx row is invalid (combine poisons y)
   __shared__ float s_w[kMaxK];
@@ -164,46 +171,51 @@ __global__ __launch_bounds__(kDnS1Waves * 64) void k_down_s1(FfnArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int NE = a.k + (a.Is > 0 ? 1 : 0);
   const int Imax = max(a.I, a.Is), ngm = Imax / kGroup, nt = a.H / kDnRows;
-  const int t0 = blockIdx.x * a.tb, t1 = min(nt, t0 + a.tb);
-  // Order of the first loads (they return in order, so a value that is waited
-  // for waits for everything issued before it): the wave's resolved expert
-  // pointer (written by the gate/up kernel: one load instead of idx then
-  // table), this thread's first group of h (staging), the wave's first two
-  // tiles; idx and w for the combine last.
+  const int t0 = blockIdx.x * a.tb, t1 = min(nt, t0 + a.tb), nb = t1 - t0, U = NE * nb;
   float *hf_lds = (float *)(hlds + (size_t)NE * ngm * 24);
   auto h_group = [&](int i, bool &use, float (&v)[32]) {
     const int e2 = i / ngm, g = i - e2 * ngm;
     use = HLDS && i < NE * ngm && g * kGroup < (e2 == a.k ? a.Is : a.I);
     // unconditional (a group that is not used reads group 0 and is dropped), so
-    // that the wait for the expert pointer loaded before it can be exact
+    // that the waits for the loads issued before it can be exact
     load32(a.h, 0, use ? (size_t)e2 * Imax + (size_t)g * kGroup : 0, v);
   };
-  int j = wave;
-  const uint8_t *dn = a.base;
-  int inter = a.I;
-  bool valid = false;
-  DnTile<NGD> q0, q1;
-  auto ex_of = [&](int jj) -> const uint8_t * {
-    return jj == a.k ? a.shared : (const uint8_t *)(uintptr_t)ldg<uint64_t>(a.eptr + min(jj, a.k - 1));
+  // unit -> expert, tile, weights (clamped: units past U repeat the last unit and are not computed)
+  struct Unit {
+    int j, t, inter;
+    bool valid;
+    const uint8_t *dn;
   };
-  auto resolve = [&](int jj, const uint8_t *ex) {
-    inter = jj == a.k ? a.Is : a.I;
-    valid = ex != nullptr;
-    if (!valid) inter = a.I;
-    dn = uniform_ptr((valid ? ex : a.base) + down_offset(a.H, inter));
+  auto ex_of = [&](int jj) -> const uint8_t * {  // the load is unconditional (exact waits)
+    const uint8_t *p = (const uint8_t *)(uintptr_t)ldg<uint64_t>(a.eptr + min(jj, a.k - 1));
+    return jj == a.k ? a.shared : p;
   };
-  const uint8_t *ex0 = ex_of(j);
+  auto unit_of = [&](int u, const uint8_t *ex) {
+    Unit r;
+    u = min(u, U - 1);
+    r.j = u / nb;
+    r.t = t0 + (u - r.j * nb);
+    r.valid = ex != nullptr;
+    r.inter = (r.j == a.k && r.valid) ? a.Is : a.I;
+    r.dn = uniform_ptr((r.valid ? ex : a.base) + down_offset(a.H, r.inter));
+    return r;
+  };
+  auto unit_expert = [&](int u) { return min(u, U - 1) / nb; };
+  DnTile<NGD> q[2];
+  Unit un[2];
+  // order of the first loads: the units' expert pointers, this thread's first
+  // group of h, the first unit's tile, idx and w for the combine
+  const uint8_t *ex[MU];
+#pragma unroll
+  for (int m = 0; m < MU; ++m) ex[m] = ex_of(unit_expert(wave + nw * m));
   bool use_h;
   float hv0[32];
   h_group(threadIdx.x, use_h, hv0);
-  if (j < NE) {
-    resolve(j, ex0);
-    dn_tile_load(q0, dn, inter, t0, t1, lane);
-    dn_tile_load(q1, dn, inter, t0 + 1, t1, lane);
-  }
+  un[0] = unit_of(wave, ex[0]);
+  dn_tile_load(q[0], un[0].dn, un[0].inter, un[0].t, un[0].t + 1, lane);
   int my_idx = 0;
   float my_w = 0.f;
-  if ((int)threadIdx.x < a.k) {  // for the combine (stored to LDS after the tiles)
+  if ((int)threadIdx.x < a.k) {
     my_idx = ldg<int>(a.idx + threadIdx.x);
     my_w = ldg<float>(a.w + threadIdx.x);
   }
@@ -222,40 +234,46 @@ __global__ __launch_bounds__(kDnS1Waves * 64) void k_down_s1(FfnArgs a) {
     }
   }
   __syncthreads();
-  for (; j < NE; j += nw) {
-    if (j != wave) {
-      resolve(j, ex_of(j));
-      dn_tile_load(q0, dn, inter, t0, t1, lane);
-      dn_tile_load(q1, dn, inter, t0 + 1, t1, lane);
-    }
-    const int ng = inter / kGroup;
+  auto compute = [&](const DnTile<NGD> &b, const Unit &uu) {
+    const int ng = uu.inter / kGroup;
     Limbs hv[NGD];
 #pragma unroll
     for (int g2 = 0; g2 < NGD; ++g2) {
       const int g = min(lane + 64 * g2, ng - 1);
-      if (HLDS) load_limbs_lds(hlds + ((size_t)j * ngm + g) * 24, hf_lds + (size_t)j * ngm + g, hv[g2]);
-      else load_limbs_global(a.hl + ((size_t)j * ngm + g) * 24, a.hf + (size_t)j * ngm + g, hv[g2]);
+      if (HLDS) load_limbs_lds(hlds + ((size_t)uu.j * ngm + g) * 24, hf_lds + (size_t)uu.j * ngm + g, hv[g2]);
+      else load_limbs_global(a.hl + ((size_t)uu.j * ngm + g) * 24, a.hf + (size_t)uu.j * ngm + g, hv[g2]);
       if (lane + 64 * g2 >= ng) hv[g2].f = 0.f;  // clamped duplicate group contributes zero
     }
-    float *dst = &part[j][0];
-    for (int t = t0; t < t1; t += 2) {
-      float acc[kDnRows];
-      dn_tile_dots(q0, hv, acc);
-      if (lane == 63) {
-        const int o = (t - t0) * kDnRows;
+    float acc[kDnRows];
+    dn_tile_dots(b, hv, acc);
+    if (lane == 63) {
+      float *dst = &part[uu.j][(uu.t - t0) * kDnRows];
 #pragma unroll
-        for (int i = 0; i < kDnRows; ++i) dst[o + i] = valid ? acc[i] : __builtin_nanf("");
-      }
-      dn_tile_load(q0, dn, inter, t + 2, t1, lane);
-      if (t + 1 < t1) {
-        dn_tile_dots(q1, hv, acc);
-        if (lane == 63) {
-          const int o = (t + 1 - t0) * kDnRows;
+      for (int i = 0; i < kDnRows; ++i) dst[i] = uu.valid ? acc[i] : __builtin_nanf("");
+    }
+  };
 #pragma unroll
-          for (int i = 0; i < kDnRows; ++i) dst[o + i] = valid ? acc[i] : __builtin_nanf("");
-        }
+  for (int m = 0; m < MU; ++m) {
+    if (m + 1 < MU) {
+      un[(m + 1) & 1] = unit_of(wave + nw * (m + 1), ex[m + 1]);
+      dn_tile_load(q[(m + 1) & 1], un[(m + 1) & 1].dn, un[(m + 1) & 1].inter, un[(m + 1) & 1].t,
+                   un[(m + 1) & 1].t + 1, lane);
+    }
+    if (wave + nw * m < U) compute(q[m & 1], un[m & 1]);
+  }
+  // further rounds (more units than MU per wave), same pipeline
+  for (int base = nw * MU; base < U; base += nw * MU) {
+    un[0] = unit_of(base + wave, ex_of(unit_expert(base + wave)));
+    dn_tile_load(q[0], un[0].dn, un[0].inter, un[0].t, un[0].t + 1, lane);
+#pragma unroll
+    for (int m = 0; m < MU; ++m) {
+      if (m + 1 < MU) {
+        const int u = base + wave + nw * (m + 1);
+        un[(m + 1) & 1] = unit_of(u, ex_of(unit_expert(u)));
+        dn_tile_load(q[(m + 1) & 1], un[(m + 1) & 1].dn, un[(m + 1) & 1].inter, un[(m + 1) & 1].t,
+                     un[(m + 1) & 1].t + 1, lane);
       }
-      dn_tile_load(q1, dn, inter, t + 3, t1, lane);
+      if (base + wave + nw * m < U) compute(q[m & 1], un[m & 1]);
     }
   }
   if ((int)threadIdx.x < a.k) {
@@ -271,7 +289,7 @@ __global__ __launch_bounds__(kDnS1Waves * 64) void k_down_s1(FfnArgs a) {
     if (lane == 0) s_idx[0] = bad;
   }
   __syncthreads();
-  const int rows = (t1 - t0) * kDnRows;
+  const int rows = nb * kDnRows;
   if ((int)threadIdx.x < rows) {
     const bool bad = s_idx[0] != 0;
     const int i = threadIdx.x;
@@ -713,7 +731,7 @@ hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st) {
       if (e != hipSuccess) return e;
     }
     ProfScope ps("down_s1", st);
-    const dim3 g((unsigned)a.n_blk), blk(64 * std::min(NE, kDnS1Waves));
+    const dim3 g((unsigned)a.n_blk), blk(64 * std::min(NE * a.tb, kDnS1Waves));
     if (in_lds) {
       MOE_DISPATCH_NG(ceil_groups(Imax), k_down_s1, g, blk, hlds, st, true);
     } else {
