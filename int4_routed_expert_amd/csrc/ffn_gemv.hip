@@ -405,7 +405,7 @@ __device__ inline void poison_h(const FfnArgs &a, int ntok, const int *pairs, in
     for (int tt = 0; tt < ntok; ++tt) a.h[(size_t)pairs[tt] * inter_stride + feat0 + lane] = __builtin_nanf("");
 }
 
-constexpr int kGuWaves = 8;  // waves per small-batch gate/up workgroup, one tile each
+constexpr int kGuWaves = 4;  // waves per small-batch gate/up workgroup, one tile each (two workgroups per CU)
 
 template <int NG>
 __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_small(FfnArgs a) {
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_small(FfnArgs a) {
 // One workgroup per 8-row tile of y; its waves take the union's experts and leave
 // per-(token, rank) dot products in LDS; the workgroup sums them in route order.
 template <int NGD>
-__global__ __launch_bounds__(1024, 1) void k_down_small(FfnArgs a) {
+__global__ __launch_bounds__(512, 4) void k_down_small(FfnArgs a) {
   __shared__ SmallPlan plan;
   __shared__ float part[kSmallS * (kMaxK + 1)][kDnRows];
   build_small_plan(a, plan);
@@ -442,33 +442,53 @@ __global__ __launch_bounds__(1024, 1) void k_down_small(FfnArgs a) {
   const int Imax = max(a.I, a.Is), ngm = Imax / kGroup;
   const int rt = blockIdx.x;
   const int nu = plan.U + (a.Is > 0 ? 1 : 0);
-  for (int u = wave; u < nu; u += nw) {
+  // the wave's experts u = wave, wave + nw, ...: the next one's tile is
+  // requested before the current one is computed (loads clamped to the last)
+  auto expert_of = [&](int u, int &inter) -> const uint8_t * {
+    u = min(u, nu - 1);
     const bool sh = u == plan.U;
-    const uint8_t *ex = sh ? a.shared : expert_ptr(a, plan.uniq[u]);
-    const int inter = sh ? a.Is : a.I;
-    if (!ex) {
+    inter = sh ? a.Is : a.I;
+    return sh ? a.shared : expert_ptr(a, plan.uniq[u]);
+  };
+  auto tile_src = [&](const uint8_t *ex, int inter) {
+    return uniform_ptr((ex ? ex : a.base) + down_offset(a.H, ex ? inter : a.I));
+  };
+  DnTile<NGD> q0, q1;
+  int inter_c = a.I;
+  const uint8_t *ex_c = expert_of(wave, inter_c);
+  if (wave < nu) dn_tile_load(q0, tile_src(ex_c, inter_c), ex_c ? inter_c : a.I, rt, rt + 1, lane);
+  // unit u from `cur` (already requested); requests unit u + nw into `nxt`
+  auto step = [&](const DnTile<NGD> &cur, DnTile<NGD> &nxt, int u) {
+    int inter_n = a.I;
+    const uint8_t *ex_n = expert_of(u + nw, inter_n);
+    dn_tile_load(nxt, tile_src(ex_n, inter_n), ex_n ? inter_n : a.I, rt, rt + 1, lane);
+    if (!ex_c) {
       if (lane < kDnRows)
         for (int tt = 0; tt < plan.ntok[u]; ++tt) part[plan.pair[u][tt]][lane] = __builtin_nanf("");
-      continue;
-    }
-    DnTile<NGD> q;
-    dn_tile_load(q, uniform_ptr(ex + down_offset(a.H, inter)), inter, rt, rt + 1, lane);
-    const int ng = inter / kGroup;
-    for (int tt = 0; tt < plan.ntok[u]; ++tt) {
-      const int pr = plan.pair[u][tt];
-      Limbs hv[NGD];
+    } else {
+      const int ng = inter_c / kGroup;
+      for (int tt = 0; tt < plan.ntok[u]; ++tt) {
+        const int pr = plan.pair[u][tt];
+        Limbs hv[NGD];
 #pragma unroll
-      for (int g2 = 0; g2 < NGD; ++g2) {
-        const int g = min(lane + 64 * g2, ng - 1);
-        load_limbs_global(a.hl + ((size_t)pr * ngm + g) * 24, a.hf + (size_t)pr * ngm + g, hv[g2]);
-        if (lane + 64 * g2 >= ng) hv[g2].f = 0.f;
+        for (int g2 = 0; g2 < NGD; ++g2) {
+          const int g = min(lane + 64 * g2, ng - 1);
+          load_limbs_global(a.hl + ((size_t)pr * ngm + g) * 24, a.hf + (size_t)pr * ngm + g, hv[g2]);
+          if (lane + 64 * g2 >= ng) hv[g2].f = 0.f;
+        }
+        float acc[kDnRows];
+        dn_tile_dots(cur, hv, acc);
+        if (lane == 63)
+#pragma unroll
+          for (int i = 0; i < kDnRows; ++i) part[pr][i] = acc[i];
       }
-      float acc[kDnRows];
-      dn_tile_dots(q, hv, acc);
-      if (lane == 63)
-#pragma unroll
-        for (int i = 0; i < kDnRows; ++i) part[pr][i] = acc[i];
     }
+    ex_c = ex_n;
+    inter_c = inter_n;
+  };
+  for (int u = wave; u < nu; u += 2 * nw) {
+    step(q0, q1, u);
+    if (u + nw < nu) step(q1, q0, u + nw);
   }
   __syncthreads();
   const int tid = threadIdx.x;
@@ -759,7 +779,7 @@ hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   ProfScope ps("down_small", st);
-  const int nw = std::min(Umax + 1, 16);
+  const int nw = std::min(Umax + 1, 8);
   const dim3 g2(a.H / kDnRows), b2(64 * nw);
   MOE_DISPATCH_NG(ceil_groups(Imax), k_down_small, g2, b2, 0, st);
   return hipGetLastError();

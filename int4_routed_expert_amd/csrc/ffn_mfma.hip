@@ -157,7 +157,7 @@ __device__ inline void stage_mfma(GemmAcc &C, const bf16x8 (&A)[kMB][kKG], const
     }
 }
 
-template <bool ABF>
+template <bool ABF, int kDepth, int MBV>
 __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_colp, const uint8_t *const *s_sclp,
                                  uint8_t *s_b, const void *abase, const size_t *arow, int wn, int lane) {
   const int tid = threadIdx.x;
@@ -165,7 +165,6 @@ __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_col
   const uint8_t *colp = s_colp[bc];
   const uint8_t *sclp = s_sclp[bc];
   const int oct = lane >> 4;  // this lane's K octet in A and B fragments
-  const int ns = (ng + kKG - 1) / kKG;
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
@@ -174,8 +173,8 @@ __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_col
     uint2 w;
     uint16_t sc;
   };
-  auto load_b = [&](int st) {
-    const int g = min(st, ng - 1);
+  auto load_b = [&](int g) {
+    g = min(g, ng - 1);
     return BRaw{ldg<uint2>(colp + (size_t)g * 16 + bp * 8), ldg<uint16_t>(sclp + (size_t)g * 16)};
   };
   auto store_b = [&](int buf, const BRaw &r) {
@@ -184,41 +183,62 @@ __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_col
     *(uint4 *)(d) = dequant8(r.w.x, s);
     *(uint4 *)(d + 16) = dequant8(r.w.y, s);
   };
-  auto load_a = [&](int st, ARaw<ABF> (&r)[kMB][kKG]) {
+  auto load_a = [&](int g, ARaw<ABF> (&r)[kMB]) {
+    g = min(g, ng - 1);
 #pragma unroll
-    for (int gi = 0; gi < kKG; ++gi) {
-      const int g = min(st * kKG + gi, ng - 1);
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) r[mb][gi].load(abase, arow[mb] + (size_t)g * 32 + oct * 8);
-    }
+    for (int mb = 0; mb < MBV; ++mb) r[mb].load(abase, arow[mb] + (size_t)g * 32 + oct * 8);
   };
-  bf16x8 A[kMB][kKG];
-  BRaw b1 = load_b(min(1, ns - 1));  // stage 1's weights; stage 0's are stored below
-  {
-    const BRaw b0 = load_b(0);
-    ARaw<ABF> r[kMB][kKG];
-    load_a(0, r);
-    store_b(0, b0);
+  // Ring of kDepth stages in registers: A of stage s is requested kDepth
+  // stages before its MFMAs, B of stage s kDepth stages before it is
+  // dequantised into LDS (one stage before its MFMAs).  Loads are clamped to
+  // the last group, so every one is unconditional; the stages past the last
+  // group (padding to a multiple of kDepth) multiply zeroed A fragments.
+  ARaw<ABF> aq[kDepth][kMB];
+  BRaw bq[kDepth];
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-      for (int gi = 0; gi < kKG; ++gi) A[mb][gi] = r[mb][gi].get();
+  for (int d = 0; d < kDepth; ++d) {
+    load_a(d, aq[d]);
+    bq[d] = load_b(d);
   }
+  store_b(0, bq[0]);
+  bq[0] = load_b(kDepth);
   __syncthreads();
-  for (int st = 0; st < ns; ++st) {
-    const BRaw b2 = load_b(min(st + 2, ns - 1));  // unconditional prefetch (the last ones repeat)
-    ARaw<ABF> An[kMB][kKG];
-    load_a(min(st + 1, ns - 1), An);
-    const uint8_t *sb = s_b + (st & 1) * kBStage + (wn * 16 * kNB) * kBStride;
-    stage_mfma<kMB>(C, A, sb, lane, oct);  // rows past the tile's end repeat its last row; not stored
-    store_b((st + 1) & 1, b1);
-    b1 = b2;
+  const int ns = (ng + kDepth - 1) / kDepth * kDepth;
+  for (int st = 0; st < ns; st += kDepth) {
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
+    for (int d = 0; d < kDepth; ++d) {
+      const int s = st + d;
+      const uint32_t live = s < ng ? ~0u : 0u;
+      bf16x8 A[kMB][kKG];
 #pragma unroll
-      for (int gi = 0; gi < kKG; ++gi) A[mb][gi] = An[mb][gi].get();
-    __syncthreads();
+      for (int mb = 0; mb < MBV; ++mb) {
+        const uint4 v = __builtin_bit_cast(uint4, aq[d][mb].get());
+        A[mb][0] = __builtin_bit_cast(bf16x8, make_uint4(v.x & live, v.y & live, v.z & live, v.w & live));
+      }
+      load_a(s + kDepth, aq[d]);
+      const uint8_t *sb = s_b + (s & 1) * kBStage + (wn * 16 * kNB) * kBStride;
+      if (MBV > 0) stage_mfma<MBV>(C, A, sb, lane, oct);  // rows past the tile's end repeat its last row; not stored
+      store_b((s + 1) & 1, bq[(d + 1) % kDepth]);
+      bq[(d + 1) % kDepth] = load_b(s + 1 + kDepth);
+      __syncthreads();
+    }
   }
+}
+
+// Row block rb (16 rows) of a tile belongs to wave rb % kWaves (slot rb /
+// kWaves), so that a partial tile's valid blocks spread over all SIMDs; a wave
+// multiplies only its valid blocks (MBV), every wave dequantises its share of B.
+__device__ inline int row_of(int wave, int mb, int r16) { return (wave + kWaves * mb) * 16 + r16; }
+
+template <bool ABF, int kDepth>
+__device__ inline void gemm_rows(GemmAcc &C, int rows, int ng, const uint8_t *const *s_colp,
+                                 const uint8_t *const *s_sclp, uint8_t *s_b, const void *abase, const size_t *arow,
+                                 int wave, int lane) {
+  const int nblk = (rows + 15) / 16;
+  const int mbv = (wave < nblk ? 1 : 0) + (wave + kWaves < nblk ? 1 : 0);
+  if (mbv == 2) gemm_loop<ABF, kDepth, 2>(C, ng, s_colp, s_sclp, s_b, abase, arow, 0, lane);
+  else if (mbv == 1) gemm_loop<ABF, kDepth, 1>(C, ng, s_colp, s_sclp, s_b, abase, arow, 0, lane);
+  else gemm_loop<ABF, kDepth, 0>(C, ng, s_colp, s_sclp, s_b, abase, arow, 0, lane);
 }
 
 // Gate/up for one (M tile, N tile of kNT/2 features): h[pair][feature] = silu(g) * u.
@@ -250,12 +270,13 @@ __global__ __launch_bounds__(kThreads) void k_gu_mfma(FfnArgs a) {
   tile_rows(a, mt, s_tok, s_pair);
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave, wn = 0;  // rows 32 wm .. 32 wm + 31, all columns
+  const int wn = 0;  // all columns
   size_t arow[kMB];
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) arow[mb] = (size_t)s_tok[wm * 32 + mb * 16 + (lane & 15)] * a.H;
+  for (int mb = 0; mb < kMB; ++mb) arow[mb] = (size_t)s_tok[row_of(wave, mb, lane & 15)] * a.H;
   GemmAcc C;
-  gemm_loop<true>(C, a.H / kGroup, s_colp, s_sclp, s_b, a.x_bf16 ? a.x : (const void *)a.xb, arow, wn, lane);
+  gemm_rows<true, 3>(C, mt.n, a.H / kGroup, s_colp, s_sclp, s_b, a.x_bf16 ? a.x : (const void *)a.xb, arow, wave,
+                     lane);
   // epilogue: even columns are gate, the next lane holds the matching up
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb)
@@ -265,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void k_gu_mfma(FfnArgs a) {
       for (int i = 0; i < 4; ++i) {
         const float gv = C.acc[mb][nb][i];
         const float uv = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(gv), 0xB1, 0xF, 0xF, false));
-        const int j = wm * 32 + mb * 16 + (lane >> 4) * 4 + i;
+        const int j = row_of(wave, mb, (lane >> 4) * 4 + i);
         const int c = wn * 16 * kNB + nb * 16 + (lane & 15);
         const int f = nt * (kNT / 2) + (c / 8) * kGuPairs + (c % 8) / 2;
         if ((c & 1) == 0 && j < mt.n && f < inter) {
@@ -308,19 +329,19 @@ __global__ __launch_bounds__(kThreads) void k_dn_mfma(FfnArgs a) {
   }
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave, wn = 0;
+  const int wn = 0;
   size_t arow[kMB];
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) arow[mb] = (size_t)s_pair[wm * 32 + mb * 16 + (lane & 15)] * 2 * Imax;
+  for (int mb = 0; mb < kMB; ++mb) arow[mb] = (size_t)s_pair[row_of(wave, mb, lane & 15)] * 2 * Imax;
   GemmAcc C;
-  gemm_loop<true>(C, inter / kGroup, s_colp, s_sclp, s_b, a.h, arow, wn, lane);
+  gemm_rows<true, 2>(C, mt.n, inter / kGroup, s_colp, s_sclp, s_b, a.h, arow, wave, lane);
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = wm * 32 + mb * 16 + (lane >> 4) * 4 + i;
+        const int j = row_of(wave, mb, (lane >> 4) * 4 + i);
         const int n = n0 + wn * 16 * kNB + nb * 16 + (lane & 15);
         if (j < mt.n && n < a.H) a.part[(size_t)s_pair[j] * a.H + n] = C.acc[mb][nb][i];
       }
