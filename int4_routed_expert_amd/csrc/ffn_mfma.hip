@@ -241,19 +241,33 @@ __device__ inline void gemm_rows(GemmAcc &C, int rows, int ng, const uint8_t *co
   else gemm_loop<ABF, kDepth, 0>(C, ng, s_colp, s_sclp, s_b, abase, arow, 0, lane);
 }
 
+// Workgroups go to the 8 XCDs (each with its own L2) round-robin in launch
+// order, so block b runs on XCD b % 8.  M tile m is given to XCD m % 8 with all
+// its N tiles back to back: the N tiles of an M tile share its activation rows
+// and run together in one L2 instead of fetching the rows once per N tile.
+constexpr int kXcds = 8;
+__device__ inline void tile_of_block(int n_tiles, int &m, int &nt) {
+  const int b = blockIdx.x, x = b % kXcds, local = b / kXcds;
+  m = (local / n_tiles) * kXcds + x;
+  nt = local % n_tiles;
+}
+inline unsigned tile_blocks(int max_mtiles, int n_tiles) {
+  return (unsigned)((max_mtiles + kXcds - 1) / kXcds * kXcds * n_tiles);
+}
+
 // Gate/up for one (M tile, N tile of kNT/2 features): h[pair][feature] = silu(g) * u.
 __global__ __launch_bounds__(kThreads) void k_gu_mfma(FfnArgs a) {
   __shared__ __align__(16) uint8_t s_b[2 * kBStage];
   __shared__ const uint8_t *s_colp[kNT];
   __shared__ const uint8_t *s_sclp[kNT];
   __shared__ int s_tok[kMT], s_pair[kMT];
-  const int m = blockIdx.x;
+  int m, nt;  // features nt*kNT/2 ..
+  tile_of_block((2 * max(a.I, a.Is) + kNT - 1) / kNT, m, nt);
   const int n_mt = a.n_items[2] + a.n_items[3];
   if (m >= n_mt) return;
   const MTile mt = mtile_of(a, m);
   const bool sh = mt.e == a.E;
   const int inter = sh ? a.Is : a.I;
-  const int nt = blockIdx.y;  // features nt*kNT/2 ..
   if (nt * (kNT / 2) >= inter) return;
   const uint8_t *ex = sh ? a.shared : expert_ptr(a, mt.e);
   if (!ex) return;  // the down GEMM poisons this tile's rows
@@ -303,13 +317,14 @@ __global__ __launch_bounds__(kThreads) void k_dn_mfma(FfnArgs a) {
   __shared__ const uint8_t *s_colp[kNT];
   __shared__ const uint8_t *s_sclp[kNT];
   __shared__ int s_tok[kMT], s_pair[kMT];
-  const int m = blockIdx.x;
+  int m, nt;
+  tile_of_block((a.H + kNT - 1) / kNT, m, nt);
   const int n_mt = a.n_items[2] + a.n_items[3];
   if (m >= n_mt) return;
   const MTile mt = mtile_of(a, m);
   const bool sh = mt.e == a.E;
   const int inter = sh ? a.Is : a.I;
-  const int n0 = blockIdx.y * kNT;
+  const int n0 = nt * kNT;
   const uint8_t *ex = sh ? a.shared : expert_ptr(a, mt.e);
   tile_rows(a, mt, s_tok, s_pair);
   if (!ex) {
@@ -368,15 +383,14 @@ hipError_t launch_gu_mfma(const FfnArgs &a, hipStream_t st) {
   }
   ProfScope ps("gateup_mfma", st);
   const int Imax = std::max(a.I, a.Is);
-  MOE_LAUNCH(k_gu_mfma, dim3((unsigned)a.max_mtiles, (unsigned)((2 * Imax + kNT - 1) / kNT)), dim3(kThreads), 0, st,
-             a);
+  MOE_LAUNCH(k_gu_mfma, dim3(tile_blocks(a.max_mtiles, (2 * Imax + kNT - 1) / kNT)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_dn_mfma(const FfnArgs &a, hipStream_t st) {
   if (a.mfma_thr <= 0 || a.max_mtiles <= 0) return hipSuccess;
   ProfScope ps("down_mfma", st);
-  MOE_LAUNCH(k_dn_mfma, dim3((unsigned)a.max_mtiles, (unsigned)((a.H + kNT - 1) / kNT)), dim3(kThreads), 0, st, a);
+  MOE_LAUNCH(k_dn_mfma, dim3(tile_blocks(a.max_mtiles, (a.H + kNT - 1) / kNT)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
