@@ -146,17 +146,17 @@ __device__ inline void to_limbs(const float *v, Limbs &out) {
   }
 }
 
-// sum_c q_c X_c of one group (exact), returned as fp32.
+// sum_c q_c X_c of one group (exact), returned as fp32: Horner over the limbs,
+// T = 16 T + (limb l's four dot8), from the top limb down (|T| <= 2^30).
 __device__ inline float group_dot(const uint4 q, const Limbs &x) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-  int S[6] = {0, 0, 0, 0, 0, 0};
+  int T = 0;
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
+  for (int l = 5; l >= 0; --l) {
+    T <<= 4;
 #pragma unroll
-    for (int l = 0; l < 6; ++l) S[l] = __builtin_amdgcn_sdot8((int)w[d], (int)x.L[l][d], S[l], false);
-  int T = S[5];
-#pragma unroll
-  for (int l = 4; l >= 0; --l) T = (T << 4) + S[l];
+    for (int d = 0; d < 4; ++d) T = __builtin_amdgcn_sdot8((int)w[d], (int)x.L[l][d], T, false);
+  }
   return (float)T;
 }
 

@@ -405,30 +405,113 @@ __device__ inline void poison_h(const FfnArgs &a, int ntok, const int *pairs, in
     for (int tt = 0; tt < ntok; ++tt) a.h[(size_t)pairs[tt] * inter_stride + feat0 + lane] = __builtin_nanf("");
 }
 
-constexpr int kGuWaves = 4;  // waves per small-batch gate/up workgroup, one tile each (two workgroups per CU)
+constexpr int kGuSmallWaves = 8;  // waves per small-batch gate/up workgroup (one workgroup per CU)
 
+// Two to four tokens, gate/up: persistent streaming over the batch union's
+// features like the one-token kernel.  Each wave owns an equal share of the
+// shared expert's features (first: no routing needed) and of the union's routed
+// features (unique experts ascending, I features each); a 3-slot ring keeps
+// two features in flight while one is applied to every token that chose its
+// expert.  The workgroup converts the S tokens' activations to limbs in LDS
+// once; a (feature, token) result parks in a lane and is stored 64 at a time.
 template <int NG>
-__global__ __launch_bounds__(kGuWaves * 64) void k_gateup_small(FfnArgs a) {
+__global__ __launch_bounds__(kGuSmallWaves * 64) void k_gateup_small(FfnArgs a) {
   __shared__ SmallPlan plan;
+  __shared__ const uint8_t *s_ptr[kSmallS * kMaxK];
+  // [S][H/32] groups of 24 limb words at a stride of kXs words (conflict-free
+  // 16-byte reads across lanes), then [S][H/32] factors; H <= 8192
+  constexpr int kXs = 28;
+  __shared__ __align__(16) uint32_t xlds[kSmallS * 256 * (kXs + 1)];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ng = a.H / kGroup, Imax = max(a.I, a.Is), nx = a.S * ng;
+  float *xf_lds = (float *)(xlds + (size_t)nx * kXs);
+  // activations of group threadIdx.x (and + blockDim.x) of the S tokens, loaded first
+  float v0[32], v1[32];
+  const int i0 = threadIdx.x, i1 = threadIdx.x + blockDim.x;
+  load32(a.x, a.x_bf16, (size_t)min(i0, nx - 1) * kGroup, v0);
+  load32(a.x, a.x_bf16, (size_t)min(i1, nx - 1) * kGroup, v1);
   build_small_plan(a, plan);
-  const int wave = threadIdx.x >> 6;
-  const int Imax = max(a.I, a.Is);
-  const int tr = a.I / kGuPairs, ts = a.Is / kGuPairs;
-  const int total = plan.U * tr + ts;
-  const int tile = blockIdx.x * kGuWaves + wave;
-  if (tile >= total) return;
-  int u, t;
-  const uint8_t *ex;
-  if (tile < plan.U * tr) {
-    u = tile / tr; t = tile - u * tr;
-    ex = expert_ptr(a, plan.uniq[u]);
-  } else {
-    u = plan.U; t = tile - plan.U * tr;
-    ex = a.shared;
+  const int U = plan.U;
+  const int W = gridDim.x * (blockDim.x >> 6), wid = blockIdx.x * (blockDim.x >> 6) + wave;
+  const long Is = a.Is, Fr = (long)U * a.I;
+  const int s0 = (int)(wid * Is / W), s1 = (int)((wid + 1) * Is / W);
+  const int r0 = (int)(wid * Fr / W), r1 = (int)((wid + 1) * Fr / W);
+  const int ns = s1 - s0, n = ns + (r1 - r0);
+  GuFeat<NG> b0, b1, b2;
+  // item i -> unique slot (U: shared) and feature
+  auto item = [&](int i, int &u, int &f) {
+    i = min(i, n - 1);
+    if (i < ns) {
+      u = U;
+      f = s0 + i;
+    } else {
+      const int r = r0 + i - ns;
+      u = r / a.I;
+      f = r - u * a.I;
+    }
+  };
+  auto load = [&](GuFeat<NG> &bb, int i) {
+    int u, f;
+    item(i, u, f);
+    gu_row_load(bb, a, u == U ? a.shared : uniform_ptr(s_ptr[u]), f, lane);
+  };
+  const bool early = n > 0 && ns >= 1;  // a shared first feature needs no expert pointer
+  if (early) gu_row_load(b0, a, a.shared, s0, lane);
+  if ((int)threadIdx.x < U) s_ptr[threadIdx.x] = expert_ptr(a, plan.uniq[threadIdx.x]);
+  if (i0 < nx) {
+    Limbs L;
+    to_limbs(v0, L);
+    store_limbs(xlds + (size_t)i0 * kXs, xf_lds + i0, L);
   }
-  if (!ex) { poison_h(a, plan.ntok[u], plan.pair[u], t * kGuPairs, Imax); return; }
-  gateup_tile<NG>(a, uniform_ptr(ex + (size_t)t * gu_tile_bytes(a.H)), plan.ntok[u], plan.tok[u], plan.pair[u],
-                  t * kGuPairs, Imax);
+  if (i1 < nx) {
+    Limbs L;
+    to_limbs(v1, L);
+    store_limbs(xlds + (size_t)i1 * kXs, xf_lds + i1, L);
+  }
+  for (int i = threadIdx.x + 2 * blockDim.x; i < nx; i += blockDim.x) {  // S * H/32 > 2 * blockDim
+    float v[32];
+    load32(a.x, a.x_bf16, (size_t)i * kGroup, v);
+    Limbs L;
+    to_limbs(v, L);
+    store_limbs(xlds + (size_t)i * kXs, xf_lds + i, L);
+  }
+  __syncthreads();
+  if (n <= 0) return;
+  if (!early) load(b0, 0);
+  load(b1, 1);
+  float hout = 0.f;
+  int hrow_p = 0, c = 0;
+  // applies a loaded feature to every token of its expert
+  auto apply = [&](const GuFeat<NG> &bb, int i) {
+    int u, f;
+    item(i, u, f);
+    const int nt = plan.ntok[u];
+    for (int tt = 0; tt < nt; ++tt) {
+      const int t = plan.tok[u][tt];
+      Limbs xv[NG];
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {  // lanes past the last group repeat it with a zero factor
+        const int g = min(lane + 64 * j, ng - 1);
+        load_limbs_lds(xlds + ((size_t)t * ng + g) * kXs, xf_lds + (size_t)t * ng + g, xv[j]);
+        if (lane + 64 * j >= ng) xv[j].f = 0.f;
+      }
+      hout = gu_feat_compute(bb, xv, c, hout);
+      if (lane == c) hrow_p = plan.pair[u][tt] * Imax + f;
+      if (++c == 64) {
+        stg<float>(a.h + hrow_p, hout);
+        c = 0;
+      }
+    }
+  };
+  for (int i = 0; i < n; i += 3) {
+    load(b2, i + 2);
+    apply(b0, i);
+    load(b0, i + 3);
+    if (i + 1 < n) apply(b1, i + 1);
+    load(b1, i + 4);
+    if (i + 2 < n) apply(b2, i + 2);
+  }
+  if (lane < c) stg<float>(a.h + hrow_p, hout);
 }
 
 // One workgroup per 8-row tile of y; its waves take the union's experts and leave
@@ -759,16 +842,10 @@ hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st) {
     }
     return hipGetLastError();
   }
-  {
-    ProfScope ps("x_limbs", st);
-    e = launch_to_limbs(a.x, a.x_bf16, a.S, a.H, a.H, a.xl, a.xf, st);
-    if (e != hipSuccess) return e;
-  }
   const int Umax = std::min(a.S * a.k, a.E);
   {
     ProfScope ps("gateup_small", st);
-    const long tiles = (long)Umax * (a.I / kGuPairs) + a.Is / kGuPairs;
-    const dim3 g((unsigned)((tiles + kGuWaves - 1) / kGuWaves)), blk(kGuWaves * 64);
+    const dim3 g((unsigned)a.n_cu), blk(kGuSmallWaves * 64);
     MOE_DISPATCH_NG(ceil_groups(a.H), k_gateup_small, g, blk, 0, st);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -80,24 +80,13 @@ __device__ inline uint64_t routed_ptr_lane(const FfnArgs &a, int lane) {
   return p;
 }
 
-// Loads of feature i of this wave's list (clamped into range so that loads are
-// unconditional; lanes past the last group read the last group and contribute
-// zero because their activation limbs are zero).
+// Loads of gate/up row pair r (feature r) of expert ex (null: an unresident
+// expert, read from a stand-in and marked invalid).  Lanes past the last group
+// read the last group and contribute zero because their activation limbs are
+// zero.
 template <int NG>
-__device__ inline void gu_feat_load(GuFeat<NG> &b, const FfnArgs &a, int i, int n, int ns, int s0, int r0,
-                                    uint64_t my_ptr, int lane) {
+__device__ inline void gu_row_load(GuFeat<NG> &b, const FfnArgs &a, const uint8_t *ex, int r, int lane) {
   const int H = a.H, ng = H / kGroup;
-  i = min(i, n - 1);
-  int r;
-  const uint8_t *ex;
-  if (i < ns) {
-    r = s0 + i;
-    ex = a.shared;
-  } else {
-    const int f = r0 + i - ns, j = f / a.I;
-    r = f - j * a.I;
-    ex = lane_ptr(my_ptr, j);
-  }
   b.valid = ex != nullptr;
   if (!ex) ex = a.base;  // readable stand-in; the result is replaced by NaN
   const int pos = r & 3;
@@ -110,6 +99,22 @@ __device__ inline void gu_feat_load(GuFeat<NG> &b, const FfnArgs &a, int i, int 
     b.g[j] = ldg<uint4>(rg + g * 16);
     b.u[j] = ldg<uint4>(rg + H / 2 + g * 16);
     b.s[j] = ldg<uint32_t>(sc + g * 16);
+  }
+}
+
+// Loads of feature i of this wave's list (clamped into range so that loads are
+// unconditional): items [0, ns) are shared features s0 + i, the rest routed
+// features r0 + i - ns of the list (expert j = feature / I, its pointer in lane j
+// of my_ptr).
+template <int NG>
+__device__ inline void gu_feat_load(GuFeat<NG> &b, const FfnArgs &a, int i, int n, int ns, int s0, int r0,
+                                    uint64_t my_ptr, int lane) {
+  i = min(i, n - 1);
+  if (i < ns) {
+    gu_row_load(b, a, a.shared, s0 + i, lane);
+  } else {
+    const int f = r0 + i - ns, j = f / a.I;
+    gu_row_load(b, a, lane_ptr(my_ptr, j), f - j * a.I, lane);
   }
 }
 
