@@ -33,81 +33,70 @@ __global__ __launch_bounds__(256) void k_route_select(RouteArgs a) {
   select_wave_dispatch(a, t, skey, ssg, lane);
 }
 
-// Many tokens: the logits GEMM in fp64, one workgroup per 64 tokens x 32
-// experts.  K advances in chunks of 32 staged in LDS (double-buffered, as fp32:
-// bf16 and fp32 inputs both widen to fp32 exactly); each
-// thread accumulates 4 tokens (strided by 16, so that its LDS reads are free of
-// bank conflicts) x 2 experts with fp64 FMA in h order.
-constexpr int kLT = 64, kLE = 32, kLK = 32, kLPad = 36;  // row stride 144 B
+// Many tokens: the logits GEMM in fp64 on the matrix cores
+// (v_mfma_f64_16x16x4f64: products of fp32 inputs are exact in fp64, sums in
+// fp64), one workgroup per 32 tokens x 32 experts (two workgroups per CU).  K
+// advances in chunks of 32 staged in LDS as fp32 (bf16 and fp32 inputs both
+// widen to fp32 exactly; rows padded to 34 floats so that the fragment reads
+// are free of bank conflicts), double-buffered with one barrier per chunk;
+// wave w owns the 16 x 16 block (tokens 16 (w % 2), experts 16 (w / 2)).  Fragment layouts (checked on
+// the GPU): A lane l = (row l%16, k l/16), B lane l = (k l/16, column l%16),
+// D lane l value i = (row l/16 + 4i, column l%16).
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kLT = 32, kLE = 32, kLK = 32, kLPad = 34;
 __global__ __launch_bounds__(256) void k_route_logits_tiled(RouteArgs a) {
   __shared__ __align__(16) float xs[2][kLT][kLPad];
   __shared__ __align__(16) float wsm[2][kLE][kLPad];
   const int t0 = blockIdx.x * kLT, e0 = blockIdx.y * kLE;
-  const int tid = threadIdx.x;
-  const int xr = tid >> 2, xc = (tid & 3) * 8;  // loader: x row, 8 columns
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int xr = tid >> 3, xc = (tid & 7) * 4;  // loader: x row, 4 columns
   const int wr = tid >> 3, wc = (tid & 7) * 4;  // loader: W row, 4 columns
   const size_t xrow = (size_t)min(t0 + xr, a.S - 1) * a.H;  // rows past S / E are clamped, not stored
   const float *wrow = a.W + (size_t)min(e0 + wr, a.E - 1) * a.H;
-  const int ct = tid & 15, ce = (tid >> 4) * 2;
-  auto load_x = [&](int k0, float4 &p, float4 &q) {
+  auto load_x = [&](int k0, float4 &p) {
     if (a.x_bf16) {
-      const uint4 r = *(const uint4 *)((const uint16_t *)a.x + xrow + k0 + xc);
+      const uint2 r = *(const uint2 *)((const uint16_t *)a.x + xrow + k0 + xc);
       p = make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u), __uint_as_float(r.y << 16),
                       __uint_as_float(r.y & 0xFFFF0000u));
-      q = make_float4(__uint_as_float(r.z << 16), __uint_as_float(r.z & 0xFFFF0000u), __uint_as_float(r.w << 16),
-                      __uint_as_float(r.w & 0xFFFF0000u));
     } else {
       p = *(const float4 *)((const float *)a.x + xrow + k0 + xc);
-      q = *(const float4 *)((const float *)a.x + xrow + k0 + xc + 4);
     }
   };
-  float4 px, qx, pw;
-  load_x(0, px, qx);
+  auto stage = [&](int b, const float4 &p, const float4 &w) {
+    float2 *xd = (float2 *)&xs[b][xr][xc];
+    xd[0] = make_float2(p.x, p.y);
+    xd[1] = make_float2(p.z, p.w);
+    float2 *wd = (float2 *)&wsm[b][wr][wc];
+    wd[0] = make_float2(w.x, w.y);
+    wd[1] = make_float2(w.z, w.w);
+  };
+  float4 px, pw;
+  load_x(0, px);
   pw = *(const float4 *)(wrow + wc);
-  *(float4 *)&xs[0][xr][xc] = px;
-  *(float4 *)&xs[0][xr][xc + 4] = qx;
-  *(float4 *)&wsm[0][wr][wc] = pw;
+  stage(0, px, pw);
   __syncthreads();
-  double acc[4][2];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) acc[r][0] = acc[r][1] = 0.0;
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  const int tb = (wave & 1) * 16, eb = (wave >> 1) * 16, kq = lane >> 4;
   const int nk = a.H / kLK;
   for (int kc = 0; kc < nk; ++kc) {
     const int kn = min(kc + 1, nk - 1) * kLK;  // unconditional prefetch (the last one repeats)
-    load_x(kn, px, qx);
+    load_x(kn, px);
     pw = *(const float4 *)(wrow + kn + wc);
     const int b = kc & 1;
 #pragma unroll
     for (int kk = 0; kk < kLK; kk += 4) {
-      float4 xv[4], wv[2];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) xv[r] = *(const float4 *)&xs[b][ct + 16 * r][kk];
-      wv[0] = *(const float4 *)&wsm[b][ce][kk];
-      wv[1] = *(const float4 *)&wsm[b][ce + 1][kk];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          double t = acc[r][c];
-          t = fma((double)xv[r].x, (double)wv[c].x, t);
-          t = fma((double)xv[r].y, (double)wv[c].y, t);
-          t = fma((double)xv[r].z, (double)wv[c].z, t);
-          t = fma((double)xv[r].w, (double)wv[c].w, t);
-          acc[r][c] = t;
-        }
+      const double av = (double)xs[b][tb + (lane & 15)][kk + kq];
+      const double bv = (double)wsm[b][eb + (lane & 15)][kk + kq];
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
     }
-    *(float4 *)&xs[b ^ 1][xr][xc] = px;
-    *(float4 *)&xs[b ^ 1][xr][xc + 4] = qx;
-    *(float4 *)&wsm[b ^ 1][wr][wc] = pw;
+    stage(b ^ 1, px, pw);
     __syncthreads();
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int t = t0 + ct + 16 * r, e = e0 + ce + c;
-      if (t < a.S && e < a.E) a.logits[(size_t)t * a.E + e] = acc[r][c];
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + tb + (lane >> 4) + 4 * i, e = e0 + eb + (lane & 15);
+    if (t < a.S && e < a.E) a.logits[(size_t)t * a.E + e] = acc[i];
+  }
 }
 
 // Few tokens (S <= kFewTokens), one launch for the whole router: one workgroup
