@@ -596,34 +596,65 @@ constexpr int kTB = 4;  // tokens per work item
 // Per-expert token list in token order: block e scans idx in order and compacts
 // the entries equal to e (each token names an expert at most once).
 __global__ __launch_bounds__(256) void k_bucket(FfnArgs a) {
-  __shared__ int wtot[4];
-  __shared__ int base_s;
+  // Entries i of idx in blocks of 64 rows x 256; per (row, wave) a ballot of the
+  // entries equal to e; an exclusive scan over (row, wave) in order gives each
+  // wave's offset, so the list keeps the order of i.
+  __shared__ unsigned long long s_mask[64][4];
+  __shared__ int s_off[64 * 4];
+  __shared__ int s_wsum[4];
   const int e = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = a.S * a.k;
-  if (tid == 0) base_s = 0;
-  __syncthreads();
-  for (int c0 = 0; c0 < n; c0 += 256) {
-    const int i = c0 + tid;
-    bool m = i < n && ldg<int>(a.idx + i) == e;
-    if (m) {  // a token that names e twice contributes once; the combine poisons it
-      const int t0 = i / a.k * a.k;
-      for (int j = t0; j < i; ++j) m = m && ldg<int>(a.idx + j) != e;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int base = 0;
+  for (int b0 = 0; b0 < n; b0 += 64 * 256) {
+    const int rows = min(64, (n - b0 + 255) / 256);
+    for (int r0 = 0; r0 < rows; r0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {  // loads of 16 rows in flight together
+        const int i = b0 + (r0 + r) * 256 + tid;
+        v[r] = ldg<int>(a.idx + min(i, n - 1));
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = b0 + (r0 + r) * 256 + tid;
+        bool m = r0 + r < rows && i < n && v[r] == e;
+        if (m) {  // a token that names e twice contributes once; the combine poisons it
+          const int t0 = i / a.k * a.k;
+          for (int j = t0; j < i; ++j) m = m && ldg<int>(a.idx + j) != e;
+        }
+        const unsigned long long bal = __ballot(m);
+        if (lane == 0 && r0 + r < rows) s_mask[r0 + r][wave] = bal;
+      }
     }
-    const unsigned long long bal = __ballot(m);
-    const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wtot[wave] = __popcll(bal);
     __syncthreads();
-    int off = base_s;
-    for (int w2 = 0; w2 < wave; ++w2) off += wtot[w2];
-    if (m) {
-      const int t = i / a.k, j = i - t * a.k;
-      a.lists[(size_t)e * a.S + off + pre] = t * (a.k + 1) + j;
+    // exclusive scan of the (row, wave) counts; thread tid holds entry tid = row * 4 + wave
+    const int cnt = (tid >> 2) < rows ? __popcll(s_mask[tid >> 2][tid & 3]) : 0;
+    int inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(inc, o);
+      if (lane >= o) inc += u;
     }
+    if (lane == 63) s_wsum[wave] = inc;
     __syncthreads();
-    if (tid == 0) base_s += wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    int pre = base;
+    for (int w2 = 0; w2 < wave; ++w2) pre += s_wsum[w2];
+    s_off[tid] = pre + inc - cnt;
+    const int block_total = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
     __syncthreads();
+    for (int r = 0; r < rows; ++r) {
+      const unsigned long long msk = s_mask[r][wave];
+      if ((msk >> lane) & 1ull) {
+        const int i = b0 + r * 256 + tid;
+        const int t = i / a.k, j = i - t * a.k;
+        a.lists[(size_t)e * a.S + s_off[r * 4 + wave] + __popcll(msk & lt)] = t * (a.k + 1) + j;
+      }
+    }
+    base += block_total;
+    __syncthreads();  // the next block reuses s_mask, s_off and s_wsum
   }
-  if (tid == 0) a.counts[e] = base_s;
+  if (tid == 0) a.counts[e] = base;
 }
 
 // Work items {expert, first list position, n tokens}: routed experts in id order,
@@ -763,25 +794,32 @@ __global__ __launch_bounds__(256) void k_down_items(FfnArgs a) {
 // y[t, c] = sum_j w[t, j] * part[t, j, c] (route order) + part[t, k, c]; a token
 // whose idx row is out of range or repeats an expert gets NaN.
 __global__ __launch_bounds__(256) void k_combine(FfnArgs a) {
-  __shared__ int bad;
-  const int t = blockIdx.y;
-  if (threadIdx.x == 0) {
-    int b = 0;
-    for (int j = 0; j < a.k; ++j) {
-      const int e = ldg<int>(a.idx + t * a.k + j);
-      b |= (e < 0 || e >= a.E);
-      for (int i = 0; i < j; ++i) b |= ldg<int>(a.idx + t * a.k + i) == e;
-    }
-    bad = b;
+  const int t = blockIdx.y, lane = threadIdx.x & 63;
+  // the token's idx row: every entry in [0, E) and no entry twice (lane j < k holds entry j)
+  const int my_idx = lane < a.k ? ldg<int>(a.idx + (size_t)t * a.k + lane) : 0;
+  const float my_w = lane < a.k ? ldg<float>(a.w + (size_t)t * a.k + lane) : 0.f;
+  bool bad_j = lane < a.k && (my_idx < 0 || my_idx >= a.E);
+  for (int ii = 0; ii < a.k; ++ii) {
+    const int e = __builtin_amdgcn_readlane(my_idx, ii);
+    bad_j |= ii < lane && lane < a.k && e == my_idx;
   }
-  __syncthreads();
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  const bool bad = __ballot(bad_j) != 0;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;  // four columns per thread (H is a multiple of 32)
   if (c >= a.H) return;
-  float acc = 0.f;
-  for (int j = 0; j < a.k; ++j)
-    acc = fmaf(ldg<float>(a.w + t * a.k + j), ldg<float>(a.part + ((size_t)t * (a.k + 1) + j) * a.H + c), acc);
-  if (a.Is > 0) acc += ldg<float>(a.part + ((size_t)t * (a.k + 1) + a.k) * a.H + c);
-  stg<float>(a.y + (size_t)t * a.H + c, bad ? __builtin_nanf("") : acc);
+  const float *pt = a.part + (size_t)t * (a.k + 1) * a.H + c;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+  for (int j = 0; j < a.k; ++j) {
+    const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
+    const float4 p = ldg<float4>(pt + (size_t)j * a.H);
+    acc = make_float4(fmaf(wj, p.x, acc.x), fmaf(wj, p.y, acc.y), fmaf(wj, p.z, acc.z), fmaf(wj, p.w, acc.w));
+  }
+  if (a.Is > 0) {
+    const float4 p = ldg<float4>(pt + (size_t)a.k * a.H);
+    acc = make_float4(acc.x + p.x, acc.y + p.y, acc.z + p.z, acc.w + p.w);
+  }
+  const float nan = __builtin_nanf("");
+  stg<float4>(a.y + (size_t)t * a.H + c, bad ? make_float4(nan, nan, nan, nan) : acc);
 }
 
 int ceil_groups(int K) { return (K / kGroup + 63) / 64; }
@@ -903,7 +941,7 @@ hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st) {
   if (e != hipSuccess) return e;
   {
     ProfScope ps("combine", st);
-    MOE_LAUNCH(k_combine, dim3((a.H + 255) / 256, a.S), dim3(256), 0, st, a);
+    MOE_LAUNCH(k_combine, dim3((a.H + 1023) / 1024, a.S), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
