@@ -233,7 +233,7 @@ def bench_prefill(args) -> int:
     from int4_routed_expert_amd import moe as M
     w = gen.WORKLOADS["prefill"]
     c, S = w.cfg, w.tokens
-    cfg = M.make_cfg(c)
+    cfg = M.make_cfg(c, args.mfma_min_tokens)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     L = pack_layer(w, 0, dev, cfg)
@@ -276,7 +276,7 @@ def bench_prefill(args) -> int:
           "ms_per_step": el * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
           "dtype": "f32", "data": "synthetic",
           "config": {"workload": "glm52_moe_layer_prefill_S2048", "tokens_per_call": S, "x": "bf16",
-                     "bias": w.bias_recipe, "batches_rotated": nb},
+                     "bias": w.bias_recipe, "batches_rotated": nb, "mfma_min_tokens": args.mfma_min_tokens},
           "experts_used": used, "effective_gbps": bytes_call / el / 1e9,
           "pct_hbm_peak": 100.0 * bytes_call / el / 1e9 / HBM_PEAK_GBPS,
           "tflops": flop / el / 1e12, "kernels_us": kernels})
@@ -419,6 +419,8 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=4, help="resident layer instances rotated per step")
     ap.add_argument("--tokens", type=int, default=1024, help="distinct tokens rotated per step")
     ap.add_argument("--profile-steps", type=int, default=512)
+    ap.add_argument("--mfma-min-tokens", type=int, default=16,
+                    help="prefill: experts with at least this many tokens use the matrix cores")
     ap.add_argument("--call", default="layer", choices=["layer", "split"],
                     help="decode: one moe_layer call per step, or moe_route then moe_ffn")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

@@ -11,18 +11,17 @@
 // scale per row and group of 32) and down row tiles of eight output rows.
 //
 // Tiles: a workgroup (8 waves) owns up to 256 token rows of one expert's list
-// (kMT) and 256 output columns (kNT); each wave computes 32 rows x 256
-// columns of it, so an
-// activation row is read once per 256 columns and a dequantised weight feeds
-// 256 rows.  One
-// MFMA contracts exactly one quantisation group (K = 32), so each lane's B
-// fragment carries a single scale.  Per group the 256 x 32 B tile is
-// dequantised once by the whole workgroup (32 values per thread: exact
-// n*s - 8s in fp32, then round-to-nearest-even to bf16) into LDS and read by
-// all eight waves; A fragments (token rows, 8 consecutive K per lane) come
-// straight from global memory.  Two groups form a pipeline stage (64 MFMAs
-// per wave); weights are loaded two stages ahead and activations one stage
-// ahead; one barrier per stage (double-buffered B, 80 KB of LDS).
+// (kMT) and 256 output columns (kNT); each wave computes two 16-row blocks x
+// 256 columns of it, so an activation row is read once per 256 columns and a
+// dequantised weight feeds 256 rows.  One MFMA contracts exactly one
+// quantisation group (K = 32), so each lane's B fragment carries a single
+// scale.  A pipeline stage is two groups: the two lanes of a B column read its
+// 32 contiguous nibble bytes of the stage and each dequantises one group (32
+// values: exact n*s - 8s in fp32, then round-to-nearest-even to bf16) into LDS,
+// read by all eight waves; A fragments (token rows, 8 consecutive K per lane)
+// come straight from global memory.  Weights and activations come from a
+// register ring two stages deep; one barrier per stage (double-buffered B,
+// 80 KB of LDS).
 //
 // Gate/up: column c of an N tile is tile row c % 8 of gate/up tile c / 8, so
 // gate and up of a feature sit in adjacent lanes of the accumulator layout;
@@ -44,12 +43,12 @@ constexpr int kMT = kMfmaTileTokens;  // token rows per workgroup tile
 constexpr int kNT = 256;              // output columns per workgroup tile
 constexpr int kMB = 2;                // MFMA row blocks (16 rows) per wave: 32 rows
 constexpr int kNB = 16;               // MFMA column blocks (16 columns) per wave: all 256 columns
-constexpr int kKG = 1;                // quantisation groups (K = 32 each) per pipeline stage
+constexpr int kKG = 2;                // quantisation groups (K = 32 each) per pipeline stage
 constexpr int kBStride = 80;          // bytes per column of an LDS B group (64 + 16 padding: no bank conflicts)
 constexpr int kBGroup = kNT * kBStride;
 constexpr int kBStage = kKG * kBGroup;
 constexpr int kBParts = kThreads / kNT;  // threads that dequantise one column of a group (8 bytes each)
-static_assert(kMT == kWaves * 16 * kMB && kNT == 16 * kNB && kKG == 1 && kBParts == 2, "tile shape");
+static_assert(kMT == kWaves * 16 * kMB && kNT == 16 * kNB && kKG == 2 && kBParts == kKG, "tile shape");
 
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
@@ -161,39 +160,48 @@ template <bool ABF, int kDepth, int MBV>
 __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_colp, const uint8_t *const *s_sclp,
                                  uint8_t *s_b, const void *abase, const size_t *arow, int wn, int lane) {
   const int tid = threadIdx.x;
-  const int bc = tid % kNT, bp = tid / kNT;  // this thread's B column and half of the group's 16 nibble bytes
+  // this thread dequantises group kKG s + bp of B column bc: the two lanes of a
+  // column read its 32 contiguous nibble bytes of the stage together
+  const int bc = tid >> 1, bp = tid & 1;
   const uint8_t *colp = s_colp[bc];
   const uint8_t *sclp = s_sclp[bc];
   const int oct = lane >> 4;  // this lane's K octet in A and B fragments
+  const int ns = (ng + kKG - 1) / kKG;  // stages
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) C.acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   struct BRaw {
-    uint2 w;
+    uint4 w;
     uint16_t sc;
   };
-  auto load_b = [&](int g) {
-    g = min(g, ng - 1);
-    return BRaw{ldg<uint2>(colp + (size_t)g * 16 + bp * 8), ldg<uint16_t>(sclp + (size_t)g * 16)};
+  auto load_b = [&](int st) {
+    const int g = min(st * kKG + bp, ng - 1);
+    return BRaw{ldg<uint4>(colp + (size_t)g * 16), ldg<uint16_t>(sclp + (size_t)g * 16)};
   };
   auto store_b = [&](int buf, const BRaw &r) {
-    const float s = half_bits_to_float(r.sc);
-    uint8_t *d = s_b + buf * kBStage + bc * kBStride + bp * 32;
-    *(uint4 *)(d) = dequant8(r.w.x, s);
-    *(uint4 *)(d + 16) = dequant8(r.w.y, s);
+    const float sc = half_bits_to_float(r.sc);
+    uint8_t *d = s_b + buf * kBStage + bp * kBGroup + bc * kBStride;
+    *(uint4 *)(d) = dequant8(r.w.x, sc);
+    *(uint4 *)(d + 16) = dequant8(r.w.y, sc);
+    *(uint4 *)(d + 32) = dequant8(r.w.z, sc);
+    *(uint4 *)(d + 48) = dequant8(r.w.w, sc);
   };
-  auto load_a = [&](int g, ARaw<ABF> (&r)[kMB]) {
-    g = min(g, ng - 1);
+  auto load_a = [&](int st, ARaw<ABF> (&r)[kMB][kKG]) {
 #pragma unroll
-    for (int mb = 0; mb < MBV; ++mb) r[mb].load(abase, arow[mb] + (size_t)g * 32 + oct * 8);
+    for (int gi = 0; gi < kKG; ++gi) {
+      const int g = min(st * kKG + gi, ng - 1);
+#pragma unroll
+      for (int mb = 0; mb < MBV; ++mb) r[mb][gi].load(abase, arow[mb] + (size_t)g * 32 + oct * 8);
+    }
   };
-  // Ring of kDepth stages in registers: A of stage s is requested kDepth
-  // stages before its MFMAs, B of stage s kDepth stages before it is
+  // Ring of kDepth stages in registers: A of stage s is requested after the
+  // MFMAs of stage s - kDepth, B of stage s kDepth stages before it is
   // dequantised into LDS (one stage before its MFMAs).  Loads are clamped to
-  // the last group, so every one is unconditional; the stages past the last
-  // group (padding to a multiple of kDepth) multiply zeroed A fragments.
-  ARaw<ABF> aq[kDepth][kMB];
+  // the last group, so every one is unconditional; groups past the last one
+  // (an odd group count, padding to a multiple of kDepth stages) multiply
+  // zeroed A fragments.
+  ARaw<ABF> aq[kDepth][kMB][kKG];
   BRaw bq[kDepth];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) {
@@ -203,21 +211,24 @@ __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_col
   store_b(0, bq[0]);
   bq[0] = load_b(kDepth);
   __syncthreads();
-  const int ns = (ng + kDepth - 1) / kDepth * kDepth;
-  for (int st = 0; st < ns; st += kDepth) {
+  const int nsp = (ns + kDepth - 1) / kDepth * kDepth;
+  for (int st = 0; st < nsp; st += kDepth) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
       const int s = st + d;
-      const uint32_t live = s < ng ? ~0u : 0u;
       bf16x8 A[kMB][kKG];
 #pragma unroll
-      for (int mb = 0; mb < MBV; ++mb) {
-        const uint4 v = __builtin_bit_cast(uint4, aq[d][mb].get());
-        A[mb][0] = __builtin_bit_cast(bf16x8, make_uint4(v.x & live, v.y & live, v.z & live, v.w & live));
+      for (int gi = 0; gi < kKG; ++gi) {
+        const uint32_t live = s * kKG + gi < ng ? ~0u : 0u;
+#pragma unroll
+        for (int mb = 0; mb < MBV; ++mb) {
+          const uint4 v = __builtin_bit_cast(uint4, aq[d][mb][gi].get());
+          A[mb][gi] = __builtin_bit_cast(bf16x8, make_uint4(v.x & live, v.y & live, v.z & live, v.w & live));
+        }
       }
-      load_a(s + kDepth, aq[d]);
       const uint8_t *sb = s_b + (s & 1) * kBStage + (wn * 16 * kNB) * kBStride;
       if (MBV > 0) stage_mfma<MBV>(C, A, sb, lane, oct);  // rows past the tile's end repeat its last row; not stored
+      load_a(s + kDepth, aq[d]);  // after the MFMAs: the slot's registers are free again
       store_b((s + 1) & 1, bq[(d + 1) % kDepth]);
       bq[(d + 1) % kDepth] = load_b(s + 1 + kDepth);
       __syncthreads();
@@ -289,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void k_gu_mfma(FfnArgs a) {
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb) arow[mb] = (size_t)s_tok[row_of(wave, mb, lane & 15)] * a.H;
   GemmAcc C;
-  gemm_rows<true, 3>(C, mt.n, a.H / kGroup, s_colp, s_sclp, s_b, a.x_bf16 ? a.x : (const void *)a.xb, arow, wave,
+  gemm_rows<true, 2>(C, mt.n, a.H / kGroup, s_colp, s_sclp, s_b, a.x_bf16 ? a.x : (const void *)a.xb, arow, wave,
                      lane);
   // epilogue: even columns are gate, the next lane holds the matching up
 #pragma unroll
