@@ -78,7 +78,8 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_writ
     each scaled by what the same counter reads for a copy kernel that moves copy_mib MiB each way."""
     def one(path, counter, name_part):
         means = _pmc_means(path, counter)
-        hit = [v for k, v in means.items() if name_part in k]
+        # a kernel name is followed by its template arguments or its parameter list
+        hit = [v for k, v in means.items() if name_part + "<" in k or name_part + "(" in k]
         if len(hit) != 1:
             raise SystemExit(f"{path}: expected one kernel matching {name_part!r}, found {len(hit)}")
         return hit[0]
@@ -86,8 +87,8 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_writ
     f_scale = true_kib / one(copy_fetch_csv, "FETCH_SIZE", "k_copy")
     w_scale = true_kib / one(copy_write_csv, "WRITE_SIZE", "k_copy")
     for short in kernels:
-        fetch = one(fetch_csv, "FETCH_SIZE", f"k_{short}<")
-        write = one(write_csv, "WRITE_SIZE", f"k_{short}<")
+        fetch = one(fetch_csv, "FETCH_SIZE", f"k_{short}")
+        write = one(write_csv, "WRITE_SIZE", f"k_{short}")
         out = {"kernel": short, "source_sha256": kernel_source_hash(),
                "fetch_kib_per_dispatch_raw": fetch, "write_kib_per_dispatch_raw": write,
                "fetch_scale": f_scale, "write_scale": w_scale,
@@ -178,7 +179,13 @@ def bench_verify(args) -> int:
     log(f"verify: kernel-stamped averages (us, per call): {kernels}")
     # experts streamed per call: the batch union plus the shared expert
     idx_h = idx.cpu().numpy()
-    U = np.array([len(set(idx_h[o].ravel().tolist())) for o in range(min(nb, n_out))])
+    U, shared, on_shared = [], [], []
+    for o in range(min(nb, n_out)):
+        _, cnt = np.unique(idx_h[o].ravel(), return_counts=True)
+        U.append(len(cnt))
+        shared.append(float((cnt >= 2).mean()))           # union experts chosen by >= 2 tokens
+        on_shared.append(float(cnt[cnt >= 2].sum()) / idx_h[o].size)  # selections landing on them
+    U = np.array(U)
     per_call = (U.mean() + 1) * layers[0]["sb"]
     gbps = per_call / (ms_per_step * 1e-3) / 1e9
     emit({"metric": "MoE-layer tokens/s and effective int4 weight GB/s (% of HBM peak), GLM-5.2",
@@ -188,7 +195,7 @@ def bench_verify(args) -> int:
           "config": {"workload": "glm52_moe_layer_verify_S4", "tokens_per_call": S, "bias": w.bias_recipe,
                      "layers_rotated": args.layers, "batches_rotated": nb, "launch": "hip graphs of 16 calls"},
           "union_mean": float(U.mean()), "union_min": int(U.min()), "union_max": int(U.max()),
-          "shared_fraction": float(1.0 - U.mean() / (S * c.top_k)),
+          "shared_fraction": float(np.mean(shared)), "selections_on_shared": float(np.mean(on_shared)),
           "effective_gbps": gbps, "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS, "kernels_us": kernels})
     return 0
 

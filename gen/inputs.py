@@ -41,9 +41,9 @@ KIND_PERM = 6
 
 # Bias skews (calibrated against the realised routing statistics that
 # tests/test_workload_stats.py measures with the oracle).
-BETA_SHARED = 0.16   # verify batch: about 40% of the union experts chosen by >= 2 of 4 tokens
+BETA_SHARED = 0.28   # verify batch: about 40% of the union experts chosen by >= 2 of 4 tokens (union ~20)
 BETA_ZIPF = 0.16     # prefill: per-expert token counts Zipf-like, log-log slope about -1.1
-BETA_HOT = 0.30      # stack: a random 20% of experts receive about 80% of selections
+BETA_HOT = 0.20      # stack: a random 20% of experts receive about 80% of selections
 
 
 def build_lib(force: bool = False) -> str:

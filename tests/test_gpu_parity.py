@@ -230,6 +230,47 @@ def test_layer_call_matches_route_then_ffn(tiny, mid, glm, layer):
                 assert max_rel_err(y_l.cpu().numpy(), ref) <= TOL_FP32
 
 
+@pytest.mark.parametrize("layer", ["tiny", "glm"])
+def test_layer_call_graph_replays(tiny, glm, layer):
+    """The one-token moe_layer captured in a HIP graph: replays with new inputs
+    written between them, interleaved with eager calls on the same workspace,
+    each bitwise equal to the eager call on the same input."""
+    dl = {"tiny": tiny, "glm": glm}[layer]
+    c = dl.c
+    ws = dl.workspace(1)
+    xbuf = torch.empty((1, c.hidden), dtype=torch.float32, device="cuda")
+    idx = torch.empty((1, c.top_k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((1, c.top_k), dtype=torch.float32, device="cuda")
+    y = torch.empty((1, c.hidden), dtype=torch.float32, device="cuda")
+    view = dl.view()
+
+    def call():
+        M.moe_layer(dl.cfg, xbuf, M.MOE_F32, 1, dl.W, dl.bias, idx, wt, view, dl.shared, y, ws, ws.numel())
+
+    xs = [dev(gen.tokens(dl.w.with_(tokens=1), step=900 + i)) for i in range(4)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        xbuf.copy_(xs[0])
+        call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    for i in range(1, 4):
+        xbuf.copy_(xs[i])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (idx.clone(), wt.clone(), y.clone())
+        i_e, w_e, y_e = dl.layer(xs[i], M.MOE_F32, ws=ws)  # eager call on the same workspace
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], i_e) and torch.equal(got[1], w_e), (layer, i)
+        assert torch.equal(got[2], y_e), (layer, i)
+        assert not torch.isnan(y_e).any(), (layer, i)
+
+
 def test_layer_call_unresident_and_tied(tiny):
     """moe_layer for one token with an unresident selected expert (its row is
     NaN, as from moe_ffn) and with exactly tied router rows (lowest indices)."""
