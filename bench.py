@@ -164,6 +164,10 @@ def bench_verify(args) -> int:
     def step(j):
         L, b, o = layers[j % len(layers)], j % nb, j % n_out
         xb = x[b * S:(b + 1) * S]
+        if args.call == "layer":
+            M.moe_layer(cfg, xb, dt, S, L["W"], L["bias"], idx[o], wt[o], views[j % len(layers)], L["shared"], y[o],
+                        ws, ws.numel())
+            return
         M.moe_route(cfg, xb, dt, S, L["W"], L["bias"], idx[o], wt[o], ws, ws.numel())
         M.moe_ffn(cfg, xb, dt, S, idx[o], wt[o], views[j % len(layers)], L["shared"], y[o], ws, ws.numel())
 
@@ -193,7 +197,8 @@ def bench_verify(args) -> int:
           "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
           "dtype": "f32", "data": "synthetic",
           "config": {"workload": "glm52_moe_layer_verify_S4", "tokens_per_call": S, "bias": w.bias_recipe,
-                     "layers_rotated": args.layers, "batches_rotated": nb, "launch": "hip graphs of 16 calls"},
+                     "layers_rotated": args.layers, "batches_rotated": nb, "launch": "hip graphs of 16 calls",
+                     "call": "moe_layer" if args.call == "layer" else "moe_route + moe_ffn"},
           "union_mean": float(U.mean()), "union_min": int(U.min()), "union_max": int(U.max()),
           "shared_fraction": float(np.mean(shared)), "selections_on_shared": float(np.mean(on_shared)),
           "effective_gbps": gbps, "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS, "kernels_us": kernels})
@@ -429,7 +434,7 @@ def main() -> int:
     ap.add_argument("--mfma-min-tokens", type=int, default=16,
                     help="prefill: experts with at least this many tokens use the matrix cores")
     ap.add_argument("--call", default="layer", choices=["layer", "split"],
-                    help="decode: one moe_layer call per step, or moe_route then moe_ffn")
+                    help="decode and verify: one moe_layer call per step, or moe_route then moe_ffn")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--blobs", type=int, default=0, help="stack: distinct pinned weight blobs (0: 1024)")

@@ -106,15 +106,14 @@ int64_t moe_expert_bytes(const moe_cfg *cfg, int32_t inter);
 size_t moe_workspace_bytes(const moe_cfg *cfg, int32_t max_S);
 
 /* Initialise a workspace once, before its first use by moe_route or moe_ffn:
- * writes the 256-byte header at its start (two magic words and completion
- * counters) with a small kernel on `stream` (no memset node, so it may be
- * captured in a graph).  Every call leaves the counters back at zero, so the
- * header stays valid across calls and graph replays; re-initialise only when no
- * call using the workspace is in flight.  A workspace is used by one call at a
- * time (calls that share one must be stream-ordered).  moe_route with S <= 8
- * checks the magic words and, on a workspace that was not initialised, writes
- * idx = -1 and w = NaN for every token (moe_ffn then yields NaN rows).
- * ws_bytes must be at least 256.  Errors: MOE_ENULL, MOE_EWORKSPACE, MOE_EHIP. */
+ * writes the 256-byte header at its start (two magic words, then zeros) with a
+ * small kernel on `stream` (no memset node, so it may be captured in a graph).
+ * No call changes the header, so it stays valid across calls and graph
+ * replays.  A workspace is used by one call at a time (calls that share one
+ * must be stream-ordered).  moe_route with S <= 8 checks the magic words and,
+ * on a workspace that was not initialised, writes idx = -1 and w = NaN for
+ * every token (moe_ffn then yields NaN rows).  ws_bytes must be at least 256.
+ * Errors: MOE_ENULL, MOE_EWORKSPACE, MOE_EHIP. */
 int moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Pack one expert from the interchange format into the slot layout.
@@ -144,9 +143,10 @@ int moe_unpack_expert(const moe_cfg *cfg, int32_t inter, const void *src, uint8_
  * x: [S, H] fp32 or bf16 (x_dtype); W_gate: [E, H] fp32 row-major; bias: [E] fp32.
  * Out: idx [S, k] int32, w [S, k] fp32, both rank-ordered.  S = 0 is a no-op.
  * ws: device workspace of at least moe_workspace_bytes(cfg, S) bytes, initialised
- * by moe_workspace_init.  S <= 8 runs as one kernel: each expert's workgroup
- * computes its logits and the last one to finish (device-scope counter in the
- * workspace header) selects for all tokens. */
+ * by moe_workspace_init.  S <= 8: one workgroup per expert computes its logits
+ * and stores the tokens' scores and keys, then one workgroup per token selects
+ * (two kernels); larger S: an fp64 matrix-core logits GEMM, then one wave per
+ * token selects. */
 int moe_route(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, const float *W_gate,
               const float *bias, int32_t *idx, float *w, void *ws, size_t ws_bytes, void *stream);
 
@@ -157,21 +157,24 @@ int moe_route(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, con
  * tokens that chose it.  x: [S, H] fp32 or bf16; idx/w: [S, k] as from moe_route;
  * experts: routed slots (host struct holding device pointers); shared: the packed
  * shared expert (moe_expert_bytes(cfg, shared_inter) bytes), ignored when
- * shared_inter = 0.  Out: y [S, H] fp32.  Arithmetic: S <= 4 uses fp32
- * dequantise-and-multiply-accumulate throughout; larger batches use the same for
- * experts with few tokens and bf16 MFMA (fp32 accumulation) for the others. */
+ * shared_inter = 0.  Out: y [S, H] fp32.  Arithmetic: each 32-element group's
+ * dot product of int4 weights with the activations in block fixed point
+ * (2^-22 of the group's largest |value|) is an exact integer, scaled once by
+ * the group's scale and summed in fp32; larger batches use the same for experts
+ * with fewer than mfma_min_tokens tokens and bf16 MFMA (fp32 accumulation) for
+ * the others. */
 int moe_ffn(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, const int32_t *idx, const float *w,
             const moe_slot_view *experts, const void *shared, float *y, void *ws, size_t ws_bytes, void *stream);
 
 /* One MoE layer forward: moe_route followed by moe_ffn on the same stream, with
  * the same arguments and bit-identical results (idx, w and y); [PORT] N1 (the
  * layer is the router, then the routed experts, then their route-order
- * combine with the shared expert).  For S = 1 it runs as three kernels instead
- * of four: the router kernel only stores each expert's score and key (no
- * completion count, no use of the workspace header), and the gate/up kernel
- * selects the experts itself in every workgroup from those values (workgroup
- * 0 also writes idx and w), so the selection costs no grid-wide hand-off.
- * Other S: moe_route then moe_ffn.  Errors: those of moe_route and moe_ffn. */
+ * combine with the shared expert).  For S = 1 the router kernel only stores
+ * each expert's score and key and the gate/up kernel selects the experts itself
+ * in every workgroup from those values (workgroup 0 also writes idx and w), so
+ * the selection needs no kernel of its own (and the workspace header is not
+ * read).  Other S: moe_route then moe_ffn.  Errors: those of moe_route and
+ * moe_ffn. */
 int moe_layer(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, const float *W_gate, const float *bias,
               int32_t *idx, float *w, const moe_slot_view *experts, const void *shared, float *y, void *ws,
               size_t ws_bytes, void *stream);

@@ -98,8 +98,10 @@ WsLayout ws_layout(const moe_cfg &c, int32_t S) {
   L.eptr = off; off += align256((size_t)kMaxK * sizeof(uint64_t));
   L.max_items = 0;
   L.max_mtiles = 0;
-  if (S > kSmallS) {
+  if (S >= 2) {  // per-(token, rank) expert outputs, added in route order by the combine
     L.part = off; off += align256((size_t)S * k1 * c.hidden * sizeof(float));
+  }
+  if (S > kSmallS) {
     L.lists = off; off += align256((size_t)c.n_experts * S * sizeof(int32_t));
     L.counts = off; off += align256((size_t)(c.n_experts + 1) * sizeof(int32_t));
     L.max_items = (int32_t)(((size_t)S * c.top_k + 3) / 4 + c.n_experts + (S + 3) / 4);
@@ -331,13 +333,13 @@ static int ffn_args(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S,
   a.hf = (float *)(b + L.hf);
   a.eptr = (uint64_t *)(b + L.eptr);
   a.n_cu = device_cus();
+  if (S >= 2) a.part = (float *)(b + L.part);
   if (S <= kSmallS) {
     // one-token down kernel: about one row block per compute unit, at most 8 tiles each
     const int nt = c->hidden / kDnRows;
     a.tb = std::min(8, std::max(1, (nt + a.n_cu - 1) / a.n_cu));
     a.n_blk = (nt + a.tb - 1) / a.tb;
   } else {
-    a.part = (float *)(b + L.part);
     a.lists = (int32_t *)(b + L.lists);
     a.counts = (int32_t *)(b + L.counts);
     a.items = (int32_t *)(b + L.items);
@@ -388,7 +390,7 @@ int moe_layer(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const
   if (v) return v;
   const hipStream_t st = (hipStream_t)stream;
   hipError_t e;
-  if (S == 1) {
+  if (S == 1) {  // the router kernel stores scores and keys; the gate/up kernel selects
     e = launch_route_scores(r, st);
     if (e == hipSuccess) {
       f.sel = 1;

@@ -21,10 +21,9 @@ constexpr int kMaxE = 1024;      // n_experts limit
 constexpr int kMaxG = 64;        // n_group limit
 
 // Workspace header (first kWsSyncBytes bytes): two magic words written by
-// moe_workspace_init, then completion counters that every call leaves at zero.
+// moe_workspace_init (the router refuses a workspace without them), then zeros.
 constexpr int kWsSyncBytes = 256;
 constexpr uint32_t kWsMagic0 = 0x6D6F6534u, kWsMagic1 = 0x77733031u;
-constexpr int kSyncRouteCtr = 2;  // word index: expert workgroups done (one-launch router)
 
 // ---- slot layout of one packed expert (inter = I, hidden = H) -------------
 // gate/up: I/4 tiles.  Tile t holds 8 rows, in order (g 4t, u 4t, g 4t+1, u 4t+1,

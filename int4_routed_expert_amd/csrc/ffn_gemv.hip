@@ -315,17 +315,17 @@ struct SmallPlan {
   int pair[kSmallS * kMaxK + 1][kSmallS];
 };
 
-// Needs blockDim.x > S * k.
-__device__ void build_small_plan(const FfnArgs &a, SmallPlan &p) {
+// Needs blockDim.x > S * k.  idx: the batch's [S, k] rows (global or LDS).
+__device__ void build_small_plan(const FfnArgs &a, SmallPlan &p, const int32_t *idx) {
   const int n = a.S * a.k, tid = threadIdx.x;
   if (tid == 0) p.U = 0;
   if (tid < a.S) p.tokbad[tid] = 0;
   __syncthreads();
   if (tid < n) {
-    const int e = ldg<int>(a.idx + tid);
+    const int e = idx[tid];
     const int t = tid / a.k;
     bool ok = e >= 0 && e < a.E;
-    for (int j = t * a.k; j < tid && ok; ++j) ok = ldg<int>(a.idx + j) != e;
+    for (int j = t * a.k; j < tid && ok; ++j) ok = idx[j] != e;
     p.sidx[tid] = ok ? e : -1;
     if (!ok) atomicOr(&p.tokbad[t], 1);
   }
@@ -407,17 +407,27 @@ __device__ inline void poison_h(const FfnArgs &a, int ntok, const int *pairs, in
 
 constexpr int kGuSmallWaves = 8;  // waves per small-batch gate/up workgroup (one workgroup per CU)
 
-// Two to four tokens, gate/up: persistent streaming over the batch union's
-// features like the one-token kernel.  Each wave owns an equal share of the
-// shared expert's features (first: no routing needed) and of the union's routed
-// features (unique experts ascending, I features each); a 3-slot ring keeps
-// two features in flight while one is applied to every token that chose its
-// expert.  The workgroup converts the S tokens' activations to limbs in LDS
-// once; a (feature, token) result parks in a lane and is stored 64 at a time.
+// Two to four tokens, gate/up: the batch's (feature, token) pairs stream
+// through the waves token-major, so that a wave's activation limbs stay in
+// registers as in the one-token kernel (reloading them from LDS for every
+// (feature, token) pair would put two dependent LDS round trips in front of
+// every pair's dot products).  Pair order: the shared expert's features for
+// token 0, 1, ... (S * Is pairs), then each unique expert u (ascending) in
+// blocks of 32 features, each block once for every token that chose u
+// (ascending).  Each wave takes an equal share of the shared pairs (they need
+// no routing, so they stream while the union is built) and of the others; the
+// limbs are reloaded from LDS only when the token changes (at most every 32
+// pairs).  An expert chosen by several tokens is read once per token, by the
+// same or the next wave right after (four tokens' limbs would not fit in the
+// registers next to the prefetch ring).  The per-pair arithmetic is the
+// one-token kernel's, so a token's h does not depend on the other tokens of
+// its batch.  Results park in lanes (value and h row) and are stored 64 at a
+// time.
 template <int NG>
 __global__ __launch_bounds__(kGuSmallWaves * 64) void k_gateup_small(FfnArgs a) {
   __shared__ SmallPlan plan;
   __shared__ const uint8_t *s_ptr[kSmallS * kMaxK];
+  __shared__ int seg_start[kSmallS * kMaxK + 1];  // first union pair of unique expert u; [U]: all
   // [S][H/32] groups of 24 limb words at a stride of kXs words (conflict-free
   // 16-byte reads across lanes), then [S][H/32] factors; H <= 8192
   constexpr int kXs = 28;
@@ -430,33 +440,29 @@ __global__ __launch_bounds__(kGuSmallWaves * 64) void k_gateup_small(FfnArgs a) 
   const int i0 = threadIdx.x, i1 = threadIdx.x + blockDim.x;
   load32(a.x, a.x_bf16, (size_t)min(i0, nx - 1) * kGroup, v0);
   load32(a.x, a.x_bf16, (size_t)min(i1, nx - 1) * kGroup, v1);
-  build_small_plan(a, plan);
-  const int U = plan.U;
   const int W = gridDim.x * (blockDim.x >> 6), wid = blockIdx.x * (blockDim.x >> 6) + wave;
-  const long Is = a.Is, Fr = (long)U * a.I;
-  const int s0 = (int)(wid * Is / W), s1 = (int)((wid + 1) * Is / W);
-  const int r0 = (int)(wid * Fr / W), r1 = (int)((wid + 1) * Fr / W);
-  const int ns = s1 - s0, n = ns + (r1 - r0);
+  const long Ps = (long)a.S * a.Is;
+  const int sp0 = (int)(wid * Ps / W), ns = (int)((wid + 1) * Ps / W) - sp0;
   GuFeat<NG> b0, b1, b2;
-  // item i -> unique slot (U: shared) and feature
-  auto item = [&](int i, int &u, int &f) {
-    i = min(i, n - 1);
-    if (i < ns) {
-      u = U;
-      f = s0 + i;
-    } else {
-      const int r = r0 + i - ns;
-      u = r / a.I;
-      f = r - u * a.I;
+  int row0 = 0, row1 = 0, row2 = 0, tok0 = 0, tok1 = 0, tok2 = 0;  // slot tags: h row and token
+  auto shared_item = [&](GuFeat<NG> &b, int i, int &row, int &tok) {
+    const int p = sp0 + i, t = p / a.Is, f = p - t * a.Is;
+    gu_row_load(b, a, a.shared, f, lane);
+    tok = t;
+    row = (t * (a.k + 1) + a.k) * Imax + f;
+  };
+  if (ns >= 1) shared_item(b0, 0, row0, tok0);
+  if (ns >= 2) shared_item(b1, 1, row1, tok1);
+  build_small_plan(a, plan, a.idx);
+  const int U = plan.U;
+  if (threadIdx.x == 0) {
+    int start = 0;
+    for (int u = 0; u < U; ++u) {
+      seg_start[u] = start;
+      start += plan.ntok[u] * a.I;
     }
-  };
-  auto load = [&](GuFeat<NG> &bb, int i) {
-    int u, f;
-    item(i, u, f);
-    gu_row_load(bb, a, u == U ? a.shared : uniform_ptr(s_ptr[u]), f, lane);
-  };
-  const bool early = n > 0 && ns >= 1;  // a shared first feature needs no expert pointer
-  if (early) gu_row_load(b0, a, a.shared, s0, lane);
+    seg_start[U] = start;
+  }
   if ((int)threadIdx.x < U) s_ptr[threadIdx.x] = expert_ptr(a, plan.uniq[threadIdx.x]);
   if (i0 < nx) {
     Limbs L;
@@ -476,113 +482,168 @@ __global__ __launch_bounds__(kGuSmallWaves * 64) void k_gateup_small(FfnArgs a) 
     store_limbs(xlds + (size_t)i * kXs, xf_lds + i, L);
   }
   __syncthreads();
+  const long Pu = seg_start[U];
+  const int up0 = (int)(wid * Pu / W), n = ns + (int)((wid + 1) * Pu / W) - up0;
   if (n <= 0) return;
-  if (!early) load(b0, 0);
-  load(b1, 1);
+  int lc = 0;  // unique expert of the last union pair requested (a wave's pairs increase)
+  // item i of the wave (clamped to its last one, so that loads are unconditional)
+  auto load_item = [&](GuFeat<NG> &b, int i, int &row, int &tok) {
+    i = min(i, n - 1);
+    if (i < ns) {
+      shared_item(b, i, row, tok);
+      return;
+    }
+    const int p = up0 + (i - ns);
+    while (p >= seg_start[lc + 1]) ++lc;
+    const int u = lc, nt = plan.ntok[u], q = p - seg_start[u];
+    const int blk = q / (kGroup * nt), r = q - blk * kGroup * nt, tt = r / kGroup;
+    const int f = blk * kGroup + (r - tt * kGroup);
+    gu_row_load(b, a, uniform_ptr(s_ptr[u]), f, lane);
+    tok = plan.tok[u][tt];
+    row = plan.pair[u][tt] * Imax + f;
+  };
+  if (ns < 1) load_item(b0, 0, row0, tok0);
+  if (ns < 2) load_item(b1, 1, row1, tok1);
+  Limbs xv[NG];
+  int xt = -1;  // token whose limbs are in xv
   float hout = 0.f;
-  int hrow_p = 0, c = 0;
-  // applies a loaded feature to every token of its expert
-  auto apply = [&](const GuFeat<NG> &bb, int i) {
-    int u, f;
-    item(i, u, f);
-    const int nt = plan.ntok[u];
-    for (int tt = 0; tt < nt; ++tt) {
-      const int t = plan.tok[u][tt];
-      Limbs xv[NG];
+  int prow = 0, c = 0;
+  auto finish = [&](const GuFeat<NG> &b, int row, int tok) {
+    if (tok != xt) {
+      xt = tok;
 #pragma unroll
       for (int j = 0; j < NG; ++j) {  // lanes past the last group repeat it with a zero factor
         const int g = min(lane + 64 * j, ng - 1);
-        load_limbs_lds(xlds + ((size_t)t * ng + g) * kXs, xf_lds + (size_t)t * ng + g, xv[j]);
+        load_limbs_lds(xlds + ((size_t)tok * ng + g) * kXs, xf_lds + (size_t)tok * ng + g, xv[j]);
         if (lane + 64 * j >= ng) xv[j].f = 0.f;
       }
-      hout = gu_feat_compute(bb, xv, c, hout);
-      if (lane == c) hrow_p = plan.pair[u][tt] * Imax + f;
-      if (++c == 64) {
-        stg<float>(a.h + hrow_p, hout);
-        c = 0;
-      }
+    }
+    hout = gu_feat_compute(b, xv, c, hout);
+    if (lane == c) prow = row;
+    if (++c == 64) {
+      stg<float>(a.h + prow, hout);
+      c = 0;
     }
   };
   for (int i = 0; i < n; i += 3) {
-    load(b2, i + 2);
-    apply(b0, i);
-    load(b0, i + 3);
-    if (i + 1 < n) apply(b1, i + 1);
-    load(b1, i + 4);
-    if (i + 2 < n) apply(b2, i + 2);
+    load_item(b2, i + 2, row2, tok2);
+    finish(b0, row0, tok0);
+    load_item(b0, i + 3, row0, tok0);
+    if (i + 1 < n) finish(b1, row1, tok1);
+    load_item(b1, i + 4, row1, tok1);
+    if (i + 2 < n) finish(b2, row2, tok2);
   }
-  if (lane < c) stg<float>(a.h + hrow_p, hout);
+  if (lane < c) stg<float>(a.h + prow, hout);
 }
 
-// One workgroup per 8-row tile of y; its waves take the union's experts and leave
-// per-(token, rank) dot products in LDS; the workgroup sums them in route order.
+// Two to four tokens, down projection: the (expert, token, tile) units stream
+// through the waves with the pair's h in limb form held in registers (reloaded
+// only when the (expert, token) pair changes), and each unit's 8 row dots are
+// stored as per-(token, rank) partial rows; k_combine then adds them in route
+// order with the shared expert.  Unit order: for each unique expert u
+// (ascending, then the shared expert with every token) blocks of B tiles,
+// each block once for every token of u, so a tile that several tokens need is
+// requested again by the same or the next wave right after.  Each wave takes
+// an equal share of the units, with two tiles in flight while one is computed
+// (measured faster than holding every token's limbs and reading each tile
+// once, which leaves room for fewer tiles in flight).  The per-unit arithmetic
+// is the one-token kernel's.
+constexpr int kDnSmallWaves = 8;
 template <int NGD>
-__global__ __launch_bounds__(512, 4) void k_down_small(FfnArgs a) {
+__global__ __launch_bounds__(kDnSmallWaves * 64) void k_down_small(FfnArgs a) {
   __shared__ SmallPlan plan;
-  __shared__ float part[kSmallS * (kMaxK + 1)][kDnRows];
-  build_small_plan(a, plan);
-  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6, lane = threadIdx.x & 63;
-  const int Imax = max(a.I, a.Is), ngm = Imax / kGroup;
-  const int rt = blockIdx.x;
-  const int nu = plan.U + (a.Is > 0 ? 1 : 0);
-  // the wave's experts u = wave, wave + nw, ...: the next one's tile is
-  // requested before the current one is computed (loads clamped to the last)
-  auto expert_of = [&](int u, int &inter) -> const uint8_t * {
-    u = min(u, nu - 1);
-    const bool sh = u == plan.U;
-    inter = sh ? a.Is : a.I;
-    return sh ? a.shared : expert_ptr(a, plan.uniq[u]);
+  __shared__ const uint8_t *s_ptr[kSmallS * kMaxK + 1];
+  __shared__ int seg_start[kSmallS * kMaxK + 2];  // first unit of unique expert u (U: shared); [U + 1]: all
+  build_small_plan(a, plan, a.idx);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int U = plan.U, Imax = max(a.I, a.Is), nt = a.H / kDnRows;
+  const int B = (nt % 16 == 0) ? 16 : 4;  // tiles per block (nt is a multiple of 4)
+  if (threadIdx.x == 0) {
+    int start = 0;
+    for (int u = 0; u <= U; ++u) {
+      seg_start[u] = start;
+      start += (u == U ? (a.Is > 0 ? a.S : 0) : plan.ntok[u]) * nt;
+    }
+    seg_start[U + 1] = start;
+  }
+  if ((int)threadIdx.x < U) s_ptr[threadIdx.x] = expert_ptr(a, plan.uniq[threadIdx.x]);
+  if ((int)threadIdx.x == U) s_ptr[U] = a.shared;
+  __syncthreads();
+  const int W = gridDim.x * (blockDim.x >> 6), wid = blockIdx.x * (blockDim.x >> 6) + wave;
+  const long P = seg_start[U + 1];
+  const int p0 = (int)(wid * P / W), n = (int)((wid + 1) * P / W) - p0;
+  if (n <= 0) return;
+  struct Unit {
+    int pair, t, inter;
+    bool valid;
+    const uint8_t *dn;
   };
-  auto tile_src = [&](const uint8_t *ex, int inter) {
-    return uniform_ptr((ex ? ex : a.base) + down_offset(a.H, ex ? inter : a.I));
+  int lc = 0;  // unique expert of the last unit requested (a wave's units increase)
+  auto unit_of = [&](int i) {
+    const int p = p0 + min(i, n - 1);
+    while (p >= seg_start[lc + 1]) ++lc;
+    const int u = lc, ntu = u == U ? a.S : plan.ntok[u], q = p - seg_start[u];
+    const int blk = q / (B * ntu), r = q - blk * B * ntu, tt = r / B;
+    Unit un;
+    un.t = blk * B + (r - tt * B);
+    un.pair = u == U ? tt * (a.k + 1) + a.k : plan.pair[u][tt];
+    const uint8_t *ex = uniform_ptr(s_ptr[u]);
+    un.valid = ex != nullptr;
+    un.inter = (u == U && un.valid) ? a.Is : a.I;
+    un.dn = uniform_ptr((un.valid ? ex : a.base) + down_offset(a.H, un.inter));
+    return un;
   };
   DnTile<NGD> q0, q1;
-  int inter_c = a.I;
-  const uint8_t *ex_c = expert_of(wave, inter_c);
-  if (wave < nu) dn_tile_load(q0, tile_src(ex_c, inter_c), ex_c ? inter_c : a.I, rt, rt + 1, lane);
-  // unit u from `cur` (already requested); requests unit u + nw into `nxt`
-  auto step = [&](const DnTile<NGD> &cur, DnTile<NGD> &nxt, int u) {
-    int inter_n = a.I;
-    const uint8_t *ex_n = expert_of(u + nw, inter_n);
-    dn_tile_load(nxt, tile_src(ex_n, inter_n), ex_n ? inter_n : a.I, rt, rt + 1, lane);
-    if (!ex_c) {
-      if (lane < kDnRows)
-        for (int tt = 0; tt < plan.ntok[u]; ++tt) part[plan.pair[u][tt]][lane] = __builtin_nanf("");
-    } else {
-      const int ng = inter_c / kGroup;
-      for (int tt = 0; tt < plan.ntok[u]; ++tt) {
-        const int pr = plan.pair[u][tt];
-        Limbs hv[NGD];
+  Unit u0 = unit_of(0), u1 = unit_of(1);
+  dn_tile_load(q0, u0.dn, u0.inter, u0.t, u0.t + 1, lane);
+  dn_tile_load(q1, u1.dn, u1.inter, u1.t, u1.t + 1, lane);
+  Limbs hv[NGD];
+  int hp = -1;  // pair whose h limbs are in hv
+  auto finish = [&](const DnTile<NGD> &b, const Unit &uu) {
+    const int ngi = uu.inter / kGroup;
+    if (uu.pair != hp) {
+      hp = uu.pair;
 #pragma unroll
-        for (int g2 = 0; g2 < NGD; ++g2) {
-          const int g = min(lane + 64 * g2, ng - 1);
-          load_limbs_global(a.hl + ((size_t)pr * ngm + g) * 24, a.hf + (size_t)pr * ngm + g, hv[g2]);
-          if (lane + 64 * g2 >= ng) hv[g2].f = 0.f;
-        }
-        float acc[kDnRows];
-        dn_tile_dots(cur, hv, acc);
-        if (lane == 63)
-#pragma unroll
-          for (int i = 0; i < kDnRows; ++i) part[pr][i] = acc[i];
+      for (int g2 = 0; g2 < NGD; ++g2) {  // lanes past the last group repeat it with a zero factor
+        const int g = min(lane + 64 * g2, ngi - 1);
+        float v[32];
+        load32(a.h, 0, (size_t)uu.pair * Imax + (size_t)g * kGroup, v);
+        to_limbs(v, hv[g2]);
+        if (lane + 64 * g2 >= ngi) hv[g2].f = 0.f;
       }
     }
-    ex_c = ex_n;
-    inter_c = inter_n;
+    float acc[kDnRows];
+    dn_tile_dots(b, hv, acc);
+    if (lane == 63) {
+      const float nan = __builtin_nanf("");
+      float4 *d = (float4 *)(a.part + (size_t)uu.pair * a.H + (size_t)uu.t * kDnRows);
+      stg<float4>(d, uu.valid ? make_float4(acc[0], acc[1], acc[2], acc[3]) : make_float4(nan, nan, nan, nan));
+      stg<float4>(d + 1, uu.valid ? make_float4(acc[4], acc[5], acc[6], acc[7]) : make_float4(nan, nan, nan, nan));
+    }
   };
-  for (int u = wave; u < nu; u += 2 * nw) {
-    step(q0, q1, u);
-    if (u + nw < nu) step(q1, q0, u + nw);
-  }
-  __syncthreads();
-  const int tid = threadIdx.x;
-  if (tid < a.S * kDnRows) {
-    const int t = tid / kDnRows, i = tid % kDnRows;
-    float acc = 0.f;
-    const bool bad = plan.tokbad[t] != 0;
-    if (!bad)
-      for (int j = 0; j < a.k; ++j) acc = fmaf(ldg<float>(a.w + t * a.k + j), part[t * (a.k + 1) + j][i], acc);
-    if (a.Is > 0) acc += part[t * (a.k + 1) + a.k][i];
-    stg<float>(a.y + (size_t)t * a.H + rt * kDnRows + i, bad ? __builtin_nanf("") : acc);
+  if constexpr (NGD == 1) {  // three tiles: two in flight while one is computed
+    DnTile<NGD> q2;
+    Unit u2;
+    for (int i = 0; i < n; i += 3) {
+      u2 = unit_of(i + 2);
+      dn_tile_load(q2, u2.dn, u2.inter, u2.t, u2.t + 1, lane);
+      finish(q0, u0);
+      u0 = unit_of(i + 3);
+      dn_tile_load(q0, u0.dn, u0.inter, u0.t, u0.t + 1, lane);
+      if (i + 1 < n) finish(q1, u1);
+      u1 = unit_of(i + 4);
+      dn_tile_load(q1, u1.dn, u1.inter, u1.t, u1.t + 1, lane);
+      if (i + 2 < n) finish(q2, u2);
+    }
+  } else {  // wider tiles (inter > 2048): two, to stay within the register file
+    for (int i = 0; i < n; i += 2) {
+      finish(q0, u0);
+      u0 = unit_of(i + 2);
+      dn_tile_load(q0, u0.dn, u0.inter, u0.t, u0.t + 1, lane);
+      if (i + 1 < n) finish(q1, u1);
+      u1 = unit_of(i + 3);
+      dn_tile_load(q1, u1.dn, u1.inter, u1.t, u1.t + 1, lane);
+    }
   }
 }
 
@@ -880,7 +941,6 @@ hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st) {
     }
     return hipGetLastError();
   }
-  const int Umax = std::min(a.S * a.k, a.E);
   {
     ProfScope ps("gateup_small", st);
     const dim3 g((unsigned)a.n_cu), blk(kGuSmallWaves * 64);
@@ -889,14 +949,14 @@ hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   {
-    ProfScope ps("h_limbs", st);
-    e = launch_to_limbs(a.h, 0, a.S * (a.k + 1), Imax, Imax, a.hl, a.hf, st);
+    ProfScope ps("down_small", st);
+    const dim3 g2((unsigned)a.n_cu), b2(kDnSmallWaves * 64);
+    MOE_DISPATCH_NG(ceil_groups(Imax), k_down_small, g2, b2, 0, st);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  ProfScope ps("down_small", st);
-  const int nw = std::min(Umax + 1, 8);
-  const dim3 g2(a.H / kDnRows), b2(64 * nw);
-  MOE_DISPATCH_NG(ceil_groups(Imax), k_down_small, g2, b2, 0, st);
+  ProfScope ps("combine", st);
+  MOE_LAUNCH(k_combine, dim3((a.H + 1023) / 1024, a.S), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

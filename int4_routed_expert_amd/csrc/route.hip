@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void k_route_select(RouteArgs a) {
   const double *lt = a.logits + (size_t)t * a.E;
   for (int e = lane; e < a.E; e += 64) score(lt[e], a.bias[e], ssg[e], skey[e]);
   wave_lds_sync();
-  select_wave_dispatch(a, t, skey, ssg, lane);
+  select_wave_dispatch(sel_cfg(a), skey, ssg, lane, a.idx + (size_t)t * a.k, a.w + (size_t)t * a.k);
 }
 
 // Many tokens: the logits GEMM in fp64 on the matrix cores
@@ -99,37 +99,6 @@ __global__ __launch_bounds__(256) void k_route_logits_tiled(RouteArgs a) {
   }
 }
 
-// Few tokens (S <= kFewTokens), one launch for the whole router: one workgroup
-// per expert computes that expert's logits (its 4 waves split H; every load of
-// a lane is issued before the FMAs; partial sums meet in LDS in a fixed order)
-// and their scores and keys, publishes them and counts itself done on a
-// device-scope counter in the workspace header; the workgroup that completes
-// the count selects for all tokens (whole workgroup per token) and puts the
-// counter back to zero.  A workspace without the header's magic words gets
-// idx = -1 and w = NaN.
-__global__ __launch_bounds__(256) void k_route_fused(RouteArgs a) {
-  __shared__ SelLds sel;
-  __shared__ double part[4][kFewTokens];
-  __shared__ int s_last;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int e = blockIdx.x;
-  float4 wv[kFewChunks];
-  few_logits_load(a, e, wave, lane, wv);
-  const uint32_t m0 = a.sync[0], m1 = a.sync[1];
-  if (m0 != kWsMagic0 || m1 != kWsMagic1) {
-    if (e == 0)
-      for (int i = threadIdx.x; i < a.S * a.k; i += blockDim.x) {
-        a.idx[i] = -1;
-        a.w[i] = __builtin_nanf("");
-      }
-    return;
-  }
-  few_logits_finish(a, e, wave, lane, wv, part);
-  if (!few_logits_publish(a, (uint32_t)a.E, &s_last)) return;
-  few_select(a, sel);
-  if (threadIdx.x == 0) __hip_atomic_store(a.sync + kSyncRouteCtr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Few tokens, logits and selection inputs only (the selection runs in the
 // consumer's first kernel): one workgroup per expert stores the tokens' scores
 // and keys.  No completion count, so no workspace header is involved.
@@ -140,6 +109,26 @@ __global__ __launch_bounds__(256) void k_route_scores(RouteArgs a) {
   float4 wv[kFewChunks];
   few_logits_load(a, e, wave, lane, wv);
   few_logits_finish(a, e, wave, lane, wv, part);
+}
+
+// Few tokens, selection: one workgroup per token from the scores and keys that
+// k_route_scores stored (the kernel boundary is the hand-off).  A workspace
+// without the header's magic words gets idx = -1 and w = NaN.
+template <int EPT>
+__global__ __launch_bounds__(256) void k_route_select_few(RouteArgs a) {
+  __shared__ SelLds sel;
+  const int t = blockIdx.x;
+  if (a.sync[0] != kWsMagic0 || a.sync[1] != kWsMagic1) {
+    if ((int)threadIdx.x < a.k) {
+      a.idx[(size_t)t * a.k + threadIdx.x] = -1;
+      a.w[(size_t)t * a.k + threadIdx.x] = __builtin_nanf("");
+    }
+    return;
+  }
+  const SelCfg c = sel_cfg(a);
+  SelIn<EPT> in;
+  sel_load<EPT, false>(c, a.keys + (size_t)t * a.E, a.scores + (size_t)t * a.E, nullptr, in);
+  select_block<EPT, false>(c, t, in, sel, a.idx, a.w);
 }
 
 __global__ void k_ws_init(uint32_t *sync) {
@@ -153,8 +142,18 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
   if (a.S == 0) return hipSuccess;
   const size_t sel_lds = (size_t)4 * a.E * (sizeof(double) + sizeof(float)) + (size_t)a.E * sizeof(float);
   if (a.S <= kFewTokens) {
-    ProfScope ps("route_fused", st);
-    MOE_LAUNCH(k_route_fused, dim3(a.E), dim3(256), 0, st, a);
+    {
+      ProfScope ps("route_scores", st);
+      MOE_LAUNCH(k_route_scores, dim3(a.E), dim3(256), 0, st, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ProfScope ps("route_select", st);
+    if (a.E <= 256) {
+      MOE_LAUNCH(k_route_select_few<1>, dim3(a.S), dim3(256), 0, st, a);
+    } else {
+      MOE_LAUNCH(k_route_select_few<4>, dim3(a.S), dim3(256), 0, st, a);
+    }
     return hipGetLastError();
   }
   {

@@ -62,12 +62,19 @@ __device__ inline void score(double l, float bias, double &s, float &key) {
   key = __double2float_rn(s + (double)bias);
 }
 
-// One wave selects for token t from its keys and scores already in LDS (skey,
-// ssg: E entries each): group scores, the Gk kept groups, then k rounds of
-// wave arg-max over the kept experts' keys.  Lane l holds experts l, l+64, ...
-// (NPL experts per lane, E <= 64*NPL).
+struct SelCfg {
+  int E, G, Gk, k, norm;
+  float rsf;
+};
+
+// One wave selects for one token from its keys and scores already in LDS
+// (skey, ssg: E entries each): group scores, the Gk kept groups, then k rounds
+// of wave arg-max over the kept experts' keys; lanes r < k store rank r's
+// expert and weight into idx_row[r] and w_row[r] (global or LDS).  Lane l holds
+// experts l, l+64, ... (NPL experts per lane, E <= 64*NPL).
 template <int NPL>
-__device__ void select_wave(const RouteArgs &a, int t, const float *skey, const double *ssg, int lane) {
+__device__ void select_wave(const SelCfg &a, const float *skey, const double *ssg, int lane, int32_t *idx_row,
+                            float *w_row) {
   const int E = a.E, G = a.G, per = a.E / a.G;
   // group score: fp32 sum of the group's two largest keys (one lane per group)
   float gs = -INFINITY;
@@ -139,18 +146,19 @@ __device__ void select_wave(const RouteArgs &a, int t, const float *skey, const 
   }
   if (lane < a.k) {
     const double wv = a.norm ? my_s / denom * (double)a.rsf : my_s * (double)a.rsf;
-    a.idx[(size_t)t * a.k + lane] = my_idx;
-    a.w[(size_t)t * a.k + lane] = my_idx >= 0 ? (float)wv : __builtin_nanf("");
+    idx_row[lane] = my_idx;
+    w_row[lane] = my_idx >= 0 ? (float)wv : __builtin_nanf("");
   }
 }
 
-__device__ void select_wave_dispatch(const RouteArgs &a, int t, const float *skey, const double *ssg, int lane) {
+__device__ inline void select_wave_dispatch(const SelCfg &a, const float *skey, const double *ssg, int lane,
+                                            int32_t *idx_row, float *w_row) {
   const int npl = (a.E + 63) / 64;
-  if (npl <= 1) select_wave<1>(a, t, skey, ssg, lane);
-  else if (npl <= 2) select_wave<2>(a, t, skey, ssg, lane);
-  else if (npl <= 4) select_wave<4>(a, t, skey, ssg, lane);
-  else if (npl <= 8) select_wave<8>(a, t, skey, ssg, lane);
-  else select_wave<16>(a, t, skey, ssg, lane);
+  if (npl <= 1) select_wave<1>(a, skey, ssg, lane, idx_row, w_row);
+  else if (npl <= 2) select_wave<2>(a, skey, ssg, lane, idx_row, w_row);
+  else if (npl <= 4) select_wave<4>(a, skey, ssg, lane, idx_row, w_row);
+  else if (npl <= 8) select_wave<8>(a, skey, ssg, lane, idx_row, w_row);
+  else select_wave<16>(a, skey, ssg, lane, idx_row, w_row);
 }
 
 // fp64 sum over the wave into lane 63 (DPP on the two halves; fixed order).
@@ -245,18 +253,6 @@ __device__ inline void few_logits_finish(const RouteArgs &a, int e, int wave, in
   }
 }
 
-// Publishes this workgroup's logits (written by wave 0) and reports whether it
-// completed the count of `total` expert workgroups.  All threads call it.
-__device__ inline bool few_logits_publish(const RouteArgs &a, uint32_t total, int *s_flag) {
-  if (threadIdx.x == 0) {
-    const uint32_t old =
-        __hip_atomic_fetch_add(a.sync + kSyncRouteCtr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    *s_flag = old == total - 1;
-  }
-  __syncthreads();
-  return *s_flag != 0;
-}
-
 // ---- selection of one token by a whole workgroup ---------------------------------
 // Each expert's key becomes a unique 64-bit value (ordered key above, inverted
 // index below), so "larger value" is exactly "higher key, lower index on ties".
@@ -275,11 +271,6 @@ __device__ inline bool few_logits_publish(const RouteArgs &a, uint32_t total, in
 __device__ inline uint64_t packed_rank_value(float key, int e) {
   return ((uint64_t)ordered_key(key) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
 }
-
-struct SelCfg {
-  int E, G, Gk, k, norm;
-  float rsf;
-};
 
 struct SelLds {
   alignas(16) uint64_t v[kMaxE];            // packed values of the token's experts
@@ -409,53 +400,5 @@ __device__ void select_block(const SelCfg &c, int t, const SelIn<EPT> &in, SelLd
 }
 
 __device__ inline SelCfg sel_cfg(const RouteArgs &a) { return SelCfg{a.E, a.G, a.Gk, a.k, a.norm, a.rsf}; }
-
-// Selection for all S <= kFewTokens tokens by the workgroup that completed the
-// count, one token after another (the next token's inputs are loaded while the
-// current one is selected), from the scores and keys the expert workgroups
-// published.
-template <int EPT>
-__device__ inline void few_select_t(const RouteArgs &a, SelLds &L) {
-  const SelCfg c = sel_cfg(a);
-  SelIn<EPT> cur, nxt;
-  sel_load<EPT, false>(c, a.keys, a.scores, nullptr, cur);
-  for (int t = 0; t < a.S; ++t) {
-    const int tn = min(t + 1, a.S - 1);
-    sel_load<EPT, false>(c, a.keys + (size_t)tn * a.E, a.scores + (size_t)tn * a.E, nullptr, nxt);
-    select_block<EPT, false>(c, t, cur, L, a.idx, a.w);
-    cur = nxt;
-  }
-}
-
-// Two or more tokens with E <= 256: tokens in rounds of four, wave w selects
-// token r + w with the one-wave selection (keys and scores staged in LDS, in
-// the space of the block selection's arrays).
-__device__ inline void few_select_waves(const RouteArgs &a, SelLds &L) {
-  static_assert(sizeof(L.v) >= 4 * 256 * sizeof(double) && sizeof(L.top) >= 4 * 256 * sizeof(float), "LDS reuse");
-  double *ssg = (double *)L.v;
-  float *skey = (float *)L.top;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int r = 0; r < a.S; r += 4) {
-    const int nt = min(4, a.S - r);
-    for (int i = threadIdx.x; i < nt * a.E; i += blockDim.x) {
-      ssg[i] = ldg<double>(a.scores + (size_t)r * a.E + i);
-      skey[i] = ldg<float>(a.keys + (size_t)r * a.E + i);
-    }
-    __syncthreads();
-    if (wave < nt) select_wave_dispatch(a, r + wave, skey + (size_t)wave * a.E, ssg + (size_t)wave * a.E, lane);
-    __syncthreads();
-  }
-}
-
-__device__ inline void few_select(const RouteArgs &a, SelLds &L) {
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  if (a.S >= 2 && a.E <= 256 && blockDim.x == 256) {
-    few_select_waves(a, L);
-    return;
-  }
-  const int ept = (a.E + (int)blockDim.x - 1) / (int)blockDim.x;
-  if (ept <= 1) few_select_t<1>(a, L);
-  else few_select_t<4>(a, L);
-}
 
 }  // namespace moe
