@@ -789,6 +789,34 @@ __device__ inline int item_tokens(const FfnArgs &a, const int *it, int *toks, in
   return n;
 }
 
+// Limb form of just the rows the GEMV items read (most of a large batch goes to
+// the matrix cores): X: the items' tokens' x (H/32 groups); else the items'
+// (token, rank) rows of h (inter/32 groups).  A token or row named by several
+// items is converted more than once, to the same values.  Grid-stride over
+// (item, token slot, group).
+template <bool X>
+__global__ __launch_bounds__(256) void k_item_limbs(FfnArgs a) {
+  const int Imax = max(a.I, a.Is), ng = X ? a.H / kGroup : Imax / kGroup;
+  const long n_it = a.n_items[0] + a.n_items[1], total = n_it * kTB * ng;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (long)gridDim.x * blockDim.x) {
+    const int item = (int)(i / (kTB * ng)), r = (int)(i - (long)item * kTB * ng), tt = r / ng, g = r - tt * ng;
+    const int *it = a.items + 3 * (size_t)item;
+    const int e = it[0];
+    if (tt >= it[2] || (!X && g * kGroup >= (e == a.E ? a.Is : a.I))) continue;
+    const int pair = e == a.E ? (it[1] + tt) * (a.k + 1) + a.k : a.lists[(size_t)e * a.S + it[1] + tt];
+    const int row = X ? pair / (a.k + 1) : pair;
+    float v[32];
+    if (X) load32(a.x, a.x_bf16, (size_t)row * a.H + (size_t)g * kGroup, v);
+    else load32(a.h, 0, (size_t)row * Imax + (size_t)g * kGroup, v);
+    Limbs L;
+    to_limbs(v, L);
+    uint32_t *dl = (X ? a.xl : a.hl) + ((size_t)row * ng + g) * 24;
+#pragma unroll
+    for (int l = 0; l < 6; ++l) stg<uint4>((uint4 *)dl + l, make_uint4(L.L[l][0], L.L[l][1], L.L[l][2], L.L[l][3]));
+    stg<float>((X ? a.xf : a.hf) + (size_t)row * ng + g, L.f);
+  }
+}
+
 template <int NG>
 __global__ __launch_bounds__(256) void k_gateup_items(FfnArgs a) {
   const int wave = threadIdx.x >> 6;
@@ -964,11 +992,6 @@ hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st) {
   const int Imax = std::max(a.I, a.Is);
   hipError_t e;
   {
-    ProfScope ps("x_limbs", st);
-    e = launch_to_limbs(a.x, a.x_bf16, a.S, a.H, a.H, a.xl, a.xf, st);
-    if (e != hipSuccess) return e;
-  }
-  {
     ProfScope ps("bucket", st);
     MOE_LAUNCH(k_bucket, dim3(a.E), dim3(256), 0, st, a);
   }
@@ -979,6 +1002,12 @@ hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
+    ProfScope ps("x_limbs", st);
+    MOE_LAUNCH(k_item_limbs<true>, dim3((unsigned)a.n_cu * 4), dim3(256), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
     ProfScope ps("gateup_items", st);
     const long tiles_max = (long)a.max_items * (Imax / kGuPairs);
     const dim3 g((unsigned)std::min<long>((tiles_max + 3) / 4, 8192)), blk(256);
@@ -988,7 +1017,8 @@ hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st) {
   if (e != hipSuccess) return e;
   {
     ProfScope ps("h_limbs", st);
-    e = launch_to_limbs(a.h, 0, a.S * (a.k + 1), Imax, Imax, a.hl, a.hf, st);
+    MOE_LAUNCH(k_item_limbs<false>, dim3((unsigned)a.n_cu * 4), dim3(256), 0, st, a);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {

@@ -11,9 +11,11 @@
 // scale per row and group of 32) and down row tiles of eight output rows.
 //
 // Tiles: a workgroup (8 waves) owns up to 256 token rows of one expert's list
-// (kMT) and 256 output columns (kNT); each wave computes two 16-row blocks x
-// 256 columns of it, so an activation row is read once per 256 columns and a
-// dequantised weight feeds 256 rows.  One MFMA contracts exactly one
+// (kMT) and 256 output columns (kNT); wave w computes four 16-row blocks (row
+// band w % 4) x 128 columns (half w / 4) of it.  Every wave reads its half of
+// the dequantised B stage from LDS, so the LDS reads per MFMA are half those of
+// a 32 x 256 wave tile (at 32 x 256 the CU's LDS bandwidth matched the
+// matrix-core time exactly); activation rows are read once per 128 columns.  One MFMA contracts exactly one
 // quantisation group (K = 32), so each lane's B fragment carries a single
 // scale.  A pipeline stage is two groups: the two lanes of a B column read its
 // 32 contiguous nibble bytes of the stage and each dequantises one group (32
@@ -37,18 +39,20 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;             // waves per workgroup; wave w owns token rows 32w .. 32w+31
+constexpr int kWaves = 8;             // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMT = kMfmaTileTokens;  // token rows per workgroup tile
 constexpr int kNT = 256;              // output columns per workgroup tile
+constexpr int kWM = 8;                // row bands of a tile (wave w: band w % kWM)
+constexpr int kWN = kWaves / kWM;     // column parts of a tile (wave w: part w / kWM)
 constexpr int kMB = 2;                // MFMA row blocks (16 rows) per wave: 32 rows
-constexpr int kNB = 16;               // MFMA column blocks (16 columns) per wave: all 256 columns
+constexpr int kNB = 16;               // MFMA column blocks (16 columns) per wave: 256 columns
 constexpr int kKG = 2;                // quantisation groups (K = 32 each) per pipeline stage
 constexpr int kBStride = 80;          // bytes per column of an LDS B group (64 + 16 padding: no bank conflicts)
 constexpr int kBGroup = kNT * kBStride;
 constexpr int kBStage = kKG * kBGroup;
 constexpr int kBParts = kThreads / kNT;  // threads that dequantise one column of a group (8 bytes each)
-static_assert(kMT == kWaves * 16 * kMB && kNT == 16 * kNB && kKG == 2 && kBParts == kKG, "tile shape");
+static_assert(kMT == kWM * 16 * kMB && kNT == kWN * 16 * kNB && kKG == 2 && kBParts == kKG, "tile shape");
 
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
@@ -129,31 +133,26 @@ struct GemmAcc {
   f32x4 acc[kMB][kNB];  // [M block of 16 rows][N block of 16 columns] of this wave
 };
 
-// Stage s is group s.  Thread i dequantises half of column i % kNT (8 bytes of
-// nibbles and the scale, loaded two stages ahead) into the LDS stage; each
-// wave then runs 2 x kNB MFMAs from it with its activations (loaded one stage
-// ahead).  One barrier per stage.
-// One stage's MFMAs for the first MBV row blocks of this wave.
-// B fragments are read from LDS four at a time (a compiler fence between the
-// chunks keeps the reads from all being hoisted, which would exhaust registers).
+// One quantisation group's MFMAs for the first MBV row blocks of this wave:
+// A[mb] holds the group's activations of row block mb, sb the group's
+// dequantised B columns of this wave.  B fragments are read from LDS four at a
+// time (a compiler fence between the chunks keeps the reads from all being
+// hoisted, which would exhaust registers).
 template <int MBV>
-__device__ inline void stage_mfma(GemmAcc &C, const bf16x8 (&A)[kMB][kKG], const uint8_t *sb, int lane, int oct) {
+__device__ inline void group_mfma(GemmAcc &C, const bf16x8 (&A)[kMB], const uint8_t *sb, int lane, int oct) {
 #pragma unroll
-  for (int gi = 0; gi < kKG; ++gi)
+  for (int n4 = 0; n4 < kNB; n4 += 4) {
+    bf16x8 B[4];
 #pragma unroll
-    for (int n4 = 0; n4 < kNB; n4 += 4) {
-      bf16x8 B[4];
+    for (int q = 0; q < 4; ++q)
+      B[q] = __builtin_bit_cast(bf16x8, *(const uint4 *)(sb + ((n4 + q) * 16 + (lane & 15)) * kBStride + oct * 16));
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        B[q] = __builtin_bit_cast(
-            bf16x8, *(const uint4 *)(sb + gi * kBGroup + ((n4 + q) * 16 + (lane & 15)) * kBStride + oct * 16));
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int mb = 0; mb < MBV; ++mb)
-          C.acc[mb][n4 + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][gi], B[q], C.acc[mb][n4 + q], 0, 0, 0);
-      asm volatile("" ::: "memory");
-    }
+      for (int mb = 0; mb < MBV; ++mb)
+        C.acc[mb][n4 + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb], B[q], C.acc[mb][n4 + q], 0, 0, 0);
+    asm volatile("" ::: "memory");
+  }
 }
 
 template <bool ABF, int kDepth, int MBV>
@@ -187,27 +186,24 @@ __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_col
     *(uint4 *)(d + 32) = dequant8(r.w.z, sc);
     *(uint4 *)(d + 48) = dequant8(r.w.w, sc);
   };
-  auto load_a = [&](int st, ARaw<ABF> (&r)[kMB][kKG]) {
+  // activations of group gi of stage st (clamped to the last group)
+  auto load_a = [&](int st, int gi, ARaw<ABF> (&r)[kMB]) {
+    const int g = min(st * kKG + gi, ng - 1);
 #pragma unroll
-    for (int gi = 0; gi < kKG; ++gi) {
-      const int g = min(st * kKG + gi, ng - 1);
-#pragma unroll
-      for (int mb = 0; mb < MBV; ++mb) r[mb][gi].load(abase, arow[mb] + (size_t)g * 32 + oct * 8);
-    }
+    for (int mb = 0; mb < MBV; ++mb) r[mb].load(abase, arow[mb] + (size_t)g * 32 + oct * 8);
   };
-  // Ring of kDepth stages in registers: A of stage s is requested after the
-  // MFMAs of stage s - kDepth, B of stage s kDepth stages before it is
-  // dequantised into LDS (one stage before its MFMAs).  Loads are clamped to
-  // the last group, so every one is unconditional; groups past the last one
-  // (an odd group count, padding to a multiple of kDepth stages) multiply
-  // zeroed A fragments.
-  ARaw<ABF> aq[kDepth][kMB][kKG];
+  // Rings: the activations of group gi of stage s + 1 are requested right after
+  // the MFMAs of group gi of stage s (they come mostly from L2); B of stage s is
+  // requested kDepth stages before it is dequantised into LDS (one stage before
+  // its MFMAs).  Loads are clamped to the last group, so every one is
+  // unconditional; groups past the last one (an odd group count, padding to a
+  // multiple of kDepth stages) multiply zeroed A fragments.
+  ARaw<ABF> aq[kKG][kMB];
   BRaw bq[kDepth];
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d) {
-    load_a(d, aq[d]);
-    bq[d] = load_b(d);
-  }
+  for (int gi = 0; gi < kKG; ++gi) load_a(0, gi, aq[gi]);
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) bq[d] = load_b(d);
   store_b(0, bq[0]);
   bq[0] = load_b(kDepth);
   __syncthreads();
@@ -216,19 +212,20 @@ __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_col
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
       const int s = st + d;
-      bf16x8 A[kMB][kKG];
+      const uint8_t *sb = s_b + (s & 1) * kBStage + (wn * 16 * kNB) * kBStride;
 #pragma unroll
       for (int gi = 0; gi < kKG; ++gi) {
         const uint32_t live = s * kKG + gi < ng ? ~0u : 0u;
+        bf16x8 A[kMB];
 #pragma unroll
         for (int mb = 0; mb < MBV; ++mb) {
-          const uint4 v = __builtin_bit_cast(uint4, aq[d][mb][gi].get());
-          A[mb][gi] = __builtin_bit_cast(bf16x8, make_uint4(v.x & live, v.y & live, v.z & live, v.w & live));
+          const uint4 v = __builtin_bit_cast(uint4, aq[gi][mb].get());
+          A[mb] = __builtin_bit_cast(bf16x8, make_uint4(v.x & live, v.y & live, v.z & live, v.w & live));
         }
+        // rows past the tile's end repeat its last row; not stored
+        if (MBV > 0) group_mfma<MBV>(C, A, sb + gi * kBGroup, lane, oct);
+        load_a(s + 1, gi, aq[gi]);  // after the MFMAs: the slot's registers are free again
       }
-      const uint8_t *sb = s_b + (s & 1) * kBStage + (wn * 16 * kNB) * kBStride;
-      if (MBV > 0) stage_mfma<MBV>(C, A, sb, lane, oct);  // rows past the tile's end repeat its last row; not stored
-      load_a(s + kDepth, aq[d]);  // after the MFMAs: the slot's registers are free again
       store_b((s + 1) & 1, bq[(d + 1) % kDepth]);
       bq[(d + 1) % kDepth] = load_b(s + 1 + kDepth);
       __syncthreads();
@@ -236,20 +233,22 @@ __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_col
   }
 }
 
-// Row block rb (16 rows) of a tile belongs to wave rb % kWaves (slot rb /
-// kWaves), so that a partial tile's valid blocks spread over all SIMDs; a wave
+// Row block rb (16 rows) of a tile belongs to row band rb % kWM (slot rb /
+// kWM), so that a partial tile's valid blocks spread over all bands; a wave
 // multiplies only its valid blocks (MBV), every wave dequantises its share of B.
-__device__ inline int row_of(int wave, int mb, int r16) { return (wave + kWaves * mb) * 16 + r16; }
+__device__ inline int row_of(int wave, int mb, int r16) { return (wave % kWM + kWM * mb) * 16 + r16; }
 
 template <bool ABF, int kDepth>
 __device__ inline void gemm_rows(GemmAcc &C, int rows, int ng, const uint8_t *const *s_colp,
                                  const uint8_t *const *s_sclp, uint8_t *s_b, const void *abase, const size_t *arow,
                                  int wave, int lane) {
-  const int nblk = (rows + 15) / 16;
-  const int mbv = (wave < nblk ? 1 : 0) + (wave + kWaves < nblk ? 1 : 0);
-  if (mbv == 2) gemm_loop<ABF, kDepth, 2>(C, ng, s_colp, s_sclp, s_b, abase, arow, 0, lane);
-  else if (mbv == 1) gemm_loop<ABF, kDepth, 1>(C, ng, s_colp, s_sclp, s_b, abase, arow, 0, lane);
-  else gemm_loop<ABF, kDepth, 0>(C, ng, s_colp, s_sclp, s_b, abase, arow, 0, lane);
+  const int nblk = (rows + 15) / 16, band = wave % kWM, wn = wave / kWM;
+  const int mbv = min(kMB, max(0, (nblk - band + kWM - 1) / kWM));  // valid blocks band, band + kWM, ...
+  switch (mbv) {
+    case 2: gemm_loop<ABF, kDepth, 2>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
+    case 1: gemm_loop<ABF, kDepth, 1>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
+    default: gemm_loop<ABF, kDepth, 0>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
+  }
 }
 
 // Workgroups go to the 8 XCDs (each with its own L2) round-robin in launch
@@ -295,12 +294,12 @@ __global__ __launch_bounds__(kThreads) void k_gu_mfma(FfnArgs a) {
   tile_rows(a, mt, s_tok, s_pair);
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wn = 0;  // all columns
+  const int wn = wave / kWM;  // column part
   size_t arow[kMB];
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb) arow[mb] = (size_t)s_tok[row_of(wave, mb, lane & 15)] * a.H;
   GemmAcc C;
-  gemm_rows<true, 2>(C, mt.n, a.H / kGroup, s_colp, s_sclp, s_b, a.x_bf16 ? a.x : (const void *)a.xb, arow, wave,
+  gemm_rows<true, 3>(C, mt.n, a.H / kGroup, s_colp, s_sclp, s_b, a.x_bf16 ? a.x : (const void *)a.xb, arow, wave,
                      lane);
   // epilogue: even columns are gate, the next lane holds the matching up
 #pragma unroll
@@ -355,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void k_dn_mfma(FfnArgs a) {
   }
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wn = 0;
+  const int wn = wave / kWM;  // column part
   size_t arow[kMB];
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb) arow[mb] = (size_t)s_pair[row_of(wave, mb, lane & 15)] * 2 * Imax;
