@@ -665,6 +665,7 @@ __global__ __launch_bounds__(256) void k_bucket(FfnArgs a) {
   __shared__ int s_wsum[4];
   const int e = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = a.S * a.k;
+  const bool lane_tok = 64 % a.k == 0;  // entries i of one token share a wave (i % k == lane % k)
   const unsigned long long lt = (1ull << lane) - 1ull;
   int base = 0;
   for (int b0 = 0; b0 < n; b0 += 64 * 256) {
@@ -680,7 +681,14 @@ __global__ __launch_bounds__(256) void k_bucket(FfnArgs a) {
       for (int r = 0; r < 16; ++r) {
         const int i = b0 + (r0 + r) * 256 + tid;
         bool m = r0 + r < rows && i < n && v[r] == e;
-        if (m) {  // a token that names e twice contributes once; the combine poisons it
+        // a token that names e twice contributes once (the combine poisons it)
+        if (lane_tok) {  // the token's entries are k consecutive lanes: compare with the earlier ones
+          const int pos = lane % a.k;
+          for (int j = 1; j < a.k; ++j) {
+            const int o = __shfl(v[r], lane - j);
+            m = m && !(j <= pos && o == e);
+          }
+        } else if (m) {
           const int t0 = i / a.k * a.k;
           for (int j = t0; j < i; ++j) m = m && ldg<int>(a.idx + j) != e;
         }
