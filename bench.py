@@ -364,26 +364,56 @@ def bench_stack(args) -> int:
     y = torch.empty((1, c.hidden), dtype=torch.float32, device=dev)
     misses = np.zeros((steps, NL), np.int64)
     kernel_bytes = 0
+    # --prefetch: the next layer's routing (its router on its input, computed one
+    # layer ahead) is prefetched into the pool while the current layer computes
+    seq = [(st, l) for st in range(steps) for l in range(NL)]
+    idx2 = [torch.empty((1, c.top_k), dtype=torch.int32, device=dev) for _ in range(2)]
+    wt2 = [torch.empty((1, c.top_k), dtype=torch.float32, device=dev) for _ in range(2)]
+    idx_h2 = [torch.empty((1, c.top_k), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    ev2 = [torch.cuda.Event() for _ in range(2)]
+
+    def route_into(b, st, l):
+        M.moe_route(cfg, xs[l][st:st + 1], M.MOE_F32, 1, layers[l]["W"], layers[l]["bias"], idx2[b], wt2[b], ws,
+                    ws.numel())
+        idx_h2[b].copy_(idx2[b], non_blocking=True)
+        ev2[b].record(compute)
+
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for st in range(steps):
-        for l in range(NL):
-            L = layers[l]
-            x = xs[l][st:st + 1]
+    if args.prefetch:
+        route_into(0, *seq[0])
+    for j, (st, l) in enumerate(seq):
+        L = layers[l]
+        x = xs[l][st:st + 1]
+        if args.prefetch:
+            b = j % 2
+            ev2[b].synchronize()  # this layer's routing is on the host
+            if j + 1 < len(seq):
+                route_into(1 - b, *seq[j + 1])  # ahead of this layer's fill wait on the compute stream
+            ih, i_d, w_d = idx_h2[b], idx2[b], wt2[b]
+            view, n_miss = pool.acquire(l, ih.numpy(), compute, side)
+            M.moe_ffn(cfg, x, M.MOE_F32, 1, i_d, w_d, view, L["shared"], y, ws, ws.numel())
+            pool.release(l, compute)
+            if j + 1 < len(seq):
+                ev2[1 - b].synchronize()
+                pool.prefetch(seq[j + 1][1], idx_h2[1 - b].numpy(), side)
+        else:
+            ih = idx_h
             M.moe_route(cfg, x, M.MOE_F32, 1, L["W"], L["bias"], idx, wt, ws, ws.numel())
             idx_h.copy_(idx, non_blocking=True)
             compute.synchronize()  # the host decides residency
             view, n_miss = pool.acquire(l, idx_h.numpy(), compute, side)
             M.moe_ffn(cfg, x, M.MOE_F32, 1, idx, wt, view, L["shared"], y, ws, ws.numel())
             pool.release(l, compute)
-            misses[st, l] = n_miss
-            kernel_bytes += (len(set(idx_h.numpy().ravel().tolist())) + 1) * sb
-        if st == 0:
-            torch.cuda.synchronize()
-            t_step0 = time.perf_counter() - t_start
-            log(f"step 0 (cold pool): {t_step0 * 1e3:.1f} ms, {misses[0].sum()} misses")
-        elif st % 8 == 0:
-            log(f"step {st}: {time.perf_counter() - t_start:.2f} s, {misses[st].sum()} misses this step")
+        misses[st, l] = n_miss
+        kernel_bytes += (len(set(ih.numpy().ravel().tolist())) + 1) * sb
+        if l == NL - 1:
+            if st == 0:
+                torch.cuda.synchronize()
+                t_step0 = time.perf_counter() - t_start
+                log(f"step 0 (cold pool): {t_step0 * 1e3:.1f} ms, {misses[0].sum()} misses at acquire")
+            elif st % 8 == 0:
+                log(f"step {st}: {time.perf_counter() - t_start:.2f} s, {misses[st].sum()} misses at acquire this step")
     torch.cuda.synchronize()
     el = time.perf_counter() - t_start
     stt = pool.stats()
@@ -393,16 +423,20 @@ def bench_stack(args) -> int:
     hit_rest = 1.0 - misses[1:].sum() / (sel * max(1, steps - 1))
     warm_el = el - t_step0
     log(f"stack: {el:.3f} s for {steps} steps x {NL} layers; hit rate step0 {hit0:.3f}, steps 1+ {hit_rest:.3f}; "
-        f"fills {stt['fill_bytes'] / 1e9:.1f} GB; H2D ceiling {h2d_gbps:.1f} GB/s")
+        f"fills {stt['fill_bytes'] / 1e9:.1f} GB (prefetched {stt['prefetch_fills']} experts); "
+        f"H2D ceiling {h2d_gbps:.1f} GB/s")
     emit({"metric": "MoE-layer tokens/s and effective int4 weight GB/s (% of HBM peak), GLM-5.2",
           "value": steps / el, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": 0,
           "ms_per_step": el * 1e3 / steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
           "dtype": "f32", "data": "synthetic",
           "config": {"workload": "glm52_moe_stack_75_layers_decode", "layers": NL, "steps": steps,
                      "slots_per_layer": spl, "pool_gb": NL * spl * sb / 1e9, "distinct_blobs": w.n_blobs,
-                     "bias": w.bias_recipe, "launch": "eager; host sync per layer for residency"},
+                     "bias": w.bias_recipe, "prefetch": bool(args.prefetch),
+                     "launch": ("eager; next layer routed ahead and prefetched" if args.prefetch
+                                else "eager; host sync per layer for residency")},
           "tokens_per_s_warm": (steps - 1) / warm_el if steps > 1 else None,
           "hit_rate_step0": hit0, "hit_rate_steps_1_plus": hit_rest, "misses": int(misses.sum()),
+          "prefetch_fills": int(stt["prefetch_fills"]), "prefetch_hits": int(stt["prefetch_hits"]),
           "fill_bytes": int(stt["fill_bytes"]), "fill_gbps_wall": stt["fill_bytes"] / el / 1e9,
           "h2d_ceiling_gbps": h2d_gbps, "kernel_bytes": kernel_bytes,
           "kernel_bytes_gbps_wall": kernel_bytes / el / 1e9})
@@ -440,6 +474,8 @@ def main() -> int:
     ap.add_argument("--blobs", type=int, default=0, help="stack: distinct pinned weight blobs (0: 1024)")
     ap.add_argument("--slots-per-layer", type=int, default=100, help="stack: HBM slots per layer")
     ap.add_argument("--stack-steps", type=int, default=0, help="stack: decode steps (0: 64)")
+    ap.add_argument("--prefetch", action="store_true",
+                    help="stack: route each next layer ahead and prefetch its experts into the pool")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

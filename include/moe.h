@@ -208,10 +208,30 @@ int moe_pool_register_host(moe_pool *pool, int32_t layer, int32_t expert, const 
 int moe_pool_acquire(moe_pool *pool, int32_t layer, const int32_t *idx_host, int32_t n, moe_slot_view *view_out,
                      int32_t *n_miss_out, void *compute_stream, void *side_stream);
 int moe_pool_release(moe_pool *pool, int32_t layer, void *compute_stream);
+/* Predictive prefetch ([PORT] "What Colibri is actually doing", item 10: the
+ * next layer's router applied ahead of time, real loads only for a future
+ * layer, residency rechecked, no partially filled slot ever published; [README]
+ * "What's implemented", router-lookahead prefetch).  idx_host (host memory, n
+ * entries) is a predicted routing of `layer`.  Its resident experts become
+ * recently used; each missing one takes a free slot or the least recently used
+ * unleased slot of the layer (ties: lowest; never a leased slot) and its copy
+ * is enqueued on side_stream after the victim's last consumer, with nothing
+ * leased and nothing published.  The next moe_pool_acquire of the layer finds
+ * those experts resident, makes its compute stream wait for their copies and
+ * uploads the table, so results are the same as without the prefetch; a
+ * prediction that is never acquired only takes slots (and may evict experts
+ * that would have hit: [PORT] "What not to copy blindly").  When every slot is
+ * leased the rest of the prediction is dropped.  n_fill_out (optional): copies
+ * enqueued.  Errors: MOE_ENOSLOT (union larger than slots_per_layer), MOE_ENULL
+ * (a missing expert has no registered host source), MOE_EINVAL, MOE_EHIP. */
+int moe_pool_prefetch(moe_pool *pool, int32_t layer, const int32_t *idx_host, int32_t n, int32_t *n_fill_out,
+                      void *side_stream);
 /* The last acquire's decisions as (expert, slot, hit) triples in out[3 * i ..];
  * returns the number of triples, or a negative status (cap too small). */
 int moe_pool_trace(const moe_pool *pool, int32_t *out, int32_t cap);
-/* {"acquires", "hits", "misses", "evictions", "fill_bytes", ...} as JSON. */
+/* {"acquires", "hits", "misses", "evictions", "fill_bytes", "prefetches",
+ * "prefetch_fills", "prefetch_hits", ...} as JSON (prefetch_hits: acquire hits
+ * on prefetched slots). */
 int moe_pool_stats(const moe_pool *pool, char *out_json, size_t cap);
 
 /* Timing instrumentation (not part of the layer's computation).  While enabled,

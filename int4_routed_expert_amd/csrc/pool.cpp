@@ -17,6 +17,14 @@
 // are published in the device table on the compute stream only after their copy
 // completed (the compute stream waits on the copy's event).  release() records
 // the consumer-done event of every leased slot.
+//
+// prefetch() (the same page, "What Colibri is actually doing", item 10,
+// predictive prefetch: real loads only for a future layer, residency rechecked,
+// no partially filled slot published) fills a predicted union the same way but
+// leases nothing and publishes nothing: each copied slot keeps its own copy
+// event and is marked pending; the next acquire of the layer makes its compute
+// stream wait for the pending slots it leases and uploads the table.  Any later
+// copy into a pending slot waits for the earlier copy first.
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
@@ -47,14 +55,18 @@ struct moe_pool {
     bool leased = false;
     hipEvent_t done = nullptr;  // consumer-done event (valid when used)
     bool has_done = false;
+    hipEvent_t fill_ev = nullptr;  // copy-done event of a prefetch
+    bool pending = false;          // prefetched; no acquire has waited for the copy yet
   };
   std::vector<Slot> slots;  // [n_layers][spl]
   std::vector<int> leased_layer;  // per layer: number of slots leased by the open acquire, -1 none
   std::vector<std::vector<int>> lease_list;
   std::vector<hipEvent_t> ev_pool;
+  std::vector<char> table_dirty;  // per layer: host table changed by a prefetch since the last upload
   uint64_t clock = 0;
   // statistics
   uint64_t hits = 0, misses = 0, evictions = 0, fill_bytes = 0, acquires = 0;
+  uint64_t prefetches = 0, prefetch_fills = 0, prefetch_hits = 0;
   std::vector<int32_t> trace;  // last acquire: (expert, slot, hit) triples
 };
 
@@ -67,6 +79,46 @@ static hipEvent_t get_event(moe_pool *p) {
   hipEvent_t e = nullptr;
   if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
   return e;
+}
+
+// Victim for a miss of `layer`: a free slot (lowest) first, else the least
+// recently used unleased slot (ties: lowest); -1 if every slot is leased.
+static int pick_victim(moe_pool *p, int layer) {
+  moe_pool::Slot *base = &p->slots[(size_t)layer * p->spl];
+  for (int s = 0; s < p->spl; ++s)
+    if (base[s].expert < 0 && !base[s].leased) return s;
+  int victim = -1;
+  for (int s = 0; s < p->spl; ++s)
+    if (!base[s].leased && (victim < 0 || base[s].last_use < base[victim].last_use)) victim = s;
+  return victim;
+}
+
+// Enqueues the copy of expert e into slot s of `layer` on `ss`, after the slot's
+// last consumer and (for a pending prefetch) its last copy.
+static hipError_t enqueue_fill(moe_pool *p, int layer, int e, int s, hipStream_t ss) {
+  moe_pool::Slot &sl = p->slots[(size_t)layer * p->spl + s];
+  uint8_t *dst = p->slab + ((size_t)layer * p->spl + s) * (size_t)p->slot_bytes;
+  hipError_t err = hipSuccess;
+  if (sl.has_done) err = hipStreamWaitEvent(ss, sl.done, 0);  // previous consumer of the victim is done
+  if (err == hipSuccess && sl.pending) err = hipStreamWaitEvent(ss, sl.fill_ev, 0);  // previous copy is done
+  if (err == hipSuccess && p->poison) err = hipMemsetAsync(dst, 0xFF, (size_t)p->slot_bytes, ss);
+  if (err == hipSuccess)
+    err = hipMemcpyAsync(dst, p->src[(size_t)layer * p->E + e], (size_t)p->slot_bytes, hipMemcpyHostToDevice, ss);
+  p->fill_bytes += (uint64_t)p->slot_bytes;
+  return err;
+}
+
+// Union of idx[0..n) in first-appearance order, with the acquire/prefetch checks.
+static int union_of(moe_pool *p, int layer, const int32_t *idx, int32_t n, std::vector<int> &uniq) {
+  for (int i = 0; i < n; ++i) {
+    const int e = idx[i];
+    if (e < 0 || e >= p->E) return MOE_EINVAL;
+    if (std::find(uniq.begin(), uniq.end(), e) == uniq.end()) uniq.push_back(e);
+  }
+  if ((int)uniq.size() > p->spl) return MOE_ENOSLOT;
+  for (int e : uniq)
+    if (p->table[(size_t)layer * p->E + e] < 0 && !p->src[(size_t)layer * p->E + e]) return MOE_ENULL;
+  return MOE_OK;
 }
 
 extern "C" {
@@ -90,6 +142,7 @@ int moe_pool_create(const moe_cfg *cfg, int32_t n_layers, int32_t slots_per_laye
   p->slots.resize((size_t)n_layers * slots_per_layer);
   p->leased_layer.assign(n_layers, -1);
   p->lease_list.resize(n_layers);
+  p->table_dirty.assign(n_layers, 0);
   if (p->device) {
     const size_t slab = (size_t)n_layers * slots_per_layer * (size_t)p->slot_bytes;
     hipError_t e = hipMalloc(&p->slab, slab);
@@ -113,8 +166,10 @@ int moe_pool_create(const moe_cfg *cfg, int32_t n_layers, int32_t slots_per_laye
 void moe_pool_destroy(moe_pool *p) {
   if (!p) return;
   if (p->device) (void)hipDeviceSynchronize();
-  for (auto &s : p->slots)
+  for (auto &s : p->slots) {
     if (s.done) (void)hipEventDestroy(s.done);
+    if (s.fill_ev) (void)hipEventDestroy(s.fill_ev);
+  }
   for (auto e : p->ev_pool) (void)hipEventDestroy(e);
   for (auto e : p->table_ev)
     if (e) (void)hipEventDestroy(e);
@@ -136,22 +191,15 @@ int moe_pool_acquire(moe_pool *p, int32_t layer, const int32_t *idx, int32_t n, 
   if (!p || !view || (n > 0 && !idx)) return MOE_ENULL;
   if (layer < 0 || layer >= p->n_layers || n < 0) return MOE_EINVAL;
   if (p->leased_layer[layer] >= 0) return MOE_ESTALE;  // previous lease of this layer not released
-  // union of the named experts, in first-appearance order
-  std::vector<int> uniq;
-  for (int i = 0; i < n; ++i) {
-    const int e = idx[i];
-    if (e < 0 || e >= p->E) return MOE_EINVAL;
-    if (std::find(uniq.begin(), uniq.end(), e) == uniq.end()) uniq.push_back(e);
-  }
-  if ((int)uniq.size() > p->spl) return MOE_ENOSLOT;
-  for (int e : uniq)
-    if (p->table[(size_t)layer * p->E + e] < 0 && !p->src[(size_t)layer * p->E + e]) return MOE_ENULL;
+  std::vector<int> uniq;  // union of the named experts, in first-appearance order
+  const int u = union_of(p, layer, idx, n, uniq);
+  if (u) return u;
   moe_pool::Slot *base = &p->slots[(size_t)layer * p->spl];
   int32_t *tab = &p->table[(size_t)layer * p->E];
   ++p->acquires;
   const uint64_t now = ++p->clock;
   p->trace.clear();
-  std::vector<int> leased;
+  std::vector<int> leased, waits;  // waits: prefetched slots whose copy the compute stream must wait for
   // hits first: lease them so that misses cannot evict them
   for (int e : uniq) {
     const int s = tab[e];
@@ -160,18 +208,17 @@ int moe_pool_acquire(moe_pool *p, int32_t layer, const int32_t *idx, int32_t n, 
       base[s].last_use = now;
       leased.push_back(s);
       ++p->hits;
+      if (base[s].pending) {
+        waits.push_back(s);
+        ++p->prefetch_hits;
+      }
       p->trace.insert(p->trace.end(), {e, s, 1});
     }
   }
   std::vector<std::pair<int, int>> fills;  // (expert, slot)
   for (int e : uniq) {
     if (tab[e] >= 0) continue;
-    int victim = -1;
-    for (int s = 0; s < p->spl; ++s)  // free slot first (lowest), else least recently used unleased (ties: lowest)
-      if (base[s].expert < 0 && !base[s].leased) { victim = s; break; }
-    if (victim < 0)
-      for (int s = 0; s < p->spl; ++s)
-        if (!base[s].leased && (victim < 0 || base[s].last_use < base[victim].last_use)) victim = s;
+    const int victim = pick_victim(p, layer);
     if (victim < 0) return MOE_ENOSLOT;  // cannot happen: uniq <= spl
     if (base[victim].expert >= 0) {
       tab[base[victim].expert] = -1;
@@ -194,18 +241,20 @@ int moe_pool_acquire(moe_pool *p, int32_t layer, const int32_t *idx, int32_t n, 
   view->slot_bytes = p->slot_bytes;
   view->table = p->d_tables ? p->d_tables + (size_t)layer * p->E : nullptr;
   view->n_slots = p->spl;
-  if (!p->device) return MOE_OK;
+  if (!p->device) {
+    for (int s : waits) base[s].pending = false;
+    return MOE_OK;
+  }
   hipStream_t cs = (hipStream_t)compute, ss = (hipStream_t)side;
   hipError_t err = hipSuccess;
   for (auto &f : fills) {
-    moe_pool::Slot &sl = base[f.second];
-    uint8_t *dst = p->slab + ((size_t)layer * p->spl + f.second) * (size_t)p->slot_bytes;
-    if (sl.has_done) err = hipStreamWaitEvent(ss, sl.done, 0);  // previous consumer of the victim is done
-    if (err == hipSuccess && p->poison) err = hipMemsetAsync(dst, 0xFF, (size_t)p->slot_bytes, ss);
-    if (err == hipSuccess)
-      err = hipMemcpyAsync(dst, p->src[(size_t)layer * p->E + f.first], (size_t)p->slot_bytes, hipMemcpyHostToDevice, ss);
-    p->fill_bytes += (uint64_t)p->slot_bytes;
+    err = enqueue_fill(p, layer, f.first, f.second, ss);
+    base[f.second].pending = false;  // this acquire's event covers the slot from here on
     if (err != hipSuccess) break;
+  }
+  for (int s : waits) {  // prefetched copies: publish only complete slots
+    if (err == hipSuccess) err = hipStreamWaitEvent(cs, base[s].fill_ev, 0);
+    base[s].pending = false;
   }
   if (err == hipSuccess && !fills.empty()) {
     hipEvent_t filled = get_event(p);
@@ -214,7 +263,8 @@ int moe_pool_acquire(moe_pool *p, int32_t layer, const int32_t *idx, int32_t n, 
     if (err == hipSuccess) err = hipStreamWaitEvent(cs, filled, 0);  // publish only complete slots
     if (filled) p->ev_pool.push_back(filled);  // reusable: the wait has captured its state
   }
-  if (err == hipSuccess && !fills.empty()) {  // the table changed: upload it on the compute stream
+  if (err == hipSuccess && (!fills.empty() || p->table_dirty[layer])) {  // table changed: upload on the compute stream
+    p->table_dirty[layer] = 0;
     int32_t *stage = p->h_stage + (size_t)layer * p->E;
     err = hipEventSynchronize(p->table_ev[layer]);  // the staging buffer's previous upload is complete
     if (err == hipSuccess) {
@@ -222,6 +272,71 @@ int moe_pool_acquire(moe_pool *p, int32_t layer, const int32_t *idx, int32_t n, 
       err = hipMemcpyAsync(p->d_tables + (size_t)layer * p->E, stage, sizeof(int32_t) * p->E, hipMemcpyHostToDevice, cs);
     }
     if (err == hipSuccess) err = hipEventRecord(p->table_ev[layer], cs);
+  }
+  if (err != hipSuccess) {
+    set_hip_error(err);
+    return MOE_EHIP;
+  }
+  return MOE_OK;
+}
+
+int moe_pool_prefetch(moe_pool *p, int32_t layer, const int32_t *idx, int32_t n, int32_t *n_fill, void *side) {
+  if (!p || (n > 0 && !idx)) return MOE_ENULL;
+  if (layer < 0 || layer >= p->n_layers || n < 0) return MOE_EINVAL;
+  std::vector<int> uniq;
+  const int u = union_of(p, layer, idx, n, uniq);
+  if (u) return u;
+  moe_pool::Slot *base = &p->slots[(size_t)layer * p->spl];
+  int32_t *tab = &p->table[(size_t)layer * p->E];
+  ++p->prefetches;
+  const uint64_t now = ++p->clock;
+  // residency rechecked: resident experts only become recently used; each
+  // missing one takes a victim like an acquire miss (never a leased slot, nor
+  // a slot of this prediction: those are held like leases during the call)
+  std::vector<std::pair<int, int>> fills;
+  std::vector<int> held;
+  for (int e : uniq)
+    if (tab[e] >= 0) {
+      moe_pool::Slot &sl = base[tab[e]];
+      sl.last_use = now;
+      if (!sl.leased) {
+        sl.leased = true;
+        held.push_back(tab[e]);
+      }
+    }
+  for (int e : uniq) {
+    if (tab[e] >= 0) continue;
+    const int victim = pick_victim(p, layer);
+    if (victim < 0) break;  // no slot left: the rest of the prediction is dropped
+    base[victim].leased = true;
+    held.push_back(victim);
+    if (base[victim].expert >= 0) {
+      tab[base[victim].expert] = -1;
+      ++p->evictions;
+    }
+    base[victim].expert = e;
+    base[victim].last_use = now;
+    base[victim].gen += 1;
+    tab[e] = victim;
+    fills.emplace_back(e, victim);
+    ++p->prefetch_fills;
+  }
+  for (int s : held) base[s].leased = false;
+  if (n_fill) *n_fill = (int32_t)fills.size();
+  if (!fills.empty()) p->table_dirty[layer] = 1;
+  if (!p->device) {
+    for (auto &f : fills) base[f.second].pending = true;
+    return MOE_OK;
+  }
+  hipStream_t ss = (hipStream_t)side;
+  hipError_t err = hipSuccess;
+  for (auto &f : fills) {
+    moe_pool::Slot &sl = base[f.second];
+    err = enqueue_fill(p, layer, f.first, f.second, ss);
+    if (err == hipSuccess && !sl.fill_ev) err = hipEventCreateWithFlags(&sl.fill_ev, hipEventDisableTiming);
+    if (err == hipSuccess) err = hipEventRecord(sl.fill_ev, ss);
+    if (err != hipSuccess) break;
+    sl.pending = true;
   }
   if (err != hipSuccess) {
     set_hip_error(err);
@@ -266,10 +381,13 @@ int moe_pool_stats(const moe_pool *p, char *out, size_t cap) {
   char buf[512];
   const int len = std::snprintf(buf, sizeof buf,
                                 "{\"acquires\": %llu, \"hits\": %llu, \"misses\": %llu, \"evictions\": %llu, "
-                                "\"fill_bytes\": %llu, \"slots_per_layer\": %d, \"layers\": %d, \"slot_bytes\": %lld}",
+                                "\"fill_bytes\": %llu, \"prefetches\": %llu, \"prefetch_fills\": %llu, "
+                                "\"prefetch_hits\": %llu, \"slots_per_layer\": %d, \"layers\": %d, \"slot_bytes\": %lld}",
                                 (unsigned long long)p->acquires, (unsigned long long)p->hits,
                                 (unsigned long long)p->misses, (unsigned long long)p->evictions,
-                                (unsigned long long)p->fill_bytes, p->spl, p->n_layers, (long long)p->slot_bytes);
+                                (unsigned long long)p->fill_bytes, (unsigned long long)p->prefetches,
+                                (unsigned long long)p->prefetch_fills, (unsigned long long)p->prefetch_hits, p->spl,
+                                p->n_layers, (long long)p->slot_bytes);
   if (len < 0 || (size_t)len + 1 > cap) return MOE_EINVAL;
   std::memcpy(out, buf, (size_t)len + 1);
   return MOE_OK;

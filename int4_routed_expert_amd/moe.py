@@ -69,6 +69,7 @@ def _load():
         "moe_pool_register_host": (ctypes.c_int, [p, i32, i32, p]),
         "moe_pool_acquire": (ctypes.c_int, [p, i32, p, i32, ctypes.POINTER(moe_slot_view), ctypes.POINTER(i32), p, p]),
         "moe_pool_release": (ctypes.c_int, [p, i32, p]),
+        "moe_pool_prefetch": (ctypes.c_int, [p, i32, p, i32, ctypes.POINTER(i32), p]),
         "moe_pool_trace": (ctypes.c_int, [p, p, i32]),
         "moe_pool_stats": (ctypes.c_int, [p, ctypes.c_char_p, sz]),
         "moe_profile_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -217,6 +218,15 @@ class Pool:
         _check(_lib.moe_pool_acquire(self.h, layer, idx.ctypes.data, idx.size, ctypes.byref(view), ctypes.byref(n_miss),
                                      c, s_), "moe_pool_acquire")
         return view, n_miss.value
+
+    def prefetch(self, layer: int, idx_host, side=None) -> int:
+        """Predicted routing idx_host (int32 numpy array) of `layer`; -> copies enqueued."""
+        import numpy as np
+        idx = np.ascontiguousarray(idx_host, np.int32).ravel()
+        n_fill = ctypes.c_int32(0)
+        _check(_lib.moe_pool_prefetch(self.h, layer, idx.ctypes.data, idx.size, ctypes.byref(n_fill),
+                                      stream_handle(side) if side is not None else None), "moe_pool_prefetch")
+        return n_fill.value
 
     def release(self, layer: int, compute=None) -> None:
         c = stream_handle(compute) if compute is not None else None

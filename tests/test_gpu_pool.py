@@ -18,7 +18,11 @@ pytestmark = pytest.mark.gpu
 MID = gen.LayerConfig(hidden=512, n_experts=32, n_group=4, topk_group=2, top_k=4, moe_inter=256, shared_inter=192)
 
 
-def run_stack(w: gen.Workload, n_layers: int, steps: int, spl: int, flags: int, check_ffn_every: int = 1):
+def run_stack(w: gen.Workload, n_layers: int, steps: int, spl: int, flags: int, check_ffn_every: int = 1,
+              prefetch: str | None = None):
+    """prefetch: None; "next" (the next (step, layer)'s routing, computed ahead on
+    its own input, is prefetched while the current layer's lease is open); or
+    "wrong" (random experts of the next layer are prefetched instead)."""
     c = w.cfg
     cfg = M.make_cfg(c)
     E, I = c.n_experts, c.moe_inter
@@ -44,7 +48,10 @@ def run_stack(w: gen.Workload, n_layers: int, steps: int, spl: int, flags: int, 
     compute = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     ws = M.workspace(cfg, 1)
+    ws2 = M.workspace(cfg, 1)
+    rng = np.random.default_rng(7)
     worst, n_checked = 0.0, 0
+    ys = []
     for step in range(steps):
         for l in range(n_layers):
             L = layers[l]
@@ -55,9 +62,22 @@ def run_stack(w: gen.Workload, n_layers: int, steps: int, spl: int, flags: int, 
             M.moe_route(cfg, x, M.MOE_F32, 1, dev(L["W"]), dev(L["b"]), idx, wt, ws, ws.numel())
             idx_h = idx.cpu().numpy()  # the host decides residency: one sync per layer
             view, n_miss = pool.acquire(l, idx_h, compute, side)
+            if prefetch:
+                ns, nl = (step, l + 1) if l + 1 < n_layers else (step + 1, 0)
+                if prefetch == "next":
+                    L2 = layers[nl]
+                    i2 = torch.empty((1, c.top_k), dtype=torch.int32, device="cuda")
+                    w2 = torch.empty((1, c.top_k), dtype=torch.float32, device="cuda")
+                    M.moe_route(cfg, dev(gen.tokens(w, layer=nl, step=ns)), M.MOE_F32, 1, dev(L2["W"]), dev(L2["b"]),
+                                i2, w2, ws2, ws2.numel())
+                    pred = i2.cpu().numpy()
+                else:
+                    pred = rng.choice(E, size=c.top_k, replace=False).astype(np.int32)
+                pool.prefetch(nl, pred, side)
             y = torch.full((1, c.hidden), float("nan"), device="cuda")
             M.moe_ffn(cfg, x, M.MOE_F32, 1, idx, wt, view, L["shared"], y, ws, ws.numel())
             pool.release(l, compute)
+            ys.append(y)
             ridx, rw, _, flags_, _ = O.route(c, xh, L["W"], L["b"])
             assert not flags_.any()
             assert np.array_equal(idx_h, ridx), (step, l)
@@ -72,19 +92,37 @@ def run_stack(w: gen.Workload, n_layers: int, steps: int, spl: int, flags: int, 
     torch.cuda.synchronize()
     st = pool.stats()
     pool.close()
-    return st, worst, n_checked
+    return st, worst, n_checked, np.concatenate([y.cpu().numpy() for y in ys])
 
 
 @pytest.mark.parametrize("flags", [0, M.MOE_POOL_POISON])
 def test_pool_stack_mid_shape_heavy_churn(flags):
     w = gen.Workload("stack-mid", MID, tokens=1, bias_recipe="hotset", layers=6, steps=8, seed=41)
-    st, worst, n = run_stack(w, n_layers=6, steps=8, spl=5, flags=flags)
+    st, worst, n, _ = run_stack(w, n_layers=6, steps=8, spl=5, flags=flags)
     print("pool stats", st, "worst", worst, "checked", n, flush=True)
     assert st["misses"] > 6 * 4 and st["evictions"] > 0 and st["hits"] > 0
 
 
 def test_pool_stack_glm_shape():
     w = gen.WORKLOADS["stack"]
-    st, worst, n = run_stack(w, n_layers=2, steps=3, spl=12, flags=M.MOE_POOL_POISON, check_ffn_every=2)
+    st, worst, n, _ = run_stack(w, n_layers=2, steps=3, spl=12, flags=M.MOE_POOL_POISON, check_ffn_every=2)
     print("pool stats", st, "worst", worst, "checked", n, flush=True)
     assert st["evictions"] >= 0 and st["misses"] >= 16
+
+
+@pytest.mark.parametrize("n_layers", [1, 3])
+def test_pool_prefetch_is_value_preserving(n_layers):
+    """Predictive prefetch (the next layer's routing computed ahead, or random
+    mispredictions), with every refilled slot poisoned first: the outputs are
+    bitwise those of the run without prefetch and match the oracle; with the
+    exact prediction every routed expert is resident at its acquire.  With one
+    layer the prefetch targets the layer whose lease is still open."""
+    w = gen.Workload("stack-mid", MID, tokens=1, bias_recipe="hotset", layers=n_layers, steps=6, seed=43)
+    base, _, _, y0 = run_stack(w, n_layers=n_layers, steps=6, spl=6, flags=M.MOE_POOL_POISON)
+    nxt, _, _, y1 = run_stack(w, n_layers=n_layers, steps=6, spl=6, flags=M.MOE_POOL_POISON, prefetch="next")
+    bad, _, _, y2 = run_stack(w, n_layers=n_layers, steps=6, spl=6, flags=M.MOE_POOL_POISON, prefetch="wrong")
+    print("no prefetch", base, "\nnext", nxt, "\nwrong", bad, flush=True)
+    assert np.array_equal(y0, y1) and np.array_equal(y0, y2)
+    assert nxt["prefetch_fills"] > 0 and nxt["prefetch_hits"] > 0 and bad["prefetch_fills"] > 0
+    if n_layers > 1:  # exact predictions of other layers: acquires after the first one only hit
+        assert nxt["misses"] <= w.cfg.top_k

@@ -15,6 +15,46 @@ class RefLRU:
         self.expert = [[-1] * spl for _ in range(n_layers)]
         self.last = [[0] * spl for _ in range(n_layers)]
         self.clock = 0
+        self.leased = [set() for _ in range(n_layers)]  # slots of an open acquire
+
+    def _victim(self, layer, busy):
+        ex, last = self.expert[layer], self.last[layer]
+        free = [s for s in range(self.spl) if ex[s] < 0 and s not in busy]
+        if free:
+            return free[0]
+        cands = [s for s in range(self.spl) if s not in busy]
+        return min(cands, key=lambda s: (last[s], s)) if cands else -1
+
+    def prefetch(self, layer, idx):
+        """Predictive prefetch: resident experts become recently used, missing ones
+        take victims like misses (never a leased slot, nor one of the prediction's
+        own slots); returns the copies made."""
+        uniq = []
+        for e in idx:
+            if e not in uniq:
+                uniq.append(e)
+        self.clock += 1
+        ex, last = self.expert[layer], self.last[layer]
+        busy = set(self.leased[layer])  # plus the prediction's own slots during the call
+        for e in uniq:
+            if e in ex:
+                last[ex.index(e)] = self.clock
+                busy.add(ex.index(e))
+        fills = 0
+        for e in uniq:
+            if e in ex:
+                continue
+            v = self._victim(layer, busy)
+            if v < 0:
+                break
+            ex[v] = e
+            last[v] = self.clock
+            busy.add(v)
+            fills += 1
+        return fills
+
+    def release(self, layer):
+        self.leased[layer] = set()
 
     def acquire(self, layer, idx):
         uniq = []
@@ -44,6 +84,7 @@ class RefLRU:
             last[v] = self.clock
             leased.add(v)
             out.append((e, v, 0))
+        self.leased[layer] = leased
         return out
 
 
@@ -120,3 +161,65 @@ def test_leased_slots_are_never_evicted():
     evicted_slots = {int(t[1]) for t in tr if t[2] == 0}
     assert evicted_slots == {2, 3}
     pool.release(0)
+
+
+@pytest.mark.parametrize("spl", [4, 6])
+def test_prefetch_policy_matches_reference(spl):
+    """Random acquires, releases and predictive prefetches (some while the layer
+    holds a lease, some of experts that are never acquired): every acquire's
+    decisions and every prefetch's copy count follow the reference policy, and a
+    prefetched expert is a hit at the next acquire."""
+    rng = np.random.default_rng(100 + spl)
+    n_layers, E = 2, 12
+    pool = make_pool(n_layers, spl, E)
+    ref = RefLRU(n_layers, spl)
+    open_lease = [False] * n_layers
+    pf_hits_ref = 0
+    pending = [set() for _ in range(n_layers)]  # prefetched, not yet acquired
+    for it in range(600):
+        layer = int(rng.integers(0, n_layers))
+        op = rng.random()
+        idx = [int(rng.integers(0, E)) for _ in range(int(rng.integers(1, spl + 1)))]
+        if len(set(idx)) > spl:
+            continue
+        if op < 0.35:
+            n_fill = pool.prefetch(layer, np.array(idx, np.int32))
+            want = ref.prefetch(layer, idx)
+            assert n_fill == want, (it, layer, idx)
+            # a prefetched slot stays "prefetched" until an acquire leases it or it is refilled
+            ex = ref.expert[layer]
+            pending[layer] = {e for e in pending[layer] if e in ex} | {e for e in set(idx) if e in ex}
+        elif not open_lease[layer]:
+            _, n_miss = pool.acquire(layer, np.array(idx, np.int32))
+            got = [tuple(int(v) for v in t) for t in pool.trace()]
+            want = ref.acquire(layer, idx)
+            assert got == want, (it, layer, idx)
+            hits = {t[0] for t in want if t[2] == 1}
+            pf_hits_ref += len(hits & pending[layer])
+            pending[layer] -= hits
+            pending[layer] = {e for e in pending[layer] if e in ref.expert[layer]}
+            open_lease[layer] = True
+        else:
+            pool.release(layer)
+            ref.release(layer)
+            open_lease[layer] = False
+    st = pool.stats()
+    assert st["prefetches"] > 0 and st["prefetch_fills"] > 0
+
+
+def test_prefetch_then_acquire_hits_and_leases_are_kept():
+    pool = make_pool(1, 4)
+    assert pool.prefetch(0, np.array([3, 7], np.int32)) == 2
+    assert pool.prefetch(0, np.array([3, 7], np.int32)) == 0  # resident: no copy
+    _, n_miss = pool.acquire(0, np.array([7, 3], np.int32))
+    assert n_miss == 0 and pool.stats()["prefetch_hits"] == 2
+    # with the lease open, a prediction can only use the two unleased slots
+    assert pool.prefetch(0, np.array([1, 2, 4, 5], np.int32)) == 2
+    tr_slots = {int(t[1]) for t in pool.trace()}
+    pool.release(0)
+    _, n_miss = pool.acquire(0, np.array([3, 7], np.int32))  # still resident in their slots
+    assert n_miss == 0 and {int(t[1]) for t in pool.trace()} == tr_slots
+    pool.release(0)
+    with pytest.raises(M.MoeError) as e:
+        pool.prefetch(0, np.array([1, 2, 3, 4, 5], np.int32))  # union of 5 > 4 slots
+    assert e.value.status == M.MOE_ENOSLOT
