@@ -13,11 +13,19 @@ contraction, groups of 32 along K):
     consecutive elements of a row.
 An expert has gate ``[I, H]``, up ``[I, H]`` and down ``[H, I]`` matrices.
 
+Row-scaled formats (``LayerConfig.weight_format``): 1 = the same int4 bytes with
+``s`` float32 ``[R]``, one scale per row (the production container's whole-row
+group); 2 = ``q`` int8 ``[R, K]`` (two's complement, element ``(r, c)`` at byte
+``(r, c)``) with ``s`` float32 ``[R]`` (the MTP layer's signed int8 experts).
+
 Distributions (N(0, v) names the variance v; the scale recipe's 0.02 is a
 standard deviation, the usual weight-init convention):
   x ~ N(0, 1) in fp32 (prefill: fp32 draw rounded RNE to bf16);
   router W ~ N(0, 1/H) fp32; bias ~ U(-0.1, 0.1) plus a workload skew;
-  int4 values uniform on [-8, 7]; scales |N(0, 0.02^2)| rounded RNE to fp16.
+  int4 values uniform on [-8, 7]; scales |N(0, 0.02^2)| rounded RNE to fp16;
+  row-scaled int4: the same nibbles, scales |N(0, 0.02^2)| in fp32; int8 values
+  uniform on [-128, 127], scales |N(0, (0.02/16)^2)| in fp32 (about the int4
+  experts' output magnitude).
 """
 from __future__ import annotations
 
@@ -162,6 +170,7 @@ class LayerConfig:
     group_size: int = 32
     routed_scaling_factor: float = 2.5
     norm_topk_prob: int = 1
+    weight_format: int = 0        # 0: int4 + fp16 per 32; 1: int4 + fp32 per row; 2: int8 + fp32 per row
 
 
 @dataclass(frozen=True)
@@ -249,18 +258,28 @@ class ExpertWeights:
     su: np.ndarray
     qd: np.ndarray
     sd: np.ndarray
+    fmt: int = 0
 
     def parts(self):
         return (self.qg, self.sg, self.qu, self.su, self.qd, self.sd)
 
 
 def empty_expert(cfg: LayerConfig, inter: int) -> ExpertWeights:
-    H, g = cfg.hidden, cfg.group_size
+    H, g, f = cfg.hidden, cfg.group_size, cfg.weight_format
+    if f == 0:
+        return ExpertWeights(
+            inter,
+            np.empty((inter, H // 2), np.uint8), np.empty((inter, H // g), np.uint16),
+            np.empty((inter, H // 2), np.uint8), np.empty((inter, H // g), np.uint16),
+            np.empty((H, inter // 2), np.uint8), np.empty((H, inter // g), np.uint16),
+        )
+    qt, d = (np.uint8, 2) if f == 1 else (np.int8, 1)
     return ExpertWeights(
         inter,
-        np.empty((inter, H // 2), np.uint8), np.empty((inter, H // g), np.uint16),
-        np.empty((inter, H // 2), np.uint8), np.empty((inter, H // g), np.uint16),
-        np.empty((H, inter // 2), np.uint8), np.empty((H, inter // g), np.uint16),
+        np.empty((inter, H // d), qt), np.empty(inter, np.float32),
+        np.empty((inter, H // d), qt), np.empty(inter, np.float32),
+        np.empty((H, inter // d), qt), np.empty(H, np.float32),
+        f,
     )
 
 
@@ -283,8 +302,11 @@ def expert_weights(w: Workload, layer: int, e: int, out: ExpertWeights | None = 
     bl, be = blob_of(w, layer, e)
     for part, arr in enumerate(ex.parts()):
         k = key(w.seed, KIND_EXPERT, bl, be, part)
-        if arr.dtype == np.uint8:
-            fill_bytes(k, arr)
-        else:
+        if arr.dtype in (np.uint8, np.int8):
+            fill_bytes(k, arr.view(np.uint8))
+        elif arr.dtype == np.uint16:
             absnormal_f16_bits(k, arr, 0.02)
+        else:  # fp32 row scales
+            lib().synth_fill_normal_f32(k, arr.size, 0.02 / 16 if c.weight_format == 2 else 0.02, _ptr(arr))
+            np.abs(arr, out=arr)
     return ex

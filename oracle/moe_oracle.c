@@ -31,6 +31,12 @@
  *  R4 SwiGLU expert: h = silu(Wg x) * (Wu x), y_e = Wd h, silu(z) = z/(1+e^-z);
  *     no biases, no clamp.  Shared expert has weight 1, added after the routed sum.
  *  R5 int4 scales are fp16, one per 32 consecutive elements along the contraction.
+ *  R6 weight formats ([PORT] "G2 implementation status", "G3 implementation
+ *     status", "G4"): fmt 0 = int4, fp16 scale per 32 elements (R5); fmt 1 = int4
+ *     with one fp32 scale per row (the production container's whole-row group:
+ *     the group size is the row length); fmt 2 = signed int8 (two's complement
+ *     bytes) with one fp32 scale per row (the MTP layer's routed experts).  In
+ *     every format W[r,c] = q[r,c] * scale, exact in fp64.
  *
  * Parity pins: tests/test_oracle_pins.py (brute force, closed forms, invariants).
  */
@@ -82,6 +88,23 @@ void oracle_dequant(int R, int K, int gsz, const uint8_t *q, const uint16_t *s, 
     for (int c = 0; c < K; ++c)
       out[(size_t)r * K + c] =
           (double)q_of(q + (size_t)r * (K / 2), c) * oracle_f16_to_f64(s[(size_t)r * (K / gsz) + c / gsz]);
+}
+
+/* One weight W[r,c] of an R x K matrix in format fmt (R6); q is the matrix's
+ * bytes (K/2 per row for int4, K for int8), s its scales (fp16 bits [R, K/gsz]
+ * for fmt 0, fp32 [R] otherwise). */
+static double w_at(int fmt, int K, int gsz, const uint8_t *q, const void *s, int r, int c) {
+  if (fmt == 0)
+    return (double)q_of(q + (size_t)r * (K / 2), c) * oracle_f16_to_f64(((const uint16_t *)s)[(size_t)r * (K / gsz) + c / gsz]);
+  double scale = (double)((const float *)s)[r];
+  if (fmt == 1) return (double)q_of(q + (size_t)r * (K / 2), c) * scale;
+  return (double)(int8_t)q[(size_t)r * K + c] * scale;
+}
+
+/* Dequantised [R, K] matrix in any format. */
+void oracle_dequant_fmt(int fmt, int R, int K, int gsz, const uint8_t *q, const void *s, double *out) {
+  for (int r = 0; r < R; ++r)
+    for (int c = 0; c < K; ++c) out[(size_t)r * K + c] = w_at(fmt, K, gsz, q, s, r, c);
 }
 
 /* ------------------------------------------------------------------ router */
@@ -243,45 +266,46 @@ int oracle_route(int S, int H, int E, int G, int Gk, int k, double rsf, int norm
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
 /* y[H] = Wd (silu(Wg x) * (Wu x)) for one token, fp64.  Matrices in the
- * interchange layout: gate/up [I, H], down [H, I], nibbles + fp16 group scales.
+ * interchange layout of format fmt (R6): gate/up [I, H], down [H, I].
  * h_out (optional) receives the [I] hidden activation. */
-void oracle_expert_ffn(int H, int I, int gsz, const uint8_t *qg, const uint16_t *sg, const uint8_t *qu,
-                       const uint16_t *su, const uint8_t *qd, const uint16_t *sd, const double *x, double *y,
-                       double *h_out) {
+void oracle_expert_ffn_fmt(int fmt, int H, int I, int gsz, const uint8_t *qg, const void *sg, const uint8_t *qu,
+                           const void *su, const uint8_t *qd, const void *sd, const double *x, double *y,
+                           double *h_out) {
   double *h = malloc(sizeof(double) * I);
 #pragma omp parallel for schedule(static)
   for (int r = 0; r < I; ++r) {
-    const uint8_t *rg = qg + (size_t)r * (H / 2), *ru = qu + (size_t)r * (H / 2);
     double g = 0.0, u = 0.0;
     for (int c = 0; c < H; ++c) {
-      double wg = (double)q_of(rg, c) * oracle_f16_to_f64(sg[(size_t)r * (H / gsz) + c / gsz]);
-      double wu = (double)q_of(ru, c) * oracle_f16_to_f64(su[(size_t)r * (H / gsz) + c / gsz]);
-      g += wg * x[c];
-      u += wu * x[c];
+      g += w_at(fmt, H, gsz, qg, sg, r, c) * x[c];
+      u += w_at(fmt, H, gsz, qu, su, r, c) * x[c];
     }
     h[r] = silu(g) * u;
   }
 #pragma omp parallel for schedule(static)
   for (int r = 0; r < H; ++r) {
-    const uint8_t *rd = qd + (size_t)r * (I / 2);
     double acc = 0.0;
-    for (int c = 0; c < I; ++c)
-      acc += (double)q_of(rd, c) * oracle_f16_to_f64(sd[(size_t)r * (I / gsz) + c / gsz]) * h[c];
+    for (int c = 0; c < I; ++c) acc += w_at(fmt, I, gsz, qd, sd, r, c) * h[c];
     y[r] = acc;
   }
   if (h_out) memcpy(h_out, h, sizeof(double) * I);
   free(h);
 }
 
+void oracle_expert_ffn(int H, int I, int gsz, const uint8_t *qg, const uint16_t *sg, const uint8_t *qu,
+                       const uint16_t *su, const uint8_t *qd, const uint16_t *sd, const double *x, double *y,
+                       double *h_out) {
+  oracle_expert_ffn_fmt(0, H, I, gsz, qg, sg, qu, su, qd, sd, x, y, h_out);
+}
+
 /* The layer for S tokens given routing (idx, w):
  *   y[t] = sum_j w[t,j] * FFN_{idx[t,j]}(x_t)  (rank order)  +  FFN_shared(x_t).
  * Expert e's six parts are qg[e], sg[e], ... (pointer arrays of length E+1; entry E
  * is the shared expert, NULL when the layer has none).  Only experts that the
- * routing names need non-NULL pointers. */
-int oracle_moe_ffn(int S, int H, int E, int k, int I, int Is, int gsz, int x_is_bf16, const void *x,
-                   const int32_t *idx, const double *w, const uint8_t *const *qg, const uint16_t *const *sg,
-                   const uint8_t *const *qu, const uint16_t *const *su, const uint8_t *const *qd,
-                   const uint16_t *const *sd, double *y) {
+ * routing names need non-NULL pointers.  Every expert is in format fmt (R6). */
+int oracle_moe_ffn_fmt(int fmt, int S, int H, int E, int k, int I, int Is, int gsz, int x_is_bf16, const void *x,
+                       const int32_t *idx, const double *w, const uint8_t *const *qg, const void *const *sg,
+                       const uint8_t *const *qu, const void *const *su, const uint8_t *const *qd,
+                       const void *const *sd, double *y) {
   double *xt = malloc(sizeof(double) * H), *ye = malloc(sizeof(double) * H), *acc = malloc(sizeof(double) * H);
   int rc = 0;
   for (int t = 0; t < S && !rc; ++t) {
@@ -290,19 +314,27 @@ int oracle_moe_ffn(int S, int H, int E, int k, int I, int Is, int gsz, int x_is_
     for (int j = 0; j < k; ++j) {
       int e = idx[(size_t)t * k + j];
       if (e < 0 || e >= E || !qg[e] || !sg[e] || !qu[e] || !su[e] || !qd[e] || !sd[e]) { rc = -1; break; }
-      oracle_expert_ffn(H, I, gsz, qg[e], sg[e], qu[e], su[e], qd[e], sd[e], xt, ye, NULL);
+      oracle_expert_ffn_fmt(fmt, H, I, gsz, qg[e], sg[e], qu[e], su[e], qd[e], sd[e], xt, ye, NULL);
       for (int c = 0; c < H; ++c) acc[c] += w[(size_t)t * k + j] * ye[c];
     }
     if (rc) break;
     if (Is > 0) {
       if (!qg[E]) { rc = -1; break; }
-      oracle_expert_ffn(H, Is, gsz, qg[E], sg[E], qu[E], su[E], qd[E], sd[E], xt, ye, NULL);
+      oracle_expert_ffn_fmt(fmt, H, Is, gsz, qg[E], sg[E], qu[E], su[E], qd[E], sd[E], xt, ye, NULL);
       for (int c = 0; c < H; ++c) acc[c] += ye[c];
     }
     for (int c = 0; c < H; ++c) y[(size_t)t * H + c] = acc[c];
   }
   free(xt); free(ye); free(acc);
   return rc;
+}
+
+int oracle_moe_ffn(int S, int H, int E, int k, int I, int Is, int gsz, int x_is_bf16, const void *x,
+                   const int32_t *idx, const double *w, const uint8_t *const *qg, const uint16_t *const *sg,
+                   const uint8_t *const *qu, const uint16_t *const *su, const uint8_t *const *qd,
+                   const uint16_t *const *sd, double *y) {
+  return oracle_moe_ffn_fmt(0, S, H, E, k, I, Is, gsz, x_is_bf16, x, idx, w, qg, (const void *const *)sg, qu,
+                            (const void *const *)su, qd, (const void *const *)sd, y);
 }
 
 int oracle_num_threads(void) {

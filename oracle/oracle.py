@@ -53,6 +53,12 @@ def lib():
         L.oracle_expert_ffn.argtypes = [i, i, i, p, p, p, p, p, p, p, p, p]
         L.oracle_moe_ffn.restype = i
         L.oracle_moe_ffn.argtypes = [i] * 8 + [p] * 10
+        L.oracle_dequant_fmt.restype = None
+        L.oracle_dequant_fmt.argtypes = [i, i, i, i, p, p, p]
+        L.oracle_expert_ffn_fmt.restype = None
+        L.oracle_expert_ffn_fmt.argtypes = [i, i, i, i, p, p, p, p, p, p, p, p, p]
+        L.oracle_moe_ffn_fmt.restype = i
+        L.oracle_moe_ffn_fmt.argtypes = [i] * 9 + [p] * 10
         L.oracle_num_threads.restype = i
         _lib = L
     return _lib
@@ -78,6 +84,16 @@ def dequant(q: np.ndarray, s: np.ndarray, gsz: int = 32) -> np.ndarray:
     K = q.shape[1] * 2
     out = np.empty((R, K), np.float64)
     lib().oracle_dequant(R, K, gsz, _p(np.ascontiguousarray(q)), _p(np.ascontiguousarray(s)), _p(out))
+    return out
+
+
+def dequant_fmt(fmt: int, q: np.ndarray, s: np.ndarray, gsz: int = 32) -> np.ndarray:
+    """[R, K] fp64 weights of a matrix in weight format ``fmt`` (0: int4 + fp16 per
+    ``gsz``; 1: int4 + fp32 per row; 2: int8 + fp32 per row)."""
+    R = q.shape[0]
+    K = q.shape[1] if fmt == 2 else q.shape[1] * 2
+    out = np.empty((R, K), np.float64)
+    lib().oracle_dequant_fmt(fmt, R, K, gsz, _p(np.ascontiguousarray(q)), _p(np.ascontiguousarray(s)), _p(out))
     return out
 
 
@@ -123,7 +139,8 @@ def expert_ffn(ex, x: np.ndarray, H: int, gsz: int = 32, return_h: bool = False)
     x = np.ascontiguousarray(x, np.float64)
     y = np.empty(H, np.float64)
     h = np.empty(I, np.float64)
-    lib().oracle_expert_ffn(H, I, gsz, *[_p(np.ascontiguousarray(a)) for a in ex.parts()], _p(x), _p(y), _p(h))
+    lib().oracle_expert_ffn_fmt(ex.fmt, H, I, gsz, *[_p(np.ascontiguousarray(a)) for a in ex.parts()], _p(x), _p(y),
+                                _p(h))
     return (y, h) if return_h else y
 
 
@@ -133,6 +150,10 @@ def moe_ffn(cfg, x: np.ndarray, idx: np.ndarray, w: np.ndarray, experts: dict, x
     S, H = x.shape
     E, k = cfg.n_experts, cfg.top_k
     arrs = [[None] * (E + 1) for _ in range(6)]
+    fmts = {ex.fmt for ex in experts.values()}
+    if len(fmts) > 1:
+        raise ValueError("oracle_moe_ffn: experts in mixed weight formats")
+    fmt = fmts.pop() if fmts else 0
     for e, ex in experts.items():
         for j, a in enumerate(ex.parts()):
             arrs[j][e] = _p(np.ascontiguousarray(a))
@@ -141,8 +162,8 @@ def moe_ffn(cfg, x: np.ndarray, idx: np.ndarray, w: np.ndarray, experts: dict, x
     x = np.ascontiguousarray(x)
     idx = np.ascontiguousarray(idx, np.int32)
     w = np.ascontiguousarray(w, np.float64)
-    rc = lib().oracle_moe_ffn(S, H, E, k, cfg.moe_inter, cfg.shared_inter, cfg.group_size, int(x_is_bf16),
-                              _p(x), _p(idx), _p(w), *[ctypes.cast(pp, ctypes.c_void_p) for pp in ptrs], _p(y))
+    rc = lib().oracle_moe_ffn_fmt(fmt, S, H, E, k, cfg.moe_inter, cfg.shared_inter, cfg.group_size, int(x_is_bf16),
+                                  _p(x), _p(idx), _p(w), *[ctypes.cast(pp, ctypes.c_void_p) for pp in ptrs], _p(y))
     if rc:
         raise ValueError("oracle_moe_ffn: routing names an expert without weights")
     return y

@@ -340,3 +340,115 @@ def test_missing_expert_is_an_error():
     idx = np.array([[0, 1]], np.int32)
     with pytest.raises(ValueError):
         O.moe_ffn(c, x, idx, np.ones((1, 2)), {0: gen.expert_weights(w, 0, 0)})
+
+
+# ------------------------------------------------------ row-scaled weight formats
+# Format 1 is Colibri's production int4 container (one fp32 scale per row,
+# "G3 implementation status"), format 2 the MTP layer's signed int8 experts
+# ("G4"); "G2 implementation status" states that repeating a row's scale over
+# 32-element groups leaves every dequantised value unchanged.
+
+def fmt_cfg(fmt, **kw):
+    return gen.LayerConfig(**{**gen.TINY.__dict__, "weight_format": fmt, **kw})
+
+
+def as_group_scaled(ex):
+    """A format-1 expert whose scales are fp16-representable, as format 0 with the
+    row scale repeated over every 32-element group."""
+    parts = []
+    for q, s in ((ex.qg, ex.sg), (ex.qu, ex.su), (ex.qd, ex.sd)):
+        h = gen.encode_f16(s.astype(np.float64))
+        assert np.array_equal(h.view(np.float16).astype(np.float32), s)  # representable
+        parts += [q, np.repeat(h[:, None], q.shape[1] * 2 // 32, axis=1)]
+    return gen.ExpertWeights(ex.inter, *parts)
+
+
+def row_expert_fp16_scales(seed, fmt=1):
+    c = fmt_cfg(fmt)
+    ex = gen.expert_weights(gen.WORKLOADS["tiny"].with_(cfg=c, seed=seed), 0, 2)
+    for s in (ex.sg, ex.su, ex.sd):  # round the scales to fp16 values, kept in fp32
+        s[:] = gen.encode_f16(s.astype(np.float64)).view(np.float16).astype(np.float32)
+    return c, ex
+
+
+def test_row_scale_is_repeated_group_scale():
+    c, ex = row_expert_fp16_scales(11)
+    g = as_group_scaled(ex)
+    for (q, s), (q0, s0) in zip(((ex.qg, ex.sg), (ex.qu, ex.su), (ex.qd, ex.sd)),
+                                ((g.qg, g.sg), (g.qu, g.su), (g.qd, g.sd))):
+        assert np.array_equal(O.dequant_fmt(1, q, s), O.dequant(q0, s0))
+    x = gen.tokens(gen.WORKLOADS["tiny"])[0].astype(np.float64)
+    y1, h1 = O.expert_ffn(ex, x, c.hidden, return_h=True)
+    y0, h0 = O.expert_ffn(g, x, c.hidden, return_h=True)
+    assert np.array_equal(h1, h0) and np.array_equal(y1, y0)
+
+
+def test_row_scale_layer_equals_group_scale_layer():
+    w = gen.WORKLOADS["tiny"].with_(tokens=3)
+    c1 = fmt_cfg(1)
+    x = gen.tokens(w)
+    idx, wt, _, _, _ = O.route(c1, x, gen.router_weights(w), gen.router_bias(w))
+    ex1, ex0 = {}, {}
+    for e in set(idx.ravel().tolist()) | {c1.n_experts}:
+        _, ex = row_expert_fp16_scales(100 + e)
+        ex1[e], ex0[e] = ex, as_group_scaled(ex)
+    assert np.array_equal(O.moe_ffn(c1, x, idx, wt, ex1), O.moe_ffn(w.cfg, x, idx, wt, ex0))
+
+
+def test_int8_every_byte_and_row_scale():
+    q = np.arange(256, dtype=np.uint8).reshape(1, 256).repeat(3, axis=0).view(np.int8)
+    s = np.array([1.0, 0.5, 3.0], np.float32)
+    got = O.dequant_fmt(2, q, s)
+    two = np.array([b if b < 128 else b - 256 for b in range(256)], np.float64)  # two's complement
+    assert np.array_equal(got, np.stack([two, two * 0.5, two * 3.0]))
+
+
+def test_int8_small_values_equal_int4_row_format():
+    rng = np.random.default_rng(9)
+    v = rng.integers(-8, 8, (6, 64))
+    q8 = v.astype(np.int8)
+    q4 = ((v[:, 0::2] + 8) | ((v[:, 1::2] + 8) << 4)).astype(np.uint8)  # offset-binary nibbles
+    s = np.abs(rng.normal(0, 0.02, 6)).astype(np.float32)
+    assert np.array_equal(O.dequant_fmt(2, q8, s), O.dequant_fmt(1, q4, s))
+
+
+def test_int8_expert_one_hot_closed_form():
+    """One nonzero weight per row: every output is a closed form of a few scalars."""
+    c = fmt_cfg(2)
+    H, I = c.hidden, c.moe_inter
+    rng = np.random.default_rng(13)
+    ex = gen.empty_expert(c, I)
+    for q in (ex.qg, ex.qu, ex.qd):
+        q[:] = 0
+    cg, cu, cd = rng.integers(0, H, I), rng.integers(0, H, I), rng.integers(0, I, H)
+    ag, au, ad = rng.integers(-128, 128, I), rng.integers(-128, 128, I), rng.integers(-128, 128, H)
+    ex.qg[np.arange(I), cg] = ag
+    ex.qu[np.arange(I), cu] = au
+    ex.qd[np.arange(H), cd] = ad
+    for s in (ex.sg, ex.su, ex.sd):
+        s[:] = np.abs(rng.normal(0, 0.01, s.size)).astype(np.float32)
+    x = rng.normal(0, 1, H)
+    y, h = O.expert_ffn(ex, x, H, return_h=True)
+    for r in range(I):
+        g = float(ag[r]) * float(ex.sg[r]) * x[cg[r]]
+        u = float(au[r]) * float(ex.su[r]) * x[cu[r]]
+        assert h[r] == pytest.approx(g / (1.0 + math.exp(-g)) * u, rel=1e-14, abs=1e-300)
+    for j in range(H):
+        assert y[j] == pytest.approx(float(ad[j]) * float(ex.sd[j]) * h[cd[j]], rel=1e-14, abs=1e-300)
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_row_scale_power_of_two_is_exact(fmt):
+    """Doubling every down-row scale doubles y exactly; doubling one gate row's
+    scale changes only that row's h."""
+    c = fmt_cfg(fmt)
+    ex = gen.expert_weights(gen.WORKLOADS["tiny"].with_(cfg=c), 0, 4)
+    x = gen.tokens(gen.WORKLOADS["tiny"])[0].astype(np.float64)
+    y, h = O.expert_ffn(ex, x, c.hidden, return_h=True)
+    ex2 = gen.ExpertWeights(ex.inter, ex.qg, ex.sg.copy(), ex.qu, ex.su, ex.qd, ex.sd * 2, fmt)
+    ex2.sg[5] *= 2
+    y2, h2 = O.expert_ffn(ex2, x, c.hidden, return_h=True)
+    changed = np.nonzero(h2 != h)[0]
+    assert list(changed) == [5]
+    ex3 = gen.ExpertWeights(ex.inter, ex.qg, ex.sg, ex.qu, ex.su, ex.qd, ex.sd * 2, fmt)
+    assert np.array_equal(O.expert_ffn(ex3, x, c.hidden), 2 * y)
