@@ -57,12 +57,24 @@ enum moe_status {
 
 enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
 
+/* Expert weight formats (moe_cfg.weight_format).  In each, W[r,c] = q[r,c] * scale:
+ *  MOE_WF_Q4_G32: int4, fp16 scale per 32 consecutive elements of a row (the
+ *                 grouped-int4 container);
+ *  MOE_WF_Q4_ROW: int4, one fp32 scale per row ([PORT] "G2 implementation
+ *                 status": Colibri's production Q4 format, whose group is the
+ *                 whole row; "G3 implementation status": 18,939,904 B per GLM-5.2
+ *                 expert there, nibbles and fp32 row scales in page-aligned parts);
+ *  MOE_WF_Q8_ROW: signed int8, one fp32 scale per row ([PORT] "G4": the MTP
+ *                 layer's signed-Q8 routed experts; [README] "What's implemented":
+ *                 int8 and packed int4 with per-row scales). */
+enum moe_weight_format { MOE_WF_Q4_G32 = 0, MOE_WF_Q4_ROW = 1, MOE_WF_Q8_ROW = 2 };
+
 /* Layer constants.  Limits checked by moe_validate_cfg:
  *  hidden H, moe_inter I, shared_inter Is: multiples of 32, H and I in [32, 8192],
  *  Is = 0 (no shared expert) or in [32, 8192]; group_size = 32;
  *  1 <= n_experts E <= 1024, n_group G divides E, 1 <= topk_group Gk <= G <= 64,
  *  1 <= top_k k <= min(16, Gk * E / G); norm_topk_prob 0 or 1;
- *  routed_scaling_factor finite. */
+ *  routed_scaling_factor finite; weight_format a moe_weight_format. */
 typedef struct moe_cfg {
   int32_t hidden;
   int32_t n_experts;
@@ -79,6 +91,8 @@ typedef struct moe_cfg {
    * rounded to bf16, weights dequantised to bf16, fp32 accumulation); the others
    * keep the exact fp32 path.  0 disables the matrix-core path.  >= 0. */
   int32_t mfma_min_tokens;
+  /* moe_weight_format of every expert of the layer (routed and shared). */
+  int32_t weight_format;
 } moe_cfg;
 
 /* Where the routed experts live.  Expert e's packed weights start at
@@ -133,6 +147,22 @@ int moe_pack_expert(const moe_cfg *cfg, int32_t inter, const uint8_t *q_gate, co
 int moe_unpack_expert(const moe_cfg *cfg, int32_t inter, const void *src, uint8_t *q_gate, uint16_t *s_gate,
                       uint8_t *q_up, uint16_t *s_up, uint8_t *q_down, uint16_t *s_down);
 
+/* moe_pack_expert for the row-scaled formats (cfg->weight_format MOE_WF_Q4_ROW or
+ * MOE_WF_Q8_ROW; MOE_EINVAL otherwise, and moe_pack_expert returns MOE_EINVAL
+ * for them).  Interchange format of an R x K matrix:
+ *   MOE_WF_Q4_ROW: q uint8 [R, K/2], offset-binary nibbles as for moe_pack_expert;
+ *   MOE_WF_Q8_ROW: q int8 [R, K], two's complement, element (r, c) at byte (r, c);
+ *   s: fp32 [R], the scale of row r.
+ * Gate and up are [inter, H], down is [H, inter]; dst receives
+ * moe_expert_bytes(cfg, inter) bytes; `where` and `stream` as for moe_pack_expert. */
+int moe_pack_expert_rows(const moe_cfg *cfg, int32_t inter, const void *q_gate, const float *s_gate,
+                         const void *q_up, const float *s_up, const void *q_down, const float *s_down, void *dst,
+                         int32_t where, void *stream);
+
+/* Inverse of moe_pack_expert_rows for host memory. */
+int moe_unpack_expert_rows(const moe_cfg *cfg, int32_t inter, const void *src, void *q_gate, float *s_gate,
+                           void *q_up, float *s_up, void *q_down, float *s_down);
+
 /* Router ([PORT] N1 and G2 status; [README] "What's implemented"; [MODELS] 4.3):
  *   l[t,e] = sum_h x[t,h] W_gate[e,h]         (fp64 accumulation)
  *   s = sigmoid(l) (fp64); key = fp32(s + bias)
@@ -158,11 +188,12 @@ int moe_route(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, con
  * experts: routed slots (host struct holding device pointers); shared: the packed
  * shared expert (moe_expert_bytes(cfg, shared_inter) bytes), ignored when
  * shared_inter = 0.  Out: y [S, H] fp32.  Arithmetic: each 32-element group's
- * dot product of int4 weights with the activations in block fixed point
- * (2^-22 of the group's largest |value|) is an exact integer, scaled once by
- * the group's scale and summed in fp32; larger batches use the same for experts
- * with fewer than mfma_min_tokens tokens and bf16 MFMA (fp32 accumulation) for
- * the others. */
+ * dot product of int4 (or int8) weights with the activations in block fixed
+ * point (2^-22 of the group's largest |value|) is an exact integer, rounded once
+ * to fp32, scaled by the group's scale (MOE_WF_Q4_G32) and summed in fp32; the
+ * row-scaled formats multiply the row's sum by its scale instead.  Larger
+ * batches use the same for experts with fewer than mfma_min_tokens tokens and
+ * bf16 MFMA (fp32 accumulation) for the others. */
 int moe_ffn(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, const int32_t *idx, const float *w,
             const moe_slot_view *experts, const void *shared, float *y, void *ws, size_t ws_bytes, void *stream);
 

@@ -133,7 +133,9 @@ int moe_validate_cfg(const moe_cfg *c) {
                   c->n_experts % c->n_group == 0 && c->topk_group >= 1 && c->topk_group <= c->n_group &&
                   c->top_k >= 1 && c->top_k <= kMaxK && c->top_k <= c->topk_group * (c->n_experts / c->n_group) &&
                   (c->norm_topk_prob == 0 || c->norm_topk_prob == 1) && std::isfinite(c->routed_scaling_factor) &&
-                  c->mfma_min_tokens >= 0;
+                  c->mfma_min_tokens >= 0 &&
+                  (c->weight_format == MOE_WF_Q4_G32 || c->weight_format == MOE_WF_Q4_ROW ||
+                   c->weight_format == MOE_WF_Q8_ROW);
   return ok ? MOE_OK : MOE_EINVAL;
 }
 
@@ -196,7 +198,7 @@ int64_t moe_expert_bytes(const moe_cfg *c, int32_t inter) {
   const int v = moe_validate_cfg(c);
   if (v) return v;
   if (inter < 32 || inter > 8192 || inter % 32) return MOE_EINVAL;
-  return slot_stride(c->hidden, inter);
+  return slot_stride(c->hidden, inter, c->weight_format);
 }
 
 size_t moe_workspace_bytes(const moe_cfg *c, int32_t max_S) {
@@ -217,7 +219,9 @@ int moe_pack_expert(const moe_cfg *c, int32_t inter, const uint8_t *qg, const ui
   if (nb < 0) return (int)nb;
   if (!qg || !sg || !qu || !su || !qd || !sd || !dst) return MOE_ENULL;
   if (where != 0 && where != 1) return MOE_EINVAL;
+  if (c->weight_format != MOE_WF_Q4_G32) return MOE_EINVAL;
   const int H = c->hidden, I = inter;
+  const int wf = kWfQ4G32;
   if (where == 1) {
     hipError_t e = launch_pack(H, I, qg, sg, qu, su, qd, sd, (uint8_t *)dst, (hipStream_t)stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e);
@@ -225,7 +229,7 @@ int moe_pack_expert(const moe_cfg *c, int32_t inter, const uint8_t *qg, const ui
   uint8_t *d = (uint8_t *)dst;
   const int ngh = H / kGroup, ngi = I / kGroup;
   for (int t = 0; t < I / kGuPairs; ++t) {
-    uint8_t *tile = d + (size_t)t * gu_tile_bytes(H);
+    uint8_t *tile = d + (size_t)t * gu_tile_bytes(H, wf);
     uint16_t *scl = (uint16_t *)(tile + (size_t)kGuRows * (H / 2));
     for (int i = 0; i < kGuRows; ++i) {
       const int r = kGuPairs * t + i / 2;
@@ -236,7 +240,7 @@ int moe_pack_expert(const moe_cfg *c, int32_t inter, const uint8_t *qg, const ui
     }
   }
   for (int t = 0; t < H / kDnRows; ++t) {
-    uint8_t *tile = d + down_offset(H, I) + (size_t)t * dn_tile_bytes(I);
+    uint8_t *tile = d + down_offset(H, I, wf) + (size_t)t * dn_tile_bytes(I, wf);
     uint16_t *scl = (uint16_t *)(tile + (size_t)kDnRows * (I / 2));
     for (int i = 0; i < kDnRows; ++i) {
       const int r = kDnRows * t + i;
@@ -244,7 +248,7 @@ int moe_pack_expert(const moe_cfg *c, int32_t inter, const uint8_t *qg, const ui
       for (int g = 0; g < ngi; ++g) scl[g * kDnRows + i] = sd[(size_t)r * ngi + g];
     }
   }
-  const size_t used = (size_t)packed_bytes(H, I);
+  const size_t used = (size_t)packed_bytes(H, I, wf);
   std::memset(d + used, 0, (size_t)nb - used);
   return MOE_OK;
 }
@@ -254,11 +258,13 @@ int moe_unpack_expert(const moe_cfg *c, int32_t inter, const void *src, uint8_t 
   const int64_t nb = moe_expert_bytes(c, inter);
   if (nb < 0) return (int)nb;
   if (!src || !qg || !sg || !qu || !su || !qd || !sd) return MOE_ENULL;
+  if (c->weight_format != MOE_WF_Q4_G32) return MOE_EINVAL;
   const int H = c->hidden, I = inter;
+  const int wf = kWfQ4G32;
   const uint8_t *d = (const uint8_t *)src;
   const int ngh = H / kGroup, ngi = I / kGroup;
   for (int t = 0; t < I / kGuPairs; ++t) {
-    const uint8_t *tile = d + (size_t)t * gu_tile_bytes(H);
+    const uint8_t *tile = d + (size_t)t * gu_tile_bytes(H, wf);
     const uint16_t *scl = (const uint16_t *)(tile + (size_t)kGuRows * (H / 2));
     for (int i = 0; i < kGuRows; ++i) {
       const int r = kGuPairs * t + i / 2;
@@ -269,7 +275,7 @@ int moe_unpack_expert(const moe_cfg *c, int32_t inter, const void *src, uint8_t 
     }
   }
   for (int t = 0; t < H / kDnRows; ++t) {
-    const uint8_t *tile = d + down_offset(H, I) + (size_t)t * dn_tile_bytes(I);
+    const uint8_t *tile = d + down_offset(H, I, wf) + (size_t)t * dn_tile_bytes(I, wf);
     const uint16_t *scl = (const uint16_t *)(tile + (size_t)kDnRows * (I / 2));
     for (int i = 0; i < kDnRows; ++i) {
       const int r = kDnRows * t + i;
@@ -277,6 +283,77 @@ int moe_unpack_expert(const moe_cfg *c, int32_t inter, const void *src, uint8_t 
       for (int g = 0; g < ngi; ++g) sd[(size_t)r * ngi + g] = scl[g * kDnRows + i];
     }
   }
+  return MOE_OK;
+}
+
+// Row-scaled formats: rows copied whole (int4 nibbles flipped between offset
+// binary and two's complement, int8 bytes as they are), 8 fp32 scales per tile.
+static void pack_rows_host(int H, int I, int wf, bool unpack, uint8_t *slot, uint8_t *qg, float *sg, uint8_t *qu,
+                           float *su, uint8_t *qd, float *sd) {
+  auto move = [&](uint8_t *packed, uint8_t *inter, size_t n) {
+    if (wf == kWfQ8Row) {
+      if (unpack) std::memcpy(inter, packed, n);
+      else std::memcpy(packed, inter, n);
+    } else {
+      if (unpack) copy_flip(inter, packed, n);
+      else copy_flip(packed, inter, n);
+    }
+  };
+  const int64_t rbh = row_bytes(H, wf), rbi = row_bytes(I, wf);
+  for (int t = 0; t < I / kGuPairs; ++t) {
+    uint8_t *tile = slot + (size_t)t * gu_tile_bytes(H, wf);
+    float *scl = (float *)(tile + (size_t)kGuRows * rbh);
+    for (int i = 0; i < kGuRows; ++i) {
+      const int r = kGuPairs * t + i / 2;
+      move(tile + (size_t)i * rbh, ((i & 1) ? qu : qg) + (size_t)r * rbh, (size_t)rbh);
+      float *s = (i & 1) ? su : sg;
+      if (unpack) s[r] = scl[i];
+      else scl[i] = s[r];
+    }
+  }
+  for (int t = 0; t < H / kDnRows; ++t) {
+    uint8_t *tile = slot + down_offset(H, I, wf) + (size_t)t * dn_tile_bytes(I, wf);
+    float *scl = (float *)(tile + (size_t)kDnRows * rbi);
+    for (int i = 0; i < kDnRows; ++i) {
+      const int r = kDnRows * t + i;
+      move(tile + (size_t)i * rbi, qd + (size_t)r * rbi, (size_t)rbi);
+      if (unpack) sd[r] = scl[i];
+      else scl[i] = sd[r];
+    }
+  }
+}
+
+int moe_pack_expert_rows(const moe_cfg *c, int32_t inter, const void *qg, const float *sg, const void *qu,
+                         const float *su, const void *qd, const float *sd, void *dst, int32_t where, void *stream) {
+  const int64_t nb = moe_expert_bytes(c, inter);
+  if (nb < 0) return (int)nb;
+  if (!qg || !sg || !qu || !su || !qd || !sd || !dst) return MOE_ENULL;
+  if (where != 0 && where != 1) return MOE_EINVAL;
+  const int wf = c->weight_format;
+  if (wf != kWfQ4Row && wf != kWfQ8Row) return MOE_EINVAL;
+  const int H = c->hidden, I = inter;
+  if (where == 1) {
+    hipError_t e = launch_pack_rows(H, I, wf, (const uint8_t *)qg, sg, (const uint8_t *)qu, su, (const uint8_t *)qd,
+                                    sd, (uint8_t *)dst, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+  }
+  uint8_t *d = (uint8_t *)dst;
+  pack_rows_host(H, I, wf, false, d, (uint8_t *)qg, (float *)sg, (uint8_t *)qu, (float *)su, (uint8_t *)qd,
+                 (float *)sd);
+  const size_t used = (size_t)packed_bytes(H, I, wf);
+  std::memset(d + used, 0, (size_t)nb - used);
+  return MOE_OK;
+}
+
+int moe_unpack_expert_rows(const moe_cfg *c, int32_t inter, const void *src, void *qg, float *sg, void *qu,
+                           float *su, void *qd, float *sd) {
+  const int64_t nb = moe_expert_bytes(c, inter);
+  if (nb < 0) return (int)nb;
+  if (!src || !qg || !sg || !qu || !su || !qd || !sd) return MOE_ENULL;
+  const int wf = c->weight_format;
+  if (wf != kWfQ4Row && wf != kWfQ8Row) return MOE_EINVAL;
+  pack_rows_host(c->hidden, inter, wf, true, (uint8_t *)src, (uint8_t *)qg, sg, (uint8_t *)qu, su, (uint8_t *)qd,
+                 sd);
   return MOE_OK;
 }
 
@@ -315,12 +392,15 @@ static int ffn_args(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S,
   if (S == 0) return MOE_OK;
   if (!x || !idx || !w || !ex || !y || !ws || !ex->base || !ex->table) return MOE_ENULL;
   if (c->shared_inter > 0 && !shared) return MOE_ENULL;
-  if (ex->n_slots < 1 || ex->slot_bytes < slot_stride(c->hidden, c->moe_inter) || ex->slot_bytes % 256) return MOE_EINVAL;
+  if (ex->n_slots < 1 || ex->slot_bytes < slot_stride(c->hidden, c->moe_inter, c->weight_format) ||
+      ex->slot_bytes % 256)
+    return MOE_EINVAL;
   const WsLayout L = ws_layout(*c, S);
   if (ws_bytes < L.total) return MOE_EWORKSPACE;
   a = FfnArgs{};
   a.H = c->hidden; a.E = c->n_experts; a.k = c->top_k; a.I = c->moe_inter; a.Is = c->shared_inter; a.S = S;
   a.x_bf16 = x_dtype == MOE_BF16;
+  a.wf = c->weight_format;
   a.x = x; a.idx = idx; a.w = w;
   a.base = (const uint8_t *)ex->base; a.slot_bytes = ex->slot_bytes; a.table = ex->table; a.n_slots = ex->n_slots;
   a.shared = (const uint8_t *)shared;

@@ -27,18 +27,29 @@ constexpr uint32_t kWsMagic0 = 0x6D6F6534u, kWsMagic1 = 0x77733031u;
 
 // ---- slot layout of one packed expert (inter = I, hidden = H) -------------
 // gate/up: I/4 tiles.  Tile t holds 8 rows, in order (g 4t, u 4t, g 4t+1, u 4t+1,
-// ..., g 4t+3, u 4t+3), each row H/2 bytes, then the tile's scales as
-// [H/32 groups][8 rows] fp16.
-// down: H/8 tiles.  Tile t holds rows 8t..8t+7 (I/2 bytes each), then scales
-// [I/32 groups][8 rows] fp16.
-// Element order within a row is the interchange order (element 2j in the low
-// nibble of byte j), but each nibble holds the int4 value in two's complement
-// (interchange nibble XOR 8), the operand format of v_dot8_i32_i4.
-__host__ __device__ inline int64_t gu_tile_bytes(int H) { return (int64_t)kGuRows * (H / 2) + (int64_t)(H / kGroup) * kGuRows * 2; }
-__host__ __device__ inline int64_t dn_tile_bytes(int I) { return (int64_t)kDnRows * (I / 2) + (int64_t)(I / kGroup) * kDnRows * 2; }
-__host__ __device__ inline int64_t down_offset(int H, int I) { return (int64_t)(I / kGuPairs) * gu_tile_bytes(H); }
-__host__ __device__ inline int64_t packed_bytes(int H, int I) { return down_offset(H, I) + (int64_t)(H / kDnRows) * dn_tile_bytes(I); }
-inline int64_t slot_stride(int H, int I) { return (packed_bytes(H, I) + 4095) / 4096 * 4096; }
+// ..., g 4t+3, u 4t+3), then the tile's scales.
+// down: H/8 tiles.  Tile t holds rows 8t..8t+7, then the tile's scales.
+// A row of K elements takes K/2 bytes (int4) or K bytes (int8).  Scales of a
+// tile: MOE_WF_Q4_G32 [K/32 groups][8 rows] fp16; the row-scaled formats 8 fp32
+// in the tile's row order.
+// int4 element order within a row is the interchange order (element 2j in the
+// low nibble of byte j), but each nibble holds the value in two's complement
+// (interchange nibble XOR 8), the operand format of v_dot8_i32_i4; int8
+// elements are the interchange bytes (two's complement, v_dot4_i32_i8's).
+constexpr int kWfQ4G32 = MOE_WF_Q4_G32, kWfQ4Row = MOE_WF_Q4_ROW, kWfQ8Row = MOE_WF_Q8_ROW;
+__host__ __device__ constexpr int64_t row_bytes(int K, int wf) { return wf == kWfQ8Row ? K : K / 2; }
+// bytes of one 32-element group of a row: 16 (int4) or 32 (int8)
+__host__ __device__ constexpr int group_bytes(int wf) { return wf == kWfQ8Row ? 32 : 16; }
+__host__ __device__ constexpr int64_t tile_scale_bytes(int K, int wf) {
+  return wf == kWfQ4G32 ? (int64_t)(K / kGroup) * 8 * 2 : 8 * 4;
+}
+__host__ __device__ inline int64_t gu_tile_bytes(int H, int wf) { return (int64_t)kGuRows * row_bytes(H, wf) + tile_scale_bytes(H, wf); }
+__host__ __device__ inline int64_t dn_tile_bytes(int I, int wf) { return (int64_t)kDnRows * row_bytes(I, wf) + tile_scale_bytes(I, wf); }
+__host__ __device__ inline int64_t down_offset(int H, int I, int wf) { return (int64_t)(I / kGuPairs) * gu_tile_bytes(H, wf); }
+__host__ __device__ inline int64_t packed_bytes(int H, int I, int wf) {
+  return down_offset(H, I, wf) + (int64_t)(H / kDnRows) * dn_tile_bytes(I, wf);
+}
+inline int64_t slot_stride(int H, int I, int wf) { return (packed_bytes(H, I, wf) + 4095) / 4096 * 4096; }
 
 // ---- kernel arguments -------------------------------------------------------
 struct RouteArgs {
@@ -57,6 +68,7 @@ struct RouteArgs {
 
 struct FfnArgs {
   int H, E, k, I, Is, S, x_bf16;
+  int wf;  // moe_weight_format
   const void *x;
   const int32_t *idx;
   const float *w;
@@ -136,9 +148,11 @@ hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st);   // S > kSmallS
 hipError_t launch_gu_mfma(const FfnArgs &a, hipStream_t st);
 hipError_t launch_dn_mfma(const FfnArgs &a, hipStream_t st);
 hipError_t launch_to_limbs(const void *src, int src_bf16, int rows, int K, int src_stride, uint32_t *limbs,
-                           float *factors, hipStream_t st);
+                           float *factors, int wf, hipStream_t st);
 hipError_t launch_pack(int H, int I, const uint8_t *qg, const uint16_t *sg, const uint8_t *qu, const uint16_t *su,
                        const uint8_t *qd, const uint16_t *sd, uint8_t *dst, hipStream_t st);
+hipError_t launch_pack_rows(int H, int I, int wf, const uint8_t *qg, const float *sg, const uint8_t *qu,
+                            const float *su, const uint8_t *qd, const float *sd, uint8_t *dst, hipStream_t st);
 
 // workspace layout (bytes, each region 256-aligned)
 struct WsLayout {

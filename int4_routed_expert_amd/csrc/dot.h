@@ -57,6 +57,12 @@ __device__ inline void stg<uint4>(void *p, const uint4 &v) {
   *(__attribute__((address_space(1))) u32x4_t *)p = w;
 }
 template <>
+__device__ inline void stg<float2>(void *p, const float2 &v) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t w = {v.x, v.y};
+  *(__attribute__((address_space(1))) f32x2_t *)p = w;
+}
+template <>
 __device__ inline void stg<float4>(void *p, const float4 &v) {
   const f32x4_t w = {v.x, v.y, v.z, v.w};
   *(__attribute__((address_space(1))) f32x4_t *)p = w;
@@ -158,6 +164,73 @@ __device__ inline float group_dot(const uint4 q, const Limbs &x) {
     for (int d = 0; d < 4; ++d) T = __builtin_amdgcn_sdot8((int)w[d], (int)x.L[l][d], T, false);
   }
   return (float)T;
+}
+
+// int8 weights (v_dot4_i32_i8) take the same block fixed point X_c with three
+// balanced base-256 digits d_l in [-128, 127] (X_c = sum_l 256^l d_l): with
+// Z = X + 0x808080 (0 <= Z < 2^24), digit l is z_l - 128, whose 8-bit two's
+// complement is z_l ^ 0x80, so Y = Z ^ 0x808080 holds the three digits of one
+// element and the limb words are a byte transpose of four Y.  Limb l of
+// elements 4m..4m+3 (element 4m+i in byte i, as the int8 weights) is stored at
+// L[2l + m/4][m%4]: the same 24 words as the int4 limbs.
+__device__ inline void to_limbs8(const float *v, Limbs &out) {
+  float m = 0.f;
+#pragma unroll
+  for (int c = 0; c < 32; ++c) m = fmaxf(m, fabsf(v[c]));
+  int E = 0;
+  (void)frexpf(m, &E);
+  const int sh = 22 - E;
+  out.f = ldexpf(1.0f, -sh);
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    uint32_t Y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Y[i] = ((uint32_t)((int)rintf(ldexpf(v[4 * d + i], sh)) + 0x808080)) ^ 0x808080u;
+#pragma unroll
+    for (int l = 0; l < 3; ++l) {
+      const uint32_t sel = (uint32_t)(l | ((l + 4) << 8));  // bytes: s1.l, s0.l
+      const uint32_t p01 = __builtin_amdgcn_perm(Y[1], Y[0], sel);
+      const uint32_t p23 = __builtin_amdgcn_perm(Y[3], Y[2], sel);
+      out.L[2 * l + d / 4][d % 4] = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+    }
+  }
+}
+
+template <int WF>
+__device__ inline void to_limbs_wf(const float *v, Limbs &out) {
+  if constexpr (WF == kWfQ8Row) to_limbs8(v, out);
+  else to_limbs(v, out);
+}
+
+// sum_c q_c X_c of one group of int8 weights (w0: elements 0..15, w1: 16..31):
+// three exact digit sums (|each| <= 32 * 128 * 128 = 2^19) combined exactly in
+// fp64 (|total| < 2^35) and rounded once to fp32.
+__device__ inline float group_dot8(const uint4 w0, const uint4 w1, const Limbs &x) {
+  const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  int T[3];
+#pragma unroll
+  for (int l = 0; l < 3; ++l) {
+    T[l] = 0;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) T[l] = __builtin_amdgcn_sdot4((int)w[m], (int)x.L[2 * l + m / 4][m % 4], T[l], false);
+  }
+  return (float)fma((double)T[2], 65536.0, (double)(T[1] * 256 + T[0]));
+}
+
+// Weights of one 32-element group of one row: one uint4 (int4) or two (int8).
+template <int WF>
+struct QGroup {
+  uint4 q[WF == kWfQ8Row ? 2 : 1];
+};
+template <int WF>
+__device__ inline void load_group(QGroup<WF> &g, const uint8_t *row, int grp) {
+  g.q[0] = ldg<uint4>(row + (size_t)grp * group_bytes(WF));
+  if constexpr (WF == kWfQ8Row) g.q[1] = ldg<uint4>(row + (size_t)grp * group_bytes(WF) + 16);
+}
+template <int WF>
+__device__ inline float qdot(const QGroup<WF> &g, const Limbs &x) {
+  if constexpr (WF == kWfQ8Row) return group_dot8(g.q[0], g.q[1], x);
+  else return group_dot(g.q[0], x);
 }
 
 // Packed weights of routed expert e through the slot table, or null when its

@@ -36,6 +36,7 @@ namespace moe {
 namespace {
 
 // ---- activations -> limbs (global), one thread per (row, group) ---------------
+template <int WF>
 __global__ __launch_bounds__(256) void k_to_limbs(const void *src, int bf16, int rows, int K, int stride,
                                                   uint32_t *limbs, float *factors) {
   const int ng = K / kGroup;
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(256) void k_to_limbs(const void *src, int bf16, int
   float v[32];
   load32(src, bf16, (size_t)r * stride + (size_t)g * kGroup, v);
   Limbs L;
-  to_limbs(v, L);
+  to_limbs_wf<WF>(v, L);
   uint4 *d = (uint4 *)(limbs + (size_t)i * 24);
 #pragma unroll
   for (int l = 0; l < 6; ++l) stg<uint4>(d + l, make_uint4(L.L[l][0], L.L[l][1], L.L[l][2], L.L[l][3]));
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(256) void k_to_limbs(const void *src, int bf16, int
 // experts from the router's scores and keys (EPT experts per thread); the
 // loads of the selection inputs go first, then the activations and the first
 // two shared-expert features, so that the selection overlaps them.
-template <int NG, int EPT>
+template <int NG, int WF, int EPT>
 __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
   extern __shared__ uint32_t lds[];  // x limbs [H/32][24], then factors [H/32]
   const int lane = threadIdx.x & 63;
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
   const int r0 = (int)(wid * Fr / W), r1 = (int)((wid + 1) * Fr / W);
   const int ns = s1 - s0, n = ns + (r1 - r0);
   const bool has_x = (int)threadIdx.x < ng;
-  GuFeat<NG> b0, b1, b2;
+  GuFeat<NG, WF> b0, b1, b2;
   uint64_t my_ptr = 0;
   float v[32];
   float *lf = (float *)(lds + (size_t)ng * 24);
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
   auto stage_x = [&]() {
     if (has_x) {
       Limbs L;
-      to_limbs(v, L);
+      to_limbs_wf<WF>(v, L);
       store_limbs(lds + (size_t)threadIdx.x * 24, lf + threadIdx.x, L);
     }
   };
@@ -161,8 +162,8 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
 // of h (staging that waits behind a long queue of weight requests would hold
 // the whole workgroup at the barrier), and after the barrier requests unit
 // m + 1 before it computes unit m.
-template <int NGD, bool HLDS>
-__global__ __launch_bounds__(kDnS1Waves * 64) void k_down_s1(FfnArgs a) {
+template <int NGD, int WF, bool HLDS>
+__global__ __launch_bounds__(dn_s1_waves(WF) * 64) void k_down_s1(FfnArgs a) {
   constexpr int MU = 3;  // units per wave per round
   __shared__ float part[kMaxK + 1][kDnRows * kDnMaxTb];
   __shared__ int s_idx[kMaxK];  // [0]: the token's idx row is invalid (combine poisons y)
@@ -197,11 +198,11 @@ __global__ __launch_bounds__(kDnS1Waves * 64) void k_down_s1(FfnArgs a) {
     r.t = t0 + (u - r.j * nb);
     r.valid = ex != nullptr;
     r.inter = (r.j == a.k && r.valid) ? a.Is : a.I;
-    r.dn = uniform_ptr((r.valid ? ex : a.base) + down_offset(a.H, r.inter));
+    r.dn = uniform_ptr((r.valid ? ex : a.base) + down_offset(a.H, r.inter, WF));
     return r;
   };
   auto unit_expert = [&](int u) { return min(u, U - 1) / nb; };
-  DnTile<NGD> q[2];
+  DnTile<NGD, WF> q[2];
   Unit un[2];
   // order of the first loads: the units' expert pointers, this thread's first
   // group of h, the first unit's tile, idx and w for the combine
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(kDnS1Waves * 64) void k_down_s1(FfnArgs a) {
   }
   if (use_h) {
     Limbs L;
-    to_limbs(hv0, L);
+    to_limbs_wf<WF>(hv0, L);
     store_limbs(hlds + (size_t)threadIdx.x * 24, hf_lds + threadIdx.x, L);
   }
   for (int i = threadIdx.x + blockDim.x; HLDS && i < NE * ngm; i += blockDim.x) {
@@ -229,12 +230,12 @@ __global__ __launch_bounds__(kDnS1Waves * 64) void k_down_s1(FfnArgs a) {
     h_group(i, use_h, v);
     if (use_h) {
       Limbs L;
-      to_limbs(v, L);
+      to_limbs_wf<WF>(v, L);
       store_limbs(hlds + (size_t)i * 24, hf_lds + i, L);
     }
   }
   __syncthreads();
-  auto compute = [&](const DnTile<NGD> &b, const Unit &uu) {
+  auto compute = [&](const DnTile<NGD, WF> &b, const Unit &uu) {
     const int ng = uu.inter / kGroup;
     Limbs hv[NGD];
 #pragma unroll
@@ -362,40 +363,64 @@ __device__ void build_small_plan(const FfnArgs &a, SmallPlan &p, const int32_t *
 }
 
 
-// One gate/up tile (4 features) for a set of tokens; x limbs from global.
-template <int NG>
+// One gate/up tile (4 features) for a set of tokens; x limbs from global.  The
+// tile's rows are taken RC at a time (int8: 4, so that the weights of a chunk
+// stay within the register file next to the activation limbs).
+template <int NG, int WF>
 __device__ inline void gateup_tile(const FfnArgs &a, const uint8_t *tile, int ntok, const int *toks, const int *pairs,
                                    int feat0, int inter_stride) {
+  constexpr int RC = WF == kWfQ8Row ? 4 : kGuRows;
   const int lane = threadIdx.x & 63, H = a.H, ng = H / kGroup;
-  uint4 q[kGuRows][NG], sc[NG];
-#pragma unroll
-  for (int j = 0; j < NG; ++j) {
-    const int g = min(lane + 64 * j, ng - 1);
-#pragma unroll
-    for (int i = 0; i < kGuRows; ++i) q[i][j] = ldg<uint4>(tile + (size_t)i * (H / 2) + g * 16);
-    sc[j] = ldg<uint4>(tile + (size_t)kGuRows * (H / 2) + g * 16);
-  }
-  for (int tt = 0; tt < ntok; ++tt) {
-    Limbs xv[NG];
+  const int64_t rb = row_bytes(H, WF);
+  const uint8_t *scp = tile + (size_t)kGuRows * rb;
+#pragma unroll 1
+  for (int r0 = 0; r0 < kGuRows; r0 += RC) {
+    QGroup<WF> q[RC][NG];
+    uint4 sc[NG];
+    float rs[RC];
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
       const int g = min(lane + 64 * j, ng - 1);
-      load_limbs_global(a.xl + ((size_t)toks[tt] * ng + g) * 24, a.xf + (size_t)toks[tt] * ng + g, xv[j]);
-      if (lane + 64 * j >= ng) xv[j].f = 0.f;
+#pragma unroll
+      for (int i = 0; i < RC; ++i) load_group(q[i][j], tile + (size_t)(r0 + i) * rb, g);
+      if constexpr (WF == kWfQ4G32) sc[j] = ldg<uint4>(scp + g * 16);
     }
-    float acc[kGuRows];
+    if constexpr (WF != kWfQ4G32) {
 #pragma unroll
-    for (int i = 0; i < kGuRows; ++i) acc[i] = 0.f;
+      for (int i = 0; i < RC; ++i) rs[i] = ldg<float>(scp + 4 * (r0 + i));
+    }
+    for (int tt = 0; tt < ntok; ++tt) {
+      Limbs xv[NG];
 #pragma unroll
-    for (int j = 0; j < NG; ++j)
+      for (int j = 0; j < NG; ++j) {
+        const int g = min(lane + 64 * j, ng - 1);
+        load_limbs_global(a.xl + ((size_t)toks[tt] * ng + g) * 24, a.xf + (size_t)toks[tt] * ng + g, xv[j]);
+        if (lane + 64 * j >= ng) xv[j].f = 0.f;
+      }
+      float acc[RC];
 #pragma unroll
-      for (int i = 0; i < kGuRows; ++i) acc[i] = fmaf(group_dot(q[i][j], xv[j]), scale_of(sc[j], i) * xv[j].f, acc[i]);
+      for (int i = 0; i < RC; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int i = 0; i < kGuRows; ++i) acc[i] = wave_sum_to63(acc[i]);
-    if (lane == 63)
-      stg<float4>(a.h + (size_t)pairs[tt] * inter_stride + feat0,
-                  make_float4(silu_mul(acc[0], acc[1]), silu_mul(acc[2], acc[3]), silu_mul(acc[4], acc[5]),
-                              silu_mul(acc[6], acc[7])));
+      for (int j = 0; j < NG; ++j)
+#pragma unroll
+        for (int i = 0; i < RC; ++i) {
+          if constexpr (WF == kWfQ4G32) acc[i] = fmaf(qdot(q[i][j], xv[j]), scale_of(sc[j], r0 + i) * xv[j].f, acc[i]);
+          else acc[i] = fmaf(qdot(q[i][j], xv[j]), xv[j].f, acc[i]);
+        }
+#pragma unroll
+      for (int i = 0; i < RC; ++i) {
+        acc[i] = wave_sum_to63(acc[i]);
+        if constexpr (WF != kWfQ4G32) acc[i] *= rs[i];
+      }
+      if (lane == 63) {
+        float *dst = a.h + (size_t)pairs[tt] * inter_stride + feat0 + r0 / 2;
+        if constexpr (RC == 8)
+          stg<float4>(dst, make_float4(silu_mul(acc[0], acc[1]), silu_mul(acc[2], acc[3]), silu_mul(acc[4], acc[5]),
+                                       silu_mul(acc[6], acc[7])));
+        else
+          stg<float2>(dst, make_float2(silu_mul(acc[0], acc[1]), silu_mul(acc[2], acc[3])));
+      }
+    }
   }
 }
 
@@ -423,7 +448,7 @@ constexpr int kGuSmallWaves = 8;  // waves per small-batch gate/up workgroup (on
 // one-token kernel's, so a token's h does not depend on the other tokens of
 // its batch.  Results park in lanes (value and h row) and are stored 64 at a
 // time.
-template <int NG>
+template <int NG, int WF>
 __global__ __launch_bounds__(kGuSmallWaves * 64) void k_gateup_small(FfnArgs a) {
   __shared__ SmallPlan plan;
   __shared__ const uint8_t *s_ptr[kSmallS * kMaxK];
@@ -443,9 +468,9 @@ __global__ __launch_bounds__(kGuSmallWaves * 64) void k_gateup_small(FfnArgs a) 
   const int W = gridDim.x * (blockDim.x >> 6), wid = blockIdx.x * (blockDim.x >> 6) + wave;
   const long Ps = (long)a.S * a.Is;
   const int sp0 = (int)(wid * Ps / W), ns = (int)((wid + 1) * Ps / W) - sp0;
-  GuFeat<NG> b0, b1, b2;
+  GuFeat<NG, WF> b0, b1, b2;
   int row0 = 0, row1 = 0, row2 = 0, tok0 = 0, tok1 = 0, tok2 = 0;  // slot tags: h row and token
-  auto shared_item = [&](GuFeat<NG> &b, int i, int &row, int &tok) {
+  auto shared_item = [&](GuFeat<NG, WF> &b, int i, int &row, int &tok) {
     const int p = sp0 + i, t = p / a.Is, f = p - t * a.Is;
     gu_row_load(b, a, a.shared, f, lane);
     tok = t;
@@ -466,19 +491,19 @@ __global__ __launch_bounds__(kGuSmallWaves * 64) void k_gateup_small(FfnArgs a) 
   if ((int)threadIdx.x < U) s_ptr[threadIdx.x] = expert_ptr(a, plan.uniq[threadIdx.x]);
   if (i0 < nx) {
     Limbs L;
-    to_limbs(v0, L);
+    to_limbs_wf<WF>(v0, L);
     store_limbs(xlds + (size_t)i0 * kXs, xf_lds + i0, L);
   }
   if (i1 < nx) {
     Limbs L;
-    to_limbs(v1, L);
+    to_limbs_wf<WF>(v1, L);
     store_limbs(xlds + (size_t)i1 * kXs, xf_lds + i1, L);
   }
   for (int i = threadIdx.x + 2 * blockDim.x; i < nx; i += blockDim.x) {  // S * H/32 > 2 * blockDim
     float v[32];
     load32(a.x, a.x_bf16, (size_t)i * kGroup, v);
     Limbs L;
-    to_limbs(v, L);
+    to_limbs_wf<WF>(v, L);
     store_limbs(xlds + (size_t)i * kXs, xf_lds + i, L);
   }
   __syncthreads();
@@ -487,7 +512,7 @@ __global__ __launch_bounds__(kGuSmallWaves * 64) void k_gateup_small(FfnArgs a) 
   if (n <= 0) return;
   int lc = 0;  // unique expert of the last union pair requested (a wave's pairs increase)
   // item i of the wave (clamped to its last one, so that loads are unconditional)
-  auto load_item = [&](GuFeat<NG> &b, int i, int &row, int &tok) {
+  auto load_item = [&](GuFeat<NG, WF> &b, int i, int &row, int &tok) {
     i = min(i, n - 1);
     if (i < ns) {
       shared_item(b, i, row, tok);
@@ -508,7 +533,7 @@ __global__ __launch_bounds__(kGuSmallWaves * 64) void k_gateup_small(FfnArgs a) 
   int xt = -1;  // token whose limbs are in xv
   float hout = 0.f;
   int prow = 0, c = 0;
-  auto finish = [&](const GuFeat<NG> &b, int row, int tok) {
+  auto finish = [&](const GuFeat<NG, WF> &b, int row, int tok) {
     if (tok != xt) {
       xt = tok;
 #pragma unroll
@@ -525,13 +550,22 @@ __global__ __launch_bounds__(kGuSmallWaves * 64) void k_gateup_small(FfnArgs a) 
       c = 0;
     }
   };
-  for (int i = 0; i < n; i += 3) {
-    load_item(b2, i + 2, row2, tok2);
-    finish(b0, row0, tok0);
-    load_item(b0, i + 3, row0, tok0);
-    if (i + 1 < n) finish(b1, row1, tok1);
-    load_item(b1, i + 4, row1, tok1);
-    if (i + 2 < n) finish(b2, row2, tok2);
+  if constexpr (WF != kWfQ8Row) {
+    for (int i = 0; i < n; i += 3) {
+      load_item(b2, i + 2, row2, tok2);
+      finish(b0, row0, tok0);
+      load_item(b0, i + 3, row0, tok0);
+      if (i + 1 < n) finish(b1, row1, tok1);
+      load_item(b1, i + 4, row1, tok1);
+      if (i + 2 < n) finish(b2, row2, tok2);
+    }
+  } else {  // int8 features are twice as large: two slots, one in flight while one is computed
+    for (int i = 0; i < n; i += 2) {
+      finish(b0, row0, tok0);
+      load_item(b0, i + 2, row0, tok0);
+      if (i + 1 < n) finish(b1, row1, tok1);
+      load_item(b1, i + 3, row1, tok1);
+    }
   }
   if (lane < c) stg<float>(a.h + prow, hout);
 }
@@ -549,7 +583,7 @@ __global__ __launch_bounds__(kGuSmallWaves * 64) void k_gateup_small(FfnArgs a) 
 // once, which leaves room for fewer tiles in flight).  The per-unit arithmetic
 // is the one-token kernel's.
 constexpr int kDnSmallWaves = 8;
-template <int NGD>
+template <int NGD, int WF>
 __global__ __launch_bounds__(kDnSmallWaves * 64) void k_down_small(FfnArgs a) {
   __shared__ SmallPlan plan;
   __shared__ const uint8_t *s_ptr[kSmallS * kMaxK + 1];
@@ -590,16 +624,16 @@ __global__ __launch_bounds__(kDnSmallWaves * 64) void k_down_small(FfnArgs a) {
     const uint8_t *ex = uniform_ptr(s_ptr[u]);
     un.valid = ex != nullptr;
     un.inter = (u == U && un.valid) ? a.Is : a.I;
-    un.dn = uniform_ptr((un.valid ? ex : a.base) + down_offset(a.H, un.inter));
+    un.dn = uniform_ptr((un.valid ? ex : a.base) + down_offset(a.H, un.inter, WF));
     return un;
   };
-  DnTile<NGD> q0, q1;
+  DnTile<NGD, WF> q0, q1;
   Unit u0 = unit_of(0), u1 = unit_of(1);
   dn_tile_load(q0, u0.dn, u0.inter, u0.t, u0.t + 1, lane);
   dn_tile_load(q1, u1.dn, u1.inter, u1.t, u1.t + 1, lane);
   Limbs hv[NGD];
   int hp = -1;  // pair whose h limbs are in hv
-  auto finish = [&](const DnTile<NGD> &b, const Unit &uu) {
+  auto finish = [&](const DnTile<NGD, WF> &b, const Unit &uu) {
     const int ngi = uu.inter / kGroup;
     if (uu.pair != hp) {
       hp = uu.pair;
@@ -608,7 +642,7 @@ __global__ __launch_bounds__(kDnSmallWaves * 64) void k_down_small(FfnArgs a) {
         const int g = min(lane + 64 * g2, ngi - 1);
         float v[32];
         load32(a.h, 0, (size_t)uu.pair * Imax + (size_t)g * kGroup, v);
-        to_limbs(v, hv[g2]);
+        to_limbs_wf<WF>(v, hv[g2]);
         if (lane + 64 * g2 >= ngi) hv[g2].f = 0.f;
       }
     }
@@ -621,8 +655,8 @@ __global__ __launch_bounds__(kDnSmallWaves * 64) void k_down_small(FfnArgs a) {
       stg<float4>(d + 1, uu.valid ? make_float4(acc[4], acc[5], acc[6], acc[7]) : make_float4(nan, nan, nan, nan));
     }
   };
-  if constexpr (NGD == 1) {  // three tiles: two in flight while one is computed
-    DnTile<NGD> q2;
+  if constexpr (NGD == 1 && WF != kWfQ8Row) {  // three tiles: two in flight while one is computed
+    DnTile<NGD, WF> q2;
     Unit u2;
     for (int i = 0; i < n; i += 3) {
       u2 = unit_of(i + 2);
@@ -635,7 +669,7 @@ __global__ __launch_bounds__(kDnSmallWaves * 64) void k_down_small(FfnArgs a) {
       dn_tile_load(q1, u1.dn, u1.inter, u1.t, u1.t + 1, lane);
       if (i + 2 < n) finish(q2, u2);
     }
-  } else {  // wider tiles (inter > 2048): two, to stay within the register file
+  } else {  // wider tiles (inter > 2048, or int8 weights): two, to stay within the register file
     for (int i = 0; i < n; i += 2) {
       finish(q0, u0);
       u0 = unit_of(i + 2);
@@ -802,7 +836,7 @@ __device__ inline int item_tokens(const FfnArgs &a, const int *it, int *toks, in
 // (token, rank) rows of h (inter/32 groups).  A token or row named by several
 // items is converted more than once, to the same values.  Grid-stride over
 // (item, token slot, group).
-template <bool X>
+template <bool X, int WF>
 __global__ __launch_bounds__(256) void k_item_limbs(FfnArgs a) {
   const int Imax = max(a.I, a.Is), ng = X ? a.H / kGroup : Imax / kGroup;
   const long n_it = a.n_items[0] + a.n_items[1], total = n_it * kTB * ng;
@@ -817,7 +851,7 @@ __global__ __launch_bounds__(256) void k_item_limbs(FfnArgs a) {
     if (X) load32(a.x, a.x_bf16, (size_t)row * a.H + (size_t)g * kGroup, v);
     else load32(a.h, 0, (size_t)row * Imax + (size_t)g * kGroup, v);
     Limbs L;
-    to_limbs(v, L);
+    to_limbs_wf<WF>(v, L);
     uint32_t *dl = (X ? a.xl : a.hl) + ((size_t)row * ng + g) * 24;
 #pragma unroll
     for (int l = 0; l < 6; ++l) stg<uint4>((uint4 *)dl + l, make_uint4(L.L[l][0], L.L[l][1], L.L[l][2], L.L[l][3]));
@@ -825,7 +859,7 @@ __global__ __launch_bounds__(256) void k_item_limbs(FfnArgs a) {
   }
 }
 
-template <int NG>
+template <int NG, int WF>
 __global__ __launch_bounds__(256) void k_gateup_items(FfnArgs a) {
   const int wave = threadIdx.x >> 6;
   const int nr = a.n_items[0], nsh = a.n_items[1];
@@ -841,11 +875,11 @@ __global__ __launch_bounds__(256) void k_gateup_items(FfnArgs a) {
     const int n = item_tokens(a, it, toks, pairs);
     const uint8_t *ex = it[0] == a.E ? a.shared : expert_ptr(a, it[0]);
     if (!ex) { poison_h(a, n, pairs, t * kGuPairs, Imax); continue; }
-    gateup_tile<NG>(a, uniform_ptr(ex + (size_t)t * gu_tile_bytes(a.H)), n, toks, pairs, t * kGuPairs, Imax);
+    gateup_tile<NG, WF>(a, uniform_ptr(ex + (size_t)t * gu_tile_bytes(a.H, WF)), n, toks, pairs, t * kGuPairs, Imax);
   }
 }
 
-template <int NGD>
+template <int NGD, int WF>
 __global__ __launch_bounds__(256) void k_down_items(FfnArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nr = a.n_items[0], nsh = a.n_items[1];
@@ -865,8 +899,8 @@ __global__ __launch_bounds__(256) void k_down_items(FfnArgs a) {
         for (int tt = 0; tt < n; ++tt) a.part[(size_t)pairs[tt] * a.H + rt * kDnRows + lane] = __builtin_nanf("");
       continue;
     }
-    DnTile<NGD> q;
-    dn_tile_load(q, uniform_ptr(ex + down_offset(a.H, inter)), inter, rt, rt + 1, lane);
+    DnTile<NGD, WF> q;
+    dn_tile_load(q, uniform_ptr(ex + down_offset(a.H, inter, WF)), inter, rt, rt + 1, lane);
     const int ng = inter / kGroup;
     for (int tt = 0; tt < n; ++tt) {
       const int pr = pairs[tt];
@@ -924,22 +958,32 @@ int ceil_groups(int K) { return (K / kGroup + 63) / 64; }
 }  // namespace
 
 hipError_t launch_to_limbs(const void *src, int src_bf16, int rows, int K, int src_stride, uint32_t *limbs,
-                           float *factors, hipStream_t st) {
+                           float *factors, int wf, hipStream_t st) {
   const long n = (long)rows * (K / kGroup);
   if (n == 0) return hipSuccess;
-  MOE_LAUNCH(k_to_limbs, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, src_bf16, rows, K,
-                     src_stride, limbs, factors);
+  const dim3 g((unsigned)((n + 255) / 256)), b(256);
+  if (wf == kWfQ8Row) MOE_LAUNCH(k_to_limbs<kWfQ8Row>, g, b, 0, st, src, src_bf16, rows, K, src_stride, limbs, factors);
+  else MOE_LAUNCH(k_to_limbs<kWfQ4G32>, g, b, 0, st, src, src_bf16, rows, K, src_stride, limbs, factors);
   return hipGetLastError();
 }
 
-#define MOE_DISPATCH_NG(ng, KERNEL, GRID, BLOCK, LDS, ST, ...)                                          \
-  switch (ng) {                                                                                         \
-    case 1: MOE_LAUNCH((KERNEL<1 __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;   \
-    case 2: MOE_LAUNCH((KERNEL<2 __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;   \
-    case 3: MOE_LAUNCH((KERNEL<3 __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;   \
-    default: MOE_LAUNCH((KERNEL<4 __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;  \
+// KERNEL<NG, WF, extra...> for NG = 1..4 groups per lane and the weight format.
+#define MOE_NG_CASES(NG_, WFV, KERNEL, GRID, BLOCK, LDS, ST, ...)                                       \
+  switch (NG_) {                                                                                      \
+    case 1: MOE_LAUNCH((KERNEL<1, WFV __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;   \
+    case 2: MOE_LAUNCH((KERNEL<2, WFV __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;   \
+    case 3: MOE_LAUNCH((KERNEL<3, WFV __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;   \
+    default: MOE_LAUNCH((KERNEL<4, WFV __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;  \
   }
-
+#define MOE_DISPATCH_NG(ng, KERNEL, GRID, BLOCK, LDS, ST, ...)                                       \
+  do {                                                                                               \
+    const int ng_ = (ng);                                                                            \
+    switch (a.wf) {                                                                                  \
+      case kWfQ4Row: MOE_NG_CASES(ng_, kWfQ4Row, KERNEL, GRID, BLOCK, LDS, ST, __VA_ARGS__); break;  \
+      case kWfQ8Row: MOE_NG_CASES(ng_, kWfQ8Row, KERNEL, GRID, BLOCK, LDS, ST, __VA_ARGS__); break;  \
+      default: MOE_NG_CASES(ng_, kWfQ4G32, KERNEL, GRID, BLOCK, LDS, ST, __VA_ARGS__); break;        \
+    }                                                                                                \
+  } while (0)
 hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st) {
   const int Imax = std::max(a.I, a.Is);
   hipError_t e;
@@ -965,11 +1009,11 @@ hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st) {
     const bool in_lds = hlds <= 64 * 1024;
     if (!in_lds) {
       ProfScope ps("h_limbs", st);
-      e = launch_to_limbs(a.h, 0, NE, Imax, Imax, a.hl, a.hf, st);
+      e = launch_to_limbs(a.h, 0, NE, Imax, Imax, a.hl, a.hf, a.wf, st);
       if (e != hipSuccess) return e;
     }
     ProfScope ps("down_s1", st);
-    const dim3 g((unsigned)a.n_blk), blk(64 * std::min(NE * a.tb, kDnS1Waves));
+    const dim3 g((unsigned)a.n_blk), blk(64 * std::min(NE * a.tb, dn_s1_waves(a.wf)));
     if (in_lds) {
       MOE_DISPATCH_NG(ceil_groups(Imax), k_down_s1, g, blk, hlds, st, true);
     } else {
@@ -1011,7 +1055,8 @@ hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st) {
   if (e != hipSuccess) return e;
   {
     ProfScope ps("x_limbs", st);
-    MOE_LAUNCH(k_item_limbs<true>, dim3((unsigned)a.n_cu * 4), dim3(256), 0, st, a);
+    if (a.wf == kWfQ8Row) MOE_LAUNCH((k_item_limbs<true, kWfQ8Row>), dim3((unsigned)a.n_cu * 4), dim3(256), 0, st, a);
+    else MOE_LAUNCH((k_item_limbs<true, kWfQ4G32>), dim3((unsigned)a.n_cu * 4), dim3(256), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1025,7 +1070,8 @@ hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st) {
   if (e != hipSuccess) return e;
   {
     ProfScope ps("h_limbs", st);
-    MOE_LAUNCH(k_item_limbs<false>, dim3((unsigned)a.n_cu * 4), dim3(256), 0, st, a);
+    if (a.wf == kWfQ8Row) MOE_LAUNCH((k_item_limbs<false, kWfQ8Row>), dim3((unsigned)a.n_cu * 4), dim3(256), 0, st, a);
+    else MOE_LAUNCH((k_item_limbs<false, kWfQ4G32>), dim3((unsigned)a.n_cu * 4), dim3(256), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -80,6 +80,16 @@ __device__ inline uint4 dequant8(uint32_t w, float s) {
   return make_uint4(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7]));
 }
 
+// Eight int8 weights (two dwords, element 4m+i in byte i of dword m) times the
+// row scale, as eight bf16: q * s rounded to fp32, then to bf16 (RNE).
+__device__ inline uint4 dequant8_i8(uint32_t w0, uint32_t w1, float s) {
+  const uint32_t d[2] = {w0, w1};
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = (float)(int8_t)(d[j >> 2] >> (8 * (j & 3))) * s;
+  return make_uint4(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7]));
+}
+
 // Eight consecutive activations, raw: bf16 bits, or fp32 values that become
 // bf16 (RNE) only where they are used, so that a prefetch does not wait.
 template <bool ABF>
@@ -159,7 +169,7 @@ __device__ inline void group_mfma(GemmAcc &C, const bf16x8 (&A)[kMB], const uint
   }
 }
 
-template <bool ABF, int kDepth, int MBV>
+template <bool ABF, int kDepth, int MBV, int WF>
 __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_colp, const uint8_t *const *s_sclp,
                                  uint8_t *s_b, const void *abase, const size_t *arow, int wn, int lane) {
   const int tid = threadIdx.x;
@@ -174,21 +184,33 @@ __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_col
   for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) C.acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // a column's scale: per group (fp16, loaded with the group) or per row (fp32, once)
+  const float row_sc = WF == kWfQ4G32 ? 0.f : ldg<float>(sclp);
   struct BRaw {
-    uint4 w;
+    QGroup<WF> w;
     uint16_t sc;
   };
   auto load_b = [&](int st) {
     const int g = min(st * kKG + bp, ng - 1);
-    return BRaw{ldg<uint4>(colp + (size_t)g * 16), ldg<uint16_t>(sclp + (size_t)g * 16)};
+    BRaw r;
+    load_group(r.w, colp, g);
+    r.sc = WF == kWfQ4G32 ? ldg<uint16_t>(sclp + (size_t)g * 16) : (uint16_t)0;
+    return r;
   };
   auto store_b = [&](int buf, const BRaw &r) {
-    const float sc = half_bits_to_float(r.sc);
     uint8_t *d = s_b + buf * kBStage + bp * kBGroup + bc * kBStride;
-    *(uint4 *)(d) = dequant8(r.w.x, sc);
-    *(uint4 *)(d + 16) = dequant8(r.w.y, sc);
-    *(uint4 *)(d + 32) = dequant8(r.w.z, sc);
-    *(uint4 *)(d + 48) = dequant8(r.w.w, sc);
+    if constexpr (WF == kWfQ8Row) {
+      *(uint4 *)(d) = dequant8_i8(r.w.q[0].x, r.w.q[0].y, row_sc);
+      *(uint4 *)(d + 16) = dequant8_i8(r.w.q[0].z, r.w.q[0].w, row_sc);
+      *(uint4 *)(d + 32) = dequant8_i8(r.w.q[1].x, r.w.q[1].y, row_sc);
+      *(uint4 *)(d + 48) = dequant8_i8(r.w.q[1].z, r.w.q[1].w, row_sc);
+    } else {
+      const float sc = WF == kWfQ4G32 ? half_bits_to_float(r.sc) : row_sc;
+      *(uint4 *)(d) = dequant8(r.w.q[0].x, sc);
+      *(uint4 *)(d + 16) = dequant8(r.w.q[0].y, sc);
+      *(uint4 *)(d + 32) = dequant8(r.w.q[0].z, sc);
+      *(uint4 *)(d + 48) = dequant8(r.w.q[0].w, sc);
+    }
   };
   // activations of group gi of stage st (clamped to the last group)
   auto load_a = [&](int st, int gi, ARaw<ABF> (&r)[kMB]) {
@@ -242,16 +264,16 @@ __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_col
 // multiplies only its valid blocks (MBV), every wave dequantises its share of B.
 __device__ inline int row_of(int wave, int mb, int r16) { return (wave % kWM + kWM * mb) * 16 + r16; }
 
-template <bool ABF, int kDepth>
+template <bool ABF, int kDepth, int WF>
 __device__ inline void gemm_rows(GemmAcc &C, int rows, int ng, const uint8_t *const *s_colp,
                                  const uint8_t *const *s_sclp, uint8_t *s_b, const void *abase, const size_t *arow,
                                  int wave, int lane) {
   const int nblk = (rows + 15) / 16, band = wave % kWM, wn = wave / kWM;
   const int mbv = min(kMB, max(0, (nblk - band + kWM - 1) / kWM));  // valid blocks band, band + kWM, ...
   switch (mbv) {
-    case 2: gemm_loop<ABF, kDepth, 2>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
-    case 1: gemm_loop<ABF, kDepth, 1>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
-    default: gemm_loop<ABF, kDepth, 0>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
+    case 2: gemm_loop<ABF, kDepth, 2, WF>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
+    case 1: gemm_loop<ABF, kDepth, 1, WF>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
+    default: gemm_loop<ABF, kDepth, 0, WF>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
   }
 }
 
@@ -270,6 +292,7 @@ inline unsigned tile_blocks(int max_mtiles, int n_tiles) {
 }
 
 // Gate/up for one (M tile, N tile of kNT/2 features): h[pair][feature] = silu(g) * u.
+template <int WF>
 __global__ __launch_bounds__(kThreads) void k_gu_mfma(FfnArgs a) {
   __shared__ __align__(16) uint8_t s_b[2 * kBStage];
   __shared__ const uint8_t *s_colp[kNT];
@@ -286,14 +309,14 @@ __global__ __launch_bounds__(kThreads) void k_gu_mfma(FfnArgs a) {
   const uint8_t *ex = sh ? a.shared : expert_ptr(a, mt.e);
   if (!ex) return;  // the down GEMM poisons this tile's rows
   const int Imax = max(a.I, a.Is);
-  const size_t gtb = gu_tile_bytes(a.H);
+  const size_t gtb = gu_tile_bytes(a.H, WF), rb = row_bytes(a.H, WF);
   if (threadIdx.x < kNT) {
     const int c = threadIdx.x;
     // columns past 2 * inter (a partial last tile) read the last gate/up tile and are not stored
     const int tt = min(nt * (kNT / 8) + c / 8, inter / kGuPairs - 1);
     const uint8_t *tile = ex + (size_t)tt * gtb;
-    s_colp[c] = tile + (size_t)(c % 8) * (a.H / 2);
-    s_sclp[c] = tile + (size_t)kGuRows * (a.H / 2) + 2 * (c % 8);
+    s_colp[c] = tile + (size_t)(c % 8) * rb;
+    s_sclp[c] = tile + (size_t)kGuRows * rb + (WF == kWfQ4G32 ? 2 : 4) * (c % 8);
   }
   tile_rows(a, mt, s_tok, s_pair);
   __syncthreads();
@@ -303,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void k_gu_mfma(FfnArgs a) {
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb) arow[mb] = (size_t)s_tok[row_of(wave, mb, lane & 15)] * a.H;
   GemmAcc C;
-  gemm_rows<true, 3>(C, mt.n, a.H / kGroup, s_colp, s_sclp, s_b, a.x_bf16 ? a.x : (const void *)a.xb, arow, wave,
+  gemm_rows<true, 3, WF>(C, mt.n, a.H / kGroup, s_colp, s_sclp, s_b, a.x_bf16 ? a.x : (const void *)a.xb, arow, wave,
                      lane);
   // epilogue: even columns are gate, the next lane holds the matching up
 #pragma unroll
@@ -326,6 +349,7 @@ __global__ __launch_bounds__(kThreads) void k_gu_mfma(FfnArgs a) {
 }
 
 // Down for one (M tile, N tile of kNT output rows): part[pair][row] = Wd h.
+template <int WF>
 __global__ __launch_bounds__(kThreads) void k_dn_mfma(FfnArgs a) {
   __shared__ __align__(16) uint8_t s_b[2 * kBStage];
   __shared__ const uint8_t *s_colp[kNT];
@@ -352,9 +376,10 @@ __global__ __launch_bounds__(kThreads) void k_dn_mfma(FfnArgs a) {
   const int Imax = max(a.I, a.Is);
   if (threadIdx.x < kNT) {
     const int n = min(n0 + (int)threadIdx.x, a.H - 1);  // columns past H read row H-1 and are not stored
-    const uint8_t *tile = ex + down_offset(a.H, inter) + (size_t)(n / kDnRows) * dn_tile_bytes(inter);
-    s_colp[threadIdx.x] = tile + (size_t)(n % kDnRows) * (inter / 2);
-    s_sclp[threadIdx.x] = tile + (size_t)kDnRows * (inter / 2) + 2 * (n % kDnRows);
+    const size_t rb = row_bytes(inter, WF);
+    const uint8_t *tile = ex + down_offset(a.H, inter, WF) + (size_t)(n / kDnRows) * dn_tile_bytes(inter, WF);
+    s_colp[threadIdx.x] = tile + (size_t)(n % kDnRows) * rb;
+    s_sclp[threadIdx.x] = tile + (size_t)kDnRows * rb + (WF == kWfQ4G32 ? 2 : 4) * (n % kDnRows);
   }
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -363,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void k_dn_mfma(FfnArgs a) {
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb) arow[mb] = (size_t)s_pair[row_of(wave, mb, lane & 15)] * 2 * Imax;
   GemmAcc C;
-  gemm_rows<true, 2>(C, mt.n, inter / kGroup, s_colp, s_sclp, s_b, a.h, arow, wave, lane);
+  gemm_rows<true, 2, WF>(C, mt.n, inter / kGroup, s_colp, s_sclp, s_b, a.h, arow, wave, lane);
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
@@ -397,14 +422,24 @@ hipError_t launch_gu_mfma(const FfnArgs &a, hipStream_t st) {
   }
   ProfScope ps("gateup_mfma", st);
   const int Imax = std::max(a.I, a.Is);
-  MOE_LAUNCH(k_gu_mfma, dim3(tile_blocks(a.max_mtiles, (2 * Imax + kNT - 1) / kNT)), dim3(kThreads), 0, st, a);
+  const dim3 g(tile_blocks(a.max_mtiles, (2 * Imax + kNT - 1) / kNT));
+  switch (a.wf) {
+    case kWfQ4Row: MOE_LAUNCH(k_gu_mfma<kWfQ4Row>, g, dim3(kThreads), 0, st, a); break;
+    case kWfQ8Row: MOE_LAUNCH(k_gu_mfma<kWfQ8Row>, g, dim3(kThreads), 0, st, a); break;
+    default: MOE_LAUNCH(k_gu_mfma<kWfQ4G32>, g, dim3(kThreads), 0, st, a); break;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_dn_mfma(const FfnArgs &a, hipStream_t st) {
   if (a.mfma_thr <= 0 || a.max_mtiles <= 0) return hipSuccess;
   ProfScope ps("down_mfma", st);
-  MOE_LAUNCH(k_dn_mfma, dim3(tile_blocks(a.max_mtiles, (a.H + kNT - 1) / kNT)), dim3(kThreads), 0, st, a);
+  const dim3 g(tile_blocks(a.max_mtiles, (a.H + kNT - 1) / kNT));
+  switch (a.wf) {
+    case kWfQ4Row: MOE_LAUNCH(k_dn_mfma<kWfQ4Row>, g, dim3(kThreads), 0, st, a); break;
+    case kWfQ8Row: MOE_LAUNCH(k_dn_mfma<kWfQ8Row>, g, dim3(kThreads), 0, st, a); break;
+    default: MOE_LAUNCH(k_dn_mfma<kWfQ4G32>, g, dim3(kThreads), 0, st, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
 
 MOE_OK, MOE_EINVAL, MOE_ENULL, MOE_EDTYPE, MOE_EWORKSPACE, MOE_ENOSLOT, MOE_ESTALE, MOE_EHIP = 0, -1, -2, -3, -4, -5, -6, -7
 MOE_F32, MOE_BF16 = 0, 1
+MOE_WF_Q4_G32, MOE_WF_Q4_ROW, MOE_WF_Q8_ROW = 0, 1, 2
 
 
 class MoeError(RuntimeError):
@@ -33,7 +34,7 @@ class moe_cfg(ctypes.Structure):
                 ("topk_group", ctypes.c_int32), ("top_k", ctypes.c_int32), ("moe_inter", ctypes.c_int32),
                 ("shared_inter", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("routed_scaling_factor", ctypes.c_float), ("norm_topk_prob", ctypes.c_int32),
-                ("mfma_min_tokens", ctypes.c_int32)]
+                ("mfma_min_tokens", ctypes.c_int32), ("weight_format", ctypes.c_int32)]
 
 
 class moe_slot_view(ctypes.Structure):
@@ -61,6 +62,8 @@ def _load():
         "moe_workspace_init": (ctypes.c_int, [p, sz, p]),
         "moe_pack_expert": (ctypes.c_int, [cp, i32, p, p, p, p, p, p, p, i32, p]),
         "moe_unpack_expert": (ctypes.c_int, [cp, i32, p, p, p, p, p, p, p]),
+        "moe_pack_expert_rows": (ctypes.c_int, [cp, i32, p, p, p, p, p, p, p, i32, p]),
+        "moe_unpack_expert_rows": (ctypes.c_int, [cp, i32, p, p, p, p, p, p, p]),
         "moe_route": (ctypes.c_int, [cp, p, i32, i32, p, p, p, p, p, sz, p]),
         "moe_ffn": (ctypes.c_int, [cp, p, i32, i32, p, p, ctypes.POINTER(moe_slot_view), p, p, p, sz, p]),
         "moe_layer": (ctypes.c_int, [cp, p, i32, i32, p, p, p, p, ctypes.POINTER(moe_slot_view), p, p, p, sz, p]),
@@ -102,7 +105,8 @@ MFMA_MIN_TOKENS = 16  # default threshold of the matrix-core path (tokens per ex
 def make_cfg(c, mfma_min_tokens: int = MFMA_MIN_TOKENS) -> moe_cfg:
     """moe_cfg from any object with the LayerConfig field names."""
     return moe_cfg(c.hidden, c.n_experts, c.n_group, c.topk_group, c.top_k, c.moe_inter, c.shared_inter,
-                   c.group_size, c.routed_scaling_factor, c.norm_topk_prob, mfma_min_tokens)
+                   c.group_size, c.routed_scaling_factor, c.norm_topk_prob, mfma_min_tokens,
+                   getattr(c, "weight_format", MOE_WF_Q4_G32))
 
 
 def ptr(t) -> int | None:
@@ -161,6 +165,23 @@ def moe_pack_expert(cfg: moe_cfg, inter: int, qg, sg, qu, su, qd, sd, dst, where
 def moe_unpack_expert(cfg: moe_cfg, inter: int, src, qg, sg, qu, su, qd, sd) -> None:
     _check(_lib.moe_unpack_expert(ctypes.byref(cfg), inter, ptr(src), ptr(qg), ptr(sg), ptr(qu), ptr(su), ptr(qd),
                                   ptr(sd)), "moe_unpack_expert")
+
+
+def moe_pack_expert_rows(cfg: moe_cfg, inter: int, qg, sg, qu, su, qd, sd, dst, where: int, stream=None) -> None:
+    st = stream_handle(stream) if where == 1 else None
+    _check(_lib.moe_pack_expert_rows(ctypes.byref(cfg), inter, ptr(qg), ptr(sg), ptr(qu), ptr(su), ptr(qd), ptr(sd),
+                                     ptr(dst), where, st), "moe_pack_expert_rows")
+
+
+def moe_unpack_expert_rows(cfg: moe_cfg, inter: int, src, qg, sg, qu, su, qd, sd) -> None:
+    _check(_lib.moe_unpack_expert_rows(ctypes.byref(cfg), inter, ptr(src), ptr(qg), ptr(sg), ptr(qu), ptr(su),
+                                       ptr(qd), ptr(sd)), "moe_unpack_expert_rows")
+
+
+def pack_expert(cfg: moe_cfg, inter: int, qg, sg, qu, su, qd, sd, dst, where: int, stream=None) -> None:
+    """moe_pack_expert or moe_pack_expert_rows, by cfg.weight_format."""
+    f = moe_pack_expert if cfg.weight_format == MOE_WF_Q4_G32 else moe_pack_expert_rows
+    f(cfg, inter, qg, sg, qu, su, qd, sd, dst, where, stream)
 
 
 def moe_route(cfg: moe_cfg, x, x_dtype: int, S: int, W, bias, idx, w, ws, ws_bytes: int, stream=None) -> None:

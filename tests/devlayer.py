@@ -34,7 +34,7 @@ class DeviceLayer:
             gen.expert_weights(w, layer, e, out=stage)
             self._pack(stage, c.moe_inter, self.slab[e * self.slot_bytes:(e + 1) * self.slot_bytes])
             if host_experts:
-                self.host[e] = gen.ExpertWeights(stage.inter, *[a.copy() for a in stage.parts()])
+                self.host[e] = gen.ExpertWeights(stage.inter, *[a.copy() for a in stage.parts()], stage.fmt)
         self.shared = None
         if c.shared_inter > 0:
             sb = M.moe_expert_bytes(self.cfg, c.shared_inter)
@@ -50,7 +50,7 @@ class DeviceLayer:
 
     def _pack(self, ex: gen.ExpertWeights, inter: int, dst: torch.Tensor) -> None:
         parts = [dev(a) for a in ex.parts()]
-        M.moe_pack_expert(self.cfg, inter, *parts, dst, 1)
+        M.pack_expert(self.cfg, inter, *parts, dst, 1)
         torch.cuda.current_stream().synchronize()
 
     def host_expert(self, e: int, layer: int = 0) -> gen.ExpertWeights:

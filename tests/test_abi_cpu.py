@@ -106,6 +106,71 @@ def test_host_pack_round_trip_and_layout(shape):
     assert np.all(dst[d0 + (H // 8) * dtile:] == 0)
 
 
+def test_expert_bytes_row_formats():
+    # int4 nibbles or int8 bytes of the three matrices plus one fp32 scale per row
+    # (tiles of 8 rows carry 32 B of scales); 40,960 B of scales for GLM-5.2
+    for fmt, per_w in ((M.MOE_WF_Q4_ROW, 0.5), (M.MOE_WF_Q8_ROW, 1.0)):
+        c = M.make_cfg(gen.LayerConfig(**{**gen.GLM52.__dict__, "weight_format": fmt}))
+        payload = int(3 * 6144 * 2048 * per_w) + (2048 // 4 + 6144 // 8) * 32
+        assert M.moe_expert_bytes(c, 2048) == (payload + 4095) // 4096 * 4096
+    assert M.moe_expert_bytes(M.make_cfg(gen.LayerConfig(**{**gen.GLM52.__dict__, "weight_format": 1})),
+                              2048) == 18_915_328
+    bad = M.make_cfg(gen.GLM52)
+    bad.weight_format = 3
+    assert M.moe_validate_cfg(bad) == M.MOE_EINVAL
+
+
+@pytest.mark.parametrize("fmt", [M.MOE_WF_Q4_ROW, M.MOE_WF_Q8_ROW])
+@pytest.mark.parametrize("base", [gen.TINY, gen.LayerConfig(hidden=96, n_experts=4, n_group=2, topk_group=1,
+                                                                top_k=2, moe_inter=64, shared_inter=32)])
+def test_host_pack_rows_round_trip_and_layout(fmt, base):
+    shape = gen.LayerConfig(**{**base.__dict__, "weight_format": fmt})
+    c = M.make_cfg(shape)
+    ex = _expert_host(shape, shape.moe_inter)
+    nb = M.moe_expert_bytes(c, shape.moe_inter)
+    dst = np.full(nb, 0xAB, np.uint8)
+    M.moe_pack_expert_rows(c, shape.moe_inter, *ex.parts(), dst, 0)
+    out = gen.empty_expert(shape, shape.moe_inter)
+    M.moe_unpack_expert_rows(c, shape.moe_inter, dst, *out.parts())
+    for a, b in zip(ex.parts(), out.parts()):
+        assert np.array_equal(a, b)
+    # documented layout, re-derived: 8 rows per tile (gate/up interleaved), then 8 fp32 scales
+    H, I = shape.hidden, shape.moe_inter
+    rb = (lambda K: K) if fmt == M.MOE_WF_Q8_ROW else (lambda K: K // 2)
+    conv = (lambda q: q.view(np.uint8)) if fmt == M.MOE_WF_Q8_ROW else (lambda q: q ^ np.uint8(0x88))
+    tile = 8 * rb(H) + 32
+    for t in range(I // 4):
+        base_ = t * tile
+        for i in range(8):
+            src = ex.qu if i % 2 else ex.qg
+            assert np.array_equal(dst[base_ + i * rb(H): base_ + (i + 1) * rb(H)], conv(src[4 * t + i // 2]))
+        scl = dst[base_ + 8 * rb(H): base_ + tile].view(np.float32)
+        assert np.array_equal(scl[0::2], ex.sg[4 * t: 4 * t + 4]) and np.array_equal(scl[1::2], ex.su[4 * t: 4 * t + 4])
+    dtile = 8 * rb(I) + 32
+    d0 = (I // 4) * tile
+    for t in range(H // 8):
+        base_ = d0 + t * dtile
+        for i in range(8):
+            assert np.array_equal(dst[base_ + i * rb(I): base_ + (i + 1) * rb(I)], conv(ex.qd[8 * t + i]))
+        assert np.array_equal(dst[base_ + 8 * rb(I): base_ + dtile].view(np.float32), ex.sd[8 * t: 8 * t + 8])
+    assert np.all(dst[d0 + (H // 8) * dtile:] == 0)
+
+
+def test_pack_entry_points_reject_the_other_formats():
+    L = M.lib()
+    g = M.make_cfg(gen.TINY)
+    r = M.make_cfg(gen.LayerConfig(**{**gen.TINY.__dict__, "weight_format": 1}))
+    exg, exr = _expert_host(gen.TINY, 128), _expert_host(gen.LayerConfig(**{**gen.TINY.__dict__, "weight_format": 1}), 128)
+    dst = np.zeros(max(M.moe_expert_bytes(g, 128), M.moe_expert_bytes(r, 128)), np.uint8)
+    pg = [M.ptr(a) for a in exg.parts()]
+    pr = [M.ptr(a) for a in exr.parts()]
+    assert L.moe_pack_expert(ctypes.byref(r), 128, *pg, M.ptr(dst), 0, None) == M.MOE_EINVAL
+    assert L.moe_pack_expert_rows(ctypes.byref(g), 128, *pr, M.ptr(dst), 0, None) == M.MOE_EINVAL
+    assert L.moe_unpack_expert(ctypes.byref(r), 128, M.ptr(dst), *pg) == M.MOE_EINVAL
+    assert L.moe_unpack_expert_rows(ctypes.byref(g), 128, M.ptr(dst), *pr) == M.MOE_EINVAL
+    assert L.moe_pack_expert_rows(ctypes.byref(r), 128, *pr[:5], None, M.ptr(dst), 0, None) == M.MOE_ENULL
+
+
 def test_pack_argument_errors():
     c = M.make_cfg(gen.TINY)
     ex = _expert_host(gen.TINY, 128)
