@@ -43,10 +43,31 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(kernel: str):
+FORMATS = {"q4g32": 0, "q4row": 1, "q8row": 2}  # moe_weight_format
+FORMAT_DESC = {"q4g32": "int4 g32 fp16 scales", "q4row": "int4 fp32 row scales", "q8row": "int8 fp32 row scales"}
+
+
+def traffic_name(kernel: str, fmt: str = "q4g32") -> str:
+    return f"traffic_{kernel}.json" if fmt == "q4g32" else f"traffic_{kernel}_{fmt}.json"
+
+
+def with_format(w, fmt: str):
+    """The workload with its experts in weight format `fmt`."""
+    from gen import inputs as gen
+    return w.with_(cfg=gen.LayerConfig(**{**w.cfg.__dict__, "weight_format": FORMATS[fmt]}))
+
+
+def gu_bytes(fmt: str, H: int, I: int) -> int:
+    """Algorithmic bytes of one expert's gate and up matrices (weights and scales)."""
+    if fmt == "q4g32":
+        return 2 * (I * H // 2 + I * (H // 32) * 2)
+    return 2 * (I * (H if fmt == "q8row" else H // 2) + I * 4)
+
+
+def measured_traffic(kernel: str, fmt: str = "q4g32"):
     """HBM bytes per launch of `kernel` from the committed counter summary, or None when
     the summary is missing or was taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    path = os.path.join(ROOT, "profiles", traffic_name(kernel, fmt))
     if not os.path.exists(path):
         return None
     try:
@@ -73,7 +94,7 @@ def _pmc_means(path: str, counter: str) -> dict:
 
 
 def summarize_pmc(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str, copy_mib: int,
-                  kernels: list) -> None:
+                  kernels: list, fmt: str = "q4g32") -> None:
     """Writes profiles/traffic_<kernel>.json: HBM bytes per launch from FETCH_SIZE and WRITE_SIZE,
     each scaled by what the same counter reads for a copy kernel that moves copy_mib MiB each way."""
     def one(path, counter, name_part):
@@ -94,7 +115,8 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_writ
                "fetch_scale": f_scale, "write_scale": w_scale,
                "bytes_per_launch": (fetch * f_scale + write * w_scale) * 1024.0,
                "calibration": f"copy kernel moving {copy_mib} MiB read + {copy_mib} MiB write"}
-        path = os.path.join(ROOT, "profiles", f"traffic_{short}.json")
+        out["weight_format"] = fmt
+        path = os.path.join(ROOT, "profiles", traffic_name(short, fmt))
         with open(path, "w") as fh:
             json.dump(out, fh, indent=1)
             fh.write("\n")
@@ -117,9 +139,9 @@ def pack_layer(w, l, dev, cfg):
         ex = gen.expert_weights(w, l, e, out=stage if e < E else None)
         parts = [torch.from_numpy(a).to(dev) for a in ex.parts()]
         if e < E:
-            M.moe_pack_expert(cfg, I, *parts, slab[e * sb:(e + 1) * sb], 1)
+            M.pack_expert(cfg, I, *parts, slab[e * sb:(e + 1) * sb], 1)
         else:
-            M.moe_pack_expert(cfg, c.shared_inter, *parts, shared, 1)
+            M.pack_expert(cfg, c.shared_inter, *parts, shared, 1)
         torch.cuda.current_stream().synchronize()
     return dict(slab=slab, shared=shared, table=torch.arange(E, dtype=torch.int32, device=dev),
                 W=torch.from_numpy(gen.router_weights(w, l)).to(dev),
@@ -146,7 +168,7 @@ def bench_verify(args) -> int:
     import torch
     from gen import inputs as gen
     from int4_routed_expert_amd import moe as M
-    w = gen.WORKLOADS["verify"]
+    w = with_format(gen.WORKLOADS["verify"], args.weight_format)
     c, S = w.cfg, w.tokens
     cfg = M.make_cfg(c)
     dev = torch.device("cuda:0")
@@ -197,6 +219,7 @@ def bench_verify(args) -> int:
           "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
           "dtype": "f32", "data": "synthetic",
           "config": {"workload": "glm52_moe_layer_verify_S4", "tokens_per_call": S, "bias": w.bias_recipe,
+                     "quant": FORMAT_DESC[args.weight_format],
                      "layers_rotated": args.layers, "batches_rotated": nb, "launch": "hip graphs of 16 calls",
                      "call": "moe_layer" if args.call == "layer" else "moe_route + moe_ffn"},
           "union_mean": float(U.mean()), "union_min": int(U.min()), "union_max": int(U.max()),
@@ -243,7 +266,7 @@ def bench_prefill(args) -> int:
     import torch
     from gen import inputs as gen
     from int4_routed_expert_amd import moe as M
-    w = gen.WORKLOADS["prefill"]
+    w = with_format(gen.WORKLOADS["prefill"], args.weight_format)
     c, S = w.cfg, w.tokens
     cfg = M.make_cfg(c, args.mfma_min_tokens)
     dev = torch.device("cuda:0")
@@ -288,6 +311,7 @@ def bench_prefill(args) -> int:
           "ms_per_step": el * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
           "dtype": "f32", "data": "synthetic",
           "config": {"workload": "glm52_moe_layer_prefill_S2048", "tokens_per_call": S, "x": "bf16",
+                     "quant": FORMAT_DESC[args.weight_format],
                      "bias": w.bias_recipe, "batches_rotated": nb, "mfma_min_tokens": args.mfma_min_tokens},
           "experts_used": used, "effective_gbps": bytes_call / el / 1e9,
           "pct_hbm_peak": 100.0 * bytes_call / el / 1e9 / HBM_PEAK_GBPS,
@@ -304,7 +328,7 @@ def bench_stack(args) -> int:
     import torch
     from gen import inputs as gen
     from int4_routed_expert_amd import moe as M
-    w = gen.WORKLOADS["stack"]
+    w = with_format(gen.WORKLOADS["stack"], args.weight_format)
     if args.blobs:
         w = w.with_(n_blobs=args.blobs)
     c = w.cfg
@@ -324,7 +348,7 @@ def bench_stack(args) -> int:
             if b not in blob_ids:
                 ex = gen.expert_weights(w, l, e, out=stage)
                 parts = [torch.from_numpy(a).to(dev) for a in ex.parts()]
-                M.moe_pack_expert(cfg, I, *parts, stage_d, 1)
+                M.pack_expert(cfg, I, *parts, stage_d, 1)
                 host[b].copy_(stage_d)
                 blob_ids[b] = True
     torch.cuda.synchronize()
@@ -338,7 +362,7 @@ def bench_stack(args) -> int:
     for l in range(NL):
         sh = gen.expert_weights(w, l, E)
         shared = torch.empty(M.moe_expert_bytes(cfg, c.shared_inter), dtype=torch.uint8, device=dev)
-        M.moe_pack_expert(cfg, c.shared_inter, *[torch.from_numpy(a).to(dev) for a in sh.parts()], shared, 1)
+        M.pack_expert(cfg, c.shared_inter, *[torch.from_numpy(a).to(dev) for a in sh.parts()], shared, 1)
         layers.append(dict(W=torch.from_numpy(gen.router_weights(w, l)).to(dev),
                            bias=torch.from_numpy(gen.router_bias(w, l)).to(dev), shared=shared))
     xs = [torch.from_numpy(np.concatenate([gen.tokens(w, layer=l, step=s) for s in range(steps)])).to(dev)
@@ -431,7 +455,7 @@ def bench_stack(args) -> int:
           "dtype": "f32", "data": "synthetic",
           "config": {"workload": "glm52_moe_stack_75_layers_decode", "layers": NL, "steps": steps,
                      "slots_per_layer": spl, "pool_gb": NL * spl * sb / 1e9, "distinct_blobs": w.n_blobs,
-                     "bias": w.bias_recipe, "prefetch": bool(args.prefetch),
+                     "bias": w.bias_recipe, "prefetch": bool(args.prefetch), "quant": FORMAT_DESC[args.weight_format],
                      "launch": ("eager; next layer routed ahead and prefetched" if args.prefetch
                                 else "eager; host sync per layer for residency")},
           "tokens_per_s_warm": (steps - 1) / warm_el if steps > 1 else None,
@@ -453,13 +477,17 @@ def main() -> int:
         ap.add_argument("--copy-write", required=True)
         ap.add_argument("--copy-mib", type=int, default=1024)
         ap.add_argument("--kernels", default="gateup_s1,down_s1")
+        ap.add_argument("--weight-format", default="q4g32", choices=list(FORMATS))
         a = ap.parse_args()
-        summarize_pmc(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib, a.kernels.split(","))
+        summarize_pmc(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib, a.kernels.split(","),
+                      a.weight_format)
         return 0
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="decode", choices=["decode", "verify", "prefill", "stack"],
                     help="decode (default, the headline line); verify, prefill and stack are separate lines")
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--weight-format", default="q4g32", choices=list(FORMATS),
+                    help="expert format: int4 + fp16 per 32 (default), int4 + fp32 per row, int8 + fp32 per row")
     ap.add_argument("--steps", type=int, default=4096)
     ap.add_argument("--warmup", type=int, default=512)
     ap.add_argument("--layers", type=int, default=4, help="resident layer instances rotated per step")
@@ -493,7 +521,8 @@ def main() -> int:
     from gen import inputs as gen
     from int4_routed_expert_amd import moe as M
 
-    w = gen.WORKLOADS["decode"]
+    fmt = args.weight_format
+    w = with_format(gen.WORKLOADS["decode"], fmt)
     c = w.cfg
     cfg = M.make_cfg(c)
     E, H, I, k = c.n_experts, c.hidden, c.moe_inter, c.top_k
@@ -512,10 +541,10 @@ def main() -> int:
             ex = gen.expert_weights(w, l, e, out=stage if e < E else None)
             parts = [torch.from_numpy(a).to(dev, non_blocking=False) for a in ex.parts()]
             if e < E:
-                M.moe_pack_expert(cfg, I, *parts, slab[e * sb:(e + 1) * sb], 1)
+                M.pack_expert(cfg, I, *parts, slab[e * sb:(e + 1) * sb], 1)
             else:
                 shared = torch.empty(ssb, dtype=torch.uint8, device=dev)
-                M.moe_pack_expert(cfg, c.shared_inter, *parts, shared, 1)
+                M.pack_expert(cfg, c.shared_inter, *parts, shared, 1)
             torch.cuda.current_stream().synchronize()
         layers.append(dict(
             slab=slab, shared=shared, table=torch.arange(E, dtype=torch.int32, device=dev),
@@ -596,10 +625,10 @@ def main() -> int:
     kernels = {name: {"avg_us": ms * 1e3 / n, "launches": n} for name, (ms, n) in prof.items()}
     log("per-kernel (hipEvent) averages:", json.dumps(kernels))
     rk = "gateup_s1"  # dominant kernel: gate/up of the 9 experts (payload and scales)
-    alg_bytes = 9 * 2 * (I * H // 2 + I * (H // 32) * 2)
+    alg_bytes = 9 * gu_bytes(fmt, H, I)
     k_us = kernels[rk]["avg_us"]
     achieved = alg_bytes / (k_us * 1e-6) / 1e9
-    traffic = measured_traffic(rk)
+    traffic = measured_traffic(rk, fmt)
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample ------------------------
     cpu = None
@@ -641,7 +670,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": "glm52_moe_layer_decode_S1", "hidden": H, "n_experts": E, "n_group": c.n_group,
                    "topk_group": c.topk_group, "top_k": k, "moe_inter": I, "shared_inter": c.shared_inter,
-                   "quant": "int4 g32 fp16 scales", "layers_rotated": args.layers, "tokens_rotated": args.tokens,
+                   "quant": FORMAT_DESC[fmt], "layers_rotated": args.layers, "tokens_rotated": args.tokens,
                    "launch": "hip graphs of 16 steps",
                    "call": "moe_layer" if args.call == "layer" else "moe_route + moe_ffn"},
         "effective_gbps": gbps,

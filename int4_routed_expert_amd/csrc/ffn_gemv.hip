@@ -57,6 +57,11 @@ __global__ __launch_bounds__(256) void k_to_limbs(const void *src, int bf16, int
 // experts from the router's scores and keys (EPT experts per thread); the
 // loads of the selection inputs go first, then the activations and the first
 // two shared-expert features, so that the selection overlaps them.
+#ifndef MOE_GU_RING
+#define MOE_GU_RING 3
+#endif
+constexpr int kGuRing = MOE_GU_RING;  // feature slots of the one-token gate/up ring (kGuRing - 1 in flight)
+
 template <int NG, int WF, int EPT>
 __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
   extern __shared__ uint32_t lds[];  // x limbs [H/32][24], then factors [H/32]
@@ -68,7 +73,8 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
   const int r0 = (int)(wid * Fr / W), r1 = (int)((wid + 1) * Fr / W);
   const int ns = s1 - s0, n = ns + (r1 - r0);
   const bool has_x = (int)threadIdx.x < ng;
-  GuFeat<NG, WF> b0, b1, b2;
+  GuFeat<NG, WF> b[kGuRing];
+  GuFeat<NG, WF> &b0 = b[0];
   uint64_t my_ptr = 0;
   float v[32];
   float *lf = (float *)(lds + (size_t)ng * 24);
@@ -98,7 +104,9 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
     }
     if (blockIdx.x == 0 && threadIdx.x < 64 && lane < a.k) a.eptr[lane] = my_ptr;  // for the down kernel
     if (n > 0 && !early) gu_feat_load(b0, a, 0, n, ns, s0, r0, my_ptr, lane);
-    if (n > 0) gu_feat_load(b1, a, 1, n, ns, s0, r0, my_ptr, lane);
+#pragma unroll
+    for (int r = 1; r < kGuRing - 1; ++r)
+      if (n > 0) gu_feat_load(b[r], a, r, n, ns, s0, r0, my_ptr, lane);
   } else {
     // Order (loads return in order): lane j's expert id, the activations, then
     // the expert's slot; all unconditional (clamped) so the waits are exact.
@@ -109,12 +117,14 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
     my_ptr = e_ok && slot >= 0 && slot < a.n_slots ? (uint64_t)(uintptr_t)(a.base + (size_t)slot * (size_t)a.slot_bytes)
                                                     : 0;
     if (blockIdx.x == 0 && threadIdx.x < 64 && lane < a.k) a.eptr[lane] = my_ptr;  // for the down kernel
-    // three-slot ring, two features in flight while one is computed.  Loads are
-    // unconditional (indices clamped; repeats at the tail hit in cache) so the
-    // load counter order is fixed.
+    // kGuRing-slot ring, kGuRing - 1 features in flight while one is computed.
+    // Loads are unconditional (indices clamped; repeats at the tail hit in
+    // cache) so the load counter order is fixed.
     if (n > 0) gu_feat_load(b0, a, 0, n, ns, s0, r0, my_ptr, lane);
     stage_x();
-    if (n > 0) gu_feat_load(b1, a, 1, n, ns, s0, r0, my_ptr, lane);
+#pragma unroll
+    for (int r = 1; r < kGuRing - 1; ++r)
+      if (n > 0) gu_feat_load(b[r], a, r, n, ns, s0, r0, my_ptr, lane);
   }
   __syncthreads();
   if (n <= 0) return;
@@ -133,13 +143,13 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
     }
   }
   float hout = 0.f;
-  for (int i = 0; i < n; i += 3) {
-    gu_feat_load(b2, a, i + 2, n, ns, s0, r0, my_ptr, lane);
-    hout = gu_feat_compute(b0, xv, i, hout);
-    gu_feat_load(b0, a, i + 3, n, ns, s0, r0, my_ptr, lane);
-    if (i + 1 < n) hout = gu_feat_compute(b1, xv, i + 1, hout);
-    gu_feat_load(b1, a, i + 4, n, ns, s0, r0, my_ptr, lane);
-    if (i + 2 < n) hout = gu_feat_compute(b2, xv, i + 2, hout);
+  for (int i = 0; i < n; i += kGuRing) {
+    // step r requests feature i + r + kGuRing - 1 into the slot computed at step r - 1
+#pragma unroll
+    for (int r = 0; r < kGuRing; ++r) {
+      gu_feat_load(b[(r + kGuRing - 1) % kGuRing], a, i + r + kGuRing - 1, n, ns, s0, r0, my_ptr, lane);
+      if (r == 0 || i + r < n) hout = gu_feat_compute(b[r], xv, i + r, hout);
+    }
   }
   if (lane < n) {
     int hrow;
