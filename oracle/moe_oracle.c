@@ -37,6 +37,14 @@
  *     the group size is the row length); fmt 2 = signed int8 (two's complement
  *     bytes) with one fp32 scale per row (the MTP layer's routed experts).  In
  *     every format W[r,c] = q[r,c] * scale, exact in fp64.
+ *  R7 int8 activations ([PORT] "G2 implementation status": Colibri's IDOT=1
+ *     quantises each activation row to int8 before the packed-int4 dot
+ *     product, an approximate mode; [README] "Integer-dot kernels": int8
+ *     activations): a row v of length n (the layer input of a token, and each
+ *     expert's hidden activation h after it is rounded to fp32) becomes
+ *     d = fp32(amax / 127) with amax = max |v| (fp32), q_c = rint(fp32(v_c / d))
+ *     (ties to even; q = 0 for an all-zero row), and the matmul uses q_c * d
+ *     (exact in fp64) in place of v_c.
  *
  * Parity pins: tests/test_oracle_pins.py (brute force, closed forms, invariants).
  */
@@ -265,12 +273,26 @@ int oracle_route(int S, int H, int E, int G, int Gk, int k, double rsf, int norm
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
+/* R7: v[n] (fp32 values) -> q[n] (int8 values) and the row's scale d; out[c] =
+ * q_c * d in fp64.  The decisions are taken in fp32 (IEEE division). */
+float oracle_quant_row(int n, const float *v, int8_t *q, double *out) {
+  float amax = 0.0f;
+  for (int c = 0; c < n; ++c) amax = fmaxf(amax, fabsf(v[c]));
+  float d = amax / 127.0f;
+  for (int c = 0; c < n; ++c) {
+    float r = d > 0.0f ? rintf(v[c] / d) : 0.0f;
+    if (q) q[c] = (int8_t)r;
+    if (out) out[c] = (double)r * (double)d;
+  }
+  return d;
+}
+
 /* y[H] = Wd (silu(Wg x) * (Wu x)) for one token, fp64.  Matrices in the
  * interchange layout of format fmt (R6): gate/up [I, H], down [H, I].
  * h_out (optional) receives the [I] hidden activation. */
-void oracle_expert_ffn_fmt(int fmt, int H, int I, int gsz, const uint8_t *qg, const void *sg, const uint8_t *qu,
-                           const void *su, const uint8_t *qd, const void *sd, const double *x, double *y,
-                           double *h_out) {
+static void expert_ffn_impl(int fmt, int act_int8, int H, int I, int gsz, const uint8_t *qg, const void *sg,
+                            const uint8_t *qu, const void *su, const uint8_t *qd, const void *sd, const double *x,
+                            double *y, double *h_out) {
   double *h = malloc(sizeof(double) * I);
 #pragma omp parallel for schedule(static)
   for (int r = 0; r < I; ++r) {
@@ -281,14 +303,37 @@ void oracle_expert_ffn_fmt(int fmt, int H, int I, int gsz, const uint8_t *qg, co
     }
     h[r] = silu(g) * u;
   }
+  if (h_out) memcpy(h_out, h, sizeof(double) * I);
+  if (act_int8) { /* R7: the down projection sees h rounded to fp32, then quantised */
+    float *h32 = malloc(sizeof(float) * I);
+    for (int c = 0; c < I; ++c) h32[c] = (float)h[c];
+    oracle_quant_row(I, h32, NULL, h);
+    free(h32);
+  }
 #pragma omp parallel for schedule(static)
   for (int r = 0; r < H; ++r) {
     double acc = 0.0;
     for (int c = 0; c < I; ++c) acc += w_at(fmt, I, gsz, qd, sd, r, c) * h[c];
     y[r] = acc;
   }
-  if (h_out) memcpy(h_out, h, sizeof(double) * I);
   free(h);
+}
+
+/* x is the activation the gate/up matmuls see (already quantised in R7 mode). */
+void oracle_expert_ffn_fmt(int fmt, int H, int I, int gsz, const uint8_t *qg, const void *sg, const uint8_t *qu,
+                           const void *su, const uint8_t *qd, const void *sd, const double *x, double *y,
+                           double *h_out) {
+  expert_ffn_impl(fmt, 0, H, I, gsz, qg, sg, qu, su, qd, sd, x, y, h_out);
+}
+
+/* R7 mode: x (fp32 values) is quantised here; h_out receives h before its quantisation. */
+void oracle_expert_ffn_int8act(int fmt, int H, int I, int gsz, const uint8_t *qg, const void *sg, const uint8_t *qu,
+                               const void *su, const uint8_t *qd, const void *sd, const float *x, double *y,
+                               double *h_out) {
+  double *xq = malloc(sizeof(double) * H);
+  oracle_quant_row(H, x, NULL, xq);
+  expert_ffn_impl(fmt, 1, H, I, gsz, qg, sg, qu, su, qd, sd, xq, y, h_out);
+  free(xq);
 }
 
 void oracle_expert_ffn(int H, int I, int gsz, const uint8_t *qg, const uint16_t *sg, const uint8_t *qu,
@@ -302,31 +347,43 @@ void oracle_expert_ffn(int H, int I, int gsz, const uint8_t *qg, const uint16_t 
  * Expert e's six parts are qg[e], sg[e], ... (pointer arrays of length E+1; entry E
  * is the shared expert, NULL when the layer has none).  Only experts that the
  * routing names need non-NULL pointers.  Every expert is in format fmt (R6). */
-int oracle_moe_ffn_fmt(int fmt, int S, int H, int E, int k, int I, int Is, int gsz, int x_is_bf16, const void *x,
-                       const int32_t *idx, const double *w, const uint8_t *const *qg, const void *const *sg,
-                       const uint8_t *const *qu, const void *const *su, const uint8_t *const *qd,
-                       const void *const *sd, double *y) {
+int oracle_moe_ffn_mode(int fmt, int act_int8, int S, int H, int E, int k, int I, int Is, int gsz, int x_is_bf16,
+                        const void *x, const int32_t *idx, const double *w, const uint8_t *const *qg,
+                        const void *const *sg, const uint8_t *const *qu, const void *const *su,
+                        const uint8_t *const *qd, const void *const *sd, double *y) {
   double *xt = malloc(sizeof(double) * H), *ye = malloc(sizeof(double) * H), *acc = malloc(sizeof(double) * H);
+  float *x32 = malloc(sizeof(float) * H);
   int rc = 0;
   for (int t = 0; t < S && !rc; ++t) {
     for (int c = 0; c < H; ++c) xt[c] = x_at(x, x_is_bf16, (size_t)t * H + c);
+    if (act_int8) { /* R7: every expert of the token sees the quantised input */
+      for (int c = 0; c < H; ++c) x32[c] = (float)xt[c];  /* fp32 and bf16 inputs are exact in fp32 */
+      oracle_quant_row(H, x32, NULL, xt);
+    }
     for (int c = 0; c < H; ++c) acc[c] = 0.0;
     for (int j = 0; j < k; ++j) {
       int e = idx[(size_t)t * k + j];
       if (e < 0 || e >= E || !qg[e] || !sg[e] || !qu[e] || !su[e] || !qd[e] || !sd[e]) { rc = -1; break; }
-      oracle_expert_ffn_fmt(fmt, H, I, gsz, qg[e], sg[e], qu[e], su[e], qd[e], sd[e], xt, ye, NULL);
+      expert_ffn_impl(fmt, act_int8, H, I, gsz, qg[e], sg[e], qu[e], su[e], qd[e], sd[e], xt, ye, NULL);
       for (int c = 0; c < H; ++c) acc[c] += w[(size_t)t * k + j] * ye[c];
     }
     if (rc) break;
     if (Is > 0) {
       if (!qg[E]) { rc = -1; break; }
-      oracle_expert_ffn_fmt(fmt, H, Is, gsz, qg[E], sg[E], qu[E], su[E], qd[E], sd[E], xt, ye, NULL);
+      expert_ffn_impl(fmt, act_int8, H, Is, gsz, qg[E], sg[E], qu[E], su[E], qd[E], sd[E], xt, ye, NULL);
       for (int c = 0; c < H; ++c) acc[c] += ye[c];
     }
     for (int c = 0; c < H; ++c) y[(size_t)t * H + c] = acc[c];
   }
-  free(xt); free(ye); free(acc);
+  free(xt); free(ye); free(acc); free(x32);
   return rc;
+}
+
+int oracle_moe_ffn_fmt(int fmt, int S, int H, int E, int k, int I, int Is, int gsz, int x_is_bf16, const void *x,
+                       const int32_t *idx, const double *w, const uint8_t *const *qg, const void *const *sg,
+                       const uint8_t *const *qu, const void *const *su, const uint8_t *const *qd,
+                       const void *const *sd, double *y) {
+  return oracle_moe_ffn_mode(fmt, 0, S, H, E, k, I, Is, gsz, x_is_bf16, x, idx, w, qg, sg, qu, su, qd, sd, y);
 }
 
 int oracle_moe_ffn(int S, int H, int E, int k, int I, int Is, int gsz, int x_is_bf16, const void *x,

@@ -59,6 +59,12 @@ def lib():
         L.oracle_expert_ffn_fmt.argtypes = [i, i, i, i, p, p, p, p, p, p, p, p, p]
         L.oracle_moe_ffn_fmt.restype = i
         L.oracle_moe_ffn_fmt.argtypes = [i] * 9 + [p] * 10
+        L.oracle_moe_ffn_mode.restype = i
+        L.oracle_moe_ffn_mode.argtypes = [i] * 10 + [p] * 10
+        L.oracle_quant_row.restype = ctypes.c_float
+        L.oracle_quant_row.argtypes = [i, p, p, p]
+        L.oracle_expert_ffn_int8act.restype = None
+        L.oracle_expert_ffn_int8act.argtypes = [i, i, i, i, p, p, p, p, p, p, p, p, p]
         L.oracle_num_threads.restype = i
         _lib = L
     return _lib
@@ -95,6 +101,25 @@ def dequant_fmt(fmt: int, q: np.ndarray, s: np.ndarray, gsz: int = 32) -> np.nda
     out = np.empty((R, K), np.float64)
     lib().oracle_dequant_fmt(fmt, R, K, gsz, _p(np.ascontiguousarray(q)), _p(np.ascontiguousarray(s)), _p(out))
     return out
+
+
+def quant_row(v: np.ndarray):
+    """int8 activation quantisation of one fp32 row: (q int8[n], d fp32, q * d fp64[n])."""
+    v = np.ascontiguousarray(v, np.float32)
+    q = np.empty(v.size, np.int8)
+    out = np.empty(v.size, np.float64)
+    d = lib().oracle_quant_row(v.size, _p(v), _p(q), _p(out))
+    return q, np.float32(d), out
+
+
+def expert_ffn_int8act(ex, x: np.ndarray, H: int, gsz: int = 32, return_h: bool = False):
+    """One expert on one fp32 token in int8-activation mode: x and h are quantised per row."""
+    x = np.ascontiguousarray(x, np.float32)
+    y = np.empty(H, np.float64)
+    h = np.empty(ex.inter, np.float64)
+    lib().oracle_expert_ffn_int8act(ex.fmt, H, ex.inter, gsz, *[_p(np.ascontiguousarray(a)) for a in ex.parts()],
+                                    _p(x), _p(y), _p(h))
+    return (y, h) if return_h else y
 
 
 def select(cfg, logits: np.ndarray, bias: np.ndarray):
@@ -144,9 +169,11 @@ def expert_ffn(ex, x: np.ndarray, H: int, gsz: int = 32, return_h: bool = False)
     return (y, h) if return_h else y
 
 
-def moe_ffn(cfg, x: np.ndarray, idx: np.ndarray, w: np.ndarray, experts: dict, x_is_bf16: bool = False):
+def moe_ffn(cfg, x: np.ndarray, idx: np.ndarray, w: np.ndarray, experts: dict, x_is_bf16: bool = False,
+            act_int8: bool = False):
     """The layer's FFN for S tokens given routing; ``experts`` maps expert id -> ExpertWeights
-    (id ``n_experts`` is the shared expert).  Returns y[S,H] fp64."""
+    (id ``n_experts`` is the shared expert).  act_int8: x and every h are quantised to int8 per
+    row before their matmuls.  Returns y[S,H] fp64."""
     S, H = x.shape
     E, k = cfg.n_experts, cfg.top_k
     arrs = [[None] * (E + 1) for _ in range(6)]
@@ -162,8 +189,9 @@ def moe_ffn(cfg, x: np.ndarray, idx: np.ndarray, w: np.ndarray, experts: dict, x
     x = np.ascontiguousarray(x)
     idx = np.ascontiguousarray(idx, np.int32)
     w = np.ascontiguousarray(w, np.float64)
-    rc = lib().oracle_moe_ffn_fmt(fmt, S, H, E, k, cfg.moe_inter, cfg.shared_inter, cfg.group_size, int(x_is_bf16),
-                                  _p(x), _p(idx), _p(w), *[ctypes.cast(pp, ctypes.c_void_p) for pp in ptrs], _p(y))
+    rc = lib().oracle_moe_ffn_mode(fmt, int(act_int8), S, H, E, k, cfg.moe_inter, cfg.shared_inter, cfg.group_size,
+                                   int(x_is_bf16), _p(x), _p(idx), _p(w),
+                                   *[ctypes.cast(pp, ctypes.c_void_p) for pp in ptrs], _p(y))
     if rc:
         raise ValueError("oracle_moe_ffn: routing names an expert without weights")
     return y

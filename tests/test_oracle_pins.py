@@ -452,3 +452,109 @@ def test_row_scale_power_of_two_is_exact(fmt):
     assert list(changed) == [5]
     ex3 = gen.ExpertWeights(ex.inter, ex.qg, ex.sg, ex.qu, ex.su, ex.qd, ex.sd * 2, fmt)
     assert np.array_equal(O.expert_ffn(ex3, x, c.hidden), 2 * y)
+
+
+# ------------------------------------------------------ int8 activations (IDOT)
+# [PORT] "G2 implementation status": Colibri's IDOT=1 quantises each activation
+# row to int8 before the packed-int4 dot product (about 0.3 % extra RMS error per
+# matmul); the oracle's reading: d = amax / 127, q = rint(v / d), both in fp32.
+
+def test_quant_row_grid_values_are_exact():
+    k = np.arange(-127, 128)
+    v = (k * 2.0 ** -3).astype(np.float32)
+    q, d, out = O.quant_row(v)
+    assert d == np.float32(2.0 ** -3)
+    assert np.array_equal(q, k.astype(np.int8)) and np.array_equal(out, v.astype(np.float64))
+
+
+def test_quant_row_ties_to_even_and_whole_row_scale():
+    v = np.array([127.0, 2.5, 3.5, -2.5, 0.5, -0.5, 1.5, 0.4, -126.6], np.float32)
+    q, d, out = O.quant_row(v)
+    assert d == np.float32(1.0)
+    assert q.tolist() == [127, 2, 4, -2, 0, 0, 2, 0, -127]
+    # the scale is the whole row's: the same small values in a row of small values keep their resolution
+    q2, d2, _ = O.quant_row(np.array([2.5, 0.4, -1.27], np.float32))
+    assert d2 == np.float32(np.float32(2.5) / np.float32(127)) and q2[0] == 127 and q2[1] != 0
+
+
+def test_quant_row_zero_row():
+    q, d, out = O.quant_row(np.zeros(64, np.float32))
+    assert d == 0.0 and not q.any() and not out.any()
+
+
+def test_int8act_grid_input_gives_the_exact_gate_up():
+    """With x on the quantisation grid the gate/up products (h before its own
+    quantisation) equal the exact path's bitwise."""
+    c = gen.TINY
+    ex = gen.expert_weights(gen.WORKLOADS["tiny"], 0, 3)
+    rng = np.random.default_rng(4)
+    k = rng.integers(-127, 128, c.hidden)
+    k[0] = 127
+    x = (k * 2.0 ** -5).astype(np.float32)
+    _, h_q = O.expert_ffn_int8act(ex, x, c.hidden, return_h=True)
+    _, h_e = O.expert_ffn(ex, x.astype(np.float64), c.hidden, return_h=True)
+    assert np.array_equal(h_q, h_e)
+
+
+def test_int8act_down_uses_the_quantised_hidden_row():
+    """One-hot int8 weights: y_j = ad_j * sd_j * hhat[cd_j], where hhat is h (closed
+    form) rounded to fp32 and quantised with the whole row's scale."""
+    c = gen.LayerConfig(**{**gen.TINY.__dict__, "weight_format": 2})
+    H, I = c.hidden, c.moe_inter
+    rng = np.random.default_rng(17)
+    ex = gen.empty_expert(c, I)
+    for q in (ex.qg, ex.qu, ex.qd):
+        q[:] = 0
+    cg, cu, cd = rng.integers(0, H, I), rng.integers(0, H, I), rng.integers(0, I, H)
+    ag, au, ad = rng.integers(-128, 128, I), rng.integers(-128, 128, I), rng.integers(-128, 128, H)
+    ex.qg[np.arange(I), cg] = ag
+    ex.qu[np.arange(I), cu] = au
+    ex.qd[np.arange(H), cd] = ad
+    for s in (ex.sg, ex.su, ex.sd):
+        s[:] = np.abs(rng.normal(0, 0.01, s.size)).astype(np.float32)
+    kx = rng.integers(-127, 128, H)
+    kx[5] = -127
+    x = (kx * 2.0 ** -6).astype(np.float32)  # on the grid: x is its own quantisation
+    y, h = O.expert_ffn_int8act(ex, x, H, return_h=True)
+    for r in range(I):
+        g = float(ag[r]) * float(ex.sg[r]) * float(x[cg[r]])
+        u = float(au[r]) * float(ex.su[r]) * float(x[cu[r]])
+        assert h[r] == pytest.approx(g / (1.0 + math.exp(-g)) * u, rel=1e-14, abs=1e-300)
+    h32 = h.astype(np.float32)
+    amax = float(np.abs(h32).max())
+    d = float(np.float32(np.float32(amax) / np.float32(127.0)))
+    hhat = np.array([float(np.rint(np.float32(v) / np.float32(d))) * d for v in h32])
+    for j in range(H):
+        assert y[j] == pytest.approx(float(ad[j]) * float(ex.sd[j]) * hhat[cd[j]], rel=1e-14, abs=1e-300)
+    assert not np.allclose(hhat, h)  # the quantisation really changes h
+
+
+def test_int8act_error_is_the_pages_order():
+    """Extra RMS error of one expert in int8-activation mode, relative to the exact
+    output: the pages quote about 0.3 % per matmul; a per-row int8 grid on Gaussian
+    activations gives a few tenths of a percent to about one percent."""
+    w = gen.WORKLOADS["tiny"].with_(cfg=gen.LayerConfig(**{**gen.TINY.__dict__, "hidden": 2048, "moe_inter": 512}))
+    ex = gen.expert_weights(w, 0, 1)
+    errs = []
+    for t in range(4):
+        x = gen.tokens(w, step=t)[0]
+        y_e = O.expert_ffn(ex, x.astype(np.float64), w.cfg.hidden)
+        y_q = O.expert_ffn_int8act(ex, x, w.cfg.hidden)
+        errs.append(np.sqrt(np.mean((y_q - y_e) ** 2)) / np.sqrt(np.mean(y_e ** 2)))
+    assert 1e-3 < np.mean(errs) < 2e-2, errs
+
+
+def test_int8act_layer_is_the_weighted_sum_of_int8act_experts():
+    w = gen.WORKLOADS["tiny"].with_(tokens=3)
+    c = w.cfg
+    x = gen.tokens(w)
+    idx, wt, _, _, _ = O.route(c, x, gen.router_weights(w), gen.router_bias(w))
+    experts = {e: gen.expert_weights(w, 0, e) for e in set(idx.ravel().tolist()) | {c.n_experts}}
+    y = O.moe_ffn(c, x, idx, wt, experts, act_int8=True)
+    for t in range(3):
+        ref = np.zeros(c.hidden)
+        for j in range(c.top_k):
+            ref += wt[t, j] * O.expert_ffn_int8act(experts[idx[t, j]], x[t], c.hidden)
+        ref += O.expert_ffn_int8act(experts[c.n_experts], x[t], c.hidden)
+        assert np.array_equal(y[t], ref)
+    assert not np.array_equal(y, O.moe_ffn(c, x, idx, wt, experts))
