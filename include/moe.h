@@ -74,7 +74,7 @@ enum moe_weight_format { MOE_WF_Q4_G32 = 0, MOE_WF_Q4_ROW = 1, MOE_WF_Q8_ROW = 2
  *  Is = 0 (no shared expert) or in [32, 8192]; group_size = 32;
  *  1 <= n_experts E <= 1024, n_group G divides E, 1 <= topk_group Gk <= G <= 64,
  *  1 <= top_k k <= min(16, Gk * E / G); norm_topk_prob 0 or 1;
- *  routed_scaling_factor finite; weight_format a moe_weight_format. */
+ *  routed_scaling_factor finite; weight_format a moe_weight_format; act_int8 0 or 1. */
 typedef struct moe_cfg {
   int32_t hidden;
   int32_t n_experts;
@@ -93,6 +93,14 @@ typedef struct moe_cfg {
   int32_t mfma_min_tokens;
   /* moe_weight_format of every expert of the layer (routed and shared). */
   int32_t weight_format;
+  /* 1: int8 activations, an approximate mode ([PORT] "G2 implementation status":
+   * Colibri's IDOT=1 quantises each activation row to int8 before the packed-int4
+   * dot product; [README] "Integer-dot kernels").  Each token's x and each
+   * (token, expert) hidden row h (in fp32) is replaced by q * d with
+   * d = fp32(max|v| / 127) and q = rint(fp32(v / d)) in [-127, 127] (a row with a
+   * NaN gets d = NaN); the dot products of q with the weights are exact integers.
+   * 0: the exact contract (no activation quantisation). */
+  int32_t act_int8;
 } moe_cfg;
 
 /* Where the routed experts live.  Expert e's packed weights start at

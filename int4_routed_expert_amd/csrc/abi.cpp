@@ -114,6 +114,12 @@ WsLayout ws_layout(const moe_cfg &c, int32_t S) {
     L.mtiles = off; off += align256((size_t)L.max_mtiles * 3 * sizeof(int32_t));
     L.xb = off; off += align256((size_t)S * c.hidden * sizeof(uint16_t));
   }
+  if (c.act_int8) {
+    L.xq = off; off += align256((size_t)S * c.hidden);
+    L.dx = off; off += align256((size_t)S * sizeof(float));
+    L.hq = off; off += align256((size_t)S * k1 * imax);
+    L.dh = off; off += align256((size_t)S * k1 * sizeof(float));
+  }
   L.total = std::max<size_t>(off, 256);
   return L;
 }
@@ -135,7 +141,8 @@ int moe_validate_cfg(const moe_cfg *c) {
                   (c->norm_topk_prob == 0 || c->norm_topk_prob == 1) && std::isfinite(c->routed_scaling_factor) &&
                   c->mfma_min_tokens >= 0 &&
                   (c->weight_format == MOE_WF_Q4_G32 || c->weight_format == MOE_WF_Q4_ROW ||
-                   c->weight_format == MOE_WF_Q8_ROW);
+                   c->weight_format == MOE_WF_Q8_ROW) &&
+                  (c->act_int8 == 0 || c->act_int8 == 1);
   return ok ? MOE_OK : MOE_EINVAL;
 }
 
@@ -401,6 +408,7 @@ static int ffn_args(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S,
   a.H = c->hidden; a.E = c->n_experts; a.k = c->top_k; a.I = c->moe_inter; a.Is = c->shared_inter; a.S = S;
   a.x_bf16 = x_dtype == MOE_BF16;
   a.wf = c->weight_format;
+  a.act_q = c->act_int8;
   a.x = x; a.idx = idx; a.w = w;
   a.base = (const uint8_t *)ex->base; a.slot_bytes = ex->slot_bytes; a.table = ex->table; a.n_slots = ex->n_slots;
   a.shared = (const uint8_t *)shared;
@@ -414,6 +422,12 @@ static int ffn_args(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S,
   a.eptr = (uint64_t *)(b + L.eptr);
   a.n_cu = device_cus();
   if (S >= 2) a.part = (float *)(b + L.part);
+  if (a.act_q) {
+    a.xq = (int8_t *)(b + L.xq);
+    a.dx = (float *)(b + L.dx);
+    a.hq = (int8_t *)(b + L.hq);
+    a.dh = (float *)(b + L.dh);
+  }
   if (S <= kSmallS) {
     // one-token down kernel: about one row block per compute unit, at most 8 tiles each
     const int nt = c->hidden / kDnRows;
@@ -428,7 +442,8 @@ static int ffn_args(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S,
     a.mtiles = (int32_t *)(b + L.mtiles);
     a.xb = (uint16_t *)(b + L.xb);
     a.max_mtiles = L.max_mtiles;
-    a.mfma_thr = c->mfma_min_tokens;
+    // int8 activations run every expert on the exact-integer GEMV items
+    a.mfma_thr = c->act_int8 ? 0 : c->mfma_min_tokens;
   }
   return MOE_OK;
 }

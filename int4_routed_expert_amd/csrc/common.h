@@ -69,6 +69,7 @@ struct RouteArgs {
 struct FfnArgs {
   int H, E, k, I, Is, S, x_bf16;
   int wf;  // moe_weight_format
+  int act_q;  // int8 activations: x and h rows quantised (xq/dx, hq/dh) before their matmuls
   const void *x;
   const int32_t *idx;
   const float *w;
@@ -95,6 +96,11 @@ struct FfnArgs {
   float *xf;
   uint32_t *hl;    // h: S*(k+1) rows of Imax/32 groups
   float *hf;
+  // int8 activations: quantised rows and their scales
+  int8_t *xq;      // [S, H]
+  float *dx;       // [S]
+  int8_t *hq;      // [S * (k+1), Imax]
+  float *dh;       // [S * (k+1)]
   // one-token decode path
   uint64_t *eptr;  // [k] routed experts' packed weights (0: not resident), resolved by the gate/up kernel
   int32_t n_blk;   // row blocks of the down kernel
@@ -148,7 +154,9 @@ hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st);   // S > kSmallS
 hipError_t launch_gu_mfma(const FfnArgs &a, hipStream_t st);
 hipError_t launch_dn_mfma(const FfnArgs &a, hipStream_t st);
 hipError_t launch_to_limbs(const void *src, int src_bf16, int rows, int K, int src_stride, uint32_t *limbs,
-                           float *factors, int wf, hipStream_t st);
+                           float *factors, int wf, const int8_t *q, const float *dq, hipStream_t st);
+hipError_t launch_quant_x(const FfnArgs &a, hipStream_t st);  // x -> xq, dx (int8 activations)
+hipError_t launch_quant_h(const FfnArgs &a, hipStream_t st);  // h -> hq, dh (int8 activations)
 hipError_t launch_pack(int H, int I, const uint8_t *qg, const uint16_t *sg, const uint8_t *qu, const uint16_t *su,
                        const uint8_t *qd, const uint16_t *sd, uint8_t *dst, hipStream_t st);
 hipError_t launch_pack_rows(int H, int I, int wf, const uint8_t *qg, const float *sg, const uint8_t *qu,
@@ -156,7 +164,8 @@ hipError_t launch_pack_rows(int H, int I, int wf, const uint8_t *qg, const float
 
 // workspace layout (bytes, each region 256-aligned)
 struct WsLayout {
-  size_t sync, logits, scores, keys, h, xl, xf, hl, hf, eptr, part, lists, counts, items, n_items, mtiles, xb, total;
+  size_t sync, logits, scores, keys, h, xl, xf, hl, hf, eptr, part, lists, counts, items, n_items, mtiles, xb, xq, dx,
+      hq, dh, total;
   int32_t max_items, max_mtiles;
 };
 WsLayout ws_layout(const moe_cfg &c, int32_t S);

@@ -36,17 +36,23 @@ namespace moe {
 namespace {
 
 // ---- activations -> limbs (global), one thread per (row, group) ---------------
+// q != null: int8 activations, the rows' quantised integers q (same layout as
+// src) and their scales dq.
 template <int WF>
 __global__ __launch_bounds__(256) void k_to_limbs(const void *src, int bf16, int rows, int K, int stride,
-                                                  uint32_t *limbs, float *factors) {
+                                                  uint32_t *limbs, float *factors, const int8_t *q,
+                                                  const float *dq) {
   const int ng = K / kGroup;
   const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (long)rows * ng) return;
   const int r = (int)(i / ng), g = (int)(i - (long)r * ng);
   float v[32];
-  load32(src, bf16, (size_t)r * stride + (size_t)g * kGroup, v);
+  const size_t off = (size_t)r * stride + (size_t)g * kGroup;
+  if (q) load32_i8(q + off, v);
+  else load32(src, bf16, off, v);
   Limbs L;
   to_limbs_wf<WF>(v, L);
+  if (q) L.f *= ldg<float>(dq + r);
   uint4 *d = (uint4 *)(limbs + (size_t)i * 24);
 #pragma unroll
   for (int l = 0; l < 6; ++l) stg<uint4>(d + l, make_uint4(L.L[l][0], L.L[l][1], L.L[l][2], L.L[l][3]));
@@ -85,6 +91,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
     if (has_x) {
       Limbs L;
       to_limbs_wf<WF>(v, L);
+      L.f *= act_scale(a, true, 0);
       store_limbs(lds + (size_t)threadIdx.x * 24, lf + threadIdx.x, L);
     }
   };
@@ -93,7 +100,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
     const SelCfg c{a.E, a.G, a.Gk, a.k, a.norm, a.rsf};
     SelIn<EPT> in;
     sel_load<EPT, true>(c, a.keys, a.scores, a.table, in);
-    load32(a.x, a.x_bf16, (size_t)min((int)threadIdx.x, ng - 1) * kGroup, v);
+    load_act32(a, true, (size_t)min((int)threadIdx.x, ng - 1) * kGroup, v);
     const bool early = n > 0 && ns >= 1;  // a first feature of the shared expert needs no selection
     if (early) gu_feat_load(b0, a, 0, n, ns, s0, r0, 0, lane);
     stage_x();
@@ -111,7 +118,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
     // Order (loads return in order): lane j's expert id, the activations, then
     // the expert's slot; all unconditional (clamped) so the waits are exact.
     const int e_raw = ldg<int>(a.idx + min(lane, a.k - 1));
-    load32(a.x, a.x_bf16, (size_t)min((int)threadIdx.x, ng - 1) * kGroup, v);
+    load_act32(a, true, (size_t)min((int)threadIdx.x, ng - 1) * kGroup, v);
     const bool e_ok = lane < a.k && e_raw >= 0 && e_raw < a.E;
     const int slot = ldg<int>(a.table + (e_ok ? e_raw : 0));
     my_ptr = e_ok && slot >= 0 && slot < a.n_slots ? (uint64_t)(uintptr_t)(a.base + (size_t)slot * (size_t)a.slot_bytes)
@@ -189,7 +196,7 @@ __global__ __launch_bounds__(dn_s1_waves(WF) * 64) void k_down_s1(FfnArgs a) {
     use = HLDS && i < NE * ngm && g * kGroup < (e2 == a.k ? a.Is : a.I);
     // unconditional (a group that is not used reads group 0 and is dropped), so
     // that the waits for the loads issued before it can be exact
-    load32(a.h, 0, use ? (size_t)e2 * Imax + (size_t)g * kGroup : 0, v);
+    load_act32(a, false, use ? (size_t)e2 * Imax + (size_t)g * kGroup : 0, v);
   };
   // unit -> expert, tile, weights (clamped: units past U repeat the last unit and are not computed)
   struct Unit {
@@ -233,6 +240,7 @@ __global__ __launch_bounds__(dn_s1_waves(WF) * 64) void k_down_s1(FfnArgs a) {
   if (use_h) {
     Limbs L;
     to_limbs_wf<WF>(hv0, L);
+    L.f *= act_scale(a, false, (int)threadIdx.x / ngm);
     store_limbs(hlds + (size_t)threadIdx.x * 24, hf_lds + threadIdx.x, L);
   }
   for (int i = threadIdx.x + blockDim.x; HLDS && i < NE * ngm; i += blockDim.x) {
@@ -241,6 +249,7 @@ __global__ __launch_bounds__(dn_s1_waves(WF) * 64) void k_down_s1(FfnArgs a) {
     if (use_h) {
       Limbs L;
       to_limbs_wf<WF>(v, L);
+      L.f *= act_scale(a, false, i / ngm);
       store_limbs(hlds + (size_t)i * 24, hf_lds + i, L);
     }
   }
@@ -473,8 +482,8 @@ __global__ __launch_bounds__(kGuSmallWaves * 64) void k_gateup_small(FfnArgs a) 
   // activations of group threadIdx.x (and + blockDim.x) of the S tokens, loaded first
   float v0[32], v1[32];
   const int i0 = threadIdx.x, i1 = threadIdx.x + blockDim.x;
-  load32(a.x, a.x_bf16, (size_t)min(i0, nx - 1) * kGroup, v0);
-  load32(a.x, a.x_bf16, (size_t)min(i1, nx - 1) * kGroup, v1);
+  load_act32(a, true, (size_t)min(i0, nx - 1) * kGroup, v0);
+  load_act32(a, true, (size_t)min(i1, nx - 1) * kGroup, v1);
   const int W = gridDim.x * (blockDim.x >> 6), wid = blockIdx.x * (blockDim.x >> 6) + wave;
   const long Ps = (long)a.S * a.Is;
   const int sp0 = (int)(wid * Ps / W), ns = (int)((wid + 1) * Ps / W) - sp0;
@@ -502,18 +511,21 @@ __global__ __launch_bounds__(kGuSmallWaves * 64) void k_gateup_small(FfnArgs a) 
   if (i0 < nx) {
     Limbs L;
     to_limbs_wf<WF>(v0, L);
+    L.f *= act_scale(a, true, i0 / ng);
     store_limbs(xlds + (size_t)i0 * kXs, xf_lds + i0, L);
   }
   if (i1 < nx) {
     Limbs L;
     to_limbs_wf<WF>(v1, L);
+    L.f *= act_scale(a, true, i1 / ng);
     store_limbs(xlds + (size_t)i1 * kXs, xf_lds + i1, L);
   }
   for (int i = threadIdx.x + 2 * blockDim.x; i < nx; i += blockDim.x) {  // S * H/32 > 2 * blockDim
     float v[32];
-    load32(a.x, a.x_bf16, (size_t)i * kGroup, v);
+    load_act32(a, true, (size_t)i * kGroup, v);
     Limbs L;
     to_limbs_wf<WF>(v, L);
+    L.f *= act_scale(a, true, i / ng);
     store_limbs(xlds + (size_t)i * kXs, xf_lds + i, L);
   }
   __syncthreads();
@@ -651,8 +663,9 @@ __global__ __launch_bounds__(kDnSmallWaves * 64) void k_down_small(FfnArgs a) {
       for (int g2 = 0; g2 < NGD; ++g2) {  // lanes past the last group repeat it with a zero factor
         const int g = min(lane + 64 * g2, ngi - 1);
         float v[32];
-        load32(a.h, 0, (size_t)uu.pair * Imax + (size_t)g * kGroup, v);
+        load_act32(a, false, (size_t)uu.pair * Imax + (size_t)g * kGroup, v);
         to_limbs_wf<WF>(v, hv[g2]);
+        hv[g2].f *= act_scale(a, false, uu.pair);
         if (lane + 64 * g2 >= ngi) hv[g2].f = 0.f;
       }
     }
@@ -858,10 +871,10 @@ __global__ __launch_bounds__(256) void k_item_limbs(FfnArgs a) {
     const int pair = e == a.E ? (it[1] + tt) * (a.k + 1) + a.k : a.lists[(size_t)e * a.S + it[1] + tt];
     const int row = X ? pair / (a.k + 1) : pair;
     float v[32];
-    if (X) load32(a.x, a.x_bf16, (size_t)row * a.H + (size_t)g * kGroup, v);
-    else load32(a.h, 0, (size_t)row * Imax + (size_t)g * kGroup, v);
+    load_act32(a, X, X ? (size_t)row * a.H + (size_t)g * kGroup : (size_t)row * Imax + (size_t)g * kGroup, v);
     Limbs L;
     to_limbs_wf<WF>(v, L);
+    L.f *= act_scale(a, X, row);
     uint32_t *dl = (X ? a.xl : a.hl) + ((size_t)row * ng + g) * 24;
 #pragma unroll
     for (int l = 0; l < 6; ++l) stg<uint4>((uint4 *)dl + l, make_uint4(L.L[l][0], L.L[l][1], L.L[l][2], L.L[l][3]));
@@ -963,17 +976,94 @@ __global__ __launch_bounds__(256) void k_combine(FfnArgs a) {
   stg<float4>(a.y + (size_t)t * a.H + c, bad ? make_float4(nan, nan, nan, nan) : acc);
 }
 
+// int8 activations: one workgroup per row.  Row r (elements r * stride ...) has
+// `len` elements, or `len_last` when kp1 > 0 and r % kp1 == kp1 - 1 (the shared
+// expert's hidden row of a token); d = fp32(amax / 127) and q = rint(fp32(v / d)),
+// with IEEE divisions; a row holding a NaN gets d = NaN (its outputs stay NaN).
+__global__ __launch_bounds__(256) void k_quant_rows(const void *src, int bf16, int stride, int len, int len_last,
+                                                    int kp1, int8_t *q, float *d) {
+  __shared__ float s_max[4];
+  __shared__ int s_nan[4];
+  const int r = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = (kp1 > 0 && r % kp1 == kp1 - 1) ? len_last : len;
+  const size_t base = (size_t)r * stride;
+  auto load4 = [&](int c, float *v) {
+    if (bf16) {
+      const uint2 w = ldg<uint2>((const uint16_t *)src + base + c);
+      v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xFFFF0000u);
+      v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xFFFF0000u);
+    } else {
+      const float4 f = ldg<float4>((const float *)src + base + c);
+      v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+    }
+  };
+  float m = 0.f;
+  int nan = 0;
+  for (int c = threadIdx.x * 4; c < n; c += 1024) {  // n is a multiple of 32
+    float v[4];
+    load4(c, v);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      nan |= v[j] != v[j];
+      m = fmaxf(m, fabsf(v[j]));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    m = fmaxf(m, __shfl_xor(m, o));
+    nan |= __shfl_xor(nan, o);
+  }
+  if (lane == 0) {
+    s_max[wave] = m;
+    s_nan[wave] = nan;
+  }
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  const bool any_nan = (s_nan[0] | s_nan[1] | s_nan[2] | s_nan[3]) != 0;
+  const float dd = any_nan ? __builtin_nanf("") : __fdiv_rn(amax, 127.0f);
+  if (threadIdx.x == 0) stg<float>(d + r, dd);
+  for (int c = threadIdx.x * 4; c < n; c += 1024) {
+    float v[4];
+    load4(c, v);
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int qi = dd > 0.f ? (int)rintf(__fdiv_rn(v[j], dd)) : 0;
+      w |= ((uint32_t)qi & 0xFFu) << (8 * j);
+    }
+    stg<uint32_t>(q + base + c, w);
+  }
+}
+
 int ceil_groups(int K) { return (K / kGroup + 63) / 64; }
 
 }  // namespace
 
 hipError_t launch_to_limbs(const void *src, int src_bf16, int rows, int K, int src_stride, uint32_t *limbs,
-                           float *factors, int wf, hipStream_t st) {
+                           float *factors, int wf, const int8_t *q, const float *dq, hipStream_t st) {
   const long n = (long)rows * (K / kGroup);
   if (n == 0) return hipSuccess;
   const dim3 g((unsigned)((n + 255) / 256)), b(256);
-  if (wf == kWfQ8Row) MOE_LAUNCH(k_to_limbs<kWfQ8Row>, g, b, 0, st, src, src_bf16, rows, K, src_stride, limbs, factors);
-  else MOE_LAUNCH(k_to_limbs<kWfQ4G32>, g, b, 0, st, src, src_bf16, rows, K, src_stride, limbs, factors);
+  if (wf == kWfQ8Row)
+    MOE_LAUNCH(k_to_limbs<kWfQ8Row>, g, b, 0, st, src, src_bf16, rows, K, src_stride, limbs, factors, q, dq);
+  else
+    MOE_LAUNCH(k_to_limbs<kWfQ4G32>, g, b, 0, st, src, src_bf16, rows, K, src_stride, limbs, factors, q, dq);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_x(const FfnArgs &a, hipStream_t st) {
+  if (!a.act_q || a.S == 0) return hipSuccess;
+  ProfScope ps("quant_x", st);
+  MOE_LAUNCH(k_quant_rows, dim3((unsigned)a.S), dim3(256), 0, st, a.x, a.x_bf16, a.H, a.H, a.H, 0, a.xq, a.dx);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_h(const FfnArgs &a, hipStream_t st) {
+  if (!a.act_q || a.S == 0) return hipSuccess;
+  ProfScope ps("quant_h", st);
+  const int Imax = std::max(a.I, a.Is), kp1 = a.k + 1;
+  MOE_LAUNCH(k_quant_rows, dim3((unsigned)(a.S * kp1)), dim3(256), 0, st, (const void *)a.h, 0, Imax, a.I,
+             a.Is > 0 ? a.Is : a.I, kp1, a.hq, a.dh);
   return hipGetLastError();
 }
 
@@ -996,7 +1086,8 @@ hipError_t launch_to_limbs(const void *src, int src_bf16, int rows, int K, int s
   } while (0)
 hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st) {
   const int Imax = std::max(a.I, a.Is);
-  hipError_t e;
+  hipError_t e = launch_quant_x(a, st);
+  if (e != hipSuccess) return e;
   if (a.S == 1) {
     {
       ProfScope ps("gateup_s1", st);
@@ -1014,12 +1105,14 @@ hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st) {
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
+    e = launch_quant_h(a, st);
+    if (e != hipSuccess) return e;
     const int NE = a.k + (a.Is > 0 ? 1 : 0);
     const size_t hlds = (size_t)NE * (Imax / kGroup) * 25 * sizeof(uint32_t);
     const bool in_lds = hlds <= 64 * 1024;
     if (!in_lds) {
       ProfScope ps("h_limbs", st);
-      e = launch_to_limbs(a.h, 0, NE, Imax, Imax, a.hl, a.hf, a.wf, st);
+      e = launch_to_limbs(a.h, 0, NE, Imax, Imax, a.hl, a.hf, a.wf, a.act_q ? a.hq : nullptr, a.dh, st);
       if (e != hipSuccess) return e;
     }
     ProfScope ps("down_s1", st);
@@ -1038,6 +1131,8 @@ hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  e = launch_quant_h(a, st);
+  if (e != hipSuccess) return e;
   {
     ProfScope ps("down_small", st);
     const dim3 g2((unsigned)a.n_cu), b2(kDnSmallWaves * 64);
@@ -1052,7 +1147,8 @@ hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st) {
 
 hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st) {
   const int Imax = std::max(a.I, a.Is);
-  hipError_t e;
+  hipError_t e = launch_quant_x(a, st);
+  if (e != hipSuccess) return e;
   {
     ProfScope ps("bucket", st);
     MOE_LAUNCH(k_bucket, dim3(a.E), dim3(256), 0, st, a);
@@ -1077,6 +1173,8 @@ hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st) {
     MOE_DISPATCH_NG(ceil_groups(a.H), k_gateup_items, g, blk, 0, st);
   }
   e = launch_gu_mfma(a, st);
+  if (e != hipSuccess) return e;
+  e = launch_quant_h(a, st);
   if (e != hipSuccess) return e;
   {
     ProfScope ps("h_limbs", st);

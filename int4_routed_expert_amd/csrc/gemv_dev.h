@@ -35,6 +35,25 @@ __device__ inline void load32(const void *x, int bf16, size_t off, float *v) {
   }
 }
 
+// 32 int8 values (an int8-activation row's quantised integers) as floats, exact.
+__device__ inline void load32_i8(const int8_t *p, float *v) {
+  const uint4 r0 = ldg<uint4>(p), r1 = ldg<uint4>(p + 16);
+  const uint32_t d[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = (float)(int8_t)(d[i >> 2] >> (8 * (i & 3)));
+}
+
+// The activations of one group as the contraction sees them: the exact values,
+// or with int8 activations the row's quantised integers (the limbs' factor then
+// takes the row scale d: T * 2^-sh * d is the group's dot with q * d).
+__device__ inline void load_act32(const FfnArgs &a, bool x, size_t off, float *v) {
+  if (!a.act_q) load32(x ? a.x : (const void *)a.h, x ? a.x_bf16 : 0, off, v);
+  else load32_i8((x ? a.xq : a.hq) + off, v);
+}
+__device__ inline float act_scale(const FfnArgs &a, bool x, int row) {
+  return a.act_q ? ldg<float>((x ? a.dx : a.dh) + row) : 1.0f;
+}
+
 __device__ inline void store_limbs(uint32_t *dst, float *fdst, const Limbs &L) {
   uint4 *d = (uint4 *)dst;
 #pragma unroll

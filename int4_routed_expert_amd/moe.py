@@ -34,7 +34,7 @@ class moe_cfg(ctypes.Structure):
                 ("topk_group", ctypes.c_int32), ("top_k", ctypes.c_int32), ("moe_inter", ctypes.c_int32),
                 ("shared_inter", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("routed_scaling_factor", ctypes.c_float), ("norm_topk_prob", ctypes.c_int32),
-                ("mfma_min_tokens", ctypes.c_int32), ("weight_format", ctypes.c_int32)]
+                ("mfma_min_tokens", ctypes.c_int32), ("weight_format", ctypes.c_int32), ("act_int8", ctypes.c_int32)]
 
 
 class moe_slot_view(ctypes.Structure):
@@ -102,11 +102,11 @@ def lib() -> ctypes.CDLL:
 MFMA_MIN_TOKENS = 16  # default threshold of the matrix-core path (tokens per expert)
 
 
-def make_cfg(c, mfma_min_tokens: int = MFMA_MIN_TOKENS) -> moe_cfg:
+def make_cfg(c, mfma_min_tokens: int = MFMA_MIN_TOKENS, act_int8: int = 0) -> moe_cfg:
     """moe_cfg from any object with the LayerConfig field names."""
     return moe_cfg(c.hidden, c.n_experts, c.n_group, c.topk_group, c.top_k, c.moe_inter, c.shared_inter,
                    c.group_size, c.routed_scaling_factor, c.norm_topk_prob, mfma_min_tokens,
-                   getattr(c, "weight_format", MOE_WF_Q4_G32))
+                   getattr(c, "weight_format", MOE_WF_Q4_G32), act_int8)
 
 
 def ptr(t) -> int | None:

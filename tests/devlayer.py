@@ -18,11 +18,12 @@ class DeviceLayer:
     expert in its own buffer, router weights on the device."""
 
     def __init__(self, w: gen.Workload, layer: int = 0, experts=None, host_experts: bool = False,
-                 mfma_min_tokens: int = M.MFMA_MIN_TOKENS):
+                 mfma_min_tokens: int = M.MFMA_MIN_TOKENS, act_int8: int = 0):
         self.w = w
         c = w.cfg
         self.c = c
-        self.cfg = M.make_cfg(c, mfma_min_tokens)
+        self.act_int8 = act_int8
+        self.cfg = M.make_cfg(c, mfma_min_tokens, act_int8)
         E = c.n_experts
         self.slot_bytes = M.moe_expert_bytes(self.cfg, c.moe_inter)
         self.experts = list(range(E)) if experts is None else sorted(set(experts))
@@ -78,7 +79,7 @@ class DeviceLayer:
         """moe_ffn; mfma_min_tokens overrides the layer's threshold of the matrix-core path."""
         S = x.shape[0]
         ws = self.workspace(S) if ws is None else ws
-        cfg = self.cfg if mfma_min_tokens is None else M.make_cfg(self.c, mfma_min_tokens)
+        cfg = self.cfg if mfma_min_tokens is None else M.make_cfg(self.c, mfma_min_tokens, self.act_int8)
         y = torch.full((S, self.c.hidden), float("nan"), dtype=torch.float32, device="cuda")
         M.moe_ffn(cfg, x, x_dtype, S, idx, wt, self.view(table), self.shared, y, ws, ws.numel())
         return y

@@ -1,0 +1,101 @@
+"""int8-activation mode (moe_cfg.act_int8 = 1) on the GPU, through the C ABI,
+against the oracle's int8-activation mode: each token's x and each expert's
+hidden row h are quantised per row (d = amax / 127, q = rint(v / d)) before their
+matmuls.  The quantisation of x is decided in fp32 on both sides, so it agrees
+exactly; h is the GPU's fp32 result, which differs from the oracle's fp64 h
+rounded to fp32 by a few ulps, so an element of h that sits on a rounding tie of
+the int8 grid may land one step apart (a change of about d_h * |w| in the
+affected outputs: up to about d_h * max|Wd| / max|y|, a few 1e-3).  Bar: max
+relative error per token 5e-3, and the median over tokens below 1e-5 (the fp32
+level of the exact path)."""
+import numpy as np
+import pytest
+import torch
+
+from gen import inputs as gen
+from int4_routed_expert_amd import moe as M
+from oracle import oracle as O
+from tests.devlayer import DeviceLayer, max_rel_err, x_device
+from tests.test_gpu_parity import MID, check_route, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+TOL_MAX = 5e-3
+TOL_MEDIAN = 1e-5
+
+
+def fmt_workload(w: gen.Workload, fmt: int) -> gen.Workload:
+    return w.with_(cfg=gen.LayerConfig(**{**w.cfg.__dict__, "weight_format": fmt}))
+
+
+def check_int8act(dl: DeviceLayer, x_host, ridx, rw, y, tokens):
+    c = dl.c
+    need = set(ridx[tokens].ravel().tolist())
+    experts = {e: dl.host_expert(e) for e in need}
+    if c.shared_inter > 0:
+        experts[c.n_experts] = dl.host[c.n_experts]
+    bf = dl.w.x_dtype == "bf16"
+    xs = np.ascontiguousarray(x_host[tokens])
+    ref = O.moe_ffn(c, xs, ridx[tokens], rw[tokens], experts, x_is_bf16=bf, act_int8=True)
+    errs = [max_rel_err(y[t:t + 1], ref[i:i + 1]) for i, t in enumerate(tokens)]
+    exact = O.moe_ffn(c, xs, ridx[tokens], rw[tokens], experts, x_is_bf16=bf)
+    dev_from_exact = max_rel_err(ref, exact)
+    say(f"  int8-act: max rel err {max(errs):.3e}, median {np.median(errs):.3e} over {len(tokens)} tokens; "
+        f"oracle int8-act vs exact {dev_from_exact:.3e}")
+    assert max(errs) <= TOL_MAX and np.median(errs) <= TOL_MEDIAN
+    assert dev_from_exact > 10 * TOL_MEDIAN  # the mode really quantises
+
+
+@pytest.fixture(scope="module", params=[0, 1, 2], ids=["q4g32", "q4row", "q8row"])
+def tiny_q(request):
+    return DeviceLayer(fmt_workload(gen.WORKLOADS["tiny"], request.param), host_experts=True, mfma_min_tokens=0,
+                       act_int8=1)
+
+
+@pytest.mark.parametrize("S", [1, 2, 4, 5, 37])
+def test_tiny_layer(tiny_q, S):
+    x = gen.tokens(tiny_q.w.with_(tokens=S), step=300 + S)
+    idx, wt, y = run_gpu(tiny_q, x)
+    ridx, rw = check_route(tiny_q, x, idx, wt)
+    check_int8act(tiny_q, x, ridx, rw, y, np.arange(S))
+
+
+@pytest.mark.parametrize("fmt", [0, 2], ids=["q4g32", "q8row"])
+def test_mid_layer(fmt):
+    dl = DeviceLayer(fmt_workload(gen.Workload("mid", MID, tokens=67, seed=11), fmt), host_experts=True, act_int8=1)
+    for S in (1, 4, 67):
+        x = gen.tokens(dl.w.with_(tokens=S), step=500 + S)
+        idx, wt, y = run_gpu(dl, x)
+        ridx, rw = check_route(dl, x, idx, wt)
+        check_int8act(dl, x, ridx, rw, y, np.arange(S))
+
+
+def test_layer_call_and_poison(tiny_q):
+    x = gen.tokens(tiny_q.w.with_(tokens=3), step=9)
+    xt, dt = x_device(tiny_q.w, x)
+    idx, wt, y = tiny_q.layer(xt[:1], dt)
+    idx2, wt2 = tiny_q.route(xt[:1], dt)
+    assert torch.equal(y, tiny_q.ffn(xt[:1], dt, idx2, wt2))
+    idx3, wt3 = tiny_q.route(xt, dt)
+    ih = idx3.cpu().numpy()
+    table = tiny_q.table.clone()
+    table[int(ih[0, 0])] = -1
+    y3 = tiny_q.ffn(xt, dt, idx3, wt3, table=table).cpu().numpy()
+    hit = (ih == ih[0, 0]).any(axis=1)
+    assert np.isnan(y3[hit]).all(axis=1).all() and np.isfinite(y3[~hit]).all()
+
+
+@pytest.mark.parametrize("fmt", [0, 1], ids=["q4g32", "q4row"])
+def test_glm_shape_decode_and_verify(fmt):
+    say(f"packing 257 GLM-5.2-shaped experts (format {fmt})")
+    dl = DeviceLayer(fmt_workload(gen.WORKLOADS["decode"], fmt), act_int8=1)
+    for step in range(3):
+        x = gen.tokens(dl.w, step=step)
+        xt, dt = x_device(dl.w, x)
+        idx, wt, y = dl.layer(xt, dt)
+        ridx, rw = check_route(dl, x, idx.cpu().numpy(), wt.cpu().numpy())
+        check_int8act(dl, x, ridx, rw, y.cpu().numpy(), np.arange(1))
+    x = gen.tokens(dl.w.with_(tokens=4), step=60)
+    idx, wt, y = run_gpu(dl, x)
+    ridx, rw = check_route(dl, x, idx, wt)
+    check_int8act(dl, x, ridx, rw, y, np.arange(4))
