@@ -170,7 +170,7 @@ def bench_verify(args) -> int:
     from int4_routed_expert_amd import moe as M
     w = with_format(gen.WORKLOADS["verify"], args.weight_format)
     c, S = w.cfg, w.tokens
-    cfg = M.make_cfg(c)
+    cfg = M.make_cfg(c, act_int8=args.act_int8)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     layers = [pack_layer(w, l, dev, cfg) for l in range(args.layers)]
@@ -219,7 +219,7 @@ def bench_verify(args) -> int:
           "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
           "dtype": "f32", "data": "synthetic",
           "config": {"workload": "glm52_moe_layer_verify_S4", "tokens_per_call": S, "bias": w.bias_recipe,
-                     "quant": FORMAT_DESC[args.weight_format],
+                     "quant": FORMAT_DESC[args.weight_format] + (", int8 activations" if args.act_int8 else ""),
                      "layers_rotated": args.layers, "batches_rotated": nb, "launch": "hip graphs of 16 calls",
                      "call": "moe_layer" if args.call == "layer" else "moe_route + moe_ffn"},
           "union_mean": float(U.mean()), "union_min": int(U.min()), "union_max": int(U.max()),
@@ -268,7 +268,7 @@ def bench_prefill(args) -> int:
     from int4_routed_expert_amd import moe as M
     w = with_format(gen.WORKLOADS["prefill"], args.weight_format)
     c, S = w.cfg, w.tokens
-    cfg = M.make_cfg(c, args.mfma_min_tokens)
+    cfg = M.make_cfg(c, args.mfma_min_tokens, args.act_int8)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     L = pack_layer(w, 0, dev, cfg)
@@ -311,7 +311,7 @@ def bench_prefill(args) -> int:
           "ms_per_step": el * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
           "dtype": "f32", "data": "synthetic",
           "config": {"workload": "glm52_moe_layer_prefill_S2048", "tokens_per_call": S, "x": "bf16",
-                     "quant": FORMAT_DESC[args.weight_format],
+                     "quant": FORMAT_DESC[args.weight_format] + (", int8 activations" if args.act_int8 else ""),
                      "bias": w.bias_recipe, "batches_rotated": nb, "mfma_min_tokens": args.mfma_min_tokens},
           "experts_used": used, "effective_gbps": bytes_call / el / 1e9,
           "pct_hbm_peak": 100.0 * bytes_call / el / 1e9 / HBM_PEAK_GBPS,
@@ -332,7 +332,7 @@ def bench_stack(args) -> int:
     if args.blobs:
         w = w.with_(n_blobs=args.blobs)
     c = w.cfg
-    cfg = M.make_cfg(c)
+    cfg = M.make_cfg(c, act_int8=args.act_int8)
     E, I, NL, steps = c.n_experts, c.moe_inter, w.layers, args.stack_steps or w.steps
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -455,7 +455,7 @@ def bench_stack(args) -> int:
           "dtype": "f32", "data": "synthetic",
           "config": {"workload": "glm52_moe_stack_75_layers_decode", "layers": NL, "steps": steps,
                      "slots_per_layer": spl, "pool_gb": NL * spl * sb / 1e9, "distinct_blobs": w.n_blobs,
-                     "bias": w.bias_recipe, "prefetch": bool(args.prefetch), "quant": FORMAT_DESC[args.weight_format],
+                     "bias": w.bias_recipe, "prefetch": bool(args.prefetch), "quant": FORMAT_DESC[args.weight_format] + (", int8 activations" if args.act_int8 else ""),
                      "launch": ("eager; next layer routed ahead and prefetched" if args.prefetch
                                 else "eager; host sync per layer for residency")},
           "tokens_per_s_warm": (steps - 1) / warm_el if steps > 1 else None,
@@ -488,6 +488,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--weight-format", default="q4g32", choices=list(FORMATS),
                     help="expert format: int4 + fp16 per 32 (default), int4 + fp32 per row, int8 + fp32 per row")
+    ap.add_argument("--act-int8", type=int, default=0, choices=[0, 1],
+                    help="1: int8 activations (approximate mode: x and h quantised per row)")
     ap.add_argument("--steps", type=int, default=4096)
     ap.add_argument("--warmup", type=int, default=512)
     ap.add_argument("--layers", type=int, default=4, help="resident layer instances rotated per step")
@@ -524,7 +526,7 @@ def main() -> int:
     fmt = args.weight_format
     w = with_format(gen.WORKLOADS["decode"], fmt)
     c = w.cfg
-    cfg = M.make_cfg(c)
+    cfg = M.make_cfg(c, act_int8=args.act_int8)
     E, H, I, k = c.n_experts, c.hidden, c.moe_inter, c.top_k
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -670,7 +672,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": "glm52_moe_layer_decode_S1", "hidden": H, "n_experts": E, "n_group": c.n_group,
                    "topk_group": c.topk_group, "top_k": k, "moe_inter": I, "shared_inter": c.shared_inter,
-                   "quant": FORMAT_DESC[fmt], "layers_rotated": args.layers, "tokens_rotated": args.tokens,
+                   "quant": FORMAT_DESC[fmt] + (", int8 activations" if args.act_int8 else ""), "layers_rotated": args.layers, "tokens_rotated": args.tokens,
                    "launch": "hip graphs of 16 steps",
                    "call": "moe_layer" if args.call == "layer" else "moe_route + moe_ffn"},
         "effective_gbps": gbps,

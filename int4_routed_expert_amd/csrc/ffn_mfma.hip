@@ -401,6 +401,234 @@ __global__ __launch_bounds__(kThreads) void k_dn_mfma(FfnArgs a) {
       }
 }
 
+// ---- int8 activations with row-scaled weights: integer matrix cores ---------------
+// With one scale per weight row and one per activation row, a whole row of K
+// products accumulates exactly in int32 (|sum| <= K * 127 * 128 < 2^31 for K <=
+// 8192), so the tile runs v_mfma_i32_16x16x64_i8 over int8 activations (the
+// quantised rows) and int8 weights (int4 nibbles sign-extended to bytes, or the
+// int8 weights themselves) and scales once in the epilogue:
+// y = fp32(acc) * d_row * s_col.  Lane layout (checked on the GPU against a host
+// matmul): A lane l = (row l % 16, k 16 (l / 16) .. + 15), B lane l = (column
+// l % 16, the same k), D as for the bf16 MFMA.  A pipeline stage is K = 64 (two
+// quantisation groups, one MFMA per 16 x 16 block); the two threads of a B column
+// each write one group's 32 bytes into LDS.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBStageI8 = kNT * kBStride;  // one 64-byte column (+ 16 padding) per output column
+
+// Eight int4 weights (two's-complement nibbles, element 2j in the low nibble of
+// byte j) as eight int8 in element order: each nibble is sign-extended within
+// its byte (n | (bit 3 of n) * 0x1E0 / 0x10), then the low- and high-nibble bytes
+// are interleaved.
+__device__ inline uint2 nib_to_i8(uint32_t w) {
+  uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  lo |= (lo & 0x08080808u) * 0x1Eu;
+  hi |= (hi & 0x08080808u) * 0x1Eu;
+  return make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u));
+}
+
+struct GemmAccI {
+  i32x4 acc[kMB][kNB];
+};
+
+template <int kDepth, int MBV, int WF>
+__device__ inline void gemm_loop_i8(GemmAccI &C, int ng, const uint8_t *const *s_colp, uint8_t *s_b,
+                                    const int8_t *abase, const size_t *arow, int wn, int lane) {
+  const int tid = threadIdx.x;
+  const int bc = tid >> 1, bp = tid & 1;  // this thread writes group 2 st + bp of B column bc
+  const uint8_t *colp = s_colp[bc];
+  const int kq = lane >> 4;               // this lane's 16-byte quarter of the stage's K = 64
+  const int ns = (ng + 1) / 2;            // stages
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) C.acc[mb][nb] = i32x4{0, 0, 0, 0};
+  auto load_b = [&](int st) {
+    QGroup<WF> r;
+    load_group(r, colp, min(st * 2 + bp, ng - 1));
+    return r;
+  };
+  auto store_b = [&](int buf, const QGroup<WF> &r) {
+    uint8_t *d = s_b + buf * kBStageI8 + bc * kBStride + bp * 32;
+    if constexpr (WF == kWfQ8Row) {
+      *(uint4 *)(d) = r.q[0];
+      *(uint4 *)(d + 16) = r.q[1];
+    } else {
+      const uint2 a0 = nib_to_i8(r.q[0].x), a1 = nib_to_i8(r.q[0].y), a2 = nib_to_i8(r.q[0].z),
+                  a3 = nib_to_i8(r.q[0].w);
+      *(uint4 *)(d) = make_uint4(a0.x, a0.y, a1.x, a1.y);
+      *(uint4 *)(d + 16) = make_uint4(a2.x, a2.y, a3.x, a3.y);
+    }
+  };
+  // activations of stage st: this lane's 16 bytes of K (clamped to the last group)
+  auto load_a = [&](int st, uint4 (&r)[kMB]) {
+    const int g = min(st * 2 + (kq >> 1), ng - 1);
+#pragma unroll
+    for (int mb = 0; mb < MBV; ++mb) r[mb] = ldg<uint4>(abase + arow[mb] + (size_t)g * 32 + (kq & 1) * 16);
+  };
+  uint4 aq[kMB];
+  QGroup<WF> bq[kDepth];
+  load_a(0, aq);
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) bq[d] = load_b(d);
+  store_b(0, bq[0]);
+  bq[0] = load_b(kDepth);
+  __syncthreads();
+  const int nsp = (ns + kDepth - 1) / kDepth * kDepth;
+  for (int st = 0; st < nsp; st += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int s = st + d;
+      const uint8_t *sb = s_b + (s & 1) * kBStageI8 + (wn * 16 * kNB) * kBStride;
+      // a lane whose group is past the last one (odd group count, padded stages) contributes zero
+      const uint32_t live = s * 2 + (kq >> 1) < ng ? ~0u : 0u;
+      i32x4 A[kMB];
+#pragma unroll
+      for (int mb = 0; mb < MBV; ++mb)
+        A[mb] = __builtin_bit_cast(i32x4, make_uint4(aq[mb].x & live, aq[mb].y & live, aq[mb].z & live, aq[mb].w & live));
+      load_a(s + 1, aq);
+      if (MBV > 0) {
+#pragma unroll
+        for (int n4 = 0; n4 < kNB; n4 += 4) {
+          i32x4 B[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            B[q] = __builtin_bit_cast(i32x4, *(const uint4 *)(sb + ((n4 + q) * 16 + (lane & 15)) * kBStride + kq * 16));
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int mb = 0; mb < MBV; ++mb)
+              C.acc[mb][n4 + q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[mb], B[q], C.acc[mb][n4 + q], 0, 0, 0);
+          asm volatile("" ::: "memory");
+        }
+      }
+      store_b((s + 1) & 1, bq[(d + 1) % kDepth]);
+      bq[(d + 1) % kDepth] = load_b(s + 1 + kDepth);
+      __syncthreads();
+    }
+  }
+}
+
+template <int kDepth, int WF>
+__device__ inline void gemm_rows_i8(GemmAccI &C, int rows, int ng, const uint8_t *const *s_colp, uint8_t *s_b,
+                                    const int8_t *abase, const size_t *arow, int wave, int lane) {
+  const int nblk = (rows + 15) / 16, band = wave % kWM, wn = wave / kWM;
+  const int mbv = min(kMB, max(0, (nblk - band + kWM - 1) / kWM));
+  switch (mbv) {
+    case 2: gemm_loop_i8<kDepth, 2, WF>(C, ng, s_colp, s_b, abase, arow, wn, lane); break;
+    case 1: gemm_loop_i8<kDepth, 1, WF>(C, ng, s_colp, s_b, abase, arow, wn, lane); break;
+    default: gemm_loop_i8<kDepth, 0, WF>(C, ng, s_colp, s_b, abase, arow, wn, lane); break;
+  }
+}
+
+// Gate/up with int8 activations: h[pair][feature] = silu(g) * u in fp32 (the
+// down projection quantises h per row).
+template <int WF>
+__global__ __launch_bounds__(kThreads) void k_gu_mfma_i8(FfnArgs a) {
+  __shared__ __align__(16) uint8_t s_b[2 * kBStageI8];
+  __shared__ const uint8_t *s_colp[kNT];
+  __shared__ float s_cs[kNT];
+  __shared__ int s_tok[kMT], s_pair[kMT];
+  int m, nt;
+  tile_of_block((2 * max(a.I, a.Is) + kNT - 1) / kNT, m, nt);
+  const int n_mt = a.n_items[2] + a.n_items[3];
+  if (m >= n_mt) return;
+  const MTile mt = mtile_of(a, m);
+  const bool sh = mt.e == a.E;
+  const int inter = sh ? a.Is : a.I;
+  if (nt * (kNT / 2) >= inter) return;
+  const uint8_t *ex = sh ? a.shared : expert_ptr(a, mt.e);
+  if (!ex) return;  // the down GEMM poisons this tile's rows
+  const int Imax = max(a.I, a.Is);
+  const size_t gtb = gu_tile_bytes(a.H, WF), rb = row_bytes(a.H, WF);
+  if (threadIdx.x < kNT) {
+    const int c = threadIdx.x;
+    const int tt = min(nt * (kNT / 8) + c / 8, inter / kGuPairs - 1);
+    const uint8_t *tile = ex + (size_t)tt * gtb;
+    s_colp[c] = tile + (size_t)(c % 8) * rb;
+    s_cs[c] = ldg<float>(tile + (size_t)kGuRows * rb + 4 * (c % 8));
+  }
+  tile_rows(a, mt, s_tok, s_pair);
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wn = wave / kWM;
+  size_t arow[kMB];
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb) arow[mb] = (size_t)s_tok[row_of(wave, mb, lane & 15)] * a.H;
+  GemmAccI C;
+  gemm_rows_i8<3, WF>(C, mt.n, a.H / kGroup, s_colp, s_b, a.xq, arow, wave, lane);
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = row_of(wave, mb, (lane >> 4) * 4 + i);
+      const float dxr = ldg<float>(a.dx + s_tok[min(j, mt.n - 1)]);
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        const int c = wn * 16 * kNB + nb * 16 + (lane & 15);
+        const float gv = (float)C.acc[mb][nb][i] * dxr * s_cs[c];
+        const float uv = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(gv), 0xB1, 0xF, 0xF, false));
+        const int f = nt * (kNT / 2) + (c / 8) * kGuPairs + (c % 8) / 2;
+        if ((c & 1) == 0 && j < mt.n && f < inter) a.h[(size_t)s_pair[j] * Imax + f] = gv / (1.0f + expf(-gv)) * uv;
+      }
+    }
+}
+
+// Down with int8 activations (the quantised h rows): part[pair][row] = acc * dh * s.
+template <int WF>
+__global__ __launch_bounds__(kThreads) void k_dn_mfma_i8(FfnArgs a) {
+  __shared__ __align__(16) uint8_t s_b[2 * kBStageI8];
+  __shared__ const uint8_t *s_colp[kNT];
+  __shared__ float s_cs[kNT];
+  __shared__ int s_tok[kMT], s_pair[kMT];
+  int m, nt;
+  tile_of_block((a.H + kNT - 1) / kNT, m, nt);
+  const int n_mt = a.n_items[2] + a.n_items[3];
+  if (m >= n_mt) return;
+  const MTile mt = mtile_of(a, m);
+  const bool sh = mt.e == a.E;
+  const int inter = sh ? a.Is : a.I;
+  const int n0 = nt * kNT;
+  const uint8_t *ex = sh ? a.shared : expert_ptr(a, mt.e);
+  tile_rows(a, mt, s_tok, s_pair);
+  if (!ex) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < mt.n * kNT; i += blockDim.x) {
+      const int j = i / kNT, n = n0 + i % kNT;
+      if (n < a.H) a.part[(size_t)s_pair[j] * a.H + n] = __builtin_nanf("");
+    }
+    return;
+  }
+  const int Imax = max(a.I, a.Is);
+  if (threadIdx.x < kNT) {
+    const int n = min(n0 + (int)threadIdx.x, a.H - 1);
+    const size_t rb = row_bytes(inter, WF);
+    const uint8_t *tile = ex + down_offset(a.H, inter, WF) + (size_t)(n / kDnRows) * dn_tile_bytes(inter, WF);
+    s_colp[threadIdx.x] = tile + (size_t)(n % kDnRows) * rb;
+    s_cs[threadIdx.x] = ldg<float>(tile + (size_t)kDnRows * rb + 4 * (n % kDnRows));
+  }
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wn = wave / kWM;
+  size_t arow[kMB];
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb) arow[mb] = (size_t)s_pair[row_of(wave, mb, lane & 15)] * Imax;
+  GemmAccI C;
+  gemm_rows_i8<2, WF>(C, mt.n, inter / kGroup, s_colp, s_b, a.hq, arow, wave, lane);
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = row_of(wave, mb, (lane >> 4) * 4 + i);
+      const float dhr = ldg<float>(a.dh + s_pair[min(j, mt.n - 1)]);
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        const int c = wn * 16 * kNB + nb * 16 + (lane & 15);
+        const int n = n0 + c;
+        if (j < mt.n && n < a.H) a.part[(size_t)s_pair[j] * a.H + n] = (float)C.acc[mb][nb][i] * dhr * s_cs[c];
+      }
+    }
+}
+
 // fp32 activations -> bf16 (RNE), eight per thread.
 __global__ __launch_bounds__(256) void k_x_to_bf16(const float *x, uint16_t *xb, long n8) {
   const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -413,6 +641,13 @@ __global__ __launch_bounds__(256) void k_x_to_bf16(const float *x, uint16_t *xb,
 
 hipError_t launch_gu_mfma(const FfnArgs &a, hipStream_t st) {
   if (a.mfma_thr <= 0 || a.max_mtiles <= 0) return hipSuccess;
+  if (a.act_q) {  // int8 activations: row-scaled formats only (the threshold is 0 otherwise)
+    ProfScope ps("gateup_mfma", st);
+    const dim3 g(tile_blocks(a.max_mtiles, (2 * std::max(a.I, a.Is) + kNT - 1) / kNT));
+    if (a.wf == kWfQ8Row) MOE_LAUNCH(k_gu_mfma_i8<kWfQ8Row>, g, dim3(kThreads), 0, st, a);
+    else MOE_LAUNCH(k_gu_mfma_i8<kWfQ4Row>, g, dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+  }
   if (!a.x_bf16) {
     ProfScope ps("x_bf16", st);
     const long n8 = (long)a.S * a.H / 8;
@@ -434,6 +669,12 @@ hipError_t launch_gu_mfma(const FfnArgs &a, hipStream_t st) {
 hipError_t launch_dn_mfma(const FfnArgs &a, hipStream_t st) {
   if (a.mfma_thr <= 0 || a.max_mtiles <= 0) return hipSuccess;
   ProfScope ps("down_mfma", st);
+  if (a.act_q) {
+    const dim3 g(tile_blocks(a.max_mtiles, (a.H + kNT - 1) / kNT));
+    if (a.wf == kWfQ8Row) MOE_LAUNCH(k_dn_mfma_i8<kWfQ8Row>, g, dim3(kThreads), 0, st, a);
+    else MOE_LAUNCH(k_dn_mfma_i8<kWfQ4Row>, g, dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+  }
   const dim3 g(tile_blocks(a.max_mtiles, (a.H + kNT - 1) / kNT));
   switch (a.wf) {
     case kWfQ4Row: MOE_LAUNCH(k_dn_mfma<kWfQ4Row>, g, dim3(kThreads), 0, st, a); break;

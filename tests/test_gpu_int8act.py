@@ -99,3 +99,42 @@ def test_glm_shape_decode_and_verify(fmt):
     idx, wt, y = run_gpu(dl, x)
     ridx, rw = check_route(dl, x, idx, wt)
     check_int8act(dl, x, ridx, rw, y, np.arange(4))
+
+
+@pytest.mark.parametrize("fmt", [1, 2], ids=["q4row", "q8row"])
+@pytest.mark.parametrize("S,thr", [(37, 4), (67, 4), (300, 16)])
+def test_matrix_core_path(fmt, S, thr):
+    """Row-scaled weights with int8 activations: experts over the threshold run the
+    integer matrix-core GEMM (exact int32 sums, scaled once); the others the GEMV
+    items.  Both against the oracle's int8-activation mode."""
+    base = gen.WORKLOADS["tiny"] if S == 37 else gen.Workload("mid", MID, tokens=S, seed=11)
+    dl = DeviceLayer(fmt_workload(base, fmt), host_experts=True, mfma_min_tokens=thr, act_int8=1)
+    w = dl.w.with_(tokens=S)
+    x = gen.tokens(w, step=700 + S)
+    xt, dt = x_device(w, x)
+    idx, wt = dl.route(xt, dt)
+    y_mfma = dl.ffn(xt, dt, idx, wt).cpu().numpy()
+    y_gemv = dl.ffn(xt, dt, idx, wt, mfma_min_tokens=0).cpu().numpy()
+    ridx, rw = check_route(dl, x, idx.cpu().numpy(), wt.cpu().numpy())
+    counts = np.bincount(ridx.ravel(), minlength=dl.c.n_experts)
+    say(f"S={S}: {(counts >= thr).sum()} experts at or over {thr} tokens")
+    assert (counts >= thr).any()
+    check_int8act(dl, x, ridx, rw, y_mfma, np.arange(S))
+    check_int8act(dl, x, ridx, rw, y_gemv, np.arange(S))
+    assert not np.array_equal(y_mfma, y_gemv)
+
+
+def test_glm_shape_batch_row_scales():
+    """2048 bf16 tokens, GLM-5.2 shape, int4 with row scales, int8 activations: the
+    integer matrix-core path for the many-token experts; sampled tokens."""
+    w = fmt_workload(gen.WORKLOADS["decode"], 1).with_(x_dtype="bf16", tokens=2048)
+    dl = DeviceLayer(w, act_int8=1)
+    x = gen.tokens(w)
+    idx, wt, y = run_gpu(dl, x)
+    ridx, rw = check_route(dl, x, idx, wt)
+    counts = np.bincount(ridx.ravel(), minlength=w.cfg.n_experts)
+    say(f"experts with >= 16 tokens: {(counts >= 16).sum()}")
+    hot = int(np.argmax(counts))
+    tokens = np.array(sorted({0, 777, 2047, int(np.where((ridx == hot).any(axis=1))[0][0])}))
+    check_int8act(dl, x, ridx, rw, y, tokens)
+    assert np.isfinite(y).all()
