@@ -495,7 +495,7 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=4, help="resident layer instances rotated per step")
     ap.add_argument("--tokens", type=int, default=1024, help="distinct tokens rotated per step")
     ap.add_argument("--profile-steps", type=int, default=512)
-    ap.add_argument("--mfma-min-tokens", type=int, default=16,
+    ap.add_argument("--mfma-min-tokens", type=int, default=8,
                     help="prefill: experts with at least this many tokens use the matrix cores")
     ap.add_argument("--call", default="layer", choices=["layer", "split"],
                     help="decode and verify: one moe_layer call per step, or moe_route then moe_ffn")

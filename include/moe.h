@@ -201,7 +201,11 @@ int moe_route(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, con
  * to fp32, scaled by the group's scale (MOE_WF_Q4_G32) and summed in fp32; the
  * row-scaled formats multiply the row's sum by its scale instead.  Larger
  * batches use the same for experts with fewer than mfma_min_tokens tokens and
- * bf16 MFMA (fp32 accumulation) for the others. */
+ * bf16 MFMA (fp32 accumulation) for the others.  With act_int8 the quantised
+ * integers take the activations' place in the same exact dot products (the row
+ * scale folds into each group's factor); larger batches with row-scaled weights
+ * send the many-token experts to int8 MFMA (exact int32 row sums, scaled once),
+ * and with MOE_WF_Q4_G32 weights every expert stays on the exact path. */
 int moe_ffn(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, const int32_t *idx, const float *w,
             const moe_slot_view *experts, const void *shared, float *y, void *ws, size_t ws_bytes, void *stream);
 
