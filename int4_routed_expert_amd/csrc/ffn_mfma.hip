@@ -11,19 +11,22 @@
 // scale per row and group of 32) and down row tiles of eight output rows.
 //
 // Tiles: a workgroup (8 waves) owns up to 256 token rows of one expert's list
-// (kMT) and 256 output columns (kNT); wave w computes four 16-row blocks (row
-// band w % 4) x 128 columns (half w / 4) of it.  Every wave reads its half of
-// the dequantised B stage from LDS, so the LDS reads per MFMA are half those of
-// a 32 x 256 wave tile (at 32 x 256 the CU's LDS bandwidth matched the
-// matrix-core time exactly); activation rows are read once per 128 columns.  One MFMA contracts exactly one
+// (kMT) and 256 output columns (kNT); wave w computes two 16-row blocks (blocks
+// w and w + 8, so that a partial tile's rows spread over all SIMDs) x all 256
+// columns.  Every wave reads the whole dequantised B stage from LDS (at this
+// wave tile the CU's LDS read bandwidth and its matrix-core time per stage are
+// about equal; a 64 x 128 wave tile halves the LDS reads but doubles the
+// activation loads and measured slower).  One MFMA contracts exactly one
 // quantisation group (K = 32), so each lane's B fragment carries a single
-// scale.  A pipeline stage is two groups: the two lanes of a B column read its
-// 32 contiguous nibble bytes of the stage and each dequantises one group (32
-// values: exact n*s - 8s in fp32, then round-to-nearest-even to bf16) into LDS,
-// read by all eight waves; A fragments (token rows, 8 consecutive K per lane)
-// come straight from global memory.  Weights and activations come from a
-// register ring two stages deep; one barrier per stage (double-buffered B,
-// 80 KB of LDS).
+// scale.  A pipeline stage is two groups: the two threads of a B column read its
+// contiguous weight bytes of the stage and each dequantises one group (32
+// values: n*s - 8s in fp32, exact for fp16 scales, then round-to-nearest-even to
+// bf16) into LDS, read by all eight waves; A fragments (token rows, 8
+// consecutive K per lane) come straight from global memory.  Weights come from a
+// register ring three stages deep for gate/up (two for down), activations one
+// stage ahead; one barrier per stage (double-buffered B, 80 KB of LDS).  The
+// weight format is a template parameter (row scales: one fp32 scale per column,
+// loaded once; int8 weights: 32 bytes per group).
 //
 // Gate/up: column c of an N tile is tile row c % 8 of gate/up tile c / 8, so
 // gate and up of a feature sit in adjacent lanes of the accumulator layout;
