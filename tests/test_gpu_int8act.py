@@ -138,3 +138,43 @@ def test_glm_shape_batch_row_scales():
     tokens = np.array(sorted({0, 777, 2047, int(np.where((ridx == hot).any(axis=1))[0][0])}))
     check_int8act(dl, x, ridx, rw, y, tokens)
     assert np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("S", [1, 3])
+def test_layer_call_graph_replays(tiny_q, S):
+    """moe_layer with int8 activations captured in a HIP graph (the quantisation
+    kernels included): replays with new inputs, each bitwise equal to the eager
+    call on the same input and workspace."""
+    dl = tiny_q
+    c = dl.c
+    ws = dl.workspace(S)
+    xbuf = torch.empty((S, c.hidden), dtype=torch.float32, device="cuda")
+    idx = torch.empty((S, c.top_k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((S, c.top_k), dtype=torch.float32, device="cuda")
+    y = torch.empty((S, c.hidden), dtype=torch.float32, device="cuda")
+    view = dl.view()
+
+    def call():
+        M.moe_layer(dl.cfg, xbuf, M.MOE_F32, S, dl.W, dl.bias, idx, wt, view, dl.shared, y, ws, ws.numel())
+
+    xs = [torch.from_numpy(gen.tokens(dl.w.with_(tokens=S), step=950 + i)).cuda() for i in range(4)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        xbuf.copy_(xs[0])
+        call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    for i in range(1, 4):
+        xbuf.copy_(xs[i])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (idx.clone(), wt.clone(), y.clone())
+        i_e, w_e, y_e = dl.layer(xs[i], M.MOE_F32, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], i_e) and torch.equal(got[1], w_e) and torch.equal(got[2], y_e), i
+        assert torch.isfinite(y_e).all()

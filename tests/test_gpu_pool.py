@@ -33,7 +33,7 @@ def run_stack(w: gen.Workload, n_layers: int, steps: int, spl: int, flags: int, 
         for e in range(E):
             ex = gen.expert_weights(w, l, e)
             hostw[(l, e)] = ex
-            M.moe_pack_expert(cfg, I, *ex.parts(), host[l * E + e].numpy(), 0)
+            M.pack_expert(cfg, I, *ex.parts(), host[l * E + e].numpy(), 0)
     pool = M.Pool(cfg, n_layers, spl, flags)
     for l in range(n_layers):
         for e in range(E):
@@ -42,7 +42,7 @@ def run_stack(w: gen.Workload, n_layers: int, steps: int, spl: int, flags: int, 
     for l in range(n_layers):
         sh = gen.expert_weights(w, l, E)
         shared = torch.zeros(M.moe_expert_bytes(cfg, c.shared_inter), dtype=torch.uint8, device="cuda")
-        M.moe_pack_expert(cfg, c.shared_inter, *[dev(a) for a in sh.parts()], shared, 1)
+        M.pack_expert(cfg, c.shared_inter, *[dev(a) for a in sh.parts()], shared, 1)
         layers.append(dict(W=gen.router_weights(w, l), b=gen.router_bias(w, l), shared=shared, shared_h=sh))
     torch.cuda.synchronize()
     compute = torch.cuda.current_stream()
@@ -126,3 +126,14 @@ def test_pool_prefetch_is_value_preserving(n_layers):
     assert nxt["prefetch_fills"] > 0 and nxt["prefetch_hits"] > 0 and bad["prefetch_fills"] > 0
     if n_layers > 1:  # exact predictions of other layers: acquires after the first one only hit
         assert nxt["misses"] <= w.cfg.top_k
+
+
+@pytest.mark.parametrize("fmt", [1, 2], ids=["q4row", "q8row"])
+def test_pool_row_scaled_experts(fmt):
+    """The slot pool with row-scaled experts (slots sized by the format), heavy
+    churn and poisoned refills: every (step, layer) matches the oracle."""
+    cfg = gen.LayerConfig(**{**MID.__dict__, "weight_format": fmt})
+    w = gen.Workload("stack-mid", cfg, tokens=1, bias_recipe="hotset", layers=3, steps=5, seed=47)
+    st, worst, n, _ = run_stack(w, n_layers=3, steps=5, spl=5, flags=M.MOE_POOL_POISON)
+    print("pool stats", st, "worst", worst, "checked", n, flush=True)
+    assert st["misses"] > 3 * 4 and st["evictions"] > 0
