@@ -48,8 +48,8 @@ constexpr int kMT = kMfmaTileTokens;  // token rows per workgroup tile
 constexpr int kNT = 256;              // output columns per workgroup tile
 constexpr int kWM = 8;                // row bands of a tile (wave w: band w % kWM)
 constexpr int kWN = kWaves / kWM;     // column parts of a tile (wave w: part w / kWM)
-constexpr int kMB = 2;                // MFMA row blocks (16 rows) per wave: 32 rows
-constexpr int kNB = 16;               // MFMA column blocks (16 columns) per wave: 256 columns
+constexpr int kMB = kMT / 16 / kWM;   // MFMA row blocks (16 rows) per wave
+constexpr int kNB = kNT / 16 / kWN;   // MFMA column blocks (16 columns) per wave
 constexpr int kKG = 2;                // quantisation groups (K = 32 each) per pipeline stage
 constexpr int kBStride = 80;          // bytes per column of an LDS B group (64 + 16 padding: no bank conflicts)
 // The second group of a stage starts 64 bytes past the first group's end: the
@@ -274,6 +274,8 @@ __device__ inline void gemm_rows(GemmAcc &C, int rows, int ng, const uint8_t *co
   const int nblk = (rows + 15) / 16, band = wave % kWM, wn = wave / kWM;
   const int mbv = min(kMB, max(0, (nblk - band + kWM - 1) / kWM));  // valid blocks band, band + kWM, ...
   switch (mbv) {
+    case 4: if constexpr (kMB >= 4) gemm_loop<ABF, kDepth, 4, WF>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
+    case 3: if constexpr (kMB >= 3) gemm_loop<ABF, kDepth, 3, WF>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
     case 2: gemm_loop<ABF, kDepth, 2, WF>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
     case 1: gemm_loop<ABF, kDepth, 1, WF>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
     default: gemm_loop<ABF, kDepth, 0, WF>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
@@ -517,6 +519,8 @@ __device__ inline void gemm_rows_i8(GemmAccI &C, int rows, int ng, const uint8_t
   const int nblk = (rows + 15) / 16, band = wave % kWM, wn = wave / kWM;
   const int mbv = min(kMB, max(0, (nblk - band + kWM - 1) / kWM));
   switch (mbv) {
+    case 4: if constexpr (kMB >= 4) gemm_loop_i8<kDepth, 4, WF>(C, ng, s_colp, s_b, abase, arow, wn, lane); break;
+    case 3: if constexpr (kMB >= 3) gemm_loop_i8<kDepth, 3, WF>(C, ng, s_colp, s_b, abase, arow, wn, lane); break;
     case 2: gemm_loop_i8<kDepth, 2, WF>(C, ng, s_colp, s_b, abase, arow, wn, lane); break;
     case 1: gemm_loop_i8<kDepth, 1, WF>(C, ng, s_colp, s_b, abase, arow, wn, lane); break;
     default: gemm_loop_i8<kDepth, 0, WF>(C, ng, s_colp, s_b, abase, arow, wn, lane); break;
