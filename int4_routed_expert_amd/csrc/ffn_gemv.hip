@@ -8,10 +8,14 @@
 // "What's implemented" (batch-union MoE): every unique expert of the batch is
 // read once and applied to all tokens that chose it.
 //
-// Every weight group is contracted with the exact integer dot product of dot.h.
-// All paths use the same per-token arithmetic in the same order (lane groups in
-// order, then one fixed wave reduction, then the route-order combine), so a
-// token's output does not depend on which other tokens share its batch.
+// Every weight group is contracted with the exact integer dot product of dot.h,
+// for each weight format (template parameter WF: int4 with fp16 scales per 32,
+// int4 or int8 with one fp32 scale per row).  With int8 activations
+// (k_quant_rows) the quantised integers take the activations' place and the
+// row scale folds into each group's factor.  All paths use the same per-token
+// arithmetic in the same order (lane groups in order, then one fixed wave
+// reduction, then the route-order combine), so a token's output does not depend
+// on which other tokens share its batch.
 //
 // One token (the decode step): two streaming kernels.
 //  * k_gateup_s1: the work is the list of features (gate row r and up row r of
