@@ -120,6 +120,18 @@ def test_expert_bytes_row_formats():
     assert M.moe_validate_cfg(bad) == M.MOE_EINVAL
 
 
+def test_int8_activation_flag_and_workspace():
+    c = M.make_cfg(gen.GLM52, act_int8=1)
+    assert M.moe_validate_cfg(c) == M.MOE_OK
+    for v in (2, -1):
+        c.act_int8 = v
+        assert M.moe_validate_cfg(c) == M.MOE_EINVAL
+    # the quantised rows (S*H + S*(k+1)*Imax bytes) and their scales come on top of the exact-mode workspace
+    for S in (1, 4, 2048):
+        extra = M.moe_workspace_bytes(M.make_cfg(gen.GLM52, act_int8=1), S) - M.moe_workspace_bytes(M.make_cfg(gen.GLM52), S)
+        assert extra >= S * 6144 + S * 9 * 2048 + S * 4 + S * 9 * 4
+
+
 @pytest.mark.parametrize("fmt", [M.MOE_WF_Q4_ROW, M.MOE_WF_Q8_ROW])
 @pytest.mark.parametrize("base", [gen.TINY, gen.LayerConfig(hidden=96, n_experts=4, n_group=2, topk_group=1,
                                                                 top_k=2, moe_inter=64, shared_inter=32)])
