@@ -61,9 +61,13 @@ constexpr int kBStage = kKG * kBGroup;
 constexpr int kBParts = kThreads / kNT;  // threads that dequantise one column of a group (8 bytes each)
 static_assert(kMT == kWM * 16 * kMB && kNT == kWN * 16 * kNB && kKG == 2 && kBParts == kKG, "tile shape");
 
+// Two fp32 values as bf16 (RNE), lo in the low half: one v_cvt_pk_bf16_f32 (two
+// scalar conversions would cost a shift and an or on top).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Eight int4 weights (slot layout: two's-complement nibbles, element 2j in the
@@ -72,7 +76,10 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
 // times an 11-bit significand), so the only rounding is the final one to bf16.
 __device__ inline uint4 dequant8(uint32_t w, float s) {
   const uint32_t u = w ^ 0x88888888u;
-  const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
+  uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
+  // kept opaque so that each element converts straight from its byte
+  // (v_cvt_f32_ubyte1..3) instead of a bit-field extract per element
+  asm volatile("" : "+v"(lo), "+v"(hi));
   const float m8 = -8.0f * s;
   float v[8];
 #pragma unroll
@@ -225,8 +232,8 @@ __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_col
   // the MFMAs of group gi of stage s (they come mostly from L2); B of stage s is
   // requested kDepth stages before it is dequantised into LDS (one stage before
   // its MFMAs).  Loads are clamped to the last group, so every one is
-  // unconditional; groups past the last one (an odd group count, padding to a
-  // multiple of kDepth stages) multiply zeroed A fragments.
+  // unconditional; the MFMAs of groups past the last one (an odd group count,
+  // padding to a multiple of kDepth stages) are skipped.
   ARaw<ABF> aq[kKG][kMB];
   BRaw bq[kDepth];
 #pragma unroll
@@ -244,15 +251,12 @@ __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_col
       const uint8_t *sb = s_b + (s & 1) * kBStage + (wn * 16 * kNB) * kBStride;
 #pragma unroll
       for (int gi = 0; gi < kKG; ++gi) {
-        const uint32_t live = s * kKG + gi < ng ? ~0u : 0u;
         bf16x8 A[kMB];
 #pragma unroll
-        for (int mb = 0; mb < MBV; ++mb) {
-          const uint4 v = __builtin_bit_cast(uint4, aq[gi][mb].get());
-          A[mb] = __builtin_bit_cast(bf16x8, make_uint4(v.x & live, v.y & live, v.z & live, v.w & live));
-        }
-        // rows past the tile's end repeat its last row; not stored
-        if (MBV > 0) group_mfma<MBV>(C, A, sb + gi * kBGroup, lane, oct);
+        for (int mb = 0; mb < MBV; ++mb) A[mb] = aq[gi][mb].get();
+        // rows past the tile's end repeat its last row (not stored); groups past
+        // the last one (a wave-uniform condition) are skipped
+        if (MBV > 0 && s * kKG + gi < ng) group_mfma<MBV>(C, A, sb + gi * kBGroup, lane, oct);
         load_a(s + 1, gi, aq[gi]);  // after the MFMAs: the slot's registers are free again
       }
       store_b((s + 1) & 1, bq[(d + 1) % kDepth]);
