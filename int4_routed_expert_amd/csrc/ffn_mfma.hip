@@ -160,21 +160,29 @@ struct GemmAcc {
 // One quantisation group's MFMAs for the first MBV row blocks of this wave:
 // A[mb] holds the group's activations of row block mb, sb the group's
 // dequantised B columns of this wave.  B fragments are read from LDS four at a
-// time (a compiler fence between the chunks keeps the reads from all being
-// hoisted, which would exhaust registers).
+// time, one chunk ahead of the MFMAs that use them (a compiler fence between the
+// chunks keeps the reads from all being hoisted, which would exhaust registers).
 template <int MBV>
 __device__ inline void group_mfma(GemmAcc &C, const bf16x8 (&A)[kMB], const uint8_t *sb, int lane, int oct) {
+  auto frag = [&](int n) {
+    return __builtin_bit_cast(bf16x8, *(const uint4 *)(sb + (n * 16 + (lane & 15)) * kBStride + oct * 16));
+  };
+  bf16x8 B[2][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) B[0][q] = frag(q);
 #pragma unroll
   for (int n4 = 0; n4 < kNB; n4 += 4) {
-    bf16x8 B[4];
+    const int cur = (n4 / 4) & 1;
+    // the next four fragments are requested before this chunk's MFMAs
+    if (n4 + 4 < kNB) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      B[q] = __builtin_bit_cast(bf16x8, *(const uint4 *)(sb + ((n4 + q) * 16 + (lane & 15)) * kBStride + oct * 16));
+      for (int q = 0; q < 4; ++q) B[cur ^ 1][q] = frag(n4 + 4 + q);
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int mb = 0; mb < MBV; ++mb)
-        C.acc[mb][n4 + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb], B[q], C.acc[mb][n4 + q], 0, 0, 0);
+        C.acc[mb][n4 + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb], B[cur][q], C.acc[mb][n4 + q], 0, 0, 0);
     asm volatile("" ::: "memory");
   }
 }
