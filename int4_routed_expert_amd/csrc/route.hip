@@ -70,27 +70,41 @@ __global__ __launch_bounds__(256) void k_route_logits_tiled(RouteArgs a) {
     wd[0] = make_float2(w.x, w.y);
     wd[1] = make_float2(w.z, w.w);
   };
-  float4 px, pw;
-  load_x(0, px);
-  pw = *(const float4 *)(wrow + wc);
-  stage(0, px, pw);
+  // chunks are requested kPf chunks before they are staged (a chunk's MFMAs take
+  // well under one global-load latency)
+  constexpr int kPf = 3;
+  const int nk = a.H / kLK;
+  float4 px[kPf], pw[kPf];
+#pragma unroll
+  for (int d = 0; d < kPf; ++d) {
+    const int k0 = min(d, nk - 1) * kLK;
+    load_x(k0, px[d]);
+    pw[d] = *(const float4 *)(wrow + k0 + wc);
+  }
+  stage(0, px[0], pw[0]);
   __syncthreads();
   f64x4 acc = {0.0, 0.0, 0.0, 0.0};
   const int tb = (wave & 1) * 16, eb = (wave >> 1) * 16, kq = lane >> 4;
-  const int nk = a.H / kLK;
-  for (int kc = 0; kc < nk; ++kc) {
-    const int kn = min(kc + 1, nk - 1) * kLK;  // unconditional prefetch (the last one repeats)
-    load_x(kn, px);
-    pw = *(const float4 *)(wrow + kn + wc);
-    const int b = kc & 1;
+  for (int kc0 = 0; kc0 < nk; kc0 += kPf) {
 #pragma unroll
-    for (int kk = 0; kk < kLK; kk += 4) {
-      const double av = (double)xs[b][tb + (lane & 15)][kk + kq];
-      const double bv = (double)wsm[b][eb + (lane & 15)][kk + kq];
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+    for (int d = 0; d < kPf; ++d) {
+      const int kc = kc0 + d;
+      if (kc < nk) {  // uniform
+        // the slot of chunk kc was staged; it now receives chunk kc + kPf (the last one repeats)
+        const int kn = min(kc + kPf, nk - 1) * kLK;
+        load_x(kn, px[d]);
+        pw[d] = *(const float4 *)(wrow + kn + wc);
+        const int b = kc & 1;
+#pragma unroll
+        for (int kk = 0; kk < kLK; kk += 4) {
+          const double av = (double)xs[b][tb + (lane & 15)][kk + kq];
+          const double bv = (double)wsm[b][eb + (lane & 15)][kk + kq];
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+        }
+        stage(b ^ 1, px[(d + 1) % kPf], pw[(d + 1) % kPf]);
+        __syncthreads();
+      }
     }
-    stage(b ^ 1, px, pw);
-    __syncthreads();
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
