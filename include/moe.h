@@ -146,7 +146,11 @@ int moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
  * Gate and up are [inter, H], down is [H, inter].  dst receives
  * moe_expert_bytes(cfg, inter) bytes.  where = 0: all pointers are host memory and
  * the packing runs on the CPU (stream ignored); where = 1: all pointers are device
- * memory and a kernel packs on `stream`. */
+ * memory and a kernel packs on `stream`.  The device packer writes the packed
+ * bytes only (the slot's padding up to moe_expert_bytes is left as it was).
+ * cfg->weight_format must be MOE_WF_Q4_G32 (MOE_EINVAL otherwise; the row-scaled
+ * formats use moe_pack_expert_rows).  Errors: MOE_EINVAL (configuration, inter,
+ * where), MOE_ENULL, MOE_EHIP. */
 int moe_pack_expert(const moe_cfg *cfg, int32_t inter, const uint8_t *q_gate, const uint16_t *s_gate,
                     const uint8_t *q_up, const uint16_t *s_up, const uint8_t *q_down, const uint16_t *s_down,
                     void *dst, int32_t where, void *stream);
