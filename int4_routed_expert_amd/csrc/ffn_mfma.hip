@@ -433,13 +433,13 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBStageI8 = kNT * kBStride;  // one 64-byte column (+ 16 padding) per output column
 
 // Eight int4 weights (two's-complement nibbles, element 2j in the low nibble of
-// byte j) as eight int8 in element order: each nibble is sign-extended within
-// its byte (n | (bit 3 of n) * 0x1E0 / 0x10), then the low- and high-nibble bytes
-// are interleaved.
+// byte j) as eight int8 in element order: each nibble n becomes the byte
+// ((n ^ 8) + 0x78) ^ 0x80 = n - 16 (n >= 8) or n (no carry leaves a byte), then
+// the low- and high-nibble bytes are interleaved.
 __device__ inline uint2 nib_to_i8(uint32_t w) {
   uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-  lo |= (lo & 0x08080808u) * 0x1Eu;
-  hi |= (hi & 0x08080808u) * 0x1Eu;
+  lo = ((lo ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u;
+  hi = ((hi ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u;
   return make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u));
 }
 
@@ -496,12 +496,17 @@ __device__ inline void gemm_loop_i8(GemmAccI &C, int ng, const uint8_t *const *s
     for (int d = 0; d < kDepth; ++d) {
       const int s = st + d;
       const uint8_t *sb = s_b + (s & 1) * kBStageI8 + (wn * 16 * kNB) * kBStride;
-      // a lane whose group is past the last one (odd group count, padded stages) contributes zero
-      const uint32_t live = s * 2 + (kq >> 1) < ng ? ~0u : 0u;
+      // a lane whose group is past the last one (odd group count, padded stages)
+      // contributes zero; the masking is needed only in such a stage (uniform)
+      if (s * 2 + 1 >= ng) {
+        const uint32_t live = s * 2 + (kq >> 1) < ng ? ~0u : 0u;
+#pragma unroll
+        for (int mb = 0; mb < MBV; ++mb)
+          aq[mb] = make_uint4(aq[mb].x & live, aq[mb].y & live, aq[mb].z & live, aq[mb].w & live);
+      }
       i32x4 A[kMB];
 #pragma unroll
-      for (int mb = 0; mb < MBV; ++mb)
-        A[mb] = __builtin_bit_cast(i32x4, make_uint4(aq[mb].x & live, aq[mb].y & live, aq[mb].z & live, aq[mb].w & live));
+      for (int mb = 0; mb < MBV; ++mb) A[mb] = __builtin_bit_cast(i32x4, aq[mb]);
       load_a(s + 1, aq);
       if (MBV > 0) {
 #pragma unroll
