@@ -86,6 +86,16 @@ def test_matrix_core_path_mid(mid_f, S, thr):
     matrix_core_case(mid_f, S, thr)
 
 
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_matrix_core_odd_group_count(fmt):
+    """H = 544 (17 groups), I = 96 (3 groups), shared 64, bf16 input: the bf16
+    grouped GEMM skips the group past the end of each row's last stage."""
+    from tests.test_gpu_parity import RAGGED
+    w = fmt_workload(gen.Workload("ragged", RAGGED, tokens=40, seed=31, x_dtype="bf16"), FORMATS[fmt])
+    dl = DeviceLayer(w, host_experts=True, mfma_min_tokens=0)
+    matrix_core_case(dl, 40, 2)
+
+
 @pytest.mark.parametrize("S", [1, 3, 8])
 def test_unresident_slot_poisons_only_its_tokens(tiny_f, S):
     w = tiny_f.w.with_(tokens=S)

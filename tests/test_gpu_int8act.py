@@ -124,6 +124,22 @@ def test_matrix_core_path(fmt, S, thr):
     assert not np.array_equal(y_mfma, y_gemv)
 
 
+@pytest.mark.parametrize("fmt", [1, 2], ids=["q4row", "q8row"])
+def test_matrix_core_odd_group_count(fmt):
+    """H = 544 (17 groups: the integer GEMM's last stage has one live group and
+    lanes of the other are masked), I = 96, shared 64, bf16 input."""
+    from tests.test_gpu_parity import RAGGED
+    w = fmt_workload(gen.Workload("ragged", RAGGED, tokens=40, seed=31, x_dtype="bf16"), fmt)
+    dl = DeviceLayer(w, host_experts=True, mfma_min_tokens=2, act_int8=1)
+    x = gen.tokens(w, step=41)
+    xt, dt = x_device(w, x)
+    idx, wt = dl.route(xt, dt)
+    y = dl.ffn(xt, dt, idx, wt).cpu().numpy()
+    ridx, rw = check_route(dl, x, idx.cpu().numpy(), wt.cpu().numpy())
+    assert (np.bincount(ridx.ravel(), minlength=dl.c.n_experts) >= 2).any()
+    check_int8act(dl, x, ridx, rw, y, np.arange(40))
+
+
 def test_glm_shape_batch_row_scales():
     """2048 bf16 tokens, GLM-5.2 shape, int4 with row scales, int8 activations: the
     integer matrix-core path for the many-token experts; sampled tokens."""
