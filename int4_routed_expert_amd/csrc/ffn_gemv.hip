@@ -1001,15 +1001,22 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void *src, int bf16, i
       v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
     }
   };
+  // the row (at most 8192 elements, 32 per thread) stays in registers between
+  // the two passes, so it is read from memory once
+  constexpr int kIt = 8;
+  float v[kIt][4];
   float m = 0.f;
   int nan = 0;
-  for (int c = threadIdx.x * 4; c < n; c += 1024) {  // n is a multiple of 32
-    float v[4];
-    load4(c, v);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      nan |= v[j] != v[j];
-      m = fmaxf(m, fabsf(v[j]));
+  for (int it = 0; it < kIt; ++it) {
+    const int c = threadIdx.x * 4 + it * 1024;  // n is a multiple of 32
+    if (c < n) {
+      load4(c, v[it]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        nan |= v[it][j] != v[it][j];
+        m = fmaxf(m, fabsf(v[it][j]));
+      }
     }
   }
 #pragma unroll
@@ -1026,16 +1033,18 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void *src, int bf16, i
   const bool any_nan = (s_nan[0] | s_nan[1] | s_nan[2] | s_nan[3]) != 0;
   const float dd = any_nan ? __builtin_nanf("") : __fdiv_rn(amax, 127.0f);
   if (threadIdx.x == 0) stg<float>(d + r, dd);
-  for (int c = threadIdx.x * 4; c < n; c += 1024) {
-    float v[4];
-    load4(c, v);
-    uint32_t w = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int qi = dd > 0.f ? (int)rintf(__fdiv_rn(v[j], dd)) : 0;
-      w |= ((uint32_t)qi & 0xFFu) << (8 * j);
+  for (int it = 0; it < kIt; ++it) {
+    const int c = threadIdx.x * 4 + it * 1024;
+    if (c < n) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int qi = dd > 0.f ? (int)rintf(__fdiv_rn(v[it][j], dd)) : 0;
+        w |= ((uint32_t)qi & 0xFFu) << (8 * j);
+      }
+      stg<uint32_t>(q + base + c, w);
     }
-    stg<uint32_t>(q + base + c, w);
   }
 }
 
