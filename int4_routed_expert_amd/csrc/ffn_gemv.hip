@@ -728,6 +728,7 @@ __global__ __launch_bounds__(256) void k_bucket(FfnArgs a) {
   const int n = a.S * a.k;
   const bool lane_tok = 64 % a.k == 0;  // entries i of one token share a wave (i % k == lane % k)
   const unsigned long long lt = (1ull << lane) - 1ull;
+  const unsigned long long seg_lo = (1ull << (lane - lane % a.k)) - 1ull;  // lanes before this token's segment
   int base = 0;
   for (int b0 = 0; b0 < n; b0 += 64 * 256) {
     const int rows = min(64, (n - b0 + 255) / 256);
@@ -743,12 +744,9 @@ __global__ __launch_bounds__(256) void k_bucket(FfnArgs a) {
         const int i = b0 + (r0 + r) * 256 + tid;
         bool m = r0 + r < rows && i < n && v[r] == e;
         // a token that names e twice contributes once (the combine poisons it)
-        if (lane_tok) {  // the token's entries are k consecutive lanes: compare with the earlier ones
-          const int pos = lane % a.k;
-          for (int j = 1; j < a.k; ++j) {
-            const int o = __shfl(v[r], lane - j);
-            m = m && !(j <= pos && o == e);
-          }
+        if (lane_tok) {  // the token's entries are k consecutive lanes: an earlier match in the segment
+          const unsigned long long hits = __ballot(m);
+          m = m && (hits & lt & ~seg_lo) == 0ull;
         } else if (m) {
           const int t0 = i / a.k * a.k;
           for (int j = t0; j < i; ++j) m = m && ldg<int>(a.idx + j) != e;
