@@ -202,36 +202,49 @@ __device__ inline void few_logits_finish(const RouteArgs &a, int e, int wave, in
   const size_t seg = (size_t)wave * q;
   if (wave < 4) {
     double acc[kFewTokens];
+    // the activations of up to four tokens are requested together, then used
+    // (one load latency per four tokens instead of one per token)
 #pragma unroll
-    for (int s = 0; s < kFewTokens; ++s) {
-      acc[s] = 0.0;
-      if (s < a.S) {
-        float4 xv[kFewChunks];
-        if (a.x_bf16) {
-          const __amdgpu_buffer_rsrc_t rx =
-              share_rsrc((const uint16_t *)a.x + (size_t)s * a.H + seg, (uint32_t)q * 2u);
-          uint2 raw[kFewChunks];
+    for (int sb = 0; sb < kFewTokens; sb += 4) {
+      if (sb < a.S) {
+        float4 xv[4][kFewChunks];
 #pragma unroll
-          for (int m = 0; m < kFewChunks; ++m) raw[m] = buf_u2(rx, (uint32_t)(m * 256 + lane * 4) * 2u);
+        for (int j = 0; j < 4; ++j) {
+          const int s = sb + j;
+          if (s < a.S) {
+            if (a.x_bf16) {
+              const __amdgpu_buffer_rsrc_t rx =
+                  share_rsrc((const uint16_t *)a.x + (size_t)s * a.H + seg, (uint32_t)q * 2u);
+              uint2 raw[kFewChunks];
 #pragma unroll
-          for (int m = 0; m < kFewChunks; ++m)
-            xv[m] = make_float4(__uint_as_float(raw[m].x << 16), __uint_as_float(raw[m].x & 0xFFFF0000u),
-                                __uint_as_float(raw[m].y << 16), __uint_as_float(raw[m].y & 0xFFFF0000u));
-        } else {
-          const __amdgpu_buffer_rsrc_t rx =
-              share_rsrc((const float *)a.x + (size_t)s * a.H + seg, (uint32_t)q * 4u);
+              for (int m = 0; m < kFewChunks; ++m) raw[m] = buf_u2(rx, (uint32_t)(m * 256 + lane * 4) * 2u);
 #pragma unroll
-          for (int m = 0; m < kFewChunks; ++m) xv[m] = buf_f4(rx, (uint32_t)(m * 256 + lane * 4) * 4u);
+              for (int m = 0; m < kFewChunks; ++m)
+                xv[j][m] = make_float4(__uint_as_float(raw[m].x << 16), __uint_as_float(raw[m].x & 0xFFFF0000u),
+                                       __uint_as_float(raw[m].y << 16), __uint_as_float(raw[m].y & 0xFFFF0000u));
+            } else {
+              const __amdgpu_buffer_rsrc_t rx =
+                  share_rsrc((const float *)a.x + (size_t)s * a.H + seg, (uint32_t)q * 4u);
+#pragma unroll
+              for (int m = 0; m < kFewChunks; ++m) xv[j][m] = buf_f4(rx, (uint32_t)(m * 256 + lane * 4) * 4u);
+            }
+          }
         }
-        double t = 0.0;
 #pragma unroll
-        for (int m = 0; m < kFewChunks; ++m) {
-          t = fma((double)wv[m].x, (double)xv[m].x, t);
-          t = fma((double)wv[m].y, (double)xv[m].y, t);
-          t = fma((double)wv[m].z, (double)xv[m].z, t);
-          t = fma((double)wv[m].w, (double)xv[m].w, t);
+        for (int j = 0; j < 4; ++j) {
+          const int s = sb + j;
+          if (s < a.S) {
+            double t = 0.0;
+#pragma unroll
+            for (int m = 0; m < kFewChunks; ++m) {
+              t = fma((double)wv[m].x, (double)xv[j][m].x, t);
+              t = fma((double)wv[m].y, (double)xv[j][m].y, t);
+              t = fma((double)wv[m].z, (double)xv[j][m].z, t);
+              t = fma((double)wv[m].w, (double)xv[j][m].w, t);
+            }
+            acc[s] = t;
+          }
         }
-        acc[s] = t;
       }
     }
 #pragma unroll
