@@ -194,3 +194,23 @@ def test_layer_call_graph_replays(tiny_q, S):
         torch.cuda.synchronize()
         assert torch.equal(got[0], i_e) and torch.equal(got[1], w_e) and torch.equal(got[2], y_e), i
         assert torch.isfinite(y_e).all()
+
+
+def test_zero_and_nan_rows(tiny_q):
+    """An all-zero token quantises to zeros (d = 0) and gives exactly zero output;
+    a token holding a NaN gets d = NaN and NaN outputs, and the other tokens of
+    the batch are untouched (int8 activations, decode and batch paths)."""
+    for S in (3, 9):
+        x = gen.tokens(tiny_q.w.with_(tokens=S), step=1234 + S).copy()
+        x[0] = 0.0
+        x[1, 7] = np.nan
+        xt, dt = x_device(tiny_q.w, x)
+        # route the finite tokens on a clean copy (a NaN logit has no defined selection)
+        xr = x.copy()
+        xr[1] = xr[2]
+        idx, wt = tiny_q.route(x_device(tiny_q.w, xr)[0], dt)
+        y = tiny_q.ffn(xt, dt, idx, wt).cpu().numpy()
+        assert np.all(y[0] == 0.0), S
+        assert np.isnan(y[1]).all(), S
+        ridx, rw = check_route(tiny_q, xr, idx.cpu().numpy(), wt.cpu().numpy())
+        check_int8act(tiny_q, x, ridx, rw, y, np.arange(2, S))
