@@ -46,7 +46,9 @@
  *     (ties to even; q = 0 for an all-zero row), and the matmul uses q_c * d
  *     (exact in fp64) in place of v_c.
  *
- * Parity pins: tests/test_oracle_pins.py (brute force, closed forms, invariants).
+ * Parity pins: tests/test_oracle_pins.py (brute force, closed forms, invariants)
+ * and tests/test_oracle_diag.py (the decision margins and the near-midpoint flag
+ * on hand-built keys).
  */
 #include <math.h>
 #include <stdint.h>
