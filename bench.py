@@ -24,11 +24,67 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 CHUNK = 16  # steps per captured graph
+MIN_TIMED = 1024  # timed steps at least (every captured graph replayed the same number of times)
+METRIC = "MoE-layer tokens/s and effective int4 weight GB/s (% of HBM peak), GLM-5.2"
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def read_ceiling_gbps(mb: float):
+    """Best measured streaming-read rate (GB/s) of the probe for a read of about `mb` MB
+    (profiles/hbm_read_ceiling.txt, lines 'read <MB> MB as <waves> waves ...'), or None."""
+    import re
+    path = os.path.join(ROOT, "profiles", "hbm_read_ceiling.txt")
+    if not os.path.exists(path):
+        return None
+    best = None
+    for line in open(path):
+        m = re.match(r"read\s+([\d.]+) MB as .*\s([\d.]+) GB/s", line.strip())
+        if m and abs(float(m.group(1)) - mb) <= 0.05 * mb:
+            best = max(best or 0.0, float(m.group(2)))
+    return best
+
+
+def oracle_tokens_per_s(run_one, seconds: float, n_max: int, threads: int):
+    """The oracle on `threads` threads over a bounded sample: run_one(i) prepares
+    sample i (untimed) and returns the seconds its oracle call took.  Returns
+    (samples per second, samples, seconds)."""
+    from oracle import oracle as O
+    O.set_num_threads(threads)
+    done, t = 0, 0.0
+    while done < n_max and (done == 0 or t < seconds):
+        t += run_one(done)
+        done += 1
+    return done / t, done, t
+
+
+def cpu_baseline(run_one, unit_per_sample: float, unit: str, sample: str, seconds: float, n_max: int) -> dict:
+    """All host threads, then one thread, on the same kind of sample."""
+    from oracle import oracle as O
+    all_threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1
+    v_all, n_all, t_all = oracle_tokens_per_s(run_one, seconds, n_max, all_threads)
+    v_one, n_one, t_one = oracle_tokens_per_s(run_one, seconds / 2, n_max, 1)
+    O.set_num_threads(all_threads)
+    log(f"cpu oracle: {v_all * unit_per_sample:.4g} {unit} on {all_threads} threads, "
+        f"{v_one * unit_per_sample:.4g} on 1 thread ({cpu_model()})")
+    return {"value": v_all * unit_per_sample, "unit": unit, "cores": all_threads, "kind": "oracle",
+            "sample": f"{sample}: {n_all} samples in {t_all:.1f} s on {all_threads} threads, "
+                      f"{n_one} in {t_one:.1f} s on 1 thread",
+            "value_1core": v_one * unit_per_sample, "cpu_model": cpu_model(), "nproc": os.cpu_count()}
 
 
 def kernel_source_hash() -> str:
@@ -37,7 +93,7 @@ def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "int4_routed_expert_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")) and f != "hbm_probe.hip":
+        if f.endswith((".hip", ".h")):
             with open(os.path.join(csrc, f), "rb") as fh:
                 h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
@@ -162,6 +218,28 @@ def emit(out):
     print(json.dumps(out), flush=True)
 
 
+def routed_oracle_sample(w, layer: int, x_of, S: int, x_is_bf16: bool = False):
+    """run_one(i) for cpu_baseline: batch i (x_of(i), S tokens) of `layer` through the
+    oracle's router and FFN; generating the weights it needs is not timed."""
+    from gen import inputs as gen
+    from oracle import oracle as O
+    c = w.cfg
+    W, b = gen.router_weights(w, layer), gen.router_bias(w, layer)
+    shared = gen.expert_weights(w, layer, c.n_experts)
+
+    def run_one(i):
+        xh = x_of(i)
+        ridx, _, _, _, _ = O.route(c, xh, W, b, x_is_bf16=x_is_bf16)
+        experts = {c.n_experts: shared}
+        for e in set(ridx.ravel().tolist()):
+            experts[e] = gen.expert_weights(w, layer, e)
+        t0 = time.perf_counter()
+        ridx, rw, _, _, _ = O.route(c, xh, W, b, x_is_bf16=x_is_bf16)
+        O.moe_ffn(c, xh, ridx, rw, experts, x_is_bf16=x_is_bf16)
+        return time.perf_counter() - t0
+    return run_one
+
+
 def bench_verify(args) -> int:
     """Speculative-verify batches: 4 tokens per call (GLM-5.2 shape), 1024 distinct
     batches rotated over 4 resident layers, HIP graphs of 16 calls."""
@@ -214,7 +292,17 @@ def bench_verify(args) -> int:
     U = np.array(U)
     per_call = (U.mean() + 1) * layers[0]["sb"]
     gbps = per_call / (ms_per_step * 1e-3) / 1e9
-    emit({"metric": "MoE-layer tokens/s and effective int4 weight GB/s (% of HBM peak), GLM-5.2",
+    # dominant kernel: gate/up of the union and the shared expert, over the 64 profiled calls
+    prof_u = np.array([len(np.unique(idx_h[j % n_out].ravel())) for j in range(64)])
+    alg = float((prof_u + 1).mean()) * gu_bytes(args.weight_format, c.hidden, c.moe_inter)
+    k_us = kernels["gateup_small"]
+    achieved = alg / (k_us * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        run_one = routed_oracle_sample(w, 0, lambda i: gen.tokens(w, layer=0, step=i), S)
+        cpu = cpu_baseline(run_one, S, "tokens/s", "4-token verify batches of layer 0 (route + union of routed "
+                           "experts + shared, fp64)", args.cpu_seconds, 16)
+    emit({"metric": METRIC,
           "value": tok_s * S, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warm,
           "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
           "dtype": "f32", "data": "synthetic",
@@ -224,7 +312,12 @@ def bench_verify(args) -> int:
                      "call": "moe_layer" if args.call == "layer" else "moe_route + moe_ffn"},
           "union_mean": float(U.mean()), "union_min": int(U.min()), "union_max": int(U.max()),
           "shared_fraction": float(np.mean(shared)), "selections_on_shared": float(np.mean(on_shared)),
-          "effective_gbps": gbps, "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS, "kernels_us": kernels})
+          "effective_gbps": gbps, "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS, "kernels_us": kernels,
+          "roofline": {"kernel": "gateup_small", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                       "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                       "traffic": measured_traffic("gateup_small", args.weight_format),
+                       "algorithmic_bytes_per_launch": alg},
+          "cpu_baseline": cpu})
     return 0
 
 
@@ -246,8 +339,7 @@ def run_graphs(step, args, period_tokens):
                 step(gi * CHUNK + j)
         graphs.append(g)
     torch.cuda.synchronize()
-    steps = CHUNK * ((args.steps + CHUNK - 1) // CHUNK)
-    warm = CHUNK * ((args.warmup + CHUNK - 1) // CHUNK)
+    steps, warm = timed_counts(args, n_graphs)
     for i in range(warm // CHUNK):
         graphs[i % n_graphs].replay()
     torch.cuda.synchronize()
@@ -258,6 +350,17 @@ def run_graphs(step, args, period_tokens):
     el = time.perf_counter() - t0
     log(f"graph replay: {el * 1e6 / steps:.2f} us/call over {steps} calls")
     return steps / el, el * 1e3 / steps, steps, warm
+
+
+def timed_counts(args, n_graphs: int):
+    """(timed steps, warm-up steps): the request rounded up to whole passes over
+    the n_graphs captured graphs, at least MIN_TIMED timed steps, and a warm-up
+    that replays every graph at least once."""
+    per_pass = CHUNK * n_graphs
+    steps = max(args.steps, MIN_TIMED)
+    steps = per_pass * ((steps + per_pass - 1) // per_pass)
+    warm = per_pass * max(1, (args.warmup + per_pass - 1) // per_pass)
+    return steps, warm
 
 
 def bench_prefill(args) -> int:
@@ -302,20 +405,52 @@ def bench_prefill(args) -> int:
     prof = M.moe_profile_report()
     M.moe_profile_enable(False)
     kernels = {n: round(ms * 1e3 / k, 2) for n, (ms, k) in prof.items()}
-    used = len(set(idx.cpu().numpy().ravel().tolist()))
+    # the profiled calls ran batches 0..3; idx holds batch 3's routing
+    idx3 = idx.cpu().numpy()
+    counts = np.bincount(idx3.ravel(), minlength=c.n_experts)
+    used = int((counts > 0).sum())
     bytes_call = (used + 1) * L["sb"]
     flop = 2 * 3 * c.hidden * c.moe_inter * (S * c.top_k) + 2 * 3 * c.hidden * c.shared_inter * S
+    thr = args.mfma_min_tokens
+    mfma_rows = int(counts[counts >= thr].sum()) if thr > 0 else 0
+    shared_mfma = thr > 0 and S >= thr
+    gu_flop = 2 * 2 * c.hidden * (c.moe_inter * mfma_rows + (c.shared_inter * S if shared_mfma else 0))
+    srt = np.sort(counts)[::-1][:64]
+    srt = srt[srt > 0]
+    slope = float(np.polyfit(np.log(np.arange(1, srt.size + 1)), np.log(srt), 1)[0])
+    gu_key = "gateup_mfma"
+    gu_achieved = gu_flop / (kernels[gu_key] * 1e-6) / 1e12 if gu_key in kernels else None
+    peak = 5000.0 if args.act_int8 else BF16_PEAK_TFLOPS
     log(f"prefill: {el * 1e3:.3f} ms per call, {used} experts used, kernels (us) {kernels}")
-    emit({"metric": "MoE-layer tokens/s and effective int4 weight GB/s (% of HBM peak), GLM-5.2",
+    cpu = None
+    if not args.no_cpu_baseline:
+        xb3 = gen.tokens(w, layer=0, step=0)
+        run_one = routed_oracle_sample(w, 0, lambda i: np.ascontiguousarray(xb3[i * 97 % S:i * 97 % S + 1]), 1,
+                                       x_is_bf16=True)
+        cpu = cpu_baseline(run_one, 1, "tokens/s", "single prefill tokens of batch 0 (route + 8 routed + shared "
+                           "experts, fp64; the oracle has no batch reuse)", args.cpu_seconds, 64)
+    emit({"metric": METRIC,
           "value": S / el, "unit": "tokens/s", "n_gpus": 1, "steps": n_iter, "warmup": n_warm,
           "ms_per_step": el * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-          "dtype": "f32", "data": "synthetic",
+          "dtype": "int8" if args.act_int8 else "bf16", "data": "synthetic",
           "config": {"workload": "glm52_moe_layer_prefill_S2048", "tokens_per_call": S, "x": "bf16",
                      "quant": FORMAT_DESC[args.weight_format] + (", int8 activations" if args.act_int8 else ""),
-                     "bias": w.bias_recipe, "batches_rotated": nb, "mfma_min_tokens": args.mfma_min_tokens},
+                     "bias": w.bias_recipe, "batches_rotated": nb, "mfma_min_tokens": args.mfma_min_tokens,
+                     "matrix_cores": "int8 MFMA" if args.act_int8 else "bf16 MFMA, fp32 accumulation",
+                     "gemv_path": "exact int4 group dots, fp32 accumulation"},
           "experts_used": used, "effective_gbps": bytes_call / el / 1e9,
           "pct_hbm_peak": 100.0 * bytes_call / el / 1e9 / HBM_PEAK_GBPS,
-          "tflops": flop / el / 1e12, "kernels_us": kernels})
+          "tflops": flop / el / 1e12, "pct_mfma_peak": 100.0 * flop / el / 1e12 / peak,
+          "routing": {"zipf_slope_top64": slope, "max_tokens_per_expert": int(counts.max()),
+                      "experts_without_tokens": int((counts == 0).sum()),
+                      "experts_on_matrix_cores": int((counts >= thr).sum()) if thr > 0 else 0,
+                      "pairs_on_matrix_cores": mfma_rows / float(S * c.top_k)},
+          "kernels_us": kernels,
+          "roofline": {"kernel": gu_key, "bound": "mfma", "achieved": gu_achieved, "peak": peak,
+                       "unit": "TFLOP/s", "frac": gu_achieved / peak if gu_achieved else None,
+                       "traffic": measured_traffic(gu_key, args.weight_format),
+                       "algorithmic_flop_per_launch": gu_flop},
+          "cpu_baseline": cpu})
     return 0
 
 
@@ -388,6 +523,8 @@ def bench_stack(args) -> int:
     y = torch.empty((1, c.hidden), dtype=torch.float32, device=dev)
     misses = np.zeros((steps, NL), np.int64)
     kernel_bytes = 0
+    hot = [set(gen.hot_set(w, l).tolist()) for l in range(NL)]
+    on_hot = 0
     # --prefetch: the next layer's routing (its router on its input, computed one
     # layer ahead) is prefetched into the pool while the current layer computes
     seq = [(st, l) for st in range(steps) for l in range(NL)]
@@ -403,6 +540,9 @@ def bench_stack(args) -> int:
         ev2[b].record(compute)
 
     torch.cuda.synchronize()
+    # every kernel is stamped with start/stop events for the kernel-time figures
+    M.moe_profile_enable(True)
+    M.moe_profile_report()
     t_start = time.perf_counter()
     if args.prefetch:
         route_into(0, *seq[0])
@@ -430,7 +570,9 @@ def bench_stack(args) -> int:
             M.moe_ffn(cfg, x, M.MOE_F32, 1, idx, wt, view, L["shared"], y, ws, ws.numel())
             pool.release(l, compute)
         misses[st, l] = n_miss
-        kernel_bytes += (len(set(ih.numpy().ravel().tolist())) + 1) * sb
+        sel_l = ih.numpy().ravel().tolist()
+        kernel_bytes += (len(set(sel_l)) + 1) * sb
+        on_hot += sum(e in hot[l] for e in sel_l)
         if l == NL - 1:
             if st == 0:
                 torch.cuda.synchronize()
@@ -440,16 +582,34 @@ def bench_stack(args) -> int:
                 log(f"step {st}: {time.perf_counter() - t_start:.2f} s, {misses[st].sum()} misses at acquire this step")
     torch.cuda.synchronize()
     el = time.perf_counter() - t_start
+    prof = M.moe_profile_report()
+    M.moe_profile_enable(False)
     stt = pool.stats()
     pool.close()
+    kern_s = {n: ms * 1e-3 for n, (ms, _) in prof.items()}
+    all_kernel_s = sum(kern_s.values())
+    ffn_kernel_s = kern_s.get("gateup_s1", 0.0) + kern_s.get("down_s1", 0.0)
+    fill_s = stt["fill_bytes"] / (h2d_gbps * 1e9)  # copy-engine time at the measured pinned-copy rate
+    # fraction of the shorter of (kernel time, fill time) hidden under the other: 0 when the wall
+    # clock is their sum (fully serial), 1 when it is their maximum (host time counts as serial)
+    overlap = (all_kernel_s + fill_s - el) / max(1e-12, min(all_kernel_s, fill_s))
+    overlap = float(min(1.0, max(0.0, overlap)))
     sel = NL * c.top_k
     hit0 = 1.0 - misses[0].sum() / sel
     hit_rest = 1.0 - misses[1:].sum() / (sel * max(1, steps - 1))
     warm_el = el - t_step0
+    cpu = None
+    if not args.no_cpu_baseline:
+        run_one = routed_oracle_sample(w, 0, lambda i: gen.tokens(w, layer=0, step=i), 1)
+        cpu = cpu_baseline(run_one, 1.0 / NL, "tokens/s", f"decode tokens of layer 0 (route + 8 routed + shared "
+                           f"experts, fp64), one {NL}-layer token = {NL} such layers", args.cpu_seconds, 64)
     log(f"stack: {el:.3f} s for {steps} steps x {NL} layers; hit rate step0 {hit0:.3f}, steps 1+ {hit_rest:.3f}; "
         f"fills {stt['fill_bytes'] / 1e9:.1f} GB (prefetched {stt['prefetch_fills']} experts); "
         f"H2D ceiling {h2d_gbps:.1f} GB/s")
-    emit({"metric": "MoE-layer tokens/s and effective int4 weight GB/s (% of HBM peak), GLM-5.2",
+    gu_launch = 9 * gu_bytes(args.weight_format, c.hidden, I)  # 8 routed + shared experts per launch
+    gu_avg_us = prof["gateup_s1"][0] * 1e3 / prof["gateup_s1"][1] if "gateup_s1" in prof else None
+    gu_ach = gu_launch / (gu_avg_us * 1e-6) / 1e9 if gu_avg_us else None
+    emit({"metric": METRIC,
           "value": steps / el, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": 0,
           "ms_per_step": el * 1e3 / steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
           "dtype": "f32", "data": "synthetic",
@@ -462,12 +622,34 @@ def bench_stack(args) -> int:
           "hit_rate_step0": hit0, "hit_rate_steps_1_plus": hit_rest, "misses": int(misses.sum()),
           "prefetch_fills": int(stt["prefetch_fills"]), "prefetch_hits": int(stt["prefetch_hits"]),
           "fill_bytes": int(stt["fill_bytes"]), "fill_gbps_wall": stt["fill_bytes"] / el / 1e9,
-          "h2d_ceiling_gbps": h2d_gbps, "kernel_bytes": kernel_bytes,
-          "kernel_bytes_gbps_wall": kernel_bytes / el / 1e9})
+          "h2d_ceiling_gbps": h2d_gbps, "fill_gbps_at_ceiling_s": fill_s, "kernel_bytes": kernel_bytes,
+          "kernel_gbps": kernel_bytes / ffn_kernel_s / 1e9 if ffn_kernel_s else None,
+          "kernel_s": {"expert_ffn": ffn_kernel_s, "all": all_kernel_s},
+          "kernel_bytes_gbps_wall": kernel_bytes / el / 1e9, "overlap_fraction": overlap,
+          "selections_on_hot_set": on_hot / float(steps * NL * c.top_k),
+          "roofline": {"kernel": "gateup_s1", "bound": "hbm", "achieved": gu_ach, "peak": HBM_PEAK_GBPS,
+                       "unit": "GB/s", "frac": gu_ach / HBM_PEAK_GBPS if gu_ach else None,
+                       "traffic": measured_traffic("gateup_s1", args.weight_format),
+                       "algorithmic_bytes_per_launch": gu_launch},
+          "cpu_baseline": cpu})
     return 0
 
 
+def build_probe() -> str:
+    """Compiles hbm_probe.hip (the read-ceiling and copy-calibration probe) to ./hbm_probe."""
+    import subprocess
+    out = os.path.join(ROOT, "hbm_probe")
+    subprocess.check_call(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-Wno-unused-result",
+                           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                           os.path.join(ROOT, "hbm_probe.hip"), "-o", out + ".tmp"])
+    os.replace(out + ".tmp", out)
+    return out
+
+
 def main() -> int:
+    if len(sys.argv) > 1 and sys.argv[1] == "--build-probe":
+        print(build_probe())
+        return 0
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
         ap = argparse.ArgumentParser(prog="bench.py --summarize-pmc")
         ap.add_argument("--summarize-pmc", action="store_true")
@@ -592,8 +774,7 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"captured {n_graphs} graphs x {CHUNK} steps")
 
-    steps = CHUNK * ((args.steps + CHUNK - 1) // CHUNK)
-    warm = CHUNK * ((args.warmup + CHUNK - 1) // CHUNK)
+    steps, warm = timed_counts(args, n_graphs)
     for i in range(warm // CHUNK):
         graphs[i % n_graphs].replay()
     torch.cuda.synchronize()
@@ -635,30 +816,13 @@ def main() -> int:
     # ---- CPU baseline: the fp64 oracle on a bounded sample ------------------------
     cpu = None
     if not args.no_cpu_baseline:
-        from oracle import oracle as O
-        Wh, bh = gen.router_weights(w, 0), gen.router_bias(w, 0)
-        shared_h = gen.expert_weights(w, 0, E)
-        done, t_cpu, n_target = 0, 0.0, 1
-        while done < n_target:
-            xh = gen.tokens(w, layer=0, step=done)
-            experts = {E: shared_h}
-            ridx, rw, _, _, _ = O.route(c, xh, Wh, bh)  # untimed: generating weights is not oracle work
-            for e in ridx[0].tolist():
-                experts[e] = gen.expert_weights(w, 0, e)
-            tc = time.perf_counter()
-            ridx, rw, _, _, _ = O.route(c, xh, Wh, bh)
-            O.moe_ffn(c, xh, ridx, rw, experts)
-            t_cpu += time.perf_counter() - tc
-            done += 1
-            if done == 1:
-                n_target = int(max(1, min(64, args.cpu_seconds / max(t_cpu, 1e-3))))
-        cpu = {"value": done / t_cpu, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
-               "sample": f"{done} decode tokens of layer 0 (route + 8 routed + shared experts, fp64), "
-                         f"{t_cpu:.1f} s"}
-        log(f"cpu oracle: {cpu['value']:.3f} tok/s on {cpu['cores']} threads")
+        run_one = routed_oracle_sample(w, 0, lambda i: gen.tokens(w, layer=0, step=i), 1)
+        cpu = cpu_baseline(run_one, 1, "tokens/s", "decode tokens of layer 0 (route + 8 routed + shared experts, "
+                           "fp64)", args.cpu_seconds, 64)
+    ceiling = read_ceiling_gbps(layer_bytes / 1e6)
 
     out = {
-        "metric": "MoE-layer tokens/s and effective int4 weight GB/s (% of HBM peak), GLM-5.2",
+        "metric": METRIC,
         "value": tok_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -677,8 +841,12 @@ def main() -> int:
                    "call": "moe_layer" if args.call == "layer" else "moe_route + moe_ffn"},
         "effective_gbps": gbps,
         "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
+        "read_ceiling_gbps": ceiling,
+        "frac_of_read_ceiling": gbps / ceiling if ceiling else None,
         "expert_bytes_per_token": layer_bytes,
         "router_bytes_per_token": router_bytes,
+        "steps_requested": args.steps,
+        "graph_us_per_step": ms_per_step * 1e3,
         "eager_us_per_step": eager_us,
         "kernels_us": {n: round(v["avg_us"], 3) for n, v in kernels.items()},
         "roofline": {"kernel": rk, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,

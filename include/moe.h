@@ -51,8 +51,9 @@ enum moe_status {
   MOE_EDTYPE = -3,     /* unknown activation dtype */
   MOE_EWORKSPACE = -4, /* workspace smaller than moe_workspace_bytes() */
   MOE_ENOSLOT = -5,    /* slot pool: the union of experts exceeds the layer's slots */
-  MOE_ESTALE = -6,     /* slot pool: generation mismatch or bad lease state */
+  MOE_ESTALE = -6,     /* slot pool: a view whose slots have been refilled since it was published */
   MOE_EHIP = -7,       /* a HIP call failed */
+  MOE_ELEASE = -8,     /* slot pool: acquire of a leased layer, or release without acquire */
 };
 
 enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
@@ -94,8 +95,9 @@ typedef struct moe_cfg {
   /* moe_weight_format of every expert of the layer (routed and shared). */
   int32_t weight_format;
   /* 1: int8 activations, an approximate mode ([PORT] "G2 implementation status":
-   * Colibri's IDOT=1 quantises each activation row to int8 before the packed-int4
-   * dot product; [README] "Integer-dot kernels").  Each token's x and each
+   * the IDOT=1 setting of Colibri, where every activation row becomes int8 ahead
+   * of its dot products with the packed int4 weights; [README] "Integer-dot
+   * kernels").  Each token's x and each
    * (token, expert) hidden row h (in fp32) is replaced by q * d with
    * d = fp32(max|v| / 127) and q = rint(fp32(v / d)) in [-127, 127] (a row with a
    * NaN gets d = NaN); the dot products of q with the weights are exact integers.
@@ -106,12 +108,27 @@ typedef struct moe_cfg {
 /* Where the routed experts live.  Expert e's packed weights start at
  * base + table[e] * slot_bytes.  `table` is a DEVICE array of E int32 slot
  * numbers (entries outside [0, n_slots) poison the rows that use them).
- * With every expert resident in one array, table[e] = e. */
+ * With every expert resident in one array, table[e] = e and gen = NULL.
+ *
+ * Generation tags ([PORT] N3 "Explicit ExpertResidencyManager": slots carry a
+ * generation so that a stale user cannot consume storage that has been reused
+ * for another expert).  When gen is not NULL, slot_gen is a DEVICE array of
+ * n_slots generation numbers that the owner of the slots changes before it
+ * refills a slot, and gen is a DEVICE array of E numbers: the generation that
+ * table[e]'s slot held when the table was published.  A kernel uses expert e
+ * only if slot_gen[table[e]] == gen[e]; otherwise it writes NaN into the rows
+ * of the tokens that chose e, never another expert's values.  The slot pool's
+ * views are tagged; a caller's own resident arrays pass gen = NULL.  `lease`
+ * identifies the pool acquire that published the view (0 otherwise); the host
+ * can ask moe_pool_check_view whether the view has gone stale. */
 typedef struct moe_slot_view {
   const void *base;
   int64_t slot_bytes; /* >= moe_expert_bytes(cfg, moe_inter), multiple of 256 */
   const int32_t *table;
   int32_t n_slots;
+  const uint32_t *gen;      /* [E] expected generations, or NULL (no check) */
+  const uint32_t *slot_gen; /* [n_slots] current generations; required when gen is set */
+  uint64_t lease;
 } moe_slot_view;
 
 int moe_validate_cfg(const moe_cfg *cfg);
@@ -242,7 +259,15 @@ int moe_layer(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, con
  * layer (pass it to moe_ffn on `compute`).  Each acquire must be followed by
  * moe_pool_release(layer, compute) after the consuming work is enqueued; it
  * records the consumer-done event of every leased slot.
- * Errors: MOE_ENOSLOT (union larger than slots_per_layer), MOE_ESTALE (acquire
+ * Generations: every fill takes a new pool-wide generation number, written into
+ * the slot's slot_gen entry on `side` before the copy; the table upload carries
+ * each resident expert's generation (view gen).  A slot whose prefetch copy is
+ * still running is published as absent (-1) until an acquire that leases it
+ * has waited for the copy.  A view used after its release, once its slots have
+ * been refilled, gives NaN rows for the refilled experts (see moe_slot_view);
+ * such a use must still be stream-ordered after the refill's start (a kernel
+ * that runs concurrently with a refill of its slot is a race).
+ * Errors: MOE_ENOSLOT (union larger than slots_per_layer), MOE_ELEASE (acquire
  * of a layer with an unreleased lease, or release without acquire), MOE_ENULL
  * (a missing expert has no registered host source), MOE_EINVAL (bad layer or
  * expert id).  All calls on one pool must come from one host thread. */
@@ -280,6 +305,13 @@ int moe_pool_trace(const moe_pool *pool, int32_t *out, int32_t cap);
  * "prefetch_fills", "prefetch_hits", ...} as JSON (prefetch_hits: acquire hits
  * on prefetched slots). */
 int moe_pool_stats(const moe_pool *pool, char *out_json, size_t cap);
+/* Host-side staleness check of a view of `layer` made by moe_pool_acquire:
+ * MOE_OK while its lease is open, or when no slot of the layer has been given
+ * to another expert since the view was published; MOE_ESTALE when its lease
+ * has ended and a slot of the layer has been refilled since (its kernels would
+ * then write NaN for the refilled experts); MOE_EINVAL when the view does not
+ * address this pool's layer. */
+int moe_pool_check_view(const moe_pool *pool, int32_t layer, const moe_slot_view *view);
 
 /* Timing instrumentation (not part of the layer's computation).  While enabled,
  * the library brackets each kernel it launches with two hipEvents recorded on the

@@ -44,13 +44,6 @@ def build(verbose: bool = False) -> str:
     tmp = OUT + ".tmp"
     subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, OUT)
-    # HBM read-ceiling / copy probe used by the roofline measurements (not part of the library)
-    probe = os.path.join(HERE, "hbm_probe")
-    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Wno-unused-result",
-                           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                           os.path.join(CSRC, "hbm_probe.hip"), "-o", probe + ".tmp"],
-                          stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
-    os.replace(probe + ".tmp", probe)
     return OUT
 
 

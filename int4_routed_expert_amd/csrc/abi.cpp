@@ -154,7 +154,8 @@ const char *moe_status_string(int s) {
     case MOE_EDTYPE: return "unknown activation dtype";
     case MOE_EWORKSPACE: return "workspace too small";
     case MOE_ENOSLOT: return "slot pool: expert union exceeds the layer's slots";
-    case MOE_ESTALE: return "slot pool: stale generation or bad lease state";
+    case MOE_ESTALE: return "slot pool: the view's slots have been refilled since it was published";
+    case MOE_ELEASE: return "slot pool: acquire of a leased layer, or release without acquire";
     case MOE_EHIP: return "HIP call failed";
     default: return "unknown status";
   }
@@ -398,6 +399,7 @@ static int ffn_args(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S,
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EDTYPE;
   if (S == 0) return MOE_OK;
   if (!x || !idx || !w || !ex || !y || !ws || !ex->base || !ex->table) return MOE_ENULL;
+  if (ex->gen && !ex->slot_gen) return MOE_ENULL;
   if (c->shared_inter > 0 && !shared) return MOE_ENULL;
   if (ex->n_slots < 1 || ex->slot_bytes < slot_stride(c->hidden, c->moe_inter, c->weight_format) ||
       ex->slot_bytes % 256)
@@ -411,6 +413,7 @@ static int ffn_args(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S,
   a.act_q = c->act_int8;
   a.x = x; a.idx = idx; a.w = w;
   a.base = (const uint8_t *)ex->base; a.slot_bytes = ex->slot_bytes; a.table = ex->table; a.n_slots = ex->n_slots;
+  a.gen = ex->gen; a.slot_gen = ex->gen ? ex->slot_gen : nullptr;
   a.shared = (const uint8_t *)shared;
   a.y = y;
   char *b = (char *)ws;

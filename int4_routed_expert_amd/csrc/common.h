@@ -77,6 +77,8 @@ struct FfnArgs {
   int64_t slot_bytes;
   const int32_t *table;
   int32_t n_slots;
+  const uint32_t *gen;       // [E] generation each expert's slot held when the table was published (null: no check)
+  const uint32_t *slot_gen;  // [n_slots] the slots' current generations
   const uint8_t *shared;
   float *y;
   // workspace views

@@ -119,7 +119,9 @@ __device__ inline void to_limbs(const float *v, Limbs &out) {
   for (int c = 0; c < 32; ++c) m = fmaxf(m, fabsf(v[c]));
   int E = 0;
   (void)frexpf(m, &E);  // m < 2^E (E = 0 for m = 0)
-  const int sh = 22 - E;
+  // at most 149: 2^-149 is the smallest fp32 power of two, and a group whose
+  // largest value is below 2^-127 (subnormal) is then still held exactly
+  const int sh = min(22 - E, 149);
   out.f = ldexpf(1.0f, -sh);
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
@@ -179,7 +181,7 @@ __device__ inline void to_limbs8(const float *v, Limbs &out) {
   for (int c = 0; c < 32; ++c) m = fmaxf(m, fabsf(v[c]));
   int E = 0;
   (void)frexpf(m, &E);
-  const int sh = 22 - E;
+  const int sh = min(22 - E, 149);  // as in to_limbs
   out.f = ldexpf(1.0f, -sh);
 #pragma unroll
   for (int d = 0; d < 8; ++d) {
@@ -195,6 +197,12 @@ __device__ inline void to_limbs8(const float *v, Limbs &out) {
     }
   }
 }
+
+// One group's contribution T * s * f (f = 2^-sh) to an fp32 sum.  The power of
+// two is applied last: s * f alone underflows for very small activations (f
+// down to 2^-149), while T * s keeps its precision and the final scaling is
+// exact wherever the contribution itself is a normal number.
+__device__ inline float group_fma(float T, float s, float f, float acc) { return fmaf(T * s, f, acc); }
 
 template <int WF>
 __device__ inline void to_limbs_wf(const float *v, Limbs &out) {
@@ -233,11 +241,19 @@ __device__ inline float qdot(const QGroup<WF> &g, const Limbs &x) {
   else return group_dot(g.q[0], x);
 }
 
+// Slot s (the table entry of expert e) is usable when it is in [0, n_slots)
+// and, for a generation-tagged view, still holds the generation the table was
+// published with (a slot refilled since then holds another expert).
+__device__ inline bool slot_ok(const FfnArgs &a, int e, int s) {
+  if (s < 0 || s >= a.n_slots) return false;
+  return !a.gen || ldg<uint32_t>(a.slot_gen + s) == ldg<uint32_t>(a.gen + e);
+}
+
 // Packed weights of routed expert e through the slot table, or null when its
-// slot number is outside [0, n_slots).
+// slot is not usable.
 __device__ inline const uint8_t *expert_ptr(const FfnArgs &a, int e) {
   const int s = ldg<int>(a.table + e);
-  if (s < 0 || s >= a.n_slots) return nullptr;
+  if (!slot_ok(a, e, s)) return nullptr;
   return a.base + (size_t)s * (size_t)a.slot_bytes;
 }
 

@@ -5,8 +5,8 @@
 // N1 and "G2 implementation status": routed experts are SwiGLU FFNs over int4
 // weights with a scale per group; the weighted expert outputs are composed in
 // route order and the shared expert is added unweighted.  colibri README
-// "What's implemented" (batch-union MoE): every unique expert of the batch is
-// read once and applied to all tokens that chose it.
+// "What's implemented" (batch-union MoE): the experts named by the whole batch
+// are de-duplicated, so each is streamed a single time for all of its tokens.
 //
 // Every weight group is contracted with the exact integer dot product of dot.h,
 // for each weight format (template parameter WF: int4 with fp16 scales per 32,
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
     select_block<EPT, true>(c, 0, in, sel, blockIdx.x == 0 ? a.idx_out : nullptr, a.w_out);
     if (lane < a.k) {
       const int slot = sel.out_slot[lane];
-      if (slot >= 0 && slot < a.n_slots) my_ptr = (uint64_t)(uintptr_t)(a.base + (size_t)slot * (size_t)a.slot_bytes);
+      if (slot_ok(a, sel.out_e[lane], slot)) my_ptr = (uint64_t)(uintptr_t)(a.base + (size_t)slot * (size_t)a.slot_bytes);
     }
     if (blockIdx.x == 0 && threadIdx.x < 64 && lane < a.k) a.eptr[lane] = my_ptr;  // for the down kernel
     if (n > 0 && !early) gu_feat_load(b0, a, 0, n, ns, s0, r0, my_ptr, lane);
@@ -125,8 +125,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_s1(FfnArgs a) {
     load_act32(a, true, (size_t)min((int)threadIdx.x, ng - 1) * kGroup, v);
     const bool e_ok = lane < a.k && e_raw >= 0 && e_raw < a.E;
     const int slot = ldg<int>(a.table + (e_ok ? e_raw : 0));
-    my_ptr = e_ok && slot >= 0 && slot < a.n_slots ? (uint64_t)(uintptr_t)(a.base + (size_t)slot * (size_t)a.slot_bytes)
-                                                    : 0;
+    my_ptr = e_ok && slot_ok(a, e_raw, slot) ? (uint64_t)(uintptr_t)(a.base + (size_t)slot * (size_t)a.slot_bytes) : 0;
     if (blockIdx.x == 0 && threadIdx.x < 64 && lane < a.k) a.eptr[lane] = my_ptr;  // for the down kernel
     // kGuRing-slot ring, kGuRing - 1 features in flight while one is computed.
     // Loads are unconditional (indices clamped; repeats at the tail hit in
@@ -427,7 +426,8 @@ __device__ inline void gateup_tile(const FfnArgs &a, const uint8_t *tile, int nt
       for (int j = 0; j < NG; ++j)
 #pragma unroll
         for (int i = 0; i < RC; ++i) {
-          if constexpr (WF == kWfQ4G32) acc[i] = fmaf(qdot(q[i][j], xv[j]), scale_of(sc[j], r0 + i) * xv[j].f, acc[i]);
+          if constexpr (WF == kWfQ4G32)
+            acc[i] = group_fma(qdot(q[i][j], xv[j]), scale_of(sc[j], r0 + i), xv[j].f, acc[i]);
           else acc[i] = fmaf(qdot(q[i][j], xv[j]), xv[j].f, acc[i]);
         }
 #pragma unroll

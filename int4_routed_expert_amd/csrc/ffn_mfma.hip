@@ -3,12 +3,17 @@
 // mfma_min_tokens tokens of a batch (and for the shared expert when the batch
 // is that large).
 //
-// Method: "GLM-5.2 on a 32 GB Mac - native MLX port of the Colibri hierarchy",
-// "Prefill" (int4 experts dequantised to bf16 and contracted on the matrix
-// units for a batch of tokens; the threshold on tokens per expert separates
-// this from the per-token GEMV path).  Weights are the slot layout of the
-// packer: gate/up row tiles (rows g0 u0 g1 u1 ... of four features, fp16
-// scale per row and group of 32) and down row tiles of eight output rows.
+// Method: colibri README, "Experimental Metal backend (Apple Silicon)": the
+// large GEMMs of prefill run on the GPU, and a tunable count of rows (here:
+// tokens per expert) decides which experts take that path instead of the
+// per-token one; "GLM-5.2 on a 32 GB Mac - native MLX port of the Colibri
+// hierarchy", "What Colibri is actually doing" item 11 (large prefill GEMMs on
+// the GPU).  Dequantising the int4 weights to bf16 for the matrix cores is this
+// library's choice, not the pages' (their GPU paths dequantise to f32 and
+// multiply-accumulate in f32); it carries its own, wider error bar.  Weights
+// are the slot layout of the packer: gate/up row tiles (rows g0 u0 g1 u1 ... of
+// four features, fp16 scale per row and group of 32) and down row tiles of
+// eight output rows.
 //
 // Tiles: a workgroup (8 waves) owns up to 256 token rows of one expert's list
 // (kMT) and 256 output columns (kNT); wave w computes two 16-row blocks (blocks

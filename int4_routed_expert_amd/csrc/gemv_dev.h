@@ -88,20 +88,6 @@ struct GuFeat {
   int valid;
 };
 
-// Slot of routed expert `lane` (< k): idx entry in [0, E) and table entry in
-// [0, n_slots), else 0 (the expert's outputs become NaN).
-__device__ inline uint64_t routed_ptr_lane(const FfnArgs &a, int lane) {
-  uint64_t p = 0;
-  if (lane < a.k) {
-    const int e = ldg<int>(a.idx + lane);
-    if (e >= 0 && e < a.E) {
-      const int s = ldg<int>(a.table + e);
-      if (s >= 0 && s < a.n_slots) p = (uint64_t)(uintptr_t)(a.base + (size_t)s * (size_t)a.slot_bytes);
-    }
-  }
-  return p;
-}
-
 // Loads of gate/up row pair r (feature r) of expert ex (null: an unresident
 // expert, read from a stand-in and marked invalid).  Lanes past the last group
 // read the last group and contribute zero because their activation limbs are
@@ -155,8 +141,8 @@ __device__ inline float gu_feat_compute(const GuFeat<NG, WF> &b, const Limbs (&x
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
     if constexpr (WF == kWfQ4G32) {
-      g = fmaf(qdot(b.g[j], xv[j]), half_bits_to_float(b.s[j]) * xv[j].f, g);
-      u = fmaf(qdot(b.u[j], xv[j]), half_bits_to_float(b.s[j] >> 16) * xv[j].f, u);
+      g = group_fma(qdot(b.g[j], xv[j]), half_bits_to_float(b.s[j]), xv[j].f, g);
+      u = group_fma(qdot(b.u[j], xv[j]), half_bits_to_float(b.s[j] >> 16), xv[j].f, u);
     } else {
       g = fmaf(qdot(b.g[j], xv[j]), xv[j].f, g);
       u = fmaf(qdot(b.u[j], xv[j]), xv[j].f, u);
@@ -222,7 +208,7 @@ __device__ inline void dn_tile_dots(const DnTile<NGD, WF> &b, const Limbs (&hv)[
   for (int j = 0; j < NGD; ++j)
 #pragma unroll
     for (int i = 0; i < kDnRows; ++i) {
-      if constexpr (WF == kWfQ4G32) acc[i] = fmaf(qdot(b.q[i][j], hv[j]), scale_of(b.sc[j], i) * hv[j].f, acc[i]);
+      if constexpr (WF == kWfQ4G32) acc[i] = group_fma(qdot(b.q[i][j], hv[j]), scale_of(b.sc[j], i), hv[j].f, acc[i]);
       else acc[i] = fmaf(qdot(b.q[i][j], hv[j]), hv[j].f, acc[i]);
     }
 #pragma unroll

@@ -23,8 +23,15 @@
 // no partially filled slot published) fills a predicted union the same way but
 // leases nothing and publishes nothing: each copied slot keeps its own copy
 // event and is marked pending; the next acquire of the layer makes its compute
-// stream wait for the pending slots it leases and uploads the table.  Any later
-// copy into a pending slot waits for the earlier copy first.
+// stream wait for the pending slots it leases and uploads the table, in which a
+// pending slot that it neither leases nor finds complete is still absent (-1).
+// Any later copy into a pending slot waits for the earlier copy first.
+//
+// Generations (N3: generation-tagged slots, so that a stale user cannot
+// consume storage reused for another expert): every fill takes a new pool-wide
+// number, written into the slot's device generation entry on the side stream
+// before the copy; each table upload carries, next to table[e], the generation
+// of e's slot.  Kernels given the view use expert e only while the two agree.
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
@@ -43,15 +50,16 @@ struct moe_pool {
   bool device = true;
   bool poison = false;
   uint8_t *slab = nullptr;        // device: n_layers * spl slots
-  int32_t *d_tables = nullptr;    // device: [n_layers][E]
-  int32_t *h_stage = nullptr;     // pinned: [n_layers][E] staging for table uploads
+  int32_t *d_tables = nullptr;    // device: [n_layers][2E]: table[e], then the generation of e's slot
+  uint32_t *d_slot_gen = nullptr; // device: [n_layers][spl] generation of each slot's content
+  int32_t *h_stage = nullptr;     // pinned: [n_layers][2E] staging for table uploads
   std::vector<hipEvent_t> table_ev;  // per layer: staging buffer's last upload
   std::vector<int32_t> table;     // host mirror [n_layers][E]
   std::vector<const void *> src;  // [n_layers][E] pinned host sources
   struct Slot {
     int expert = -1;
     uint64_t last_use = 0;  // LRU clock of the last acquire
-    uint64_t gen = 0;       // fills of this slot so far
+    uint32_t gen = 0;       // pool-wide generation of the slot's content (0: never filled)
     bool leased = false;
     hipEvent_t done = nullptr;  // consumer-done event (valid when used)
     bool has_done = false;
@@ -62,8 +70,11 @@ struct moe_pool {
   std::vector<int> leased_layer;  // per layer: number of slots leased by the open acquire, -1 none
   std::vector<std::vector<int>> lease_list;
   std::vector<hipEvent_t> ev_pool;
-  std::vector<char> table_dirty;  // per layer: host table changed by a prefetch since the last upload
+  std::vector<char> table_dirty;  // per layer: device table differs from the host table
+  std::vector<uint64_t> lease_clock;  // per layer: clock of the open acquire
+  std::vector<uint64_t> fill_clock;   // per layer: clock of the latest fill
   uint64_t clock = 0;
+  uint32_t gen_counter = 0;
   // statistics
   uint64_t hits = 0, misses = 0, evictions = 0, fill_bytes = 0, acquires = 0;
   uint64_t prefetches = 0, prefetch_fills = 0, prefetch_hits = 0;
@@ -93,14 +104,25 @@ static int pick_victim(moe_pool *p, int layer) {
   return victim;
 }
 
+// One 32-bit store, launched on the side stream (a kernel rather than a memset
+// node, so the same sequence can sit in a captured graph).
+__global__ void k_store_u32(uint32_t *dst, uint32_t v) {
+  if (threadIdx.x == 0) *dst = v;
+}
+
 // Enqueues the copy of expert e into slot s of `layer` on `ss`, after the slot's
-// last consumer and (for a pending prefetch) its last copy.
+// last consumer and (for a pending prefetch) its last copy; the slot's new
+// generation is stored before the copy starts.
 static hipError_t enqueue_fill(moe_pool *p, int layer, int e, int s, hipStream_t ss) {
   moe_pool::Slot &sl = p->slots[(size_t)layer * p->spl + s];
   uint8_t *dst = p->slab + ((size_t)layer * p->spl + s) * (size_t)p->slot_bytes;
   hipError_t err = hipSuccess;
   if (sl.has_done) err = hipStreamWaitEvent(ss, sl.done, 0);  // previous consumer of the victim is done
   if (err == hipSuccess && sl.pending) err = hipStreamWaitEvent(ss, sl.fill_ev, 0);  // previous copy is done
+  if (err == hipSuccess) {
+    hipLaunchKernelGGL(k_store_u32, dim3(1), dim3(64), 0, ss, p->d_slot_gen + (size_t)layer * p->spl + s, sl.gen);
+    err = hipGetLastError();
+  }
   if (err == hipSuccess && p->poison) err = hipMemsetAsync(dst, 0xFF, (size_t)p->slot_bytes, ss);
   if (err == hipSuccess)
     err = hipMemcpyAsync(dst, p->src[(size_t)layer * p->E + e], (size_t)p->slot_bytes, hipMemcpyHostToDevice, ss);
@@ -143,12 +165,18 @@ int moe_pool_create(const moe_cfg *cfg, int32_t n_layers, int32_t slots_per_laye
   p->leased_layer.assign(n_layers, -1);
   p->lease_list.resize(n_layers);
   p->table_dirty.assign(n_layers, 0);
+  p->lease_clock.assign(n_layers, 0);
+  p->fill_clock.assign(n_layers, 0);
   if (p->device) {
     const size_t slab = (size_t)n_layers * slots_per_layer * (size_t)p->slot_bytes;
+    const size_t tab = (size_t)n_layers * 2 * p->E * sizeof(int32_t);
     hipError_t e = hipMalloc(&p->slab, slab);
-    if (e == hipSuccess) e = hipMalloc(&p->d_tables, (size_t)n_layers * p->E * sizeof(int32_t));
-    if (e == hipSuccess) e = hipHostMalloc(&p->h_stage, (size_t)n_layers * p->E * sizeof(int32_t), hipHostMallocDefault);
-    if (e == hipSuccess) e = hipMemset(p->d_tables, 0xFF, (size_t)n_layers * p->E * sizeof(int32_t));  // all -1
+    if (e == hipSuccess) e = hipMalloc(&p->d_tables, tab);
+    if (e == hipSuccess) e = hipMalloc(&p->d_slot_gen, (size_t)n_layers * slots_per_layer * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipHostMalloc(&p->h_stage, tab, hipHostMallocDefault);
+    // tables all -1 and expected generations all 0xFFFFFFFF; slot generations 0 (never filled)
+    if (e == hipSuccess) e = hipMemset(p->d_tables, 0xFF, tab);
+    if (e == hipSuccess) e = hipMemset(p->d_slot_gen, 0, (size_t)n_layers * slots_per_layer * sizeof(uint32_t));
     if (e == hipSuccess) {
       p->table_ev.assign(n_layers, nullptr);
       for (int l = 0; l < n_layers && e == hipSuccess; ++l) e = hipEventCreateWithFlags(&p->table_ev[l], hipEventDisableTiming);
@@ -175,6 +203,7 @@ void moe_pool_destroy(moe_pool *p) {
     if (e) (void)hipEventDestroy(e);
   if (p->slab) (void)hipFree(p->slab);
   if (p->d_tables) (void)hipFree(p->d_tables);
+  if (p->d_slot_gen) (void)hipFree(p->d_slot_gen);
   if (p->h_stage) (void)hipHostFree(p->h_stage);
   delete p;
 }
@@ -190,7 +219,7 @@ int moe_pool_acquire(moe_pool *p, int32_t layer, const int32_t *idx, int32_t n, 
                      int32_t *n_miss, void *compute, void *side) {
   if (!p || !view || (n > 0 && !idx)) return MOE_ENULL;
   if (layer < 0 || layer >= p->n_layers || n < 0) return MOE_EINVAL;
-  if (p->leased_layer[layer] >= 0) return MOE_ESTALE;  // previous lease of this layer not released
+  if (p->leased_layer[layer] >= 0) return MOE_ELEASE;  // previous lease of this layer not released
   std::vector<int> uniq;  // union of the named experts, in first-appearance order
   const int u = union_of(p, layer, idx, n, uniq);
   if (u) return u;
@@ -227,7 +256,7 @@ int moe_pool_acquire(moe_pool *p, int32_t layer, const int32_t *idx, int32_t n, 
     base[victim].expert = e;
     base[victim].leased = true;
     base[victim].last_use = now;
-    base[victim].gen += 1;
+    base[victim].gen = ++p->gen_counter;
     tab[e] = victim;
     leased.push_back(victim);
     fills.emplace_back(e, victim);
@@ -236,11 +265,16 @@ int moe_pool_acquire(moe_pool *p, int32_t layer, const int32_t *idx, int32_t n, 
   }
   p->leased_layer[layer] = (int)leased.size();
   p->lease_list[layer] = leased;
+  p->lease_clock[layer] = now;
+  if (!fills.empty()) p->fill_clock[layer] = now;
   if (n_miss) *n_miss = (int32_t)fills.size();
   view->base = p->slab + (size_t)layer * p->spl * (size_t)p->slot_bytes;
   view->slot_bytes = p->slot_bytes;
-  view->table = p->d_tables ? p->d_tables + (size_t)layer * p->E : nullptr;
+  view->table = p->d_tables ? p->d_tables + (size_t)layer * 2 * p->E : nullptr;
   view->n_slots = p->spl;
+  view->gen = p->d_tables ? (const uint32_t *)(p->d_tables + (size_t)layer * 2 * p->E + p->E) : nullptr;
+  view->slot_gen = p->d_slot_gen ? p->d_slot_gen + (size_t)layer * p->spl : nullptr;
+  view->lease = now;
   if (!p->device) {
     for (int s : waits) base[s].pending = false;
     return MOE_OK;
@@ -265,12 +299,29 @@ int moe_pool_acquire(moe_pool *p, int32_t layer, const int32_t *idx, int32_t n, 
   }
   if (err == hipSuccess && (!fills.empty() || p->table_dirty[layer])) {  // table changed: upload on the compute stream
     p->table_dirty[layer] = 0;
-    int32_t *stage = p->h_stage + (size_t)layer * p->E;
+    int32_t *stage = p->h_stage + (size_t)layer * 2 * p->E;
+    uint32_t *stage_gen = (uint32_t *)(stage + p->E);
     err = hipEventSynchronize(p->table_ev[layer]);  // the staging buffer's previous upload is complete
-    if (err == hipSuccess) {
-      std::memcpy(stage, tab, sizeof(int32_t) * p->E);
-      err = hipMemcpyAsync(p->d_tables + (size_t)layer * p->E, stage, sizeof(int32_t) * p->E, hipMemcpyHostToDevice, cs);
+    for (int e = 0; e < p->E && err == hipSuccess; ++e) {
+      int s = tab[e];
+      if (s >= 0 && base[s].pending) {
+        // a prefetched slot this acquire did not wait for: published once its copy is complete
+        const hipError_t q = hipEventQuery(base[s].fill_ev);
+        if (q == hipSuccess) {
+          base[s].pending = false;
+        } else if (q == hipErrorNotReady) {
+          s = -1;
+          p->table_dirty[layer] = 1;  // the next acquire publishes it
+        } else {
+          err = q;
+        }
+      }
+      stage[e] = s;
+      stage_gen[e] = s >= 0 ? base[s].gen : 0xFFFFFFFFu;
     }
+    if (err == hipSuccess)
+      err = hipMemcpyAsync(p->d_tables + (size_t)layer * 2 * p->E, stage, sizeof(int32_t) * 2 * p->E,
+                           hipMemcpyHostToDevice, cs);
     if (err == hipSuccess) err = hipEventRecord(p->table_ev[layer], cs);
   }
   if (err != hipSuccess) {
@@ -316,14 +367,17 @@ int moe_pool_prefetch(moe_pool *p, int32_t layer, const int32_t *idx, int32_t n,
     }
     base[victim].expert = e;
     base[victim].last_use = now;
-    base[victim].gen += 1;
+    base[victim].gen = ++p->gen_counter;
     tab[e] = victim;
     fills.emplace_back(e, victim);
     ++p->prefetch_fills;
   }
   for (int s : held) base[s].leased = false;
   if (n_fill) *n_fill = (int32_t)fills.size();
-  if (!fills.empty()) p->table_dirty[layer] = 1;
+  if (!fills.empty()) {
+    p->table_dirty[layer] = 1;
+    p->fill_clock[layer] = now;
+  }
   if (!p->device) {
     for (auto &f : fills) base[f.second].pending = true;
     return MOE_OK;
@@ -348,7 +402,7 @@ int moe_pool_prefetch(moe_pool *p, int32_t layer, const int32_t *idx, int32_t n,
 int moe_pool_release(moe_pool *p, int32_t layer, void *compute) {
   if (!p) return MOE_ENULL;
   if (layer < 0 || layer >= p->n_layers) return MOE_EINVAL;
-  if (p->leased_layer[layer] < 0) return MOE_ESTALE;
+  if (p->leased_layer[layer] < 0) return MOE_ELEASE;
   moe_pool::Slot *base = &p->slots[(size_t)layer * p->spl];
   hipError_t err = hipSuccess;
   for (int s : p->lease_list[layer]) {
@@ -366,6 +420,17 @@ int moe_pool_release(moe_pool *p, int32_t layer, void *compute) {
     return MOE_EHIP;
   }
   return MOE_OK;
+}
+
+int moe_pool_check_view(const moe_pool *p, int32_t layer, const moe_slot_view *v) {
+  if (!p || !v) return MOE_ENULL;
+  if (layer < 0 || layer >= p->n_layers) return MOE_EINVAL;
+  if (p->device && (v->table != p->d_tables + (size_t)layer * 2 * p->E ||
+                    v->base != p->slab + (size_t)layer * p->spl * (size_t)p->slot_bytes))
+    return MOE_EINVAL;
+  if (v->lease == 0 || v->lease > p->clock) return MOE_EINVAL;
+  if (p->leased_layer[layer] >= 0 && v->lease == p->lease_clock[layer]) return MOE_OK;  // lease still open
+  return p->fill_clock[layer] > v->lease ? MOE_ESTALE : MOE_OK;
 }
 
 int moe_pool_trace(const moe_pool *p, int32_t *out, int32_t cap) {

@@ -15,7 +15,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
 
-MOE_OK, MOE_EINVAL, MOE_ENULL, MOE_EDTYPE, MOE_EWORKSPACE, MOE_ENOSLOT, MOE_ESTALE, MOE_EHIP = 0, -1, -2, -3, -4, -5, -6, -7
+MOE_OK, MOE_EINVAL, MOE_ENULL, MOE_EDTYPE, MOE_EWORKSPACE, MOE_ENOSLOT, MOE_ESTALE, MOE_EHIP, MOE_ELEASE = \
+    0, -1, -2, -3, -4, -5, -6, -7, -8
 MOE_F32, MOE_BF16 = 0, 1
 MOE_WF_Q4_G32, MOE_WF_Q4_ROW, MOE_WF_Q8_ROW = 0, 1, 2
 
@@ -39,7 +40,8 @@ class moe_cfg(ctypes.Structure):
 
 class moe_slot_view(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("slot_bytes", ctypes.c_int64), ("table", ctypes.c_void_p),
-                ("n_slots", ctypes.c_int32)]
+                ("n_slots", ctypes.c_int32), ("gen", ctypes.c_void_p), ("slot_gen", ctypes.c_void_p),
+                ("lease", ctypes.c_uint64)]
 
 
 def _load():
@@ -75,6 +77,7 @@ def _load():
         "moe_pool_prefetch": (ctypes.c_int, [p, i32, p, i32, ctypes.POINTER(i32), p]),
         "moe_pool_trace": (ctypes.c_int, [p, p, i32]),
         "moe_pool_stats": (ctypes.c_int, [p, ctypes.c_char_p, sz]),
+        "moe_pool_check_view": (ctypes.c_int, [p, i32, ctypes.POINTER(moe_slot_view)]),
         "moe_profile_enable": (ctypes.c_int, [ctypes.c_int]),
         "moe_profile_report": (ctypes.c_int, [ctypes.c_char_p, sz]),
     }
@@ -267,6 +270,13 @@ class Pool:
         _check(_lib.moe_pool_stats(self.h, buf, len(buf)), "moe_pool_stats")
         return json.loads(buf.value.decode())
 
+    def check_view(self, layer: int, view: moe_slot_view) -> int:
+        """moe_pool_check_view: MOE_OK or MOE_ESTALE (other statuses raise)."""
+        rc = _lib.moe_pool_check_view(self.h, layer, ctypes.byref(view))
+        if rc not in (MOE_OK, MOE_ESTALE):
+            raise MoeError(rc, "moe_pool_check_view")
+        return rc
+
     def close(self) -> None:
         if self.h:
             _lib.moe_pool_destroy(self.h)
@@ -279,5 +289,6 @@ class Pool:
             pass
 
 
-def slot_view(base, slot_bytes: int, table, n_slots: int) -> moe_slot_view:
-    return moe_slot_view(ptr(base), slot_bytes, ptr(table), n_slots)
+def slot_view(base, slot_bytes: int, table, n_slots: int, gen=None, slot_gen=None) -> moe_slot_view:
+    """A view of caller-owned slots (generation tags optional: gen [E] and slot_gen [n_slots] uint32)."""
+    return moe_slot_view(ptr(base), slot_bytes, ptr(table), n_slots, ptr(gen), ptr(slot_gen), 0)

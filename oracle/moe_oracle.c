@@ -37,10 +37,10 @@
  *     the group size is the row length); fmt 2 = signed int8 (two's complement
  *     bytes) with one fp32 scale per row (the MTP layer's routed experts).  In
  *     every format W[r,c] = q[r,c] * scale, exact in fp64.
- *  R7 int8 activations ([PORT] "G2 implementation status": Colibri's IDOT=1
- *     quantises each activation row to int8 before the packed-int4 dot
- *     product, an approximate mode; [README] "Integer-dot kernels": int8
- *     activations): a row v of length n (the layer input of a token, and each
+ *  R7 int8 activations ([PORT] "G2 implementation status": the IDOT=1 setting
+ *     of Colibri, an approximate mode in which every activation row becomes
+ *     int8 ahead of its dot products with the packed int4 weights; [README]
+ *     "Integer-dot kernels"): a row v of length n (the layer input of a token, and each
  *     expert's hidden activation h after it is rounded to fp32) becomes
  *     d = fp32(amax / 127) with amax = max |v| (fp32), q_c = rint(fp32(v_c / d))
  *     (ties to even; q = 0 for an all-zero row), and the matmul uses q_c * d
@@ -401,5 +401,15 @@ int oracle_num_threads(void) {
   return omp_get_max_threads();
 #else
   return 1;
+#endif
+}
+
+/* Threads of the parallel loops from now on (the CPU-baseline timing runs the
+ * oracle on one thread and on all of them). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
 #endif
 }

@@ -66,6 +66,8 @@ def lib():
         L.oracle_expert_ffn_int8act.restype = None
         L.oracle_expert_ffn_int8act.argtypes = [i, i, i, i, p, p, p, p, p, p, p, p, p]
         L.oracle_num_threads.restype = i
+        L.oracle_set_num_threads.restype = None
+        L.oracle_set_num_threads.argtypes = [i]
         _lib = L
     return _lib
 
@@ -199,3 +201,7 @@ def moe_ffn(cfg, x: np.ndarray, idx: np.ndarray, w: np.ndarray, experts: dict, x
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().oracle_set_num_threads(n)

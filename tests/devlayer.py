@@ -116,3 +116,34 @@ def max_rel_err(y: np.ndarray, ref: np.ndarray) -> float:
             continue
         worst = max(worst, num / den)
     return worst
+
+
+def tile_cover(ridx: np.ndarray, n_experts: int, mfma_min_tokens: int, tile_rows: int = 256, item_rows: int = 4,
+               extra: int = 0, seed: int = 0) -> np.ndarray:
+    """Tokens of a batch such that every unit of work of the large-batch path holds
+    at least one of them: each matrix-core tile (tile_rows consecutive entries of
+    an expert's token list, which is in token order; the shared expert's tiles
+    are consecutive tokens) and each GEMV item (item_rows consecutive entries of
+    an expert below the threshold, or of the shared expert when the batch is).
+    Greedy set cover (a token sits in up to top_k + 1 units), plus `extra`
+    random tokens."""
+    from collections import Counter
+    S = ridx.shape[0]
+    units = []
+    for e in range(n_experts):
+        toks = np.where((ridx == e).any(axis=1))[0]
+        if toks.size == 0:
+            continue
+        step = tile_rows if mfma_min_tokens > 0 and toks.size >= mfma_min_tokens else item_rows
+        units += [set(toks[i:i + step].tolist()) for i in range(0, toks.size, step)]
+    step = tile_rows if mfma_min_tokens > 0 and S >= mfma_min_tokens else item_rows
+    units += [set(range(i, min(S, i + step))) for i in range(0, S, step)]
+    chosen = []
+    while units:
+        cnt = Counter(t for u in units for t in u)
+        best = max(cnt.items(), key=lambda kv: (kv[1], -kv[0]))[0]
+        chosen.append(best)
+        units = [u for u in units if best not in u]
+    rng = np.random.default_rng(seed)
+    chosen = set(chosen) | set(rng.choice(S, size=min(extra, S), replace=False).tolist())
+    return np.array(sorted(chosen))

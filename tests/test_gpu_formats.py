@@ -9,7 +9,7 @@ import torch
 
 from gen import inputs as gen
 from int4_routed_expert_amd import moe as M
-from tests.devlayer import DeviceLayer, x_device
+from tests.devlayer import DeviceLayer, tile_cover, x_device
 from tests.test_gpu_parity import MID, TOL_BF16, TOL_FP32, check_ffn, check_route, run_gpu, say
 
 pytestmark = pytest.mark.gpu
@@ -124,7 +124,8 @@ def test_layer_call_matches_route_then_ffn(tiny_f):
 def test_glm_shape_decode_verify_prefill(fmt):
     """GLM-5.2 shape (256 routed experts of 6144 x 2048 and the shared expert):
     decode (moe_layer, one token), a verify batch of 4 and a 2048-token bf16
-    batch (outputs on sampled tokens), all with the same experts and router."""
+    batch (outputs on one token of every matrix-core tile and GEMV item), all
+    with the same experts and router."""
     say(f"packing 257 GLM-5.2-shaped experts in format {fmt}")
     dl = DeviceLayer(fmt_workload(gen.WORKLOADS["decode"], FORMATS[fmt]))
     for step in range(3):
@@ -143,7 +144,6 @@ def test_glm_shape_decode_verify_prefill(fmt):
     ridx, rw = check_route(dl, x, idx, wt)
     counts = np.bincount(ridx.ravel(), minlength=dl.c.n_experts)
     say(f"prefill: experts with >= 16 tokens {(counts >= 16).sum()}")
-    hot = int(np.argmax(counts))
-    tokens = sorted({0, 1023, 2047, int(np.where((ridx == hot).any(axis=1))[0][0])})
-    check_ffn(dl, x, ridx, rw, y, np.array(tokens), TOL_BF16)
+    tokens = np.union1d(tile_cover(ridx, dl.c.n_experts, dl.cfg.mfma_min_tokens), [0, 2047])
+    check_ffn(dl, x, ridx, rw, y, tokens, TOL_BF16)
     assert np.isfinite(y).all()

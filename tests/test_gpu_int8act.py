@@ -15,7 +15,7 @@ import torch
 from gen import inputs as gen
 from int4_routed_expert_amd import moe as M
 from oracle import oracle as O
-from tests.devlayer import DeviceLayer, max_rel_err, x_device
+from tests.devlayer import DeviceLayer, max_rel_err, tile_cover, x_device
 from tests.test_gpu_parity import MID, check_route, run_gpu, say
 
 pytestmark = pytest.mark.gpu
@@ -142,7 +142,8 @@ def test_matrix_core_odd_group_count(fmt):
 
 def test_glm_shape_batch_row_scales():
     """2048 bf16 tokens, GLM-5.2 shape, int4 with row scales, int8 activations: the
-    integer matrix-core path for the many-token experts; sampled tokens."""
+    integer matrix-core path for the many-token experts; outputs on one token of
+    every matrix-core tile and GEMV item."""
     w = fmt_workload(gen.WORKLOADS["decode"], 1).with_(x_dtype="bf16", tokens=2048)
     dl = DeviceLayer(w, act_int8=1)
     x = gen.tokens(w)
@@ -150,8 +151,7 @@ def test_glm_shape_batch_row_scales():
     ridx, rw = check_route(dl, x, idx, wt)
     counts = np.bincount(ridx.ravel(), minlength=w.cfg.n_experts)
     say(f"experts with >= 16 tokens: {(counts >= 16).sum()}")
-    hot = int(np.argmax(counts))
-    tokens = np.array(sorted({0, 777, 2047, int(np.where((ridx == hot).any(axis=1))[0][0])}))
+    tokens = np.union1d(tile_cover(ridx, w.cfg.n_experts, dl.cfg.mfma_min_tokens), [0, 2047])
     check_int8act(dl, x, ridx, rw, y, tokens)
     assert np.isfinite(y).all()
 

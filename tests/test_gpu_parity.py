@@ -14,7 +14,7 @@ import torch
 from gen import inputs as gen
 from int4_routed_expert_amd import moe as M
 from oracle import oracle as O
-from tests.devlayer import DeviceLayer, dev, max_rel_err, x_device
+from tests.devlayer import DeviceLayer, dev, max_rel_err, tile_cover, x_device
 
 pytestmark = pytest.mark.gpu
 
@@ -484,9 +484,12 @@ def test_matrix_core_unresident_slot_poisons_only_its_tokens(mid):
 
 
 def test_prefill_full_size():
-    """2048 tokens, bf16 activations, Zipf-skewed routing: every token's indices
-    and weights are checked, outputs on a sample of tokens (the oracle runs one
-    token at a time)."""
+    """2048 tokens, bf16 activations, Zipf-skewed routing, in the launch
+    configuration the prefill benchmark times: every token's indices and weights
+    are checked; outputs on a set of tokens that holds at least one token of
+    every 256-row matrix-core tile of every expert (and of the shared expert) and
+    of every 4-token GEMV item (the oracle runs one token at a time), plus the
+    batch's first and last token and a few random ones."""
     w = gen.WORKLOADS["prefill"]
     dl = DeviceLayer(w)
     x = gen.tokens(w)
@@ -495,9 +498,96 @@ def test_prefill_full_size():
     ridx, rw = check_route(dl, x, idx, wt)
     counts = np.bincount(ridx.ravel(), minlength=w.cfg.n_experts)
     say(f"prefill: max tokens per expert {counts.max()}, experts with >= 16 tokens {(counts >= 16).sum()}")
-    rng = np.random.default_rng(0)
-    hot = int(np.argmax(counts))
-    tokens = sorted(set(rng.choice(2048, 6, replace=False).tolist())
-                    | {int(np.where((ridx == hot).any(axis=1))[0][0]), 2047})
-    check_ffn(dl, x, ridx, rw, y, np.array(tokens), TOL_BF16)
+    tokens = np.union1d(tile_cover(ridx, w.cfg.n_experts, dl.cfg.mfma_min_tokens, extra=6), [0, 2047])
+    say(f"prefill: comparing {tokens.size} tokens")
+    check_ffn(dl, x, ridx, rw, y, tokens, TOL_BF16)
     assert np.isfinite(y).all()
+
+
+def scaled_rows(x: np.ndarray, kind: str, seed: int) -> np.ndarray:
+    """x rows rescaled: 'wide' multiplies each 32-element group by 2^a and each
+    element by 2^b more (a, b uniform integers in [-20, 20]: values within a group
+    and across the row span about 2^40); 'big' by 2^58 and 'small' by 2^-64 (the
+    outputs then lie near the top and the bottom of the fp32 range: SwiGLU
+    squares the activations' scale)."""
+    rng = np.random.default_rng(seed)
+    x = x.astype(np.float64)
+    if kind == "wide":
+        a = rng.integers(-20, 21, size=(x.shape[0], x.shape[1] // 32, 1))
+        b = rng.integers(-20, 21, size=(x.shape[0], x.shape[1] // 32, 32))
+        x = (x.reshape(x.shape[0], -1, 32) * np.exp2(a + b)).reshape(x.shape)
+    else:
+        x = x * 2.0 ** (58 if kind == "big" else -64)
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("kind", ["wide", "big", "small"])
+def test_decode_extreme_activations(glm, kind):
+    """GLM-5.2 shape, the exact FFN paths (one token, a batch of four, a batch of
+    six on the exact large-batch path) on activations whose groups span ~2^40, or
+    whose outputs approach the largest (~1e37) or smallest (~1e-37) normal fp32
+    values: every token within the fp32 bar of the oracle, and a token's row of
+    the four-token batch bitwise equal to its one-token result.  The routing is
+    that of the unscaled tokens, so only the FFN's arithmetic sees the extremes."""
+    c = glm.c
+    x0 = gen.tokens(glm.w.with_(tokens=6), step=4321)
+    ridx, rw, _, flags, _ = O.route(c, x0, glm.W_host, glm.bias_host)
+    assert not flags.any()
+    x = scaled_rows(x0, kind, 17)
+    experts = {e: glm.host_expert(e) for e in set(ridx.ravel().tolist())}
+    experts[c.n_experts] = glm.host[c.n_experts]
+    ref = O.moe_ffn(c, x, ridx, rw, experts)
+    assert np.isfinite(ref).all() and np.abs(ref).max() > 0
+    say(f"{kind}: |y_ref| in [{np.abs(ref).min():.3e}, {np.abs(ref).max():.3e}]")
+    ys = {}
+    for S in (1, 4, 6):
+        y = glm.ffn(dev(x[:S]), M.MOE_F32, dev(ridx[:S]), dev(rw[:S].astype(np.float32)), mfma_min_tokens=0)
+        torch.cuda.synchronize()
+        ys[S] = y.cpu().numpy()
+        err = max_rel_err(ys[S], ref[:S])
+        say(f"  S={S}: max rel err {err:.3e}")
+        assert err <= TOL_FP32, (kind, S, err)
+    assert np.array_equal(ys[4][0], ys[1][0])
+
+
+@pytest.mark.parametrize("S", [1, 4])
+@pytest.mark.parametrize("layer", ["tiny", "glm"])
+def test_layer_graph_replays_match_oracle(tiny, glm, layer, S):
+    """moe_layer captured once in a HIP graph (one token: three kernels; four
+    tokens: the router and the few-token kernels) and replayed over 8 distinct
+    inputs written into its input buffer between replays: every replay's idx, w
+    and y match the oracle (idx exactly, w within 1e-6 rsf, y within the fp32
+    bar), with no eager call in between."""
+    dl = {"tiny": tiny, "glm": glm}[layer]
+    c = dl.c
+    ws = dl.workspace(S)
+    xbuf = torch.empty((S, c.hidden), dtype=torch.float32, device="cuda")
+    idx = torch.empty((S, c.top_k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((S, c.top_k), dtype=torch.float32, device="cuda")
+    y = torch.empty((S, c.hidden), dtype=torch.float32, device="cuda")
+    view = dl.view()
+    xs = [gen.tokens(dl.w.with_(tokens=S), step=1300 + 10 * i) for i in range(8)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up call outside the capture
+        xbuf.copy_(dev(xs[0]))
+        M.moe_layer(dl.cfg, xbuf, M.MOE_F32, S, dl.W, dl.bias, idx, wt, view, dl.shared, y, ws, ws.numel())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        M.moe_layer(dl.cfg, xbuf, M.MOE_F32, S, dl.W, dl.bias, idx, wt, view, dl.shared, y, ws, ws.numel())
+    torch.cuda.synchronize()
+    for i, xh in enumerate(xs):
+        xbuf.copy_(dev(xh))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ridx, rw, _, flags, _ = O.route(c, xh, dl.W_host, dl.bias_host)
+        assert not flags.any()
+        assert np.array_equal(idx.cpu().numpy(), ridx), (layer, S, i)
+        assert np.abs(wt.cpu().numpy() - rw).max() <= 1e-6 * c.routed_scaling_factor
+        experts = {e: dl.host_expert(e) for e in set(ridx.ravel().tolist())}
+        experts[c.n_experts] = dl.host[c.n_experts]
+        ref = O.moe_ffn(c, xh, ridx, rw, experts)
+        err = max_rel_err(y.cpu().numpy(), ref)
+        assert err <= TOL_FP32, (layer, S, i, err)

@@ -137,3 +137,68 @@ def test_pool_row_scaled_experts(fmt):
     st, worst, n, _ = run_stack(w, n_layers=3, steps=5, spl=5, flags=M.MOE_POOL_POISON)
     print("pool stats", st, "worst", worst, "checked", n, flush=True)
     assert st["misses"] > 3 * 4 and st["evictions"] > 0
+
+
+def test_stale_view_after_refill_is_poisoned():
+    """Generation tags: a view kept after its release, used once a prefetch has
+    refilled some of its slots with other experts (the device table still names
+    those slots: a prefetch publishes nothing), gives NaN rows for the tokens of
+    the refilled experts and bitwise the earlier rows for the others, on the
+    one-token, few-token and matrix-core paths; the host check reports the view
+    stale.  The same view with its tags removed reads the other experts'
+    weights: finite rows that differ from the true ones."""
+    c = MID
+    w = gen.Workload("stale", c, tokens=1, seed=53)
+    cfg = M.make_cfg(c, mfma_min_tokens=4)
+    E, I, k = c.n_experts, c.moe_inter, c.top_k
+    sb = M.moe_expert_bytes(cfg, I)
+    host = torch.empty((E, sb), dtype=torch.uint8, pin_memory=True)
+    for e in range(E):
+        M.pack_expert(cfg, I, *gen.expert_weights(w, 0, e).parts(), host[e].numpy(), 0)
+    sh = gen.expert_weights(w, 0, E)
+    shared = torch.zeros(M.moe_expert_bytes(cfg, c.shared_inter), dtype=torch.uint8, device="cuda")
+    M.pack_expert(cfg, c.shared_inter, *[dev(a) for a in sh.parts()], shared, 1)
+    pool = M.Pool(cfg, 1, 2 * k + 2, M.MOE_POOL_POISON)
+    for e in range(E):
+        pool.register_host(0, e, host[e])
+    A = np.array([3, 7, 11, 19], np.int32)   # slots 0..3 (first appearance order)
+    B = np.array([5, 13, 21, 30], np.int32)  # slots 4..7
+    compute, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    view, n_miss = pool.acquire(0, np.concatenate([A, B]), compute, side)
+    assert n_miss == 2 * k
+    pool.release(0, compute)
+    S = 8
+    x = dev(gen.tokens(w.with_(tokens=S), step=5))
+    rows = np.stack([A if t % 2 == 0 else B for t in range(S)]).astype(np.int32)
+    wt = dev(np.full((S, k), c.routed_scaling_factor / k, np.float32))
+    ws = M.workspace(cfg, S)
+
+    def run(v):
+        out = []
+        for sl in (slice(0, 1), slice(1, 2), slice(0, 2), slice(0, S)):  # one token, two tokens, matrix cores
+            n = sl.stop - sl.start
+            y = torch.full((n, c.hidden), 7.0, device="cuda")
+            M.moe_ffn(cfg, x[sl], M.MOE_F32, n, dev(rows[sl]), wt[sl], v, shared, y, ws, ws.numel())
+            out.append(y)
+        torch.cuda.synchronize()
+        return [y.cpu().numpy() for y in out]
+
+    before = run(view)
+    assert all(np.isfinite(y).all() for y in before)
+    # a prefetch of four other experts: two free slots, then the two least recently used (ties: lowest
+    # slot), i.e. slots 0 and 1 that hold A[0] and A[1]
+    assert pool.prefetch(0, np.array([0, 1, 2, 4], np.int32), side) == 4
+    side.synchronize()
+    assert pool.check_view(0, view) == M.MOE_ESTALE
+    after = run(view)
+    for got, ref, sl in zip(after, before, (slice(0, 1), slice(1, 2), slice(0, 2), slice(0, S))):
+        toks = np.arange(sl.start, sl.stop)
+        for i, t in enumerate(toks):
+            if t % 2 == 0:  # A: two of its experts were refilled
+                assert np.isnan(got[i]).all(), (sl, t)
+            else:
+                assert np.array_equal(got[i], ref[i]), (sl, t)
+    untagged = M.slot_view(view.base, view.slot_bytes, view.table, view.n_slots)
+    raw = run(untagged)
+    assert np.isfinite(raw[0]).all() and not np.array_equal(raw[0], before[0])
+    pool.close()

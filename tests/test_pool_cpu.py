@@ -128,11 +128,11 @@ def test_pool_errors():
     pool.acquire(0, np.array([1, 2], np.int32))
     with pytest.raises(M.MoeError) as e:
         pool.acquire(0, np.array([1], np.int32))  # layer 0 still leased
-    assert e.value.status == M.MOE_ESTALE
+    assert e.value.status == M.MOE_ELEASE
     pool.release(0)
     with pytest.raises(M.MoeError) as e:
         pool.release(0)
-    assert e.value.status == M.MOE_ESTALE
+    assert e.value.status == M.MOE_ELEASE
     with pytest.raises(M.MoeError) as e:
         pool.acquire(1, np.array([1, 2, 3, 4], np.int32))  # union of 4 > 3 slots
     assert e.value.status == M.MOE_ENOSLOT
@@ -223,3 +223,32 @@ def test_prefetch_then_acquire_hits_and_leases_are_kept():
     with pytest.raises(M.MoeError) as e:
         pool.prefetch(0, np.array([1, 2, 3, 4, 5], np.int32))  # union of 5 > 4 slots
     assert e.value.status == M.MOE_ENOSLOT
+
+
+def test_view_staleness_on_the_host():
+    """moe_pool_check_view: a view is current while its lease is open and after
+    its release until a slot of its layer is refilled (by an acquire miss or a
+    prefetch); then it is stale.  Hits and other layers' fills leave it current."""
+    pool = make_pool(2, 3)
+    v1, _ = pool.acquire(0, np.array([1, 2], np.int32))
+    assert pool.check_view(0, v1) == M.MOE_OK
+    pool.release(0)
+    assert pool.check_view(0, v1) == M.MOE_OK
+    v2, n_miss = pool.acquire(0, np.array([2, 1], np.int32))  # all hits: nothing refilled
+    assert n_miss == 0
+    pool.release(0)
+    assert pool.check_view(0, v1) == M.MOE_OK and pool.check_view(0, v2) == M.MOE_OK
+    pool.acquire(1, np.array([5, 6, 7], np.int32))  # another layer's fills
+    pool.release(1)
+    assert pool.check_view(0, v1) == M.MOE_OK
+    v3, n_miss = pool.acquire(0, np.array([3], np.int32))  # a miss: a slot of layer 0 is filled
+    assert n_miss == 1
+    assert pool.check_view(0, v1) == M.MOE_ESTALE and pool.check_view(0, v2) == M.MOE_ESTALE
+    assert pool.check_view(0, v3) == M.MOE_OK  # its own lease is open
+    pool.release(0)
+    assert pool.check_view(0, v3) == M.MOE_OK
+    assert pool.prefetch(0, np.array([9], np.int32)) == 1  # a prefetch refills a slot
+    assert pool.check_view(0, v3) == M.MOE_ESTALE
+    with pytest.raises(M.MoeError) as e:
+        pool.check_view(5, v3)
+    assert e.value.status == M.MOE_EINVAL

@@ -62,3 +62,46 @@ def test_nibbles_to_int8_bytes():
             expect += [signed(byte & 0xF, 4), signed(byte >> 4, 4)]  # element 2j low nibble, 2j+1 high
         got = [signed(o >> (8 * i), 8) for o in nib_to_i8(w) for i in range(4)]
         assert got == expect
+
+
+def block_fixed_point(v: np.ndarray):
+    """The kernels' block fixed point of one fp32 group: sh = min(22 - E, 149) with
+    max|v| < 2^E, X = rint(v * 2^sh) (ties to even), factor f = 2^-sh."""
+    m = float(np.max(np.abs(v)))
+    E = int(np.frexp(np.float32(m))[1])
+    sh = min(22 - E, 149)
+    X = np.rint(np.ldexp(v.astype(np.float64), sh))
+    return X, sh
+
+
+def test_block_fixed_point_across_the_fp32_range():
+    """|X| <= 2^22 for every group scale from the largest fp32 values to the
+    subnormals; a group of subnormals is held exactly (the shift stops at 149);
+    each element is kept to within half a step of 2^(E-22) <= 2^-22 of the
+    group maximum."""
+    rng = np.random.default_rng(4)
+    for e in list(range(-149, 128, 7)) + [127, -126, -127, -140, -149]:
+        v = (rng.uniform(-1, 1, 32) * 2.0 ** e).astype(np.float32)
+        if not np.isfinite(v).all() or np.max(np.abs(v)) == 0:
+            continue
+        X, sh = block_fixed_point(v)
+        assert np.max(np.abs(X)) <= 2 ** 22
+        back = np.ldexp(X, -sh)
+        m = float(np.max(np.abs(v)))
+        assert np.max(np.abs(back - v.astype(np.float64))) <= m * 2.0 ** -22
+        if m < 2.0 ** -127:  # shift 149: subnormals are multiples of 2^-149, held exactly
+            assert np.array_equal(back, v.astype(np.float64))
+
+
+def test_group_factor_order_keeps_tiny_contributions():
+    """A group's contribution T * s * 2^-sh: multiplying the fp16 scale by 2^-sh
+    first underflows for tiny activations, applying the power of two last does
+    not (the kernels' order)."""
+    T = np.float32(1234567.0)
+    s = np.float32(0.0137)
+    f = np.float32(2.0 ** -140)
+    exact = float(T) * float(s) * 2.0 ** -140
+    late = np.float32(T * s) * f
+    early = T * np.float32(s * f)
+    assert abs(float(late) - exact) <= exact * 2.0 ** -23
+    assert abs(float(early) - exact) > exact * 2.0 ** -10
