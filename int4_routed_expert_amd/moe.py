@@ -113,9 +113,9 @@ def make_cfg(c, mfma_min_tokens: int = MFMA_MIN_TOKENS, act_int8: int = 0) -> mo
 
 
 def ptr(t) -> int | None:
-    """Raw address of a torch tensor or numpy array (None passes NULL)."""
-    if t is None:
-        return None
+    """Raw address of a torch tensor or numpy array, or an address given as an int (None passes NULL)."""
+    if t is None or isinstance(t, int):
+        return t
     if hasattr(t, "data_ptr"):
         return t.data_ptr()
     return t.ctypes.data
