@@ -243,6 +243,24 @@ int moe_layer(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, con
               int32_t *idx, float *w, const moe_slot_view *experts, const void *shared, float *y, void *ws,
               size_t ws_bytes, void *stream);
 
+/* moe_layer for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It takes
+ * no workspace: the library's own fixed per-device array of MOE_SCRATCH_BYTES
+ * (8 MiB; each GPU the library runs on holds one until the process ends) serves
+ * as the workspace, and the call allocates nothing.  Same arguments as
+ * moe_layer without ws/ws_bytes, same kernels, bit-identical idx, w and y; for
+ * S > 1 it first rewrites the workspace header with a kernel on `stream`.
+ * Errors: those of moe_layer, and MOE_EWORKSPACE when moe_workspace_bytes(cfg,
+ * S) exceeds MOE_SCRATCH_BYTES (the GLM-5.2 shape fits up to S = 16; the
+ * largest supported shape up to S = 4), with nothing enqueued.  Every call on
+ * one GPU uses that GPU's array, which keeps the last call's contents: calls
+ * that overlap on one GPU (on different streams, or in graphs replayed
+ * concurrently) race and must not be made. */
+#define MOE_SCRATCH_BYTES ((size_t)8 << 20)
+int moe_layer_noalloc(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, const float *W_gate,
+                      const float *bias, int32_t *idx, float *w, const moe_slot_view *experts, const void *shared,
+                      float *y, void *stream);
+
 /* ---- HBM expert-slot pool ([PORT] N3 and G3 status; [README] per-layer LRU) ----
  * One device slab of n_layers * slots_per_layer slots of moe_expert_bytes(cfg,
  * moe_inter) bytes, a device table per layer (table[e] = slot, or -1), and a

@@ -4,6 +4,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -478,17 +479,24 @@ int moe_ffn(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const i
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
-int moe_layer(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const float *W, const float *bias,
-              int32_t *idx, float *w, const moe_slot_view *ex, const void *shared, float *y, void *ws, size_t ws_bytes,
-              void *stream) {
+}  // extern "C"
+
+namespace moe {
+
+// One layer forward on a workspace; write_header: the workspace header is
+// written first (by a kernel on the stream) when the call reads it (S > 1).
+static int layer_impl(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const float *W, const float *bias,
+                      int32_t *idx, float *w, const moe_slot_view *ex, const void *shared, float *y, void *ws,
+                      size_t ws_bytes, hipStream_t st, bool write_header) {
   RouteArgs r;
   int v = route_args(c, x, x_dtype, S, W, bias, idx, w, ws, ws_bytes, r);
   if (v || S == 0) return v;
   FfnArgs f;
   v = ffn_args(c, x, x_dtype, S, idx, w, ex, shared, y, ws, ws_bytes, f);
   if (v) return v;
-  const hipStream_t st = (hipStream_t)stream;
-  hipError_t e;
+  hipError_t e = hipSuccess;
+  if (write_header && S > 1) e = launch_ws_init(r.sync, st);
+  if (e != hipSuccess) return hip_fail(e);
   if (S == 1) {  // the router kernel stores scores and keys; the gate/up kernel selects
     e = launch_route_scores(r, st);
     if (e == hipSuccess) {
@@ -503,6 +511,59 @@ int moe_layer(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const
     if (e == hipSuccess) e = run_ffn(f, st);
   }
   return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+// ---- workspace of the entry point that allocates nothing -----------------------
+// A fixed array in the library's code object: every device the library runs on
+// holds its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: only the address hipGetSymbolAddress
+// returns for the current device is ever passed to a kernel.
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) uint8_t scratch[MOE_SCRATCH_BYTES];
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current) and kept.
+static int scratch_ptr(void **out) {
+  static std::mutex mu;
+  static void *ptrs[kScratchDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kScratchDevices) return MOE_EINVAL;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!p) return MOE_EHIP;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+int moe_layer(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const float *W, const float *bias,
+              int32_t *idx, float *w, const moe_slot_view *ex, const void *shared, float *y, void *ws, size_t ws_bytes,
+              void *stream) {
+  return layer_impl(c, x, x_dtype, S, W, bias, idx, w, ex, shared, y, ws, ws_bytes, (hipStream_t)stream, false);
+}
+
+int moe_layer_noalloc(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S, const float *W, const float *bias,
+                      int32_t *idx, float *w, const moe_slot_view *ex, const void *shared, float *y, void *stream) {
+  const int v = moe_validate_cfg(c);
+  if (v) return v;
+  if (S < 0) return MOE_EINVAL;
+  if (S == 0) return MOE_OK;
+  if (ws_layout(*c, S).total > MOE_SCRATCH_BYTES) return MOE_EWORKSPACE;
+  void *ws = nullptr;
+  const int p = scratch_ptr(&ws);
+  if (p) return p;
+  return layer_impl(c, x, x_dtype, S, W, bias, idx, w, ex, shared, y, ws, MOE_SCRATCH_BYTES, (hipStream_t)stream,
+                    true);
 }
 
 }  // extern "C"

@@ -69,6 +69,7 @@ def _load():
         "moe_route": (ctypes.c_int, [cp, p, i32, i32, p, p, p, p, p, sz, p]),
         "moe_ffn": (ctypes.c_int, [cp, p, i32, i32, p, p, ctypes.POINTER(moe_slot_view), p, p, p, sz, p]),
         "moe_layer": (ctypes.c_int, [cp, p, i32, i32, p, p, p, p, ctypes.POINTER(moe_slot_view), p, p, p, sz, p]),
+        "moe_layer_noalloc": (ctypes.c_int, [cp, p, i32, i32, p, p, p, p, ctypes.POINTER(moe_slot_view), p, p, p]),
         "moe_pool_create": (ctypes.c_int, [cp, i32, i32, i32, ctypes.POINTER(p)]),
         "moe_pool_destroy": (None, [p]),
         "moe_pool_register_host": (ctypes.c_int, [p, i32, i32, p]),
@@ -203,6 +204,15 @@ def moe_layer(cfg: moe_cfg, x, x_dtype: int, S: int, W, bias, idx, w, view: moe_
     _check(_lib.moe_layer(ctypes.byref(cfg), ptr(x), x_dtype, S, ptr(W), ptr(bias), ptr(idx), ptr(w),
                           ctypes.byref(view), ptr(shared), ptr(y), ptr(ws), ws_bytes, stream_handle(stream)),
            "moe_layer")
+
+
+def moe_layer_noalloc(cfg: moe_cfg, x, x_dtype: int, S: int, W, bias, idx, w, view: moe_slot_view, shared, y,
+                      stream=None) -> None:
+    _check(_lib.moe_layer_noalloc(ctypes.byref(cfg), ptr(x), x_dtype, S, ptr(W), ptr(bias), ptr(idx), ptr(w),
+                                  ctypes.byref(view), ptr(shared), ptr(y), stream_handle(stream)), "moe_layer_noalloc")
+
+
+MOE_SCRATCH_BYTES = 8 << 20  # the library's per-device workspace of moe_layer_noalloc
 
 
 def moe_profile_enable(on: bool) -> None:
