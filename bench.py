@@ -807,8 +807,9 @@ def main() -> int:
     M.moe_profile_enable(False)
     kernels = {name: {"avg_us": ms * 1e3 / n, "launches": n} for name, (ms, n) in prof.items()}
     log("per-kernel (hipEvent) averages:", json.dumps(kernels))
-    rk = "gateup_s1"  # dominant kernel: gate/up of the 9 experts (payload and scales)
-    alg_bytes = 9 * gu_bytes(fmt, H, I)
+    rk = "gateup_s1"  # dominant kernel: gate/up of the 8 routed experts and the shared expert (payload and scales)
+    n_gu = k + 1
+    alg_bytes = n_gu * gu_bytes(fmt, H, I)
     k_us = kernels[rk]["avg_us"]
     achieved = alg_bytes / (k_us * 1e-6) / 1e9
     traffic = measured_traffic(rk, fmt)
@@ -851,7 +852,7 @@ def main() -> int:
         "kernels_us": {n: round(v["avg_us"], 3) for n, v in kernels.items()},
         "roofline": {"kernel": rk, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": alg_bytes},
+                     "algorithmic_bytes_per_launch": alg_bytes, "experts_per_launch": n_gu},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

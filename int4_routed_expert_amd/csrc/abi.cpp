@@ -498,14 +498,12 @@ static int layer_impl(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t 
   if (write_header && S > 1) e = launch_ws_init(r.sync, st);
   if (e != hipSuccess) return hip_fail(e);
   if (S == 1) {  // the router kernel stores scores and keys; the gate/up kernel selects
+    f.sel = 1;
+    f.G = r.G; f.Gk = r.Gk; f.norm = r.norm; f.rsf = r.rsf;
+    f.keys = r.keys; f.scores = r.scores;
+    f.idx_out = idx; f.w_out = w;
     e = launch_route_scores(r, st);
-    if (e == hipSuccess) {
-      f.sel = 1;
-      f.G = r.G; f.Gk = r.Gk; f.norm = r.norm; f.rsf = r.rsf;
-      f.keys = r.keys; f.scores = r.scores;
-      f.idx_out = idx; f.w_out = w;
-      e = launch_ffn_decode(f, st);
-    }
+    if (e == hipSuccess) e = launch_ffn_decode(f, st);
   } else {
     e = launch_route(r, st);
     if (e == hipSuccess) e = run_ffn(f, st);

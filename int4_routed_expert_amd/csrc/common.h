@@ -152,6 +152,8 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t st);
 hipError_t launch_ws_init(uint32_t *sync, hipStream_t st);
 hipError_t launch_route_scores(const RouteArgs &a, hipStream_t st);  // S <= 8: scores and keys only
 hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st);  // S <= kSmallS
+hipError_t launch_gateup_s1(const FfnArgs &a, hipStream_t st);   // S = 1: gate/up (+ selection)
+hipError_t launch_down_s1(const FfnArgs &a, hipStream_t st);     // S = 1: down + combine
 hipError_t launch_ffn_batch(const FfnArgs &a, hipStream_t st);   // S > kSmallS
 hipError_t launch_gu_mfma(const FfnArgs &a, hipStream_t st);
 hipError_t launch_dn_mfma(const FfnArgs &a, hipStream_t st);
@@ -166,8 +168,8 @@ hipError_t launch_pack_rows(int H, int I, int wf, const uint8_t *qg, const float
 
 // workspace layout (bytes, each region 256-aligned)
 struct WsLayout {
-  size_t sync, logits, scores, keys, h, xl, xf, hl, hf, eptr, part, lists, counts, items, n_items, mtiles, xb, xq, dx,
-      hq, dh, total;
+  size_t sync, logits, scores, keys, h, xl, xf, hl, hf, eptr, part, lists, counts, items, n_items, mtiles, xb, xq,
+      dx, hq, dh, total;
   int32_t max_items, max_mtiles;
 };
 WsLayout ws_layout(const moe_cfg &c, int32_t S);

@@ -1095,46 +1095,52 @@ hipError_t launch_quant_h(const FfnArgs &a, hipStream_t st) {
       default: MOE_NG_CASES(ng_, kWfQ4G32, KERNEL, GRID, BLOCK, LDS, ST, __VA_ARGS__); break;        \
     }                                                                                                \
   } while (0)
-hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st) {
+hipError_t launch_gateup_s1(const FfnArgs &a, hipStream_t st) {
+  ProfScope ps("gateup_s1", st);
+  const long feats = (long)a.k * a.I + a.Is;
+  const long waves = std::max<long>((long)a.n_cu * 8, (feats + kGuMaxPerWave - 1) / kGuMaxPerWave);
+  const dim3 g((unsigned)((waves + 3) / 4)), blk(256);
+  const size_t lds = (size_t)(a.H / kGroup) * 25 * sizeof(uint32_t);
+  if (!a.sel) {
+    MOE_DISPATCH_NG(ceil_groups(a.H), k_gateup_s1, g, blk, lds, st, 0);
+  } else if (a.E <= 256) {
+    MOE_DISPATCH_NG(ceil_groups(a.H), k_gateup_s1, g, blk, lds, st, 1);
+  } else {
+    MOE_DISPATCH_NG(ceil_groups(a.H), k_gateup_s1, g, blk, lds, st, 4);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_down_s1(const FfnArgs &a, hipStream_t st) {
   const int Imax = std::max(a.I, a.Is);
+  hipError_t e = launch_quant_h(a, st);
+  if (e != hipSuccess) return e;
+  const int NE = a.k + (a.Is > 0 ? 1 : 0);
+  const size_t hlds = (size_t)NE * (Imax / kGroup) * 25 * sizeof(uint32_t);
+  const bool in_lds = hlds <= 64 * 1024;
+  if (!in_lds) {
+    ProfScope ps("h_limbs", st);
+    e = launch_to_limbs(a.h, 0, NE, Imax, Imax, a.hl, a.hf, a.wf, a.act_q ? a.hq : nullptr, a.dh, st);
+    if (e != hipSuccess) return e;
+  }
+  ProfScope ps("down_s1", st);
+  const dim3 g((unsigned)a.n_blk), blk(64 * std::min(NE * a.tb, dn_s1_waves(a.wf)));
+  if (in_lds) {
+    MOE_DISPATCH_NG(ceil_groups(Imax), k_down_s1, g, blk, hlds, st, true);
+  } else {
+    MOE_DISPATCH_NG(ceil_groups(Imax), k_down_s1, g, blk, 0, st, false);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st) {
   hipError_t e = launch_quant_x(a, st);
   if (e != hipSuccess) return e;
   if (a.S == 1) {
-    {
-      ProfScope ps("gateup_s1", st);
-      const long feats = (long)a.k * a.I + a.Is;
-      const long waves = std::max<long>((long)a.n_cu * 8, (feats + kGuMaxPerWave - 1) / kGuMaxPerWave);
-      const dim3 g((unsigned)((waves + 3) / 4)), blk(256);
-      const size_t lds = (size_t)(a.H / kGroup) * 25 * sizeof(uint32_t);
-      if (!a.sel) {
-        MOE_DISPATCH_NG(ceil_groups(a.H), k_gateup_s1, g, blk, lds, st, 0);
-      } else if (a.E <= 256) {
-        MOE_DISPATCH_NG(ceil_groups(a.H), k_gateup_s1, g, blk, lds, st, 1);
-      } else {
-        MOE_DISPATCH_NG(ceil_groups(a.H), k_gateup_s1, g, blk, lds, st, 4);
-      }
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-    e = launch_quant_h(a, st);
-    if (e != hipSuccess) return e;
-    const int NE = a.k + (a.Is > 0 ? 1 : 0);
-    const size_t hlds = (size_t)NE * (Imax / kGroup) * 25 * sizeof(uint32_t);
-    const bool in_lds = hlds <= 64 * 1024;
-    if (!in_lds) {
-      ProfScope ps("h_limbs", st);
-      e = launch_to_limbs(a.h, 0, NE, Imax, Imax, a.hl, a.hf, a.wf, a.act_q ? a.hq : nullptr, a.dh, st);
-      if (e != hipSuccess) return e;
-    }
-    ProfScope ps("down_s1", st);
-    const dim3 g((unsigned)a.n_blk), blk(64 * std::min(NE * a.tb, dn_s1_waves(a.wf)));
-    if (in_lds) {
-      MOE_DISPATCH_NG(ceil_groups(Imax), k_down_s1, g, blk, hlds, st, true);
-    } else {
-      MOE_DISPATCH_NG(ceil_groups(Imax), k_down_s1, g, blk, 0, st, false);
-    }
-    return hipGetLastError();
+    e = launch_gateup_s1(a, st);
+    return e == hipSuccess ? launch_down_s1(a, st) : e;
   }
+  const int Imax = std::max(a.I, a.Is);
   {
     ProfScope ps("gateup_small", st);
     const dim3 g((unsigned)a.n_cu), blk(kGuSmallWaves * 64);
