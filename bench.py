@@ -163,9 +163,10 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_writ
     true_kib = copy_mib * 1024.0
     f_scale = true_kib / one(copy_fetch_csv, "FETCH_SIZE", "k_copy")
     w_scale = true_kib / one(copy_write_csv, "WRITE_SIZE", "k_copy")
-    for short in kernels:
-        fetch = one(fetch_csv, "FETCH_SIZE", f"k_{short}")
-        write = one(write_csv, "WRITE_SIZE", f"k_{short}")
+    for entry in kernels:  # "name" (kernel k_name) or "name=pattern" (kernel k_pattern)
+        short, _, pat = entry.partition("=")
+        fetch = one(fetch_csv, "FETCH_SIZE", f"k_{pat or short}")
+        write = one(write_csv, "WRITE_SIZE", f"k_{pat or short}")
         out = {"kernel": short, "source_sha256": kernel_source_hash(),
                "fetch_kib_per_dispatch_raw": fetch, "write_kib_per_dispatch_raw": write,
                "fetch_scale": f_scale, "write_scale": w_scale,
@@ -658,7 +659,8 @@ def main() -> int:
         ap.add_argument("--copy-fetch", required=True)
         ap.add_argument("--copy-write", required=True)
         ap.add_argument("--copy-mib", type=int, default=1024)
-        ap.add_argument("--kernels", default="gateup_s1,down_s1")
+        ap.add_argument("--kernels", default="gateup_s1,down_s1",
+                        help="comma-separated bench kernel names, each optionally =<kernel-name pattern>")
         ap.add_argument("--weight-format", default="q4g32", choices=list(FORMATS))
         a = ap.parse_args()
         summarize_pmc(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib, a.kernels.split(","),
