@@ -56,11 +56,15 @@ constexpr int kWN = kWaves / kWM;     // column parts of a tile (wave w: part w 
 constexpr int kMB = kMT / 16 / kWM;   // MFMA row blocks (16 rows) per wave
 constexpr int kNB = kNT / 16 / kWN;   // MFMA column blocks (16 columns) per wave
 constexpr int kKG = 2;                // quantisation groups (K = 32 each) per pipeline stage
-constexpr int kBStride = 80;          // bytes per column of an LDS B group (64 + 16 padding: no bank conflicts)
-// The second group of a stage starts 64 bytes past the first group's end: the
-// two threads of a column store their groups in the same instruction, and
-// without the skew their stores met in the same LDS banks (measured: the LDS
-// bank-conflict cycles of the gate/up GEMM fell by a quarter with it).
+constexpr int kBStride = 80;          // bytes per column of an LDS B group (64 + 16 padding, see below)
+// The 16 bytes of padding put the 16-byte fragment reads of eight consecutive
+// columns on distinct banks, and the second group of a stage starts 64 bytes
+// past the first group's end: the two threads of a column store their groups in
+// the same instruction, and without the skew their stores met in the same LDS
+// banks (measured: the gate/up GEMM's bank-conflict cycles fell by a quarter).
+// The hardware still counts conflict cycles for these 128-bit accesses (about
+// four per fragment read, as many in a kernel that only reads fragments): they
+// come from how it groups the lanes of wide accesses, not from this layout.
 constexpr int kBGroup = kNT * kBStride + 64;
 constexpr int kBStage = kKG * kBGroup;
 constexpr int kBParts = kThreads / kNT;  // threads that dequantise one column of a group (8 bytes each)
@@ -164,31 +168,29 @@ struct GemmAcc {
 
 // One quantisation group's MFMAs for the first MBV row blocks of this wave:
 // A[mb] holds the group's activations of row block mb, sb the group's
-// dequantised B columns of this wave.  B fragments are read from LDS four at a
-// time, one chunk ahead of the MFMAs that use them (a compiler fence between the
-// chunks keeps the reads from all being hoisted, which would exhaust registers).
+// dequantised B columns of this wave.  Each B fragment is read from LDS
+// kFragAhead column blocks before its MFMAs; the scheduling groups pin that
+// order (left to itself the compiler reads each fragment right before its MFMAs,
+// two at a time, and the wave waits out the LDS latency at every column block).
+constexpr int kFragAhead = 4;
 template <int MBV>
 __device__ inline void group_mfma(GemmAcc &C, const bf16x8 (&A)[kMB], const uint8_t *sb, int lane, int oct) {
   auto frag = [&](int n) {
     return __builtin_bit_cast(bf16x8, *(const uint4 *)(sb + (n * 16 + (lane & 15)) * kBStride + oct * 16));
   };
-  bf16x8 B[2][4];
+  constexpr int P = kFragAhead;
+  bf16x8 B[kNB];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) B[0][q] = frag(q);
+  for (int n = 0; n < P; ++n) B[n] = frag(n);
+  __builtin_amdgcn_sched_group_barrier(0x100, P, 0);  // DS reads
 #pragma unroll
-  for (int n4 = 0; n4 < kNB; n4 += 4) {
-    const int cur = (n4 / 4) & 1;
-    // the next four fragments are requested before this chunk's MFMAs
-    if (n4 + 4 < kNB) {
+  for (int n = 0; n < kNB; ++n) {
+    if (n + P < kNB) B[n + P] = frag(n + P);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) B[cur ^ 1][q] = frag(n4 + 4 + q);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int mb = 0; mb < MBV; ++mb)
-        C.acc[mb][n4 + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb], B[cur][q], C.acc[mb][n4 + q], 0, 0, 0);
-    asm volatile("" ::: "memory");
+    for (int mb = 0; mb < MBV; ++mb)
+      C.acc[mb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb], B[n], C.acc[mb][n], 0, 0, 0);
+    if (n + P < kNB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MBV, 0);  // MFMAs
   }
 }
 

@@ -463,6 +463,46 @@ def test_matrix_core_path(tiny, mid, case):
     assert not np.array_equal(ym, ye)
 
 
+# Tokens per expert chosen so that the matrix-core tiles take every height that
+# changes which waves multiply (1 to 16 row blocks of 16, partial last blocks),
+# a full 256-row tile and experts of two tiles, beside GEMV-item experts.
+TILE_COUNTS = [8, 9, 16, 17, 24, 31, 32, 33, 48, 63, 64, 65, 80, 100, 127, 128, 129, 143, 200, 255, 256, 257, 300,
+               400]
+
+
+def crafted_routing(counts, n_experts: int, k: int, S: int, seed: int):
+    """idx (S x k) in which expert e is chosen by counts[e] tokens: expert e takes
+    the next counts[e] places of the (slot, token) order, so its tokens are
+    distinct whenever counts[e] <= S; weights uniform in [0.5, 1.5) / k."""
+    assert sum(counts) == S * k and max(counts) <= S and len(counts) <= n_experts
+    place = np.concatenate([np.full(n, e, np.int32) for e, n in enumerate(counts)])
+    idx = place.reshape(k, S).T.copy()
+    assert all(len(set(r)) == k for r in idx.tolist())
+    rng = np.random.default_rng(seed)
+    return idx, (rng.random((S, k)) + 0.5).astype(np.float32) / k
+
+
+def test_matrix_core_every_tile_height(mid):
+    """Crafted routing at the mid shape: experts with 8 to 400 tokens (tiles of
+    every height, partial blocks, one and two tiles per expert), the rest on the
+    GEMV path; all 800 tokens within the bf16 bar of the oracle."""
+    c = mid.c
+    k, S = c.top_k, 800
+    counts = list(TILE_COUNTS)
+    rest = S * k - sum(counts)
+    small = [7, 5, 3, 1, 6, 4, 2, 7]
+    counts += small
+    counts[-1] += rest - sum(small)  # one more expert of two tiles
+    assert counts[-1] <= S and len(counts) == c.n_experts, (counts[-1], len(counts))
+    idx, wt = crafted_routing(counts, c.n_experts, k, S, seed=5)
+    w = mid.w.with_(tokens=S)
+    x = gen.tokens(w, step=77)
+    xt, dt = x_device(w, x)
+    y = mid.ffn(xt, dt, dev(idx), dev(wt), mfma_min_tokens=8).cpu().numpy()
+    say(f"tokens per expert: {sorted(np.bincount(idx.ravel(), minlength=c.n_experts).tolist())}")
+    check_ffn(mid, x, idx, wt, y, np.arange(S), TOL_BF16)
+
+
 def test_matrix_core_unresident_slot_poisons_only_its_tokens(mid):
     S, thr = 67, 4
     w = mid.w.with_(tokens=S)
