@@ -36,72 +36,78 @@ __global__ __launch_bounds__(256) void k_route_select(RouteArgs a) {
 // Many tokens: the logits GEMM in fp64 on the matrix cores
 // (v_mfma_f64_16x16x4f64: products of fp32 inputs are exact in fp64, sums in
 // fp64), one workgroup per 32 tokens x 32 experts (two workgroups per CU).  K
-// advances in chunks of 32 staged in LDS as fp32 (bf16 and fp32 inputs both
-// widen to fp32 exactly; rows padded to 34 floats so that the fragment reads
-// are free of bank conflicts), double-buffered with one barrier per chunk;
-// wave w owns the 16 x 16 block (tokens 16 (w % 2), experts 16 (w / 2)).  Fragment layouts (checked on
-// the GPU): A lane l = (row l%16, k l/16), B lane l = (k l/16, column l%16),
-// D lane l value i = (row l/16 + 4i, column l%16).
+// advances in chunks of 64 staged in LDS as fp32 (bf16 and fp32 inputs both
+// widen to fp32 exactly; rows padded to 68 floats so that the fragment reads
+// are free of bank conflicts), double-buffered with one barrier per chunk and
+// requested two chunks ahead; an H that is an odd multiple of 32 ends with a
+// half chunk padded with zeros.  Wave w owns the 16 x 16 block (tokens 16 (w %
+// 2), experts 16 (w / 2)) and accumulates it in two chains (k = 0..3 and 4..7
+// of every 8), added at the end, so that consecutive MFMAs do not wait for each
+// other's results.  Fragment layouts (checked on the GPU): A lane l = (row l%16,
+// k l/16), B lane l = (k l/16, column l%16), D lane l value i = (row l/16 + 4i,
+// column l%16).
 typedef double f64x4 __attribute__((ext_vector_type(4)));
-constexpr int kLT = 32, kLE = 32, kLK = 32, kLPad = 34;
+constexpr int kLT = 32, kLE = 32, kLK = 64, kLPad = 68;
 __global__ __launch_bounds__(256) void k_route_logits_tiled(RouteArgs a) {
   __shared__ __align__(16) float xs[2][kLT][kLPad];
   __shared__ __align__(16) float wsm[2][kLE][kLPad];
   const int t0 = blockIdx.x * kLT, e0 = blockIdx.y * kLE;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int xr = tid >> 3, xc = (tid & 7) * 4;  // loader: x row, 4 columns
-  const int wr = tid >> 3, wc = (tid & 7) * 4;  // loader: W row, 4 columns
+  const int xr = tid >> 3, xc = (tid & 7) * 8;  // loader: x row, 8 columns
+  const int wr = tid >> 3, wc = (tid & 7) * 8;  // loader: W row, 8 columns
   const size_t xrow = (size_t)min(t0 + xr, a.S - 1) * a.H;  // rows past S / E are clamped, not stored
   const float *wrow = a.W + (size_t)min(e0 + wr, a.E - 1) * a.H;
-  auto load_x = [&](int k0, float4 &p) {
-    if (a.x_bf16) {
-      const uint2 r = *(const uint2 *)((const uint16_t *)a.x + xrow + k0 + xc);
-      p = make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u), __uint_as_float(r.y << 16),
-                      __uint_as_float(r.y & 0xFFFF0000u));
-    } else {
-      p = *(const float4 *)((const float *)a.x + xrow + k0 + xc);
+  struct Ld { float4 x0, x1, w0, w1; };
+  auto load = [&](int k0, Ld &p) {
+    if (k0 + xc >= a.H) {  // the last chunk of an H that is an odd multiple of 32: zero columns
+      p.x0 = p.x1 = p.w0 = p.w1 = make_float4(0.f, 0.f, 0.f, 0.f);
+      return;
     }
+    if (a.x_bf16) {
+      const uint4 r = *(const uint4 *)((const uint16_t *)a.x + xrow + k0 + xc);
+      p.x0 = make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u), __uint_as_float(r.y << 16),
+                         __uint_as_float(r.y & 0xFFFF0000u));
+      p.x1 = make_float4(__uint_as_float(r.z << 16), __uint_as_float(r.z & 0xFFFF0000u), __uint_as_float(r.w << 16),
+                         __uint_as_float(r.w & 0xFFFF0000u));
+    } else {
+      p.x0 = *(const float4 *)((const float *)a.x + xrow + k0 + xc);
+      p.x1 = *(const float4 *)((const float *)a.x + xrow + k0 + xc + 4);
+    }
+    p.w0 = *(const float4 *)(wrow + k0 + wc);
+    p.w1 = *(const float4 *)(wrow + k0 + wc + 4);
   };
-  auto stage = [&](int b, const float4 &p, const float4 &w) {
-    float2 *xd = (float2 *)&xs[b][xr][xc];
-    xd[0] = make_float2(p.x, p.y);
-    xd[1] = make_float2(p.z, p.w);
-    float2 *wd = (float2 *)&wsm[b][wr][wc];
-    wd[0] = make_float2(w.x, w.y);
-    wd[1] = make_float2(w.z, w.w);
+  auto stage = [&](int b, const Ld &p) {
+    *(float4 *)&xs[b][xr][xc] = p.x0;
+    *(float4 *)&xs[b][xr][xc + 4] = p.x1;
+    *(float4 *)&wsm[b][wr][wc] = p.w0;
+    *(float4 *)&wsm[b][wr][wc + 4] = p.w1;
   };
-  // chunks are requested kPf chunks before they are staged (a chunk's MFMAs take
-  // well under one global-load latency)
-  constexpr int kPf = 3;
-  const int nk = a.H / kLK;
-  float4 px[kPf], pw[kPf];
+  constexpr int kPf = 2;
+  const int nk = (a.H + kLK - 1) / kLK;
+  Ld pl[kPf];
 #pragma unroll
-  for (int d = 0; d < kPf; ++d) {
-    const int k0 = min(d, nk - 1) * kLK;
-    load_x(k0, px[d]);
-    pw[d] = *(const float4 *)(wrow + k0 + wc);
-  }
-  stage(0, px[0], pw[0]);
+  for (int d = 0; d < kPf; ++d) load(min(d, nk - 1) * kLK, pl[d]);
+  stage(0, pl[0]);
   __syncthreads();
-  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0}, acc2 = {0.0, 0.0, 0.0, 0.0};
   const int tb = (wave & 1) * 16, eb = (wave >> 1) * 16, kq = lane >> 4;
   for (int kc0 = 0; kc0 < nk; kc0 += kPf) {
 #pragma unroll
     for (int d = 0; d < kPf; ++d) {
       const int kc = kc0 + d;
       if (kc < nk) {  // uniform
-        // the slot of chunk kc was staged; it now receives chunk kc + kPf (the last one repeats)
-        const int kn = min(kc + kPf, nk - 1) * kLK;
-        load_x(kn, px[d]);
-        pw[d] = *(const float4 *)(wrow + kn + wc);
+        load(min(kc + kPf, nk - 1) * kLK, pl[d]);
         const int b = kc & 1;
 #pragma unroll
-        for (int kk = 0; kk < kLK; kk += 4) {
+        for (int kk = 0; kk < kLK; kk += 8) {
           const double av = (double)xs[b][tb + (lane & 15)][kk + kq];
           const double bv = (double)wsm[b][eb + (lane & 15)][kk + kq];
           acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+          const double av2 = (double)xs[b][tb + (lane & 15)][kk + 4 + kq];
+          const double bv2 = (double)wsm[b][eb + (lane & 15)][kk + 4 + kq];
+          acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64(av2, bv2, acc2, 0, 0, 0);
         }
-        stage(b ^ 1, px[(d + 1) % kPf], pw[(d + 1) % kPf]);
+        stage(b ^ 1, pl[(d + 1) % kPf]);
         __syncthreads();
       }
     }
@@ -109,7 +115,7 @@ __global__ __launch_bounds__(256) void k_route_logits_tiled(RouteArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = t0 + tb + (lane >> 4) + 4 * i, e = e0 + eb + (lane & 15);
-    if (t < a.S && e < a.E) a.logits[(size_t)t * a.E + e] = acc[i];
+    if (t < a.S && e < a.E) a.logits[(size_t)t * a.E + e] = acc[i] + acc2[i];
   }
 }
 
