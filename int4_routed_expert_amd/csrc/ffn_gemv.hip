@@ -788,20 +788,42 @@ __global__ __launch_bounds__(256) void k_bucket(FfnArgs a) {
 // Work items {expert, first list position, n tokens}: routed experts in id order,
 // then the shared expert (id E) over all tokens.  An expert with at least
 // mfma_thr tokens (mfma_thr > 0) gets matrix-core tiles of up to
-// kMfmaTileTokens rows instead, in the same order.
+// kMfmaTileTokens rows instead.  The tile list is ordered for the GEMMs' block
+// scheduling, longest first: every full tile (the shared expert's, then the
+// routed experts' in id order), then the experts' last, partial tiles by
+// decreasing rows (ties in no fixed order: the order changes which workgroup
+// computes a tile, never a result), so that the last workgroups to start are
+// the short ones.
 __global__ __launch_bounds__(1024) void k_schedule(FfnArgs a) {
+  constexpr int MT = kMfmaTileTokens;
   __shared__ int pre[kMaxE + 1], pmt[kMaxE + 1];
+  __shared__ int cur[MT];  // partial tiles per row count, then the next position of each
+  __shared__ int s_np;     // routed experts with a partial tile
   const int tid = threadIdx.x, E = a.E;
   const int thr = a.mfma_thr;
   auto is_mfma = [&](int c) { return thr > 0 && c >= thr; };
+  const bool sh_mfma = a.Is > 0 && is_mfma(a.S);
+  const int sh_full = sh_mfma ? a.S / MT : 0, sh_part = sh_mfma ? a.S % MT : 0;
+  for (int r = tid; r < MT; r += blockDim.x) cur[r] = 0;
+  if (tid == 0) s_np = 0;
   for (int e = tid; e < E; e += blockDim.x) {
     const int c = a.counts[e];
     pre[e] = is_mfma(c) ? 0 : (c + kTB - 1) / kTB;
-    pmt[e] = is_mfma(c) ? (c + kMfmaTileTokens - 1) / kMfmaTileTokens : 0;
+    pmt[e] = is_mfma(c) ? c / MT : 0;  // full tiles
   }
   __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) {
+    const int c = a.counts[e];
+    if (is_mfma(c) && c % MT) {
+      atomicAdd(&cur[c % MT], 1);
+      atomicAdd(&s_np, 1);
+    }
+  }
+  if (tid == 0 && sh_part) atomicAdd(&cur[sh_part], 1);
+  __syncthreads();
   if (tid == 0) {
-    int s = 0, m = 0;
+    int s = 0, m = sh_full;
+    const int np = s_np;
     for (int e = 0; e < E; ++e) {
       const int c = pre[e], d = pmt[e];
       pre[e] = s;
@@ -810,15 +832,47 @@ __global__ __launch_bounds__(1024) void k_schedule(FfnArgs a) {
       m += d;
     }
     pre[E] = s;
-    pmt[E] = m;
+    pmt[E] = m + np;  // routed tiles end here (their full tiles, then the partial tiles of every expert)
+    a.n_items[2] = m - sh_full + np;    // routed tiles
+    a.n_items[3] = sh_full + (sh_part ? 1 : 0);  // shared tiles
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // partial tiles start after every full tile (pmt[E] - np of them), by decreasing rows: lane l owns
+    // the row counts MT - 1 - 4 l .. MT - 4 - 4 l; a wave scan gives each lane its first position
+    static_assert(MT == 256, "four row counts per lane");
+    int n[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = MT - 1 - 4 * tid - j;
+      n[j] = r > 0 ? cur[r] : 0;
+      sum += n[j];
+    }
+    int inc = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(inc, o);
+      if (tid >= o) inc += u;
+    }
+    int q = pmt[E] - s_np + inc - sum;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = MT - 1 - 4 * tid - j;
+      if (r > 0) cur[r] = q;
+      q += n[j];
+    }
   }
   __syncthreads();
   for (int e = tid; e < E; e += blockDim.x) {
     const int c = a.counts[e];
     if (is_mfma(c)) {
-      for (int s = 0; s * kMfmaTileTokens < c; ++s) {
+      for (int s = 0; s < c / MT; ++s) {
         int *mt = a.mtiles + 3 * (size_t)(pmt[e] + s);
-        mt[0] = e; mt[1] = s * kMfmaTileTokens; mt[2] = min(kMfmaTileTokens, c - s * kMfmaTileTokens);
+        mt[0] = e; mt[1] = s * MT; mt[2] = MT;
+      }
+      if (c % MT) {
+        int *mt = a.mtiles + 3 * (size_t)atomicAdd(&cur[c % MT], 1);
+        mt[0] = e; mt[1] = c - c % MT; mt[2] = c % MT;
       }
     } else {
       for (int s = 0; s * kTB < c; ++s) {
@@ -827,23 +881,23 @@ __global__ __launch_bounds__(1024) void k_schedule(FfnArgs a) {
       }
     }
   }
-  const int nr = pre[E], mr = pmt[E];
-  const bool sh_mfma = a.Is > 0 && is_mfma(a.S);
+  const int nr = pre[E];
   const int nsh = a.Is > 0 && !sh_mfma ? (a.S + kTB - 1) / kTB : 0;
-  const int msh = sh_mfma ? (a.S + kMfmaTileTokens - 1) / kMfmaTileTokens : 0;
   for (int s = tid; s < nsh; s += blockDim.x) {
     int *it = a.items + 3 * (size_t)(nr + s);
     it[0] = E; it[1] = s * kTB; it[2] = min(kTB, a.S - s * kTB);
   }
-  for (int s = tid; s < msh; s += blockDim.x) {
-    int *mt = a.mtiles + 3 * (size_t)(mr + s);
-    mt[0] = E; mt[1] = s * kMfmaTileTokens; mt[2] = min(kMfmaTileTokens, a.S - s * kMfmaTileTokens);
+  for (int s = tid; s < sh_full; s += blockDim.x) {
+    int *mt = a.mtiles + 3 * (size_t)s;
+    mt[0] = E; mt[1] = s * MT; mt[2] = MT;
   }
   if (tid == 0) {
+    if (sh_part) {
+      int *mt = a.mtiles + 3 * (size_t)atomicAdd(&cur[sh_part], 1);
+      mt[0] = E; mt[1] = a.S - sh_part; mt[2] = sh_part;
+    }
     a.n_items[0] = nr;
     a.n_items[1] = nsh;
-    a.n_items[2] = mr;
-    a.n_items[3] = msh;
   }
 }
 
