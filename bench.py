@@ -442,7 +442,13 @@ def bench_prefill(args) -> int:
     slope = float(np.polyfit(np.log(np.arange(1, srt.size + 1)), np.log(srt), 1)[0])
     gu_key = "gateup_mfma"
     gu_achieved = gu_flop / (kernels[gu_key] * 1e-6) / 1e12 if gu_key in kernels else None
-    peak = 5000.0 if args.act_int8 else BF16_PEAK_TFLOPS
+    # int8 activations run integer tiles with row-scaled weights; with fp16 group
+    # scales they run bf16 tiles over the integers (one exact group dot per MFMA)
+    int_tiles = bool(args.act_int8) and args.weight_format != 0
+    peak = 5000.0 if int_tiles else BF16_PEAK_TFLOPS
+    mfma_desc = ("int8 MFMA, exact int32 row sums" if int_tiles else
+                 "bf16 MFMA over the int8 x int4 integers, exact per-group dots scaled in fp32" if args.act_int8 else
+                 "bf16 MFMA, fp32 accumulation")
     log(f"prefill: {el * 1e3:.3f} ms per call, {used} experts used, kernels (us) {kernels}")
     cpu = None
     if not args.no_cpu_baseline:
@@ -458,7 +464,7 @@ def bench_prefill(args) -> int:
           "config": {"workload": "glm52_moe_layer_prefill_S2048", "tokens_per_call": S, "x": "bf16",
                      "quant": FORMAT_DESC[args.weight_format] + (", int8 activations" if args.act_int8 else ""),
                      "bias": w.bias_recipe, "batches_rotated": nb, "mfma_min_tokens": args.mfma_min_tokens,
-                     "matrix_cores": "int8 MFMA" if args.act_int8 else "bf16 MFMA, fp32 accumulation",
+                     "matrix_cores": mfma_desc,
                      "gemv_path": "exact int4 group dots, fp32 accumulation"},
           "experts_used": used, "effective_gbps": bytes_call / el / 1e9,
           "pct_hbm_peak": 100.0 * bytes_call / el / 1e9 / HBM_PEAK_GBPS,

@@ -100,7 +100,9 @@ typedef struct moe_cfg {
    * kernels").  Each token's x and each
    * (token, expert) hidden row h (in fp32) is replaced by q * d with
    * d = fp32(max|v| / 127) and q = rint(fp32(v / d)) in [-127, 127] (a row with a
-   * NaN gets d = NaN); the dot products of q with the weights are exact integers.
+   * NaN gets d = NaN); the dot products of q with the weights are exact integers
+   * on every path: per group (then scaled in fp32) with fp16 group scales, per
+   * row with row scales, on the GEMV items and on the matrix cores alike.
    * 0: the exact contract (no activation quantisation). */
   int32_t act_int8;
 } moe_cfg;

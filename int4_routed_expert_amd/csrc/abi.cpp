@@ -446,9 +446,7 @@ static int ffn_args(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t S,
     a.mtiles = (int32_t *)(b + L.mtiles);
     a.xb = (uint16_t *)(b + L.xb);
     a.max_mtiles = L.max_mtiles;
-    // int8 activations reach the (integer) matrix cores only with row-scaled
-    // weights; with fp16 group scales every expert runs on the GEMV items
-    a.mfma_thr = (c->act_int8 && c->weight_format == MOE_WF_Q4_G32) ? 0 : c->mfma_min_tokens;
+    a.mfma_thr = c->mfma_min_tokens;
   }
   return MOE_OK;
 }

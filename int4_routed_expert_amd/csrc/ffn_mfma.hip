@@ -109,18 +109,21 @@ __device__ inline uint4 dequant8_i8(uint32_t w0, uint32_t w1, float s) {
   return make_uint4(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7]));
 }
 
-// Eight consecutive activations, raw: bf16 bits, or fp32 values that become
-// bf16 (RNE) only where they are used, so that a prefetch does not wait.
-template <bool ABF>
+// Eight consecutive activations, raw: bf16 bits (kActBf16), fp32 values that
+// become bf16 (RNE) only where they are used, so that a prefetch does not wait
+// (kActF32), or the int8 integers of a quantised row (kActI8: exact in bf16,
+// the row's scale is applied to the accumulators).
+constexpr int kActF32 = 0, kActBf16 = 1, kActI8 = 2;
+template <int AK>
 struct ARaw;
 template <>
-struct ARaw<true> {
+struct ARaw<kActBf16> {
   uint4 v;
   __device__ inline void load(const void *base, size_t off) { v = ldg<uint4>((const uint16_t *)base + off); }
   __device__ inline bf16x8 get() const { return __builtin_bit_cast(bf16x8, v); }
 };
 template <>
-struct ARaw<false> {
+struct ARaw<kActF32> {
   float4 p, q;
   __device__ inline void load(const void *base, size_t off) {
     p = ldg<float4>((const float *)base + off);
@@ -129,6 +132,18 @@ struct ARaw<false> {
   __device__ inline bf16x8 get() const {
     return __builtin_bit_cast(
         bf16x8, make_uint4(pack_bf16(p.x, p.y), pack_bf16(p.z, p.w), pack_bf16(q.x, q.y), pack_bf16(q.z, q.w)));
+  }
+};
+template <>
+struct ARaw<kActI8> {
+  uint2 v;
+  __device__ inline void load(const void *base, size_t off) { v = ldg<uint2>((const int8_t *)base + off); }
+  __device__ inline bf16x8 get() const {
+    float f[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = (float)(int8_t)((j < 4 ? v.x : v.y) >> (8 * (j & 3)));
+    return __builtin_bit_cast(
+        bf16x8, make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7])));
   }
 };
 
@@ -194,9 +209,60 @@ __device__ inline void group_mfma(GemmAcc &C, const bf16x8 (&A)[kMB], const uint
   }
 }
 
-template <bool ABF, int kDepth, int MBV, int WF>
+// Int8 activations with grouped weight scales: A and B both hold integers
+// (|x| <= 127, |q| <= 8, exact in bf16), so one MFMA gives a group's integer dot
+// exactly in fp32 (|sum| <= 32 * 127 * 8 < 2^24); it starts from zero, and its
+// result times the group's scale is added to the accumulator, column by column
+// (one scale per lane and column block).  The scales of the wave's columns come
+// from LDS, column n*16 + c of the group at c * kScStride + n.  A block's scaling
+// runs kGsLag column blocks behind its MFMAs, so that it does not wait for them.
+constexpr int kScStride = 20;  // floats per column residue (16 blocks + 4 padding)
+constexpr int kGsLag = 2;
+constexpr bool group_scaled(int AK, int WF) { return AK == kActI8 && WF == kWfQ4G32; }
+static_assert(kNT / 16 <= kScStride && kScStride % 4 == 0, "scale layout");
+template <int MBV>
+__device__ inline void group_mfma_gs(GemmAcc &C, const bf16x8 (&A)[kMB], const uint8_t *sb, const float *ssc,
+                                     int lane, int oct) {
+  auto frag = [&](int n) {
+    return __builtin_bit_cast(bf16x8, *(const uint4 *)(sb + (n * 16 + (lane & 15)) * kBStride + oct * 16));
+  };
+  constexpr int P = kFragAhead, D = kGsLag;
+  float sc[kNB];
+#pragma unroll
+  for (int n4 = 0; n4 < kNB; n4 += 4) {
+    const float4 v = *(const float4 *)(ssc + n4);
+    sc[n4] = v.x, sc[n4 + 1] = v.y, sc[n4 + 2] = v.z, sc[n4 + 3] = v.w;
+  }
+  bf16x8 B[kNB];
+  f32x4 T[kMB][kNB];
+#pragma unroll
+  for (int n = 0; n < P; ++n) B[n] = frag(n);
+  __builtin_amdgcn_sched_group_barrier(0x100, P + kNB / 4, 0);  // DS reads
+#pragma unroll
+  for (int n = 0; n < kNB + D; ++n) {
+    if (n < kNB) {
+      if (n + P < kNB) B[n + P] = frag(n + P);
+#pragma unroll
+      for (int mb = 0; mb < MBV; ++mb)
+        T[mb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb], B[n], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    }
+    if (n >= D) {
+#pragma unroll
+      for (int mb = 0; mb < MBV; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) C.acc[mb][n - D][i] = fmaf(T[mb][n - D][i], sc[n - D], C.acc[mb][n - D][i]);
+    }
+    if (n + P < kNB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (n < kNB) __builtin_amdgcn_sched_group_barrier(0x008, MBV, 0);  // MFMAs
+    if (n >= D) __builtin_amdgcn_sched_group_barrier(0x002, 4 * MBV, 0);  // scaling
+  }
+}
+
+template <int AK, int kDepth, int MBV, int WF>
 __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_colp, const uint8_t *const *s_sclp,
-                                 uint8_t *s_b, const void *abase, const size_t *arow, int wn, int lane) {
+                                 uint8_t *s_b, float *s_gsc, const void *abase, const size_t *arow, int wn,
+                                 int lane) {
+  constexpr bool kGS = group_scaled(AK, WF);
   const int tid = threadIdx.x;
   // this thread dequantises group kKG s + bp of B column bc: the two lanes of a
   // column read its 32 contiguous nibble bytes of the stage together
@@ -230,7 +296,11 @@ __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_col
       *(uint4 *)(d + 32) = dequant8_i8(r.w.q[1].x, r.w.q[1].y, row_sc);
       *(uint4 *)(d + 48) = dequant8_i8(r.w.q[1].z, r.w.q[1].w, row_sc);
     } else {
-      const float sc = WF == kWfQ4G32 ? half_bits_to_float(r.sc) : row_sc;
+      float sc = WF == kWfQ4G32 ? half_bits_to_float(r.sc) : row_sc;
+      if constexpr (kGS) {  // integers in LDS, the scale beside them (column bc = 16 (bc / 16) + bc % 16)
+        s_gsc[((buf * kKG + bp) * 16 + (bc & 15)) * kScStride + (bc >> 4)] = sc;
+        sc = 1.0f;
+      }
       *(uint4 *)(d) = dequant8(r.w.q[0].x, sc);
       *(uint4 *)(d + 16) = dequant8(r.w.q[0].y, sc);
       *(uint4 *)(d + 32) = dequant8(r.w.q[0].z, sc);
@@ -238,7 +308,7 @@ __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_col
     }
   };
   // activations of group gi of stage st (clamped to the last group)
-  auto load_a = [&](int st, int gi, ARaw<ABF> (&r)[kMB]) {
+  auto load_a = [&](int st, int gi, ARaw<AK> (&r)[kMB]) {
     const int g = min(st * kKG + gi, ng - 1);
 #pragma unroll
     for (int mb = 0; mb < MBV; ++mb) r[mb].load(abase, arow[mb] + (size_t)g * 32 + oct * 8);
@@ -249,7 +319,7 @@ __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_col
   // its MFMAs).  Loads are clamped to the last group, so every one is
   // unconditional; the MFMAs of groups past the last one (an odd group count,
   // padding to a multiple of kDepth stages) are skipped.
-  ARaw<ABF> aq[kKG][kMB];
+  ARaw<AK> aq[kKG][kMB];
   BRaw bq[kDepth];
 #pragma unroll
   for (int gi = 0; gi < kKG; ++gi) load_a(0, gi, aq[gi]);
@@ -271,7 +341,13 @@ __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_col
         for (int mb = 0; mb < MBV; ++mb) A[mb] = aq[gi][mb].get();
         // rows past the tile's end repeat its last row (not stored); groups past
         // the last one (a wave-uniform condition) are skipped
-        if (MBV > 0 && s * kKG + gi < ng) group_mfma<MBV>(C, A, sb + gi * kBGroup, lane, oct);
+        if (MBV > 0 && s * kKG + gi < ng) {
+          if constexpr (kGS)
+            group_mfma_gs<MBV>(C, A, sb + gi * kBGroup,
+                               s_gsc + (((s & 1) * kKG + gi) * 16 + (lane & 15)) * kScStride + wn * kNB, lane, oct);
+          else
+            group_mfma<MBV>(C, A, sb + gi * kBGroup, lane, oct);
+        }
         load_a(s + 1, gi, aq[gi]);  // after the MFMAs: the slot's registers are free again
       }
       store_b((s + 1) & 1, bq[(d + 1) % kDepth]);
@@ -286,18 +362,18 @@ __device__ inline void gemm_loop(GemmAcc &C, int ng, const uint8_t *const *s_col
 // multiplies only its valid blocks (MBV), every wave dequantises its share of B.
 __device__ inline int row_of(int wave, int mb, int r16) { return (wave % kWM + kWM * mb) * 16 + r16; }
 
-template <bool ABF, int kDepth, int WF>
+template <int AK, int kDepth, int WF>
 __device__ inline void gemm_rows(GemmAcc &C, int rows, int ng, const uint8_t *const *s_colp,
-                                 const uint8_t *const *s_sclp, uint8_t *s_b, const void *abase, const size_t *arow,
-                                 int wave, int lane) {
+                                 const uint8_t *const *s_sclp, uint8_t *s_b, float *s_gsc, const void *abase,
+                                 const size_t *arow, int wave, int lane) {
   const int nblk = (rows + 15) / 16, band = wave % kWM, wn = wave / kWM;
   const int mbv = min(kMB, max(0, (nblk - band + kWM - 1) / kWM));  // valid blocks band, band + kWM, ...
   switch (mbv) {
-    case 4: if constexpr (kMB >= 4) gemm_loop<ABF, kDepth, 4, WF>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
-    case 3: if constexpr (kMB >= 3) gemm_loop<ABF, kDepth, 3, WF>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
-    case 2: gemm_loop<ABF, kDepth, 2, WF>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
-    case 1: gemm_loop<ABF, kDepth, 1, WF>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
-    default: gemm_loop<ABF, kDepth, 0, WF>(C, ng, s_colp, s_sclp, s_b, abase, arow, wn, lane); break;
+    case 4: if constexpr (kMB >= 4) gemm_loop<AK, kDepth, 4, WF>(C, ng, s_colp, s_sclp, s_b, s_gsc, abase, arow, wn, lane); break;
+    case 3: if constexpr (kMB >= 3) gemm_loop<AK, kDepth, 3, WF>(C, ng, s_colp, s_sclp, s_b, s_gsc, abase, arow, wn, lane); break;
+    case 2: gemm_loop<AK, kDepth, 2, WF>(C, ng, s_colp, s_sclp, s_b, s_gsc, abase, arow, wn, lane); break;
+    case 1: gemm_loop<AK, kDepth, 1, WF>(C, ng, s_colp, s_sclp, s_b, s_gsc, abase, arow, wn, lane); break;
+    default: gemm_loop<AK, kDepth, 0, WF>(C, ng, s_colp, s_sclp, s_b, s_gsc, abase, arow, wn, lane); break;
   }
 }
 
@@ -316,9 +392,13 @@ inline unsigned tile_blocks(int max_mtiles, int n_tiles) {
 }
 
 // Gate/up for one (M tile, N tile of kNT/2 features): h[pair][feature] = silu(g) * u.
-template <int WF>
+// AK = kActI8 (int8 activations with grouped weight scales): A is the tokens'
+// quantised integers, g and u are scaled by the token's d, and h is stored in
+// fp32 for the per-row quantisation of the down projection's input.
+template <int WF, int AK = kActBf16>
 __global__ __launch_bounds__(kThreads) void k_gu_mfma(FfnArgs a) {
   __shared__ __align__(16) uint8_t s_b[2 * kBStage];
+  __shared__ __align__(16) float s_gsc[group_scaled(AK, WF) ? 2 * kKG * 16 * kScStride : 4];
   __shared__ const uint8_t *s_colp[kNT];
   __shared__ const uint8_t *s_sclp[kNT];
   __shared__ int s_tok[kMT], s_pair[kMT];
@@ -350,8 +430,8 @@ __global__ __launch_bounds__(kThreads) void k_gu_mfma(FfnArgs a) {
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb) arow[mb] = (size_t)s_tok[row_of(wave, mb, lane & 15)] * a.H;
   GemmAcc C;
-  gemm_rows<true, 3, WF>(C, mt.n, a.H / kGroup, s_colp, s_sclp, s_b, a.x_bf16 ? a.x : (const void *)a.xb, arow, wave,
-                     lane);
+  gemm_rows<AK, 3, WF>(C, mt.n, a.H / kGroup, s_colp, s_sclp, s_b, s_gsc,
+                       AK == kActI8 ? (const void *)a.xq : a.x_bf16 ? a.x : (const void *)a.xb, arow, wave, lane);
   // epilogue: even columns are gate, the next lane holds the matching up
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb)
@@ -359,23 +439,29 @@ __global__ __launch_bounds__(kThreads) void k_gu_mfma(FfnArgs a) {
     for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float gv = C.acc[mb][nb][i];
-        const float uv = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(gv), 0xB1, 0xF, 0xF, false));
         const int j = row_of(wave, mb, (lane >> 4) * 4 + i);
+        const float gv = AK == kActI8 ? C.acc[mb][nb][i] * ldg<float>(a.dx + s_tok[min(j, mt.n - 1)]) : C.acc[mb][nb][i];
+        const float uv = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(gv), 0xB1, 0xF, 0xF, false));
         const int c = wn * 16 * kNB + nb * 16 + (lane & 15);
         const int f = nt * (kNT / 2) + (c / 8) * kGuPairs + (c % 8) / 2;
         if ((c & 1) == 0 && j < mt.n && f < inter) {
           const float hv = gv / (1.0f + expf(-gv)) * uv;
-          // bf16 in the first half of the row's fp32 storage: the down GEMM's A operand
-          ((__bf16 *)a.h)[(size_t)s_pair[j] * 2 * Imax + f] = (__bf16)hv;
+          if constexpr (AK == kActI8) {
+            a.h[(size_t)s_pair[j] * Imax + f] = hv;
+          } else {
+            // bf16 in the first half of the row's fp32 storage: the down GEMM's A operand
+            ((__bf16 *)a.h)[(size_t)s_pair[j] * 2 * Imax + f] = (__bf16)hv;
+          }
         }
       }
 }
 
 // Down for one (M tile, N tile of kNT output rows): part[pair][row] = Wd h.
-template <int WF>
+// AK = kActI8: A is the quantised h rows, the results are scaled by each row's d.
+template <int WF, int AK = kActBf16>
 __global__ __launch_bounds__(kThreads) void k_dn_mfma(FfnArgs a) {
   __shared__ __align__(16) uint8_t s_b[2 * kBStage];
+  __shared__ __align__(16) float s_gsc[group_scaled(AK, WF) ? 2 * kKG * 16 * kScStride : 4];
   __shared__ const uint8_t *s_colp[kNT];
   __shared__ const uint8_t *s_sclp[kNT];
   __shared__ int s_tok[kMT], s_pair[kMT];
@@ -410,9 +496,11 @@ __global__ __launch_bounds__(kThreads) void k_dn_mfma(FfnArgs a) {
   const int wn = wave / kWM;  // column part
   size_t arow[kMB];
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) arow[mb] = (size_t)s_pair[row_of(wave, mb, lane & 15)] * 2 * Imax;
+  for (int mb = 0; mb < kMB; ++mb)
+    arow[mb] = (size_t)s_pair[row_of(wave, mb, lane & 15)] * (AK == kActI8 ? Imax : 2 * Imax);
   GemmAcc C;
-  gemm_rows<true, 2, WF>(C, mt.n, inter / kGroup, s_colp, s_sclp, s_b, a.h, arow, wave, lane);
+  gemm_rows<AK, 2, WF>(C, mt.n, inter / kGroup, s_colp, s_sclp, s_b, s_gsc, AK == kActI8 ? (const void *)a.hq : a.h, arow,
+                       wave, lane);
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
@@ -421,7 +509,9 @@ __global__ __launch_bounds__(kThreads) void k_dn_mfma(FfnArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int j = row_of(wave, mb, (lane >> 4) * 4 + i);
         const int n = n0 + wn * 16 * kNB + nb * 16 + (lane & 15);
-        if (j < mt.n && n < a.H) a.part[(size_t)s_pair[j] * a.H + n] = C.acc[mb][nb][i];
+        if (j < mt.n && n < a.H)
+          a.part[(size_t)s_pair[j] * a.H + n] =
+              AK == kActI8 ? C.acc[mb][nb][i] * ldg<float>(a.dh + s_pair[j]) : C.acc[mb][nb][i];
       }
 }
 
@@ -672,11 +762,12 @@ __global__ __launch_bounds__(256) void k_x_to_bf16(const float *x, uint16_t *xb,
 
 hipError_t launch_gu_mfma(const FfnArgs &a, hipStream_t st) {
   if (a.mfma_thr <= 0 || a.max_mtiles <= 0) return hipSuccess;
-  if (a.act_q) {  // int8 activations: row-scaled formats only (the threshold is 0 otherwise)
+  if (a.act_q) {  // int8 activations: integer tiles for row scales, bf16 tiles over the integers for group scales
     ProfScope ps("gateup_mfma", st);
     const dim3 g(tile_blocks(a.max_mtiles, (2 * std::max(a.I, a.Is) + kNT - 1) / kNT));
     if (a.wf == kWfQ8Row) MOE_LAUNCH(k_gu_mfma_i8<kWfQ8Row>, g, dim3(kThreads), 0, st, a);
-    else MOE_LAUNCH(k_gu_mfma_i8<kWfQ4Row>, g, dim3(kThreads), 0, st, a);
+    else if (a.wf == kWfQ4Row) MOE_LAUNCH(k_gu_mfma_i8<kWfQ4Row>, g, dim3(kThreads), 0, st, a);
+    else MOE_LAUNCH((k_gu_mfma<kWfQ4G32, kActI8>), g, dim3(kThreads), 0, st, a);
     return hipGetLastError();
   }
   if (!a.x_bf16) {
@@ -703,7 +794,8 @@ hipError_t launch_dn_mfma(const FfnArgs &a, hipStream_t st) {
   if (a.act_q) {
     const dim3 g(tile_blocks(a.max_mtiles, (a.H + kNT - 1) / kNT));
     if (a.wf == kWfQ8Row) MOE_LAUNCH(k_dn_mfma_i8<kWfQ8Row>, g, dim3(kThreads), 0, st, a);
-    else MOE_LAUNCH(k_dn_mfma_i8<kWfQ4Row>, g, dim3(kThreads), 0, st, a);
+    else if (a.wf == kWfQ4Row) MOE_LAUNCH(k_dn_mfma_i8<kWfQ4Row>, g, dim3(kThreads), 0, st, a);
+    else MOE_LAUNCH((k_dn_mfma<kWfQ4G32, kActI8>), g, dim3(kThreads), 0, st, a);
     return hipGetLastError();
   }
   const dim3 g(tile_blocks(a.max_mtiles, (a.H + kNT - 1) / kNT));

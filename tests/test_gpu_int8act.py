@@ -101,12 +101,13 @@ def test_glm_shape_decode_and_verify(fmt):
     check_int8act(dl, x, ridx, rw, y, np.arange(4))
 
 
-@pytest.mark.parametrize("fmt", [1, 2], ids=["q4row", "q8row"])
+@pytest.mark.parametrize("fmt", [0, 1, 2], ids=["q4g32", "q4row", "q8row"])
 @pytest.mark.parametrize("S,thr", [(37, 4), (67, 4), (300, 16)])
 def test_matrix_core_path(fmt, S, thr):
-    """Row-scaled weights with int8 activations: experts over the threshold run the
-    integer matrix-core GEMM (exact int32 sums, scaled once); the others the GEMV
-    items.  Both against the oracle's int8-activation mode."""
+    """int8 activations: experts over the threshold run the matrix cores (row-scaled
+    weights: the integer GEMM, exact int32 sums scaled once; fp16 group scales:
+    one exact integer group dot per MFMA, scaled per group in fp32), the others
+    the GEMV items.  Both against the oracle's int8-activation mode."""
     base = gen.WORKLOADS["tiny"] if S == 37 else gen.Workload("mid", MID, tokens=S, seed=11)
     dl = DeviceLayer(fmt_workload(base, fmt), host_experts=True, mfma_min_tokens=thr, act_int8=1)
     w = dl.w.with_(tokens=S)
@@ -124,7 +125,7 @@ def test_matrix_core_path(fmt, S, thr):
     assert not np.array_equal(y_mfma, y_gemv)
 
 
-@pytest.mark.parametrize("fmt", [1, 2], ids=["q4row", "q8row"])
+@pytest.mark.parametrize("fmt", [0, 1, 2], ids=["q4g32", "q4row", "q8row"])
 def test_matrix_core_odd_group_count(fmt):
     """H = 544 (17 groups: the integer GEMM's last stage has one live group and
     lanes of the other are masked), I = 96, shared 64, bf16 input."""
@@ -140,11 +141,13 @@ def test_matrix_core_odd_group_count(fmt):
     check_int8act(dl, x, ridx, rw, y, np.arange(40))
 
 
-def test_glm_shape_batch_row_scales():
-    """2048 bf16 tokens, GLM-5.2 shape, int4 with row scales, int8 activations: the
-    integer matrix-core path for the many-token experts; outputs on one token of
-    every matrix-core tile and GEMV item."""
-    w = fmt_workload(gen.WORKLOADS["decode"], 1).with_(x_dtype="bf16", tokens=2048)
+@pytest.mark.parametrize("fmt", [1, 0], ids=["q4row", "q4g32"])
+def test_glm_shape_batch(fmt):
+    """2048 bf16 tokens, GLM-5.2 shape, int8 activations: the matrix-core path for
+    the many-token experts (integer tiles for row scales, per-group scaled integer
+    group dots for fp16 group scales); outputs on one token of every matrix-core
+    tile and GEMV item."""
+    w = fmt_workload(gen.WORKLOADS["decode"], fmt).with_(x_dtype="bf16", tokens=2048)
     dl = DeviceLayer(w, act_int8=1)
     x = gen.tokens(w)
     idx, wt, y = run_gpu(dl, x)
