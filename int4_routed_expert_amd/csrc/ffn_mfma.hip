@@ -39,6 +39,12 @@
 // the first half of the row's fp32 storage) as the down GEMM's A operand.  Down: columns are output
 // rows of Wd; results go to the per-(token, rank) partials that the combine
 // sums in route order.
+//
+// int8 activations (moe_cfg.act_int8): with fp16 group scales the same tiles
+// run over integers on both sides (quantised activation bytes, weight nibbles
+// dequantised with scale 1), each group's MFMA starts from zero and its exact
+// integer dot is scaled into the accumulators (group_mfma_gs); with row scales
+// the integer kernels at the end of this file run v_mfma_i32_16x16x64_i8.
 #include "dot.h"
 
 namespace moe {
