@@ -472,7 +472,9 @@ def bench_prefill(args) -> int:
           "routing": {"zipf_slope_top64": slope, "max_tokens_per_expert": int(counts.max()),
                       "experts_without_tokens": int((counts == 0).sum()),
                       "experts_on_matrix_cores": int((counts >= thr).sum()) if thr > 0 else 0,
-                      "pairs_on_matrix_cores": mfma_rows / float(S * c.top_k)},
+                      "pairs_on_matrix_cores": mfma_rows / float(S * c.top_k),
+                      "matrix_core_m_tiles": (int(((counts[counts >= thr] + 255) // 256).sum()) +
+                                              ((S + 255) // 256 if shared_mfma else 0)) if thr > 0 else 0},
           "kernels_us": kernels,
           "roofline": {"kernel": gu_key, "bound": "mfma", "achieved": gu_achieved, "peak": peak,
                        "unit": "TFLOP/s", "frac": gu_achieved / peak if gu_achieved else None,
@@ -706,7 +708,7 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=4, help="resident layer instances rotated per step")
     ap.add_argument("--tokens", type=int, default=1024, help="distinct tokens rotated per step")
     ap.add_argument("--profile-steps", type=int, default=512)
-    ap.add_argument("--mfma-min-tokens", type=int, default=8,
+    ap.add_argument("--mfma-min-tokens", type=int, default=3,
                     help="prefill: experts with at least this many tokens use the matrix cores")
     ap.add_argument("--call", default="layer", choices=["layer", "split"],
                     help="decode and verify: one moe_layer call per step, or moe_route then moe_ffn")

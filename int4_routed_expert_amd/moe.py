@@ -103,7 +103,7 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-MFMA_MIN_TOKENS = 8  # default threshold of the matrix-core path (tokens per expert)
+MFMA_MIN_TOKENS = 3  # default threshold of the matrix-core path (tokens per expert)
 
 
 def make_cfg(c, mfma_min_tokens: int = MFMA_MIN_TOKENS, act_int8: int = 0) -> moe_cfg:
