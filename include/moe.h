@@ -89,8 +89,10 @@ typedef struct moe_cfg {
   int32_t norm_topk_prob;
   /* Batches of more than 4 tokens: an expert (routed or shared) that receives at
    * least this many tokens is contracted on the matrix cores in bf16 (x and h
-   * rounded to bf16, weights dequantised to bf16, fp32 accumulation); the others
-   * keep the exact fp32 path.  0 disables the matrix-core path.  >= 0. */
+   * rounded to bf16, weights dequantised to bf16, fp32 accumulation; with
+   * act_int8 the matrix cores take the quantised integers exactly, see act_int8);
+   * the others keep the exact fp32 path.  0 disables the matrix-core path.  >= 0.
+   * The binding's default is 3. */
   int32_t mfma_min_tokens;
   /* moe_weight_format of every expert of the layer (routed and shared). */
   int32_t weight_format;
