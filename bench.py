@@ -99,9 +99,24 @@ def kernel_unit(kernel: str) -> str:
     return "ffn_gemv.hip"
 
 
+_CODE_TOKENS = None
+
+
+def code_only(text: str) -> str:
+    """C/C++ source without its comments and blank lines (string and character literals kept), so
+    that a fingerprint of the code does not change when only comments or spacing do."""
+    import re
+    global _CODE_TOKENS
+    if _CODE_TOKENS is None:
+        _CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/', re.S)
+    text = _CODE_TOKENS.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
 def kernel_source_hash(kernel: str) -> str:
-    """sha256 over the source file that defines `kernel` and every header it includes, directly or
-    not (a counter reading goes stale when one of them changes, and only then)."""
+    """sha256 over the code (comments dropped) of the source file that defines `kernel` and every
+    header it includes, directly or not: a counter reading goes stale when that code changes, and
+    only then."""
     import hashlib
     import re
     seen, todo = [], [os.path.join(CSRC, kernel_unit(kernel))]
@@ -115,8 +130,8 @@ def kernel_source_hash(kernel: str) -> str:
                 todo.append(os.path.join(os.path.dirname(f), inc))
     h = hashlib.sha256()
     for f in sorted(seen):
-        with open(f, "rb") as fh:
-            h.update(os.path.relpath(f, ROOT).encode() + b"\0" + fh.read())
+        with open(f) as fh:
+            h.update(os.path.relpath(f, ROOT).encode() + b"\0" + code_only(fh.read()).encode())
     return h.hexdigest()
 
 
