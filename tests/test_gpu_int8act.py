@@ -199,10 +199,13 @@ def test_layer_call_graph_replays(tiny_q, S):
         assert torch.isfinite(y_e).all()
 
 
-def test_zero_and_nan_rows(tiny_q):
+@pytest.mark.parametrize("thr", [0, 2], ids=["gemv", "matrix_cores"])
+def test_zero_and_nan_rows(tiny_q, thr):
     """An all-zero token quantises to zeros (d = 0) and gives exactly zero output;
     a token holding a NaN gets d = NaN and NaN outputs, and the other tokens of
-    the batch are untouched (int8 activations, decode and batch paths)."""
+    the batch are untouched (int8 activations, decode and batch paths; with the
+    threshold at 2 tokens the 9-token batch sends the shared expert and every
+    expert chosen twice, zero and NaN rows included, to the matrix cores)."""
     for S in (3, 9):
         x = gen.tokens(tiny_q.w.with_(tokens=S), step=1234 + S).copy()
         x[0] = 0.0
@@ -212,7 +215,7 @@ def test_zero_and_nan_rows(tiny_q):
         xr = x.copy()
         xr[1] = xr[2]
         idx, wt = tiny_q.route(x_device(tiny_q.w, xr)[0], dt)
-        y = tiny_q.ffn(xt, dt, idx, wt).cpu().numpy()
+        y = tiny_q.ffn(xt, dt, idx, wt, mfma_min_tokens=thr).cpu().numpy()
         assert np.all(y[0] == 0.0), S
         assert np.isnan(y[1]).all(), S
         ridx, rw = check_route(tiny_q, xr, idx.cpu().numpy(), wt.cpu().numpy())

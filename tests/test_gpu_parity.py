@@ -503,6 +503,29 @@ def test_matrix_core_every_tile_height(mid):
     check_ffn(mid, x, idx, wt, y, np.arange(S), TOL_BF16)
 
 
+def test_matrix_core_zero_and_nan_rows(mid):
+    """The bf16 matrix-core tiles are row-local: in a 40-token batch with the
+    threshold at 2 tokens (every expert chosen twice, and the shared expert, on
+    the matrix cores), an all-zero token gives exactly zero output, a token with
+    one NaN activation gives NaN outputs, and every other token matches the
+    oracle."""
+    S = 40
+    w = mid.w.with_(tokens=S)
+    x = gen.tokens(w, step=4321).copy()
+    x[0] = 0.0
+    x[1, 7] = np.nan
+    xt, dt = x_device(w, x)
+    xr = x.copy()
+    xr[1] = xr[2]  # route the finite tokens on a clean copy (a NaN logit has no defined selection)
+    idx, wt = mid.route(x_device(w, xr)[0], dt)
+    ridx, rw = check_route(mid, xr, idx.cpu().numpy(), wt.cpu().numpy())
+    assert (np.bincount(ridx.ravel(), minlength=mid.c.n_experts) >= 2).any()
+    y = mid.ffn(xt, dt, idx, wt, mfma_min_tokens=2).cpu().numpy()
+    assert np.all(y[0] == 0.0)
+    assert np.isnan(y[1]).all()
+    check_ffn(mid, x, ridx, rw, y, np.arange(2, S), TOL_BF16)
+
+
 def test_matrix_core_unresident_slot_poisons_only_its_tokens(mid):
     S, thr = 67, 4
     w = mid.w.with_(tokens=S)
