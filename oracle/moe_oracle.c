@@ -45,6 +45,13 @@
  *     d = fp32(amax / 127) with amax = max |v| (fp32), q_c = rint(fp32(v_c / d))
  *     (ties to even; q = 0 for an all-zero row), and the matmul uses q_c * d
  *     (exact in fp64) in place of v_c.
+ *  R8 bf16 operands (the library's matrix-core path, its own choice and not the
+ *     pages'): for an expert so marked, the gate/up contraction sees the token's
+ *     input rounded to bf16 and every weight rounded to fp32 and then to bf16,
+ *     and the down contraction sees h rounded to fp32 and then to bf16 and its
+ *     weights rounded the same way; all roundings to nearest, ties to even; the
+ *     arithmetic stays fp64.  Which experts are marked is the caller's input
+ *     (the library marks those a batch sends to its matrix cores).
  *
  * Parity pins: tests/test_oracle_pins.py (brute force, closed forms, invariants)
  * and tests/test_oracle_diag.py (the decision margins and the near-midpoint flag
@@ -275,6 +282,20 @@ int oracle_route(int S, int H, int E, int G, int Gk, int k, double rsf, int norm
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
+/* R8: f rounded to the nearest bf16 (8 significant bits), ties to even; NaN stays
+ * NaN, and a value beyond the largest bf16 becomes an infinity. */
+float oracle_bf16_round(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u) return f; /* inf, NaN */
+  const uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7FFFu + lsb;
+  u &= 0xFFFF0000u;
+  memcpy(&f, &u, 4);
+  return f;
+}
+static double bf16_of(double v) { return (double)oracle_bf16_round((float)v); }
+
 /* R7: v[n] (fp32 values) -> q[n] (int8 values) and the row's scale d; out[c] =
  * q_c * d in fp64.  The decisions are taken in fp32 (IEEE division). */
 float oracle_quant_row(int n, const float *v, int8_t *q, double *out) {
@@ -292,20 +313,28 @@ float oracle_quant_row(int n, const float *v, int8_t *q, double *out) {
 /* y[H] = Wd (silu(Wg x) * (Wu x)) for one token, fp64.  Matrices in the
  * interchange layout of format fmt (R6): gate/up [I, H], down [H, I].
  * h_out (optional) receives the [I] hidden activation. */
-static void expert_ffn_impl(int fmt, int act_int8, int H, int I, int gsz, const uint8_t *qg, const void *sg,
-                            const uint8_t *qu, const void *su, const uint8_t *qd, const void *sd, const double *x,
-                            double *y, double *h_out) {
+/* bf16 (R8): x is already rounded by the caller; the weights and h are rounded here. */
+static void expert_ffn_impl(int fmt, int act_int8, int bf16, int H, int I, int gsz, const uint8_t *qg,
+                            const void *sg, const uint8_t *qu, const void *su, const uint8_t *qd, const void *sd,
+                            const double *x, double *y, double *h_out) {
   double *h = malloc(sizeof(double) * I);
 #pragma omp parallel for schedule(static)
   for (int r = 0; r < I; ++r) {
     double g = 0.0, u = 0.0;
     for (int c = 0; c < H; ++c) {
-      g += w_at(fmt, H, gsz, qg, sg, r, c) * x[c];
-      u += w_at(fmt, H, gsz, qu, su, r, c) * x[c];
+      double wg = w_at(fmt, H, gsz, qg, sg, r, c), wu = w_at(fmt, H, gsz, qu, su, r, c);
+      if (bf16) {
+        wg = bf16_of(wg);
+        wu = bf16_of(wu);
+      }
+      g += wg * x[c];
+      u += wu * x[c];
     }
     h[r] = silu(g) * u;
   }
   if (h_out) memcpy(h_out, h, sizeof(double) * I);
+  if (bf16)
+    for (int c = 0; c < I; ++c) h[c] = bf16_of(h[c]);
   if (act_int8) { /* R7: the down projection sees h rounded to fp32, then quantised */
     float *h32 = malloc(sizeof(float) * I);
     for (int c = 0; c < I; ++c) h32[c] = (float)h[c];
@@ -315,7 +344,10 @@ static void expert_ffn_impl(int fmt, int act_int8, int H, int I, int gsz, const 
 #pragma omp parallel for schedule(static)
   for (int r = 0; r < H; ++r) {
     double acc = 0.0;
-    for (int c = 0; c < I; ++c) acc += w_at(fmt, I, gsz, qd, sd, r, c) * h[c];
+    for (int c = 0; c < I; ++c) {
+      const double wd = w_at(fmt, I, gsz, qd, sd, r, c);
+      acc += (bf16 ? bf16_of(wd) : wd) * h[c];
+    }
     y[r] = acc;
   }
   free(h);
@@ -325,7 +357,7 @@ static void expert_ffn_impl(int fmt, int act_int8, int H, int I, int gsz, const 
 void oracle_expert_ffn_fmt(int fmt, int H, int I, int gsz, const uint8_t *qg, const void *sg, const uint8_t *qu,
                            const void *su, const uint8_t *qd, const void *sd, const double *x, double *y,
                            double *h_out) {
-  expert_ffn_impl(fmt, 0, H, I, gsz, qg, sg, qu, su, qd, sd, x, y, h_out);
+  expert_ffn_impl(fmt, 0, 0, H, I, gsz, qg, sg, qu, su, qd, sd, x, y, h_out);
 }
 
 /* R7 mode: x (fp32 values) is quantised here; h_out receives h before its quantisation. */
@@ -334,7 +366,7 @@ void oracle_expert_ffn_int8act(int fmt, int H, int I, int gsz, const uint8_t *qg
                                double *h_out) {
   double *xq = malloc(sizeof(double) * H);
   oracle_quant_row(H, x, NULL, xq);
-  expert_ffn_impl(fmt, 1, H, I, gsz, qg, sg, qu, su, qd, sd, xq, y, h_out);
+  expert_ffn_impl(fmt, 1, 0, H, I, gsz, qg, sg, qu, su, qd, sd, xq, y, h_out);
   free(xq);
 }
 
@@ -349,11 +381,17 @@ void oracle_expert_ffn(int H, int I, int gsz, const uint8_t *qg, const uint16_t 
  * Expert e's six parts are qg[e], sg[e], ... (pointer arrays of length E+1; entry E
  * is the shared expert, NULL when the layer has none).  Only experts that the
  * routing names need non-NULL pointers.  Every expert is in format fmt (R6). */
-int oracle_moe_ffn_mode(int fmt, int act_int8, int S, int H, int E, int k, int I, int Is, int gsz, int x_is_bf16,
+/* bf16_mask (optional, [E + 1], entry E the shared expert): experts computed with
+ * bf16 operands (R8); NULL or all zero is the exact layer.  Not combined with R7. */
+int oracle_moe_ffn_mask(int fmt, int act_int8, int S, int H, int E, int k, int I, int Is, int gsz, int x_is_bf16,
                         const void *x, const int32_t *idx, const double *w, const uint8_t *const *qg,
                         const void *const *sg, const uint8_t *const *qu, const void *const *su,
-                        const uint8_t *const *qd, const void *const *sd, double *y) {
-  double *xt = malloc(sizeof(double) * H), *ye = malloc(sizeof(double) * H), *acc = malloc(sizeof(double) * H);
+                        const uint8_t *const *qd, const void *const *sd, const uint8_t *bf16_mask, double *y) {
+  if (act_int8 && bf16_mask)
+    for (int e = 0; e <= E; ++e)
+      if (bf16_mask[e]) return -2;
+  double *xt = malloc(sizeof(double) * H), *xb = malloc(sizeof(double) * H), *ye = malloc(sizeof(double) * H),
+         *acc = malloc(sizeof(double) * H);
   float *x32 = malloc(sizeof(float) * H);
   int rc = 0;
   for (int t = 0; t < S && !rc; ++t) {
@@ -362,23 +400,34 @@ int oracle_moe_ffn_mode(int fmt, int act_int8, int S, int H, int E, int k, int I
       for (int c = 0; c < H; ++c) x32[c] = (float)xt[c];  /* fp32 and bf16 inputs are exact in fp32 */
       oracle_quant_row(H, x32, NULL, xt);
     }
+    for (int c = 0; c < H; ++c) xb[c] = bf16_of(xt[c]); /* R8 input (exact for bf16 inputs) */
     for (int c = 0; c < H; ++c) acc[c] = 0.0;
     for (int j = 0; j < k; ++j) {
       int e = idx[(size_t)t * k + j];
       if (e < 0 || e >= E || !qg[e] || !sg[e] || !qu[e] || !su[e] || !qd[e] || !sd[e]) { rc = -1; break; }
-      expert_ffn_impl(fmt, act_int8, H, I, gsz, qg[e], sg[e], qu[e], su[e], qd[e], sd[e], xt, ye, NULL);
+      const int b = bf16_mask && bf16_mask[e];
+      expert_ffn_impl(fmt, act_int8, b, H, I, gsz, qg[e], sg[e], qu[e], su[e], qd[e], sd[e], b ? xb : xt, ye, NULL);
       for (int c = 0; c < H; ++c) acc[c] += w[(size_t)t * k + j] * ye[c];
     }
     if (rc) break;
     if (Is > 0) {
       if (!qg[E]) { rc = -1; break; }
-      expert_ffn_impl(fmt, act_int8, H, Is, gsz, qg[E], sg[E], qu[E], su[E], qd[E], sd[E], xt, ye, NULL);
+      const int b = bf16_mask && bf16_mask[E];
+      expert_ffn_impl(fmt, act_int8, b, H, Is, gsz, qg[E], sg[E], qu[E], su[E], qd[E], sd[E], b ? xb : xt, ye, NULL);
       for (int c = 0; c < H; ++c) acc[c] += ye[c];
     }
     for (int c = 0; c < H; ++c) y[(size_t)t * H + c] = acc[c];
   }
-  free(xt); free(ye); free(acc); free(x32);
+  free(xt); free(xb); free(ye); free(acc); free(x32);
   return rc;
+}
+
+int oracle_moe_ffn_mode(int fmt, int act_int8, int S, int H, int E, int k, int I, int Is, int gsz, int x_is_bf16,
+                        const void *x, const int32_t *idx, const double *w, const uint8_t *const *qg,
+                        const void *const *sg, const uint8_t *const *qu, const void *const *su,
+                        const uint8_t *const *qd, const void *const *sd, double *y) {
+  return oracle_moe_ffn_mask(fmt, act_int8, S, H, E, k, I, Is, gsz, x_is_bf16, x, idx, w, qg, sg, qu, su, qd, sd,
+                             NULL, y);
 }
 
 int oracle_moe_ffn_fmt(int fmt, int S, int H, int E, int k, int I, int Is, int gsz, int x_is_bf16, const void *x,

@@ -61,6 +61,10 @@ def lib():
         L.oracle_moe_ffn_fmt.argtypes = [i] * 9 + [p] * 10
         L.oracle_moe_ffn_mode.restype = i
         L.oracle_moe_ffn_mode.argtypes = [i] * 10 + [p] * 10
+        L.oracle_moe_ffn_mask.restype = i
+        L.oracle_moe_ffn_mask.argtypes = [i] * 10 + [p] * 11
+        L.oracle_bf16_round.restype = ctypes.c_float
+        L.oracle_bf16_round.argtypes = [ctypes.c_float]
         L.oracle_quant_row.restype = ctypes.c_float
         L.oracle_quant_row.argtypes = [i, p, p, p]
         L.oracle_expert_ffn_int8act.restype = None
@@ -171,11 +175,17 @@ def expert_ffn(ex, x: np.ndarray, H: int, gsz: int = 32, return_h: bool = False)
     return (y, h) if return_h else y
 
 
+def bf16_round(v: float) -> float:
+    """R8's rounding of one fp32 value to the nearest bf16 (ties to even)."""
+    return float(lib().oracle_bf16_round(float(v)))
+
+
 def moe_ffn(cfg, x: np.ndarray, idx: np.ndarray, w: np.ndarray, experts: dict, x_is_bf16: bool = False,
-            act_int8: bool = False):
+            act_int8: bool = False, bf16_experts=()):
     """The layer's FFN for S tokens given routing; ``experts`` maps expert id -> ExpertWeights
     (id ``n_experts`` is the shared expert).  act_int8: x and every h are quantised to int8 per
-    row before their matmuls.  Returns y[S,H] fp64."""
+    row before their matmuls.  bf16_experts: ids (``n_experts`` for the shared expert) computed
+    with bf16 operands (R8).  Returns y[S,H] fp64."""
     S, H = x.shape
     E, k = cfg.n_experts, cfg.top_k
     arrs = [[None] * (E + 1) for _ in range(6)]
@@ -191,9 +201,14 @@ def moe_ffn(cfg, x: np.ndarray, idx: np.ndarray, w: np.ndarray, experts: dict, x
     x = np.ascontiguousarray(x)
     idx = np.ascontiguousarray(idx, np.int32)
     w = np.ascontiguousarray(w, np.float64)
-    rc = lib().oracle_moe_ffn_mode(fmt, int(act_int8), S, H, E, k, cfg.moe_inter, cfg.shared_inter, cfg.group_size,
+    mask = np.zeros(E + 1, np.uint8)
+    for e in bf16_experts:
+        mask[int(e)] = 1
+    rc = lib().oracle_moe_ffn_mask(fmt, int(act_int8), S, H, E, k, cfg.moe_inter, cfg.shared_inter, cfg.group_size,
                                    int(x_is_bf16), _p(x), _p(idx), _p(w),
-                                   *[ctypes.cast(pp, ctypes.c_void_p) for pp in ptrs], _p(y))
+                                   *[ctypes.cast(pp, ctypes.c_void_p) for pp in ptrs], _p(mask), _p(y))
+    if rc == -2:
+        raise ValueError("oracle_moe_ffn: bf16 operands are not combined with int8 activations")
     if rc:
         raise ValueError("oracle_moe_ffn: routing names an expert without weights")
     return y

@@ -104,6 +104,21 @@ def x_device(w: gen.Workload, x_host: np.ndarray):
     return dev(x_host), M.MOE_F32
 
 
+def matrix_core_experts(ridx: np.ndarray, n_experts: int, shared_inter: int, mfma_min_tokens: int) -> list:
+    """The experts (``n_experts`` for the shared one) that a batch with routing ridx
+    sends to the bf16 matrix cores (moe_cfg.mfma_min_tokens): in batches of more
+    than 4 tokens, every expert chosen by at least that many tokens, and the shared
+    expert when the batch has at least that many tokens."""
+    S = ridx.shape[0]
+    if mfma_min_tokens <= 0 or S <= 4:
+        return []
+    counts = np.bincount(ridx.ravel(), minlength=n_experts)
+    out = [int(e) for e in np.where(counts >= mfma_min_tokens)[0]]
+    if shared_inter > 0 and S >= mfma_min_tokens:
+        out.append(n_experts)
+    return out
+
+
 def max_rel_err(y: np.ndarray, ref: np.ndarray) -> float:
     """max over tokens of max_i |y - ref| / max_i |ref| (0 when both are exactly zero)."""
     worst = 0.0

@@ -72,7 +72,7 @@ def matrix_core_case(dl, S, thr):
     y_exact = dl.ffn(xt, dt, idx, wt, mfma_min_tokens=0).cpu().numpy()
     ridx, rw = check_route(dl, x, idx.cpu().numpy(), wt.cpu().numpy())
     assert (np.bincount(ridx.ravel(), minlength=dl.c.n_experts) >= thr).any()
-    check_ffn(dl, x, ridx, rw, y_mfma, np.arange(S), TOL_BF16)
+    check_ffn(dl, x, ridx, rw, y_mfma, np.arange(S), TOL_BF16, mfma_min_tokens=thr)
     check_ffn(dl, x, ridx, rw, y_exact, np.arange(S), TOL_FP32)
     assert not np.array_equal(y_mfma, y_exact)
 
@@ -145,5 +145,5 @@ def test_glm_shape_decode_verify_prefill(fmt):
     counts = np.bincount(ridx.ravel(), minlength=dl.c.n_experts)
     say(f"prefill: experts with >= 16 tokens {(counts >= 16).sum()}")
     tokens = np.union1d(tile_cover(ridx, dl.c.n_experts, dl.cfg.mfma_min_tokens), [0, 2047])
-    check_ffn(dl, x, ridx, rw, y, tokens, TOL_BF16)
+    check_ffn(dl, x, ridx, rw, y, tokens, TOL_BF16, mfma_min_tokens=dl.cfg.mfma_min_tokens)
     assert np.isfinite(y).all()

@@ -14,12 +14,15 @@ import torch
 from gen import inputs as gen
 from int4_routed_expert_amd import moe as M
 from oracle import oracle as O
-from tests.devlayer import DeviceLayer, dev, max_rel_err, tile_cover, x_device
+from tests.devlayer import matrix_core_experts, DeviceLayer, dev, max_rel_err, tile_cover, x_device
 
 pytestmark = pytest.mark.gpu
 
 TOL_FP32 = 2e-3
 TOL_BF16 = 1e-2
+# against the oracle with the same bf16 operands: only accumulation order and
+# the odd element of h on the other side of a bf16 rounding boundary differ
+TOL_BF16_OPS = 2e-3
 
 MID = gen.LayerConfig(hidden=512, n_experts=32, n_group=4, topk_group=2, top_k=4, moe_inter=256, shared_inter=192)
 
@@ -47,17 +50,30 @@ def check_route(dl: DeviceLayer, x_host, idx, wt):
     return ridx, rw
 
 
-def check_ffn(dl: DeviceLayer, x_host, ridx, rw, y, tokens, tol):
+def check_ffn(dl: DeviceLayer, x_host, ridx, rw, y, tokens, tol, mfma_min_tokens: int | None = None):
+    """y on `tokens` against the exact oracle within tol; with mfma_min_tokens, also
+    against the oracle with bf16 operands for the experts the whole batch (ridx)
+    sends to the matrix cores, within TOL_BF16_OPS."""
     c = dl.c
-    xs = x_host[tokens]
+    xs = np.ascontiguousarray(x_host[tokens])
     need = set(ridx[tokens].ravel().tolist())
     experts = {e: dl.host_expert(e) for e in need}
     if c.shared_inter > 0:
         experts[c.n_experts] = dl.host[c.n_experts]
-    ref = O.moe_ffn(c, np.ascontiguousarray(xs), ridx[tokens], rw[tokens], experts, x_is_bf16=dl.w.x_dtype == "bf16")
+    bf = dl.w.x_dtype == "bf16"
+    ref = O.moe_ffn(c, xs, ridx[tokens], rw[tokens], experts, x_is_bf16=bf)
     err = max_rel_err(y[tokens], ref)
-    say(f"  max rel err over {len(tokens)} tokens: {err:.3e}")
+    msg = f"  max rel err over {len(tokens)} tokens: {err:.3e}"
+    err_b = None
+    if mfma_min_tokens is not None:
+        mc = matrix_core_experts(ridx, c.n_experts, c.shared_inter, mfma_min_tokens)
+        ref_b = O.moe_ffn(c, xs, ridx[tokens], rw[tokens], experts, x_is_bf16=bf, bf16_experts=mc)
+        err_b = max_rel_err(y[tokens], ref_b)
+        msg += f"; against bf16 operands on the {len(mc)} matrix-core experts: {err_b:.3e}"
+    say(msg)
     assert err <= tol
+    if err_b is not None:
+        assert err_b <= TOL_BF16_OPS
     return err
 
 
@@ -458,7 +474,7 @@ def test_matrix_core_path(tiny, mid, case):
     say(f"{case}: tokens per expert max {counts.max()}, experts at or over {thr}: {(counts >= thr).sum()}")
     assert (counts >= thr).any() or S >= thr
     ym, ye = y_mfma.cpu().numpy(), y_exact.cpu().numpy()
-    check_ffn(dl, x, ridx, rw, ym, np.arange(S), TOL_BF16)
+    check_ffn(dl, x, ridx, rw, ym, np.arange(S), TOL_BF16, mfma_min_tokens=thr)
     check_ffn(dl, x, ridx, rw, ye, np.arange(S), TOL_FP32)
     assert not np.array_equal(ym, ye)
 
@@ -500,7 +516,7 @@ def test_matrix_core_every_tile_height(mid):
     xt, dt = x_device(w, x)
     y = mid.ffn(xt, dt, dev(idx), dev(wt), mfma_min_tokens=8).cpu().numpy()
     say(f"tokens per expert: {sorted(np.bincount(idx.ravel(), minlength=c.n_experts).tolist())}")
-    check_ffn(mid, x, idx, wt, y, np.arange(S), TOL_BF16)
+    check_ffn(mid, x, idx, wt, y, np.arange(S), TOL_BF16, mfma_min_tokens=8)
 
 
 def test_matrix_core_zero_and_nan_rows(mid):
@@ -523,7 +539,7 @@ def test_matrix_core_zero_and_nan_rows(mid):
     y = mid.ffn(xt, dt, idx, wt, mfma_min_tokens=2).cpu().numpy()
     assert np.all(y[0] == 0.0)
     assert np.isnan(y[1]).all()
-    check_ffn(mid, x, ridx, rw, y, np.arange(2, S), TOL_BF16)
+    check_ffn(mid, x, ridx, rw, y, np.arange(2, S), TOL_BF16, mfma_min_tokens=2)
 
 
 def test_matrix_core_unresident_slot_poisons_only_its_tokens(mid):
@@ -543,7 +559,7 @@ def test_matrix_core_unresident_slot_poisons_only_its_tokens(mid):
     assert np.isnan(y[hit]).all(axis=1).all()
     assert np.isfinite(y[~hit]).all()
     ridx, rw = check_route(mid, x, ih, wt.cpu().numpy())
-    check_ffn(mid, x, ridx, rw, y, np.where(~hit)[0], TOL_BF16)
+    check_ffn(mid, x, ridx, rw, y, np.where(~hit)[0], TOL_BF16, mfma_min_tokens=thr)
 
 
 def test_prefill_full_size():
@@ -563,7 +579,7 @@ def test_prefill_full_size():
     say(f"prefill: max tokens per expert {counts.max()}, experts with >= 16 tokens {(counts >= 16).sum()}")
     tokens = np.union1d(tile_cover(ridx, w.cfg.n_experts, dl.cfg.mfma_min_tokens, extra=6), [0, 2047])
     say(f"prefill: comparing {tokens.size} tokens")
-    check_ffn(dl, x, ridx, rw, y, tokens, TOL_BF16)
+    check_ffn(dl, x, ridx, rw, y, tokens, TOL_BF16, mfma_min_tokens=dl.cfg.mfma_min_tokens)
     assert np.isfinite(y).all()
 
 

@@ -558,3 +558,84 @@ def test_int8act_layer_is_the_weighted_sum_of_int8act_experts():
         ref += O.expert_ffn_int8act(experts[c.n_experts], x[t], c.hidden)
         assert np.array_equal(y[t], ref)
     assert not np.array_equal(y, O.moe_ffn(c, x, idx, wt, experts))
+
+
+# ------------------------------------------------------------------ bf16 operands (R8)
+
+def test_bf16_round_matches_torch():
+    """R8's rounding against torch's float32 -> bfloat16 conversion (round to
+    nearest, ties to even) on random values over the whole exponent range and on
+    constructed ties (both parities), half-way points just above and below,
+    subnormals, the largest finite values and the infinities."""
+    import torch
+    rng = np.random.default_rng(3)
+    bits = rng.integers(0, 2**32, 4000, dtype=np.uint64).astype(np.uint32)
+    ties = np.array([(m << 16) | 0x8000 for m in range(0, 2**16, 97)], np.uint32)
+    near = np.concatenate([ties + 1, ties - 1])
+    special = np.array([0x00000001, 0x00008000, 0x00018000, 0x007FFFFF, 0x7F7FFFFF, 0x7F7F8000, 0xFF7FFFFF,
+                        0x7F800000, 0xFF800000, 0x3F808000, 0x3F818000], np.uint32)
+    vals = np.concatenate([bits, ties, near, special]).view(np.float32)
+    vals = vals[np.isfinite(vals) | np.isinf(vals)]
+    vals = vals[~np.isnan(vals)]
+    ref = torch.from_numpy(vals.copy()).to(torch.bfloat16).to(torch.float32).numpy()
+    mine = np.array([O.bf16_round(float(v)) for v in vals], np.float32)
+    assert np.array_equal(mine.view(np.uint32), ref.view(np.uint32))
+
+
+def one_hot_expert(c, inter, q, s_bits):
+    """An expert whose gate, up and down matrices each hold one weight: row 0,
+    column 0, value q[part] (int4) with fp16 scale bits s_bits[part]; every other
+    weight is 0 (nibble 8) with the same scale."""
+    ex = gen.empty_expert(c, inter)
+    for j, (qa, sa) in enumerate(((ex.qg, ex.sg), (ex.qu, ex.su), (ex.qd, ex.sd))):
+        qa[:] = 0x88
+        qa[0, 0] = 0x80 | ((q[j] + 8) & 0xF)
+        sa[:] = s_bits[j]
+    return ex
+
+
+def test_bf16_operands_worked_example():
+    """Values computed by hand.  x0 = 1 + 2^-10 (bf16: 1); gate and down weights
+    1 * (1 + 2^-10) (bf16: 1), up weight 3 * (1 + 2^-10) (bf16: 3).  Exact:
+    g = (1 + 2^-10)^2, u = 3 g, y0 = (1 + 2^-10) silu(g) u.  bf16 operands:
+    g = 1, u = 3, h = silu(1) * 3 = 2.19317... -> bf16 2.1875 (steps of 2^-6
+    between 2 and 4), y0 = 2.1875.  Each rounding changes the result (without the
+    input's: g = 1 + 2^-10; without the weights': g = (1 + 2^-10)^2; without h's:
+    y0 = 2.19317...), and only marked experts round: routed and shared apart."""
+    c = gen.LayerConfig(hidden=32, n_experts=2, n_group=1, topk_group=1, top_k=1, moe_inter=32, shared_inter=32)
+    one_p = 0x3C01  # fp16 1 + 2^-10
+    ex = one_hot_expert(c, 32, (1, 3, 1), (one_p, one_p, one_p))
+    experts = {0: ex, 1: ex, 2: ex}  # routed 0 and 1, shared (id 2) the same weights
+    x = np.zeros((1, 32), np.float32)
+    x[0, 0] = 1 + 2.0**-10
+    idx = np.array([[0]], np.int32)
+    w = np.array([[1.0]])
+    a = 1 + 2.0**-10
+    g = a * a
+    exact0 = a * (g / (1 + math.exp(-g))) * (3 * g)
+    bf0 = 2.1875
+    assert O.bf16_round(3 / (1 + math.exp(-1.0))) == bf0
+    for mark, want in (((), 2 * exact0), ((0,), bf0 + exact0), ((2,), exact0 + bf0), ((0, 2), 2 * bf0),
+                       ((1,), 2 * exact0)):
+        y = O.moe_ffn(c, x, idx, w, experts, bf16_experts=mark)
+        assert y[0, 0] == pytest.approx(want, rel=1e-15), mark
+        assert np.all(y[0, 1:] == 0.0)
+    assert O.moe_ffn(c, x, idx, w, experts, bf16_experts=(0, 2))[0, 0] == 2 * bf0
+
+
+def test_bf16_operands_unmarked_is_exact_and_int8_is_refused():
+    w = gen.WORKLOADS["tiny"].with_(tokens=3)
+    c = w.cfg
+    x = gen.tokens(w)
+    idx, wt, _, _, _ = O.route(c, x, gen.router_weights(w), gen.router_bias(w))
+    experts = {e: gen.expert_weights(w, 0, e) for e in set(idx.ravel().tolist()) | {c.n_experts}}
+    exact = O.moe_ffn(c, x, idx, wt, experts)
+    assert np.array_equal(O.moe_ffn(c, x, idx, wt, experts, bf16_experts=()), exact)
+    unused = sorted(set(range(c.n_experts)) - set(idx.ravel().tolist()))
+    if unused:
+        assert np.array_equal(O.moe_ffn(c, x, idx, wt, experts, bf16_experts=unused[:1]), exact)
+    marked = O.moe_ffn(c, x, idx, wt, experts, bf16_experts=range(c.n_experts + 1))
+    rel = np.abs(marked - exact).max() / np.abs(exact).max()
+    assert 1e-5 < rel < 5e-2
+    with pytest.raises(ValueError):
+        O.moe_ffn(c, x, idx, wt, experts, act_int8=True, bf16_experts=(c.n_experts,))
