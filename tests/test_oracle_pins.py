@@ -455,9 +455,10 @@ def test_row_scale_power_of_two_is_exact(fmt):
 
 
 # ------------------------------------------------------ int8 activations (IDOT)
-# [PORT] "G2 implementation status": Colibri's IDOT=1 quantises each activation
-# row to int8 before the packed-int4 dot product (about 0.3 % extra RMS error per
-# matmul); the oracle's reading: d = amax / 127, q = rint(v / d), both in fp32.
+# [PORT] "G2 implementation status": with Colibri's IDOT=1 setting, every activation
+# row becomes int8 ahead of its dot products with the int4 weights, at a cost the
+# page puts near 0.3 % RMS per matmul; the oracle's reading: d = amax / 127,
+# q = rint(v / d), both in fp32.
 
 def test_quant_row_grid_values_are_exact():
     k = np.arange(-127, 128)
