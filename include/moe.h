@@ -12,12 +12,13 @@
  * Sources (web pages, cited by title and section):
  *  [PORT]   "GLM-5.2 on a 32 GB Mac - native MLX port of the Colibri hierarchy":
  *           N1 "GLM-5.2 graph" (router and shared expert), "G2 implementation
- *           status" (offset-binary Q4, lower expert ID wins exact ties, un-biased
- *           sigmoid weights, routed scale, unweighted shared expert, dequantise
- *           then f32 multiply-accumulate), "G3 implementation status" (slot
- *           catalog, per-layer LRU slots, batch union, resident work first).
- *  [README] colibri README, "What's implemented" (DeepSeek-V3-style sigmoid
- *           router, noaux_tc, routed_scaling_factor, batch-union MoE).
+ *           status" (the int4 nibble encoding, the tie rule between equal keys,
+ *           the weights taken from the sigmoid without its bias, the scaling of
+ *           the routed sum, the shared expert's weight of one, the dequantise-
+ *           and-accumulate contract), "G3 implementation status" (the slot
+ *           catalog and its per-layer LRU, the batch union, resident work first).
+ *  [README] colibri README, "What's implemented" (the sigmoid noaux_tc router
+ *           of the DeepSeek-V3 kind with its scaling factor, the batch union).
  *  [MODELS] "Model support" doc, 4.3 UniversalMoE (grouped routing) and 6.4.
  *
  * Conventions for every call below:

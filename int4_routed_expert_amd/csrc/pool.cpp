@@ -2,10 +2,11 @@
 // slab, filled from pinned host memory on a side stream.
 //
 // Source: "GLM-5.2 on a 32 GB Mac - native MLX port of the Colibri hierarchy",
-// N3 (explicit residency manager: resident / loading / in-use states, no reuse
-// of a slot before its consumer completes, never publish a partially filled
-// slot), "G3 implementation status" (fixed per-layer LRU slots, deterministic
-// LRU ties, batch union, resident work submitted before miss reads); the
+// N3 (an explicit residency manager: a slot is resident, loading or leased; it
+// is reused only after its consumer is done, and a slot whose copy is still
+// running is never handed out), "G3 implementation status" (a fixed number of
+// LRU slots per layer with a deterministic tie rule, the batch union, work on
+// resident experts queued ahead of the reads of missing ones); the
 // colibri README "What's implemented" (per-layer LRU of streamed experts); the
 // strata audit's slot map (residency changes by writing one table entry).
 //

@@ -7,15 +7,17 @@
  *
  * Sources (web pages; cited by title and section):
  *  [PORT]   "GLM-5.2 on a 32 GB Mac - native MLX port of the Colibri hierarchy"
- *           (mlx-bun design doc): section "N1. GLM-5.2 graph" (sigmoid scores plus
- *           correction bias select, un-biased weights execute, true top-8, optional
- *           normalisation and routed scale, shared expert in parallel);
- *           "G2 implementation status" (lower expert ID wins exact ties; unbiased
- *           sigmoid for execution; routed scaling; unweighted shared expert; Q4
- *           nibbles are offset-binary, i.e. value = nibble - 8, MLX bias = -8*scale;
- *           dequantise then f32 multiply-accumulate).
- *  [README] colibri README, "What's implemented" (DeepSeek-V3-style sigmoid
- *           router, noaux_tc, routed_scaling_factor, shared expert).
+ *           (mlx-bun design doc): section "N1. GLM-5.2 graph" (the biased sigmoid
+ *           scores choose the experts and the unbiased ones weigh them, an exact
+ *           top-8, an optional renormalisation, the routed scale, and a shared
+ *           expert computed beside the routed ones);
+ *           "G2 implementation status" (equal keys go to the lower expert index;
+ *           the expert weights come from the sigmoid without its bias; the routed
+ *           sum is scaled; the shared expert enters with weight one; an int4
+ *           nibble n stands for n - 8; weights are dequantised and then
+ *           multiplied and accumulated in f32).
+ *  [README] colibri README, "What's implemented" (the sigmoid noaux_tc router of
+ *           the DeepSeek-V3 kind with its scaling factor, and the shared expert).
  *  [MODELS] "Model support" doc, section 4.3 UniversalMoE (top-k, norm_topk_probs,
  *           sigmoid scoring, routing scale, shared expert, grouped routing in the
  *           deepseek_v3 style) and section 6.4 GLM-5.2.
