@@ -300,5 +300,9 @@ class Pool:
 
 
 def slot_view(base, slot_bytes: int, table, n_slots: int, gen=None, slot_gen=None) -> moe_slot_view:
-    """A view of caller-owned slots (generation tags optional: gen [E] and slot_gen [n_slots] uint32)."""
-    return moe_slot_view(ptr(base), slot_bytes, ptr(table), n_slots, ptr(gen), ptr(slot_gen), 0)
+    """A view of caller-owned slots (generation tags optional: gen [E] and slot_gen [n_slots] uint32).
+    The view stores raw addresses; it also holds references to the objects given, so that
+    a table built inline is not freed (and its memory reused) while the view is alive."""
+    v = moe_slot_view(ptr(base), slot_bytes, ptr(table), n_slots, ptr(gen), ptr(slot_gen), 0)
+    v._refs = (base, table, gen, slot_gen)
+    return v

@@ -257,3 +257,16 @@ def test_library_shares_torchs_hip_runtime():
     import ast
     libs = ast.literal_eval(out.stdout.strip().splitlines()[-1])
     assert len(libs) == 1, libs
+
+
+def test_slot_view_keeps_its_tensors_alive():
+    """A view holds references to the tensors whose addresses it stores: a table
+    built inline stays allocated (its address unchanged) while the view lives."""
+    import gc
+    import torch
+    base = torch.zeros(64, dtype=torch.uint8)
+    v = M.slot_view(base, 16, torch.arange(4, dtype=torch.int32), 4)
+    gc.collect()
+    table = v._refs[1]
+    assert v.table == table.data_ptr() and v.base == base.data_ptr() and v.n_slots == 4
+    assert table.tolist() == [0, 1, 2, 3]
