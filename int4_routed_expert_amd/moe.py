@@ -235,11 +235,13 @@ class Pool:
 
     def __init__(self, cfg: moe_cfg, n_layers: int, slots_per_layer: int, flags: int = 0):
         self.h = ctypes.c_void_p()
+        self._src = {}  # (layer, expert) -> registered host buffer, kept alive while the pool may copy from it
         _check(_lib.moe_pool_create(ctypes.byref(cfg), n_layers, slots_per_layer, flags, ctypes.byref(self.h)),
                "moe_pool_create")
 
     def register_host(self, layer: int, expert: int, src) -> None:
         _check(_lib.moe_pool_register_host(self.h, layer, expert, ptr(src)), "moe_pool_register_host")
+        self._src[(layer, expert)] = src
 
     def acquire(self, layer: int, idx_host, compute=None, side=None):
         """-> (moe_slot_view, n_miss); idx_host: int32 numpy array."""
@@ -291,6 +293,7 @@ class Pool:
         if self.h:
             _lib.moe_pool_destroy(self.h)
             self.h = ctypes.c_void_p()
+        self._src = {}
 
     def __del__(self):
         try:
