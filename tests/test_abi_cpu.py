@@ -270,3 +270,36 @@ def test_slot_view_keeps_its_tensors_alive():
     table = v._refs[1]
     assert v.table == table.data_ptr() and v.base == base.data_ptr() and v.n_slots == 4
     assert table.tolist() == [0, 1, 2, 3]
+
+
+def test_header_is_c11_and_links_from_c(tmp_path):
+    """include/moe.h compiles as strict C11 (-pedantic, warnings as errors) and a C
+    program links against libmoe.so and calls its host entry points."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    lib_dir = os.path.join(root, "int4_routed_expert_amd")
+    src = tmp_path / "abi_check.c"
+    src.write_text(r"""
+#include <stdio.h>
+#include "moe.h"
+int main(void) {
+  moe_cfg c = {0};
+  c.hidden = 6144; c.n_experts = 256; c.n_group = 8; c.topk_group = 4; c.top_k = 8;
+  c.moe_inter = 2048; c.shared_inter = 2048; c.group_size = 32; c.routed_scaling_factor = 2.5f;
+  c.norm_topk_prob = 1; c.mfma_min_tokens = 3; c.weight_format = MOE_WF_Q4_G32; c.act_int8 = 0;
+  printf("%d %lld\n", moe_validate_cfg(&c), (long long)moe_expert_bytes(&c, 2048));
+  c.top_k = 99;
+  printf("%d %s\n", moe_validate_cfg(&c), moe_status_string(moe_validate_cfg(&c)));
+  return 0;
+}
+""")
+    exe = tmp_path / "abi_check"
+    subprocess.check_call([gcc, "-std=c11", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(root, "include"),
+                           str(src), "-L", lib_dir, "-lmoe", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)])
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60, check=True).stdout.split("\n")
+    assert out[0] == "0 21233664"
+    assert out[1].startswith(f"{M.MOE_EINVAL} ")
