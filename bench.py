@@ -308,7 +308,12 @@ def bench_verify(args) -> int:
         M.moe_route(cfg, xb, dt, S, L["W"], L["bias"], idx[o], wt[o], ws, ws.numel())
         M.moe_ffn(cfg, xb, dt, S, idx[o], wt[o], views[j % len(layers)], L["shared"], y[o], ws, ws.numel())
 
-    tok_s, ms_per_step, steps, warm = run_graphs(step, args, nb)
+    def call_of(j):
+        L, b, o = layers[j % len(layers)], j % nb, j % n_out
+        return M.layer_call(cfg, x[b * S:(b + 1) * S], dt, S, L["W"], L["bias"], idx[o], wt[o],
+                            views[j % len(layers)], L["shared"], y[o], ws, ws.numel())
+
+    tok_s, ms_per_step, steps, warm = run_graphs(step, call_of if args.call == "layer" else None, args, nb)
     M.moe_profile_enable(True)
     M.moe_profile_report()
     for j in range(64):
@@ -345,7 +350,7 @@ def bench_verify(args) -> int:
           "dtype": "f32", "data": "synthetic",
           "config": {"workload": "glm52_moe_layer_verify_S4", "tokens_per_call": S, "bias": w.bias_recipe,
                      "quant": FORMAT_DESC[args.weight_format] + (", int8 activations" if args.act_int8 else ""),
-                     "layers_rotated": args.layers, "batches_rotated": nb, "launch": "hip graphs of 16 calls",
+                     "layers_rotated": args.layers, "batches_rotated": nb, "launch": launch_desc(args, "calls"),
                      "call": "moe_layer" if args.call == "layer" else "moe_route + moe_ffn"},
           "union_mean": float(U.mean()), "union_min": int(U.min()), "union_max": int(U.max()),
           "shared_fraction": float(np.mean(shared)), "selections_on_shared": float(np.mean(on_shared)),
@@ -358,16 +363,20 @@ def bench_verify(args) -> int:
     return 0
 
 
-def run_graphs(step, args, period_tokens):
-    """Captures HIP graphs of CHUNK steps over the rotation and times their replay."""
+def make_launchers(step, call_of, n_graphs: int, s):
+    """One launcher per group of CHUNK consecutive steps.  With call_of (each step
+    is one moe_layer call; call_of(j) gives its arguments) the group is a library
+    chain (moe_chain_create: one HIP graph owned by the library); otherwise a HIP
+    graph of the step's C-ABI calls captured by torch.  Returns (launchers, free)."""
     import torch
-    period = int(np.lcm(period_tokens, args.layers))
-    n_graphs = min((period + CHUNK - 1) // CHUNK, 64)
-    s = torch.cuda.Stream()
-    with torch.cuda.stream(s):
+    from int4_routed_expert_amd import moe as M
+    with torch.cuda.stream(s):  # one eager pass first: set-up work stays outside any graph
         for j in range(CHUNK):
             step(j)
     torch.cuda.synchronize()
+    if call_of is not None:
+        chains = [M.moe_chain_create([call_of(gi * CHUNK + j) for j in range(CHUNK)]) for gi in range(n_graphs)]
+        return [lambda ch=ch: M.moe_chain_launch(ch) for ch in chains], lambda: [M.moe_chain_destroy(c) for c in chains]
     graphs = []
     for gi in range(n_graphs):
         g = torch.cuda.CUDAGraph()
@@ -376,15 +385,32 @@ def run_graphs(step, args, period_tokens):
                 step(gi * CHUNK + j)
         graphs.append(g)
     torch.cuda.synchronize()
+    return [g.replay for g in graphs], lambda: None
+
+
+def launch_desc(args, unit: str) -> str:
+    if args.call == "layer":
+        return f"library chains (moe_chain) of {CHUNK} moe_layer {unit}"
+    return f"hip graphs of {CHUNK} {unit} (torch capture)"
+
+
+def run_graphs(step, call_of, args, period_tokens):
+    """Records the rotation in groups of CHUNK steps (make_launchers) and times their replay."""
+    import torch
+    period = int(np.lcm(period_tokens, args.layers))
+    n_graphs = min((period + CHUNK - 1) // CHUNK, 64)
+    s = torch.cuda.Stream()
+    launchers, free = make_launchers(step, call_of, n_graphs, s)
     steps, warm = timed_counts(args, n_graphs)
     for i in range(warm // CHUNK):
-        graphs[i % n_graphs].replay()
+        launchers[i % n_graphs]()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps // CHUNK):
-        graphs[i % n_graphs].replay()
+        launchers[i % n_graphs]()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+    free()
     log(f"graph replay: {el * 1e6 / steps:.2f} us/call over {steps} calls")
     return steps / el, el * 1e3 / steps, steps, warm
 
@@ -801,34 +827,31 @@ def main() -> int:
         M.moe_ffn(cfg, xs[t:t + 1], M.MOE_F32, 1, idx[o:o + 1], wt[o:o + 1], views[j % len(layers)], L["shared"],
                   y[o:o + 1], ws, ws.numel())
 
-    # ---- HIP graphs over the C-ABI calls ----------------------------------------
+    def call_of(j: int):
+        L = layers[j % len(layers)]
+        t = j % args.tokens
+        o = j % n_out
+        return M.layer_call(cfg, xs[t:t + 1], M.MOE_F32, 1, L["W"], L["bias"], idx[o:o + 1], wt[o:o + 1],
+                            views[j % len(layers)], L["shared"], y[o:o + 1], ws, ws.numel())
+
+    # ---- graphs over the C-ABI calls: library chains (moe_layer) or torch capture --------------
     period = int(np.lcm(args.tokens, args.layers))
     n_graphs = (period + CHUNK - 1) // CHUNK
     n_graphs = min(n_graphs, 64)
     s = torch.cuda.Stream()
-    graphs = []
-    with torch.cuda.stream(s):
-        for j in range(CHUNK):
-            step(j)
-    torch.cuda.synchronize()
-    for gi in range(n_graphs):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            for j in range(CHUNK):
-                step(gi * CHUNK + j)
-        graphs.append(g)
-    torch.cuda.synchronize()
-    log(f"captured {n_graphs} graphs x {CHUNK} steps")
+    launchers, free_launchers = make_launchers(step, call_of if args.call == "layer" else None, n_graphs, s)
+    log(f"recorded {n_graphs} graphs x {CHUNK} steps ({launch_desc(args, 'steps')})")
 
     steps, warm = timed_counts(args, n_graphs)
     for i in range(warm // CHUNK):
-        graphs[i % n_graphs].replay()
+        launchers[i % n_graphs]()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(steps // CHUNK):
-        graphs[i % n_graphs].replay()
+        launchers[i % n_graphs]()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
+    free_launchers()
     ms_per_step = elapsed * 1e3 / steps
     tok_s = steps / elapsed
     layer_bytes = 9 * sb  # 8 routed + 1 shared experts streamed per token
@@ -840,23 +863,21 @@ def main() -> int:
     # that its 9 experts (191 MB) stay in the 256 MB Infinity Cache --------------------------
     warm_us = None
     if args.call == "layer":
-        def warm_step(j: int) -> None:
+        def warm_call(j: int):
             L = layers[0]
             o = j % n_out
-            M.moe_layer(cfg, xs[0:1], M.MOE_F32, 1, L["W"], L["bias"], idx[o:o + 1], wt[o:o + 1], views[0], L["shared"],
-                        y[o:o + 1], ws, ws.numel())
-        gw = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gw, stream=s):
-            for j in range(CHUNK):
-                warm_step(j)
+            return M.layer_call(cfg, xs[0:1], M.MOE_F32, 1, L["W"], L["bias"], idx[o:o + 1], wt[o:o + 1], views[0],
+                                L["shared"], y[o:o + 1], ws, ws.numel())
+        gw = M.moe_chain_create([warm_call(j) for j in range(CHUNK)])
         for _ in range(8):
-            gw.replay()
+            M.moe_chain_launch(gw)
         torch.cuda.synchronize()
         tw = time.perf_counter()
         n_warm_rep = 64
         for _ in range(n_warm_rep):
-            gw.replay()
+            M.moe_chain_launch(gw)
         torch.cuda.synchronize()
+        M.moe_chain_destroy(gw)
         warm_us = (time.perf_counter() - tw) * 1e6 / (n_warm_rep * CHUNK)
         log(f"warm repeat (one token of one layer, experts cache-resident): {warm_us:.2f} us/step")
 
@@ -908,7 +929,7 @@ def main() -> int:
         "config": {"workload": "glm52_moe_layer_decode_S1", "hidden": H, "n_experts": E, "n_group": c.n_group,
                    "topk_group": c.topk_group, "top_k": k, "moe_inter": I, "shared_inter": c.shared_inter,
                    "quant": FORMAT_DESC[fmt] + (", int8 activations" if args.act_int8 else ""), "layers_rotated": args.layers, "tokens_rotated": args.tokens,
-                   "launch": "hip graphs of 16 steps",
+                   "launch": launch_desc(args, "steps"),
                    "call": "moe_layer" if args.call == "layer" else "moe_route + moe_ffn"},
         "effective_gbps": gbps,
         "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,

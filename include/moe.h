@@ -20,6 +20,8 @@
  *  [README] colibri README, "What's implemented" (the sigmoid noaux_tc router
  *           of the DeepSeek-V3 kind with its scaling factor, the batch union).
  *  [MODELS] "Model support" doc, 4.3 UniversalMoE (grouped routing) and 6.4.
+ *  [SCOUT]  "opus colibri scout" (the Colibri-vs-strata Metal audit): sections 1
+ *           and 5 (a whole decode window submitted as one command buffer).
  *
  * Conventions for every call below:
  *  - Tensor pointers are DEVICE pointers owned by the caller unless stated.
@@ -265,6 +267,62 @@ int moe_layer(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, con
 int moe_layer_noalloc(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_t S, const float *W_gate,
                       const float *bias, int32_t *idx, float *w, const moe_slot_view *experts, const void *shared,
                       float *y, void *stream);
+
+/* ---- recorded chains of layer calls: one library-owned HIP graph ----------------
+ * [SCOUT] section 1 "architecture side by side" and section 5 "where strata is
+ * ahead", item 1: the faster Metal design submits a whole decode window (every
+ * layer's router and MoE) as one command buffer, instead of one submission per
+ * layer or op.  Here that is a HIP graph: moe_chain_create records n moe_layer
+ * calls, in order, each with its own arguments, and instantiates them as one
+ * graph; moe_chain_launch enqueues the whole chain on a stream as a single graph
+ * launch.  [MODELS] "History" records a single-dispatch megakernel that was
+ * shelved at about 0.94x of the split kernels, and a one-launch kernel built for
+ * this layer measured slower too, so the chain keeps the split kernels and only
+ * removes the host's per-kernel submissions.
+ *
+ * moe_layer_call holds the arguments of one moe_layer call.  Everything in it is
+ * read at record time and kept by value: the configuration, S, the dtypes, every
+ * pointer, and the fields of the slot view.  The device memory behind those
+ * pointers is read at every launch.  So the caller writes new inputs into the
+ * same buffers between launches, and a slot pool's table updates (its device
+ * table and generation arrays) are seen by the next launch.  The output of one
+ * call may be the input of a later one (y of call i as x of call i + 1): calls
+ * run in recorded order.  The caller keeps every buffer alive, and at the same
+ * address, until moe_chain_destroy.
+ *
+ * moe_chain_create: every call is checked as moe_layer checks it before anything
+ * is recorded; the first failing call's status is returned (MOE_EINVAL also for
+ * n < 1, or while moe_profile_enable is on: kernel-stamped profiling events are
+ * not recorded in graphs).  HIP errors while recording or instantiating return
+ * MOE_EHIP.  On any error *out is NULL and nothing is enqueued.  The chain
+ * belongs to the device that is current at creation; the calls are recorded on
+ * a private stream (default priority) that is destroyed before return.
+ * moe_chain_launch: MOE_ENULL for a NULL chain, MOE_EINVAL if the current device
+ * is not the chain's; otherwise one graph launch on `stream`.  Results are
+ * bit-identical to the same moe_layer calls made one by one.  Launches of chains
+ * that share a workspace or output buffers must not overlap (different streams
+ * without ordering race, as the same moe_layer calls would).
+ * moe_chain_destroy: frees the graph (NULL is a no-op).  Launches already
+ * enqueued finish normally. */
+typedef struct moe_layer_call {
+  const moe_cfg *cfg;
+  const void *x;
+  int32_t x_dtype;
+  int32_t S;
+  const float *W_gate;
+  const float *bias;
+  int32_t *idx;
+  float *w;
+  const moe_slot_view *experts;
+  const void *shared;
+  float *y;
+  void *ws;
+  size_t ws_bytes;
+} moe_layer_call;
+typedef struct moe_chain moe_chain;
+int moe_chain_create(const moe_layer_call *calls, int32_t n, moe_chain **out);
+int moe_chain_launch(const moe_chain *chain, void *stream);
+void moe_chain_destroy(moe_chain *chain);
 
 /* ---- HBM expert-slot pool ([PORT] N3 and G3 status; [README] per-layer LRU) ----
  * One device slab of n_layers * slots_per_layer slots of moe_expert_bytes(cfg,

@@ -5,6 +5,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -560,6 +561,105 @@ int moe_layer_noalloc(const moe_cfg *c, const void *x, int32_t x_dtype, int32_t 
   if (p) return p;
   return layer_impl(c, x, x_dtype, S, W, bias, idx, w, ex, shared, y, ws, MOE_SCRATCH_BYTES, (hipStream_t)stream,
                     true);
+}
+
+}  // extern "C"
+
+// ---- recorded chains of layer calls ----------------------------------------------
+// The calls are recorded by stream capture on a private stream, so the graph
+// holds exactly the kernels (and kernel arguments) that the same moe_layer calls
+// would enqueue one by one.
+struct moe_chain {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int device = -1;
+};
+
+namespace moe {
+
+static int check_call(const moe_layer_call &c) {
+  if (!c.cfg) return MOE_ENULL;
+  RouteArgs r;
+  int v = route_args(c.cfg, c.x, c.x_dtype, c.S, c.W_gate, c.bias, c.idx, c.w, c.ws, c.ws_bytes, r);
+  if (v) return v;
+  FfnArgs f;
+  return ffn_args(c.cfg, c.x, c.x_dtype, c.S, c.idx, c.w, c.experts, c.shared, c.y, c.ws, c.ws_bytes, f);
+}
+
+}  // namespace moe
+
+extern "C" {
+
+int moe_chain_create(const moe_layer_call *calls, int32_t n, moe_chain **out) {
+  using namespace moe;
+  if (!out) return MOE_ENULL;
+  *out = nullptr;
+  if (n < 1) return MOE_EINVAL;
+  if (!calls) return MOE_ENULL;
+  if (prof_on()) return MOE_EINVAL;
+  for (int32_t i = 0; i < n; ++i) {
+    const int v = check_call(calls[i]);
+    if (v) return v;
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  hipStream_t s = nullptr;
+  e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+  if (e != hipSuccess) return hip_fail(e);
+  e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    hipStreamDestroy(s);
+    return hip_fail(e);
+  }
+  int v = MOE_OK;
+  for (int32_t i = 0; i < n && v == MOE_OK; ++i) {
+    const moe_layer_call &c = calls[i];
+    v = layer_impl(c.cfg, c.x, c.x_dtype, c.S, c.W_gate, c.bias, c.idx, c.w, c.experts, c.shared, c.y, c.ws,
+                   c.ws_bytes, s, false);
+  }
+  hipGraph_t g = nullptr;
+  const hipError_t ec = hipStreamEndCapture(s, &g);
+  hipStreamDestroy(s);
+  if (v != MOE_OK || ec != hipSuccess) {
+    if (g) hipGraphDestroy(g);
+    return v != MOE_OK ? v : hip_fail(ec);
+  }
+  hipGraphExec_t x = nullptr;
+  e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    hipGraphDestroy(g);
+    return hip_fail(e);
+  }
+  moe_chain *ch = new (std::nothrow) moe_chain;
+  if (!ch) {
+    hipGraphExecDestroy(x);
+    hipGraphDestroy(g);
+    return MOE_EINVAL;
+  }
+  ch->graph = g;
+  ch->exec = x;
+  ch->device = dev;
+  *out = ch;
+  return MOE_OK;
+}
+
+int moe_chain_launch(const moe_chain *chain, void *stream) {
+  using namespace moe;
+  if (!chain) return MOE_ENULL;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev != chain->device) return MOE_EINVAL;
+  e = hipGraphLaunch(chain->exec, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+void moe_chain_destroy(moe_chain *chain) {
+  if (!chain) return;
+  if (chain->exec) hipGraphExecDestroy(chain->exec);
+  if (chain->graph) hipGraphDestroy(chain->graph);
+  delete chain;
 }
 
 }  // extern "C"

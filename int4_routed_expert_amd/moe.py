@@ -44,6 +44,14 @@ class moe_slot_view(ctypes.Structure):
                 ("lease", ctypes.c_uint64)]
 
 
+class moe_layer_call(ctypes.Structure):
+    _fields_ = [("cfg", ctypes.POINTER(moe_cfg)), ("x", ctypes.c_void_p), ("x_dtype", ctypes.c_int32),
+                ("S", ctypes.c_int32), ("W_gate", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("idx", ctypes.c_void_p), ("w", ctypes.c_void_p), ("experts", ctypes.POINTER(moe_slot_view)),
+                ("shared", ctypes.c_void_p), ("y", ctypes.c_void_p), ("ws", ctypes.c_void_p),
+                ("ws_bytes", ctypes.c_size_t)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() (hipcc for gfx950)")
@@ -70,6 +78,9 @@ def _load():
         "moe_ffn": (ctypes.c_int, [cp, p, i32, i32, p, p, ctypes.POINTER(moe_slot_view), p, p, p, sz, p]),
         "moe_layer": (ctypes.c_int, [cp, p, i32, i32, p, p, p, p, ctypes.POINTER(moe_slot_view), p, p, p, sz, p]),
         "moe_layer_noalloc": (ctypes.c_int, [cp, p, i32, i32, p, p, p, p, ctypes.POINTER(moe_slot_view), p, p, p]),
+        "moe_chain_create": (ctypes.c_int, [ctypes.POINTER(moe_layer_call), i32, ctypes.POINTER(p)]),
+        "moe_chain_launch": (ctypes.c_int, [p, p]),
+        "moe_chain_destroy": (None, [p]),
         "moe_pool_create": (ctypes.c_int, [cp, i32, i32, i32, ctypes.POINTER(p)]),
         "moe_pool_destroy": (None, [p]),
         "moe_pool_register_host": (ctypes.c_int, [p, i32, i32, p]),
@@ -213,6 +224,30 @@ def moe_layer_noalloc(cfg: moe_cfg, x, x_dtype: int, S: int, W, bias, idx, w, vi
 
 
 MOE_SCRATCH_BYTES = 8 << 20  # the library's per-device workspace of moe_layer_noalloc
+
+
+def layer_call(cfg: moe_cfg, x, x_dtype: int, S: int, W, bias, idx, w, view: moe_slot_view, shared, y, ws,
+               ws_bytes: int) -> moe_layer_call:
+    """The arguments of one moe_layer call, for moe_chain_create (raw addresses; the struct keeps
+    references to the cfg and view it points to)."""
+    return moe_layer_call(ctypes.pointer(cfg), ptr(x), x_dtype, S, ptr(W), ptr(bias), ptr(idx), ptr(w),
+                          ctypes.pointer(view), ptr(shared), ptr(y), ptr(ws), ws_bytes)
+
+
+def moe_chain_create(calls) -> int:
+    """Records the moe_layer calls (a sequence of layer_call results) as one graph; returns the chain handle."""
+    arr = (moe_layer_call * len(calls))(*calls) if len(calls) else None
+    out = ctypes.c_void_p()
+    _check(_lib.moe_chain_create(arr, len(calls), ctypes.byref(out)), "moe_chain_create")
+    return out.value
+
+
+def moe_chain_launch(chain: int, stream=None) -> None:
+    _check(_lib.moe_chain_launch(chain, stream_handle(stream)), "moe_chain_launch")
+
+
+def moe_chain_destroy(chain: int | None) -> None:
+    _lib.moe_chain_destroy(chain)
 
 
 def moe_profile_enable(on: bool) -> None:

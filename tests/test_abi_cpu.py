@@ -236,6 +236,49 @@ def test_route_and_ffn_argument_errors_before_any_launch():
     assert F(cfg=noshared, shared=None, wsb=10) == M.MOE_EWORKSPACE
 
 
+def test_chain_argument_errors_before_any_recording():
+    """moe_chain_create checks every call before it records anything, so its errors need no GPU;
+    on any error the out handle is NULL."""
+    c = M.make_cfg(gen.TINY)
+    L = M.lib()
+    fake = 4096  # never dereferenced: every call below fails validation first
+    ws_need = M.moe_workspace_bytes(c, 1)
+    view = M.moe_slot_view(4096, M.moe_expert_bytes(c, 128), 4096, 16)
+
+    def call(**kw):
+        a = dict(cfg=c, x=fake, x_dtype=M.MOE_F32, S=1, W=fake, bias=fake, idx=fake, w=fake, view=view,
+                 shared=fake, y=fake, ws=fake, ws_bytes=ws_need)
+        a.update(kw)
+        return M.layer_call(a["cfg"], a["x"], a["x_dtype"], a["S"], a["W"], a["bias"], a["idx"], a["w"], a["view"],
+                            a["shared"], a["y"], a["ws"], a["ws_bytes"])
+
+    def create(calls, n=None):
+        arr = (M.moe_layer_call * len(calls))(*calls) if calls else None
+        out = ctypes.c_void_p(1234)
+        rc = L.moe_chain_create(arr, len(calls) if n is None else n, ctypes.byref(out))
+        assert out.value is None, "the handle must be NULL after an error"
+        return rc
+
+    assert create([]) == M.MOE_EINVAL
+    assert create([call()], n=0) == M.MOE_EINVAL
+    assert L.moe_chain_create(None, 1, ctypes.byref(ctypes.c_void_p())) == M.MOE_ENULL
+    assert L.moe_chain_create((M.moe_layer_call * 1)(call()), 1, None) == M.MOE_ENULL
+    nocfg = call()
+    nocfg.cfg = ctypes.POINTER(M.moe_cfg)()
+    assert create([nocfg]) == M.MOE_ENULL
+    bad = M.make_cfg(gen.TINY)
+    bad.n_group = 3
+    assert create([call(cfg=bad)]) == M.MOE_EINVAL
+    # the first failing call's status is returned, whichever position it has
+    assert create([call(y=None), call(x_dtype=9)]) == M.MOE_ENULL
+    assert create([call(x_dtype=9), call(y=None)]) == M.MOE_EDTYPE
+    assert create([call(S=4, x=None, ws_bytes=ws_need)]) == M.MOE_ENULL
+    assert create([call(S=4, ws_bytes=ws_need)]) == M.MOE_EWORKSPACE
+    assert create([call(), call(S=-2)]) == M.MOE_EINVAL
+    assert L.moe_chain_launch(None, None) == M.MOE_ENULL
+    M.moe_chain_destroy(None)  # a no-op
+
+
 def test_status_strings():
     for s in range(0, -8, -1):
         assert M.lib().moe_status_string(s)

@@ -1,8 +1,10 @@
 """The decode benchmark's launch configuration, checked against the oracle:
 GLM-5.2 shape, resident layers rotated step by step, one moe_layer call per
-step for one token, 16 steps captured per HIP graph with one workspace shared
-by all of them and each step writing its own rows of idx, w and y (as bench.py
-does, here with 2 layers and 32 tokens).  Every graph is replayed twice, with
+step for one token, 16 steps recorded per graph with one workspace shared by
+all of them and each step writing its own rows of idx, w and y (as bench.py
+does, here with 2 layers and 32 tokens).  The graphs are library chains
+(moe_chain_create, the bench's default) or HIP graphs captured by torch over
+the same calls (the bench's split-call mode uses those).  Every graph is replayed twice, with
 the outputs poisoned before the second replays; then every step's indices are
 exactly the oracle's, its weights within 1e-6 rsf and its output within the
 fp32 bar."""
@@ -23,7 +25,8 @@ N_LAYERS = 2
 N_TOKENS = 32
 
 
-def test_decode_graphs_of_sixteen_steps():
+@pytest.mark.parametrize("mode", ["chain", "torch_graph"])
+def test_decode_graphs_of_sixteen_steps(mode):
     w = gen.WORKLOADS["decode"]
     c = w.cfg
     layers = [DeviceLayer(w, layer=l) for l in range(N_LAYERS)]
@@ -49,24 +52,36 @@ def test_decode_graphs_of_sixteen_steps():
         for j in range(CHUNK):
             step(j)
     torch.cuda.synchronize()
-    graphs = []
+    launchers, chains = [], []
     for gi in range(period // CHUNK):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            for j in range(CHUNK):
-                step(gi * CHUNK + j)
-        graphs.append(g)
+        if mode == "chain":
+            calls = []
+            for j in range(gi * CHUNK, (gi + 1) * CHUNK):
+                L, t = layers[j % N_LAYERS], j % N_TOKENS
+                calls.append(M.layer_call(cfg, xs[t:t + 1], M.MOE_F32, 1, L.W, L.bias, idx[t:t + 1], wt[t:t + 1],
+                                          views[j % N_LAYERS], L.shared, y[t:t + 1], ws, ws.numel()))
+            ch = M.moe_chain_create(calls)
+            chains.append(ch)
+            launchers.append(lambda ch=ch: M.moe_chain_launch(ch, s))
+        else:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for j in range(CHUNK):
+                    step(gi * CHUNK + j)
+            launchers.append(g.replay)
     torch.cuda.synchronize()
-    for g in graphs:
-        g.replay()
+    for launch in launchers:
+        launch()
     torch.cuda.synchronize()
     idx.fill_(-7)
     wt.fill_(float("nan"))
     y.fill_(float("nan"))
     torch.cuda.synchronize()
-    for g in graphs:
-        g.replay()
+    for launch in launchers:
+        launch()
     torch.cuda.synchronize()
+    for ch in chains:
+        M.moe_chain_destroy(ch)
     gi_, gw, gy = idx.cpu().numpy(), wt.cpu().numpy(), y.cpu().numpy()
     worst = 0.0
     for j in range(period):
@@ -81,4 +96,4 @@ def test_decode_graphs_of_sixteen_steps():
         err = max_rel_err(gy[t:t + 1], O.moe_ffn(c, x1, ridx, rw, experts))
         worst = max(worst, err)
         assert err <= TOL_FP32, (j, err)
-    say(f"{period} steps in {len(graphs)} graphs of {CHUNK}: worst max rel err {worst:.3e}")
+    say(f"{mode}: {period} steps in {len(launchers)} graphs of {CHUNK}: worst max rel err {worst:.3e}")
