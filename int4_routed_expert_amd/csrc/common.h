@@ -107,6 +107,7 @@ struct FfnArgs {
   uint64_t *eptr;  // [k] routed experts' packed weights (0: not resident), resolved by the gate/up kernel
   int32_t n_blk;   // row blocks of the down kernel
   int32_t tb;      // down tiles (8 rows) per row block
+  int32_t dn_slots;  // two to four tokens: (token, expert) h rows the down kernel may hold in LDS per workgroup
   int32_t n_cu;    // compute units of the device
   // one-token layer: the gate/up kernel selects the experts itself from the
   // router's scores and keys (then idx and w above are written, not read)

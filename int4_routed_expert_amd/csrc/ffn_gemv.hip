@@ -596,114 +596,241 @@ __global__ __launch_bounds__(kGuSmallWaves * 64) void k_gateup_small(FfnArgs a) 
   if (lane < c) stg<float>(a.h + prow, hout);
 }
 
-// Two to four tokens, down projection: the (expert, token, tile) units stream
-// through the waves with the pair's h in limb form held in registers (reloaded
-// only when the (expert, token) pair changes), and each unit's 8 row dots are
-// stored as per-(token, rank) partial rows; k_combine then adds them in route
-// order with the shared expert.  Unit order: for each unique expert u
-// (ascending, then the shared expert with every token) blocks of B tiles,
-// each block once for every token of u, so a tile that several tokens need is
-// requested again by the same or the next wave right after.  Each wave takes
-// an equal share of the units, with two tiles in flight while one is computed
-// (measured faster than holding every token's limbs and reading each tile
-// once, which leaves room for fewer tiles in flight).  The per-unit arithmetic
-// is the one-token kernel's.
+// Two to four tokens, down projection: (expert, token, tile) units stream
+// through the waves, and each unit's 8 row dots are stored as per-(token, rank)
+// partial rows; k_combine then adds them in route order with the shared expert.
+// Each wave takes an equal share of the units, with two tiles in flight while
+// one is computed; the per-unit arithmetic is the one-token kernel's.
+//   HLDS: units in tile order, the expert's tokens innermost, so the tokens that
+//   share a tile request it back to back from the same wave (the repeats are
+//   served by the caches instead of being fetched again); the h rows of the
+//   (token, expert) pairs that the workgroup's units touch are converted to limbs
+//   once, into LDS (at most dn_slots pairs; a pair beyond that is converted in
+//   registers when it changes, as below).
+//   Otherwise: for each unique expert, blocks of B tiles, each block once for
+//   every token of the expert, with the pair's h converted to limbs in registers
+//   whenever the pair changes.
+// Unique experts ascend, then the shared expert with every token.
 constexpr int kDnSmallWaves = 8;
-template <int NGD, int WF>
+template <int NGD, int WF, bool HLDS>
 __global__ __launch_bounds__(kDnSmallWaves * 64) void k_down_small(FfnArgs a) {
   __shared__ SmallPlan plan;
   __shared__ const uint8_t *s_ptr[kSmallS * kMaxK + 1];
   __shared__ int seg_start[kSmallS * kMaxK + 2];  // first unit of unique expert u (U: shared); [U + 1]: all
+  __shared__ int s_slot0[kSmallS * kMaxK + 1];    // HLDS: LDS slot of unique expert u's first token (-1: none)
+  __shared__ int s_nslots;
+  extern __shared__ uint32_t hl[];  // HLDS: [slot][Imax/32][24] limbs, then [slot][Imax/32] factors
   build_small_plan(a, plan, a.idx);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int U = plan.U, Imax = max(a.I, a.Is), nt = a.H / kDnRows;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwb = blockDim.x >> 6;
+  const int U = plan.U, Imax = max(a.I, a.Is), nt = a.H / kDnRows, ngm = Imax / kGroup;
   const int B = (nt % 16 == 0) ? 16 : 4;  // tiles per block (nt is a multiple of 4)
+  auto ntok_of = [&](int u) { return u == U ? (a.Is > 0 ? a.S : 0) : plan.ntok[u]; };
   if (threadIdx.x == 0) {
     int start = 0;
     for (int u = 0; u <= U; ++u) {
       seg_start[u] = start;
-      start += (u == U ? (a.Is > 0 ? a.S : 0) : plan.ntok[u]) * nt;
+      start += ntok_of(u) * nt;
     }
     seg_start[U + 1] = start;
   }
   if ((int)threadIdx.x < U) s_ptr[threadIdx.x] = expert_ptr(a, plan.uniq[threadIdx.x]);
   if ((int)threadIdx.x == U) s_ptr[U] = a.shared;
   __syncthreads();
-  const int W = gridDim.x * (blockDim.x >> 6), wid = blockIdx.x * (blockDim.x >> 6) + wave;
+  const int W = gridDim.x * nwb, wid = blockIdx.x * nwb + wave;
   const long P = seg_start[U + 1];
-  const int p0 = (int)(wid * P / W), n = (int)((wid + 1) * P / W) - p0;
-  if (n <= 0) return;
-  struct Unit {
-    int pair, t, inter;
-    bool valid;
-    const uint8_t *dn;
-  };
-  int lc = 0;  // unique expert of the last unit requested (a wave's units increase)
-  auto unit_of = [&](int i) {
-    const int p = p0 + min(i, n - 1);
-    while (p >= seg_start[lc + 1]) ++lc;
-    const int u = lc, ntu = u == U ? a.S : plan.ntok[u], q = p - seg_start[u];
-    const int blk = q / (B * ntu), r = q - blk * B * ntu, tt = r / B;
-    Unit un;
-    un.t = blk * B + (r - tt * B);
-    un.pair = u == U ? tt * (a.k + 1) + a.k : plan.pair[u][tt];
-    const uint8_t *ex = uniform_ptr(s_ptr[u]);
-    un.valid = ex != nullptr;
-    un.inter = (u == U && un.valid) ? a.Is : a.I;
-    un.dn = uniform_ptr((un.valid ? ex : a.base) + down_offset(a.H, un.inter, WF));
-    return un;
-  };
-  DnTile<NGD, WF> q0, q1;
-  Unit u0 = unit_of(0), u1 = unit_of(1);
-  dn_tile_load(q0, u0.dn, u0.inter, u0.t, u0.t + 1, lane);
-  dn_tile_load(q1, u1.dn, u1.inter, u1.t, u1.t + 1, lane);
+  float *hf = (float *)(hl + (size_t)max(a.dn_slots, 0) * ngm * 24);
+  auto pair_of = [&](int u, int tt) { return u == U ? tt * (a.k + 1) + a.k : plan.pair[u][tt]; };
+  if constexpr (HLDS) {
+    // LDS slots for the pairs of the unique experts whose units meet this
+    // workgroup's share
+    if (threadIdx.x == 0) {
+      const long q0 = (long)blockIdx.x * nwb * P / W, q1 = (long)(blockIdx.x + 1) * nwb * P / W;
+      int slots = 0;
+      for (int u = 0; u <= U; ++u) {
+        const int ntu = ntok_of(u);
+        const bool meets = ntu > 0 && seg_start[u] < q1 && seg_start[u + 1] > q0;
+        if (meets && slots + ntu <= a.dn_slots) {
+          s_slot0[u] = slots;
+          slots += ntu;
+        } else {
+          s_slot0[u] = -1;
+        }
+      }
+      s_nslots = slots;
+    }
+    __syncthreads();
+  }
   Limbs hv[NGD];
   int hp = -1;  // pair whose h limbs are in hv
-  auto finish = [&](const DnTile<NGD, WF> &b, const Unit &uu) {
-    const int ngi = uu.inter / kGroup;
-    if (uu.pair != hp) {
-      hp = uu.pair;
+  // h limbs of a pair: from LDS, or converted in registers (only when the pair changes)
+  auto stage_h = [&](int pair, int slot, int ngi) {
+    if (pair == hp) return;
+    hp = pair;
 #pragma unroll
-      for (int g2 = 0; g2 < NGD; ++g2) {  // lanes past the last group repeat it with a zero factor
-        const int g = min(lane + 64 * g2, ngi - 1);
+    for (int g2 = 0; g2 < NGD; ++g2) {  // lanes past the last group repeat it with a zero factor
+      const int g = min(lane + 64 * g2, ngi - 1);
+      if (HLDS && slot >= 0) {
+        const size_t i = (size_t)slot * ngm + g;
+        load_limbs_lds(hl + i * 24, hf + i, hv[g2]);
+      } else {
         float v[32];
-        load_act32(a, false, (size_t)uu.pair * Imax + (size_t)g * kGroup, v);
+        load_act32(a, false, (size_t)pair * Imax + (size_t)g * kGroup, v);
         to_limbs_wf<WF>(v, hv[g2]);
-        hv[g2].f *= act_scale(a, false, uu.pair);
-        if (lane + 64 * g2 >= ngi) hv[g2].f = 0.f;
+        hv[g2].f *= act_scale(a, false, pair);
       }
+      if (lane + 64 * g2 >= ngi) hv[g2].f = 0.f;
     }
+  };
+  auto dots_out = [&](const DnTile<NGD, WF> &b, int pair, int t, bool valid) {
     float acc[kDnRows];
     dn_tile_dots(b, hv, acc);
     if (lane == 63) {
       const float nan = __builtin_nanf("");
-      float4 *d = (float4 *)(a.part + (size_t)uu.pair * a.H + (size_t)uu.t * kDnRows);
-      stg<float4>(d, uu.valid ? make_float4(acc[0], acc[1], acc[2], acc[3]) : make_float4(nan, nan, nan, nan));
-      stg<float4>(d + 1, uu.valid ? make_float4(acc[4], acc[5], acc[6], acc[7]) : make_float4(nan, nan, nan, nan));
+      float4 *d = (float4 *)(a.part + (size_t)pair * a.H + (size_t)t * kDnRows);
+      stg<float4>(d, valid ? make_float4(acc[0], acc[1], acc[2], acc[3]) : make_float4(nan, nan, nan, nan));
+      stg<float4>(d + 1, valid ? make_float4(acc[4], acc[5], acc[6], acc[7]) : make_float4(nan, nan, nan, nan));
     }
   };
-  if constexpr (NGD == 1 && WF != kWfQ8Row) {  // three tiles: two in flight while one is computed
-    DnTile<NGD, WF> q2;
-    Unit u2;
-    for (int i = 0; i < n; i += 3) {
-      u2 = unit_of(i + 2);
-      dn_tile_load(q2, u2.dn, u2.inter, u2.t, u2.t + 1, lane);
-      finish(q0, u0);
-      u0 = unit_of(i + 3);
-      dn_tile_load(q0, u0.dn, u0.inter, u0.t, u0.t + 1, lane);
-      if (i + 1 < n) finish(q1, u1);
-      u1 = unit_of(i + 4);
-      dn_tile_load(q1, u1.dn, u1.inter, u1.t, u1.t + 1, lane);
-      if (i + 2 < n) finish(q2, u2);
+  const int p0 = (int)(wid * P / W), n = (int)((wid + 1) * P / W) - p0;
+  int lc = 0;  // unique expert of the last unit taken (a wave's units increase)
+  if constexpr (HLDS) {
+    // The wave's units, in tile order, grouped by tile: each tile is loaded once
+    // and its tokens (those in this wave's share) are computed one after another.
+    struct TileW {
+      int u, t, tt0, cnt, inter;
+      bool valid;
+      const uint8_t *dn;
+    };
+    int cur = p0;
+    const int end = p0 + max(n, 0);
+    TileW last{};
+    auto next_tile = [&]() {
+      if (cur >= end) {  // past the share: repeat the last tile (the load stays unconditional), compute nothing
+        TileW r = last;
+        r.cnt = 0;
+        return r;
+      }
+      while (cur >= seg_start[lc + 1]) ++lc;
+      TileW r;
+      r.u = lc;
+      const int ntu = ntok_of(lc), q = cur - seg_start[lc];
+      r.t = q / ntu;
+      r.tt0 = q - r.t * ntu;
+      r.cnt = min(ntu - r.tt0, end - cur);
+      cur += r.cnt;
+      const uint8_t *ex = uniform_ptr(s_ptr[lc]);
+      r.valid = ex != nullptr;
+      r.inter = (lc == U && r.valid) ? a.Is : a.I;
+      r.dn = uniform_ptr((r.valid ? ex : a.base) + down_offset(a.H, r.inter, WF));
+      last = r;
+      return r;
+    };
+    // the first two tiles are requested before the workgroup stages h
+    DnTile<NGD, WF> q0, q1, q2;
+    TileW w0{}, w1{}, w2{};
+    if (n > 0) {
+      w0 = next_tile();
+      dn_tile_load(q0, w0.dn, w0.inter, w0.t, w0.t + 1, lane);
+      w1 = next_tile();
+      dn_tile_load(q1, w1.dn, w1.inter, w1.t, w1.t + 1, lane);
     }
-  } else {  // wider tiles (inter > 2048, or int8 weights): two, to stay within the register file
-    for (int i = 0; i < n; i += 2) {
-      finish(q0, u0);
-      u0 = unit_of(i + 2);
-      dn_tile_load(q0, u0.dn, u0.inter, u0.t, u0.t + 1, lane);
-      if (i + 1 < n) finish(q1, u1);
-      u1 = unit_of(i + 3);
-      dn_tile_load(q1, u1.dn, u1.inter, u1.t, u1.t + 1, lane);
+    for (int i = threadIdx.x; i < s_nslots * ngm; i += blockDim.x) {
+      const int slot = i / ngm, g = i - slot * ngm;
+      int u = 0;
+      while (s_slot0[u] < 0 || slot >= s_slot0[u] + ntok_of(u)) ++u;
+      const int pair = pair_of(u, slot - s_slot0[u]);
+      if (g * kGroup < (u == U ? a.Is : a.I)) {
+        float v[32];
+        load_act32(a, false, (size_t)pair * Imax + (size_t)g * kGroup, v);
+        Limbs L;
+        to_limbs_wf<WF>(v, L);
+        L.f *= act_scale(a, false, pair);
+        store_limbs(hl + (size_t)i * 24, hf + i, L);
+      }
+    }
+    __syncthreads();
+    if (n <= 0) return;
+    auto compute = [&](const DnTile<NGD, WF> &b, const TileW &tw) {
+      for (int j = 0; j < tw.cnt; ++j) {
+        const int tt = tw.tt0 + j;
+        stage_h(pair_of(tw.u, tt), s_slot0[tw.u] < 0 ? -1 : s_slot0[tw.u] + tt, tw.inter / kGroup);
+        dots_out(b, pair_of(tw.u, tt), tw.t, tw.valid);
+      }
+    };
+    if constexpr (NGD == 1 && WF != kWfQ8Row) {  // three tiles: two in flight while one is computed
+      while (w0.cnt > 0) {
+        w2 = next_tile();
+        dn_tile_load(q2, w2.dn, w2.inter, w2.t, w2.t + 1, lane);
+        compute(q0, w0);
+        w0 = next_tile();
+        dn_tile_load(q0, w0.dn, w0.inter, w0.t, w0.t + 1, lane);
+        compute(q1, w1);
+        w1 = next_tile();
+        dn_tile_load(q1, w1.dn, w1.inter, w1.t, w1.t + 1, lane);
+        compute(q2, w2);
+      }
+    } else {  // wider tiles: two, to stay within the register file
+      while (w0.cnt > 0) {
+        compute(q0, w0);
+        w0 = next_tile();
+        dn_tile_load(q0, w0.dn, w0.inter, w0.t, w0.t + 1, lane);
+        compute(q1, w1);
+        w1 = next_tile();
+        dn_tile_load(q1, w1.dn, w1.inter, w1.t, w1.t + 1, lane);
+      }
+    }
+  } else {
+    if (n <= 0) return;
+    struct Unit {
+      int pair, t, inter;
+      bool valid;
+      const uint8_t *dn;
+    };
+    auto unit_of = [&](int i) {
+      const int p = p0 + min(i, n - 1);
+      while (p >= seg_start[lc + 1]) ++lc;
+      const int u = lc, ntu = ntok_of(u), q = p - seg_start[u];
+      const int blk = q / (B * ntu), r = q - blk * B * ntu, tt = r / B;
+      Unit un;
+      un.t = blk * B + (r - tt * B);
+      un.pair = pair_of(u, tt);
+      const uint8_t *ex = uniform_ptr(s_ptr[u]);
+      un.valid = ex != nullptr;
+      un.inter = (u == U && un.valid) ? a.Is : a.I;
+      un.dn = uniform_ptr((un.valid ? ex : a.base) + down_offset(a.H, un.inter, WF));
+      return un;
+    };
+    auto finish = [&](const DnTile<NGD, WF> &b, const Unit &uu) {
+      stage_h(uu.pair, -1, uu.inter / kGroup);
+      dots_out(b, uu.pair, uu.t, uu.valid);
+    };
+    DnTile<NGD, WF> q0, q1;
+    Unit u0 = unit_of(0), u1 = unit_of(1);
+    dn_tile_load(q0, u0.dn, u0.inter, u0.t, u0.t + 1, lane);
+    dn_tile_load(q1, u1.dn, u1.inter, u1.t, u1.t + 1, lane);
+    if constexpr (NGD == 1 && WF != kWfQ8Row) {  // three tiles: two in flight while one is computed
+      DnTile<NGD, WF> q2;
+      Unit u2;
+      for (int i = 0; i < n; i += 3) {
+        u2 = unit_of(i + 2);
+        dn_tile_load(q2, u2.dn, u2.inter, u2.t, u2.t + 1, lane);
+        finish(q0, u0);
+        u0 = unit_of(i + 3);
+        dn_tile_load(q0, u0.dn, u0.inter, u0.t, u0.t + 1, lane);
+        if (i + 1 < n) finish(q1, u1);
+        u1 = unit_of(i + 4);
+        dn_tile_load(q1, u1.dn, u1.inter, u1.t, u1.t + 1, lane);
+        if (i + 2 < n) finish(q2, u2);
+      }
+    } else {  // wider tiles (inter > 2048, or int8 weights): two, to stay within the register file
+      for (int i = 0; i < n; i += 2) {
+        finish(q0, u0);
+        u0 = unit_of(i + 2);
+        dn_tile_load(q0, u0.dn, u0.inter, u0.t, u0.t + 1, lane);
+        if (i + 1 < n) finish(q1, u1);
+        u1 = unit_of(i + 3);
+        dn_tile_load(q1, u1.dn, u1.inter, u1.t, u1.t + 1, lane);
+      }
     }
   }
 }
@@ -1140,6 +1267,22 @@ hipError_t launch_quant_h(const FfnArgs &a, hipStream_t st) {
     case 3: MOE_LAUNCH((KERNEL<3, WFV __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;   \
     default: MOE_LAUNCH((KERNEL<4, WFV __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, a); break;  \
   }
+#define MOE_NG_CASES_ARGS(ARGS, NG_, WFV, KERNEL, GRID, BLOCK, LDS, ST, ...)                              \
+  switch (NG_) {                                                                                         \
+    case 1: MOE_LAUNCH((KERNEL<1, WFV __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, ARGS); break;   \
+    case 2: MOE_LAUNCH((KERNEL<2, WFV __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, ARGS); break;   \
+    case 3: MOE_LAUNCH((KERNEL<3, WFV __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, ARGS); break;   \
+    default: MOE_LAUNCH((KERNEL<4, WFV __VA_OPT__(, ) __VA_ARGS__>), GRID, BLOCK, LDS, ST, ARGS); break;  \
+  }
+#define MOE_DISPATCH_NG_ARGS(ARGS, ng, KERNEL, GRID, BLOCK, LDS, ST, ...)                                 \
+  do {                                                                                                   \
+    const int ng_ = (ng);                                                                                \
+    switch ((ARGS).wf) {                                                                                 \
+      case kWfQ4Row: MOE_NG_CASES_ARGS(ARGS, ng_, kWfQ4Row, KERNEL, GRID, BLOCK, LDS, ST, __VA_ARGS__); break; \
+      case kWfQ8Row: MOE_NG_CASES_ARGS(ARGS, ng_, kWfQ8Row, KERNEL, GRID, BLOCK, LDS, ST, __VA_ARGS__); break; \
+      default: MOE_NG_CASES_ARGS(ARGS, ng_, kWfQ4G32, KERNEL, GRID, BLOCK, LDS, ST, __VA_ARGS__); break;        \
+    }                                                                                                    \
+  } while (0)
 #define MOE_DISPATCH_NG(ng, KERNEL, GRID, BLOCK, LDS, ST, ...)                                       \
   do {                                                                                               \
     const int ng_ = (ng);                                                                            \
@@ -1207,7 +1350,20 @@ hipError_t launch_ffn_decode(const FfnArgs &a, hipStream_t st) {
   {
     ProfScope ps("down_small", st);
     const dim3 g2((unsigned)a.n_cu), b2(kDnSmallWaves * 64);
-    MOE_DISPATCH_NG(ceil_groups(Imax), k_down_small, g2, b2, 0, st);
+    // (token, expert) pairs a workgroup's share of the units can meet: the share
+    // spans at most ceil(share / nt) + 1 unique experts, each with at most S tokens
+    const long nt = a.H / kDnRows, units_max = (long)a.S * (a.k + 1) * nt;
+    const long share = (units_max + a.n_cu - 1) / a.n_cu + 1;
+    FfnArgs b = a;
+    b.dn_slots = (int)std::min<long>((long)a.S * ((share + nt - 1) / nt + 1), (long)a.S * (a.k + 1));
+    const size_t hlds = (size_t)b.dn_slots * (Imax / kGroup) * 25 * sizeof(uint32_t);
+    // one group of h per lane (I <= 2048): wider rows leave too few registers for the tile ring
+    if (hlds <= 64 * 1024 && ceil_groups(Imax) == 1) {
+      MOE_DISPATCH_NG_ARGS(b, ceil_groups(Imax), k_down_small, g2, b2, hlds, st, true);
+    } else {
+      b.dn_slots = 0;
+      MOE_DISPATCH_NG_ARGS(b, ceil_groups(Imax), k_down_small, g2, b2, 0, st, false);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
