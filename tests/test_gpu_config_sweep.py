@@ -51,6 +51,13 @@ CASES = {
     "int8_q4g32_k16_S40_mfma": (256, 128, 8, 4, 16, 96, 64, 1, 2.5, 0, 1, 40, 2, "f32"),
     "int8_q8row_noshared_S12_mfma": (288, 32, 4, 2, 4, 96, 0, 1, 2.5, 2, 1, 12, 3, "f32"),
     "int8_q4row_norm0_S1": (256, 64, 8, 4, 8, 64, 64, 0, 1.5, 1, 1, 1, 3, "f32"),
+    # two to four tokens: the down kernel's h rows as limbs in LDS (I <= 2048) with shared rows narrower or wider
+    # than the routed ones, int8 weights, int8 activations; and wider rows (the register path)
+    "shared_narrow_S4": (512, 32, 4, 2, 4, 320, 192, 1, 2.5, 0, 0, 4, 3, "f32"),
+    "shared_wide_S4": (256, 32, 4, 2, 4, 64, 160, 1, 2.5, 0, 0, 4, 3, "f32"),
+    "q8row_S3": (256, 64, 8, 4, 8, 128, 64, 1, 2.5, 2, 0, 3, 3, "f32"),
+    "int8_q4g32_S2": (256, 64, 8, 4, 8, 128, 128, 1, 2.5, 0, 1, 2, 3, "f32"),
+    "i4096_S3": (1024, 16, 4, 2, 4, 4096, 2560, 1, 2.5, 0, 0, 3, 3, "f32"),
 }
 
 

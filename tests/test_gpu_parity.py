@@ -432,12 +432,13 @@ def test_invalid_idx_poisons_only_its_token(tiny, S, mode):
 
 
 def test_largest_shapes():
-    """H = I = Is = 8192 (the largest supported), small and large-batch paths."""
+    """H = I = Is = 8192 (the largest supported): one token, three tokens (the few-token kernels with h
+    converted in registers) and the large-batch path."""
     cfg = gen.LayerConfig(hidden=8192, n_experts=8, n_group=2, topk_group=1, top_k=2, moe_inter=8192,
                           shared_inter=8192)
     w = gen.Workload("max", cfg, tokens=5, seed=21)
     dl = DeviceLayer(w, mfma_min_tokens=0)
-    for S in (1, 5):
+    for S in (1, 3, 5):
         x = gen.tokens(w.with_(tokens=S), step=S)
         idx, wt, y = run_gpu(dl, x)
         ridx, rw = check_route(dl, x, idx, wt)
