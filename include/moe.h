@@ -294,7 +294,8 @@ int moe_layer_noalloc(const moe_cfg *cfg, const void *x, int32_t x_dtype, int32_
  * is recorded; the first failing call's status is returned (MOE_EINVAL also for
  * n < 1, or while moe_profile_enable is on: kernel-stamped profiling events are
  * not recorded in graphs).  HIP errors while recording or instantiating return
- * MOE_EHIP.  On any error *out is NULL and nothing is enqueued.  The chain
+ * MOE_EHIP; MOE_EINVAL if the host cannot allocate the chain's record.  On any
+ * error *out is NULL and nothing is enqueued.  The chain
  * belongs to the device that is current at creation; the calls are recorded on
  * a private stream (default priority) that is destroyed before return.
  * moe_chain_launch: MOE_ENULL for a NULL chain, MOE_EINVAL if the current device
