@@ -226,6 +226,64 @@ def moe_layer_noalloc(cfg: moe_cfg, x, x_dtype: int, S: int, W, bias, idx, w, vi
 MOE_SCRATCH_BYTES = 8 << 20  # the library's per-device workspace of moe_layer_noalloc
 
 
+def _x_dtype(x, cfg: moe_cfg) -> int:
+    """dtype code of the activations x, which must be a contiguous [S, hidden] fp32 or bf16 tensor."""
+    import torch
+    if x.dim() != 2 or x.shape[1] != cfg.hidden or not x.is_contiguous():
+        raise ValueError(f"x must be a contiguous [S, {cfg.hidden}] tensor, not {tuple(x.shape)} "
+                         f"with strides {tuple(x.stride())}")
+    if x.dtype == torch.float32:
+        return MOE_F32
+    if x.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise ValueError(f"x must be float32 or bfloat16, not {x.dtype}")
+
+
+def _check_routing(idx, w, S: int, cfg: moe_cfg) -> None:
+    import torch
+    for name, t, dtype in (("idx", idx, torch.int32), ("w", w, torch.float32)):
+        if tuple(t.shape) != (S, cfg.top_k) or t.dtype != dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [{S}, {cfg.top_k}] {dtype} tensor")
+
+
+def route(x, W, bias, cfg: moe_cfg, ws=None, stream=None):
+    """(idx [S, k] int32, w [S, k] fp32) for the tokens x ([S, H] fp32 or bf16 device tensor): moe_route with
+    its outputs (and, when ws is None, an initialised workspace) allocated on x's device."""
+    import torch
+    dt = _x_dtype(x, cfg)
+    S = x.shape[0]
+    ws = workspace(cfg, S, device=x.device, stream=stream) if ws is None else ws
+    idx = torch.empty((S, cfg.top_k), dtype=torch.int32, device=x.device)
+    w = torch.empty((S, cfg.top_k), dtype=torch.float32, device=x.device)
+    moe_route(cfg, x, dt, S, W, bias, idx, w, ws, ws.numel(), stream)
+    return idx, w
+
+
+def ffn(x, idx, w, view: moe_slot_view, shared, cfg: moe_cfg, ws=None, stream=None):
+    """y [S, H] fp32: moe_ffn with its output (and, when ws is None, a workspace) allocated on x's device."""
+    import torch
+    dt = _x_dtype(x, cfg)
+    S = x.shape[0]
+    _check_routing(idx, w, S, cfg)
+    ws = workspace(cfg, S, device=x.device, stream=stream) if ws is None else ws
+    y = torch.empty((S, cfg.hidden), dtype=torch.float32, device=x.device)
+    moe_ffn(cfg, x, dt, S, idx, w, view, shared, y, ws, ws.numel(), stream)
+    return y
+
+
+def layer(x, W, bias, view: moe_slot_view, shared, cfg: moe_cfg, ws=None, stream=None):
+    """(idx, w, y): moe_layer with its outputs (and, when ws is None, a workspace) allocated on x's device."""
+    import torch
+    dt = _x_dtype(x, cfg)
+    S = x.shape[0]
+    ws = workspace(cfg, S, device=x.device, stream=stream) if ws is None else ws
+    idx = torch.empty((S, cfg.top_k), dtype=torch.int32, device=x.device)
+    w = torch.empty((S, cfg.top_k), dtype=torch.float32, device=x.device)
+    y = torch.empty((S, cfg.hidden), dtype=torch.float32, device=x.device)
+    moe_layer(cfg, x, dt, S, W, bias, idx, w, view, shared, y, ws, ws.numel(), stream)
+    return idx, w, y
+
+
 def layer_call(cfg: moe_cfg, x, x_dtype: int, S: int, W, bias, idx, w, view: moe_slot_view, shared, y, ws,
                ws_bytes: int) -> moe_layer_call:
     """The arguments of one moe_layer call, for moe_chain_create (raw addresses; the struct keeps

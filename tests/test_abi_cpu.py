@@ -346,3 +346,25 @@ int main(void) {
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60, check=True).stdout.split("\n")
     assert out[0] == "0 21233664"
     assert out[1].startswith(f"{M.MOE_EINVAL} ")
+
+
+def test_allocating_calls_check_shapes_first():
+    """M.route / M.ffn / M.layer refuse activations of the wrong dtype, width or layout, and routing tensors of
+    the wrong shape, before anything is allocated or launched (so these run without a GPU)."""
+    import torch
+    c = M.make_cfg(gen.TINY)
+    H, k = c.hidden, c.top_k
+    view = M.moe_slot_view(4096, M.moe_expert_bytes(c, 128), 4096, 16)
+    bad_x = [torch.zeros((2, H), dtype=torch.float64), torch.zeros((2, H - 32)), torch.zeros((2, 2 * H))[:, ::2],
+             torch.zeros((H, 1)).t().t(), torch.zeros((1, H)).t(), torch.zeros(H)]
+    for x in bad_x:
+        with pytest.raises(ValueError):
+            M.route(x, None, None, c)
+        with pytest.raises(ValueError):
+            M.layer(x, None, None, view, None, c)
+    x = torch.zeros((2, H))
+    for idx, w in [(torch.zeros((2, k + 1), dtype=torch.int32), torch.zeros((2, k))),
+                   (torch.zeros((2, k), dtype=torch.int64), torch.zeros((2, k))),
+                   (torch.zeros((2, k), dtype=torch.int32), torch.zeros((3, k)))]:
+        with pytest.raises(ValueError):
+            M.ffn(x, idx, w, view, None, c)

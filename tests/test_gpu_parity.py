@@ -671,3 +671,34 @@ def test_layer_graph_replays_match_oracle(tiny, glm, layer, S):
         ref = O.moe_ffn(c, xh, ridx, rw, experts)
         err = max_rel_err(y.cpu().numpy(), ref)
         assert err <= TOL_FP32, (layer, S, i, err)
+
+
+@pytest.mark.parametrize("S", [1, 4, 9])
+def test_allocating_binding_calls(tiny, S):
+    """M.route / M.ffn / M.layer allocate their outputs (and a workspace) on x's device and give
+    the same bits as the raw-pointer calls; routing and outputs against the oracle."""
+    w = tiny.w.with_(tokens=S)
+    xh = gen.tokens(w, step=4100 + S)
+    x = dev(xh)
+    view = tiny.view()
+    idx, wt = M.route(x, tiny.W, tiny.bias, tiny.cfg)
+    y = M.ffn(x, idx, wt, view, tiny.shared, tiny.cfg)
+    li, lw, ly = M.layer(x, tiny.W, tiny.bias, view, tiny.shared, tiny.cfg)
+    torch.cuda.synchronize()
+    assert idx.dtype == torch.int32 and wt.dtype == torch.float32 and y.dtype == torch.float32
+    assert tuple(y.shape) == (S, tiny.c.hidden) and y.device == x.device
+    ridx, rw = check_route(tiny, xh, idx.cpu().numpy(), wt.cpu().numpy())
+    check_ffn(tiny, xh, ridx, rw, y.cpu().numpy(), np.arange(S), TOL_FP32)
+    e_idx, e_w, e_y = run_gpu(tiny, xh)
+    assert np.array_equal(idx.cpu().numpy(), e_idx) and np.array_equal(wt.cpu().numpy(), e_w)
+    assert np.array_equal(y.cpu().numpy(), e_y)
+    assert np.array_equal(li.cpu().numpy(), e_idx) and np.array_equal(ly.cpu().numpy(), e_y)
+    # wrong dtype, wrong width and a strided view are refused before anything is launched
+    H = tiny.c.hidden
+    for bad in (x.double(), x[:, : H - 32].contiguous(), torch.zeros((S, 2 * H), device="cuda")[:, ::2], x.t()):
+        if bad.dim() == 2 and tuple(bad.shape) == (S, H) and bad.is_contiguous() and bad.dtype == torch.float32:
+            continue  # x.t() of a single row is itself a valid [1, H] tensor
+        with pytest.raises(ValueError):
+            M.route(bad, tiny.W, tiny.bias, tiny.cfg)
+    with pytest.raises(ValueError):
+        M.ffn(x, idx[:, :1].contiguous(), wt, view, tiny.shared, tiny.cfg)
