@@ -97,7 +97,7 @@ WsLayout ws_layout(const moe_cfg &c, int32_t S) {
   L.xf = off; off += align256((size_t)S * gh * sizeof(float));
   L.hl = off; off += align256((size_t)S * k1 * gi * 24 * sizeof(uint32_t));
   L.hf = off; off += align256((size_t)S * k1 * gi * sizeof(float));
-  L.eptr = off; off += align256((size_t)kMaxK * sizeof(uint64_t));
+  L.eptr = off; off += align256(std::max<size_t>((size_t)kMaxK * sizeof(uint64_t), kWsPlanBytes));
   L.max_items = 0;
   L.max_mtiles = 0;
   if (S >= 2) {  // per-(token, rank) expert outputs, added in route order by the combine

@@ -23,6 +23,7 @@ constexpr int kMaxG = 64;        // n_group limit
 // Workspace header (first kWsSyncBytes bytes): two magic words written by
 // moe_workspace_init (the router refuses a workspace without them), then zeros.
 constexpr int kWsSyncBytes = 256;
+constexpr int kWsPlanBytes = 4096;  // the eptr region: k pointers, or a small batch's union and pointers
 constexpr uint32_t kWsMagic0 = 0x6D6F6534u, kWsMagic1 = 0x77733031u;
 
 // ---- slot layout of one packed expert (inter = I, hidden = H) -------------
@@ -104,7 +105,10 @@ struct FfnArgs {
   int8_t *hq;      // [S * (k+1), Imax]
   float *dh;       // [S * (k+1)]
   // one-token decode path
-  uint64_t *eptr;  // [k] routed experts' packed weights (0: not resident), resolved by the gate/up kernel
+  // one-token calls: [k] routed experts' packed weights (0: not resident), resolved by the gate/up
+  // kernel; two to four tokens: the batch union and its experts' weights, as the gate/up kernel
+  // derived them (kWsPlanBytes)
+  uint64_t *eptr;
   int32_t n_blk;   // row blocks of the down kernel
   int32_t tb;      // down tiles (8 rows) per row block
   int32_t dn_slots;  // two to four tokens: (token, expert) h rows the down kernel may hold in LDS per workgroup

@@ -453,6 +453,30 @@ __device__ inline void poison_h(const FfnArgs &a, int ntok, const int *pairs, in
     for (int tt = 0; tt < ntok; ++tt) a.h[(size_t)pairs[tt] * inter_stride + feat0 + lane] = __builtin_nanf("");
 }
 
+// The union and its experts' packed weights, as the gate/up kernel's first
+// workgroup derived them, handed to the down kernel of the same call through
+// the workspace (the eptr region): the plan's words, then one pointer per
+// unique expert.  The down kernel then needs one round of loads instead of
+// the plan's dependent loads and barriers and the slot-table lookups.
+constexpr int kPlanWords = (int)(sizeof(SmallPlan) / 4);
+constexpr int kPlanPtrOff = (kPlanWords + 1) / 2;  // in 64-bit words
+static_assert((kPlanPtrOff + kSmallS * kMaxK) * 8 <= kWsPlanBytes, "the plan record fits its workspace region");
+
+__device__ inline void store_small_plan(const FfnArgs &a, const SmallPlan &p, const uint8_t *const *ptr) {
+  const uint32_t *src = (const uint32_t *)&p;
+  for (int i = threadIdx.x; i < kPlanWords; i += blockDim.x) stg<uint32_t>((uint32_t *)a.eptr + i, src[i]);
+  if ((int)threadIdx.x < p.U) stg<uint64_t>(a.eptr + kPlanPtrOff + threadIdx.x, (uint64_t)(uintptr_t)ptr[threadIdx.x]);
+}
+
+// Ends with a barrier.  ptr[u] for u < U; the entries past U hold stale words.
+__device__ inline void load_small_plan(const FfnArgs &a, SmallPlan &p, const uint8_t **ptr) {
+  uint32_t *dst = (uint32_t *)&p;
+  for (int i = threadIdx.x; i < kPlanWords; i += blockDim.x) dst[i] = ldg<uint32_t>((const uint32_t *)a.eptr + i);
+  if ((int)threadIdx.x < kSmallS * kMaxK)
+    ptr[threadIdx.x] = (const uint8_t *)(uintptr_t)ldg<uint64_t>(a.eptr + kPlanPtrOff + threadIdx.x);
+  __syncthreads();
+}
+
 constexpr int kGuSmallWaves = 8;  // waves per small-batch gate/up workgroup (one workgroup per CU)
 
 // Two to four tokens, gate/up: the batch's (feature, token) pairs stream
@@ -533,6 +557,7 @@ __global__ __launch_bounds__(kGuSmallWaves * 64) void k_gateup_small(FfnArgs a) 
     store_limbs(xlds + (size_t)i * kXs, xf_lds + i, L);
   }
   __syncthreads();
+  if (blockIdx.x == 0) store_small_plan(a, plan, s_ptr);  // for the down kernel
   const long Pu = seg_start[U];
   const int up0 = (int)(wid * Pu / W), n = ns + (int)((wid + 1) * Pu / W) - up0;
   if (n <= 0) return;
@@ -610,7 +635,8 @@ __global__ __launch_bounds__(kGuSmallWaves * 64) void k_gateup_small(FfnArgs a) 
 //   Otherwise: for each unique expert, blocks of B tiles, each block once for
 //   every token of the expert, with the pair's h converted to limbs in registers
 //   whenever the pair changes.
-// Unique experts ascend, then the shared expert with every token.
+// Unique experts ascend, then the shared expert with every token.  The union
+// and the experts' weights are the ones the gate/up kernel stored.
 constexpr int kDnSmallWaves = 8;
 template <int NGD, int WF, bool HLDS>
 __global__ __launch_bounds__(kDnSmallWaves * 64) void k_down_small(FfnArgs a) {
@@ -620,7 +646,7 @@ __global__ __launch_bounds__(kDnSmallWaves * 64) void k_down_small(FfnArgs a) {
   __shared__ int s_slot0[kSmallS * kMaxK + 1];    // HLDS: LDS slot of unique expert u's first token (-1: none)
   __shared__ int s_nslots;
   extern __shared__ uint32_t hl[];  // HLDS: [slot][Imax/32][24] limbs, then [slot][Imax/32] factors
-  build_small_plan(a, plan, a.idx);
+  load_small_plan(a, plan, s_ptr);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwb = blockDim.x >> 6;
   const int U = plan.U, Imax = max(a.I, a.Is), nt = a.H / kDnRows, ngm = Imax / kGroup;
   const int B = (nt % 16 == 0) ? 16 : 4;  // tiles per block (nt is a multiple of 4)
@@ -633,7 +659,6 @@ __global__ __launch_bounds__(kDnSmallWaves * 64) void k_down_small(FfnArgs a) {
     }
     seg_start[U + 1] = start;
   }
-  if ((int)threadIdx.x < U) s_ptr[threadIdx.x] = expert_ptr(a, plan.uniq[threadIdx.x]);
   if ((int)threadIdx.x == U) s_ptr[U] = a.shared;
   __syncthreads();
   const int W = gridDim.x * nwb, wid = blockIdx.x * nwb + wave;
